@@ -1,0 +1,28 @@
+"""CPU oracle for the Q4NX dequant-GEMV / block-GEMM / MoE path.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the package smoke check and the
+benchmark's CPU-baseline leg may import or run anything in this package; the
+library's own path never does, and it shares no code, table or constant with
+the HIP kernels.  It is plain, slow and written to be checked by eye:
+
+* ``decode``  -- chunk bytes -> logical fields -> exact weights (float64), plus
+  a pure-Python scalar decoder used as brute force on tiny grids;
+* ``ref``     -- float64 products y = W x with the per-output error scale
+  a = sum |w x|, the tolerance test, SwiGLU, the MoE layer and its combine,
+  and the Q4_K -> q4_1 repack with its rounding bound.
+
+What it follows: the 1bit engine docs, page "NPU engine", section "Q4NX chunks"
+(tile grid, chunk kinds, decode formulas, the two Q8 code layouts) and the
+project's written chunk layout for the parts that page leaves to an unpublished
+header (listed in each function that depends on them).
+"""
+from .decode import (KIND_BYTES, decode_fields, weights_exact, weights_f32, unpack_expected,
+                     scalar_decode_chunk)
+from .ref import (gemv_ref, check_tol, tol_ratio, silu, swiglu, moe_layer_ref, moe_combine_ref,
+                  repack_q4k_to_q41, repack_bound)
+
+__all__ = [
+    "KIND_BYTES", "decode_fields", "weights_exact", "weights_f32", "unpack_expected",
+    "scalar_decode_chunk", "gemv_ref", "check_tol", "tol_ratio", "silu", "swiglu",
+    "moe_layer_ref", "moe_combine_ref", "repack_q4k_to_q41", "repack_bound",
+]
