@@ -1,0 +1,205 @@
+"""Python binding of libq4nx.so (include/q4nx.h): argument marshalling only.
+
+Every computation runs in the library's HIP kernels.  PyTorch supplies device
+memory and streams: tensors are passed by ``data_ptr()`` and work is enqueued
+on ``torch.cuda.current_stream()`` unless a stream is given.  When the
+library has not been built, importing this package raises ImportError: there
+is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libq4nx.so")
+
+Q4NX_OK, E_ARG, E_CHUNK_KIND, E_SHAPE, E_SHORT, E_ALIGN, E_WORKSPACE, E_Q8_LAYOUT, E_HIP = range(9)
+CHUNK_BYTES = {"q4_1": 5120, "q4_k": 4736, "q8": 8704}
+Q8_LAYOUT = {None: -1, "A": 0, "B": 1}
+GEMV_MAX_M = 8
+GEMM_MAX_M = 64
+BATCH_MAX_JOBS = 64
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+
+class Q4nxError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"q4nx status {status}: {detail}")
+        self.status = status
+
+
+class Weight(ctypes.Structure):
+    _fields_ = [("chunks", ctypes.c_void_p), ("nbytes", ctypes.c_int64), ("rows", ctypes.c_int32),
+                ("cols", ctypes.c_int32), ("chunk_bytes", ctypes.c_int32),
+                ("q8_layout", ctypes.c_int32)]
+
+
+class GemvJob(ctypes.Structure):
+    _fields_ = [("w", Weight), ("x", ctypes.c_void_p), ("y", ctypes.c_void_p)]
+
+
+class MoeLayer(ctypes.Structure):
+    _fields_ = [("n_experts", ctypes.c_int32), ("d_model", ctypes.c_int32),
+                ("d_expert", ctypes.c_int32), ("d_shared", ctypes.c_int32),
+                ("chunk_bytes", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("gate", ctypes.c_void_p), ("up", ctypes.c_void_p), ("down", ctypes.c_void_p),
+                ("gate_stride", ctypes.c_int64), ("up_stride", ctypes.c_int64),
+                ("down_stride", ctypes.c_int64), ("gate_bytes", ctypes.c_int64),
+                ("up_bytes", ctypes.c_int64), ("down_bytes", ctypes.c_int64),
+                ("sh_gate", Weight), ("sh_up", Weight), ("sh_down", Weight)]
+
+
+class MoeDebug(ctypes.Structure):
+    _fields_ = [("h", ctypes.c_void_p), ("d", ctypes.c_void_p), ("h_shared", ctypes.c_void_p),
+                ("d_shared", ctypes.c_void_p)]
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_lib.q4nx_weight_check.argtypes = [ctypes.POINTER(Weight)]
+_lib.q4nx_gemv.argtypes = [ctypes.POINTER(Weight), _P, _P, _I, _P]
+_lib.q4nx_gemv_batched.argtypes = [ctypes.POINTER(GemvJob), _I, _I, _P]
+_lib.q4nx_gemm_block.argtypes = [ctypes.POINTER(Weight), _P, _P, _I, _P]
+_lib.q4nx_moe_ws.argtypes = [ctypes.POINTER(MoeLayer), _I, _I]
+_lib.q4nx_moe_ws.restype = ctypes.c_size_t
+_lib.q4nx_moe_experts.argtypes = [ctypes.POINTER(MoeLayer), _P, _P, _P, _I, _I, _P,
+                                  ctypes.POINTER(MoeDebug), _P, ctypes.c_size_t, _P]
+_lib.q4nx_unpack.argtypes = [ctypes.POINTER(Weight), _P, _P, _P, _P, _P]
+_lib.q4nx_decode.argtypes = [ctypes.POINTER(Weight), _P, _P]
+_lib.q4nx_status_str.argtypes = [_I]
+_lib.q4nx_status_str.restype = ctypes.c_char_p
+_lib.q4nx_last_error.restype = ctypes.c_char_p
+for _f in ("q4nx_weight_check", "q4nx_gemv", "q4nx_gemv_batched", "q4nx_gemm_block",
+           "q4nx_moe_experts", "q4nx_unpack", "q4nx_decode", "q4nx_version"):
+    getattr(_lib, _f).restype = ctypes.c_int
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raw ctypes handle)."""
+    return _lib
+
+
+def last_error() -> str:
+    return _lib.q4nx_last_error().decode()
+
+
+def status_str(status: int) -> str:
+    return _lib.q4nx_status_str(status).decode()
+
+
+def version() -> int:
+    return _lib.q4nx_version()
+
+
+def _check(status: int):
+    if status != Q4NX_OK:
+        raise Q4nxError(status, last_error())
+
+
+# ----------------------------------------------------------------------------
+# descriptors
+# ----------------------------------------------------------------------------
+def _ptr(t) -> int:
+    if t is None:
+        return 0
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _nbytes(t) -> int:
+    if t is None or isinstance(t, int):
+        return 0          # a raw address carries no size: the caller passes it explicitly
+    return t.numel() * t.element_size()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def weight(chunks, rows: int, cols: int, kind: str, q8_layout: str | None = None,
+           nbytes: int | None = None) -> Weight:
+    """Descriptor of a Q4NX weight held in ``chunks`` (a device tensor or a raw address)."""
+    return Weight(_ptr(chunks), _nbytes(chunks) if nbytes is None else nbytes, rows, cols,
+                  CHUNK_BYTES[kind] if isinstance(kind, str) else int(kind),
+                  Q8_LAYOUT[q8_layout] if q8_layout in Q8_LAYOUT else int(q8_layout))
+
+
+def weight_check(w: Weight) -> int:
+    """Host-only descriptor check; returns the status code (0 = ok)."""
+    return _lib.q4nx_weight_check(ctypes.byref(w))
+
+
+# ----------------------------------------------------------------------------
+# calls
+# ----------------------------------------------------------------------------
+def gemv(w: Weight, x, y, M: int = 1, stream=None) -> None:
+    """y[M, rows] (fp32) = x[M, cols] (bf16) @ W^T."""
+    _check(_lib.q4nx_gemv(ctypes.byref(w), _ptr(x), _ptr(y), M, _stream(stream)))
+
+
+def gemv_batched(jobs, M: int = 1, stream=None) -> None:
+    """jobs: sequence of (Weight, x, y); runs them as independent GEMVs."""
+    arr = (GemvJob * len(jobs))(*[GemvJob(w, _ptr(x), _ptr(y)) for w, x, y in jobs])
+    _check(_lib.q4nx_gemv_batched(arr, len(jobs), M, _stream(stream)))
+
+
+def gemm_block(w: Weight, X, Y, M: int, stream=None) -> None:
+    """Y[M, rows] (fp32) = X[M, cols] (bf16) @ W^T for M <= 64."""
+    _check(_lib.q4nx_gemm_block(ctypes.byref(w), _ptr(X), _ptr(Y), M, _stream(stream)))
+
+
+def moe_layer(n_experts: int, d_model: int, d_expert: int, kind: str, gate, up, down,
+              gate_stride: int, up_stride: int, down_stride: int,
+              shared=None, d_shared: int = 0, gate_bytes=None, up_bytes=None,
+              down_bytes=None) -> MoeLayer:
+    """MoE layer descriptor.  ``shared`` = (Weight gate, Weight up, Weight down) or None."""
+    L = MoeLayer()
+    L.n_experts, L.d_model, L.d_expert = n_experts, d_model, d_expert
+    L.d_shared = d_shared if shared is not None else 0
+    L.chunk_bytes = CHUNK_BYTES[kind]
+    L.reserved = 0
+    L.gate, L.up, L.down = _ptr(gate), _ptr(up), _ptr(down)
+    L.gate_stride, L.up_stride, L.down_stride = gate_stride, up_stride, down_stride
+    L.gate_bytes = _nbytes(gate) if gate_bytes is None else gate_bytes
+    L.up_bytes = _nbytes(up) if up_bytes is None else up_bytes
+    L.down_bytes = _nbytes(down) if down_bytes is None else down_bytes
+    if shared is not None:
+        L.sh_gate, L.sh_up, L.sh_down = shared
+    return L
+
+
+def moe_ws(L: MoeLayer, T: int, k: int) -> int:
+    return int(_lib.q4nx_moe_ws(ctypes.byref(L), T, k))
+
+
+def moe_experts(L: MoeLayer, X, ids, p, Y, T: int, k: int, ws, dbg: dict | None = None,
+                stream=None, ws_bytes: int | None = None) -> None:
+    """Y[T, D] = MoE layer of X[T, D] with routing ids[T, k] / p[T, k]; ws from moe_ws()."""
+    d = None
+    if dbg:
+        d = MoeDebug(_ptr(dbg.get("h")), _ptr(dbg.get("d")), _ptr(dbg.get("h_shared")),
+                     _ptr(dbg.get("d_shared")))
+    _check(_lib.q4nx_moe_experts(ctypes.byref(L), _ptr(X), _ptr(ids), _ptr(p), T, k, _ptr(Y),
+                                 ctypes.byref(d) if d is not None else None, _ptr(ws),
+                                 _nbytes(ws) if ws_bytes is None else ws_bytes,
+                                 _stream(stream)))
+
+
+def unpack(w: Weight, codes, meta0, meta1=None, row_meta=None, stream=None) -> None:
+    _check(_lib.q4nx_unpack(ctypes.byref(w), _ptr(codes), _ptr(meta0), _ptr(meta1),
+                            _ptr(row_meta), _stream(stream)))
+
+
+def decode(w: Weight, out, stream=None) -> None:
+    _check(_lib.q4nx_decode(ctypes.byref(w), _ptr(out), _stream(stream)))

@@ -1,0 +1,59 @@
+"""Build libq4nx.so in-tree with hipcc for gfx950.
+
+Each HIP source compiles to its own object in parallel, then one link.  All
+device code is built with packed-fp32 instructions disabled.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libq4nx.so")
+OBJDIR = os.path.join(os.path.dirname(HERE), "_build")
+SOURCES = ["api.hip", "gemv.hip", "gemm.hip", "decode.hip", "moe.hip"]
+ARCH = os.environ.get("Q4NX_OFFLOAD_ARCH", "gfx950")
+FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def _hipcc() -> str:
+    for c in ("/opt/rocm/bin/hipcc", "hipcc"):
+        if os.path.sep not in c or os.path.exists(c):
+            return c
+    return "hipcc"
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    err = "\n".join(l for l in r.stderr.splitlines() if "not a recognized feature" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"command failed ({r.returncode}): {' '.join(cmd)}\n{err}")
+    return err
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source and link libq4nx.so; returns the library path."""
+    os.makedirs(OBJDIR, exist_ok=True)
+    cc = _hipcc()
+    jobs = []
+    for src in SOURCES:
+        obj = os.path.join(OBJDIR, src.replace(".hip", ".o"))
+        jobs.append((obj, [cc, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]))
+    with ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 4)) as ex:
+        outs = list(ex.map(lambda j: _run(j[1]), jobs))
+    if verbose:
+        for o in outs:
+            if o.strip():
+                print(o, file=sys.stderr)
+    tmp = LIB + ".tmp"
+    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *[j[0] for j in jobs]])
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,358 @@
+// C ABI of libq4nx.so (declared in include/q4nx.h): host-side checks, then
+// launches.  Every check runs before anything is enqueued, and no check
+// touches the device, so the error paths can be exercised without a GPU.
+//
+// Check rules for a weight follow the 1bit engine docs, page "NPU engine"
+// (section "Q4NX chunks": the chunk size names the kind, the two Q8 layouts
+// cannot be told apart; section "From a GGUF": a checker refuses an unknown
+// chunk size or a tensor shorter than its layout needs).
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/q4nx.h"
+#include "moe_args.h"
+#include "q4nx_dev.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = std::string(q4nx_status_str(status)) + ": " + buf;
+  return status;
+}
+
+int ok() {
+  g_last_error.clear();
+  return Q4NX_OK;
+}
+
+int hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return ok();
+  return fail(Q4NX_E_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int kind_of(const q4nx_weight* w) {
+  switch (w->chunk_bytes) {
+    case Q4NX_Q4_1_BYTES: return q4nx::KIND_Q4_1;
+    case Q4NX_Q4_K_BYTES: return q4nx::KIND_Q4_K;
+    default: return w->q8_layout == Q4NX_Q8_LAYOUT_A ? q4nx::KIND_Q8_A : q4nx::KIND_Q8_B;
+  }
+}
+
+int check_weight(const q4nx_weight* w, const char* name) {
+  if (!w) return fail(Q4NX_E_ARG, "%s: null descriptor", name);
+  if (!w->chunks) return fail(Q4NX_E_ARG, "%s: null chunk pointer", name);
+  const int cb = w->chunk_bytes;
+  if (cb != Q4NX_Q4_1_BYTES && cb != Q4NX_Q4_K_BYTES && cb != Q4NX_Q8_BYTES)
+    return fail(Q4NX_E_CHUNK_KIND, "%s: unknown chunk size %d (5120 q4_1, 4736 Q4_K, 8704 Q8)",
+                name, cb);
+  if (cb == Q4NX_Q8_BYTES && w->q8_layout != Q4NX_Q8_LAYOUT_A && w->q8_layout != Q4NX_Q8_LAYOUT_B)
+    return fail(Q4NX_E_Q8_LAYOUT, "%s: Q8 weight needs its code layout (A or B); it cannot be "
+                "detected from the data", name);
+  if (w->rows <= 0 || w->rows % 32 || w->cols <= 0 || w->cols % 256)
+    return fail(Q4NX_E_SHAPE, "%s: %d x %d is not a whole number of 32 x 256 tiles", name,
+                w->rows, w->cols);
+  const int64_t need = (int64_t)(w->rows / 32) * (w->cols / 256) * cb;
+  if (w->nbytes < need)
+    return fail(Q4NX_E_SHORT, "%s: %lld bytes given, the %d x %d grid needs %lld", name,
+                (long long)w->nbytes, w->rows, w->cols, (long long)need);
+  if (!aligned(w->chunks, 16)) return fail(Q4NX_E_ALIGN, "%s: chunks not 16-byte aligned", name);
+  return Q4NX_OK;
+}
+
+int pick_ks_total(int64_t total_tr) {
+  if (total_tr >= 2048) return 1;
+  if (total_tr >= 1024) return 2;
+  return 4;
+}
+
+int cap_ks(int ks, int TC) {
+  const int lim = TC >= 4 ? 4 : (TC >= 2 ? 2 : 1);
+  return ks < lim ? ks : lim;
+}
+
+// Launch one kind's jobs (all valid, same M) in as few launches as the job
+// table allows.
+int run_batch(int kind, const q4nx_gemv_job* const* jobs, int n, int M, hipStream_t s) {
+  int64_t total_tr = 0;
+  for (int i = 0; i < n; ++i) total_tr += jobs[i]->w.rows / 32;
+  const int ks_all = pick_ks_total(total_tr);
+  for (int i0 = 0; i0 < n; i0 += q4nx::kMaxBatch) {
+    const int cnt = n - i0 < q4nx::kMaxBatch ? n - i0 : q4nx::kMaxBatch;
+    q4nx::GemvBatch b;
+    memset(&b, 0, sizeof b);
+    int wg = 0;
+    for (int t = 0; t < cnt; ++t) {
+      const q4nx_gemv_job* j = jobs[i0 + t];
+      q4nx::GemvJob& g = b.job[t];
+      g.w = static_cast<const uint8_t*>(j->w.chunks);
+      g.x = j->x;
+      g.y = j->y;
+      g.TR = j->w.rows / 32;
+      g.TC = j->w.cols / 256;
+      g.ldx = j->w.cols;
+      g.ldy = j->w.rows;
+      g.ks = cap_ks(ks_all, g.TC);
+      g.wg_begin = wg;
+      const int rpw = 4 / g.ks;
+      wg += (g.TR + rpw - 1) / rpw;
+    }
+    b.n_jobs = cnt;
+    const hipError_t e = q4nx::launch_gemv(kind, M, b, wg, s);
+    if (e != hipSuccess) return hip_status(e, "gemv launch");
+  }
+  return Q4NX_OK;
+}
+
+int check_gemv_io(const q4nx_weight* w, const void* x, const float* y, int M, const char* name) {
+  int st = check_weight(w, name);
+  if (st) return st;
+  if (!x || !y) return fail(Q4NX_E_ARG, "%s: null x or y", name);
+  if (M < 1 || M > Q4NX_GEMV_MAX_M)
+    return fail(Q4NX_E_ARG, "%s: M = %d outside 1..%d", name, M, (int)Q4NX_GEMV_MAX_M);
+  if (!aligned(x, 16)) return fail(Q4NX_E_ALIGN, "%s: x not 16-byte aligned", name);
+  if (!aligned(y, 4)) return fail(Q4NX_E_ALIGN, "%s: y not 4-byte aligned", name);
+  return Q4NX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* q4nx_status_str(int status) {
+  switch (status) {
+    case Q4NX_OK: return "ok";
+    case Q4NX_E_ARG: return "invalid argument";
+    case Q4NX_E_CHUNK_KIND: return "unknown or unsupported chunk kind";
+    case Q4NX_E_SHAPE: return "bad shape";
+    case Q4NX_E_SHORT: return "tensor shorter than its layout needs";
+    case Q4NX_E_ALIGN: return "misaligned pointer";
+    case Q4NX_E_WORKSPACE: return "workspace missing or too small";
+    case Q4NX_E_Q8_LAYOUT: return "Q8 code layout not given";
+    case Q4NX_E_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* q4nx_last_error(void) { return g_last_error.c_str(); }
+
+int q4nx_version(void) { return 100; }
+
+int q4nx_weight_check(const q4nx_weight* w) {
+  const int st = check_weight(w, "weight");
+  return st ? st : ok();
+}
+
+int q4nx_gemv(const q4nx_weight* w, const uint16_t* x, float* y, int M, void* stream) {
+  const int st = check_gemv_io(w, x, y, M, "gemv");
+  if (st) return st;
+  q4nx_gemv_job j{*w, x, y};
+  const q4nx_gemv_job* pj = &j;
+  const int r = run_batch(kind_of(w), &pj, 1, M, static_cast<hipStream_t>(stream));
+  return r ? r : ok();
+}
+
+int q4nx_gemv_batched(const q4nx_gemv_job* jobs, int n_jobs, int M, void* stream) {
+  if (!jobs) return fail(Q4NX_E_ARG, "gemv_batched: null job array");
+  if (n_jobs < 1 || n_jobs > Q4NX_BATCH_MAX_JOBS)
+    return fail(Q4NX_E_ARG, "gemv_batched: %d jobs outside 1..%d", n_jobs,
+                (int)Q4NX_BATCH_MAX_JOBS);
+  for (int i = 0; i < n_jobs; ++i) {
+    char name[48];
+    snprintf(name, sizeof name, "gemv_batched job %d", i);
+    const int st = check_gemv_io(&jobs[i].w, jobs[i].x, jobs[i].y, M, name);
+    if (st) return st;
+  }
+  const q4nx_gemv_job* by_kind[4][Q4NX_BATCH_MAX_JOBS];
+  int cnt[4] = {0, 0, 0, 0};
+  for (int i = 0; i < n_jobs; ++i) {
+    const int k = kind_of(&jobs[i].w);
+    by_kind[k][cnt[k]++] = &jobs[i];
+  }
+  for (int k = 0; k < 4; ++k) {
+    if (!cnt[k]) continue;
+    const int r = run_batch(k, by_kind[k], cnt[k], M, static_cast<hipStream_t>(stream));
+    if (r) return r;
+  }
+  return ok();
+}
+
+int q4nx_gemm_block(const q4nx_weight* w, const uint16_t* X, float* Y, int M, void* stream) {
+  int st = check_weight(w, "gemm_block");
+  if (st) return st;
+  if (w->chunk_bytes == Q4NX_Q8_BYTES)
+    return fail(Q4NX_E_CHUNK_KIND, "gemm_block: Q8 weights are not supported by the block GEMM");
+  if (!X || !Y) return fail(Q4NX_E_ARG, "gemm_block: null X or Y");
+  if (M < 1 || M > Q4NX_GEMM_MAX_M)
+    return fail(Q4NX_E_ARG, "gemm_block: M = %d outside 1..%d", M, (int)Q4NX_GEMM_MAX_M);
+  if (!aligned(X, 16)) return fail(Q4NX_E_ALIGN, "gemm_block: X not 16-byte aligned");
+  if (!aligned(Y, 4)) return fail(Q4NX_E_ALIGN, "gemm_block: Y not 4-byte aligned");
+  const hipError_t e = q4nx::launch_gemm(kind_of(w), static_cast<const uint8_t*>(w->chunks), X, Y,
+                                         w->rows / 32, w->cols / 256, M,
+                                         static_cast<hipStream_t>(stream));
+  return hip_status(e, "gemm_block launch");
+}
+
+// ---------------------------------------------------------------------------
+// MoE
+// ---------------------------------------------------------------------------
+static int check_arena(const void* base, int64_t stride, int64_t bytes, int n, int64_t need,
+                       const char* name) {
+  if (!base) return fail(Q4NX_E_ARG, "moe: null %s arena", name);
+  if (!aligned(base, 16) || stride % 16)
+    return fail(Q4NX_E_ALIGN, "moe: %s arena or stride not 16-byte aligned", name);
+  if (stride < need) return fail(Q4NX_E_SHAPE, "moe: %s stride %lld below one expert's %lld bytes",
+                                 name, (long long)stride, (long long)need);
+  const int64_t total = (int64_t)(n - 1) * stride + need;
+  if (bytes < total)
+    return fail(Q4NX_E_SHORT, "moe: %s arena holds %lld bytes, %d experts need %lld", name,
+                (long long)bytes, n, (long long)total);
+  return Q4NX_OK;
+}
+
+static int check_moe_layer(const q4nx_moe_layer* L) {
+  if (!L) return fail(Q4NX_E_ARG, "moe: null layer");
+  if (L->reserved) return fail(Q4NX_E_ARG, "moe: reserved field must be 0");
+  if (L->n_experts < 1 || L->n_experts >= (1 << 19))
+    return fail(Q4NX_E_ARG, "moe: n_experts = %d outside 1..524287", L->n_experts);
+  if (L->chunk_bytes != Q4NX_Q4_1_BYTES && L->chunk_bytes != Q4NX_Q4_K_BYTES)
+    return fail(Q4NX_E_CHUNK_KIND, "moe: experts must be q4_1 (5120) or Q4_K (4736), got %d",
+                L->chunk_bytes);
+  if (L->d_model <= 0 || L->d_model % 256 || L->d_expert <= 0 || L->d_expert % 256 ||
+      L->d_shared < 0 || L->d_shared % 256)
+    return fail(Q4NX_E_SHAPE, "moe: d_model, d_expert, d_shared must be multiples of 256 "
+                "(d_shared may be 0), got %d, %d, %d", L->d_model, L->d_expert, L->d_shared);
+  const int64_t cb = L->chunk_bytes;
+  const int64_t gu = (int64_t)(L->d_expert / 32) * (L->d_model / 256) * cb;
+  const int64_t dn = (int64_t)(L->d_model / 32) * (L->d_expert / 256) * cb;
+  int st = check_arena(L->gate, L->gate_stride, L->gate_bytes, L->n_experts, gu, "gate");
+  if (!st) st = check_arena(L->up, L->up_stride, L->up_bytes, L->n_experts, gu, "up");
+  if (!st) st = check_arena(L->down, L->down_stride, L->down_bytes, L->n_experts, dn, "down");
+  if (st) return st;
+  if (L->d_shared) {
+    const q4nx_weight* sw[3] = {&L->sh_gate, &L->sh_up, &L->sh_down};
+    const char* nm[3] = {"moe shared gate", "moe shared up", "moe shared down"};
+    for (int i = 0; i < 3; ++i) {
+      st = check_weight(sw[i], nm[i]);
+      if (st) return st;
+      if (sw[i]->chunk_bytes != L->chunk_bytes)
+        return fail(Q4NX_E_CHUNK_KIND, "%s: kind differs from the routed experts'", nm[i]);
+      const int rows = i < 2 ? L->d_shared : L->d_model;
+      const int cols = i < 2 ? L->d_model : L->d_shared;
+      if (sw[i]->rows != rows || sw[i]->cols != cols)
+        return fail(Q4NX_E_SHAPE, "%s: %d x %d, expected %d x %d", nm[i], sw[i]->rows,
+                    sw[i]->cols, rows, cols);
+    }
+  }
+  return Q4NX_OK;
+}
+
+static int moe_hstride(const q4nx_moe_layer* L) {
+  return L->d_expert > L->d_shared ? L->d_expert : L->d_shared;
+}
+
+size_t q4nx_moe_ws(const q4nx_moe_layer* L, int T, int k) {
+  if (check_moe_layer(L) || T < 1 || k < 1 || T > 4096 || k > 16 || T * k > q4nx::kMoeMaxPairs)
+    return 0;
+  return q4nx::moe_ws_layout(T * k, T, L->d_model, moe_hstride(L)).total;
+}
+
+int q4nx_moe_experts(const q4nx_moe_layer* L, const uint16_t* X, const int32_t* ids,
+                     const float* p, int T, int k, float* Y, const q4nx_moe_debug* dbg, void* ws,
+                     size_t ws_bytes, void* stream) {
+  int st = check_moe_layer(L);
+  if (st) return st;
+  if (!X || !ids || !p || !Y) return fail(Q4NX_E_ARG, "moe: null X, ids, p or Y");
+  if (T < 1 || T > 4096 || k < 1 || k > 16 || T * k > q4nx::kMoeMaxPairs)
+    return fail(Q4NX_E_ARG, "moe: T = %d, k = %d outside T 1..4096, k 1..16, T*k <= %d", T, k,
+                q4nx::kMoeMaxPairs);
+  if (!aligned(X, 16) || !aligned(ids, 4) || !aligned(p, 4) || !aligned(Y, 4))
+    return fail(Q4NX_E_ALIGN, "moe: X must be 16-byte, ids/p/Y 4-byte aligned");
+  const q4nx::MoeWsLayout lay = q4nx::moe_ws_layout(T * k, T, L->d_model, moe_hstride(L));
+  if (!ws || ws_bytes < lay.total)
+    return fail(Q4NX_E_WORKSPACE, "moe: workspace of %zu bytes, %zu needed", ws_bytes, lay.total);
+  if (!aligned(ws, 256)) return fail(Q4NX_E_ALIGN, "moe: workspace not 256-byte aligned");
+
+  q4nx::MoeArgs a;
+  memset(&a, 0, sizeof a);
+  a.gate = static_cast<const uint8_t*>(L->gate);
+  a.up = static_cast<const uint8_t*>(L->up);
+  a.down = static_cast<const uint8_t*>(L->down);
+  a.gate_stride = L->gate_stride;
+  a.up_stride = L->up_stride;
+  a.down_stride = L->down_stride;
+  if (L->d_shared) {
+    a.sgate = static_cast<const uint8_t*>(L->sh_gate.chunks);
+    a.sup = static_cast<const uint8_t*>(L->sh_up.chunks);
+    a.sdown = static_cast<const uint8_t*>(L->sh_down.chunks);
+  }
+  a.n_experts = L->n_experts;
+  a.D = L->d_model;
+  a.De = L->d_expert;
+  a.Ds = L->d_shared;
+  a.X = X;
+  a.ids = ids;
+  a.p = p;
+  a.Y = Y;
+  a.T = T;
+  a.k = k;
+  a.tb = T == 1 ? 1 : 4;
+  a.hstride = moe_hstride(L);
+  if (dbg) {
+    a.dbg_h = dbg->h;
+    a.dbg_d = dbg->d;
+    a.dbg_h_shared = dbg->h_shared;
+    a.dbg_d_shared = dbg->d_shared;
+  }
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  a.hdr = reinterpret_cast<uint32_t*>(w + lay.hdr);
+  a.sorted = reinterpret_cast<int32_t*>(w + lay.sorted);
+  a.seg = reinterpret_cast<int32_t*>(w + lay.seg);
+  a.batch0 = reinterpret_cast<int32_t*>(w + lay.batch0);
+  a.hbuf = reinterpret_cast<uint16_t*>(w + lay.hbuf);
+  a.dbuf = reinterpret_cast<float*>(w + lay.dbuf);
+  const hipError_t e = q4nx::launch_moe(L->chunk_bytes == Q4NX_Q4_1_BYTES ? q4nx::KIND_Q4_1
+                                                                          : q4nx::KIND_Q4_K,
+                                        a, static_cast<hipStream_t>(stream));
+  return hip_status(e, "moe launch");
+}
+
+// ---------------------------------------------------------------------------
+// decoders
+// ---------------------------------------------------------------------------
+int q4nx_unpack(const q4nx_weight* w, uint8_t* codes, uint16_t* meta0, uint16_t* meta1,
+                uint16_t* row_meta, void* stream) {
+  int st = check_weight(w, "unpack");
+  if (st) return st;
+  if (!codes || !meta0) return fail(Q4NX_E_ARG, "unpack: null codes or meta0");
+  if (!aligned(meta0, 2) || (meta1 && !aligned(meta1, 2)) || (row_meta && !aligned(row_meta, 2)))
+    return fail(Q4NX_E_ALIGN, "unpack: metadata outputs must be 2-byte aligned");
+  const hipError_t e = q4nx::launch_unpack(kind_of(w), static_cast<const uint8_t*>(w->chunks),
+                                           w->rows / 32, w->cols / 256, codes, meta0, meta1,
+                                           row_meta, static_cast<hipStream_t>(stream));
+  return hip_status(e, "unpack launch");
+}
+
+int q4nx_decode(const q4nx_weight* w, float* out, void* stream) {
+  int st = check_weight(w, "decode");
+  if (st) return st;
+  if (!out) return fail(Q4NX_E_ARG, "decode: null output");
+  if (!aligned(out, 4)) return fail(Q4NX_E_ALIGN, "decode: output not 4-byte aligned");
+  const hipError_t e = q4nx::launch_decode(kind_of(w), static_cast<const uint8_t*>(w->chunks),
+                                           w->rows / 32, w->cols / 256, out,
+                                           static_cast<hipStream_t>(stream));
+  return hip_status(e, "decode launch");
+}
+
+}  // extern "C"

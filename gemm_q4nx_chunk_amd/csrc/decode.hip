@@ -1,0 +1,116 @@
+// Chunk decoders as a test surface (1bit engine docs, page "NPU engine",
+// section "Q4NX chunks": the decoders of the three kinds are checked bit for
+// bit).  One workgroup per chunk; thread t handles row r = t/8, group g = t%8
+// (32 weights) and writes its codes, metadata and fp32 weights in logical
+// [rows][cols] order.
+//
+// fp32 values: code*scale (q4_1), S*scale*code and M*min (Q4_K) and d*code
+// (Q8) are all exact in fp32, so one fma/mul gives the exact value rounded
+// once to nearest even.
+#include "q4nx_dev.h"
+
+namespace q4nx {
+
+template <int KIND>
+__global__ __launch_bounds__(256) void k_unpack(const uint8_t* __restrict__ w, int TR, int TC,
+                                                uint8_t* __restrict__ codes,
+                                                uint16_t* __restrict__ meta0,
+                                                uint16_t* __restrict__ meta1,
+                                                uint16_t* __restrict__ row_meta,
+                                                float* __restrict__ out) {
+  constexpr int CB = ChunkBytes<KIND>::value;
+  const int chunk = blockIdx.x, tr = chunk / TC, tc = chunk - tr * TC;
+  const int r = threadIdx.x >> 3, g = threadIdx.x & 7;
+  const uint8_t* ck = w + (size_t)chunk * CB;
+  const int K = TC * 256, G = K / 32;
+  const size_t row = (size_t)tr * 32 + r;
+  const int col0 = tc * 256 + g * 32;
+
+  uint8_t c8[32];
+  uint16_t m0 = 0, m1 = 0, S = 0, Mm = 0;
+  float val[32];
+  if constexpr (KIND == KIND_Q4_1 || KIND == KIND_Q4_K) {
+    const u32x4 v0 = *reinterpret_cast<const u32x4*>(ck + r * 128 + g * 16);
+#pragma unroll
+    for (int j = 0; j < 32; ++j) c8[j] = (uint8_t)((v0[j >> 3] >> (4 * (j & 7))) & 0xFu);
+    if constexpr (KIND == KIND_Q4_1) {
+      const uint32_t sz = *reinterpret_cast<const uint32_t*>(ck + 4096 + 4 * (8 * r + g));
+      m0 = (uint16_t)(sz & 0xFFFFu);
+      m1 = (uint16_t)(sz >> 16);
+      const float s = bf16lo(sz), z = bf16hi(sz);
+#pragma unroll
+      for (int j = 0; j < 32; ++j) val[j] = fmaf((float)c8[j], s, z);
+    } else {
+      const uint16_t scmn = *reinterpret_cast<const uint16_t*>(ck + 4096 + 2 * (8 * r + g));
+      const uint32_t sm = *reinterpret_cast<const uint32_t*>(ck + 4608 + 4 * r);
+      m0 = scmn & 0xFFu;
+      m1 = scmn >> 8;
+      S = (uint16_t)(sm & 0xFFFFu);
+      Mm = (uint16_t)(sm >> 16);
+      const float a = bf16lo(sm) * (float)m0, b = bf16hi(sm) * (float)m1;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) val[j] = fmaf((float)c8[j], a, b);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const int k = g * 32 + j;
+      const int pos = (KIND == KIND_Q8_A)
+                          ? k * 32 + r
+                          : (r >> 4) * 4096 + (k >> 5) * 512 + (k & 31) * 16 + (r & 15);
+      c8[j] = ck[pos];
+    }
+    m0 = *reinterpret_cast<const uint16_t*>(ck + 8192 + 2 * (8 * r + g));
+    const float d = __uint_as_float((uint32_t)m0 << 16);
+#pragma unroll
+    for (int j = 0; j < 32; ++j) val[j] = d * (float)(int8_t)c8[j];
+  }
+
+  if (codes) {
+    uint8_t* dst = codes + row * K + col0;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) dst[j] = c8[j];
+  }
+  if (meta0) meta0[row * G + tc * 8 + g] = m0;
+  if (meta1) meta1[row * G + tc * 8 + g] = m1;
+  if (row_meta && g == 0) {
+    row_meta[(row * TC + tc) * 2 + 0] = S;
+    row_meta[(row * TC + tc) * 2 + 1] = Mm;
+  }
+  if (out) {
+    float* dst = out + row * K + col0;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) dst[j] = val[j];
+  }
+}
+
+template <int KIND>
+static void launch_k(const uint8_t* w, int TR, int TC, uint8_t* codes, uint16_t* meta0,
+                     uint16_t* meta1, uint16_t* row_meta, float* out, hipStream_t s) {
+  hipLaunchKernelGGL(k_unpack<KIND>, dim3(TR * TC), dim3(256), 0, s, w, TR, TC, codes, meta0,
+                     meta1, row_meta, out);
+}
+
+static hipError_t launch_any(int kind, const uint8_t* w, int TR, int TC, uint8_t* codes,
+                             uint16_t* meta0, uint16_t* meta1, uint16_t* row_meta, float* out,
+                             hipStream_t s) {
+  switch (kind) {
+    case KIND_Q4_1: launch_k<KIND_Q4_1>(w, TR, TC, codes, meta0, meta1, row_meta, out, s); break;
+    case KIND_Q4_K: launch_k<KIND_Q4_K>(w, TR, TC, codes, meta0, meta1, row_meta, out, s); break;
+    case KIND_Q8_A: launch_k<KIND_Q8_A>(w, TR, TC, codes, meta0, meta1, row_meta, out, s); break;
+    case KIND_Q8_B: launch_k<KIND_Q8_B>(w, TR, TC, codes, meta0, meta1, row_meta, out, s); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_unpack(int kind, const uint8_t* w, int TR, int TC, uint8_t* codes,
+                         uint16_t* meta0, uint16_t* meta1, uint16_t* row_meta, hipStream_t s) {
+  return launch_any(kind, w, TR, TC, codes, meta0, meta1, row_meta, nullptr, s);
+}
+
+hipError_t launch_decode(int kind, const uint8_t* w, int TR, int TC, float* out, hipStream_t s) {
+  return launch_any(kind, w, TR, TC, nullptr, nullptr, nullptr, nullptr, out, s);
+}
+
+}  // namespace q4nx

@@ -1,0 +1,218 @@
+// Q4NX dequant-GEMV kernels for gfx950: y[m] = W x[m] for M <= 8 activation rows.
+//
+// Decode reads every weight once per token and does two flops with it, so the
+// kernel is bound by HBM bandwidth (Strata article, section 1: decode speed is
+// set by the bytes of weights read per token).  The design keeps the weight
+// stream as wide 16-byte nontemporal loads of whole chunks, keeps x in
+// registers, unpacks and scales in registers, and leaves the ALU work per
+// weight small enough to hide under the stream.
+//
+// Work split: a 256-thread workgroup (4 waves) owns 4/ks tile rows; the ks
+// waves of one tile row take contiguous runs of its chunks, and their partial
+// row sums meet in LDS, where one pass adds them in wave order.  No atomics:
+// the result bits do not depend on timing.
+#include "q4_core.h"
+
+namespace q4nx {
+
+template <int KIND, int M>
+__global__ __launch_bounds__(256) void k_gemv_q4(const GemvBatch b) {
+  constexpr int CB = ChunkBytes<KIND>::value;
+  __shared__ float red[4][32][M];
+  const GemvJob& J = b.job[find_job(b, blockIdx.x)];
+  const int ks = J.ks, rpw = 4 / ks;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int slot = wave / ks, part = wave % ks;
+  const int tr0 = (blockIdx.x - J.wg_begin) * rpw;
+  const int tr = tr0 + slot;
+  const int g = lane & 7;
+
+  float acc[4][M];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[i][m] = 0.f;
+
+  if (tr < J.TR) {
+    const int c0 = part * J.TC / ks, c1 = (part + 1) * J.TC / ks;
+    const uint16_t* xrow[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) xrow[m] = J.x + (size_t)m * J.ldx;
+    q4_row_partial<KIND, M>(J.w + (size_t)tr * J.TC * CB, c0, c1, xrow, lane, acc);
+  }
+
+  q4_lane_reduce<M>(acc);
+  if (g == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int m = 0; m < M; ++m) red[wave][8 * i + (lane >> 3)][m] = acc[i][m];
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < rpw * 32 * M; idx += 256) {
+    const int s = idx / (32 * M), rem = idx - s * 32 * M;
+    const int r = rem / M, m = rem - r * M;
+    const int t = tr0 + s;
+    if (t < J.TR) {
+      float v = 0.f;
+      for (int p = 0; p < ks; ++p) v += red[s * ks + p][r][m];
+      J.y[(size_t)m * J.ldy + 32 * t + r] = v;
+    }
+  }
+}
+
+// ===========================================================================
+// Q8 (both code layouts)
+// ===========================================================================
+// A 16-byte piece of Q8 codes is 16 rows of one column in either layout.
+// Lane l = 8g + 4h + j takes, in every chunk, the 8 pieces of group g, row half
+// h (rows 16h .. 16h+15), columns k = 32g + 8j + i (i = 0..7):
+//   layout A (byte k*32 + r):  1024 g + 256 j + 32 i + 16 h
+//   layout B ((r/16)*4096 + (k/32)*512 + (k%32)*16 + r%16):  4096 h + 512 g + 128 j + 16 i
+// It forms part[rho] = sum_i code(16h+rho, k) * x[k] for its 8 columns, then
+// adds d(16h+rho, g) * part[rho]; the 32 lanes of one row half meet at the end.
+// Every product of an int8 code and a bf16 is exact in fp32.
+
+template <int KIND>
+__device__ __forceinline__ int q8_piece(int lane, int i) {
+  const int j = lane & 3, h = (lane >> 2) & 1, g = lane >> 3;
+  if constexpr (KIND == KIND_Q8_A) return 1024 * g + 256 * j + 32 * i + 16 * h;
+  else return 4096 * h + 512 * g + 128 * j + 16 * i;
+}
+
+template <int KIND, int M>
+__global__ __launch_bounds__(256) void k_gemv_q8(const GemvBatch b) {
+  constexpr int CB = 8704;
+  __shared__ float red[4][32][M];
+  const GemvJob& J = b.job[find_job(b, blockIdx.x)];
+  const int ks = J.ks, rpw = 4 / ks;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int slot = wave / ks, part_id = wave % ks;
+  const int tr0 = (blockIdx.x - J.wg_begin) * rpw;
+  const int tr = tr0 + slot;
+  const int j = lane & 3, h = (lane >> 2) & 1, g = lane >> 3;
+
+  float acc[16][M];
+#pragma unroll
+  for (int r = 0; r < 16; ++r)
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[r][m] = 0.f;
+
+  if (tr < J.TR) {
+    const int c0 = part_id * J.TC / ks, c1 = (part_id + 1) * J.TC / ks;
+    const uint8_t* row = J.w + (size_t)tr * J.TC * CB;
+    const int dbase = 8192 + 256 * h + 2 * g;   // d(16h + rho, g) at dbase + 16*rho
+    for (int c = c0; c < c1; ++c) {
+      const uint8_t* ck = row + (size_t)c * CB;
+      u32x4 pc[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pc[i] = load_nt16(ck + q8_piece<KIND>(lane, i));
+      float xf[M][8];
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        const u32x4 v = load16(J.x + (size_t)m * J.ldx + 256 * c + 32 * g + 8 * j);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          xf[m][2 * t] = bf16lo(v[t]);
+          xf[m][2 * t + 1] = bf16hi(v[t]);
+        }
+      }
+      uint32_t dv[8];
+#pragma unroll
+      for (int rr = 0; rr < 8; ++rr) {
+        const uint32_t lo = *reinterpret_cast<const uint16_t*>(ck + dbase + 32 * rr);
+        const uint32_t hi = *reinterpret_cast<const uint16_t*>(ck + dbase + 32 * rr + 16);
+        dv[rr] = lo | (hi << 16);
+      }
+      float part[16][M];
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+#pragma unroll
+        for (int m = 0; m < M; ++m) part[r][m] = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float cf = (float)(int8_t)(pc[i][r >> 2] >> (8 * (r & 3)));
+#pragma unroll
+          for (int m = 0; m < M; ++m) part[r][m] = fmaf(cf, xf[m][i], part[r][m]);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float d = (r & 1) ? bf16hi(dv[r >> 1]) : bf16lo(dv[r >> 1]);
+#pragma unroll
+        for (int m = 0; m < M; ++m) acc[r][m] = fmaf(d, part[r][m], acc[r][m]);
+      }
+    }
+  }
+
+#pragma unroll
+  for (int r = 0; r < 16; ++r)
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      float v = acc[r][m];
+      v += __shfl_xor(v, 1);
+      v += __shfl_xor(v, 2);
+      v += __shfl_xor(v, 8);
+      v += __shfl_xor(v, 16);
+      v += __shfl_xor(v, 32);
+      acc[r][m] = v;
+    }
+  if ((lane & ~4) == 0) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+#pragma unroll
+      for (int m = 0; m < M; ++m) red[wave][16 * h + r][m] = acc[r][m];
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < rpw * 32 * M; idx += 256) {
+    const int s = idx / (32 * M), rem = idx - s * 32 * M;
+    const int r = rem / M, m = rem - r * M;
+    const int t = tr0 + s;
+    if (t < J.TR) {
+      float v = 0.f;
+      for (int p = 0; p < ks; ++p) v += red[s * ks + p][r][m];
+      J.y[(size_t)m * J.ldy + 32 * t + r] = v;
+    }
+  }
+}
+
+// ===========================================================================
+// launcher
+// ===========================================================================
+template <int KIND, int M>
+static hipError_t launch_one(const GemvBatch& b, int n_wg, hipStream_t s) {
+  if constexpr (KIND == KIND_Q4_1 || KIND == KIND_Q4_K)
+    hipLaunchKernelGGL((k_gemv_q4<KIND, M>), dim3(n_wg), dim3(256), 0, s, b);
+  else
+    hipLaunchKernelGGL((k_gemv_q8<KIND, M>), dim3(n_wg), dim3(256), 0, s, b);
+  return hipGetLastError();
+}
+
+template <int KIND>
+static hipError_t launch_m(int M, const GemvBatch& b, int n_wg, hipStream_t s) {
+  switch (M) {
+    case 1: return launch_one<KIND, 1>(b, n_wg, s);
+    case 2: return launch_one<KIND, 2>(b, n_wg, s);
+    case 3: return launch_one<KIND, 3>(b, n_wg, s);
+    case 4: return launch_one<KIND, 4>(b, n_wg, s);
+    case 5: return launch_one<KIND, 5>(b, n_wg, s);
+    case 6: return launch_one<KIND, 6>(b, n_wg, s);
+    case 7: return launch_one<KIND, 7>(b, n_wg, s);
+    case 8: return launch_one<KIND, 8>(b, n_wg, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemv(int kind, int M, const GemvBatch& b, int n_wg, hipStream_t s) {
+  switch (kind) {
+    case KIND_Q4_1: return launch_m<KIND_Q4_1>(M, b, n_wg, s);
+    case KIND_Q4_K: return launch_m<KIND_Q4_K>(M, b, n_wg, s);
+    case KIND_Q8_A: return launch_m<KIND_Q8_A>(M, b, n_wg, s);
+    case KIND_Q8_B: return launch_m<KIND_Q8_B>(M, b, n_wg, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace q4nx

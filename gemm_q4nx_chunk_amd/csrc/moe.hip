@@ -1,0 +1,341 @@
+// Routed-expert MoE layer on Q4NX weights (gfx950).
+//
+// Shape and order of the layer (Strata article, section 2 "target model"):
+// 512 routed experts per layer, the router's top 10 per token, a shared expert
+// used by every token, then the sum.  The selected experts' chunks are read in
+// place from one arena per projection, by expert id (onw technical notes,
+// "MoE on the NPU": bind only the selected experts, never copy the table), and
+// the (token, slot) pairs are grouped by expert so that each selected expert
+// is read once for all the tokens that chose it (onw technical notes,
+// "computing MoE prompts together").
+//
+// Four kernels on one stream:
+//   route   one workgroup: stable sort of the pairs by (expert, token, slot);
+//           per-expert segments; batch counts.  Ids outside [0, n_experts) go
+//           to the end, are never dereferenced, and set bit 0 of the error word.
+//   gateup  per (token batch, tile row): gate and up rows of the expert for up
+//           to TB tokens, h = silu(g) * u, rounded to bf16.
+//   down    per (token batch, group of tile rows): d = Down h, fp32.
+//   combine y[t] = sum_j p[t][j] d[t][j] in slot order, then + the shared d.
+// No floating-point atomics anywhere; every sum has a fixed order.
+#include "q4_core.h"
+#include "moe_args.h"
+
+namespace q4nx {
+
+// ---------------------------------------------------------------------------
+// route
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void k_moe_route(MoeArgs a) {
+  __shared__ uint32_t key[kMoeMaxPairs];
+  __shared__ int32_t scan[1024];
+  __shared__ int32_t nbad;
+  const int P = a.T * a.k;
+  int NP = 1;
+  while (NP < P) NP <<= 1;
+  const int tid = threadIdx.x;
+  if (tid == 0) nbad = 0;
+  __syncthreads();
+  int bad_local = 0;
+  for (int i = tid; i < NP; i += 1024) {
+    uint32_t kv = 0xFFFFFFFFu;
+    if (i < P) {
+      const int e = a.ids[i];
+      const bool ok = e >= 0 && e < a.n_experts;
+      bad_local |= !ok;
+      kv = ((uint32_t)(ok ? e : a.n_experts) << 12) | (uint32_t)i;
+    }
+    key[i] = kv;
+  }
+  if (bad_local) atomicOr(&nbad, 1);
+  // bitonic sort, ascending
+  for (int size = 2; size <= NP; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      __syncthreads();
+      for (int i = tid; i < NP; i += 1024) {
+        const int jx = i ^ stride;
+        if (jx > i) {
+          const uint32_t ki = key[i], kj = key[jx];
+          const bool up = (i & size) == 0;
+          if ((ki > kj) == up) { key[i] = kj; key[jx] = ki; }
+        }
+      }
+    }
+  }
+  __syncthreads();
+  // segment starts among valid pairs, scanned in chunks of 1024
+  int base_seg = 0, base_batch = 0;
+  for (int c0 = 0; c0 < P; c0 += 1024) {
+    const int s = c0 + tid;
+    int start = 0, cnt = 0, e = -1;
+    if (s < P) {
+      e = (int)(key[s] >> 12);
+      if (e < a.n_experts && (s == 0 || (int)(key[s - 1] >> 12) != e)) {
+        start = 1;
+        int end = s + 1;
+        while (end < P && (int)(key[end] >> 12) == e) ++end;
+        cnt = end - s;
+      }
+      a.sorted[s] = (int32_t)(key[s] & 0xFFFu);
+    }
+    // inclusive scans of start flags and of batch counts, packed in one int
+    const int nb = start ? (cnt + a.tb - 1) / a.tb : 0;
+    scan[tid] = (start << 20) | nb;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+      const int v = tid >= off ? scan[tid - off] : 0;
+      __syncthreads();
+      scan[tid] += v;
+      __syncthreads();
+    }
+    if (start) {
+      const int u = base_seg + (scan[tid] >> 20) - 1;
+      const int bstart = base_batch + (scan[tid] & 0xFFFFF) - nb;
+      a.seg[3 * u + 0] = e;
+      a.seg[3 * u + 1] = s;
+      a.seg[3 * u + 2] = cnt;
+      a.batch0[u] = bstart;
+    }
+    base_seg += scan[1023] >> 20;
+    base_batch += scan[1023] & 0xFFFFF;
+    __syncthreads();
+  }
+  if (tid == 0) {
+    a.hdr[0] = nbad ? 1u : 0u;        // error word
+    a.hdr[1] = (uint32_t)base_seg;    // segments
+    a.hdr[2] = (uint32_t)base_batch;  // routed token batches
+    a.batch0[base_seg] = base_batch;
+  }
+}
+
+// Segment of routed batch b: the last u with batch0[u] <= b.
+__device__ __forceinline__ int find_seg(const int32_t* batch0, int nseg, int b) {
+  int lo = 0, hi = nseg - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (batch0[mid] <= b) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Work item of a (batch, tile-row group) launch: which expert, which tokens.
+struct MoeItem {
+  const uint8_t* w0;    // gate (gateup) or down (down) chunks of the expert
+  const uint8_t* w1;    // up chunks (gateup only)
+  int tr;               // first tile row
+  int ntok;             // tokens in this batch (1..TB)
+  int pos0;             // first sorted position (routed) or P + first token (shared)
+  bool shared;
+};
+
+// Items are numbered routed first (every routed batch times its tile-row
+// groups), then shared.  rpw = tile rows per workgroup for each kind of item.
+template <int TB>
+__device__ __forceinline__ bool moe_item(const MoeArgs& a, int item, int rows_r, int rows_s,
+                                         int rpw_r, int rpw_s, bool down, MoeItem& it) {
+  const int nseg = (int)a.hdr[1], nbr = (int)a.hdr[2];
+  const int P = a.T * a.k;
+  const int gr = rows_r / rpw_r, gs = rows_s / rpw_s;
+  if (item < nbr * gr) {
+    const int b = item / gr;
+    const int u = find_seg(a.batch0, nseg, b);
+    const int e = a.seg[3 * u + 0], start = a.seg[3 * u + 1], cnt = a.seg[3 * u + 2];
+    const int bi = b - a.batch0[u];
+    it.tr = (item - b * gr) * rpw_r;
+    it.pos0 = start + bi * TB;
+    it.ntok = min(TB, cnt - bi * TB);
+    it.shared = false;
+    if (down) {
+      it.w0 = a.down + (size_t)e * a.down_stride;
+      it.w1 = nullptr;
+    } else {
+      it.w0 = a.gate + (size_t)e * a.gate_stride;
+      it.w1 = a.up + (size_t)e * a.up_stride;
+    }
+    return true;
+  }
+  item -= nbr * gr;
+  const int nbs = a.Ds ? (a.T + TB - 1) / TB : 0;
+  if (item < nbs * gs) {
+    const int b = item / gs;
+    it.tr = (item - b * gs) * rpw_s;
+    it.pos0 = P + b * TB;
+    it.ntok = min(TB, a.T - b * TB);
+    it.shared = true;
+    it.w0 = down ? a.sdown : a.sgate;
+    it.w1 = down ? nullptr : a.sup;
+    return true;
+  }
+  return false;
+}
+
+// ---------------------------------------------------------------------------
+// gate / up / SwiGLU
+// ---------------------------------------------------------------------------
+// Waves 0-1 run the gate tile row, waves 2-3 the up tile row, each pair
+// splitting the D/256 chunks in two halves.
+template <int KIND, int TB>
+__global__ __launch_bounds__(256) void k_moe_gateup(MoeArgs a) {
+  constexpr int CB = ChunkBytes<KIND>::value;
+  __shared__ float red[4][32][TB];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int TC = a.D / 256;
+  const int rows_r = a.De / 32, rows_s = a.Ds / 32;
+  const int P = a.T * a.k;
+  for (int item = blockIdx.x;; item += gridDim.x) {
+    MoeItem it;
+    if (!moe_item<TB>(a, item, rows_r, rows_s, 1, 1, false, it)) break;
+    const uint16_t* xrow[TB];
+#pragma unroll
+    for (int m = 0; m < TB; ++m) {
+      const int mm = m < it.ntok ? m : 0;
+      const int t = it.shared ? it.pos0 - P + mm : a.sorted[it.pos0 + mm] / a.k;
+      xrow[m] = a.X + (size_t)t * a.D;
+    }
+    const uint8_t* w = (wave < 2 ? it.w0 : it.w1) + (size_t)it.tr * TC * CB;
+    const int half = wave & 1;
+    float acc[4][TB];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int m = 0; m < TB; ++m) acc[i][m] = 0.f;
+    q4_row_partial<KIND, TB>(w, half * TC / 2, (half + 1) * TC / 2, xrow, lane, acc);
+    q4_lane_reduce<TB>(acc);
+    if ((lane & 7) == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int m = 0; m < TB; ++m) red[wave][8 * i + (lane >> 3)][m] = acc[i][m];
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < 32 * TB; idx += 256) {
+      const int r = idx / TB, m = idx - r * TB;
+      if (m < it.ntok) {
+        const float g = red[0][r][m] + red[1][r][m];
+        const float u = red[2][r][m] + red[3][r][m];
+        const float hv = g / (1.0f + expf(-g)) * u;
+        const uint16_t hb = __builtin_bit_cast(uint16_t, (__bf16)hv);
+        const int col = 32 * it.tr + r;
+        a.hbuf[(size_t)(it.pos0 + m) * a.hstride + col] = hb;
+        if (it.shared) {
+          if (a.dbg_h_shared) a.dbg_h_shared[(size_t)(it.pos0 - P + m) * a.Ds + col] = hb;
+        } else if (a.dbg_h) {
+          a.dbg_h[(size_t)a.sorted[it.pos0 + m] * a.De + col] = hb;
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// down
+// ---------------------------------------------------------------------------
+// ks waves split one tile row's chunks; 4/ks tile rows per workgroup.
+template <int KIND, int TB>
+__global__ __launch_bounds__(256) void k_moe_down(MoeArgs a, int ks_r, int ks_s) {
+  constexpr int CB = ChunkBytes<KIND>::value;
+  __shared__ float red[4][32][TB];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int rows = a.D / 32;
+  const int P = a.T * a.k;
+  for (int item = blockIdx.x;; item += gridDim.x) {
+    MoeItem it;
+    if (!moe_item<TB>(a, item, rows, rows, 4 / ks_r, 4 / ks_s, true, it)) break;
+    const int ks = it.shared ? ks_s : ks_r, rpw = 4 / ks;
+    const int TC = (it.shared ? a.Ds : a.De) / 256;
+    const int slot = wave / ks, part = wave % ks;
+    const int tr = it.tr + slot;
+    const uint16_t* xrow[TB];
+#pragma unroll
+    for (int m = 0; m < TB; ++m) {
+      const int mm = m < it.ntok ? m : 0;
+      xrow[m] = a.hbuf + (size_t)(it.pos0 + mm) * a.hstride;
+    }
+    float acc[4][TB];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int m = 0; m < TB; ++m) acc[i][m] = 0.f;
+    if (tr < rows)
+      q4_row_partial<KIND, TB>(it.w0 + (size_t)tr * TC * CB, part * TC / ks, (part + 1) * TC / ks,
+                               xrow, lane, acc);
+    q4_lane_reduce<TB>(acc);
+    if ((lane & 7) == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int m = 0; m < TB; ++m) red[wave][8 * i + (lane >> 3)][m] = acc[i][m];
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < rpw * 32 * TB; idx += 256) {
+      const int s = idx / (32 * TB), rem = idx - s * 32 * TB;
+      const int r = rem / TB, m = rem - r * TB;
+      const int t_row = it.tr + s;
+      if (m < it.ntok && t_row < rows) {
+        float v = 0.f;
+        for (int p = 0; p < ks; ++p) v += red[s * ks + p][r][m];
+        const int dst = it.shared ? it.pos0 + m : a.sorted[it.pos0 + m];
+        a.dbuf[(size_t)dst * a.D + 32 * t_row + r] = v;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// combine
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_moe_combine(MoeArgs a) {
+  const int t = blockIdx.y;
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  if (n >= a.D) return;
+  const int P = a.T * a.k;
+  float y = 0.f;
+  for (int j = 0; j < a.k; ++j) {
+    const int pair = t * a.k + j;
+    const int e = a.ids[pair];
+    const bool ok = e >= 0 && e < a.n_experts;
+    const float d = ok ? a.dbuf[(size_t)pair * a.D + n] : 0.f;
+    if (ok) y = fmaf(a.p[pair], d, y);
+    if (a.dbg_d) a.dbg_d[(size_t)pair * a.D + n] = d;
+  }
+  if (a.Ds) {
+    const float ds = a.dbuf[(size_t)(P + t) * a.D + n];
+    y += ds;
+    if (a.dbg_d_shared) a.dbg_d_shared[(size_t)t * a.D + n] = ds;
+  }
+  a.Y[(size_t)t * a.D + n] = y;
+}
+
+// ---------------------------------------------------------------------------
+// host launcher
+// ---------------------------------------------------------------------------
+template <int KIND, int TB>
+static hipError_t moe_run(const MoeArgs& a, hipStream_t s) {
+  const int P = a.T * a.k;
+  const int nseg_max = P < a.n_experts ? P : a.n_experts;
+  const int nb_r = (P + nseg_max * (TB - 1)) / TB;        // bound on routed batches
+  const int nb_s = a.Ds ? (a.T + TB - 1) / TB : 0;
+  hipLaunchKernelGGL(k_moe_route, dim3(1), dim3(1024), 0, s, a);
+  const int gu_items = nb_r * (a.De / 32) + nb_s * (a.Ds / 32);
+  hipLaunchKernelGGL((k_moe_gateup<KIND, TB>), dim3(gu_items < 4096 ? gu_items : 4096), dim3(256),
+                     0, s, a);
+  const int tcr = a.De / 256, tcs = a.Ds ? a.Ds / 256 : 1;
+  const int ks_r = tcr >= 4 ? 4 : (tcr >= 2 ? 2 : 1);
+  const int ks_s = tcs >= 4 ? 4 : (tcs >= 2 ? 2 : 1);
+  const int rows = a.D / 32;
+  const int dn_items = nb_r * (rows / (4 / ks_r)) + nb_s * (rows / (4 / ks_s));
+  hipLaunchKernelGGL((k_moe_down<KIND, TB>), dim3(dn_items < 4096 ? dn_items : 4096), dim3(256),
+                     0, s, a, ks_r, ks_s);
+  hipLaunchKernelGGL(k_moe_combine, dim3((a.D + 255) / 256, a.T), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_moe(int kind, const MoeArgs& a, hipStream_t s) {
+  if (kind == KIND_Q4_1) return a.tb == 1 ? moe_run<KIND_Q4_1, 1>(a, s) : moe_run<KIND_Q4_1, 4>(a, s);
+  if (kind == KIND_Q4_K) return a.tb == 1 ? moe_run<KIND_Q4_K, 1>(a, s) : moe_run<KIND_Q4_K, 4>(a, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace q4nx

@@ -1,0 +1,66 @@
+// Device-side arguments of the MoE kernels (one struct, passed by value).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q4nx {
+
+constexpr int kMoeMaxPairs = 4096;   // T * k per call (the route kernel sorts them in LDS)
+
+struct MoeArgs {
+  // routed experts: expert e's chunks at base + e * stride
+  const uint8_t* gate;
+  const uint8_t* up;
+  const uint8_t* down;
+  int64_t gate_stride, up_stride, down_stride;
+  // shared expert (Ds == 0: none)
+  const uint8_t* sgate;
+  const uint8_t* sup;
+  const uint8_t* sdown;
+  int32_t n_experts, D, De, Ds;
+  // inputs / outputs
+  const uint16_t* X;
+  const int32_t* ids;
+  const float* p;
+  float* Y;
+  int32_t T, k;
+  int32_t tb;        // tokens per work item (1 or 4)
+  int32_t hstride;   // row stride of hbuf, max(De, Ds)
+  // optional stage outputs
+  uint16_t* dbg_h;
+  float* dbg_d;
+  uint16_t* dbg_h_shared;
+  float* dbg_d_shared;
+  // workspace
+  uint32_t* hdr;     // [0] error word, [1] segments, [2] routed batches
+  int32_t* sorted;   // [P] pair index at each sorted position
+  int32_t* seg;      // [P][3] (expert, first sorted position, count)
+  int32_t* batch0;   // [P + 1] first routed batch of each segment
+  uint16_t* hbuf;    // [P + T][hstride] bf16 h (routed by sorted position, shared at P + t)
+  float* dbuf;       // [P + T][D] fp32 d (routed by pair index, shared at P + t)
+};
+
+// Workspace layout for P pairs and T tokens; returns the total bytes and fills
+// the offsets (each 256-byte aligned).
+struct MoeWsLayout {
+  size_t hdr, sorted, seg, batch0, hbuf, dbuf, total;
+};
+
+inline MoeWsLayout moe_ws_layout(int P, int T, int D, int hstride) {
+  auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
+  MoeWsLayout l;
+  size_t o = 0;
+  l.hdr = o;    o = up(o + 256);
+  l.sorted = o; o = up(o + (size_t)P * 4);
+  l.seg = o;    o = up(o + (size_t)P * 12);
+  l.batch0 = o; o = up(o + (size_t)(P + 1) * 4);
+  l.hbuf = o;   o = up(o + (size_t)(P + T) * hstride * 2);
+  l.dbuf = o;   o = up(o + (size_t)(P + T) * D * 4);
+  l.total = o;
+  return l;
+}
+
+hipError_t launch_moe(int kind, const MoeArgs& a, hipStream_t s);
+
+}  // namespace q4nx

@@ -1,0 +1,152 @@
+// The q4_1 / Q4_K dequant-GEMV core shared by the GEMV and MoE kernels.
+#pragma once
+
+#include "q4nx_dev.h"
+
+namespace q4nx {
+
+// ===========================================================================
+// q4_1 and Q4_K
+// ===========================================================================
+// Lane l reads, in slice i = 0..3 of a chunk, the 16 bytes at 1024*i + 16*l:
+// the 32 codes of tile row r = 8i + l/8 in group g = l%8.  Every slice of every
+// chunk gives lane l the same group g, so the lane's 32 activations of a tile
+// column are loaded once per chunk.
+//
+// Unpack: the bf16 with bits 0x4300 | c is exactly 128 + c for a 4-bit c, so
+// (w >> 4j) & 0x000F000F | 0x43004300 makes nibbles j and j+4 of a 32-bit code
+// word into a bf16 pair, which v_dot2_f32_bf16 multiplies with the pair
+// (x[k], x[k+4]).  The same dot chain run with 136 (= 128 + 8) in place of each
+// code is subtracted, so with s the scale, z the zero of the 32-column group:
+//     sum_k (c s + z) x = s * (D - D136) + (z + 8 s) * sum_k x
+// where D - D136 = sum (c - 8) x, bit-exactly 0 when every code is 8 (the
+// identical operand bits give identical chain results).  For Q4_K, s = S*scale
+// and z = M*min (both products exact in fp32).
+
+template <int KIND>
+struct Q4Chunk {
+  u32x4 q[4];
+  uint32_t meta[4];   // q4_1: (scale, zero) bf16 pair;  Q4_K: (sc | mn << 8)
+  uint32_t rowsm[4];  // Q4_K: (S, M) bf16 pair of the lane's row
+};
+
+template <int KIND>
+__device__ __forceinline__ void q4_load(const uint8_t* __restrict__ ck, int lane, Q4Chunk<KIND>& c) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) c.q[i] = load_nt16(ck + 1024 * i + 16 * lane);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (KIND == KIND_Q4_1) {
+      c.meta[i] = *reinterpret_cast<const uint32_t*>(ck + 4096 + 256 * i + 4 * lane);
+      c.rowsm[i] = 0;
+    } else {
+      c.meta[i] = *reinterpret_cast<const uint16_t*>(ck + 4096 + 128 * i + 2 * lane);
+      c.rowsm[i] = *reinterpret_cast<const uint32_t*>(ck + 4608 + 32 * i + 4 * (lane >> 3));
+    }
+  }
+}
+
+// Activation pairs (x[k], x[k+4]) of the lane's group for one tile column, in
+// the order the code chain uses them, the 136-chain, and sum x taken as that
+// chain / 136 (a few fp32 roundings; it is only ever multiplied by z + 8s, and
+// it is exact when a single x of the group is nonzero).
+template <int M>
+struct XPrep {
+  uint32_t p[M][16];
+  float sum[M];
+  float d136[M];
+};
+
+template <int M>
+__device__ __forceinline__ void x_prep(const uint16_t* const (&xrow)[M], int col, XPrep<M>& xp) {
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const uint16_t* xc = xrow[m] + col;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const u32x4 v = load16(xc + 8 * d);   // x[8d .. 8d+7] of the group, bf16 pairs
+      // v_perm_b32 byte select: 0..3 pick bytes of the second operand, 4..7 of the first.
+      xp.p[m][4 * d + 0] = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);   // (x0, x4)
+      xp.p[m][4 * d + 1] = __builtin_amdgcn_perm(v.z, v.x, 0x07060302u);   // (x1, x5)
+      xp.p[m][4 * d + 2] = __builtin_amdgcn_perm(v.w, v.y, 0x05040100u);   // (x2, x6)
+      xp.p[m][4 * d + 3] = __builtin_amdgcn_perm(v.w, v.y, 0x07060302u);   // (x3, x7)
+    }
+    float e = 0.f;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) e = dot2bf16(0x43084308u, xp.p[m][t], e);   // (136, 136)
+    xp.d136[m] = e;
+    xp.sum[m] = e / 136.0f;
+  }
+}
+
+template <int KIND, int M>
+__device__ __forceinline__ void q4_compute(const Q4Chunk<KIND>& c, const XPrep<M>& xp,
+                                           uint32_t kMask, uint32_t kMagic, float (&acc)[4][M]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float s, zz;
+    if constexpr (KIND == KIND_Q4_1) {
+      s = bf16lo(c.meta[i]);
+      zz = fmaf(8.f, s, bf16hi(c.meta[i]));
+    } else {
+      const float S = bf16lo(c.rowsm[i]), Mn = bf16hi(c.rowsm[i]);
+      s = S * (float)(c.meta[i] & 0xFFu);
+      zz = fmaf(8.f, s, Mn * (float)((c.meta[i] >> 8) & 0xFFu));
+    }
+    uint32_t cp[16];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t w = c.q[i][d];
+      cp[4 * d + 0] = (w & kMask) | kMagic;
+      cp[4 * d + 1] = ((w >> 4) & kMask) | kMagic;
+      cp[4 * d + 2] = ((w >> 8) & kMask) | kMagic;
+      cp[4 * d + 3] = ((w >> 12) & kMask) | kMagic;
+    }
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      float D = 0.f;
+#pragma unroll
+      for (int t = 0; t < 16; ++t) D = dot2bf16(cp[t], xp.p[m][t], D);
+      acc[i][m] = fmaf(s, D - xp.d136[m], fmaf(zz, xp.sum[m], acc[i][m]));
+    }
+  }
+}
+
+// Partial sums of one tile row over chunks [c0, c1) for M activation rows.
+// acc[i][m] of lane l belongs to row 8i + l/8, group l%8 (sum over the groups
+// with q4_lane_reduce).  xrow[m] points at activation row m, column 0.
+template <int KIND, int M>
+__device__ __forceinline__ void q4_row_partial(const uint8_t* __restrict__ row, int c0, int c1,
+                                               const uint16_t* const (&xrow_in)[M], int lane,
+                                               float (&acc)[4][M]) {
+  constexpr int CB = ChunkBytes<KIND>::value;
+  const int g = lane & 7;
+  const uint16_t* xrow[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) xrow[m] = xrow_in[m] + 32 * g;
+  // Register operands let the unpack use one v_and_or_b32 (gfx9 VOP3 takes no literal).
+  uint32_t kMask = 0x000F000Fu, kMagic = 0x43004300u;
+  asm volatile("" : "+s"(kMask));
+  asm volatile("" : "+v"(kMagic));
+  Q4Chunk<KIND> cur, nxt;
+  if (c0 < c1) q4_load<KIND>(row + (size_t)c0 * CB, lane, cur);
+  for (int c = c0; c < c1; ++c) {
+    if (c + 1 < c1) q4_load<KIND>(row + (size_t)(c + 1) * CB, lane, nxt);
+    XPrep<M> xp;
+    x_prep<M>(xrow, 256 * c, xp);
+    q4_compute<KIND, M>(cur, xp, kMask, kMagic, acc);
+    cur = nxt;
+  }
+}
+
+// Sum a lane's partials over the 8 groups; afterwards every lane of the 8
+// holds the row sum of rows 8i + lane/8.
+template <int M>
+__device__ __forceinline__ void q4_lane_reduce(float (&acc)[4][M]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[i][m] = sum_lanes_xor7(acc[i][m]);
+}
+
+}  // namespace q4nx

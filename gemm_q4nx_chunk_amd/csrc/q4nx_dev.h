@@ -1,0 +1,97 @@
+// Internal device/host definitions shared by the HIP sources of libq4nx.so.
+//
+// Chunk facts used by the kernels (1bit engine docs, page "NPU engine",
+// section "Q4NX chunks"): 32 x 256 tiles, one chunk per tile, row-major over
+// the grid; q4_1 5120 B (w = code*scale + zero), Q4_K 4736 B
+// (w = S*scale*code + M*min), Q8 8704 B (w = d*code) with the two printed code
+// layouts.  In-chunk positions not printed there follow the library's layout
+// (see include/q4nx.h): 4-bit codes at byte r*128 + k/2 (even k low nibble),
+// q4_1 (scale, zero) at 4096 + 4*(8r+g), Q4_K (sc, mn) at 4096 + 2*(8r+g) and
+// (S, M) at 4608 + 4r, Q8 d at 8192 + 2*(8r+g).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q4nx {
+
+enum Kind : int { KIND_Q4_1 = 0, KIND_Q4_K = 1, KIND_Q8_A = 2, KIND_Q8_B = 3 };
+
+template <int KIND>
+struct ChunkBytes;
+template <> struct ChunkBytes<KIND_Q4_1> { static constexpr int value = 5120; };
+template <> struct ChunkBytes<KIND_Q4_K> { static constexpr int value = 4736; };
+template <> struct ChunkBytes<KIND_Q8_A> { static constexpr int value = 8704; };
+template <> struct ChunkBytes<KIND_Q8_B> { static constexpr int value = 8704; };
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// One GEMV of a batched launch.  Workgroup wg of the launch belongs to the last
+// job whose wg_begin <= wg.  ks = waves that split one tile row's chunks
+// (1, 2 or 4); a 4-wave workgroup covers 4/ks tile rows.
+struct GemvJob {
+  const uint8_t* w;
+  const uint16_t* x;
+  float* y;
+  int32_t TR, TC;
+  int32_t ldx, ldy;   // row strides of x and y, in elements
+  int32_t wg_begin;
+  int32_t ks;
+};
+
+constexpr int kMaxBatch = 64;
+
+struct GemvBatch {
+  GemvJob job[kMaxBatch];
+  int32_t n_jobs;
+};
+
+// ---------------------------------------------------------------------------
+// small device helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__device__ __forceinline__ u32x4 load_nt16(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ u32x4 load16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+__device__ __forceinline__ float dot2bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                         __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+// Sum over the 8 lanes that differ in bits 0..2 of the lane id; fixed order,
+// so every lane of the group ends with the same bits.
+__device__ __forceinline__ float sum_lanes_xor7(float v) {
+  v += __shfl_xor(v, 1);
+  v += __shfl_xor(v, 2);
+  v += __shfl_xor(v, 4);
+  return v;
+}
+
+// Pick the job of workgroup `wg`: the last one whose wg_begin <= wg.
+__device__ __forceinline__ int find_job(const GemvBatch& b, int wg) {
+  int j = 0;
+  for (int t = 1; t < b.n_jobs; ++t)
+    if (wg >= b.job[t].wg_begin) j = t;
+  return j;
+}
+
+// Host-side launchers (gemv.hip, gemm.hip, decode.hip, moe.hip).
+hipError_t launch_gemv(int kind, int M, const GemvBatch& b, int n_wg, hipStream_t s);
+hipError_t launch_gemm(int kind, const uint8_t* w, const uint16_t* X, float* Y, int TR, int TC,
+                       int M, hipStream_t s);
+hipError_t launch_unpack(int kind, const uint8_t* w, int TR, int TC, uint8_t* codes,
+                         uint16_t* meta0, uint16_t* meta1, uint16_t* row_meta, hipStream_t s);
+hipError_t launch_decode(int kind, const uint8_t* w, int TR, int TC, float* out, hipStream_t s);
+
+}  // namespace q4nx

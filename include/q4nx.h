@@ -1,0 +1,241 @@
+/*
+ * q4nx.h -- C ABI of libq4nx.so: fused dequantize-and-multiply of Q4NX-tiled
+ * low-bit weights against bf16 activations on AMD MI355X (gfx950).
+ *
+ * The weight format is the Q4NX chunk grid of the 1bit engine docs, page
+ * "NPU engine", section "Q4NX chunks": a weight of `rows` outputs by `cols`
+ * inputs is a grid of 32-row x 256-column tiles, one chunk per tile, row-major
+ * over the grid (tile (tr, tc) is chunk tr*(cols/256) + tc), and the chunk size
+ * names the kind:
+ *
+ *   5120 B  q4_1  weight = code * scale + zero    bf16 scale, zero per 32 columns of a row
+ *   4736 B  Q4_K  weight = S * scale * code + M * min
+ *                                                 u8 scale, min per 32 columns; bf16 S, M per row
+ *   8704 B  Q8    weight = d * code               int8 codes; bf16 d per 32 columns
+ *
+ * Q8 has two code layouts under the one size, and nothing in a tensor tells
+ * them apart (same section), so a Q8 weight must name its layout:
+ *   Q4NX_Q8_LAYOUT_A: code (r, k) of a tile at byte k*32 + r
+ *   Q4NX_Q8_LAYOUT_B: at (r/16)*4096 + (k/32)*512 + (k%32)*16 + r%16
+ *
+ * The byte order inside q4_1 and Q4_K chunks, and the place of the Q8 scales,
+ * are deferred by that section to a header that is not published.  This
+ * library reads them as follows (r = row in the tile 0..31, k = column in the
+ * tile 0..255, g = k/32; all fields little-endian):
+ *   q4_1: code (r, k) in byte r*128 + k/2, even k in the low nibble;
+ *         (scale, zero) bf16 pair of (r, g) at byte 4096 + 4*(8r + g).
+ *   Q4_K: codes as q4_1; (scale, min) u8 pair of (r, g) at 4096 + 2*(8r + g);
+ *         (S, M) bf16 pair of row r at 4608 + 4r.
+ *   Q8:   d bf16 of (r, g) at 8192 + 2*(8r + g).
+ *
+ * Conventions of every call:
+ *  - Pointers marked DEVICE are device memory owned by the caller; the library
+ *    keeps no pointer after a call returns and allocates no memory.
+ *  - Calls that take a stream enqueue work on it and return without waiting;
+ *    the caller synchronises before reading results.  `stream` is a
+ *    hipStream_t passed as void* (NULL = the default stream).
+ *  - Every argument, shape and size is checked on the host before anything is
+ *    enqueued; a failing check returns its status and enqueues nothing.  The
+ *    status of the last failing call on the calling thread is described by
+ *    q4nx_last_error().  No C++ exception crosses this interface.
+ *  - Activations are bf16 bit patterns (uint16_t); products accumulate in
+ *    fp32 and outputs are fp32.  Denormals are kept, never flushed.
+ *  - Results are deterministic: the same inputs give the same bytes on every
+ *    run (no floating-point atomics; every sum has a fixed order).
+ */
+#ifndef Q4NX_H
+#define Q4NX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every call (0 = success). */
+typedef enum q4nx_status {
+  Q4NX_OK = 0,
+  Q4NX_E_ARG = 1,        /* null pointer where one is required, or a count out of range */
+  Q4NX_E_CHUNK_KIND = 2, /* chunk_bytes is not 5120, 4736 or 8704, or the kind is not
+                            supported by the call */
+  Q4NX_E_SHAPE = 3,      /* rows not a positive multiple of 32 or cols of 256, or shapes
+                            that do not fit together */
+  Q4NX_E_SHORT = 4,      /* nbytes smaller than (rows/32)*(cols/256)*chunk_bytes */
+  Q4NX_E_ALIGN = 5,      /* a pointer is not aligned as the call requires */
+  Q4NX_E_WORKSPACE = 6,  /* workspace missing or smaller than the *_ws() size */
+  Q4NX_E_Q8_LAYOUT = 7,  /* a Q8 weight without Q4NX_Q8_LAYOUT_A or _B */
+  Q4NX_E_HIP = 8         /* the HIP runtime refused a launch; see q4nx_last_error() */
+} q4nx_status;
+
+enum { Q4NX_Q4_1_BYTES = 5120, Q4NX_Q4_K_BYTES = 4736, Q4NX_Q8_BYTES = 8704 };
+enum { Q4NX_Q8_LAYOUT_UNSET = -1, Q4NX_Q8_LAYOUT_A = 0, Q4NX_Q8_LAYOUT_B = 1 };
+
+/* Largest M (activation rows) of one q4nx_gemv / q4nx_gemv_batched call. */
+enum { Q4NX_GEMV_MAX_M = 8 };
+/* Largest M of one q4nx_gemm_block call (a prompt block of 64 tokens). */
+enum { Q4NX_GEMM_MAX_M = 64 };
+/* Most jobs one q4nx_gemv_batched call takes. */
+enum { Q4NX_BATCH_MAX_JOBS = 64 };
+
+/* One Q4NX weight, described on the host. */
+typedef struct q4nx_weight {
+  const void* chunks;   /* DEVICE, [rows/32][cols/256][chunk_bytes], 16-byte aligned */
+  int64_t nbytes;       /* bytes available at `chunks`; must cover every chunk */
+  int32_t rows;         /* outputs N, a positive multiple of 32 */
+  int32_t cols;         /* inputs K, a positive multiple of 256 */
+  int32_t chunk_bytes;  /* 5120 (q4_1), 4736 (Q4_K) or 8704 (Q8): the kind */
+  int32_t q8_layout;    /* Q4NX_Q8_LAYOUT_A or _B when chunk_bytes == 8704, else ignored */
+} q4nx_weight;
+
+/*
+ * Host-only check of a weight descriptor: the chunk-kind and length rules of
+ * the NPU engine page ("Q4NX chunks": an unknown chunk size or a tensor
+ * shorter than its layout needs is refused; the Q8 layout cannot be detected,
+ * so it must be given).  Touches no device memory.
+ * Returns Q4NX_OK, E_ARG (w or w->chunks NULL), E_CHUNK_KIND, E_SHAPE, E_SHORT,
+ * E_ALIGN (chunks not 16-byte aligned) or E_Q8_LAYOUT.
+ */
+int q4nx_weight_check(const q4nx_weight* w);
+
+/*
+ * y[m][n] = sum_k W[n][k] * x[m][k] for m < M: the dequantize-and-multiply of
+ * decode (Strata article, section 1: decode speed is set by the weight bytes
+ * read per token; section 4.1: a verify window reads the weights once for
+ * several tokens' mat-vecs).  Each chunk is read from HBM once per call
+ * whatever M is.
+ *   w  host descriptor (checked as q4nx_weight_check)
+ *   x  DEVICE bf16 [M][w->cols], row-major, 16-byte aligned
+ *   y  DEVICE fp32 [M][w->rows], row-major, 4-byte aligned; fully overwritten
+ *   M  1..Q4NX_GEMV_MAX_M
+ * All chunk kinds.  Error |y - y_exact| stays far inside 2e-3 * sum_k |w x| for
+ * the kernels' fp32 arithmetic (bf16 codes/activations exact, fp32 sums).
+ */
+int q4nx_gemv(const q4nx_weight* w, const uint16_t* x, float* y, int M, void* stream);
+
+/* One independent GEMV of a batch. */
+typedef struct q4nx_gemv_job {
+  q4nx_weight w;
+  const uint16_t* x;  /* DEVICE bf16 [M][w.cols] */
+  float* y;           /* DEVICE fp32 [M][w.rows] */
+} q4nx_gemv_job;
+
+/*
+ * Runs n_jobs independent GEMVs (all with the same M) as few launches as the
+ * chunk kinds allow: one per kind present.  Meant for the projections of a
+ * layer that read one input (q|k|v, gate|up) and, generally, for many small
+ * GEMVs whose single launches would be dominated by launch cost.  Jobs must
+ * not write overlapping y.
+ *   jobs    HOST array of n_jobs descriptors (read during the call only)
+ *   n_jobs  1..Q4NX_BATCH_MAX_JOBS
+ * Errors as q4nx_gemv, checked for every job before anything is enqueued.
+ */
+int q4nx_gemv_batched(const q4nx_gemv_job* jobs, int n_jobs, int M, void* stream);
+
+/*
+ * Y[m][n] = sum_k W[n][k] * X[m][k] for a prompt block of M <= 64 rows (onw
+ * technical notes, "dense model prompts in 64-token blocks": group-quantised
+ * matmul throughput levels off at 64 rows).  Each chunk is read once and
+ * dequantised once to bf16 (round to nearest even) for the bf16 matrix cores,
+ * with fp32 accumulation.
+ *   w  host descriptor; q4_1 or Q4_K (E_CHUNK_KIND for Q8)
+ *   X  DEVICE bf16 [M][w->cols], 16-byte aligned
+ *   Y  DEVICE fp32 [M][w->rows]; fully overwritten
+ *   M  1..Q4NX_GEMM_MAX_M
+ * The bf16 rounding of each weight moves it by at most 2^-8 of its size; with
+ * random signs the error of a sum over K stays well inside 2e-3 * sum |w x|.
+ */
+int q4nx_gemm_block(const q4nx_weight* w, const uint16_t* X, float* Y, int M, void* stream);
+
+/*
+ * One routed-expert MoE layer (Strata article, section 2 "target model": per
+ * layer 512 routed experts, the router picks 10, plus a shared expert every
+ * token, then the sum; onw technical notes, "MoE on the NPU": only the
+ * selected experts' weights are bound, by id, without copying the table).
+ *
+ * Routed experts all have the same kind and shape; expert e's gate, up and
+ * down chunks start at gate + e*gate_stride (etc.) of one device arena.
+ */
+typedef struct q4nx_moe_layer {
+  int32_t n_experts;     /* routed experts in the arena, >= 1 */
+  int32_t d_model;       /* model width D: gate/up cols, down rows (mult. of 256) */
+  int32_t d_expert;      /* routed intermediate width: gate/up rows, down cols (mult. of 256) */
+  int32_t d_shared;      /* shared intermediate width (mult. of 256), or 0 for none */
+  int32_t chunk_bytes;   /* kind of every expert weight: 5120 (q4_1) or 4736 (Q4_K) */
+  int32_t reserved;      /* must be 0 */
+  const void* gate;      /* DEVICE, expert e at gate + e*gate_stride, [d_expert/32][D/256] chunks */
+  const void* up;        /* DEVICE, same shape as gate */
+  const void* down;      /* DEVICE, expert e at down + e*down_stride, [D/32][d_expert/256] chunks */
+  int64_t gate_stride, up_stride, down_stride;   /* bytes between experts, 16-byte multiples */
+  int64_t gate_bytes, up_bytes, down_bytes;      /* bytes available in each arena */
+  q4nx_weight sh_gate;   /* shared expert [d_shared][D]; ignored when d_shared == 0 */
+  q4nx_weight sh_up;     /* [d_shared][D] */
+  q4nx_weight sh_down;   /* [D][d_shared] */
+} q4nx_moe_layer;
+
+/* Optional stage outputs of q4nx_moe_experts, for stage-wise checking. */
+typedef struct q4nx_moe_debug {
+  uint16_t* h;          /* DEVICE bf16 [T][k][d_expert]: silu(G x) * (U x), rounded to bf16 */
+  float* d;             /* DEVICE fp32 [T][k][D]: down projection of h, before weighting */
+  uint16_t* h_shared;   /* DEVICE bf16 [T][d_shared] */
+  float* d_shared;      /* DEVICE fp32 [T][D] */
+} q4nx_moe_debug;
+
+/* Workspace bytes q4nx_moe_experts needs for T tokens and k slots. */
+size_t q4nx_moe_ws(const q4nx_moe_layer* L, int T, int k);
+
+/*
+ * Y[t] = sum_{j<k} p[t][j] * Down_e (silu(Gate_e X[t]) * (Up_e X[t])) + (shared expert, weight 1)
+ * with e = ids[t][j].  The (token, slot) pairs are sorted by expert on the
+ * device so that each selected expert's weights are read once per call
+ * however many tokens chose it (onw technical notes, "computing MoE prompts
+ * together": tokens grouped by expert, each expert read once per prompt).
+ * The intermediate h is rounded to bf16 (nearest even) before the down
+ * projection; the weighted sum over slots runs in slot order, then the shared
+ * expert, in fp32, with no atomics.
+ *   X    DEVICE bf16 [T][D]; ids DEVICE int32 [T][k]; p DEVICE fp32 [T][k]
+ *   Y    DEVICE fp32 [T][D], fully overwritten
+ *   T    1..4096, k 1..16, T*k <= 4096
+ *   dbg  NULL, or stage outputs to fill (any member may be NULL)
+ *   ws   DEVICE workspace of at least q4nx_moe_ws(L, T, k) bytes, 256-byte aligned
+ * An id outside [0, n_experts) is never dereferenced: its slot contributes 0
+ * and bit 0 of the uint32 at ws[0] is set (cleared at the start of each call;
+ * read it after synchronising).
+ */
+int q4nx_moe_experts(const q4nx_moe_layer* L, const uint16_t* X, const int32_t* ids,
+                     const float* p, int T, int k, float* Y, const q4nx_moe_debug* dbg,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Test surface of the decoders (NPU engine page, "Q4NX chunks": the decoders
+ * of all three kinds are checked bit for bit).  Writes the fields of every
+ * chunk in logical [rows][cols] order:
+ *   codes    DEVICE u8 [rows][cols]: 4-bit code 0..15, or the int8 code's bits
+ *   meta0    DEVICE u16 [rows][cols/32]: q4_1 scale bits | Q4_K scale | Q8 d bits
+ *   meta1    DEVICE u16 [rows][cols/32] or NULL: q4_1 zero bits | Q4_K min | 0 for Q8
+ *   row_meta DEVICE u16 [rows][cols/256][2] or NULL: Q4_K (S, M) bits | 0 otherwise
+ */
+int q4nx_unpack(const q4nx_weight* w, uint8_t* codes, uint16_t* meta0, uint16_t* meta1,
+                uint16_t* row_meta, void* stream);
+
+/*
+ * Decoded weights as fp32 [rows][cols] (DEVICE `out`).  Each value is the
+ * exact product-and-sum of the formula rounded once to fp32 (every product in
+ * the three formulas is exact in fp32), so the result is bit-exact.
+ */
+int q4nx_decode(const q4nx_weight* w, float* out, void* stream);
+
+/* Static text for a status code. */
+const char* q4nx_status_str(int status);
+
+/* Detail of the last failing call on this thread ("" if none). */
+const char* q4nx_last_error(void);
+
+/* Interface version: 100 * major + minor. */
+int q4nx_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q4NX_H */

@@ -1,0 +1,157 @@
+"""The C ABI without a GPU: the library loads, exports what include/q4nx.h
+declares, and every host-side check returns its status before anything is
+enqueued (no call here reaches the device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "gemm_q4nx_chunk_amd", "libq4nx.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="library not built")
+
+
+@pytest.fixture(scope="module")
+def q():
+    import gemm_q4nx_chunk_amd as mod
+    return mod
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "q4nx.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(q4nx_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_function_is_exported(q):
+    names = _declared()
+    assert len(names) >= 11
+    lib = ctypes.CDLL(LIB)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings_and_version(q):
+    assert q.version() == 100
+    for s in range(9):
+        assert q.status_str(s) and q.status_str(s) != "unknown status"
+    assert q.status_str(99) == "unknown status"
+
+
+def _w(q, rows=64, cols=512, kind="q4_1", layout=None, nbytes=None, ptr=0x100000):
+    cb = q.CHUNK_BYTES[kind] if isinstance(kind, str) else kind
+    need = (rows // 32) * (cols // 256) * cb if rows > 0 and cols > 0 else 0
+    return q.weight(ptr, rows, cols, kind, layout, nbytes=need if nbytes is None else nbytes)
+
+
+def test_weight_check_rules(q):
+    assert q.weight_check(_w(q)) == q.Q4NX_OK and q.last_error() == ""
+    assert q.weight_check(_w(q, kind="q4_k")) == q.Q4NX_OK
+    assert q.weight_check(_w(q, kind="q8", layout="A")) == q.Q4NX_OK
+    assert q.weight_check(_w(q, kind="q8", layout="B")) == q.Q4NX_OK
+    assert q.weight_check(_w(q, ptr=0)) == q.E_ARG
+    assert q.weight_check(_w(q, kind=5000, nbytes=10 ** 6)) == q.E_CHUNK_KIND
+    assert "5000" in q.last_error()
+    assert q.weight_check(_w(q, kind="q8", layout=None)) == q.E_Q8_LAYOUT
+    assert q.weight_check(_w(q, rows=48, nbytes=10 ** 6)) == q.E_SHAPE
+    assert q.weight_check(_w(q, cols=300, nbytes=10 ** 6)) == q.E_SHAPE
+    assert q.weight_check(_w(q, rows=0, nbytes=10 ** 6)) == q.E_SHAPE
+    assert q.weight_check(_w(q, nbytes=2 * 2 * 5120 - 1)) == q.E_SHORT
+    assert q.weight_check(_w(q, ptr=0x100008)) == q.E_ALIGN
+    assert q.weight_check(_w(q)) == q.Q4NX_OK and q.last_error() == ""
+
+
+def test_null_descriptor(q):
+    assert q.lib().q4nx_weight_check(None) == q.E_ARG
+
+
+def _expect(q, status, fn, *a, **k):
+    with pytest.raises(q.Q4nxError) as e:
+        fn(*a, **k)
+    assert e.value.status == status, str(e.value)
+
+
+def test_gemv_argument_checks(q):
+    w = _w(q)
+    _expect(q, q.E_ARG, q.gemv, w, 0x2000, 0x3000, M=0, stream=0)
+    _expect(q, q.E_ARG, q.gemv, w, 0x2000, 0x3000, M=9, stream=0)
+    _expect(q, q.E_ARG, q.gemv, w, 0, 0x3000, M=1, stream=0)
+    _expect(q, q.E_ALIGN, q.gemv, w, 0x2008, 0x3000, M=1, stream=0)
+    _expect(q, q.E_ALIGN, q.gemv, w, 0x2000, 0x3002, M=1, stream=0)
+    _expect(q, q.E_Q8_LAYOUT, q.gemv, _w(q, kind="q8"), 0x2000, 0x3000, M=1, stream=0)
+    _expect(q, q.E_SHORT, q.gemv, _w(q, nbytes=100), 0x2000, 0x3000, M=1, stream=0)
+
+
+def test_gemv_batched_checks_every_job_first(q):
+    good = (_w(q), 0x2000, 0x3000)
+    bad = (_w(q, kind=1234, nbytes=10 ** 6), 0x2000, 0x3000)
+    _expect(q, q.E_CHUNK_KIND, q.gemv_batched, [good, good, bad], M=1, stream=0)
+    assert "job 2" in q.last_error()
+    arr = (q.GemvJob * 1)()
+    assert q.lib().q4nx_gemv_batched(arr, 0, 1, None) == q.E_ARG
+    assert q.lib().q4nx_gemv_batched(arr, q.BATCH_MAX_JOBS + 1, 1, None) == q.E_ARG
+
+
+def test_gemm_block_checks(q):
+    _expect(q, q.E_CHUNK_KIND, q.gemm_block, _w(q, kind="q8", layout="A"), 0x2000, 0x3000, 4, stream=0)
+    _expect(q, q.E_ARG, q.gemm_block, _w(q), 0x2000, 0x3000, 65, stream=0)
+    _expect(q, q.E_ARG, q.gemm_block, _w(q), 0x2000, 0x3000, 0, stream=0)
+    _expect(q, q.E_ALIGN, q.gemm_block, _w(q), 0x2004, 0x3000, 8, stream=0)
+
+
+def _layer(q, **over):
+    D, De, Ds, n = 2048, 512, 1024, 512
+    gu = (De // 32) * (D // 256) * 5120
+    dn = (D // 32) * (De // 256) * 5120
+    sh = (q.weight(0x200000, Ds, D, "q4_1"), q.weight(0x300000, Ds, D, "q4_1"),
+          q.weight(0x400000, D, Ds, "q4_1"))
+    for w in sh:
+        w.nbytes = (w.rows // 32) * (w.cols // 256) * 5120
+    args = dict(n_experts=n, d_model=D, d_expert=De, kind="q4_1", gate=0x10000000,
+                up=0x20000000, down=0x30000000, gate_stride=gu, up_stride=gu, down_stride=dn,
+                shared=sh, d_shared=Ds, gate_bytes=n * gu, up_bytes=n * gu, down_bytes=n * dn)
+    args.update(over)
+    return q.moe_layer(**args)
+
+
+def test_moe_workspace_size_and_checks(q):
+    L = _layer(q)
+    ws1 = q.moe_ws(L, 1, 10)
+    ws64 = q.moe_ws(L, 64, 10)
+    assert 0 < ws1 < ws64
+    # the fp32 down outputs alone need (T*k + T) * D * 4 bytes
+    assert ws64 >= (640 + 64) * 2048 * 4
+    assert q.moe_ws(L, 0, 10) == 0 and q.moe_ws(L, 512, 10) == 0 and q.moe_ws(L, 4, 17) == 0
+    assert q.moe_ws(_layer(q, kind="q8"), 1, 10) == 0
+
+    def call(L, T=1, k=10, ws=0x40000000, ws_bytes=None):
+        return q.lib().q4nx_moe_experts(ctypes.byref(L), 0x1000, 0x2000, 0x3000, T, k, 0x4000,
+                                        None, ws, ws1 if ws_bytes is None else ws_bytes, None)
+    assert call(L, ws_bytes=ws1 - 1) == q.E_WORKSPACE
+    assert call(L, ws=0) == q.E_WORKSPACE
+    assert call(L, ws=0x40000010) == q.E_ALIGN
+    assert call(L, T=0) == q.E_ARG
+    assert call(L, T=4096, k=2) == q.E_ARG
+    assert call(_layer(q, kind="q8")) == q.E_CHUNK_KIND
+    assert call(_layer(q, d_expert=500)) == q.E_SHAPE
+    assert call(_layer(q, gate_bytes=100)) == q.E_SHORT
+    assert call(_layer(q, gate_stride=1000)) == q.E_ALIGN
+    assert call(_layer(q, gate=0)) == q.E_ARG
+    L2 = _layer(q)
+    L2.reserved = 1
+    assert call(L2) == q.E_ARG
+    L3 = _layer(q)
+    L3.sh_down.rows = 1024
+    assert call(L3) in (q.E_SHAPE, q.E_SHORT)
+    L4 = _layer(q)
+    L4.n_experts = 0
+    assert call(L4) == q.E_ARG
+
+
+def test_unpack_decode_checks(q):
+    _expect(q, q.E_ARG, q.unpack, _w(q), 0, 0x2000, stream=0)
+    _expect(q, q.E_ALIGN, q.unpack, _w(q), 0x1000, 0x2001, stream=0)
+    _expect(q, q.E_ARG, q.decode, _w(q), 0, stream=0)
+    _expect(q, q.E_ALIGN, q.decode, _w(q), 0x1002, stream=0)

@@ -1,0 +1,78 @@
+"""GPU block GEMM (q4nx_gemm_block, M <= 64) vs the float64 oracle.
+
+Bar: |Y - Y_ref| <= 2e-3 * sum_k |w x| per element.  The kernel rounds each
+dequantised weight to bf16 (at most 2^-8 of its size); with random signs the
+error of a K-term sum stays far inside the bar, as these tests measure.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+from _gpu import dev_bf16, dev_u8, gemv, have_gpu, host, q, torch, weight
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not have_gpu(), reason="needs a GPU")]
+
+
+def _gen(kind, N, K, tag):
+    g = synth.rng("gpu-gemm", tag, kind, N, K)
+    return synth.gen_q4_1(g, N, K, zero="normal") if kind == "q4_1" else synth.gen_q4_k(g, N, K)
+
+
+def _gemm(ch_dev, N, K, kind, X):
+    M = X.shape[0]
+    Y = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    q().gemm_block(weight(ch_dev, N, K, kind), dev_bf16(X), Y, M)
+    return host(Y)
+
+
+@pytest.mark.parametrize("kind", ["q4_1", "q4_k"])
+@pytest.mark.parametrize("N,K", [(32, 256), (96, 512), (160, 1280), (256, 2560)])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 16, 31, 32, 33, 48, 63, 64])
+def test_gemm_shapes(kind, N, K, M):
+    ch = _gen(kind, N, K, "shapes")
+    X = synth.gen_x(synth.rng("gpu-gemm", "X", N, K, M), M, K)
+    Y = _gemm(dev_u8(ch), N, K, kind, X)
+    yr, a = oracle.gemv_ref(oracle.weights_exact(ch, kind, N, K), X)
+    r = oracle.tol_ratio(Y, yr, a)
+    assert r <= 1.0, r
+
+
+def test_gemm_rows_agree_with_gemv():
+    N, K, M = 256, 2048, 64
+    ch = _gen("q4_1", N, K, "vs-gemv")
+    X = synth.gen_x(synth.rng("gpu-gemm", "vsX"), M, K)
+    d = dev_u8(ch)
+    Y = _gemm(d, N, K, "q4_1", X)
+    yv = np.concatenate([gemv(d, N, K, "q4_1", X[m:m + 4]) for m in range(0, M, 4)])
+    yr, a = oracle.gemv_ref(oracle.weights_exact(ch, "q4_1", N, K), X)
+    assert oracle.tol_ratio(Y, yv, a) <= 1.0
+
+
+def test_gemm_repeat_bit_identical_and_zero_rows():
+    N, K, M = 128, 1024, 40
+    ch = dev_u8(_gen("q4_k", N, K, "det"))
+    X = synth.gen_x(synth.rng("gpu-gemm", "detX"), M, K)
+    X[7] = 0
+    Ys = [_gemm(ch, N, K, "q4_k", X) for _ in range(4)]
+    for Y in Ys[1:]:
+        np.testing.assert_array_equal(Y.view(np.uint32), Ys[0].view(np.uint32))
+    assert np.all(Ys[0][7] == 0)
+
+
+def test_dense_8b_layer_full_size_m64():
+    """One 8B-dense layer's seven projections at M = 64, sampled tile rows checked."""
+    X_all = {}
+    for i, spec in enumerate(synth.dense_8b_block_specs(1)):
+        ch = spec.generate()
+        if spec.K not in X_all:
+            X_all[spec.K] = synth.gen_x(synth.rng("dense_8b_block", "X", spec.K), 64, spec.K)
+        X = X_all[spec.K]
+        Y = _gemm(dev_u8(ch), spec.N, spec.K, "q4_1", X)
+        g = np.random.default_rng(i)
+        tr = np.unique(np.concatenate([[0, spec.N // 32 - 1], g.integers(0, spec.N // 32, 3)]))
+        W = oracle.weights_exact(ch[tr], "q4_1", 32 * len(tr), spec.K)
+        yr, a = oracle.gemv_ref(W, X)
+        ysub = np.concatenate([Y[:, 32 * t:32 * t + 32] for t in tr], axis=1)
+        assert oracle.tol_ratio(ysub, yr, a) <= 1.0, spec.name

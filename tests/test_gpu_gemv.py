@@ -1,0 +1,195 @@
+"""GPU dequant-GEMV (q4nx_gemv, q4nx_gemv_batched) vs the float64 oracle.
+
+Bar: every output finite and |y - y_ref| <= 2e-3 * sum_k |w x| per element.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+from _gpu import dev_bf16, dev_u8, gemv, have_gpu, host, q, torch, weight
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not have_gpu(), reason="needs a GPU")]
+
+KINDS = [("q4_1", None), ("q4_k", None), ("q8", "A"), ("q8", "B")]
+
+
+def _gen(kind, layout, N, K, tag):
+    g = synth.rng("gpu-gemv", tag, kind, layout or "-", N, K)
+    if kind == "q4_1":
+        return synth.gen_q4_1(g, N, K, zero="normal")
+    if kind == "q4_k":
+        return synth.gen_q4_k(g, N, K)
+    return synth.gen_q8(g, N, K, layout)
+
+
+def _check(y, ch, kind, N, K, x, layout, rows=None):
+    W = oracle.weights_exact(ch, kind, N, K, layout)
+    yr, a = oracle.gemv_ref(W, x)
+    if rows is not None:
+        yr, a, y = yr[:, rows], a[:, rows], y[:, rows]
+    r = oracle.tol_ratio(y, yr, a)
+    assert r <= 1.0, f"max error / (2e-3 * sum|wx|) = {r}"
+    return r
+
+
+def test_single_q4_1_gemv_1024():
+    spec = synth.single_gemv_spec()
+    ch = spec.generate()
+    x = synth.gen_x(synth.rng("q4_1_gemv_1024", 0, "x"), 1, spec.K)
+    y = gemv(dev_u8(ch), spec.N, spec.K, "q4_1", x)
+    print("tolerance ratio", _check(y, ch, "q4_1", spec.N, spec.K, x, None))
+
+
+@pytest.mark.parametrize("kind,layout", KINDS)
+@pytest.mark.parametrize("N,K", [(32, 256), (96, 768), (160, 1280), (64, 2560), (288, 3328)])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 8])
+def test_gemv_shapes(kind, layout, N, K, M):
+    ch = _gen(kind, layout, N, K, "shapes")
+    x = synth.gen_x(synth.rng("gpu-gemv", "x", N, K, M), M, K)
+    y = gemv(dev_u8(ch), N, K, kind, x, layout)
+    _check(y, ch, kind, N, K, x, layout)
+
+
+@pytest.mark.parametrize("M", [5, 6, 7])
+def test_gemv_other_m(M):
+    N, K = 96, 1280
+    ch = _gen("q4_1", None, N, K, "otherm")
+    x = synth.gen_x(synth.rng("gpu-gemv", "xm", M), M, K)
+    _check(gemv(dev_u8(ch), N, K, "q4_1", x), ch, "q4_1", N, K, x, None)
+
+
+def test_q8_layouts_give_identical_bits():
+    N, K = 2048, 2560
+    A = synth.gen_q8(synth.rng("gpu-gemv", "q8ab"), N, K, "A")
+    B = synth.q8_relayout(A, "A", "B")
+    x = synth.gen_x(synth.rng("gpu-gemv", "q8ab-x"), 1, K)
+    ya = gemv(dev_u8(A), N, K, "q8", x, "A")
+    yb = gemv(dev_u8(B), N, K, "q8", x, "B")
+    np.testing.assert_array_equal(ya.view(np.uint32), yb.view(np.uint32))
+    _check(ya, A, "q8", N, K, x, "A")
+
+
+@pytest.mark.parametrize("kind,layout", KINDS)
+def test_one_hot_activation_gives_the_column(kind, layout):
+    N, K = 64, 512
+    ch = _gen(kind, layout, N, K, "onehot")
+    W32 = oracle.weights_f32(ch, kind, N, K, layout)
+    cols = [0, 5, 31, 32, 255, 256, 511]
+    x = np.zeros((len(cols), K), np.uint16)
+    for i, k in enumerate(cols):
+        x[i, k] = 0x3F80
+    for i0 in range(0, len(cols), 4):
+        xs = x[i0:i0 + 4]
+        y = gemv(dev_u8(ch), N, K, kind, xs, layout)
+        for j in range(xs.shape[0]):
+            k = cols[i0 + j]
+            if kind in ("q8",):
+                np.testing.assert_array_equal(y[j], W32[:, k])          # d*c exact
+            else:
+                np.testing.assert_allclose(y[j], W32[:, k], rtol=2e-3, atol=0)
+
+
+def test_q4_0_style_zero_rows_are_exactly_zero():
+    """Codes all 8 with zero = -8*scale decode to w = 0: the GEMV must return exactly 0."""
+    N, K = 64, 1024
+    g = synth.rng("gpu-gemv", "zero-rows")
+    codes = g.integers(0, 16, (N, K), dtype=np.uint8)
+    codes[5, :] = 8
+    codes[40, :] = 8
+    s = synth.bf16_bits(np.abs(g.standard_normal((N, K // 32)).astype(np.float32)) * 0.02)
+    z = synth.bf16_bits(-8 * synth.bf16_to_f32(s))
+    ch = synth.pack_q4_1(codes, s, z)
+    x = synth.gen_x(g, 4, K)
+    y = gemv(dev_u8(ch), N, K, "q4_1", x)
+    assert np.all(y[:, 5] == 0) and np.all(y[:, 40] == 0)
+    _check(y, ch, "q4_1", N, K, x, None)
+
+
+def test_zero_activations_give_zero():
+    N, K = 96, 768
+    for kind, layout in KINDS:
+        ch = _gen(kind, layout, N, K, "zx")
+        y = gemv(dev_u8(ch), N, K, kind, np.zeros((2, K), np.uint16), layout)
+        assert np.all(y == 0), kind
+
+
+def test_nan_scale_poisons_exactly_its_row():
+    N, K = 64, 512
+    ch = _gen("q4_1", None, N, K, "nan")
+    # (scale, zero) of tile row 0, row r=3, group g=2 -> chunk (0, 0), byte 4096 + 4*(8*3+2)
+    ch[0, 0, 4096 + 4 * 26:4096 + 4 * 26 + 2] = np.frombuffer(np.uint16(0x7FC0).tobytes(), np.uint8)
+    x = synth.gen_x(synth.rng("gpu-gemv", "nanx"), 1, K)
+    y = gemv(dev_u8(ch), N, K, "q4_1", x)
+    bad = ~np.isfinite(y[0])
+    assert bad[3] and bad.sum() == 1
+    keep = [r for r in range(N) if r != 3]
+    _check(y, ch, "q4_1", N, K, x, None, rows=keep)
+
+
+def test_repeat_runs_are_bit_identical():
+    N, K = 1024, 2560
+    ch = dev_u8(_gen("q4_1", None, N, K, "det"))
+    x = synth.gen_x(synth.rng("gpu-gemv", "detx"), 4, K)
+    ys = [gemv(ch, N, K, "q4_1", x) for _ in range(5)]
+    for y in ys[1:]:
+        np.testing.assert_array_equal(y.view(np.uint32), ys[0].view(np.uint32))
+
+
+def test_batched_matches_single_calls():
+    shapes = [(4096, 2560), (1024, 2560), (1024, 2560), (320, 768)]
+    chs = [_gen("q4_1", None, N, K, f"b{i}") for i, (N, K) in enumerate(shapes)]
+    chs.append(_gen("q8", "B", 256, 512, "b8"))
+    shapes.append((256, 512))
+    kinds = ["q4_1"] * 4 + ["q8"]
+    lays = [None] * 4 + ["B"]
+    M = 2
+    xs = [synth.gen_x(synth.rng("gpu-gemv", "bx", i), M, K) for i, (N, K) in enumerate(shapes)]
+    dch = [dev_u8(c) for c in chs]
+    dx = [dev_bf16(x) for x in xs]
+    dy = [torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda") for N, K in shapes]
+    jobs = [(weight(dch[i], N, K, kinds[i], lays[i]), dx[i], dy[i]) for i, (N, K) in enumerate(shapes)]
+    q().gemv_batched(jobs, M)
+    for i, (N, K) in enumerate(shapes):
+        _check(host(dy[i]), chs[i], kinds[i], N, K, xs[i], lays[i])
+
+
+def _sampled_rows(N, seed, n=96):
+    g = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, 1, N - 1], g.integers(0, N, n)]))
+
+
+def test_qwen3_4b_layer_and_lm_head_full_size():
+    """One layer's seven projections and the lm_head at full size, sampled rows checked."""
+    specs = synth.qwen3_4b_decode_specs(1, True)
+    for i, spec in enumerate(specs):
+        ch = spec.generate()
+        x = synth.gen_x(synth.rng("qwen3_4b_decode", "x", spec.name), 1, spec.K)
+        y = gemv(dev_u8(ch), spec.N, spec.K, "q4_1", x)
+        rows = _sampled_rows(spec.N, i)
+        tr = np.unique(rows // 32)
+        sub = ch[tr]
+        W = oracle.weights_exact(sub, "q4_1", 32 * len(tr), spec.K)
+        yr, a = oracle.gemv_ref(W, x)
+        ysub = np.concatenate([y[:, 32 * t:32 * t + 32] for t in tr], axis=1)
+        assert oracle.tol_ratio(ysub, yr, a) <= 1.0, spec.name
+
+
+@pytest.mark.parametrize("layout", ["A", "B"])
+def test_mixed_q4k_layer_and_q8_lm_head_full_size(layout):
+    specs = synth.mixed_decode_specs(1, "A")
+    for i, spec in enumerate(specs):
+        ch = spec.generate()
+        lay = None
+        if spec.kind == "q8":
+            lay = layout
+            if layout == "B":
+                ch = synth.q8_relayout(ch, "A", "B")
+        x = synth.gen_x(synth.rng("mixed_decode", "x", spec.name), 1, spec.K)
+        y = gemv(dev_u8(ch), spec.N, spec.K, spec.kind, x, lay)
+        tr = np.unique(_sampled_rows(spec.N, 100 + i) // 32)
+        W = oracle.weights_exact(ch[tr], spec.kind, 32 * len(tr), spec.K, lay)
+        yr, a = oracle.gemv_ref(W, x)
+        ysub = np.concatenate([y[:, 32 * t:32 * t + 32] for t in tr], axis=1)
+        assert oracle.tol_ratio(ysub, yr, a) <= 1.0, spec.name
