@@ -1,0 +1,486 @@
+#!/usr/bin/env python3
+"""Throughput of the Q4NX dequant-GEMV / block-GEMM / MoE path on one MI355X.
+
+Headline (value): weight GB/s of a Qwen3-4B-shaped decode step -- 36 layers of
+distinct all-q4_1 weights (q 4096x2560, k/v 1024x2560, o 2560x4096, gate/up
+9728x2560, down 2560x9728) plus the 151936x2560 lm_head, batch 1, one bf16
+N(0,1) activation vector per projection.  A step is launched the way a decode
+engine has to: per layer one batched GEMV for q|k|v (one input), one for o,
+one for gate|up (one input), one for down, then the lm_head -- 145 launches,
+captured once in a HIP graph and replayed.  Weights are resident in HBM before
+timing starts.
+
+Also reported (legs): the kernel's roofline from per-launch HIP events; the
+CPU oracle timed on a bounded sample; the mixed Q4_K + Q8 lm_head decode step
+(Q8 in each code layout); the 64-token block GEMM over 32 layers of 8B-dense
+shapes (TFLOP/s) with its M = 1, 2, 4 GEMV variants; the MoE layer (512
+experts, top-10, shared expert, 48 layers) at T = 1 and T = 64; the single
+1024x1024 GEMV.  Inputs are synthetic and seeded (see synth).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+METRIC = "Q4NX dequant-GEMV weight GB/s (% of HBM peak); 64-tok block GEMM TFLOP/s"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--legs", default="all",
+                    help="comma list of: decode, mixed, gemm, moe, single, cpu, copyref "
+                         "(default all but copyref)")
+    ap.add_argument("--no-graph", action="store_true", help="launch the step without a HIP graph")
+    return ap.parse_args()
+
+
+args = parse()
+if args.gpus != 1:
+    print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+                      "n_gpus": args.gpus}))
+    sys.exit(2)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+import gemm_q4nx_chunk_amd as q  # noqa: E402
+import synth  # noqa: E402
+
+LEGS = set(["decode", "mixed", "gemm", "moe", "single", "cpu"] if args.legs == "all"
+           else args.legs.split(","))
+DEV = torch.device("cuda:0")
+torch.cuda.set_device(DEV)
+GEN_THREADS = min(16, len(os.sched_getaffinity(0)))
+
+
+# ----------------------------------------------------------------------------
+# helpers
+# ----------------------------------------------------------------------------
+def to_dev(a: np.ndarray):
+    return torch.from_numpy(np.ascontiguousarray(a).reshape(-1).view(np.uint8)).to(DEV)
+
+
+def bf16_dev(bits: np.ndarray):
+    return torch.from_numpy(np.ascontiguousarray(bits, np.uint16).view(np.int16)).to(DEV)
+
+
+def upload_specs(specs):
+    """Generate on host threads and upload tensor by tensor (bounded host memory)."""
+    out = []
+    for i in range(0, len(specs), GEN_THREADS):
+        chunk = specs[i:i + GEN_THREADS]
+        for s, arr in zip(chunk, synth.generate_many(chunk, GEN_THREADS)):
+            out.append(to_dev(arr))
+    return out
+
+
+def events():
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+def time_calls(fn, steps: int, warmup: int, graph: bool):
+    """ms per call of fn (a whole step), timed over `steps` calls after `warmup`."""
+    if graph:
+        s = torch.cuda.Stream()
+        with torch.cuda.stream(s):
+            fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            fn()
+        torch.cuda.synchronize()
+        run = g.replay
+    else:
+        run = fn
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = events()
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    ms = e0.elapsed_time(e1) / steps
+    return ms, wall
+
+
+def per_launch_ms(calls, reps: int = 3):
+    """Average duration of each launch, HIP events around it on the launch stream."""
+    torch.cuda.synchronize()
+    pairs = []
+    for _ in range(reps):
+        for c in calls:
+            e0, e1 = events()
+            e0.record()
+            c()
+            e1.record()
+            pairs.append((e0, e1))
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in pairs]
+
+
+# ----------------------------------------------------------------------------
+# GEMV decode steps (headline and mixed)
+# ----------------------------------------------------------------------------
+class DecodeStep:
+    """Weights, activations and outputs of one decode step, launched in phases."""
+
+    PHASES = (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))
+
+    def __init__(self, specs, tag, M=1):
+        self.specs = specs
+        self.M = M
+        self.bytes = sum(s.nbytes for s in specs)
+        t0 = time.time()
+        self.w = upload_specs(specs)
+        log(f"[{tag}] generated+uploaded {self.bytes / 1e9:.2f} GB in {time.time() - t0:.1f} s")
+        self.x, self.y, self.desc = {}, {}, {}
+        by_name = {s.name: i for i, s in enumerate(specs)}
+        self.calls = []
+        layers = sorted({int(s.name.split(".")[0][1:]) for s in specs if s.name.startswith("L")})
+        for l in layers:
+            for ph in self.PHASES:
+                idx = [by_name[f"L{l}.{n}"] for n in ph]
+                K = specs[idx[0]].K
+                x = bf16_dev(synth.gen_x(synth.rng(tag, "x", l, ph[0]), M, K))
+                jobs = []
+                for i in idx:
+                    s = specs[i]
+                    y = torch.empty((M, s.N), dtype=torch.float32, device=DEV)
+                    w = q.weight(self.w[i], s.N, s.K, s.kind, s.q8_layout if s.kind == "q8" else None)
+                    jobs.append((w, x, y))
+                    self.y[s.name] = y
+                self.calls.append(self._batched(jobs))
+        for s, dw in zip(specs, self.w):
+            if not s.name.startswith("L"):
+                x = bf16_dev(synth.gen_x(synth.rng(tag, "x", s.name), M, s.K))
+                y = torch.empty((M, s.N), dtype=torch.float32, device=DEV)
+                w = q.weight(dw, s.N, s.K, s.kind, s.q8_layout if s.kind == "q8" else None)
+                self.y[s.name] = y
+                self.calls.append(self._batched([(w, x, y)]))
+
+    def _batched(self, jobs):
+        M = self.M
+        arr = (q.GemvJob * len(jobs))(*[q.GemvJob(w, q._ptr(x), q._ptr(y)) for w, x, y in jobs])
+        keep = jobs
+        lib = q.lib()
+
+        def call():
+            st = lib.q4nx_gemv_batched(arr, len(keep), M, torch.cuda.current_stream().cuda_stream)
+            if st:
+                raise q.Q4nxError(st, q.last_error())
+        return call
+
+    def run(self):
+        for c in self.calls:
+            c()
+
+
+def decode_leg(specs, tag, steps, warmup, graph, M=1):
+    step = DecodeStep(specs, tag, M)
+    ms, wall = time_calls(step.run, steps, warmup, graph)
+    gbs = step.bytes / (ms * 1e-3) / 1e9
+    res = {"ms_per_step": ms, "wall_ms_per_step": wall, "weight_bytes": step.bytes,
+           "GB_s": gbs, "pct_hbm_peak": 100 * gbs / HBM_PEAK_GBS, "launches": len(step.calls),
+           "graph": graph}
+    return step, res
+
+
+# ----------------------------------------------------------------------------
+# CPU oracle baseline (bounded sample)
+# ----------------------------------------------------------------------------
+def cpu_baseline(specs, budget_s=15.0):
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    done_bytes, t_dec, t_dot, names = 0, 0.0, 0.0, []
+    t_start = time.time()
+    for s in specs:
+        ch = s.generate()
+        x = synth.gen_x(synth.rng("cpu", s.name), 1, s.K)
+        t0 = time.perf_counter()
+        W = oracle.weights_exact(ch, s.kind, s.N, s.K, s.q8_layout if s.kind == "q8" else None)
+        t1 = time.perf_counter()
+        oracle.gemv_ref(W, x)
+        t2 = time.perf_counter()
+        t_dec += t1 - t0
+        t_dot += t2 - t1
+        done_bytes += s.nbytes
+        names.append(s.name)
+        del W, ch
+        if time.time() - t_start > budget_s:
+            break
+    tot = t_dec + t_dot
+    return {"value": done_bytes / tot / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"float64 decode + dot of {len(names)} q4_1 tensors of the decode step "
+                      f"({names[0]}..{names[-1]}, {done_bytes / 1e6:.0f} MB of chunks)",
+            "decode_s": t_dec, "dot_s": t_dot,
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+# ----------------------------------------------------------------------------
+# block GEMM
+# ----------------------------------------------------------------------------
+def gemm_leg(steps, warmup, graph):
+    specs = synth.dense_8b_block_specs()
+    t0 = time.time()
+    w = upload_specs(specs)
+    nbytes = sum(s.nbytes for s in specs)
+    log(f"[gemm] generated+uploaded {nbytes / 1e9:.2f} GB in {time.time() - t0:.1f} s")
+    Xs = {K: bf16_dev(synth.gen_x(synth.rng("dense_8b_block", "X", K), 64, K)) for K in (4096, 14336)}
+    Ys = {N: torch.empty((64, N), dtype=torch.float32, device=DEV) for N in (1024, 4096, 14336)}
+    descs = [q.weight(dw, s.N, s.K, "q4_1") for s, dw in zip(specs, w)]
+    lib = q.lib()
+    import ctypes
+
+    def run64():
+        st = torch.cuda.current_stream().cuda_stream
+        for s, d in zip(specs, descs):
+            r = lib.q4nx_gemm_block(ctypes.byref(d), Xs[s.K].data_ptr(), Ys[s.N].data_ptr(), 64, st)
+            if r:
+                raise q.Q4nxError(r, q.last_error())
+    flops = sum(2 * 64 * s.N * s.K for s in specs)
+    ms, wall = time_calls(run64, steps, warmup, graph)
+    res = {"M64": {"ms_per_block": ms, "TFLOP_s": flops / (ms * 1e-3) / 1e12, "flops": flops,
+                   "weight_bytes": nbytes, "GB_s": nbytes / (ms * 1e-3) / 1e9,
+                   "pct_mfma_peak": 100 * flops / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+                   "pct_hbm_peak": 100 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                   "launches": len(specs)}}
+    # per-launch durations of the block GEMM kernel (roofline of this leg)
+    calls = []
+    for s, d in zip(specs[:7], descs[:7]):
+        calls.append(lambda s=s, d=d: lib.q4nx_gemm_block(ctypes.byref(d), Xs[s.K].data_ptr(),
+                                                          Ys[s.N].data_ptr(), 64,
+                                                          torch.cuda.current_stream().cuda_stream))
+    dur = per_launch_ms(calls, reps=3)
+    fl7 = sum(2 * 64 * s.N * s.K for s in specs[:7]) * 3
+    res["M64"]["kernel_TFLOP_s"] = fl7 / (sum(dur) * 1e-3) / 1e12
+    # M = 1, 2, 4 through the GEMV path (same weights)
+    for M in (1, 2, 4):
+        xm = {K: bf16_dev(synth.gen_x(synth.rng("dense_8b_block", "xm", K, M), M, K)) for K in (4096, 14336)}
+        ym = {N: torch.empty((M, N), dtype=torch.float32, device=DEV) for N in (1024, 4096, 14336)}
+        groups = []
+        for l in range(synth.DENSE_8B_LAYERS):
+            base = 7 * l
+            for ph in ((0, 1, 2), (3,), (4, 5), (6,)):
+                jobs = [(descs[base + i], xm[specs[base + i].K], ym[specs[base + i].N]) for i in ph]
+                arr = (q.GemvJob * len(jobs))(*[q.GemvJob(a, q._ptr(b), q._ptr(c)) for a, b, c in jobs])
+                groups.append((arr, len(jobs)))
+
+        def runm(M=M, groups=groups):
+            st = torch.cuda.current_stream().cuda_stream
+            for arr, n in groups:
+                r = lib.q4nx_gemv_batched(arr, n, M, st)
+                if r:
+                    raise q.Q4nxError(r, q.last_error())
+        msm, _ = time_calls(runm, steps, warmup, graph)
+        res[f"M{M}"] = {"ms_per_block": msm, "GB_s": nbytes / (msm * 1e-3) / 1e9,
+                        "pct_hbm_peak": 100 * nbytes / (msm * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    del w
+    return res
+
+
+# ----------------------------------------------------------------------------
+# MoE
+# ----------------------------------------------------------------------------
+def moe_leg(steps, warmup, graph):
+    D, De, Ds, E, L = synth.MOE_D_MODEL, synth.MOE_D_EXPERT, synth.MOE_D_SHARED, synth.MOE_EXPERTS, synth.MOE_LAYERS
+    gu = (De // 32) * (D // 256) * 5120
+    dn = (D // 32) * (De // 256) * 5120
+    res = {}
+    routes = {T: [synth.moe_router(l, T) for l in range(L)] for T in (1, 64)}
+    need = [set(np.concatenate([routes[1][l][0].ravel(), routes[64][l][0].ravel()]).tolist())
+            for l in range(L)]
+    t0 = time.time()
+    layers = []
+    for l in range(L):
+        arenas = {p: torch.empty(E * (gu if p != "down" else dn), dtype=torch.uint8, device=DEV)
+                  for p in ("gate", "up", "down")}
+        specs, where = [], []
+        for e in sorted(need[l]):
+            for p in ("gate", "up", "down"):
+                specs.append(synth.moe_expert_spec(l, p, e))
+                where.append((p, e))
+        for p in ("gate", "up", "down"):
+            specs.append(synth.moe_shared_spec(l, p))
+            where.append((p, "shared"))
+        shared = {}
+        for i in range(0, len(specs), GEN_THREADS):
+            part = specs[i:i + GEN_THREADS]
+            for (p, e), arr in zip(where[i:i + GEN_THREADS], synth.generate_many(part, GEN_THREADS)):
+                t = torch.from_numpy(arr.reshape(-1))
+                if e == "shared":
+                    shared[p] = t.to(DEV)
+                else:
+                    stride = gu if p != "down" else dn
+                    arenas[p][e * stride:(e + 1) * stride].copy_(t)
+        sw = (q.weight(shared["gate"], Ds, D, "q4_1"), q.weight(shared["up"], Ds, D, "q4_1"),
+              q.weight(shared["down"], D, Ds, "q4_1"))
+        Ld = q.moe_layer(E, D, De, "q4_1", arenas["gate"], arenas["up"], arenas["down"], gu, gu, dn,
+                         shared=sw, d_shared=Ds)
+        layers.append((Ld, arenas, shared))
+    log(f"[moe] arenas {3 * E * gu * L / 1e9:.1f} GB allocated, selected experts generated "
+        f"in {time.time() - t0:.1f} s")
+    lib = q.lib()
+    import ctypes
+    for T in (1, 64):
+        k = synth.MOE_TOP_K
+        ws_b = q.moe_ws(layers[0][0], T, k)
+        wss = [torch.empty(ws_b, dtype=torch.uint8, device=DEV) for _ in range(L)]
+        X = [bf16_dev(synth.gen_x(synth.rng("moe_512x10", l, "X", T), T, D)) for l in range(L)]
+        ids = [torch.from_numpy(routes[T][l][0]).to(DEV) for l in range(L)]
+        ps = [torch.from_numpy(routes[T][l][1]).to(DEV) for l in range(L)]
+        Ys = [torch.empty((T, D), dtype=torch.float32, device=DEV) for _ in range(L)]
+
+        def run(T=T, wss=wss, X=X, ids=ids, ps=ps, Ys=Ys, ws_b=ws_b):
+            st = torch.cuda.current_stream().cuda_stream
+            for l in range(L):
+                r = lib.q4nx_moe_experts(ctypes.byref(layers[l][0]), X[l].data_ptr(), ids[l].data_ptr(),
+                                         ps[l].data_ptr(), T, k, Ys[l].data_ptr(), None,
+                                         wss[l].data_ptr(), ws_b, st)
+                if r:
+                    raise q.Q4nxError(r, q.last_error())
+        ms, wall = time_calls(run, steps, warmup, graph)
+        # algorithmic bytes: every selected expert read once per layer, plus the shared expert
+        uniq = sum(len(np.unique(routes[T][l][0])) for l in range(L))
+        nbytes = uniq * (2 * gu + dn) + L * 3 * (Ds // 32) * (D // 256) * 5120
+        flops = L * T * (synth.MOE_TOP_K * 3 * 2 * De * D + 3 * 2 * Ds * D)
+        res[f"T{T}"] = {"ms_per_step": ms, "layers": L, "weight_bytes": nbytes,
+                        "distinct_experts_per_layer": uniq / L, "GB_s": nbytes / (ms * 1e-3) / 1e9,
+                        "pct_hbm_peak": 100 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                        "TFLOP_s": flops / (ms * 1e-3) / 1e12, "launches": 4 * L}
+        del wss, X, ids, ps, Ys
+    del layers
+    torch.cuda.empty_cache()
+    return res
+
+
+# ----------------------------------------------------------------------------
+# single 1024 x 1024 GEMV, rotated over distinct copies
+# ----------------------------------------------------------------------------
+def single_leg():
+    spec = synth.single_gemv_spec()
+    ch = spec.generate()
+    copies = 2048
+    big = torch.from_numpy(np.tile(ch.reshape(1, -1), (copies, 1)).reshape(-1)).to(DEV)
+    x = bf16_dev(synth.gen_x(synth.rng("q4_1_gemv_1024", 0, "x"), 1, spec.K))
+    y = torch.empty((1, spec.N), dtype=torch.float32, device=DEV)
+    descs = [q.weight(big[i * spec.nbytes:(i + 1) * spec.nbytes], spec.N, spec.K, "q4_1") for i in range(copies)]
+    lib = q.lib()
+    import ctypes
+
+    def run():
+        st = torch.cuda.current_stream().cuda_stream
+        for d in descs:
+            lib.q4nx_gemv(ctypes.byref(d), x.data_ptr(), y.data_ptr(), 1, st)
+    ms, _ = time_calls(run, 3, 1, graph=False)
+    per = ms / copies * 1e3
+    msg, _ = time_calls(run, 3, 1, graph=True)
+    perg = msg / copies * 1e3
+    hot = descs[0]
+
+    def run_hot():
+        st = torch.cuda.current_stream().cuda_stream
+        for _ in range(copies):
+            lib.q4nx_gemv(ctypes.byref(hot), x.data_ptr(), y.data_ptr(), 1, st)
+    msh, _ = time_calls(run_hot, 3, 1, graph=True)
+    return {"weight_bytes": spec.nbytes, "rotated_copies": copies,
+            "us_per_call_stream": per, "us_per_call_graph": perg,
+            "GB_s_graph_rotated": spec.nbytes / (perg * 1e-6) / 1e9,
+            "us_per_call_graph_hot": msh / copies * 1e3}
+
+
+# ----------------------------------------------------------------------------
+def main():
+    out = {"metric": METRIC, "value": None, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": None, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+           "config": {"workload": "qwen3_4b_decode_step_q4_1", "layers": synth.QWEN3_4B_LAYERS,
+                      "batch": 1, "lm_head": "151936x2560", "kind": "q4_1",
+                      "launches": "per layer q|k|v, o, gate|up, down batched GEMVs + lm_head",
+                      "hip_graph": not args.no_graph},
+           "device": torch.cuda.get_device_name(0)}
+    graph = not args.no_graph
+    legs = {}
+    specs = synth.qwen3_4b_decode_specs()
+    if "decode" in LEGS:
+        step, res = decode_leg(specs, "qwen3_4b_decode", args.steps, args.warmup, graph)
+        out["value"] = res["GB_s"]
+        out["ms_per_step"] = res["ms_per_step"]
+        out["config"]["weight_bytes_per_step"] = res["weight_bytes"]
+        out["pct_hbm_peak"] = res["pct_hbm_peak"]
+        legs["decode_stream_launch"] = {}
+        ms_s, _ = time_calls(step.run, args.steps, args.warmup, False)
+        legs["decode_stream_launch"] = {"ms_per_step": ms_s, "GB_s": res["weight_bytes"] / (ms_s * 1e-3) / 1e9}
+        # roofline of the dominant kernel (q4_1 GEMV, M = 1): bytes per launch / launch time
+        dur = per_launch_ms(step.calls, reps=3)
+        per_launch_bytes = res["weight_bytes"] / len(step.calls)
+        avg_ms = sum(dur) / len(dur)
+        ach = per_launch_bytes / (avg_ms * 1e-3) / 1e9
+        out["roofline"] = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": ach / HBM_PEAK_GBS, "traffic": None,
+                           "kernel": "k_gemv_q4<q4_1, M=1>",
+                           "avg_launch_us": avg_ms * 1e3, "bytes_per_launch": per_launch_bytes,
+                           "launches_timed": len(dur)}
+        legs["decode"] = res
+        del step
+        torch.cuda.empty_cache()
+    if "cpu" in LEGS:
+        out["cpu_baseline"] = cpu_baseline(specs)
+    if "mixed" in LEGS:
+        for lay in ("A", "B"):
+            ms = synth.mixed_decode_specs(q8_layout=lay)
+            if lay == "B":   # the same logical lm_head, re-encoded in layout B
+                head = ms[-1]
+                orig = head.generate
+                head.generate = lambda orig=orig: synth.q8_relayout(orig(), "A", "B")
+            st, r = decode_leg(ms, f"mixed_decode", args.steps, args.warmup, graph)
+            head_i = len(st.calls) - 1
+            dur = per_launch_ms([st.calls[head_i]], reps=10)
+            r["q8_lm_head_us"] = 1e3 * sum(dur) / len(dur)
+            r["q8_lm_head_GB_s"] = ms[-1].nbytes / (sum(dur) / len(dur) * 1e-3) / 1e9
+            legs[f"mixed_q4k_q8{lay}"] = r
+            del st
+            torch.cuda.empty_cache()
+    if "gemm" in LEGS:
+        legs["block_gemm_8b"] = gemm_leg(max(3, args.steps // 4), 2, graph)
+        torch.cuda.empty_cache()
+    if "moe" in LEGS:
+        legs["moe_512x10"] = moe_leg(max(3, args.steps // 2), 2, graph)
+    if "single" in LEGS:
+        legs["single_gemv_1024"] = single_leg()
+    if "copyref" in LEGS:
+        # a plain device copy of known size, for scaling the HBM byte counters
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=DEV)
+        b = torch.empty_like(a)
+        ms, _ = time_calls(lambda: b.copy_(a), 5, 1, graph=False)
+        legs["copy_1GiB"] = {"bytes_read": 1 << 30, "bytes_written": 1 << 30, "ms": ms,
+                             "GB_s_read_plus_write": 2 * (1 << 30) / (ms * 1e-3) / 1e9}
+        del a, b
+    out["legs"] = legs
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()
