@@ -155,9 +155,10 @@ class DecodeStep:
         self.x, self.y, self.desc = {}, {}, {}
         by_name = {s.name: i for i, s in enumerate(specs)}
         self.calls = []
+        self.plan_jobs, self.plan_phases = [], []
         layers = sorted({int(s.name.split(".")[0][1:]) for s in specs if s.name.startswith("L")})
         for l in layers:
-            for ph in self.PHASES:
+            for pi, ph in enumerate(self.PHASES):
                 idx = [by_name[f"L{l}.{n}"] for n in ph]
                 K = specs[idx[0]].K
                 x = bf16_dev(synth.gen_x(synth.rng(tag, "x", l, ph[0]), M, K))
@@ -168,6 +169,8 @@ class DecodeStep:
                     w = q.weight(self.w[i], s.N, s.K, s.kind, s.q8_layout if s.kind == "q8" else None)
                     jobs.append((w, x, y))
                     self.y[s.name] = y
+                    self.plan_jobs.append((w, x, y))
+                    self.plan_phases.append(4 * l + pi)
                 self.calls.append(self._batched(jobs))
         for s, dw in zip(specs, self.w):
             if not s.name.startswith("L"):
@@ -176,6 +179,9 @@ class DecodeStep:
                 w = q.weight(dw, s.N, s.K, s.kind, s.q8_layout if s.kind == "q8" else None)
                 self.y[s.name] = y
                 self.calls.append(self._batched([(w, x, y)]))
+                self.plan_jobs.append((w, x, y))
+                self.plan_phases.append(4 * len(layers))
+        self.plan = q.Plan(self.plan_jobs, self.plan_phases, M)
 
     def _batched(self, jobs):
         M = self.M
@@ -195,12 +201,21 @@ class DecodeStep:
 
 
 def decode_leg(specs, tag, steps, warmup, graph, M=1):
+    """The step as one plan (persistent launch per chunk kind) and as phased launches."""
     step = DecodeStep(specs, tag, M)
-    ms, wall = time_calls(step.run, steps, warmup, graph)
+    ms, wall = time_calls(step.plan.run, steps, warmup, graph)
+    errs = step.plan.errors()
+    if errs:
+        raise RuntimeError(f"plan reported error flags {errs}")
     gbs = step.bytes / (ms * 1e-3) / 1e9
+    msp, _ = time_calls(step.run, steps, warmup, graph)
     res = {"ms_per_step": ms, "wall_ms_per_step": wall, "weight_bytes": step.bytes,
-           "GB_s": gbs, "pct_hbm_peak": 100 * gbs / HBM_PEAK_GBS, "launches": len(step.calls),
-           "graph": graph}
+           "GB_s": gbs, "pct_hbm_peak": 100 * gbs / HBM_PEAK_GBS,
+           "launches": 1 + sum(1 for a, b in zip(specs, specs[1:]) if a.kind != b.kind),
+           "phases": max(step.plan_phases) + 1,
+           "graph": graph, "plan_device_bytes": step.plan.nbytes(),
+           "phased_launches": {"ms_per_step": msp, "launches": len(step.calls),
+                               "GB_s": step.bytes / (msp * 1e-3) / 1e9}}
     return step, res
 
 
@@ -418,7 +433,8 @@ def main():
            "vs_baseline": None, "dtype": "f32", "data": "synthetic",
            "config": {"workload": "qwen3_4b_decode_step_q4_1", "layers": synth.QWEN3_4B_LAYERS,
                       "batch": 1, "lm_head": "151936x2560", "kind": "q4_1",
-                      "launches": "per layer q|k|v, o, gate|up, down batched GEMVs + lm_head",
+                      "phases": "per layer q|k|v, o, gate|up, down, then lm_head (145), each "
+                                "waiting for the previous one; one persistent launch",
                       "hip_graph": not args.no_graph},
            "device": torch.cuda.get_device_name(0)}
     graph = not args.no_graph
@@ -430,18 +446,15 @@ def main():
         out["ms_per_step"] = res["ms_per_step"]
         out["config"]["weight_bytes_per_step"] = res["weight_bytes"]
         out["pct_hbm_peak"] = res["pct_hbm_peak"]
-        legs["decode_stream_launch"] = {}
-        ms_s, _ = time_calls(step.run, args.steps, args.warmup, False)
-        legs["decode_stream_launch"] = {"ms_per_step": ms_s, "GB_s": res["weight_bytes"] / (ms_s * 1e-3) / 1e9}
-        # roofline of the dominant kernel (q4_1 GEMV, M = 1): bytes per launch / launch time
-        dur = per_launch_ms(step.calls, reps=3)
-        per_launch_bytes = res["weight_bytes"] / len(step.calls)
+        # roofline of the dominant kernel (the q4_1 M=1 plan kernel, one launch per step):
+        # algorithmic bytes per launch / its average duration, HIP events on its stream
+        dur = per_launch_ms([step.plan.run], reps=max(5, args.steps))
         avg_ms = sum(dur) / len(dur)
-        ach = per_launch_bytes / (avg_ms * 1e-3) / 1e9
+        ach = res["weight_bytes"] / (avg_ms * 1e-3) / 1e9
         out["roofline"] = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": ach / HBM_PEAK_GBS, "traffic": None,
-                           "kernel": "k_gemv_q4<q4_1, M=1>",
-                           "avg_launch_us": avg_ms * 1e3, "bytes_per_launch": per_launch_bytes,
+                           "kernel": "k_plan<q4_1, M=1>",
+                           "avg_launch_us": avg_ms * 1e3, "bytes_per_launch": res["weight_bytes"],
                            "launches_timed": len(dur)}
         legs["decode"] = res
         del step
@@ -457,7 +470,7 @@ def main():
                 head.generate = lambda orig=orig: synth.q8_relayout(orig(), "A", "B")
             st, r = decode_leg(ms, f"mixed_decode", args.steps, args.warmup, graph)
             head_i = len(st.calls) - 1
-            dur = per_launch_ms([st.calls[head_i]], reps=10)
+            dur = per_launch_ms([st.calls[head_i]], reps=10)   # the Q8 lm_head GEMV alone
             r["q8_lm_head_us"] = 1e3 * sum(dur) / len(dur)
             r["q8_lm_head_GB_s"] = ms[-1].nbytes / (sum(dur) / len(dur) * 1e-3) / 1e9
             legs[f"mixed_q4k_q8{lay}"] = r

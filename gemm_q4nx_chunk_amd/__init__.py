@@ -71,11 +71,20 @@ _lib.q4nx_moe_experts.argtypes = [ctypes.POINTER(MoeLayer), _P, _P, _P, _I, _I, 
                                   ctypes.POINTER(MoeDebug), _P, ctypes.c_size_t, _P]
 _lib.q4nx_unpack.argtypes = [ctypes.POINTER(Weight), _P, _P, _P, _P, _P]
 _lib.q4nx_decode.argtypes = [ctypes.POINTER(Weight), _P, _P]
+_lib.q4nx_plan_create.argtypes = [ctypes.POINTER(GemvJob), ctypes.POINTER(ctypes.c_int32), _I, _I,
+                                  ctypes.POINTER(ctypes.c_void_p)]
+_lib.q4nx_plan_run.argtypes = [_P, _P]
+_lib.q4nx_plan_errors.argtypes = [_P, ctypes.POINTER(ctypes.c_uint32)]
+_lib.q4nx_plan_bytes.argtypes = [_P]
+_lib.q4nx_plan_bytes.restype = ctypes.c_size_t
+_lib.q4nx_plan_destroy.argtypes = [_P]
+_lib.q4nx_plan_destroy.restype = None
 _lib.q4nx_status_str.argtypes = [_I]
 _lib.q4nx_status_str.restype = ctypes.c_char_p
 _lib.q4nx_last_error.restype = ctypes.c_char_p
 for _f in ("q4nx_weight_check", "q4nx_gemv", "q4nx_gemv_batched", "q4nx_gemm_block",
-           "q4nx_moe_experts", "q4nx_unpack", "q4nx_decode", "q4nx_version"):
+           "q4nx_moe_experts", "q4nx_unpack", "q4nx_decode", "q4nx_version", "q4nx_plan_create",
+           "q4nx_plan_run", "q4nx_plan_errors"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -129,10 +138,17 @@ def _stream(stream) -> int:
 
 def weight(chunks, rows: int, cols: int, kind: str, q8_layout: str | None = None,
            nbytes: int | None = None) -> Weight:
-    """Descriptor of a Q4NX weight held in ``chunks`` (a device tensor or a raw address)."""
-    return Weight(_ptr(chunks), _nbytes(chunks) if nbytes is None else nbytes, rows, cols,
-                  CHUNK_BYTES[kind] if isinstance(kind, str) else int(kind),
-                  Q8_LAYOUT[q8_layout] if q8_layout in Q8_LAYOUT else int(q8_layout))
+    """Descriptor of a Q4NX weight held in ``chunks`` (a device tensor or a raw address).
+
+    The descriptor keeps a reference to a tensor, so the memory stays allocated
+    for as long as the descriptor is alive.
+    """
+    w = Weight(_ptr(chunks), _nbytes(chunks) if nbytes is None else nbytes, rows, cols,
+               CHUNK_BYTES[kind] if isinstance(kind, str) else int(kind),
+               Q8_LAYOUT[q8_layout] if q8_layout in Q8_LAYOUT else int(q8_layout))
+    if not isinstance(chunks, int) and chunks is not None:
+        w._owner = chunks
+    return w
 
 
 def weight_check(w: Weight) -> int:
@@ -152,6 +168,41 @@ def gemv_batched(jobs, M: int = 1, stream=None) -> None:
     """jobs: sequence of (Weight, x, y); runs them as independent GEMVs."""
     arr = (GemvJob * len(jobs))(*[GemvJob(w, _ptr(x), _ptr(y)) for w, x, y in jobs])
     _check(_lib.q4nx_gemv_batched(arr, len(jobs), M, _stream(stream)))
+
+
+class Plan:
+    """A device-resident GEMV plan (q4nx_plan_*): jobs in phases, one launch per run."""
+
+    def __init__(self, jobs, phases, M: int = 1):
+        self._jobs = (GemvJob * len(jobs))(*[GemvJob(w, _ptr(x), _ptr(y)) for w, x, y in jobs])
+        self._keep = list(jobs)
+        ph = (ctypes.c_int32 * len(jobs))(*phases)
+        h = ctypes.c_void_p()
+        _check(_lib.q4nx_plan_create(self._jobs, ph, len(jobs), M, ctypes.byref(h)))
+        self.handle = h
+        self.M = M
+
+    def run(self, stream=None) -> None:
+        _check(_lib.q4nx_plan_run(self.handle, _stream(stream)))
+
+    def errors(self) -> int:
+        f = ctypes.c_uint32()
+        _check(_lib.q4nx_plan_errors(self.handle, ctypes.byref(f)))
+        return f.value
+
+    def nbytes(self) -> int:
+        return int(_lib.q4nx_plan_bytes(self.handle))
+
+    def close(self) -> None:
+        if self.handle:
+            _lib.q4nx_plan_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def gemm_block(w: Weight, X, Y, M: int, stream=None) -> None:
@@ -176,6 +227,7 @@ def moe_layer(n_experts: int, d_model: int, d_expert: int, kind: str, gate, up, 
     L.down_bytes = _nbytes(down) if down_bytes is None else down_bytes
     if shared is not None:
         L.sh_gate, L.sh_up, L.sh_down = shared
+    L._owners = (gate, up, down, shared)
     return L
 
 

@@ -8,11 +8,14 @@
 // chunk size or a tensor shorter than its layout needs).
 #include <cstdarg>
 #include <cstdio>
+#include <algorithm>
 #include <cstring>
 #include <string>
+#include <vector>
 
 #include "../../include/q4nx.h"
 #include "moe_args.h"
+#include "plan_args.h"
 #include "q4nx_dev.h"
 
 namespace {
@@ -202,6 +205,212 @@ int q4nx_gemm_block(const q4nx_weight* w, const uint16_t* X, float* Y, int M, vo
                                          w->rows / 32, w->cols / 256, M,
                                          static_cast<hipStream_t>(stream));
   return hip_status(e, "gemm_block launch");
+}
+
+// ---------------------------------------------------------------------------
+// plans
+// ---------------------------------------------------------------------------
+}  // extern "C"
+
+struct q4nx_plan_s {
+  struct Seg {
+    int kind, grid;
+    q4nx::PlanArgs args;
+  };
+  int M = 1;
+  std::vector<Seg> segs;
+  void* dev = nullptr;
+  size_t bytes = 0;
+  std::vector<uint32_t*> ctl;   // per segment control words (device)
+};
+
+namespace {
+
+constexpr int kPlanSpinLimit = 1 << 22;
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+}  // namespace
+
+extern "C" {
+
+int q4nx_plan_create(const q4nx_gemv_job* jobs, const int32_t* phase, int n_jobs, int M,
+                     q4nx_plan* out) {
+  if (!jobs || !phase || !out) return fail(Q4NX_E_ARG, "plan: null jobs, phase or out");
+  *out = nullptr;
+  if (n_jobs < 1 || n_jobs > 65536)
+    return fail(Q4NX_E_ARG, "plan: %d jobs outside 1..65536", n_jobs);
+  if (M < 1 || M > 4) return fail(Q4NX_E_ARG, "plan: M = %d outside 1..4", M);
+  for (int i = 0; i < n_jobs; ++i) {
+    char name[40];
+    snprintf(name, sizeof name, "plan job %d", i);
+    const int st = check_gemv_io(&jobs[i].w, jobs[i].x, jobs[i].y, M, name);
+    if (st) return st;
+    if (phase[i] < 0) return fail(Q4NX_E_ARG, "plan job %d: negative phase", i);
+  }
+  std::vector<int> order(n_jobs);
+  for (int i = 0; i < n_jobs; ++i) order[i] = i;
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return phase[a] < phase[b]; });
+  // segments: maximal runs of phases whose jobs share one kind
+  struct SegH {
+    int kind;
+    std::vector<int> jobs;
+    std::vector<int> phase_of;   // local phase of each job
+    int n_phases;
+  };
+  std::vector<SegH> segs;
+  for (size_t t = 0; t < order.size();) {
+    const int ph = phase[order[t]];
+    const int kind = kind_of(&jobs[order[t]].w);
+    size_t e = t;
+    while (e < order.size() && phase[order[e]] == ph) {
+      if (kind_of(&jobs[order[e]].w) != kind)
+        return fail(Q4NX_E_CHUNK_KIND, "plan: phase %d mixes chunk kinds", ph);
+      ++e;
+    }
+    if (segs.empty() || segs.back().kind != kind) segs.push_back({kind, {}, {}, 0});
+    SegH& sg = segs.back();
+    for (size_t i = t; i < e; ++i) {
+      sg.jobs.push_back(order[i]);
+      sg.phase_of.push_back(sg.n_phases);
+    }
+    ++sg.n_phases;
+    t = e;
+  }
+  // host tables and device layout
+  struct SegT {
+    std::vector<q4nx::PlanJob> pj;
+    std::vector<int32_t> unit_job;
+    std::vector<uint32_t> need;
+    int n_slots = 0, smax = 1;
+    size_t o_jobs, o_unit, o_need, o_done, o_cnt, o_part, o_ctl;
+  };
+  std::vector<SegT> tabs(segs.size());
+  size_t total = 0;
+  for (size_t si = 0; si < segs.size(); ++si) {
+    SegH& sg = segs[si];
+    SegT& T = tabs[si];
+    T.need.assign(sg.n_phases, 0);
+    const int cpw = q4nx::plan_cpw(sg.kind);
+    int units = 0;
+    for (size_t i = 0; i < sg.jobs.size(); ++i) {
+      const q4nx_gemv_job& j = jobs[sg.jobs[i]];
+      q4nx::PlanJob p;
+      p.w = static_cast<const uint8_t*>(j.w.chunks);
+      p.x = j.x;
+      p.y = j.y;
+      p.TR = j.w.rows / 32;
+      p.TC = j.w.cols / 256;
+      p.ldx = j.w.cols;
+      p.ldy = j.w.rows;
+      p.S = (p.TC + 4 * cpw - 1) / (4 * cpw);
+      p.unit0 = units;
+      p.phase = sg.phase_of[i];
+      p.slot0 = 0;
+      if (p.S > 1) {
+        p.slot0 = T.n_slots;
+        T.n_slots += p.TR;
+        T.smax = std::max(T.smax, p.S);
+      }
+      T.need[p.phase] += (uint32_t)p.TR;
+      for (int u = 0; u < p.TR * p.S; ++u) T.unit_job.push_back((int32_t)i);
+      units += p.TR * p.S;
+      T.pj.push_back(p);
+    }
+    T.o_jobs = total;  total = align256(total + T.pj.size() * sizeof(q4nx::PlanJob));
+    T.o_unit = total;  total = align256(total + T.unit_job.size() * 4);
+    T.o_need = total;  total = align256(total + T.need.size() * 4);
+    T.o_done = total;  total = align256(total + T.need.size() * 4);
+    T.o_cnt = total;   total = align256(total + (size_t)std::max(T.n_slots, 1) * 4);
+    T.o_part = total;  total = align256(total + (size_t)T.n_slots * T.smax * 32 * M * 4);
+    T.o_ctl = total;   total = align256(total + 16);
+  }
+  // check every kernel can be resident before allocating anything
+  std::vector<int> grids(segs.size());
+  for (size_t si = 0; si < segs.size(); ++si) {
+    int blocks = 0;
+    const hipError_t e = q4nx::plan_resident_blocks(segs[si].kind, M, &blocks);
+    if (e != hipSuccess) return hip_status(e, "plan occupancy");
+    if (blocks < 1) return fail(Q4NX_E_HIP, "plan: kernel cannot be resident");
+    grids[si] = std::min(blocks, (int)tabs[si].unit_job.size());
+  }
+  void* dev = nullptr;
+  hipError_t e = hipMalloc(&dev, total);
+  if (e != hipSuccess) return hip_status(e, "plan allocation");
+  std::vector<uint8_t> host(total, 0);
+  for (size_t si = 0; si < segs.size(); ++si) {
+    SegT& T = tabs[si];
+    memcpy(host.data() + T.o_jobs, T.pj.data(), T.pj.size() * sizeof(q4nx::PlanJob));
+    memcpy(host.data() + T.o_unit, T.unit_job.data(), T.unit_job.size() * 4);
+    memcpy(host.data() + T.o_need, T.need.data(), T.need.size() * 4);
+  }
+  e = hipMemcpy(dev, host.data(), total, hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    (void)hipFree(dev);
+    return hip_status(e, "plan upload");
+  }
+  q4nx_plan_s* plan = new q4nx_plan_s;
+  plan->M = M;
+  plan->dev = dev;
+  plan->bytes = total;
+  uint8_t* d = static_cast<uint8_t*>(dev);
+  for (size_t si = 0; si < segs.size(); ++si) {
+    SegT& T = tabs[si];
+    q4nx_plan_s::Seg s;
+    s.kind = segs[si].kind;
+    s.grid = grids[si];
+    s.args.jobs = reinterpret_cast<const q4nx::PlanJob*>(d + T.o_jobs);
+    s.args.unit_job = reinterpret_cast<const int32_t*>(d + T.o_unit);
+    s.args.need = reinterpret_cast<const uint32_t*>(d + T.o_need);
+    s.args.done = reinterpret_cast<uint32_t*>(d + T.o_done);
+    s.args.row_cnt = reinterpret_cast<uint32_t*>(d + T.o_cnt);
+    s.args.partial = reinterpret_cast<float*>(d + T.o_part);
+    s.args.ctl = reinterpret_cast<uint32_t*>(d + T.o_ctl);
+    s.args.n_units = (int32_t)T.unit_job.size();
+    s.args.n_phases = segs[si].n_phases;
+    s.args.spin_limit = kPlanSpinLimit;
+    s.args.smax = T.smax;
+    plan->segs.push_back(s);
+    plan->ctl.push_back(s.args.ctl);
+  }
+  *out = plan;
+  return ok();
+}
+
+int q4nx_plan_run(q4nx_plan plan, void* stream) {
+  if (!plan) return fail(Q4NX_E_ARG, "plan_run: null plan");
+  for (const auto& s : plan->segs) {
+    const hipError_t e = q4nx::launch_plan(s.kind, plan->M, s.args, s.grid,
+                                           static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_status(e, "plan launch");
+  }
+  return ok();
+}
+
+int q4nx_plan_errors(q4nx_plan plan, uint32_t* flags) {
+  if (!plan || !flags) return fail(Q4NX_E_ARG, "plan_errors: null argument");
+  uint32_t acc = 0;
+  for (uint32_t* c : plan->ctl) {
+    uint32_t v = 0;
+    hipError_t e = hipMemcpy(&v, c + 1, 4, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_status(e, "plan_errors read");
+    acc |= v;
+    if (v) {
+      const uint32_t zero = 0;
+      e = hipMemcpy(c + 1, &zero, 4, hipMemcpyHostToDevice);
+      if (e != hipSuccess) return hip_status(e, "plan_errors clear");
+    }
+  }
+  *flags = acc;
+  return ok();
+}
+
+size_t q4nx_plan_bytes(q4nx_plan plan) { return plan ? plan->bytes : 0; }
+
+void q4nx_plan_destroy(q4nx_plan plan) {
+  if (!plan) return;
+  if (plan->dev) (void)hipFree(plan->dev);
+  delete plan;
 }
 
 // ---------------------------------------------------------------------------

@@ -4,9 +4,9 @@
 // (32 weights) and writes its codes, metadata and fp32 weights in logical
 // [rows][cols] order.
 //
-// fp32 values: code*scale (q4_1), S*scale*code and M*min (Q4_K) and d*code
-// (Q8) are all exact in fp32, so one fma/mul gives the exact value rounded
-// once to nearest even.
+// fp32 values: q4_1 is one fma (exact product, one rounding); Q8's d*code is
+// exact; Q4_K sums two exact fp64 products and rounds (see below).  Each is the
+// exact value of the formula rounded once to nearest even.
 #include "q4nx_dev.h"
 
 namespace q4nx {
@@ -47,9 +47,14 @@ __global__ __launch_bounds__(256) void k_unpack(const uint8_t* __restrict__ w, i
       m1 = scmn >> 8;
       S = (uint16_t)(sm & 0xFFFFu);
       Mm = (uint16_t)(sm >> 16);
-      const float a = bf16lo(sm) * (float)m0, b = bf16hi(sm) * (float)m1;
+      // S*scale*code and M*min are exact in fp64, and their fp64 sum rounded to
+      // fp32 is the exact value rounded once (fp64 has more than 2*24+2 bits).
+      // fp32 products could overflow where the exact sum does not, so the test
+      // surface works in fp64 with explicit, uncontracted roundings.
+      const double a = __dmul_rn((double)bf16lo(sm), (double)m0);
+      const double b = __dmul_rn((double)bf16hi(sm), (double)m1);
 #pragma unroll
-      for (int j = 0; j < 32; ++j) val[j] = fmaf((float)c8[j], a, b);
+      for (int j = 0; j < 32; ++j) val[j] = (float)__dadd_rn(__dmul_rn(a, (double)c8[j]), b);
     }
   } else {
 #pragma unroll

@@ -11,7 +11,7 @@
 // waves of one tile row take contiguous runs of its chunks, and their partial
 // row sums meet in LDS, where one pass adds them in wave order.  No atomics:
 // the result bits do not depend on timing.
-#include "q4_core.h"
+#include "gemv_core.h"
 
 namespace q4nx {
 
@@ -61,25 +61,6 @@ __global__ __launch_bounds__(256) void k_gemv_q4(const GemvBatch b) {
   }
 }
 
-// ===========================================================================
-// Q8 (both code layouts)
-// ===========================================================================
-// A 16-byte piece of Q8 codes is 16 rows of one column in either layout.
-// Lane l = 8g + 4h + j takes, in every chunk, the 8 pieces of group g, row half
-// h (rows 16h .. 16h+15), columns k = 32g + 8j + i (i = 0..7):
-//   layout A (byte k*32 + r):  1024 g + 256 j + 32 i + 16 h
-//   layout B ((r/16)*4096 + (k/32)*512 + (k%32)*16 + r%16):  4096 h + 512 g + 128 j + 16 i
-// It forms part[rho] = sum_i code(16h+rho, k) * x[k] for its 8 columns, then
-// adds d(16h+rho, g) * part[rho]; the 32 lanes of one row half meet at the end.
-// Every product of an int8 code and a bf16 is exact in fp32.
-
-template <int KIND>
-__device__ __forceinline__ int q8_piece(int lane, int i) {
-  const int j = lane & 3, h = (lane >> 2) & 1, g = lane >> 3;
-  if constexpr (KIND == KIND_Q8_A) return 1024 * g + 256 * j + 32 * i + 16 * h;
-  else return 4096 * h + 512 * g + 128 * j + 16 * i;
-}
-
 template <int KIND, int M>
 __global__ __launch_bounds__(256) void k_gemv_q8(const GemvBatch b) {
   constexpr int CB = 8704;
@@ -90,7 +71,7 @@ __global__ __launch_bounds__(256) void k_gemv_q8(const GemvBatch b) {
   const int slot = wave / ks, part_id = wave % ks;
   const int tr0 = (blockIdx.x - J.wg_begin) * rpw;
   const int tr = tr0 + slot;
-  const int j = lane & 3, h = (lane >> 2) & 1, g = lane >> 3;
+  const int h = (lane >> 2) & 1;
 
   float acc[16][M];
 #pragma unroll
@@ -100,65 +81,9 @@ __global__ __launch_bounds__(256) void k_gemv_q8(const GemvBatch b) {
 
   if (tr < J.TR) {
     const int c0 = part_id * J.TC / ks, c1 = (part_id + 1) * J.TC / ks;
-    const uint8_t* row = J.w + (size_t)tr * J.TC * CB;
-    const int dbase = 8192 + 256 * h + 2 * g;   // d(16h + rho, g) at dbase + 16*rho
-    for (int c = c0; c < c1; ++c) {
-      const uint8_t* ck = row + (size_t)c * CB;
-      u32x4 pc[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) pc[i] = load_nt16(ck + q8_piece<KIND>(lane, i));
-      float xf[M][8];
-#pragma unroll
-      for (int m = 0; m < M; ++m) {
-        const u32x4 v = load16(J.x + (size_t)m * J.ldx + 256 * c + 32 * g + 8 * j);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          xf[m][2 * t] = bf16lo(v[t]);
-          xf[m][2 * t + 1] = bf16hi(v[t]);
-        }
-      }
-      uint32_t dv[8];
-#pragma unroll
-      for (int rr = 0; rr < 8; ++rr) {
-        const uint32_t lo = *reinterpret_cast<const uint16_t*>(ck + dbase + 32 * rr);
-        const uint32_t hi = *reinterpret_cast<const uint16_t*>(ck + dbase + 32 * rr + 16);
-        dv[rr] = lo | (hi << 16);
-      }
-      float part[16][M];
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-#pragma unroll
-        for (int m = 0; m < M; ++m) part[r][m] = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float cf = (float)(int8_t)(pc[i][r >> 2] >> (8 * (r & 3)));
-#pragma unroll
-          for (int m = 0; m < M; ++m) part[r][m] = fmaf(cf, xf[m][i], part[r][m]);
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float d = (r & 1) ? bf16hi(dv[r >> 1]) : bf16lo(dv[r >> 1]);
-#pragma unroll
-        for (int m = 0; m < M; ++m) acc[r][m] = fmaf(d, part[r][m], acc[r][m]);
-      }
-    }
+    q8_row_partial<KIND, M>(J.w + (size_t)tr * J.TC * CB, c0, c1, J.x, J.ldx, lane, acc);
   }
-
-#pragma unroll
-  for (int r = 0; r < 16; ++r)
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-      float v = acc[r][m];
-      v += __shfl_xor(v, 1);
-      v += __shfl_xor(v, 2);
-      v += __shfl_xor(v, 8);
-      v += __shfl_xor(v, 16);
-      v += __shfl_xor(v, 32);
-      acc[r][m] = v;
-    }
+  q8_lane_reduce<M>(acc);
   if ((lane & ~4) == 0) {
 #pragma unroll
     for (int r = 0; r < 16; ++r)

@@ -1,4 +1,4 @@
-// The q4_1 / Q4_K dequant-GEMV core shared by the GEMV and MoE kernels.
+// The dequant-GEMV cores (q4_1 / Q4_K and Q8) shared by the GEMV, plan and MoE kernels.
 #pragma once
 
 #include "q4nx_dev.h"
@@ -110,6 +110,116 @@ __device__ __forceinline__ void q4_compute(const Q4Chunk<KIND>& c, const XPrep<M
       acc[i][m] = fmaf(s, D - xp.d136[m], fmaf(zz, xp.sum[m], acc[i][m]));
     }
   }
+}
+
+// ===========================================================================
+// Q8 (both code layouts)
+// ===========================================================================
+// A 16-byte piece of Q8 codes is 16 rows of one column in either layout.
+// Lane l = 8g + 4h + j takes, in every chunk, the 8 pieces of group g, row half
+// h (rows 16h .. 16h+15), columns k = 32g + 8j + i (i = 0..7):
+//   layout A (byte k*32 + r):  1024 g + 256 j + 32 i + 16 h
+//   layout B ((r/16)*4096 + (k/32)*512 + (k%32)*16 + r%16):  4096 h + 512 g + 128 j + 16 i
+// It forms part[rho] = sum_i code(16h+rho, k) * x[k] for its 8 columns, then
+// adds d(16h+rho, g) * part[rho]; the 32 lanes of one row half meet at the end.
+// Every product of an int8 code and a bf16 is exact in fp32.
+
+template <int KIND>
+__device__ __forceinline__ int q8_piece(int lane, int i) {
+  const int j = lane & 3, h = (lane >> 2) & 1, g = lane >> 3;
+  if constexpr (KIND == KIND_Q8_A) return 1024 * g + 256 * j + 32 * i + 16 * h;
+  else return 4096 * h + 512 * g + 128 * j + 16 * i;
+}
+
+struct Q8Chunk {
+  u32x4 pc[8];     // the lane's 8 pieces: 16 rows x 1 column each
+  uint32_t dv[8];  // d(16h + rho, g), two per word
+};
+
+__device__ __forceinline__ int q8_dbase(int lane) {
+  return 8192 + 256 * ((lane >> 2) & 1) + 2 * (lane >> 3);   // d(16h + rho, g) at dbase + 16*rho
+}
+
+template <int KIND>
+__device__ __forceinline__ void q8_load(const uint8_t* __restrict__ ck, int lane, Q8Chunk& c) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c.pc[i] = load_nt16(ck + q8_piece<KIND>(lane, i));
+  const int dbase = q8_dbase(lane);
+#pragma unroll
+  for (int rr = 0; rr < 8; ++rr) {
+    const uint32_t lo = *reinterpret_cast<const uint16_t*>(ck + dbase + 32 * rr);
+    const uint32_t hi = *reinterpret_cast<const uint16_t*>(ck + dbase + 32 * rr + 16);
+    c.dv[rr] = lo | (hi << 16);
+  }
+}
+
+// Adds chunk (tile column) c of the lane's rows into acc.  x points at
+// activation row 0, column 0; ldx is the activation row stride.
+template <int M>
+__device__ __forceinline__ void q8_compute(const Q8Chunk& ch, const uint16_t* __restrict__ x,
+                                           int ldx, int c, int lane, float (&acc)[16][M]) {
+  const int j = lane & 3, g = lane >> 3;
+  float xf[M][8];
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const u32x4 v = load16(x + (size_t)m * ldx + 256 * c + 32 * g + 8 * j);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      xf[m][2 * t] = bf16lo(v[t]);
+      xf[m][2 * t + 1] = bf16hi(v[t]);
+    }
+  }
+  float part[16][M];
+#pragma unroll
+  for (int r = 0; r < 16; ++r)
+#pragma unroll
+    for (int m = 0; m < M; ++m) part[r][m] = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float cf = (float)(int8_t)(ch.pc[i][r >> 2] >> (8 * (r & 3)));
+#pragma unroll
+      for (int m = 0; m < M; ++m) part[r][m] = fmaf(cf, xf[m][i], part[r][m]);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const float d = (r & 1) ? bf16hi(ch.dv[r >> 1]) : bf16lo(ch.dv[r >> 1]);
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[r][m] = fmaf(d, part[r][m], acc[r][m]);
+  }
+}
+
+// Partial sums of one tile row over chunks [c0, c1): acc[rho][m] of lane l
+// belongs to row 16h + rho (h = bit 2 of l), over the lane's 8 columns of each
+// chunk; q8_lane_reduce sums the 32 lanes of each row half.
+template <int KIND, int M>
+__device__ __forceinline__ void q8_row_partial(const uint8_t* __restrict__ row, int c0, int c1,
+                                               const uint16_t* __restrict__ x, int ldx, int lane,
+                                               float (&acc)[16][M]) {
+  for (int c = c0; c < c1; ++c) {
+    Q8Chunk ch;
+    q8_load<KIND>(row + (size_t)c * 8704, lane, ch);
+    q8_compute<M>(ch, x, ldx, c, lane, acc);
+  }
+}
+
+// Sum over the 32 lanes of each row half (lane bits 0, 1, 3, 4, 5).
+template <int M>
+__device__ __forceinline__ void q8_lane_reduce(float (&acc)[16][M]) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r)
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      float v = acc[r][m];
+      v += __shfl_xor(v, 1);
+      v += __shfl_xor(v, 2);
+      v += __shfl_xor(v, 8);
+      v += __shfl_xor(v, 16);
+      v += __shfl_xor(v, 32);
+      acc[r][m] = v;
+    }
 }
 
 // Partial sums of one tile row over chunks [c0, c1) for M activation rows.

@@ -18,7 +18,7 @@
 //   down    per (token batch, group of tile rows): d = Down h, fp32.
 //   combine y[t] = sum_j p[t][j] d[t][j] in slot order, then + the shared d.
 // No floating-point atomics anywhere; every sum has a fixed order.
-#include "q4_core.h"
+#include "gemv_core.h"
 #include "moe_args.h"
 
 namespace q4nx {

@@ -29,8 +29,10 @@
  *   Q8:   d bf16 of (r, g) at 8192 + 2*(8r + g).
  *
  * Conventions of every call:
- *  - Pointers marked DEVICE are device memory owned by the caller; the library
- *    keeps no pointer after a call returns and allocates no memory.
+ *  - Pointers marked DEVICE are device memory owned by the caller.  Only a
+ *    plan (q4nx_plan_create) keeps pointers past the call that takes them, and
+ *    only q4nx_plan_create allocates device memory; every other call keeps
+ *    nothing and allocates nothing.
  *  - Calls that take a stream enqueue work on it and return without waiting;
  *    the caller synchronises before reading results.  `stream` is a
  *    hipStream_t passed as void* (NULL = the default stream).
@@ -131,6 +133,44 @@ typedef struct q4nx_gemv_job {
  * Errors as q4nx_gemv, checked for every job before anything is enqueued.
  */
 int q4nx_gemv_batched(const q4nx_gemv_job* jobs, int n_jobs, int M, void* stream);
+
+/*
+ * A GEMV plan: a whole decode step in one launch (per chunk kind present).
+ *
+ * A decode step is a chain of GEMV groups that depend on each other (per
+ * layer q|k|v, o, gate|up, down, then the lm_head); run as separate launches,
+ * each short kernel pays its own start and drain and the weight stream stalls
+ * between them (Strata article, section 3.2, runs its whole 48-layer pass as
+ * one captured graph for this reason).  A plan runs every job of phase p only
+ * after every job of phase p-1 has written its y, but issues each unit's
+ * weight loads before that wait, so weight streaming continues across the
+ * phase boundaries.
+ *
+ *   jobs    HOST array of n_jobs GEMVs (copied into the plan; the weights, x
+ *           and y they point at must stay allocated while the plan is used)
+ *   phase   HOST array of n_jobs phase numbers >= 0; a job's x may be written
+ *           by jobs of lower phases; jobs of one phase must share a chunk kind
+ *   n_jobs  1..65536;  M 1..4
+ *   out     receives the plan handle
+ * q4nx_plan_create allocates the plan's device tables (hipMalloc) and copies
+ * them (synchronously); it is the only allocating call of the library.
+ * q4nx_plan_run enqueues one persistent launch per run of same-kind phases;
+ * it allocates nothing and may be captured in a HIP graph.  Runs of one plan
+ * must not overlap each other, and the launch assumes the whole GPU: it sizes
+ * its grid to stay resident.  If a phase wait ever exceeds its spin limit (a
+ * grid that could not become resident), the kernel sets an error flag instead
+ * of hanging; q4nx_plan_errors reads and clears it (synchronous).
+ */
+typedef struct q4nx_plan_s* q4nx_plan;
+
+int q4nx_plan_create(const q4nx_gemv_job* jobs, const int32_t* phase, int n_jobs, int M,
+                     q4nx_plan* out);
+int q4nx_plan_run(q4nx_plan plan, void* stream);
+/* flags: bit 0 = a phase wait timed out.  Returns Q4NX_OK or Q4NX_E_HIP. */
+int q4nx_plan_errors(q4nx_plan plan, uint32_t* flags);
+/* Device bytes the plan holds (tables, counters, partial rows). */
+size_t q4nx_plan_bytes(q4nx_plan plan);
+void q4nx_plan_destroy(q4nx_plan plan);
 
 /*
  * Y[m][n] = sum_k W[n][k] * X[m][k] for a prompt block of M <= 64 rows (onw

@@ -155,3 +155,31 @@ def test_unpack_decode_checks(q):
     _expect(q, q.E_ALIGN, q.unpack, _w(q), 0x1000, 0x2001, stream=0)
     _expect(q, q.E_ARG, q.decode, _w(q), 0, stream=0)
     _expect(q, q.E_ALIGN, q.decode, _w(q), 0x1002, stream=0)
+
+
+def test_plan_create_checks(q):
+    good = (_w(q), 0x2000, 0x3000)
+    lib = q.lib()
+
+    def create(jobs, phases, M=1):
+        arr = (q.GemvJob * len(jobs))(*[q.GemvJob(w, x, y) for w, x, y in jobs])
+        ph = (ctypes.c_int32 * len(phases))(*phases)
+        h = ctypes.c_void_p()
+        return lib.q4nx_plan_create(arr, ph, len(jobs), M, ctypes.byref(h)), h
+    assert create([good], [0], M=5)[0] == q.E_ARG
+    assert create([good], [0], M=0)[0] == q.E_ARG
+    assert create([good], [-1])[0] == q.E_ARG
+    assert create([good, (_w(q, kind="q8", layout="A"), 0x2000, 0x3000)], [0, 0])[0] == q.E_CHUNK_KIND
+    assert "mixes" in q.last_error()
+    assert create([good, (_w(q, kind=77, nbytes=10 ** 6), 0x2000, 0x3000)], [0, 1])[0] == q.E_CHUNK_KIND
+    assert lib.q4nx_plan_create(None, None, 0, 1, None) == q.E_ARG
+    assert lib.q4nx_plan_run(None, None) == q.E_ARG
+    assert q.lib().q4nx_plan_bytes(None) == 0
+    lib.q4nx_plan_destroy(None)
+
+
+def test_descriptor_keeps_its_tensor_alive(q):
+    torch = pytest.importorskip("torch")
+    t = torch.zeros(2 * 2 * 5120, dtype=torch.uint8)
+    w = q.weight(t, 64, 512, "q4_1")
+    assert w._owner is t and q.weight_check(w) == q.Q4NX_OK
