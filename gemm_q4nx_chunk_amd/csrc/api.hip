@@ -74,13 +74,33 @@ int check_weight(const q4nx_weight* w, const char* name) {
   return Q4NX_OK;
 }
 
-int pick_ks_total(int64_t total_tr) {
-  if (total_tr >= 2048) return 1;
-  if (total_tr >= 1024) return 2;
-  return 4;
+// Launch shape of a batch.  Many tile rows: 4-wave workgroups, waves per tile
+// row chosen so the launch has about 2048 waves; each wave streams a run of
+// chunks.  Few tile rows of long K (more than 16 tile columns): the launch is
+// latency-bound on each wave's run of chunks, so 16-wave workgroups spread a
+// tile row over enough waves that every wave holds about two chunks.  (Measured
+// on the decode shapes: this halves the time of a 2560 x 9728 GEMV and slows
+// the K = 2560 and K = 4096 ones, which keep 4-wave workgroups.)
+#ifndef Q4NX_SMALL_ROWS
+#define Q4NX_SMALL_ROWS 1024
+#endif
+#ifndef Q4NX_SMALL_CPW
+#define Q4NX_SMALL_CPW 2
+#endif
+
+int pow2_at_least(int v, int cap) {
+  int p = 1;
+  while (p < v && p < cap) p <<= 1;
+  return p;
 }
 
-int cap_ks(int ks, int TC) {
+int pick_waves(int64_t total_tr, int M, int max_tc) {
+  return (total_tr >= Q4NX_SMALL_ROWS || M > 2 || max_tc <= 16) ? 4 : 16;
+}
+
+int pick_ks(int waves, int64_t total_tr, int TC) {
+  if (waves == 16) return pow2_at_least((TC + Q4NX_SMALL_CPW - 1) / Q4NX_SMALL_CPW, 16);
+  int ks = total_tr >= 2048 ? 1 : (total_tr >= 1024 ? 2 : 4);
   const int lim = TC >= 4 ? 4 : (TC >= 2 ? 2 : 1);
   return ks < lim ? ks : lim;
 }
@@ -89,8 +109,12 @@ int cap_ks(int ks, int TC) {
 // table allows.
 int run_batch(int kind, const q4nx_gemv_job* const* jobs, int n, int M, hipStream_t s) {
   int64_t total_tr = 0;
-  for (int i = 0; i < n; ++i) total_tr += jobs[i]->w.rows / 32;
-  const int ks_all = pick_ks_total(total_tr);
+  int max_tc = 0;
+  for (int i = 0; i < n; ++i) {
+    total_tr += jobs[i]->w.rows / 32;
+    max_tc = std::max(max_tc, jobs[i]->w.cols / 256);
+  }
+  const int waves = pick_waves(total_tr, M, max_tc);
   for (int i0 = 0; i0 < n; i0 += q4nx::kMaxBatch) {
     const int cnt = n - i0 < q4nx::kMaxBatch ? n - i0 : q4nx::kMaxBatch;
     q4nx::GemvBatch b;
@@ -106,13 +130,13 @@ int run_batch(int kind, const q4nx_gemv_job* const* jobs, int n, int M, hipStrea
       g.TC = j->w.cols / 256;
       g.ldx = j->w.cols;
       g.ldy = j->w.rows;
-      g.ks = cap_ks(ks_all, g.TC);
+      g.ks = pick_ks(waves, total_tr, g.TC);
       g.wg_begin = wg;
-      const int rpw = 4 / g.ks;
+      const int rpw = waves / g.ks;
       wg += (g.TR + rpw - 1) / rpw;
     }
     b.n_jobs = cnt;
-    const hipError_t e = q4nx::launch_gemv(kind, M, b, wg, s);
+    const hipError_t e = q4nx::launch_gemv(kind, M, waves, b, wg, s);
     if (e != hipSuccess) return hip_status(e, "gemv launch");
   }
   return Q4NX_OK;

@@ -7,20 +7,22 @@
 // registers, unpacks and scales in registers, and leaves the ALU work per
 // weight small enough to hide under the stream.
 //
-// Work split: a 256-thread workgroup (4 waves) owns 4/ks tile rows; the ks
-// waves of one tile row take contiguous runs of its chunks, and their partial
-// row sums meet in LDS, where one pass adds them in wave order.  No atomics:
-// the result bits do not depend on timing.
+// Work split: a workgroup of WAVES waves (4 for launches with many tile rows,
+// 16 for small ones, where latency rather than bandwidth sets the time) owns
+// WAVES/ks tile rows; the ks waves of one tile row take contiguous runs of its
+// chunks, and their partial row sums meet in LDS, where one pass adds them in
+// wave order.  No atomics: the result bits do not depend on timing.
 #include "gemv_core.h"
 
 namespace q4nx {
 
-template <int KIND, int M>
-__global__ __launch_bounds__(256) void k_gemv_q4(const GemvBatch b) {
+template <int KIND, int M, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void k_gemv_q4(const GemvBatch b) {
   constexpr int CB = ChunkBytes<KIND>::value;
-  __shared__ float red[4][32][M];
+  constexpr int D = WAVES == 4 ? Q4Depth<M>::value : (M == 1 ? 2 : 1);
+  __shared__ float red[WAVES][32][M];
   const GemvJob& J = b.job[find_job(b, blockIdx.x)];
-  const int ks = J.ks, rpw = 4 / ks;
+  const int ks = J.ks, rpw = WAVES / ks;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int slot = wave / ks, part = wave % ks;
   const int tr0 = (blockIdx.x - J.wg_begin) * rpw;
@@ -38,7 +40,7 @@ __global__ __launch_bounds__(256) void k_gemv_q4(const GemvBatch b) {
     const uint16_t* xrow[M];
 #pragma unroll
     for (int m = 0; m < M; ++m) xrow[m] = J.x + (size_t)m * J.ldx;
-    q4_row_partial<KIND, M>(J.w + (size_t)tr * J.TC * CB, c0, c1, xrow, lane, acc);
+    q4_row_partial<KIND, M, D>(J.w + (size_t)tr * J.TC * CB, c0, c1, xrow, lane, acc);
   }
 
   q4_lane_reduce<M>(acc);
@@ -49,7 +51,7 @@ __global__ __launch_bounds__(256) void k_gemv_q4(const GemvBatch b) {
       for (int m = 0; m < M; ++m) red[wave][8 * i + (lane >> 3)][m] = acc[i][m];
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < rpw * 32 * M; idx += 256) {
+  for (int idx = threadIdx.x; idx < rpw * 32 * M; idx += 64 * WAVES) {
     const int s = idx / (32 * M), rem = idx - s * 32 * M;
     const int r = rem / M, m = rem - r * M;
     const int t = tr0 + s;
@@ -61,12 +63,12 @@ __global__ __launch_bounds__(256) void k_gemv_q4(const GemvBatch b) {
   }
 }
 
-template <int KIND, int M>
-__global__ __launch_bounds__(256) void k_gemv_q8(const GemvBatch b) {
+template <int KIND, int M, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void k_gemv_q8(const GemvBatch b) {
   constexpr int CB = 8704;
-  __shared__ float red[4][32][M];
+  __shared__ float red[WAVES][32][M];
   const GemvJob& J = b.job[find_job(b, blockIdx.x)];
-  const int ks = J.ks, rpw = 4 / ks;
+  const int ks = J.ks, rpw = WAVES / ks;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int slot = wave / ks, part_id = wave % ks;
   const int tr0 = (blockIdx.x - J.wg_begin) * rpw;
@@ -91,7 +93,7 @@ __global__ __launch_bounds__(256) void k_gemv_q8(const GemvBatch b) {
       for (int m = 0; m < M; ++m) red[wave][16 * h + r][m] = acc[r][m];
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < rpw * 32 * M; idx += 256) {
+  for (int idx = threadIdx.x; idx < rpw * 32 * M; idx += 64 * WAVES) {
     const int s = idx / (32 * M), rem = idx - s * 32 * M;
     const int r = rem / M, m = rem - r * M;
     const int t = tr0 + s;
@@ -106,36 +108,59 @@ __global__ __launch_bounds__(256) void k_gemv_q8(const GemvBatch b) {
 // ===========================================================================
 // launcher
 // ===========================================================================
-template <int KIND, int M>
+template <int KIND, int M, int WAVES>
 static hipError_t launch_one(const GemvBatch& b, int n_wg, hipStream_t s) {
   if constexpr (KIND == KIND_Q4_1 || KIND == KIND_Q4_K)
-    hipLaunchKernelGGL((k_gemv_q4<KIND, M>), dim3(n_wg), dim3(256), 0, s, b);
+    hipLaunchKernelGGL((k_gemv_q4<KIND, M, WAVES>), dim3(n_wg), dim3(64 * WAVES), 0, s, b);
   else
-    hipLaunchKernelGGL((k_gemv_q8<KIND, M>), dim3(n_wg), dim3(256), 0, s, b);
+    hipLaunchKernelGGL((k_gemv_q8<KIND, M, WAVES>), dim3(n_wg), dim3(64 * WAVES), 0, s, b);
   return hipGetLastError();
 }
 
-template <int KIND>
+template <int KIND, int WAVES>
 static hipError_t launch_m(int M, const GemvBatch& b, int n_wg, hipStream_t s) {
   switch (M) {
-    case 1: return launch_one<KIND, 1>(b, n_wg, s);
-    case 2: return launch_one<KIND, 2>(b, n_wg, s);
-    case 3: return launch_one<KIND, 3>(b, n_wg, s);
-    case 4: return launch_one<KIND, 4>(b, n_wg, s);
-    case 5: return launch_one<KIND, 5>(b, n_wg, s);
-    case 6: return launch_one<KIND, 6>(b, n_wg, s);
-    case 7: return launch_one<KIND, 7>(b, n_wg, s);
-    case 8: return launch_one<KIND, 8>(b, n_wg, s);
+    case 1: return launch_one<KIND, 1, WAVES>(b, n_wg, s);
+    case 2: return launch_one<KIND, 2, WAVES>(b, n_wg, s);
+    case 3: return launch_one<KIND, 3, WAVES>(b, n_wg, s);
+    case 4: return launch_one<KIND, 4, WAVES>(b, n_wg, s);
+    case 5: return launch_one<KIND, 5, WAVES>(b, n_wg, s);
+    case 6: return launch_one<KIND, 6, WAVES>(b, n_wg, s);
+    case 7: return launch_one<KIND, 7, WAVES>(b, n_wg, s);
+    case 8: return launch_one<KIND, 8, WAVES>(b, n_wg, s);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_gemv(int kind, int M, const GemvBatch& b, int n_wg, hipStream_t s) {
+template <int WAVES>
+static hipError_t launch_w(int kind, int M, const GemvBatch& b, int n_wg, hipStream_t s) {
   switch (kind) {
-    case KIND_Q4_1: return launch_m<KIND_Q4_1>(M, b, n_wg, s);
-    case KIND_Q4_K: return launch_m<KIND_Q4_K>(M, b, n_wg, s);
-    case KIND_Q8_A: return launch_m<KIND_Q8_A>(M, b, n_wg, s);
-    case KIND_Q8_B: return launch_m<KIND_Q8_B>(M, b, n_wg, s);
+    case KIND_Q4_1: return launch_m<KIND_Q4_1, WAVES>(M, b, n_wg, s);
+    case KIND_Q4_K: return launch_m<KIND_Q4_K, WAVES>(M, b, n_wg, s);
+    case KIND_Q8_A: return launch_m<KIND_Q8_A, WAVES>(M, b, n_wg, s);
+    case KIND_Q8_B: return launch_m<KIND_Q8_B, WAVES>(M, b, n_wg, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int KIND>
+static hipError_t launch_small(int M, const GemvBatch& b, int n_wg, hipStream_t s) {
+  if (M == 1) return launch_one<KIND, 1, 16>(b, n_wg, s);
+  if (M == 2) return launch_one<KIND, 2, 16>(b, n_wg, s);
+  return hipErrorInvalidValue;
+}
+
+// 16-wave workgroups hold at most 128 registers per lane, so they are used
+// for M <= 2 only.
+hipError_t launch_gemv(int kind, int M, int waves, const GemvBatch& b, int n_wg, hipStream_t s) {
+  if (waves == 4) return launch_w<4>(kind, M, b, n_wg, s);
+  if (waves == 16 && M <= 2) {
+    switch (kind) {
+      case KIND_Q4_1: return launch_small<KIND_Q4_1>(M, b, n_wg, s);
+      case KIND_Q4_K: return launch_small<KIND_Q4_K>(M, b, n_wg, s);
+      case KIND_Q8_A: return launch_small<KIND_Q8_A>(M, b, n_wg, s);
+      case KIND_Q8_B: return launch_small<KIND_Q8_B>(M, b, n_wg, s);
+    }
   }
   return hipErrorInvalidValue;
 }

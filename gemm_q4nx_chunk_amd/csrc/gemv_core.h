@@ -57,14 +57,41 @@ struct XPrep {
   float d136[M];
 };
 
+// The lane's 32 activations of one tile column, as loaded (bf16 pairs, k order).
 template <int M>
-__device__ __forceinline__ void x_prep(const uint16_t* const (&xrow)[M], int col, XPrep<M>& xp) {
+struct XRaw {
+  u32x4 v[M][4];
+};
+
+template <int M>
+__device__ __forceinline__ void x_raw(const uint16_t* const (&xrow)[M], int col, XRaw<M>& r) {
+#pragma unroll
+  for (int m = 0; m < M; ++m)
+#pragma unroll
+    for (int d = 0; d < 4; ++d) r.v[m][d] = load16(xrow[m] + col + 8 * d);
+}
+
+// Coherent variant for activations written by other workgroups of the same
+// launch: device-scope (sc1) buffer loads, which read past this XCD's L2.
+// xoff[m] is the byte offset of the lane's group in row m; rsrc covers x.
+template <int M>
+__device__ __forceinline__ void x_raw_coherent(__amdgpu_buffer_rsrc_t rsrc, const int (&xoff)[M],
+                                               int col, XRaw<M>& r) {
+#pragma unroll
+  for (int m = 0; m < M; ++m)
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+      r.v[m][d] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                rsrc, xoff[m] + 2 * (col + 8 * d), 0, kCpolSc1));
+}
+
+template <int M>
+__device__ __forceinline__ void x_prep_raw(const XRaw<M>& r, XPrep<M>& xp) {
 #pragma unroll
   for (int m = 0; m < M; ++m) {
-    const uint16_t* xc = xrow[m] + col;
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      const u32x4 v = load16(xc + 8 * d);   // x[8d .. 8d+7] of the group, bf16 pairs
+      const u32x4 v = r.v[m][d];   // x[8d .. 8d+7] of the group, bf16 pairs
       // v_perm_b32 byte select: 0..3 pick bytes of the second operand, 4..7 of the first.
       xp.p[m][4 * d + 0] = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);   // (x0, x4)
       xp.p[m][4 * d + 1] = __builtin_amdgcn_perm(v.z, v.x, 0x07060302u);   // (x1, x5)
@@ -77,6 +104,13 @@ __device__ __forceinline__ void x_prep(const uint16_t* const (&xrow)[M], int col
     xp.d136[m] = e;
     xp.sum[m] = e / 136.0f;
   }
+}
+
+template <int M>
+__device__ __forceinline__ void x_prep(const uint16_t* const (&xrow)[M], int col, XPrep<M>& xp) {
+  XRaw<M> r;
+  x_raw<M>(xrow, col, r);
+  x_prep_raw<M>(r, xp);
 }
 
 template <int KIND, int M>
@@ -153,20 +187,27 @@ __device__ __forceinline__ void q8_load(const uint8_t* __restrict__ ck, int lane
   }
 }
 
-// Adds chunk (tile column) c of the lane's rows into acc.  x points at
-// activation row 0, column 0; ldx is the activation row stride.
+// The lane's 8 activations of one Q8 chunk (k = 32g + 8j .. +7), as loaded.
 template <int M>
-__device__ __forceinline__ void q8_compute(const Q8Chunk& ch, const uint16_t* __restrict__ x,
-                                           int ldx, int c, int lane, float (&acc)[16][M]) {
-  const int j = lane & 3, g = lane >> 3;
+struct Q8XRaw {
+  u32x4 v[M];
+};
+
+__device__ __forceinline__ int q8_xcol(int lane, int c) {
+  return 256 * c + 32 * (lane >> 3) + 8 * (lane & 3);
+}
+
+// Adds the chunk's products into acc, given the lane's activations.
+template <int M>
+__device__ __forceinline__ void q8_compute_raw(const Q8Chunk& ch, const Q8XRaw<M>& xr,
+                                               float (&acc)[16][M]) {
   float xf[M][8];
 #pragma unroll
   for (int m = 0; m < M; ++m) {
-    const u32x4 v = load16(x + (size_t)m * ldx + 256 * c + 32 * g + 8 * j);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      xf[m][2 * t] = bf16lo(v[t]);
-      xf[m][2 * t + 1] = bf16hi(v[t]);
+      xf[m][2 * t] = bf16lo(xr.v[m][t]);
+      xf[m][2 * t + 1] = bf16hi(xr.v[m][t]);
     }
   }
   float part[16][M];
@@ -191,6 +232,17 @@ __device__ __forceinline__ void q8_compute(const Q8Chunk& ch, const uint16_t* __
   }
 }
 
+// Adds chunk (tile column) c of the lane's rows into acc.  x points at
+// activation row 0, column 0; ldx is the activation row stride.
+template <int M>
+__device__ __forceinline__ void q8_compute(const Q8Chunk& ch, const uint16_t* __restrict__ x,
+                                           int ldx, int c, int lane, float (&acc)[16][M]) {
+  Q8XRaw<M> xr;
+#pragma unroll
+  for (int m = 0; m < M; ++m) xr.v[m] = load16(x + (size_t)m * ldx + q8_xcol(lane, c));
+  q8_compute_raw<M>(ch, xr, acc);
+}
+
 // Partial sums of one tile row over chunks [c0, c1): acc[rho][m] of lane l
 // belongs to row 16h + rho (h = bit 2 of l), over the lane's 8 columns of each
 // chunk; q8_lane_reduce sums the 32 lanes of each row half.
@@ -198,10 +250,20 @@ template <int KIND, int M>
 __device__ __forceinline__ void q8_row_partial(const uint8_t* __restrict__ row, int c0, int c1,
                                                const uint16_t* __restrict__ x, int ldx, int lane,
                                                float (&acc)[16][M]) {
-  for (int c = c0; c < c1; ++c) {
-    Q8Chunk ch;
-    q8_load<KIND>(row + (size_t)c * 8704, lane, ch);
-    q8_compute<M>(ch, x, ldx, c, lane, acc);
+  constexpr int D = 1;   // a Q8 chunk already holds 40 registers per lane
+  const int n = c1 - c0;
+  Q8Chunk ring[D];
+#pragma unroll
+  for (int b = 0; b < D; ++b)
+    if (b < n) q8_load<KIND>(row + (size_t)(c0 + b) * 8704, lane, ring[b]);
+  for (int i = 0; i < n; i += D) {
+#pragma unroll
+    for (int b = 0; b < D; ++b) {
+      if (i + b < n) {
+        q8_compute<M>(ring[b], x, ldx, c0 + i + b, lane, acc);
+        if (i + b + D < n) q8_load<KIND>(row + (size_t)(c0 + i + b + D) * 8704, lane, ring[b]);
+      }
+    }
   }
 }
 
@@ -226,6 +288,19 @@ __device__ __forceinline__ void q8_lane_reduce(float (&acc)[16][M]) {
 // acc[i][m] of lane l belongs to row 8i + l/8, group l%8 (sum over the groups
 // with q4_lane_reduce).  xrow[m] points at activation row m, column 0.
 template <int KIND, int M>
+__device__ __forceinline__ void q4_step(const Q4Chunk<KIND>& ch, const uint16_t* const (&xrow)[M],
+                                        int c, uint32_t kMask, uint32_t kMagic, float (&acc)[4][M]) {
+  XPrep<M> xp;
+  x_prep<M>(xrow, 256 * c, xp);
+  q4_compute<KIND, M>(ch, xp, kMask, kMagic, acc);
+}
+
+// Chunks kept in flight per wave by q4_row_partial: a ring of this many chunk
+// buffers, refilled as each is consumed, so a wave's chunks are not fetched as
+// a chain of dependent round trips.
+template <int M> struct Q4Depth { static constexpr int value = 2; };
+
+template <int KIND, int M, int D = Q4Depth<M>::value>
 __device__ __forceinline__ void q4_row_partial(const uint8_t* __restrict__ row, int c0, int c1,
                                                const uint16_t* const (&xrow_in)[M], int lane,
                                                float (&acc)[4][M]) {
@@ -238,14 +313,19 @@ __device__ __forceinline__ void q4_row_partial(const uint8_t* __restrict__ row, 
   uint32_t kMask = 0x000F000Fu, kMagic = 0x43004300u;
   asm volatile("" : "+s"(kMask));
   asm volatile("" : "+v"(kMagic));
-  Q4Chunk<KIND> cur, nxt;
-  if (c0 < c1) q4_load<KIND>(row + (size_t)c0 * CB, lane, cur);
-  for (int c = c0; c < c1; ++c) {
-    if (c + 1 < c1) q4_load<KIND>(row + (size_t)(c + 1) * CB, lane, nxt);
-    XPrep<M> xp;
-    x_prep<M>(xrow, 256 * c, xp);
-    q4_compute<KIND, M>(cur, xp, kMask, kMagic, acc);
-    cur = nxt;
+  const int n = c1 - c0;
+  Q4Chunk<KIND> ring[D];
+#pragma unroll
+  for (int b = 0; b < D; ++b)
+    if (b < n) q4_load<KIND>(row + (size_t)(c0 + b) * CB, lane, ring[b]);
+  for (int i = 0; i < n; i += D) {
+#pragma unroll
+    for (int b = 0; b < D; ++b) {
+      if (i + b < n) {
+        q4_step<KIND, M>(ring[b], xrow, c0 + i + b, kMask, kMagic, acc);
+        if (i + b + D < n) q4_load<KIND>(row + (size_t)(c0 + i + b + D) * CB, lane, ring[b]);
+      }
+    }
   }
 }
 

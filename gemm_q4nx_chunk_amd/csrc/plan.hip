@@ -15,9 +15,13 @@
 //  * Units are numbered phase by phase and dealt round-robin to a grid sized to
 //    stay resident; each workgroup walks its units in increasing order.
 //  * A unit issues its weight loads first and only then waits until every
-//    tile row of the previous phase is written (agent-scope release/acquire on
-//    a per-phase counter), so the weight stream of the next phase overlaps the
-//    tail of the current one while the dependency is still honoured.
+//    tile row of the previous phase is written, so the weight stream of the
+//    next phase overlaps the tail of the current one while the dependency is
+//    still honoured.  Outputs and partial rows are published with device-scope
+//    (sc1) stores, the wave waits for their completion, and only then does one
+//    thread move the counter; consumers poll the counter and read activations
+//    and partials with device-scope loads.  Nothing here writes back or
+//    invalidates a whole L2 (an agent-scope fence would do both, per unit).
 //
 // The smallest unfinished unit only ever waits on units before it, so the
 // schedule cannot deadlock while the grid is resident.  Every wait is also
@@ -76,14 +80,15 @@ __global__ __launch_bounds__(256) void k_plan(PlanArgs a) {
         else q4_load<KIND>(row + (size_t)(c0 + i) * CB, lane, ch[i]);
       }
     }
-    // ... then the dependency on the previous phase
+    // ... then the dependency on the previous phase.  Its outputs were stored
+    // at device scope before its counters moved; x is read at device scope too.
     if (J.phase > confirmed) {
       if (threadIdx.x == 0)
         wait_at_least(a.done + J.phase - 1, a.need[J.phase - 1], a.spin_limit, a.ctl + 1);
       __syncthreads();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       confirmed = J.phase;
     }
+    const __amdgpu_buffer_rsrc_t xrs = make_rsrc(J.x, (uint32_t)(2 * M * J.ldx));
 
     if constexpr (kQ8) {
       float acc[16][M];
@@ -92,8 +97,17 @@ __global__ __launch_bounds__(256) void k_plan(PlanArgs a) {
 #pragma unroll
         for (int m = 0; m < M; ++m) acc[r][m] = 0.f;
 #pragma unroll
-      for (int i = 0; i < CPW; ++i)
-        if (i < nc) q8_compute<M>(ch[i], J.x, J.ldx, c0 + i, lane, acc);
+      for (int i = 0; i < CPW; ++i) {
+        if (i < nc) {
+          Q8XRaw<M> xr;
+#pragma unroll
+          for (int m = 0; m < M; ++m)
+            xr.v[m] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                    xrs, 2 * (m * J.ldx + q8_xcol(lane, c0 + i)), 0,
+                                                    kCpolSc1));
+          q8_compute_raw<M>(ch[i], xr, acc);
+        }
+      }
       q8_lane_reduce<M>(acc);
       if ((lane & ~4) == 0) {
         const int h = (lane >> 2) & 1;
@@ -109,14 +123,16 @@ __global__ __launch_bounds__(256) void k_plan(PlanArgs a) {
 #pragma unroll
         for (int m = 0; m < M; ++m) acc[i][m] = 0.f;
       const int g = lane & 7;
-      const uint16_t* xrow[M];
+      int xoff[M];
 #pragma unroll
-      for (int m = 0; m < M; ++m) xrow[m] = J.x + (size_t)m * J.ldx + 32 * g;
+      for (int m = 0; m < M; ++m) xoff[m] = 2 * (m * J.ldx + 32 * g);
 #pragma unroll
       for (int i = 0; i < CPW; ++i) {
         if (i < nc) {
+          XRaw<M> xr;
+          x_raw_coherent<M>(xrs, xoff, 256 * (c0 + i), xr);
           XPrep<M> xp;
-          x_prep<M>(xrow, 256 * (c0 + i), xp);
+          x_prep_raw<M>(xr, xp);
           q4_compute<KIND, M>(ch[i], xp, kMask, kMagic, acc);
         }
       }
@@ -130,41 +146,42 @@ __global__ __launch_bounds__(256) void k_plan(PlanArgs a) {
     }
     __syncthreads();
 
+    // Publish: device-scope stores, wait for them, then move the counters.
     if (J.S == 1) {
       for (int idx = threadIdx.x; idx < 32 * M; idx += 256) {
         const int r = idx / M, m = idx - r * M;
-        J.y[(size_t)m * J.ldy + 32 * tr + r] = ((red[0][r][m] + red[1][r][m]) + red[2][r][m]) + red[3][r][m];
+        st_coherent(J.y + (size_t)m * J.ldy + 32 * tr + r,
+                    ((red[0][r][m] + red[1][r][m]) + red[2][r][m]) + red[3][r][m]);
       }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      wait_stores();
       __syncthreads();
       if (threadIdx.x == 0)
-        __hip_atomic_fetch_add(a.done + J.phase, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(a.done + J.phase, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     } else {
       const size_t slot = (size_t)J.slot0 + tr;
       float* pp = a.partial + (slot * a.smax + s) * 32 * M;
       for (int idx = threadIdx.x; idx < 32 * M; idx += 256) {
         const int r = idx / M, m = idx - r * M;
-        pp[idx] = ((red[0][r][m] + red[1][r][m]) + red[2][r][m]) + red[3][r][m];
+        st_coherent(pp + idx, ((red[0][r][m] + red[1][r][m]) + red[2][r][m]) + red[3][r][m]);
       }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      wait_stores();
       __syncthreads();
       if (threadIdx.x == 0)
-        s_old = __hip_atomic_fetch_add(a.row_cnt + slot, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        s_old = __hip_atomic_fetch_add(a.row_cnt + slot, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __syncthreads();
       if (s_old == (uint32_t)J.S - 1) {   // last part of this tile row: add the parts in order
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         const float* p0 = a.partial + slot * a.smax * 32 * M;
         for (int idx = threadIdx.x; idx < 32 * M; idx += 256) {
           const int r = idx / M, m = idx - r * M;
           float v = 0.f;
-          for (int p = 0; p < J.S; ++p) v += p0[(size_t)p * 32 * M + idx];
-          J.y[(size_t)m * J.ldy + 32 * tr + r] = v;
+          for (int p = 0; p < J.S; ++p) v += ld_coherent(p0 + (size_t)p * 32 * M + idx);
+          st_coherent(J.y + (size_t)m * J.ldy + 32 * tr + r, v);
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        wait_stores();
         __syncthreads();
         if (threadIdx.x == 0) {
           __hip_atomic_store(a.row_cnt + slot, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          __hip_atomic_fetch_add(a.done + J.phase, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_fetch_add(a.done + J.phase, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
       }
     }
@@ -172,11 +189,11 @@ __global__ __launch_bounds__(256) void k_plan(PlanArgs a) {
   }
 
   if (threadIdx.x == 0) {
-    const uint32_t old = __hip_atomic_fetch_add(a.ctl, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t old = __hip_atomic_fetch_add(a.ctl, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (old == gridDim.x - 1) {   // last workgroup out: ready the counters for the next run
       for (int p = 0; p < a.n_phases; ++p)
         __hip_atomic_store(a.done + p, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(a.ctl, 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(a.ctl, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }

@@ -32,8 +32,9 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // One GEMV of a batched launch.  Workgroup wg of the launch belongs to the last
-// job whose wg_begin <= wg.  ks = waves that split one tile row's chunks
-// (1, 2 or 4); a 4-wave workgroup covers 4/ks tile rows.
+// job whose wg_begin <= wg.  ks = waves that split one tile row's chunks (a
+// power of two up to the launch's waves per workgroup W); a workgroup covers
+// W/ks tile rows.
 struct GemvJob {
   const uint8_t* w;
   const uint16_t* x;
@@ -78,6 +79,26 @@ __device__ __forceinline__ float sum_lanes_xor7(float v) {
   return v;
 }
 
+// Cache-policy operand of the buffer-load builtins: sc1 = device-scope coherent.
+constexpr int kCpolSc1 = 16;
+
+// Buffer resource over n bytes at p (raw, untyped; offsets past n read as 0).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t n) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)n, 0x00020000);
+}
+
+// Device-scope (sc1) 4-byte store and load: they reach past this XCD's L2,
+// so another workgroup of the same launch reads what was written.
+__device__ __forceinline__ void st_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_coherent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until every store this wave issued is complete (visible at device scope
+// for sc1 stores), and keep the compiler from moving memory operations across.
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // Pick the job of workgroup `wg`: the last one whose wg_begin <= wg.
 __device__ __forceinline__ int find_job(const GemvBatch& b, int wg) {
   int j = 0;
@@ -87,7 +108,7 @@ __device__ __forceinline__ int find_job(const GemvBatch& b, int wg) {
 }
 
 // Host-side launchers (gemv.hip, gemm.hip, decode.hip, moe.hip).
-hipError_t launch_gemv(int kind, int M, const GemvBatch& b, int n_wg, hipStream_t s);
+hipError_t launch_gemv(int kind, int M, int waves, const GemvBatch& b, int n_wg, hipStream_t s);
 hipError_t launch_gemm(int kind, const uint8_t* w, const uint16_t* X, float* Y, int TR, int TC,
                        int M, hipStream_t s);
 hipError_t launch_unpack(int kind, const uint8_t* w, int TR, int TC, uint8_t* codes,
