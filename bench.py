@@ -268,11 +268,14 @@ def gemm_leg(steps, warmup, graph):
     descs = [q.weight(dw, s.N, s.K, "q4_1") for s, dw in zip(specs, w)]
     lib = q.lib()
     import ctypes
+    ws_bytes = max(q.gemm_block_ws(d) for d in descs[:7])
+    ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=DEV)
 
     def run64():
         st = torch.cuda.current_stream().cuda_stream
         for s, d in zip(specs, descs):
-            r = lib.q4nx_gemm_block(ctypes.byref(d), Xs[s.K].data_ptr(), Ys[s.N].data_ptr(), 64, st)
+            r = lib.q4nx_gemm_block(ctypes.byref(d), Xs[s.K].data_ptr(), Ys[s.N].data_ptr(), 64,
+                                    ws.data_ptr(), ws.numel(), st)
             if r:
                 raise q.Q4nxError(r, q.last_error())
     flops = sum(2 * 64 * s.N * s.K for s in specs)
@@ -286,7 +289,8 @@ def gemm_leg(steps, warmup, graph):
     calls = []
     for s, d in zip(specs[:7], descs[:7]):
         calls.append(lambda s=s, d=d: lib.q4nx_gemm_block(ctypes.byref(d), Xs[s.K].data_ptr(),
-                                                          Ys[s.N].data_ptr(), 64,
+                                                          Ys[s.N].data_ptr(), 64, ws.data_ptr(),
+                                                          ws.numel(),
                                                           torch.cuda.current_stream().cuda_stream))
     dur = per_launch_ms(calls, reps=3)
     fl7 = sum(2 * 64 * s.N * s.K for s in specs[:7]) * 3

@@ -64,7 +64,9 @@ _I = ctypes.c_int
 _lib.q4nx_weight_check.argtypes = [ctypes.POINTER(Weight)]
 _lib.q4nx_gemv.argtypes = [ctypes.POINTER(Weight), _P, _P, _I, _P]
 _lib.q4nx_gemv_batched.argtypes = [ctypes.POINTER(GemvJob), _I, _I, _P]
-_lib.q4nx_gemm_block.argtypes = [ctypes.POINTER(Weight), _P, _P, _I, _P]
+_lib.q4nx_gemm_block.argtypes = [ctypes.POINTER(Weight), _P, _P, _I, _P, ctypes.c_size_t, _P]
+_lib.q4nx_gemm_block_ws.argtypes = [ctypes.POINTER(Weight)]
+_lib.q4nx_gemm_block_ws.restype = ctypes.c_size_t
 _lib.q4nx_moe_ws.argtypes = [ctypes.POINTER(MoeLayer), _I, _I]
 _lib.q4nx_moe_ws.restype = ctypes.c_size_t
 _lib.q4nx_moe_experts.argtypes = [ctypes.POINTER(MoeLayer), _P, _P, _P, _I, _I, _P,
@@ -205,9 +207,19 @@ class Plan:
             pass
 
 
-def gemm_block(w: Weight, X, Y, M: int, stream=None) -> None:
-    """Y[M, rows] (fp32) = X[M, cols] (bf16) @ W^T for M <= 64."""
-    _check(_lib.q4nx_gemm_block(ctypes.byref(w), _ptr(X), _ptr(Y), M, _stream(stream)))
+def gemm_block_ws(w: Weight) -> int:
+    """Workspace bytes q4nx_gemm_block needs for w (0 = none)."""
+    return int(_lib.q4nx_gemm_block_ws(ctypes.byref(w)))
+
+
+def gemm_block(w: Weight, X, Y, M: int, ws=None, stream=None, ws_bytes: int | None = None) -> None:
+    """Y[M, rows] (fp32) = X[M, cols] (bf16) @ W^T for M <= 64.
+
+    ws: a zero-initialised device buffer of gemm_block_ws(w) bytes (reused
+    across calls; the library leaves it zeroed), or None when that size is 0.
+    """
+    _check(_lib.q4nx_gemm_block(ctypes.byref(w), _ptr(X), _ptr(Y), M, _ptr(ws),
+                                _nbytes(ws) if ws_bytes is None else ws_bytes, _stream(stream)))
 
 
 def moe_layer(n_experts: int, d_model: int, d_expert: int, kind: str, gate, up, down,

@@ -14,6 +14,7 @@
 #include <vector>
 
 #include "../../include/q4nx.h"
+#include "gemm_args.h"
 #include "moe_args.h"
 #include "plan_args.h"
 #include "q4nx_dev.h"
@@ -215,7 +216,8 @@ int q4nx_gemv_batched(const q4nx_gemv_job* jobs, int n_jobs, int M, void* stream
   return ok();
 }
 
-int q4nx_gemm_block(const q4nx_weight* w, const uint16_t* X, float* Y, int M, void* stream) {
+int q4nx_gemm_block(const q4nx_weight* w, const uint16_t* X, float* Y, int M, void* ws,
+                    size_t ws_bytes, void* stream) {
   int st = check_weight(w, "gemm_block");
   if (st) return st;
   if (w->chunk_bytes == Q4NX_Q8_BYTES)
@@ -225,10 +227,30 @@ int q4nx_gemm_block(const q4nx_weight* w, const uint16_t* X, float* Y, int M, vo
     return fail(Q4NX_E_ARG, "gemm_block: M = %d outside 1..%d", M, (int)Q4NX_GEMM_MAX_M);
   if (!aligned(X, 16)) return fail(Q4NX_E_ALIGN, "gemm_block: X not 16-byte aligned");
   if (!aligned(Y, 4)) return fail(Q4NX_E_ALIGN, "gemm_block: Y not 4-byte aligned");
-  const hipError_t e = q4nx::launch_gemm(kind_of(w), static_cast<const uint8_t*>(w->chunks), X, Y,
-                                         w->rows / 32, w->cols / 256, M,
-                                         static_cast<hipStream_t>(stream));
+  const int TR = w->rows / 32, TC = w->cols / 256;
+  const size_t need = q4nx::gemm_ws_bytes(TR, TC);
+  if (need && (!ws || ws_bytes < need))
+    return fail(Q4NX_E_WORKSPACE, "gemm_block: workspace of %zu bytes, %zu needed", ws_bytes, need);
+  if (need && !aligned(ws, 256)) return fail(Q4NX_E_ALIGN, "gemm_block: workspace not 256-byte aligned");
+  q4nx::GemmArgs a;
+  a.w = static_cast<const uint8_t*>(w->chunks);
+  a.X = X;
+  a.Y = Y;
+  a.TR = TR;
+  a.TC = TC;
+  a.M = M;
+  a.S = q4nx::gemm_parts(TR, TC);
+  const size_t nb = (TR + q4nx::kGemmRowsPerWg - 1) / q4nx::kGemmRowsPerWg;
+  a.cnt = need ? static_cast<uint32_t*>(ws) : nullptr;
+  a.partial = need ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + ((nb * 4 + 255) & ~(size_t)255))
+                   : nullptr;
+  const hipError_t e = q4nx::launch_gemm(kind_of(w), a, static_cast<hipStream_t>(stream));
   return hip_status(e, "gemm_block launch");
+}
+
+size_t q4nx_gemm_block_ws(const q4nx_weight* w) {
+  if (check_weight(w, "gemm_block_ws")) return 0;
+  return q4nx::gemm_ws_bytes(w->rows / 32, w->cols / 256);
 }
 
 // ---------------------------------------------------------------------------

@@ -109,8 +109,6 @@ __device__ __forceinline__ int find_job(const GemvBatch& b, int wg) {
 
 // Host-side launchers (gemv.hip, gemm.hip, decode.hip, moe.hip).
 hipError_t launch_gemv(int kind, int M, int waves, const GemvBatch& b, int n_wg, hipStream_t s);
-hipError_t launch_gemm(int kind, const uint8_t* w, const uint16_t* X, float* Y, int TR, int TC,
-                       int M, hipStream_t s);
 hipError_t launch_unpack(int kind, const uint8_t* w, int TR, int TC, uint8_t* codes,
                          uint16_t* meta0, uint16_t* meta1, uint16_t* row_meta, hipStream_t s);
 hipError_t launch_decode(int kind, const uint8_t* w, int TR, int TC, float* out, hipStream_t s);

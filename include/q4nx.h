@@ -182,10 +182,18 @@ void q4nx_plan_destroy(q4nx_plan plan);
  *   X  DEVICE bf16 [M][w->cols], 16-byte aligned
  *   Y  DEVICE fp32 [M][w->rows]; fully overwritten
  *   M  1..Q4NX_GEMM_MAX_M
+ *   ws DEVICE workspace of q4nx_gemm_block_ws(w) bytes, 256-byte aligned (may
+ *      be NULL when that size is 0).  It must hold zeros before its first use;
+ *      every call leaves it ready for the next one.  One workspace serves one
+ *      call at a time.  (K is split over several workgroups when the tile rows
+ *      alone would leave CUs idle; the workspace holds their partial tiles.)
  * The bf16 rounding of each weight moves it by at most 2^-8 of its size; with
  * random signs the error of a sum over K stays well inside 2e-3 * sum |w x|.
  */
-int q4nx_gemm_block(const q4nx_weight* w, const uint16_t* X, float* Y, int M, void* stream);
+int q4nx_gemm_block(const q4nx_weight* w, const uint16_t* X, float* Y, int M, void* ws,
+                    size_t ws_bytes, void* stream);
+/* Workspace bytes q4nx_gemm_block needs for this weight (0 = none). */
+size_t q4nx_gemm_block_ws(const q4nx_weight* w);
 
 /*
  * One routed-expert MoE layer (Strata article, section 2 "target model": per

@@ -99,6 +99,12 @@ def test_gemm_block_checks(q):
     _expect(q, q.E_ARG, q.gemm_block, _w(q), 0x2000, 0x3000, 65, stream=0)
     _expect(q, q.E_ARG, q.gemm_block, _w(q), 0x2000, 0x3000, 0, stream=0)
     _expect(q, q.E_ALIGN, q.gemm_block, _w(q), 0x2004, 0x3000, 8, stream=0)
+    big = _w(q, rows=1024, cols=8192)
+    need = q.gemm_block_ws(big)
+    assert need > 0 and q.gemm_block_ws(_w(q, rows=14336, cols=4096)) > 0
+    _expect(q, q.E_WORKSPACE, q.gemm_block, big, 0x2000, 0x3000, 64, stream=0)
+    _expect(q, q.E_WORKSPACE, q.gemm_block, big, 0x2000, 0x3000, 64, ws=0x100000, ws_bytes=need - 1, stream=0)
+    _expect(q, q.E_ALIGN, q.gemm_block, big, 0x2000, 0x3000, 64, ws=0x100010, ws_bytes=need, stream=0)
 
 
 def _layer(q, **over):

@@ -20,15 +20,30 @@ def _gen(kind, N, K, tag):
     return synth.gen_q4_1(g, N, K, zero="normal") if kind == "q4_1" else synth.gen_q4_k(g, N, K)
 
 
+_WS = {}
+
+
+def _ws(w):
+    """One zero-initialised workspace per size, reused by every call (as the API allows)."""
+    n = q().gemm_block_ws(w)
+    if n == 0:
+        return None
+    if n not in _WS:
+        _WS[n] = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    return _WS[n]
+
+
 def _gemm(ch_dev, N, K, kind, X):
     M = X.shape[0]
     Y = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
-    q().gemm_block(weight(ch_dev, N, K, kind), dev_bf16(X), Y, M)
+    w = weight(ch_dev, N, K, kind)
+    q().gemm_block(w, dev_bf16(X), Y, M, _ws(w))
     return host(Y)
 
 
 @pytest.mark.parametrize("kind", ["q4_1", "q4_k"])
-@pytest.mark.parametrize("N,K", [(32, 256), (96, 512), (160, 1280), (256, 2560)])
+@pytest.mark.parametrize("N,K", [(32, 256), (96, 512), (160, 1280), (256, 2560), (288, 4096),
+                                 (64, 14336)])
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 16, 31, 32, 33, 48, 63, 64])
 def test_gemm_shapes(kind, N, K, M):
     ch = _gen(kind, N, K, "shapes")
@@ -76,3 +91,23 @@ def test_dense_8b_layer_full_size_m64():
         yr, a = oracle.gemv_ref(W, X)
         ysub = np.concatenate([Y[:, 32 * t:32 * t + 32] for t in tr], axis=1)
         assert oracle.tol_ratio(ysub, yr, a) <= 1.0, spec.name
+
+
+def test_split_k_workspace_is_left_zeroed_and_reusable():
+    """A weight whose K is split over workgroups: the counters return to zero after every call."""
+    N, K = 1024, 8192
+    w_ch = _gen("q4_1", N, K, "ws")
+    d = dev_u8(w_ch)
+    w = weight(d, N, K, "q4_1")
+    n = q().gemm_block_ws(w)
+    assert n > 0
+    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    yr_all = oracle.gemv_ref(oracle.weights_exact(w_ch, "q4_1", N, K),
+                             synth.gen_x(synth.rng("gpu-gemm", "wsX"), 64, K))
+    X = synth.gen_x(synth.rng("gpu-gemm", "wsX"), 64, K)
+    for M in (64, 17, 64):
+        Y = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+        q().gemm_block(w, dev_bf16(X[:M]), Y, M, ws)
+        assert oracle.tol_ratio(host(Y), yr_all[0][:M], yr_all[1][:M]) <= 1.0
+    nb = (N // 32 + 7) // 8
+    assert torch.count_nonzero(ws[:4 * nb]).item() == 0
