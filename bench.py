@@ -10,8 +10,10 @@ one for gate|up (one input), one for down, then the lm_head -- 145 launches,
 captured once in a HIP graph and replayed.  Weights are resident in HBM before
 timing starts.
 
-Also reported (legs): the kernel's roofline from per-launch HIP events; the
-CPU oracle timed on a bounded sample; the mixed Q4_K + Q8 lm_head decode step
+Also reported: the roofline of the GEMV kernel (the step's bytes per launch
+over its average launch duration, HIP events around the timed region) with the
+HBM traffic rocprofv3 counted for it; the CPU oracle timed on a bounded
+sample; and, as legs, the same step as one persistent plan launch; the mixed Q4_K + Q8 lm_head decode step
 (Q8 in each code layout); the 64-token block GEMM over 32 layers of 8B-dense
 shapes (TFLOP/s) with its M = 1, 2, 4 GEMV variants; the MoE layer (512
 experts, top-10, shared expert, 48 layers) at T = 1 and T = 64; the single
@@ -37,8 +39,108 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# Kernel sources whose rocprofv3 counter summary (under profiles/) stays valid
+# while they are unchanged.
+KERNEL_SOURCES = {
+    "k_gemv_q4": ["gemv.hip", "gemv_core.h", "q4nx_dev.h"],
+    "k_gemm_q4": ["gemm.hip", "gemm_args.h", "q4nx_dev.h"],
+}
+PROFILE_FILES = {
+    "k_gemv_q4": "k_gemv_q4__qwen3_4b_decode_step.md",
+    "k_gemm_q4": "k_gemm_q4__dense_8b_block_m64.md",
+}
+
+
+def source_sha1(kernel: str) -> str:
+    import hashlib
+    h = hashlib.sha1()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "gemm_q4nx_chunk_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def profiled_traffic(kernel: str):
+    """HBM bytes per launch from the committed counter summary, or None when the
+    summary is missing or the kernel's sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", PROFILE_FILES[kernel])
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and line.split(":", 1)[0].strip() in ("traffic_bytes_per_launch", "source_sha1"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip().strip("`")
+    if vals.get("source_sha1") != source_sha1(kernel) or "traffic_bytes_per_launch" not in vals:
+        return None
+    return float(vals["traffic_bytes_per_launch"])
+
+
+def summarize(trace_db, fetch_db, write_db, kernel, title, commands):
+    """Markdown summary of rocprofv3 results (kernel trace + FETCH_SIZE / WRITE_SIZE
+    passes) for one kernel family; the counters are scaled by what they read for
+    the 1 GiB copy of the copyref leg."""
+    import sqlite3
+    from collections import defaultdict
+    out = [f"# {kernel}: {title}", "", "Commands (from the repository root, rocprofv3 output under gpurun_out/):", ""]
+    out += [f"    {c}" for c in commands]
+    db = sqlite3.connect(trace_db)
+    per = defaultdict(list)
+    for name, dur in db.execute("select name, duration from kernels"):
+        per[name].append(dur)
+    out += ["", "## Kernel trace (--kernel-trace --stats)", "",
+            "| kernel | dispatches | avg us | total ms |", "|---|---:|---:|---:|"]
+    fam = []
+    for name, v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+        out.append(f"| `{name[:70]}` | {len(v)} | {sum(v) / len(v) / 1e3:.2f} | {sum(v) / 1e6:.2f} |")
+        if kernel in name:
+            fam += v
+    out += ["", f"{kernel} (all template variants): {len(fam)} dispatches, "
+                f"average {sum(fam) / len(fam) / 1e3:.2f} us"]
+
+    def counters(path, counter):
+        c = sqlite3.connect(path)
+        rows = c.execute("select kernel_name, grid_size_x, value from counters_collection "
+                         "where counter_name = ?", (counter,)).fetchall()
+        return rows
+    fr, wr = counters(fetch_db, "FETCH_SIZE"), counters(write_db, "WRITE_SIZE")
+    copy_f = [v for n, g, v in fr if "copyBuffer" in n and v > 500000]
+    copy_w = [v for n, g, v in wr if "copyBuffer" in n and v > 500000]
+    gib_kib = float(1 << 20)
+    sf = gib_kib / (sum(copy_f) / len(copy_f))
+    sw = gib_kib / (sum(copy_w) / len(copy_w))
+    out += ["", "## HBM traffic (--pmc FETCH_SIZE, then --pmc WRITE_SIZE; KiB per dispatch)", "",
+            f"Copy kernel moving 1 GiB (1048576 KiB each way): FETCH_SIZE {sum(copy_f) / len(copy_f):.0f} KiB, "
+            f"WRITE_SIZE {sum(copy_w) / len(copy_w):.0f} KiB, so FETCH_SIZE is scaled by {sf:.3f} and "
+            f"WRITE_SIZE by {sw:.3f}.", "",
+            "| kernel | grid (threads) | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB |", "|---|---:|---:|---:|---:|"]
+    agg = defaultdict(lambda: [0, 0.0, 0, 0.0])
+    for n, g, v in fr:
+        if kernel in n:
+            a = agg[(n, g)]; a[0] += 1; a[1] += v
+    for n, g, v in wr:
+        if kernel in n:
+            a = agg[(n, g)]; a[2] += 1; a[3] += v
+    tf = tw = 0.0
+    nf = nw = 0
+    for (n, g), (cf, vf, cw, vw) in sorted(agg.items(), key=lambda kv: -kv[1][1]):
+        out.append(f"| `{n[:60]}` | {g} | {cf} | {vf / max(cf, 1):.1f} | {vw / max(cw, 1):.1f} |")
+        tf += vf; nf += cf; tw += vw; nw += cw
+    per_launch = (tf / nf * sf + tw / nw * sw) * 1024
+    out += ["", f"Scaled HBM bytes per {kernel} dispatch (fetch + write, averaged over "
+                f"{nf} dispatches): {per_launch / 1e6:.3f} MB", "",
+            f"traffic_bytes_per_launch: {per_launch:.0f}",
+            f"source_sha1: `{source_sha1(kernel)}`"]
+    return "\n".join(out) + "\n"
+
+
 def parse():
     ap = argparse.ArgumentParser()
+    ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DB", "FETCH_DB", "WRITE_DB"),
+                    help="print the markdown summary of rocprofv3 results for --kernel and exit")
+    ap.add_argument("--kernel", default="k_gemv_q4", choices=sorted(KERNEL_SOURCES))
+    ap.add_argument("--title", default="")
+    ap.add_argument("--commands", default="", help="the rocprofv3 commands, separated by ';'")
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
@@ -50,8 +152,12 @@ def parse():
 
 
 args = parse()
+if args.summarize:
+    print(summarize(*args.summarize, args.kernel, args.title,
+                    [c.strip() for c in args.commands.split(";") if c.strip()]), end="")
+    sys.exit(0)
 if args.gpus != 1:
-    print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+    print(json.dumps({"error": "one GPU only: the library has no multi-GPU path; --gpus must be 1",
                       "n_gpus": args.gpus}))
     sys.exit(2)
 
@@ -201,21 +307,21 @@ class DecodeStep:
 
 
 def decode_leg(specs, tag, steps, warmup, graph, M=1):
-    """The step as one plan (persistent launch per chunk kind) and as phased launches."""
+    """The step as phased launches (one batched GEMV launch per dependent phase,
+    each waiting for the previous one) and as one persistent plan launch."""
     step = DecodeStep(specs, tag, M)
-    ms, wall = time_calls(step.plan.run, steps, warmup, graph)
+    ms, wall = time_calls(step.run, steps, warmup, graph)
+    gbs = step.bytes / (ms * 1e-3) / 1e9
+    msp, _ = time_calls(step.plan.run, steps, warmup, graph)
     errs = step.plan.errors()
     if errs:
         raise RuntimeError(f"plan reported error flags {errs}")
-    gbs = step.bytes / (ms * 1e-3) / 1e9
-    msp, _ = time_calls(step.run, steps, warmup, graph)
     res = {"ms_per_step": ms, "wall_ms_per_step": wall, "weight_bytes": step.bytes,
            "GB_s": gbs, "pct_hbm_peak": 100 * gbs / HBM_PEAK_GBS,
-           "launches": 1 + sum(1 for a, b in zip(specs, specs[1:]) if a.kind != b.kind),
-           "phases": max(step.plan_phases) + 1,
-           "graph": graph, "plan_device_bytes": step.plan.nbytes(),
-           "phased_launches": {"ms_per_step": msp, "launches": len(step.calls),
-                               "GB_s": step.bytes / (msp * 1e-3) / 1e9}}
+           "launches": len(step.calls), "graph": graph,
+           "plan": {"ms_per_step": msp, "GB_s": step.bytes / (msp * 1e-3) / 1e9,
+                    "launches": 1 + sum(1 for a, b in zip(specs, specs[1:]) if a.kind != b.kind),
+                    "phases": max(step.plan_phases) + 1, "device_bytes": step.plan.nbytes()}}
     return step, res
 
 
@@ -264,37 +370,49 @@ def gemm_leg(steps, warmup, graph):
     nbytes = sum(s.nbytes for s in specs)
     log(f"[gemm] generated+uploaded {nbytes / 1e9:.2f} GB in {time.time() - t0:.1f} s")
     Xs = {K: bf16_dev(synth.gen_x(synth.rng("dense_8b_block", "X", K), 64, K)) for K in (4096, 14336)}
-    Ys = {N: torch.empty((64, N), dtype=torch.float32, device=DEV) for N in (1024, 4096, 14336)}
+    names = [n for n, _, _ in synth.DENSE_8B_LAYER]
+    Ys = {n: torch.empty((64, N), dtype=torch.float32, device=DEV) for n, N, _ in synth.DENSE_8B_LAYER}
     descs = [q.weight(dw, s.N, s.K, "q4_1") for s, dw in zip(specs, w)]
     lib = q.lib()
     import ctypes
-    ws_bytes = max(q.gemm_block_ws(d) for d in descs[:7])
+    # One launch per dependent phase of a layer: q/k/v share X, so do gate/up.
+    PHASES = ((0, 1, 2), (3,), (4, 5), (6,))
+    launches = []
+    for l in range(synth.DENSE_8B_LAYERS):
+        for ph in PHASES:
+            jobs = [(descs[7 * l + i], Ys[names[i]]) for i in ph]
+            launches.append((q._gemm_jobs(jobs), len(jobs), Xs[specs[7 * l + ph[0]].K]))
+    ws_bytes = max(lib.q4nx_gemm_batched_ws(arr, n) for arr, n, _ in launches[:4])
     ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=DEV)
 
+    def launch(arr, n, X):
+        r = lib.q4nx_gemm_batched(arr, n, X.data_ptr(), 64, ws.data_ptr(), ws.numel(),
+                                  torch.cuda.current_stream().cuda_stream)
+        if r:
+            raise q.Q4nxError(r, q.last_error())
+
     def run64():
-        st = torch.cuda.current_stream().cuda_stream
-        for s, d in zip(specs, descs):
-            r = lib.q4nx_gemm_block(ctypes.byref(d), Xs[s.K].data_ptr(), Ys[s.N].data_ptr(), 64,
-                                    ws.data_ptr(), ws.numel(), st)
-            if r:
-                raise q.Q4nxError(r, q.last_error())
+        for arr, n, X in launches:
+            launch(arr, n, X)
     flops = sum(2 * 64 * s.N * s.K for s in specs)
     ms, wall = time_calls(run64, steps, warmup, graph)
     res = {"M64": {"ms_per_block": ms, "TFLOP_s": flops / (ms * 1e-3) / 1e12, "flops": flops,
                    "weight_bytes": nbytes, "GB_s": nbytes / (ms * 1e-3) / 1e9,
                    "pct_mfma_peak": 100 * flops / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
                    "pct_hbm_peak": 100 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                   "launches": len(specs)}}
-    # per-launch durations of the block GEMM kernel (roofline of this leg)
-    calls = []
-    for s, d in zip(specs[:7], descs[:7]):
-        calls.append(lambda s=s, d=d: lib.q4nx_gemm_block(ctypes.byref(d), Xs[s.K].data_ptr(),
-                                                          Ys[s.N].data_ptr(), 64, ws.data_ptr(),
-                                                          ws.numel(),
-                                                          torch.cuda.current_stream().cuda_stream))
-    dur = per_launch_ms(calls, reps=3)
-    fl7 = sum(2 * 64 * s.N * s.K for s in specs[:7]) * 3
-    res["M64"]["kernel_TFLOP_s"] = fl7 / (sum(dur) * 1e-3) / 1e12
+                   "launches": len(launches)}}
+    # roofline of the block GEMM kernel: its launches run back to back, so the timed
+    # region over the launch count is the average launch duration.  At 64 rows a
+    # q4_1 weight byte carries 204.8 flops, under the MI355X ridge (~312), so the
+    # bound is HBM; the bf16 matrix-core fraction is reported beside it.
+    n_launch = len(launches)
+    ach = nbytes / (ms * 1e-3) / 1e9
+    res["M64"]["roofline"] = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                              "frac": ach / HBM_PEAK_GBS, "traffic": profiled_traffic("k_gemm_q4"),
+                              "kernel": "k_gemm_q4<q4_1, M=64>",
+                              "avg_launch_us": ms * 1e3 / n_launch,
+                              "bytes_per_launch": nbytes / n_launch,
+                              "mfma_frac": flops / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS}
     # M = 1, 2, 4 through the GEMV path (same weights)
     for M in (1, 2, 4):
         xm = {K: bf16_dev(synth.gen_x(synth.rng("dense_8b_block", "xm", K, M), M, K)) for K in (4096, 14336)}
@@ -438,7 +556,7 @@ def main():
            "config": {"workload": "qwen3_4b_decode_step_q4_1", "layers": synth.QWEN3_4B_LAYERS,
                       "batch": 1, "lm_head": "151936x2560", "kind": "q4_1",
                       "phases": "per layer q|k|v, o, gate|up, down, then lm_head (145), each "
-                                "waiting for the previous one; one persistent launch",
+                                "waiting for the previous one; one batched launch per phase",
                       "hip_graph": not args.no_graph},
            "device": torch.cuda.get_device_name(0)}
     graph = not args.no_graph
@@ -450,16 +568,19 @@ def main():
         out["ms_per_step"] = res["ms_per_step"]
         out["config"]["weight_bytes_per_step"] = res["weight_bytes"]
         out["pct_hbm_peak"] = res["pct_hbm_peak"]
-        # roofline of the dominant kernel (the q4_1 M=1 plan kernel, one launch per step):
-        # algorithmic bytes per launch / its average duration, HIP events on its stream
-        dur = per_launch_ms([step.plan.run], reps=max(5, args.steps))
-        avg_ms = sum(dur) / len(dur)
-        ach = res["weight_bytes"] / (avg_ms * 1e-3) / 1e9
+        # roofline of the dominant kernel: the batched q4_1 M=1 GEMV kernel, which makes
+        # every launch of the step.  The step's launches run back to back, so the
+        # timed region (HIP events on the launch stream) over the launch count is the
+        # average launch duration; bytes per launch = step bytes / launches.
+        n_launch = len(step.calls)
+        avg_ms = res["ms_per_step"] / n_launch
+        per_launch_bytes = res["weight_bytes"] / n_launch
+        ach = per_launch_bytes / (avg_ms * 1e-3) / 1e9
         out["roofline"] = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                           "frac": ach / HBM_PEAK_GBS, "traffic": None,
-                           "kernel": "k_plan<q4_1, M=1>",
-                           "avg_launch_us": avg_ms * 1e3, "bytes_per_launch": res["weight_bytes"],
-                           "launches_timed": len(dur)}
+                           "frac": ach / HBM_PEAK_GBS, "traffic": profiled_traffic("k_gemv_q4"),
+                           "kernel": "k_gemv_q4<q4_1, M=1>",
+                           "avg_launch_us": avg_ms * 1e3, "bytes_per_launch": per_launch_bytes,
+                           "launches_timed": n_launch * args.steps}
         legs["decode"] = res
         del step
         torch.cuda.empty_cache()

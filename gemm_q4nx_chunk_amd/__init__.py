@@ -43,6 +43,10 @@ class GemvJob(ctypes.Structure):
     _fields_ = [("w", Weight), ("x", ctypes.c_void_p), ("y", ctypes.c_void_p)]
 
 
+class GemmJob(ctypes.Structure):
+    _fields_ = [("w", Weight), ("Y", ctypes.c_void_p)]
+
+
 class MoeLayer(ctypes.Structure):
     _fields_ = [("n_experts", ctypes.c_int32), ("d_model", ctypes.c_int32),
                 ("d_expert", ctypes.c_int32), ("d_shared", ctypes.c_int32),
@@ -67,6 +71,9 @@ _lib.q4nx_gemv_batched.argtypes = [ctypes.POINTER(GemvJob), _I, _I, _P]
 _lib.q4nx_gemm_block.argtypes = [ctypes.POINTER(Weight), _P, _P, _I, _P, ctypes.c_size_t, _P]
 _lib.q4nx_gemm_block_ws.argtypes = [ctypes.POINTER(Weight)]
 _lib.q4nx_gemm_block_ws.restype = ctypes.c_size_t
+_lib.q4nx_gemm_batched.argtypes = [ctypes.POINTER(GemmJob), _I, _P, _I, _P, ctypes.c_size_t, _P]
+_lib.q4nx_gemm_batched_ws.argtypes = [ctypes.POINTER(GemmJob), _I]
+_lib.q4nx_gemm_batched_ws.restype = ctypes.c_size_t
 _lib.q4nx_moe_ws.argtypes = [ctypes.POINTER(MoeLayer), _I, _I]
 _lib.q4nx_moe_ws.restype = ctypes.c_size_t
 _lib.q4nx_moe_experts.argtypes = [ctypes.POINTER(MoeLayer), _P, _P, _P, _I, _I, _P,
@@ -84,7 +91,7 @@ _lib.q4nx_plan_destroy.restype = None
 _lib.q4nx_status_str.argtypes = [_I]
 _lib.q4nx_status_str.restype = ctypes.c_char_p
 _lib.q4nx_last_error.restype = ctypes.c_char_p
-for _f in ("q4nx_weight_check", "q4nx_gemv", "q4nx_gemv_batched", "q4nx_gemm_block",
+for _f in ("q4nx_weight_check", "q4nx_gemv", "q4nx_gemv_batched", "q4nx_gemm_block", "q4nx_gemm_batched",
            "q4nx_moe_experts", "q4nx_unpack", "q4nx_decode", "q4nx_version", "q4nx_plan_create",
            "q4nx_plan_run", "q4nx_plan_errors"):
     getattr(_lib, _f).restype = ctypes.c_int
@@ -220,6 +227,21 @@ def gemm_block(w: Weight, X, Y, M: int, ws=None, stream=None, ws_bytes: int | No
     """
     _check(_lib.q4nx_gemm_block(ctypes.byref(w), _ptr(X), _ptr(Y), M, _ptr(ws),
                                 _nbytes(ws) if ws_bytes is None else ws_bytes, _stream(stream)))
+
+
+def _gemm_jobs(jobs):
+    return (GemmJob * len(jobs))(*[GemmJob(w, _ptr(Y)) for w, Y in jobs])
+
+
+def gemm_batched_ws(jobs) -> int:
+    """Workspace bytes q4nx_gemm_batched needs for jobs = [(Weight, Y), ...] (0 = none)."""
+    return int(_lib.q4nx_gemm_batched_ws(_gemm_jobs(jobs), len(jobs)))
+
+
+def gemm_batched(jobs, X, M: int, ws=None, stream=None, ws_bytes: int | None = None) -> None:
+    """Y_j = X @ W_j^T for jobs = [(Weight, Y_j), ...] sharing X (same kind and cols)."""
+    _check(_lib.q4nx_gemm_batched(_gemm_jobs(jobs), len(jobs), _ptr(X), M, _ptr(ws),
+                                  _nbytes(ws) if ws_bytes is None else ws_bytes, _stream(stream)))
 
 
 def moe_layer(n_experts: int, d_model: int, d_expert: int, kind: str, gate, up, down,

@@ -19,6 +19,8 @@
 #include "plan_args.h"
 #include "q4nx_dev.h"
 
+static_assert(Q4NX_GEMM_BATCH_MAX_JOBS == q4nx::kGemmMaxJobs, "GEMM job table size");
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -216,41 +218,108 @@ int q4nx_gemv_batched(const q4nx_gemv_job* jobs, int n_jobs, int M, void* stream
   return ok();
 }
 
+}  // extern "C"
+
+namespace {
+
+// Checks a block-GEMM launch over weights w[0..n-1] sharing X and fills the
+// kernel arguments (all but the workspace).  Returns a status.
+int gemm_setup(const q4nx_weight* const* w, float* const* Y, int n, const uint16_t* X, int M,
+               const char* name, q4nx::GemmArgs& a) {
+  if (n < 1 || n > q4nx::kGemmMaxJobs)
+    return fail(Q4NX_E_ARG, "%s: %d weights outside 1..%d", name, n, q4nx::kGemmMaxJobs);
+  for (int i = 0; i < n; ++i) {
+    const int st = check_weight(w[i], name);
+    if (st) return st;
+    if (w[i]->chunk_bytes == Q4NX_Q8_BYTES)
+      return fail(Q4NX_E_CHUNK_KIND, "%s: Q8 weights are not supported by the block GEMM", name);
+    if (kind_of(w[i]) != kind_of(w[0]) || w[i]->cols != w[0]->cols)
+      return fail(Q4NX_E_SHAPE, "%s: weight %d differs from weight 0 in chunk kind or columns", name, i);
+    if (!Y[i]) return fail(Q4NX_E_ARG, "%s: null Y of weight %d", name, i);
+    if (!aligned(Y[i], 4)) return fail(Q4NX_E_ALIGN, "%s: Y of weight %d not 4-byte aligned", name, i);
+  }
+  if (!X) return fail(Q4NX_E_ARG, "%s: null X", name);
+  if (M < 1 || M > Q4NX_GEMM_MAX_M)
+    return fail(Q4NX_E_ARG, "%s: M = %d outside 1..%d", name, M, (int)Q4NX_GEMM_MAX_M);
+  if (!aligned(X, 16)) return fail(Q4NX_E_ALIGN, "%s: X not 16-byte aligned", name);
+  a = q4nx::GemmArgs{};
+  int nb = 0;
+  for (int i = 0; i < n; ++i) {
+    a.job[i].w = static_cast<const uint8_t*>(w[i]->chunks);
+    a.job[i].Y = Y[i];
+    a.job[i].TR = (int32_t)(w[i]->rows / 32);
+    a.job[i].nb0 = nb;
+    nb += q4nx::gemm_blocks(a.job[i].TR);
+  }
+  a.n_jobs = n;
+  a.X = X;
+  a.TC = (int32_t)(w[0]->cols / 256);
+  a.M = M;
+  a.NB = nb;
+  a.S = q4nx::gemm_parts(nb, a.TC);
+  return Q4NX_OK;
+}
+
+int gemm_launch(q4nx::GemmArgs& a, int kind, void* ws, size_t ws_bytes, void* stream,
+                const char* name) {
+  const size_t need = q4nx::gemm_ws_bytes(a.NB, a.TC);
+  if (need && (!ws || ws_bytes < need))
+    return fail(Q4NX_E_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", name, ws_bytes, need);
+  if (need && !aligned(ws, 256)) return fail(Q4NX_E_ALIGN, "%s: workspace not 256-byte aligned", name);
+  a.cnt = need ? static_cast<uint32_t*>(ws) : nullptr;
+  a.partial = need ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + q4nx::gemm_cnt_bytes(a.NB))
+                   : nullptr;
+  const hipError_t e = q4nx::launch_gemm(kind, a, static_cast<hipStream_t>(stream));
+  return hip_status(e, name);
+}
+
+}  // namespace
+
+extern "C" {
+
 int q4nx_gemm_block(const q4nx_weight* w, const uint16_t* X, float* Y, int M, void* ws,
                     size_t ws_bytes, void* stream) {
-  int st = check_weight(w, "gemm_block");
-  if (st) return st;
-  if (w->chunk_bytes == Q4NX_Q8_BYTES)
-    return fail(Q4NX_E_CHUNK_KIND, "gemm_block: Q8 weights are not supported by the block GEMM");
-  if (!X || !Y) return fail(Q4NX_E_ARG, "gemm_block: null X or Y");
-  if (M < 1 || M > Q4NX_GEMM_MAX_M)
-    return fail(Q4NX_E_ARG, "gemm_block: M = %d outside 1..%d", M, (int)Q4NX_GEMM_MAX_M);
-  if (!aligned(X, 16)) return fail(Q4NX_E_ALIGN, "gemm_block: X not 16-byte aligned");
-  if (!aligned(Y, 4)) return fail(Q4NX_E_ALIGN, "gemm_block: Y not 4-byte aligned");
-  const int TR = w->rows / 32, TC = w->cols / 256;
-  const size_t need = q4nx::gemm_ws_bytes(TR, TC);
-  if (need && (!ws || ws_bytes < need))
-    return fail(Q4NX_E_WORKSPACE, "gemm_block: workspace of %zu bytes, %zu needed", ws_bytes, need);
-  if (need && !aligned(ws, 256)) return fail(Q4NX_E_ALIGN, "gemm_block: workspace not 256-byte aligned");
   q4nx::GemmArgs a;
-  a.w = static_cast<const uint8_t*>(w->chunks);
-  a.X = X;
-  a.Y = Y;
-  a.TR = TR;
-  a.TC = TC;
-  a.M = M;
-  a.S = q4nx::gemm_parts(TR, TC);
-  const size_t nb = (TR + q4nx::kGemmRowsPerWg - 1) / q4nx::kGemmRowsPerWg;
-  a.cnt = need ? static_cast<uint32_t*>(ws) : nullptr;
-  a.partial = need ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + ((nb * 4 + 255) & ~(size_t)255))
-                   : nullptr;
-  const hipError_t e = q4nx::launch_gemm(kind_of(w), a, static_cast<hipStream_t>(stream));
-  return hip_status(e, "gemm_block launch");
+  const int st = gemm_setup(&w, &Y, 1, X, M, "gemm_block", a);
+  if (st) return st;
+  const int r = gemm_launch(a, kind_of(w), ws, ws_bytes, stream, "gemm_block");
+  return r ? r : ok();
 }
 
 size_t q4nx_gemm_block_ws(const q4nx_weight* w) {
   if (check_weight(w, "gemm_block_ws")) return 0;
-  return q4nx::gemm_ws_bytes(w->rows / 32, w->cols / 256);
+  return q4nx::gemm_ws_bytes(q4nx::gemm_blocks((int)(w->rows / 32)), (int)(w->cols / 256));
+}
+
+int q4nx_gemm_batched(const q4nx_gemm_job* jobs, int n_jobs, const uint16_t* X, int M, void* ws,
+                      size_t ws_bytes, void* stream) {
+  if (!jobs) return fail(Q4NX_E_ARG, "gemm_batched: null job array");
+  if (n_jobs < 1 || n_jobs > Q4NX_GEMM_BATCH_MAX_JOBS)
+    return fail(Q4NX_E_ARG, "gemm_batched: %d jobs outside 1..%d", n_jobs, (int)Q4NX_GEMM_BATCH_MAX_JOBS);
+  const q4nx_weight* w[Q4NX_GEMM_BATCH_MAX_JOBS];
+  float* Y[Q4NX_GEMM_BATCH_MAX_JOBS];
+  for (int i = 0; i < n_jobs; ++i) {
+    w[i] = &jobs[i].w;
+    Y[i] = jobs[i].Y;
+  }
+  q4nx::GemmArgs a;
+  const int st = gemm_setup(w, Y, n_jobs, X, M, "gemm_batched", a);
+  if (st) return st;
+  const int r = gemm_launch(a, kind_of(w[0]), ws, ws_bytes, stream, "gemm_batched");
+  return r ? r : ok();
+}
+
+size_t q4nx_gemm_batched_ws(const q4nx_gemm_job* jobs, int n_jobs) {
+  if (!jobs || n_jobs < 1 || n_jobs > Q4NX_GEMM_BATCH_MAX_JOBS) {
+    fail(Q4NX_E_ARG, "gemm_batched_ws: bad job array");
+    return 0;
+  }
+  int nb = 0;
+  for (int i = 0; i < n_jobs; ++i) {
+    if (check_weight(&jobs[i].w, "gemm_batched_ws")) return 0;
+    nb += q4nx::gemm_blocks((int)(jobs[i].w.rows / 32));
+  }
+  return q4nx::gemm_ws_bytes(nb, (int)(jobs[0].w.cols / 256));
 }
 
 // ---------------------------------------------------------------------------

@@ -37,8 +37,13 @@
 
 namespace q4nx {
 
-constexpr int kXs = 264;   // LDS row stride of the X tile in bf16 (256 + 8: 4-bank skew per row)
+constexpr int kXs = 264;   // LDS row stride of an X tile in bf16 (256 + 8: 4-bank skew per row)
 constexpr int kGemmWaves = 8;
+#ifndef Q4NX_GEMM_DEPTH
+#define Q4NX_GEMM_DEPTH 2
+#endif
+constexpr int kGemmDepth = Q4NX_GEMM_DEPTH;   // chunk loads in flight per wave
+static_assert(kGemmWaves == kGemmRowsPerWg, "one tile row per wave");
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
@@ -48,17 +53,25 @@ struct GemmChunk {
   u32x4 meta;   // q4_1: (scale, zero) of groups 4h..4h+3; Q4_K: .x,.y = (sc,mn) bytes, .z = (S, M)
 };
 
+// Chunk of tile column t of the lane's row: rs covers the row's chunks of this
+// workgroup's K part, off = (t - first tile column) * chunk bytes.  Offsets past
+// the part read as zero without touching memory, so the prefetch past the last
+// tile column needs no branch.
 template <int KIND>
-__device__ __forceinline__ void gemm_load(const uint8_t* __restrict__ ck, int n, int h, GemmChunk<KIND>& c) {
+__device__ __forceinline__ void gemm_load(__amdgpu_buffer_rsrc_t rs, uint32_t off, int n, int h,
+                                          GemmChunk<KIND>& c) {
+  constexpr int kNt = 2;   // nontemporal: weights are read once
 #pragma unroll
-  for (int q = 0; q < 4; ++q) c.q[q] = load_nt16(ck + 128 * n + 64 * h + 16 * q);
+  for (int q = 0; q < 4; ++q)
+    c.q[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                           rs, off + 128 * n + 64 * h + 16 * q, 0, kNt));
   if constexpr (KIND == KIND_Q4_1) {
-    c.meta = *reinterpret_cast<const u32x4*>(ck + 4096 + 32 * n + 16 * h);
+    c.meta = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 4096 + 32 * n + 16 * h, 0, 0));
   } else {
-    const u32x2 scmn = *reinterpret_cast<const u32x2*>(ck + 4096 + 16 * n + 8 * h);
+    const u32x2 scmn = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, off + 4096 + 16 * n + 8 * h, 0, 0));
     c.meta.x = scmn.x;
     c.meta.y = scmn.y;
-    c.meta.z = *reinterpret_cast<const uint32_t*>(ck + 4608 + 4 * n);
+    c.meta.z = __builtin_amdgcn_raw_buffer_load_b32(rs, off + 4608 + 4 * n, 0, 0);
     c.meta.w = 0;
   }
 }
@@ -96,35 +109,65 @@ __device__ __forceinline__ bf16x8 dequant8(uint32_t w, float s, float z_lo, floa
   return b;
 }
 
-template <int KIND, bool TWO>
-__global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_q4(GemmArgs a) {
+// The X columns of the current tile column (XR x 256 bf16) sit in LDS, double
+// buffered: the next tile column's X is loaded into registers at the start of
+// a step and written to the other buffer at its end.  Chunk loads of tile
+// column t run D tile columns ahead of its products, in a ring of D register
+// sets.  All loads are unconditional (buffer loads past the end read zero
+// without touching memory) and every branch is uniform, so the compiler's
+// wait counts stay exact: a step waits only for its own chunk and, at its
+// end, for the next X tile.  Waves past the last tile row and X rows past M
+// read clamped, in-bounds data whose results are not stored.
+template <int KIND, bool TWO, int D>
+#ifndef Q4NX_GEMM_WAVES_PER_EU
+#define Q4NX_GEMM_WAVES_PER_EU 4
+#endif
+// Two workgroups per CU (4 waves per SIMD, at most 128 VGPRs each).
+__global__ __launch_bounds__(64 * kGemmWaves) __attribute__((amdgpu_waves_per_eu(Q4NX_GEMM_WAVES_PER_EU, Q4NX_GEMM_WAVES_PER_EU)))
+void k_gemm_q4(GemmArgs a) {
   constexpr int CB = ChunkBytes<KIND>::value;
   constexpr int NT = 64 * kGemmWaves;
-  __shared__ __attribute__((aligned(16))) uint16_t xs[2][64 * kXs];
+  constexpr int XR = TWO ? 64 : 32;          // token rows staged in LDS
+  constexpr int G = TWO ? 8 : 4;             // f32x4 groups of the accumulators
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][XR * kXs];
   __shared__ uint32_t s_old;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave: row data in SGPRs
   const int h = lane >> 5, n = lane & 31;
   const int nb = blockIdx.x, part = blockIdx.y;
-  const int tr = nb * kGemmWaves + wave;
-  const bool active = tr < a.TR;
-  const int K = a.TC * 256, N = a.TR * 32, M = a.M;
+  int ji = 0;
+  for (int i = 1; i < a.n_jobs; ++i)
+    if (nb >= a.job[i].nb0) ji = i;
+  const GemmJob& job = a.job[ji];
+  const int tr_raw = (nb - job.nb0) * kGemmWaves + wave;
+  const bool active = tr_raw < job.TR;
+  const int tr = active ? tr_raw : job.TR - 1;
+  const int K = a.TC * 256, N = job.TR * 32, M = a.M;
   const int tc0 = part * a.TC / a.S, tc1 = (part + 1) * a.TC / a.S;
-  const uint8_t* rowp = a.w + (size_t)(active ? tr : 0) * a.TC * CB;
+  const __amdgpu_buffer_rsrc_t wrs =
+      make_rsrc(job.w + ((size_t)tr * a.TC + tc0) * CB, (uint32_t)((tc1 - tc0) * CB));
 
   uint32_t kMaskLo = 0x000F000Fu, kMaskHi = 0x00F000F0u, kMagic = 0x64006400u;
   asm volatile("" : "+s"(kMaskLo));
   asm volatile("" : "+s"(kMaskHi));
   asm volatile("" : "+v"(kMagic));
 
-  // X tile loader: 64 rows x 32 pieces of 16 B over NT threads.
-  constexpr int XP = 64 * 32 / NT;
+  // X tile loader: XR rows x 32 pieces of 16 B over NT threads (row clamped to
+  // M - 1).  Past the last tile column of X the loads read zeros or the next
+  // row; that tile is never used.
+  constexpr int XP = XR * 32 / NT;
+  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(a.X, (uint32_t)(M * K * 2));
+  uint32_t xoff[XP];
+#pragma unroll
+  for (int p = 0; p < XP; ++p) {
+    const int piece = tid + NT * p, row = piece >> 5, c16 = piece & 31;
+    xoff[p] = (uint32_t)((row < M ? row : M - 1) * K + c16 * 8) * 2;
+  }
   u32x4 xr[XP];
   auto xload = [&](int tc) {
 #pragma unroll
-    for (int p = 0; p < XP; ++p) {
-      const int piece = tid + NT * p, row = piece >> 5, c16 = piece & 31;
-      xr[p] = row < M ? load16(a.X + (size_t)row * K + tc * 256 + c16 * 8) : u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int p = 0; p < XP; ++p)
+      xr[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs, xoff[p] + tc * 512, 0, 0));
   };
   auto xstore = [&](int buf) {
 #pragma unroll
@@ -138,96 +181,121 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_q4(GemmArgs a) {
 #pragma unroll
   for (int v = 0; v < 16; ++v) { acc0[v] = 0.f; acc1[v] = 0.f; }
 
-  GemmChunk<KIND> cur, nxt;
+  GemmChunk<KIND> c[D];
   xload(tc0);
+#pragma unroll
+  for (int j = 0; j < D; ++j) gemm_load<KIND>(wrs, j * CB, n, h, c[j]);
   xstore(0);
-  if (active) gemm_load<KIND>(rowp + (size_t)tc0 * CB, n, h, cur);
 
-  for (int tc = tc0; tc < tc1; ++tc) {
-    const int buf = (tc - tc0) & 1;
-    __syncthreads();                       // X tile tc is in xs[buf]
-    const bool more = tc + 1 < tc1;
-    if (more) {
-      xload(tc + 1);
-      if (active) gemm_load<KIND>(rowp + (size_t)(tc + 1) * CB, n, h, nxt);
-    }
-    if (active) {
-      const uint16_t* xb = xs[buf] + n * kXs + 128 * h;
+  // One tile column: t's X tile is in xs[(t - tc0) & 1] and its chunk in c[j].
+  auto step = [&](int j, int t) {
+    const int buf = (t - tc0) & 1;
+    __syncthreads();                       // X tile t is in xs[buf]; xs[buf ^ 1] is free
+    xload(t + 1);
+    __builtin_amdgcn_sched_barrier(0);     // issue the X loads before the products
+    const uint16_t* xb = xs[buf] + n * kXs + 128 * h;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float s, z;
-        group_sz<KIND>(cur, q, s, z);
-        const float z_lo = fmaf(-1024.f, s, z), s16 = s * 0.0625f, z_hi = fmaf(-64.f, s, z);
+    for (int q = 0; q < 4; ++q) {
+      float s, z;
+      group_sz<KIND>(c[j], q, s, z);
+      const float z_lo = fmaf(-1024.f, s, z), s16 = s * 0.0625f, z_hi = fmaf(-64.f, s, z);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int st = 4 * q + e;
-          const bf16x8 B = dequant8(cur.q[q][e], s, z_lo, s16, z_hi, kMaskLo, kMaskHi, kMagic);
-          const bf16x8 A0 = *reinterpret_cast<const bf16x8*>(xb + 8 * st);
-          acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A0, B, acc0, 0, 0, 0);
-          if constexpr (TWO) {
-            const bf16x8 A1 = *reinterpret_cast<const bf16x8*>(xb + 32 * kXs + 8 * st);
-            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A1, B, acc1, 0, 0, 0);
-          }
+      for (int e = 0; e < 4; ++e) {
+        const int st = 4 * q + e;
+        const bf16x8 B = dequant8(c[j].q[q][e], s, z_lo, s16, z_hi, kMaskLo, kMaskHi, kMagic);
+        const bf16x8 A0 = *reinterpret_cast<const bf16x8*>(xb + 8 * st);
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A0, B, acc0, 0, 0, 0);
+        if constexpr (TWO) {
+          const bf16x8 A1 = *reinterpret_cast<const bf16x8*>(xb + 32 * kXs + 8 * st);
+          acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A1, B, acc1, 0, 0, 0);
         }
       }
     }
-    if (more) {
-      xstore((tc + 1 - tc0) & 1);          // that buffer was last read before this barrier
-      cur = nxt;
-    }
+    gemm_load<KIND>(wrs, (uint32_t)(t + D - tc0) * CB, n, h, c[j]);
+    xstore(buf ^ 1);
+  };
+  // Full groups of D tile columns, then the last (tc1 - tc0) % D: no branch
+  // inside a group, so every wait is for the chunk D tile columns back.
+  int base = tc0;
+  for (; base + D <= tc1; base += D) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) step(j, base + j);
   }
+#pragma unroll
+  for (int j = 0; j + 1 < D; ++j)
+    if (base + j < tc1) step(j, base + j);
 
   // 32x32 accumulator: register v of lane holds token row 8*(v/4) + 4*h + v%4, output column n.
-  if (a.S == 1) {
-    if (active) {
-      float* yc = a.Y + 32 * tr + n;
+  auto store_y = [&](const f32x4* r) {
+    float* yc = job.Y + 32 * tr + n;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int m = 8 * (v >> 2) + 4 * h + (v & 3);
-        if (m < M) yc[(size_t)m * N] = acc0[v];
-        if (TWO && m + 32 < M) yc[(size_t)(m + 32) * N] = acc1[v];
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = 32 * (g >> 2) + 8 * (g & 3) + 4 * h + i;
+        if (m < M) yc[(size_t)m * N] = r[g][i];
       }
-    }
+  };
+  f32x4 mine[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mine[g][i] = g < 4 ? acc0[4 * g + i] : acc1[4 * (g - 4) + i];
+  if (a.S == 1) {
+    if (active) store_y(mine);
     return;
   }
-  // split K: partial tile [M][8 tile rows x 32] of this part, then the last part adds them
-  const int ncol = kGemmWaves * 32;
-  float* pt = a.partial + ((size_t)nb * a.S + part) * 64 * ncol;
-  {
-    float* pc = pt + wave * 32 + n;
+
+  // Split K: each part stores its accumulators in register order (16 B per
+  // lane and group, device-coherent), and the last part of the block to
+  // arrive adds all parts, its own read back too, in part order.  Loads past
+  // the last part fall outside the buffer resource and read zero.
+  constexpr size_t kPartBytes = (size_t)kGemmWaves * 8 * 64 * 16;
+  const uint32_t part_bytes = (uint32_t)(kPartBytes * a.S);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.partial + (size_t)nb * a.S * (kPartBytes / 4), part_bytes);
+  const uint32_t lane_off = (uint32_t)(wave * 8 * 64 + lane) * 16;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int m = 8 * (v >> 2) + 4 * h + (v & 3);
-      if (m < M) st_coherent(pc + (size_t)m * ncol, acc0[v]);
-      if (TWO && m + 32 < M) st_coherent(pc + (size_t)(m + 32) * ncol, acc1[v]);
-    }
-  }
+  for (int g = 0; g < G; ++g)
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, mine[g]), rs,
+                                           lane_off + part * (uint32_t)kPartBytes + g * 1024, 0, kCpolSc1);
   wait_stores();
   __syncthreads();
   if (tid == 0)
     s_old = __hip_atomic_fetch_add(a.cnt + nb, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   if (s_old != (uint32_t)a.S - 1) return;
-  const float* p0 = a.partial + (size_t)nb * a.S * 64 * ncol;
-  for (int idx = tid; idx < M * ncol; idx += NT) {
-    const int m = idx / ncol, c = idx - m * ncol;
-    const int col = nb * ncol + c;
-    float v = 0.f;
-    for (int p = 0; p < a.S; ++p) v += ld_coherent(p0 + (size_t)p * 64 * ncol + idx);
-    if (col < N) a.Y[(size_t)m * N + col] = v;
+
+  constexpr int PB = 16 / G;                 // parts loaded per round trip (64 registers)
+  f32x4 sum[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) sum[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int p0 = 0; p0 < a.S; p0 += PB) {
+    f32x4 in[PB][G];
+#pragma unroll
+    for (int j = 0; j < PB; ++j)
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+        in[j][g] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 rs, lane_off + (p0 + j) * (uint32_t)kPartBytes + g * 1024, 0, kCpolSc1));
+#pragma unroll
+    for (int j = 0; j < PB; ++j)
+      if (p0 + j < a.S)
+#pragma unroll
+        for (int g = 0; g < G; ++g) sum[g] += in[j][g];
   }
+  if (active) store_y(sum);
   if (tid == 0) __hip_atomic_store(a.cnt + nb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 hipError_t launch_gemm(int kind, const GemmArgs& a, hipStream_t s) {
-  const dim3 grid((a.TR + kGemmWaves - 1) / kGemmWaves, a.S), block(64 * kGemmWaves);
+  const dim3 grid(a.NB, a.S), block(64 * kGemmWaves);
   const bool two = a.M > 32;
   if (kind == KIND_Q4_1) {
-    if (two) hipLaunchKernelGGL((k_gemm_q4<KIND_Q4_1, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_gemm_q4<KIND_Q4_1, false>), grid, block, 0, s, a);
+    if (two) hipLaunchKernelGGL((k_gemm_q4<KIND_Q4_1, true, kGemmDepth>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_gemm_q4<KIND_Q4_1, false, kGemmDepth>), grid, block, 0, s, a);
   } else if (kind == KIND_Q4_K) {
-    if (two) hipLaunchKernelGGL((k_gemm_q4<KIND_Q4_K, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_gemm_q4<KIND_Q4_K, false>), grid, block, 0, s, a);
+    if (two) hipLaunchKernelGGL((k_gemm_q4<KIND_Q4_K, true, kGemmDepth>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_gemm_q4<KIND_Q4_K, false, kGemmDepth>), grid, block, 0, s, a);
   } else {
     return hipErrorInvalidValue;
   }

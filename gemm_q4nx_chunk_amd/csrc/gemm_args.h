@@ -7,36 +7,57 @@
 
 namespace q4nx {
 
-struct GemmArgs {
+// One weight of a block-GEMM launch: its tile rows are workgroup rows
+// nb0 .. nb0 + ceil(TR / 8) - 1 of the grid.
+struct GemmJob {
   const uint8_t* w;
+  float* Y;         // [M][32 * TR]
+  int32_t TR, nb0;
+};
+
+constexpr int kGemmMaxJobs = 8;
+
+struct GemmArgs {
+  GemmJob job[kGemmMaxJobs];
+  int32_t n_jobs;
   const uint16_t* X;
-  float* Y;
-  float* partial;   // [n_blocks][S][64][8*32] fp32 when S > 1
-  uint32_t* cnt;    // [n_blocks] parts arrived; zero between calls
-  int32_t TR, TC, M, S;
+  float* partial;   // [NB][S][8 waves][8 groups][64 lanes][4] fp32 when S > 1
+  uint32_t* cnt;    // [NB] parts arrived; zero between calls
+  int32_t TC, M, S, NB;
 };
 
 // Tile rows per workgroup of the block GEMM.
 constexpr int kGemmRowsPerWg = 8;
 
-// K parts for a weight of TR x TC tiles: enough workgroups to give every CU
-// dequantisation work (about 384 workgroups), but at least 4 tile columns per
-// part so the fp32 partial tiles stay small next to the weights they summarise.
-inline int gemm_parts(int TR, int TC) {
-  const int nb = (TR + kGemmRowsPerWg - 1) / kGemmRowsPerWg;
-  int S = (384 + nb - 1) / nb;
-  const int lim = TC / 4 > 0 ? TC / 4 : 1;
+// Workgroups a launch aims for (two per CU), and the fewest tile columns a K
+// part may hold (so the fp32 partial tiles stay small next to the weights
+// they summarise).
+#ifndef Q4NX_GEMM_WG_TARGET
+#define Q4NX_GEMM_WG_TARGET 512
+#endif
+#ifndef Q4NX_GEMM_MIN_COLS
+#define Q4NX_GEMM_MIN_COLS 4
+#endif
+
+inline int gemm_blocks(int TR) { return (TR + kGemmRowsPerWg - 1) / kGemmRowsPerWg; }
+
+// K parts for a launch of nb workgroup rows over TC tile columns: as many as
+// keep all workgroups resident at once (nb * S <= the target), at most one
+// per Q4NX_GEMM_MIN_COLS tile columns.
+inline int gemm_parts(int nb, int TC) {
+  int S = Q4NX_GEMM_WG_TARGET / nb;
+  const int lim = TC / Q4NX_GEMM_MIN_COLS > 0 ? TC / Q4NX_GEMM_MIN_COLS : 1;
   if (S > lim) S = lim;
   if (S < 1) S = 1;
   return S;
 }
 
-inline size_t gemm_ws_bytes(int TR, int TC) {
-  const int S = gemm_parts(TR, TC);
+// Bytes of the arrival counters (256-byte aligned) and of the partial tiles.
+inline size_t gemm_cnt_bytes(int nb) { return ((size_t)nb * 4 + 255) & ~(size_t)255; }
+inline size_t gemm_ws_bytes(int nb, int TC) {
+  const int S = gemm_parts(nb, TC);
   if (S == 1) return 0;
-  const size_t nb = (TR + kGemmRowsPerWg - 1) / kGemmRowsPerWg;
-  const size_t cnt = (nb * 4 + 255) & ~(size_t)255;
-  return cnt + nb * S * 64 * kGemmRowsPerWg * 32 * 4;
+  return gemm_cnt_bytes(nb) + (size_t)nb * S * 64 * kGemmRowsPerWg * 32 * 4;
 }
 
 hipError_t launch_gemm(int kind, const GemmArgs& a, hipStream_t s);

@@ -79,6 +79,8 @@ enum { Q4NX_GEMV_MAX_M = 8 };
 enum { Q4NX_GEMM_MAX_M = 64 };
 /* Most jobs one q4nx_gemv_batched call takes. */
 enum { Q4NX_BATCH_MAX_JOBS = 64 };
+/* Most weights of one q4nx_gemm_batched call. */
+enum { Q4NX_GEMM_BATCH_MAX_JOBS = 8 };
 
 /* One Q4NX weight, described on the host. */
 typedef struct q4nx_weight {
@@ -194,6 +196,28 @@ int q4nx_gemm_block(const q4nx_weight* w, const uint16_t* X, float* Y, int M, vo
                     size_t ws_bytes, void* stream);
 /* Workspace bytes q4nx_gemm_block needs for this weight (0 = none). */
 size_t q4nx_gemm_block_ws(const q4nx_weight* w);
+
+/*
+ * The block GEMM of several weights that read the same X (the q, k and v
+ * projections of a layer, or its gate and up projections) in one launch:
+ * Y_j = W_j X for every job, exactly as q4nx_gemm_block computes each.
+ *   jobs    n_jobs (1..Q4NX_GEMM_BATCH_MAX_JOBS) weights with their outputs;
+ *           every weight has the chunk kind (q4_1 or Q4_K) and the column
+ *           count of jobs[0] (E_SHAPE otherwise)
+ *   X       DEVICE bf16 [M][cols], 16-byte aligned, shared by all jobs
+ *   Y_j     DEVICE fp32 [M][w.rows]; fully overwritten
+ *   ws      DEVICE workspace of q4nx_gemm_batched_ws(jobs, n_jobs) bytes, with
+ *           the rules of q4nx_gemm_block's workspace
+ */
+typedef struct q4nx_gemm_job {
+  q4nx_weight w;
+  float* Y;
+} q4nx_gemm_job;
+
+int q4nx_gemm_batched(const q4nx_gemm_job* jobs, int n_jobs, const uint16_t* X, int M, void* ws,
+                      size_t ws_bytes, void* stream);
+/* Workspace bytes of q4nx_gemm_batched for these jobs (0 = none or bad jobs). */
+size_t q4nx_gemm_batched_ws(const q4nx_gemm_job* jobs, int n_jobs);
 
 /*
  * One routed-expert MoE layer (Strata article, section 2 "target model": per

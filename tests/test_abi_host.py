@@ -107,6 +107,25 @@ def test_gemm_block_checks(q):
     _expect(q, q.E_ALIGN, q.gemm_block, big, 0x2000, 0x3000, 64, ws=0x100010, ws_bytes=need, stream=0)
 
 
+def test_gemm_batched_checks(q):
+    a, b = _w(q, rows=1024, cols=4096), _w(q, rows=4096, cols=4096)
+    jobs = [(a, 0x3000), (b, 0x4000)]
+    need = q.gemm_batched_ws(jobs)
+    # one workgroup row per 8 tile rows of each weight, K split over parts
+    assert need == q.gemm_batched_ws([(b, 0x4000), (a, 0x3000)]) and need > 0
+    _expect(q, q.E_SHAPE, q.gemm_batched, [(a, 0x3000), (_w(q, rows=1024, cols=2048), 0x4000)],
+            0x2000, 64, stream=0)
+    _expect(q, q.E_SHAPE, q.gemm_batched, [(a, 0x3000), (_w(q, kind="q4_k", rows=1024, cols=4096), 0x4000)],
+            0x2000, 64, stream=0)
+    _expect(q, q.E_CHUNK_KIND, q.gemm_batched, [(a, 0x3000), (_w(q, kind="q8", layout="A"), 0x4000)],
+            0x2000, 64, stream=0)
+    _expect(q, q.E_ARG, q.gemm_batched, [(a, 0x3000)] * 9, 0x2000, 64, stream=0)
+    _expect(q, q.E_ARG, q.gemm_batched, [(a, 0)], 0x2000, 64, stream=0)
+    _expect(q, q.E_ALIGN, q.gemm_batched, [(a, 0x3002)], 0x2000, 64, stream=0)
+    _expect(q, q.E_WORKSPACE, q.gemm_batched, jobs, 0x2000, 64, ws=0x100000, ws_bytes=need - 1, stream=0)
+    _expect(q, q.E_ALIGN, q.gemm_batched, jobs, 0x2000, 64, ws=0x100010, ws_bytes=need, stream=0)
+
+
 def _layer(q, **over):
     D, De, Ds, n = 2048, 512, 1024, 512
     gu = (De // 32) * (D // 256) * 5120

@@ -111,3 +111,50 @@ def test_split_k_workspace_is_left_zeroed_and_reusable():
         assert oracle.tol_ratio(host(Y), yr_all[0][:M], yr_all[1][:M]) <= 1.0
     nb = (N // 32 + 7) // 8
     assert torch.count_nonzero(ws[:4 * nb]).item() == 0
+
+
+def _ws_bytes(n):
+    if n == 0:
+        return None
+    if n not in _WS:
+        _WS[n] = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    return _WS[n]
+
+
+@pytest.mark.parametrize("kind", ["q4_1", "q4_k"])
+@pytest.mark.parametrize("M", [1, 17, 64])
+def test_gemm_batched_each_job_matches_oracle(kind, M):
+    """Weights sharing X in one launch: q/k/v-like rows, one with a ragged last workgroup."""
+    K = 1280
+    shapes = [256, 64, 96, 32]
+    chs = [_gen(kind, N, K, f"batched{i}") for i, N in enumerate(shapes)]
+    X = synth.gen_x(synth.rng("gpu-gemm", "batchedX", M), M, K)
+    devs = [dev_u8(c) for c in chs]
+    ws_ = [weight(d, N, K, kind) for d, N in zip(devs, shapes)]
+    Ys = [torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda") for N in shapes]
+    jobs = list(zip(ws_, Ys))
+    q().gemm_batched(jobs, dev_bf16(X), M, _ws_bytes(q().gemm_batched_ws(jobs)))
+    for c, N, Y in zip(chs, shapes, Ys):
+        yr, a = oracle.gemv_ref(oracle.weights_exact(c, kind, N, K), X)
+        assert oracle.tol_ratio(host(Y), yr, a) <= 1.0, N
+
+
+def test_gemm_batched_dense_8b_qkv_and_gate_up_full_size():
+    """The 8B-dense q/k/v and gate/up launches at M = 64, sampled tile rows of every job."""
+    specs = {s.name: s for s in synth.dense_8b_block_specs(1)}
+    X = synth.gen_x(synth.rng("dense_8b_block", "X", 4096), 64, 4096)
+    Xd = dev_bf16(X)
+    for group in (("L0.q", "L0.k", "L0.v"), ("L0.gate", "L0.up")):
+        chs = [specs[n].generate() for n in group]
+        ws_ = [weight(dev_u8(c), specs[n].N, specs[n].K, "q4_1") for c, n in zip(chs, group)]
+        Ys = [torch.full((64, specs[n].N), float("nan"), dtype=torch.float32, device="cuda") for n in group]
+        jobs = list(zip(ws_, Ys))
+        q().gemm_batched(jobs, Xd, 64, _ws_bytes(q().gemm_batched_ws(jobs)))
+        for i, (c, n, Y) in enumerate(zip(chs, group, Ys)):
+            TR = specs[n].N // 32
+            g = np.random.default_rng(100 + i)
+            tr = np.unique(np.concatenate([[0, TR - 1], g.integers(0, TR, 3)]))
+            yr, a = oracle.gemv_ref(oracle.weights_exact(c[tr], "q4_1", 32 * len(tr), 4096), X)
+            Yh = host(Y)
+            ysub = np.concatenate([Yh[:, 32 * t:32 * t + 32] for t in tr], axis=1)
+            assert oracle.tol_ratio(ysub, yr, a) <= 1.0, n
