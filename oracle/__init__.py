@@ -15,6 +15,11 @@ What it follows: the 1bit engine docs, page "NPU engine", section "Q4NX chunks"
 (tile grid, chunk kinds, decode formulas, the two Q8 code layouts) and the
 project's written chunk layout for the parts that page leaves to an unpublished
 header (listed in each function that depends on them).
+
+Parity unpinned: that in-chunk byte order of the q4_1 / Q4_K codes and of the
+q4_1, Q4_K and Q8 metadata, against real model files (no header or real tile
+is available to compare with).  Everything else here is pinned by tests that
+do not reuse this code's formulas (tests/test_oracle_pins.py).
 """
 from .decode import (KIND_BYTES, decode_fields, weights_exact, weights_f32, unpack_expected,
                      scalar_decode_chunk)
