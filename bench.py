@@ -578,7 +578,7 @@ def main():
         ach = per_launch_bytes / (avg_ms * 1e-3) / 1e9
         out["roofline"] = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": ach / HBM_PEAK_GBS, "traffic": profiled_traffic("k_gemv_q4"),
-                           "kernel": "k_gemv_q4<q4_1, M=1>",
+                           "kernel": "k_gemv_q4x<q4_1, M=1> (k_gemv_q4 family)",
                            "avg_launch_us": avg_ms * 1e3, "bytes_per_launch": per_launch_bytes,
                            "launches_timed": n_launch * args.steps}
         legs["decode"] = res

@@ -97,8 +97,12 @@ int pow2_at_least(int v, int cap) {
   return p;
 }
 
+#ifndef Q4NX_SMALL_MIN_TC
+#define Q4NX_SMALL_MIN_TC 17
+#endif
+
 int pick_waves(int64_t total_tr, int M, int max_tc) {
-  return (total_tr >= Q4NX_SMALL_ROWS || M > 2 || max_tc <= 16) ? 4 : 16;
+  return (total_tr >= Q4NX_SMALL_ROWS || M > 2 || max_tc < Q4NX_SMALL_MIN_TC) ? 4 : 16;
 }
 
 int pick_ks(int waves, int64_t total_tr, int TC) {
@@ -139,7 +143,8 @@ int run_batch(int kind, const q4nx_gemv_job* const* jobs, int n, int M, hipStrea
       wg += (g.TR + rpw - 1) / rpw;
     }
     b.n_jobs = cnt;
-    const hipError_t e = q4nx::launch_gemv(kind, M, waves, b, wg, s);
+    const hipError_t e =
+        q4nx::launch_gemv(kind, M, waves, b, wg, q4nx::gemv_xl_bytes(kind, M, waves, max_tc), s);
     if (e != hipSuccess) return hip_status(e, "gemv launch");
   }
   return Q4NX_OK;

@@ -63,6 +63,132 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_q4(const GemvBatch b) {
   }
 }
 
+// The same GEMV with the workgroup's activations prepared once in LDS.
+//
+// Per (activation row m, tile column c, group g) the 16 bf16 pairs the dot
+// chain takes and the group's (136-chain, sum x) are computed once per
+// workgroup instead of once per lane and chunk, and a wave's loop then reads
+// them from LDS (lgkmcnt) while its chunk loads are counted alone on vmcnt.
+// The activation loads are issued before the first chunk loads, so waiting for
+// them never waits for a chunk; chunk loads are unconditional buffer loads
+// (past the wave's run they read zero without memory traffic) running D chunks
+// ahead of the products, and there is no branch inside a group of D steps, so
+// every wait is for the chunk D steps back.  The host uses this kernel when
+// the prepared records (M * TC * 8 per job, 72 bytes each) fit XRP per thread
+// and the LDS budget; otherwise k_gemv_q4.
+template <int KIND, int M, int WAVES, int D>
+__global__ __launch_bounds__(64 * WAVES) void k_gemv_q4x(const GemvBatch b) {
+  constexpr int NT = 64 * WAVES;
+  constexpr int XRP = 2;
+  constexpr int CB = ChunkBytes<KIND>::value;
+  extern __shared__ __attribute__((aligned(16))) uint32_t xl[];
+  __shared__ float red[WAVES][32][M];
+  const GemvJob& J = b.job[find_job(b, blockIdx.x)];
+  const int ks = J.ks, rpw = WAVES / ks;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int slot = wave / ks, part = wave % ks;
+  const int tr0 = (blockIdx.x - J.wg_begin) * rpw;
+  const int tr = tr0 + slot < J.TR ? tr0 + slot : J.TR - 1;   // spare waves redo the last row, unstored
+  const int TC = J.TC, g = lane & 7;
+  const int c0 = part * TC / ks, c1 = (part + 1) * TC / ks;
+  const int R = M * TC * 8;
+
+  // 1. activations of record r = (m * TC + c) * 8 + g: 32 bf16 at x[m][32 * (8c + g)]
+  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(J.x, (uint32_t)(((M - 1) * J.ldx + TC * 256) * 2));
+  u32x4 xr[XRP][4];
+#pragma unroll
+  for (int p = 0; p < XRP; ++p) {
+    const int r = tid + NT * p, m = r / (TC * 8), rem = r - m * TC * 8;
+    const uint32_t off = (uint32_t)(m * J.ldx + 32 * rem) * 2;   // r >= R: m >= M, past the resource
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+      xr[p][d] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs, off + 16 * d, 0, 0));
+  }
+  // 2. the first D chunks of the wave's run
+  const __amdgpu_buffer_rsrc_t wrs =
+      make_rsrc(J.w + ((size_t)tr * TC + c0) * CB, (uint32_t)((c1 - c0) * CB));
+  Q4Chunk<KIND> ring[D];
+#pragma unroll
+  for (int j = 0; j < D; ++j) q4_load_rs<KIND>(wrs, j * CB, lane, ring[j]);
+  // 3. prepared records to LDS: pairs at xl[16 r], (d136, sum) at xl[16 R + 2 r]
+  float* sums = reinterpret_cast<float*>(xl + 16 * R);
+#pragma unroll
+  for (int p = 0; p < XRP; ++p) {
+    const int r = tid + NT * p;
+    XRaw<1> raw;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) raw.v[0][d] = xr[p][d];
+    XPrep<1> xp;
+    x_prep_raw<1>(raw, xp);
+    if (r < R) {
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+        *reinterpret_cast<u32x4*>(xl + 16 * r + 4 * d) =
+            u32x4{xp.p[0][4 * d], xp.p[0][4 * d + 1], xp.p[0][4 * d + 2], xp.p[0][4 * d + 3]};
+      sums[2 * r] = xp.d136[0];
+      sums[2 * r + 1] = xp.sum[0];
+    }
+  }
+  __syncthreads();
+
+  uint32_t kMask = 0x000F000Fu, kMagic = 0x43004300u;
+  asm volatile("" : "+s"(kMask));
+  asm volatile("" : "+v"(kMagic));
+  float acc[4][M];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[i][m] = 0.f;
+  auto step = [&](int j, int c) {
+    __builtin_amdgcn_sched_barrier(0);
+    XPrep<M> xp;
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const int r = (m * TC + c) * 8 + g;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(xl + 16 * r + 4 * d);
+        xp.p[m][4 * d] = v.x;
+        xp.p[m][4 * d + 1] = v.y;
+        xp.p[m][4 * d + 2] = v.z;
+        xp.p[m][4 * d + 3] = v.w;
+      }
+      xp.d136[m] = sums[2 * r];
+      xp.sum[m] = sums[2 * r + 1];
+    }
+    q4_compute<KIND, M>(ring[j], xp, kMask, kMagic, acc);
+    q4_load_rs<KIND>(wrs, (uint32_t)(c + D - c0) * CB, lane, ring[j]);
+  };
+  int base = c0;
+  for (; base + D <= c1; base += D) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) step(j, base + j);
+  }
+#pragma unroll
+  for (int j = 0; j + 1 < D; ++j)
+    if (base + j < c1) step(j, base + j);
+
+  q4_lane_reduce<M>(acc);
+  if (g == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int m = 0; m < M; ++m) red[wave][8 * i + (lane >> 3)][m] = acc[i][m];
+  }
+  __syncthreads();
+  for (int idx = tid; idx < rpw * 32 * M; idx += NT) {
+    const int s = idx / (32 * M), rem = idx - s * 32 * M;
+    const int r = rem / M, m = rem - r * M;
+    const int t = tr0 + s;
+    if (t < J.TR) {
+      float v = 0.f;
+      for (int p = 0; p < ks; ++p) v += red[s * ks + p][r][m];
+      J.y[(size_t)m * J.ldy + 32 * t + r] = v;
+    }
+  }
+}
+
 template <int KIND, int M, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void k_gemv_q8(const GemvBatch b) {
   constexpr int CB = 8704;
@@ -108,58 +234,86 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_q8(const GemvBatch b) {
 // ===========================================================================
 // launcher
 // ===========================================================================
+// Chunks in flight per wave in k_gemv_q4x: 2, or 1 for M > 1 in 16-wave
+// workgroups, whose waves hold at most 128 registers.  (Deeper rings cost
+// occupancy in the large launches and measured slower over a decode step.)
+#ifndef Q4NX_GEMVX_DEPTH
+#define Q4NX_GEMVX_DEPTH 2
+#endif
+template <int M, int WAVES>
+struct GemvXDepth {
+  static constexpr int value = (WAVES == 16 && M > 1) ? 1 : Q4NX_GEMVX_DEPTH;
+};
+
 template <int KIND, int M, int WAVES>
-static hipError_t launch_one(const GemvBatch& b, int n_wg, hipStream_t s) {
-  if constexpr (KIND == KIND_Q4_1 || KIND == KIND_Q4_K)
-    hipLaunchKernelGGL((k_gemv_q4<KIND, M, WAVES>), dim3(n_wg), dim3(64 * WAVES), 0, s, b);
-  else
+static hipError_t launch_one(const GemvBatch& b, int n_wg, int xl_bytes, hipStream_t s) {
+  if constexpr (KIND == KIND_Q4_1 || KIND == KIND_Q4_K) {
+    constexpr int D = GemvXDepth<M, WAVES>::value;
+    if (xl_bytes > 0)
+      hipLaunchKernelGGL((k_gemv_q4x<KIND, M, WAVES, D>), dim3(n_wg), dim3(64 * WAVES), xl_bytes, s, b);
+    else
+      hipLaunchKernelGGL((k_gemv_q4<KIND, M, WAVES>), dim3(n_wg), dim3(64 * WAVES), 0, s, b);
+  } else {
     hipLaunchKernelGGL((k_gemv_q8<KIND, M, WAVES>), dim3(n_wg), dim3(64 * WAVES), 0, s, b);
+  }
   return hipGetLastError();
 }
 
 template <int KIND, int WAVES>
-static hipError_t launch_m(int M, const GemvBatch& b, int n_wg, hipStream_t s) {
+static hipError_t launch_m(int M, const GemvBatch& b, int n_wg, int xl, hipStream_t s) {
   switch (M) {
-    case 1: return launch_one<KIND, 1, WAVES>(b, n_wg, s);
-    case 2: return launch_one<KIND, 2, WAVES>(b, n_wg, s);
-    case 3: return launch_one<KIND, 3, WAVES>(b, n_wg, s);
-    case 4: return launch_one<KIND, 4, WAVES>(b, n_wg, s);
-    case 5: return launch_one<KIND, 5, WAVES>(b, n_wg, s);
-    case 6: return launch_one<KIND, 6, WAVES>(b, n_wg, s);
-    case 7: return launch_one<KIND, 7, WAVES>(b, n_wg, s);
-    case 8: return launch_one<KIND, 8, WAVES>(b, n_wg, s);
+    case 1: return launch_one<KIND, 1, WAVES>(b, n_wg, xl, s);
+    case 2: return launch_one<KIND, 2, WAVES>(b, n_wg, xl, s);
+    case 3: return launch_one<KIND, 3, WAVES>(b, n_wg, xl, s);
+    case 4: return launch_one<KIND, 4, WAVES>(b, n_wg, xl, s);
+    case 5: return launch_one<KIND, 5, WAVES>(b, n_wg, xl, s);
+    case 6: return launch_one<KIND, 6, WAVES>(b, n_wg, xl, s);
+    case 7: return launch_one<KIND, 7, WAVES>(b, n_wg, xl, s);
+    case 8: return launch_one<KIND, 8, WAVES>(b, n_wg, xl, s);
   }
   return hipErrorInvalidValue;
 }
 
 template <int WAVES>
-static hipError_t launch_w(int kind, int M, const GemvBatch& b, int n_wg, hipStream_t s) {
+static hipError_t launch_w(int kind, int M, const GemvBatch& b, int n_wg, int xl, hipStream_t s) {
   switch (kind) {
-    case KIND_Q4_1: return launch_m<KIND_Q4_1, WAVES>(M, b, n_wg, s);
-    case KIND_Q4_K: return launch_m<KIND_Q4_K, WAVES>(M, b, n_wg, s);
-    case KIND_Q8_A: return launch_m<KIND_Q8_A, WAVES>(M, b, n_wg, s);
-    case KIND_Q8_B: return launch_m<KIND_Q8_B, WAVES>(M, b, n_wg, s);
+    case KIND_Q4_1: return launch_m<KIND_Q4_1, WAVES>(M, b, n_wg, xl, s);
+    case KIND_Q4_K: return launch_m<KIND_Q4_K, WAVES>(M, b, n_wg, xl, s);
+    case KIND_Q8_A: return launch_m<KIND_Q8_A, WAVES>(M, b, n_wg, 0, s);
+    case KIND_Q8_B: return launch_m<KIND_Q8_B, WAVES>(M, b, n_wg, 0, s);
   }
   return hipErrorInvalidValue;
 }
 
 template <int KIND>
-static hipError_t launch_small(int M, const GemvBatch& b, int n_wg, hipStream_t s) {
-  if (M == 1) return launch_one<KIND, 1, 16>(b, n_wg, s);
-  if (M == 2) return launch_one<KIND, 2, 16>(b, n_wg, s);
+static hipError_t launch_small(int M, const GemvBatch& b, int n_wg, int xl, hipStream_t s) {
+  if (M == 1) return launch_one<KIND, 1, 16>(b, n_wg, xl, s);
+  if (M == 2) return launch_one<KIND, 2, 16>(b, n_wg, xl, s);
   return hipErrorInvalidValue;
+}
+
+int gemv_xl_bytes(int kind, int M, int waves, int max_tc) {
+#if defined(Q4NX_GEMV_NO_XLDS)
+  return 0;
+#endif
+  if (kind != KIND_Q4_1 && kind != KIND_Q4_K) return 0;
+  const int R = M * max_tc * 8;
+  if (R > 2 * 64 * waves) return 0;          // two records per thread
+  const int bytes = R * 72;
+  return bytes <= 65536 ? bytes : 0;
 }
 
 // 16-wave workgroups hold at most 128 registers per lane, so they are used
 // for M <= 2 only.
-hipError_t launch_gemv(int kind, int M, int waves, const GemvBatch& b, int n_wg, hipStream_t s) {
-  if (waves == 4) return launch_w<4>(kind, M, b, n_wg, s);
+hipError_t launch_gemv(int kind, int M, int waves, const GemvBatch& b, int n_wg, int xl_bytes,
+                       hipStream_t s) {
+  if (waves == 4) return launch_w<4>(kind, M, b, n_wg, xl_bytes, s);
   if (waves == 16 && M <= 2) {
     switch (kind) {
-      case KIND_Q4_1: return launch_small<KIND_Q4_1>(M, b, n_wg, s);
-      case KIND_Q4_K: return launch_small<KIND_Q4_K>(M, b, n_wg, s);
-      case KIND_Q8_A: return launch_small<KIND_Q8_A>(M, b, n_wg, s);
-      case KIND_Q8_B: return launch_small<KIND_Q8_B>(M, b, n_wg, s);
+      case KIND_Q4_1: return launch_small<KIND_Q4_1>(M, b, n_wg, xl_bytes, s);
+      case KIND_Q4_K: return launch_small<KIND_Q4_K>(M, b, n_wg, xl_bytes, s);
+      case KIND_Q8_A: return launch_small<KIND_Q8_A>(M, b, n_wg, 0, s);
+      case KIND_Q8_B: return launch_small<KIND_Q8_B>(M, b, n_wg, 0, s);
     }
   }
   return hipErrorInvalidValue;

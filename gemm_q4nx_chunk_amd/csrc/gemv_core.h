@@ -46,6 +46,28 @@ __device__ __forceinline__ void q4_load(const uint8_t* __restrict__ ck, int lane
   }
 }
 
+// q4_load through a buffer resource over a run of chunks: off is the chunk's
+// byte offset in the run.  Offsets past the run read zero without touching
+// memory, so a prefetch past the last chunk needs no branch.
+template <int KIND>
+__device__ __forceinline__ void q4_load_rs(__amdgpu_buffer_rsrc_t rs, uint32_t off, int lane,
+                                           Q4Chunk<KIND>& c) {
+  constexpr int kNt = 2;   // nontemporal: weights are read once
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    c.q[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 1024 * i + 16 * lane, 0, kNt));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (KIND == KIND_Q4_1) {
+      c.meta[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, off + 4096 + 256 * i + 4 * lane, 0, 0);
+      c.rowsm[i] = 0;
+    } else {
+      c.meta[i] = __builtin_amdgcn_raw_buffer_load_b16(rs, off + 4096 + 128 * i + 2 * lane, 0, 0);
+      c.rowsm[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, off + 4608 + 32 * i + 4 * (lane >> 3), 0, 0);
+    }
+  }
+}
+
 // Activation pairs (x[k], x[k+4]) of the lane's group for one tile column, in
 // the order the code chain uses them, the 136-chain, and sum x taken as that
 // chain / 136 (a few fp32 roundings; it is only ever multiplied by z + 8s, and

@@ -108,7 +108,11 @@ __device__ __forceinline__ int find_job(const GemvBatch& b, int wg) {
 }
 
 // Host-side launchers (gemv.hip, gemm.hip, decode.hip, moe.hip).
-hipError_t launch_gemv(int kind, int M, int waves, const GemvBatch& b, int n_wg, hipStream_t s);
+// Dynamic LDS bytes of the prepared-activation GEMV for a launch whose jobs
+// have at most max_tc tile columns, or 0 when that kernel does not apply.
+int gemv_xl_bytes(int kind, int M, int waves, int max_tc);
+hipError_t launch_gemv(int kind, int M, int waves, const GemvBatch& b, int n_wg, int xl_bytes,
+                       hipStream_t s);
 hipError_t launch_unpack(int kind, const uint8_t* w, int TR, int TC, uint8_t* codes,
                          uint16_t* meta0, uint16_t* meta1, uint16_t* row_meta, hipStream_t s);
 hipError_t launch_decode(int kind, const uint8_t* w, int TR, int TC, float* out, hipStream_t s);
