@@ -506,7 +506,8 @@ def moe_leg(steps, warmup, graph):
         res[f"T{T}"] = {"ms_per_step": ms, "layers": L, "weight_bytes": nbytes,
                         "distinct_experts_per_layer": uniq / L, "GB_s": nbytes / (ms * 1e-3) / 1e9,
                         "pct_hbm_peak": 100 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                        "TFLOP_s": flops / (ms * 1e-3) / 1e12, "launches": 4 * L}
+                        "TFLOP_s": flops / (ms * 1e-3) / 1e12,
+                        "launches": (3 if T * k <= 64 else 4) * L}
         del wss, X, ids, ps, Ys
     del layers
     torch.cuda.empty_cache()

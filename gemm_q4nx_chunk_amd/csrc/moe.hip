@@ -284,6 +284,326 @@ __global__ __launch_bounds__(256) void k_moe_down(MoeArgs a, int ks_r, int ks_s)
 }
 
 // ---------------------------------------------------------------------------
+// weight-stationary gate/up and down
+// ---------------------------------------------------------------------------
+// One work item is one tile row of one selected expert (or of the shared
+// expert) for ALL the tokens routed to it: each wave loads its chunks of the
+// row once, keeps them in registers, and runs every batch of TB tokens against
+// them, so an expert's weights cross HBM once per call however popular it is.
+// A batch's activations are prepared once per workgroup into LDS (the dot-chain
+// pairs and group sums of k_gemv_q4x), so the loop waits on nothing but LDS.
+// The arithmetic per token is the one of the GEMV (same chunk split, chunk
+// order and reduction order), so a token's bits do not depend on its batch.
+//
+// With at most kMoeSmallPairs (token, slot) pairs every workgroup sorts them
+// itself (one wave, rank by comparison) and no route kernel runs.
+
+constexpr int kMoeSmallPairs = 64;
+// Chunks a wave keeps in registers: gate/up waves hold half a d_model row
+// (4 chunks at d_model 2048), down waves one or two chunks.
+constexpr int kMoeCpwGateUp = 4;
+constexpr int kMoeCpwDown = 2;
+
+struct MoeSmallRoute {
+  int32_t sorted[kMoeSmallPairs];   // pair index at each sorted position
+  int32_t seg[kMoeSmallPairs][3];   // (expert, first position, count)
+  int32_t nseg, bad;
+};
+
+// Wave 0 sorts the pairs by (expert, pair); invalid ids go last, unsegmented.
+__device__ __forceinline__ void moe_route_small(const MoeArgs& a, MoeSmallRoute& rt) {
+  const int lane = threadIdx.x & 63, P = a.T * a.k;
+  if (threadIdx.x < 64) {
+    uint32_t key = 0xFFFFFFFFu;
+    int e = a.n_experts;
+    bool ok = false;
+    if (lane < P) {
+      e = a.ids[lane];
+      ok = e >= 0 && e < a.n_experts;
+      key = ((uint32_t)(ok ? e : a.n_experts) << 12) | (uint32_t)lane;
+    }
+    int rank = 0;
+    for (int j = 0; j < P; ++j) rank += __shfl(key, j) < key ? 1 : 0;
+    const uint64_t bad = __ballot(lane < P && !ok);
+    if (lane < P) rt.sorted[rank] = lane;
+    // From here lane s describes sorted position s (LDS is in order within a wave).
+    __builtin_amdgcn_wave_barrier();
+    const int pi = lane < P ? rt.sorted[lane] : 0;
+    const int es = lane < P ? a.ids[pi] : -1;
+    const bool vs = lane < P && es >= 0 && es < a.n_experts;
+    const int eprev = __shfl_up(es, 1);
+    const bool start = vs && (lane == 0 || eprev != es);
+    const uint64_t starts = __ballot(start);
+    const uint64_t valid = __ballot(vs);
+    if (start) {
+      const int u = __popcll(starts & ((1ull << lane) - 1));
+      const uint64_t later = starts & ~((2ull << lane) - 1);
+      const int end = later ? __ffsll((long long)later) - 1 : __popcll(valid);
+      rt.seg[u][0] = es;
+      rt.seg[u][1] = lane;
+      rt.seg[u][2] = end - lane;
+    }
+    if (lane == 0) {
+      rt.nseg = __popcll(starts);
+      rt.bad = bad ? 1 : 0;
+    }
+  }
+  __syncthreads();
+}
+
+// Prepared activation records of TB rows (row m at src[m]) over TC tile
+// columns, record (m * TC + c) * 8 + g at xl[16 r] and its (d136, sum) at
+// xl[16 R + 2 r]; all threads of the workgroup take part.
+template <int TB>
+__device__ __forceinline__ void moe_stage(const uint16_t* const (&src)[TB], int TC, uint32_t* xl) {
+  const int R = TB * TC * 8;
+  float* sums = reinterpret_cast<float*>(xl + 16 * R);
+  for (int r = threadIdx.x; r < R; r += 256) {
+    const int m = r / (TC * 8), rem = r - m * TC * 8;
+    const uint16_t* p = src[0];
+#pragma unroll
+    for (int i = 1; i < TB; ++i)
+      if (m == i) p = src[i];
+    XRaw<1> raw;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) raw.v[0][d] = load16(p + 32 * rem + 8 * d);
+    XPrep<1> xp;
+    x_prep_raw<1>(raw, xp);
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+      *reinterpret_cast<u32x4*>(xl + 16 * r + 4 * d) =
+          u32x4{xp.p[0][4 * d], xp.p[0][4 * d + 1], xp.p[0][4 * d + 2], xp.p[0][4 * d + 3]};
+    sums[2 * r] = xp.d136[0];
+    sums[2 * r + 1] = xp.sum[0];
+  }
+}
+
+// acc += the held chunks [0, nc) (tile columns c0 + j) against the staged rows.
+template <int KIND, int TB, int CPW>
+__device__ __forceinline__ void moe_chunks(const Q4Chunk<KIND> (&ch)[CPW], int nc, int c0, int TC,
+                                           const uint32_t* xl, uint32_t kMask, uint32_t kMagic,
+                                           float (&acc)[4][TB]) {
+  const int R = TB * TC * 8, g = threadIdx.x & 7;
+  const float* sums = reinterpret_cast<const float*>(xl + 16 * R);
+#pragma unroll
+  for (int j = 0; j < CPW; ++j) {
+    if (j < nc) {
+      XPrep<TB> xp;
+#pragma unroll
+      for (int m = 0; m < TB; ++m) {
+        const int r = (m * TC + c0 + j) * 8 + g;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(xl + 16 * r + 4 * d);
+          xp.p[m][4 * d] = v.x;
+          xp.p[m][4 * d + 1] = v.y;
+          xp.p[m][4 * d + 2] = v.z;
+          xp.p[m][4 * d + 3] = v.w;
+        }
+        xp.d136[m] = sums[2 * r];
+        xp.sum[m] = sums[2 * r + 1];
+      }
+      q4_compute<KIND, TB>(ch[j], xp, kMask, kMagic, acc);
+    }
+  }
+}
+
+template <int KIND, int CPW>
+__device__ __forceinline__ void moe_load(const uint8_t* row, int c0, int nc, int lane,
+                                         Q4Chunk<KIND> (&ch)[CPW]) {
+  constexpr int CB = ChunkBytes<KIND>::value;
+#pragma unroll
+  for (int j = 0; j < CPW; ++j)
+    if (j < nc) q4_load<KIND>(row + (size_t)(c0 + j) * CB, lane, ch[j]);
+}
+
+// Segment u: (expert, first sorted position, count).
+template <bool SMALL>
+__device__ __forceinline__ void moe_seg(const MoeArgs& a, const MoeSmallRoute& rt, int u, int& e,
+                                        int& start, int& cnt) {
+  if constexpr (SMALL) {
+    e = rt.seg[u][0]; start = rt.seg[u][1]; cnt = rt.seg[u][2];
+  } else {
+    e = a.seg[3 * u]; start = a.seg[3 * u + 1]; cnt = a.seg[3 * u + 2];
+  }
+}
+
+template <bool SMALL>
+__device__ __forceinline__ int moe_sorted(const MoeArgs& a, const MoeSmallRoute& rt, int pos) {
+  if constexpr (SMALL) return rt.sorted[pos];
+  else return a.sorted[pos];
+}
+
+// Items: nseg * (De / 32) routed tile rows, then Ds / 32 shared ones.  Waves
+// 0-1 take the gate row, 2-3 the up row, each half of the row's chunks.
+template <int KIND, int TB, bool SMALL>
+__global__ __launch_bounds__(256) void k_moe_gateup_s(MoeArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint32_t xl[];
+  __shared__ float red[4][32][TB];
+  __shared__ MoeSmallRoute rt;
+  if constexpr (SMALL) {
+    moe_route_small(a, rt);
+    if (blockIdx.x == 0 && threadIdx.x == 0) a.hdr[0] = (uint32_t)rt.bad;
+  }
+  const int nseg = SMALL ? rt.nseg : (int)a.hdr[1];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int TC = a.D / 256, P = a.T * a.k;
+  const int rows_r = a.De / 32, rows_s = a.Ds / 32;
+  const int n_items = nseg * rows_r + rows_s;
+  uint32_t kMask = 0x000F000Fu, kMagic = 0x43004300u;
+  asm volatile("" : "+s"(kMask));
+  asm volatile("" : "+v"(kMagic));
+  const int half = wave & 1;
+  const int c0 = half * TC / 2, nc = (half + 1) * TC / 2 - c0;
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    const bool shared = item >= nseg * rows_r;
+    int e = 0, start = 0, cnt = a.T, tr;
+    if (!shared) {
+      const int u = item / rows_r;
+      tr = item - u * rows_r;
+      moe_seg<SMALL>(a, rt, u, e, start, cnt);
+    } else {
+      tr = item - nseg * rows_r;
+    }
+    const uint8_t* w = shared ? (wave < 2 ? a.sgate : a.sup)
+                              : (wave < 2 ? a.gate + (size_t)e * a.gate_stride : a.up + (size_t)e * a.up_stride);
+    const uint8_t* row = w + (size_t)tr * TC * ChunkBytes<KIND>::value;
+    constexpr int CPW = kMoeCpwGateUp;
+    Q4Chunk<KIND> ch[CPW];
+    for (int b0 = 0; b0 < cnt; b0 += TB) {
+      const int ntok = min(TB, cnt - b0);
+      const uint16_t* src[TB];
+#pragma unroll
+      for (int m = 0; m < TB; ++m) {
+        const int mm = m < ntok ? m : 0;
+        const int t = shared ? b0 + mm : moe_sorted<SMALL>(a, rt, start + b0 + mm) / a.k;
+        src[m] = a.X + (size_t)t * a.D;
+      }
+      float acc[4][TB];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int m = 0; m < TB; ++m) acc[i][m] = 0.f;
+      // weights first (held across batches when the wave's run fits), then this batch's rows
+      if (b0 == 0 && nc <= CPW) moe_load<KIND, CPW>(row, c0, nc, lane, ch);
+      moe_stage<TB>(src, TC, xl);
+      __syncthreads();
+      for (int r0 = 0; r0 < nc; r0 += CPW) {
+        if (nc > CPW) moe_load<KIND, CPW>(row, c0 + r0, min(CPW, nc - r0), lane, ch);
+        moe_chunks<KIND, TB, CPW>(ch, min(CPW, nc - r0), c0 + r0, TC, xl, kMask, kMagic, acc);
+      }
+      q4_lane_reduce<TB>(acc);
+      if ((lane & 7) == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int m = 0; m < TB; ++m) red[wave][8 * i + (lane >> 3)][m] = acc[i][m];
+      }
+      __syncthreads();
+      for (int idx = threadIdx.x; idx < 32 * TB; idx += 256) {
+        const int r = idx / TB, m = idx - r * TB;
+        if (m < ntok) {
+          const float g = red[0][r][m] + red[1][r][m];
+          const float u = red[2][r][m] + red[3][r][m];
+          const float hv = g / (1.0f + expf(-g)) * u;
+          const uint16_t hb = __builtin_bit_cast(uint16_t, (__bf16)hv);
+          const int col = 32 * tr + r;
+          const int pos = shared ? P + b0 + m : start + b0 + m;
+          a.hbuf[(size_t)pos * a.hstride + col] = hb;
+          if (shared) {
+            if (a.dbg_h_shared) a.dbg_h_shared[(size_t)(b0 + m) * a.Ds + col] = hb;
+          } else if (a.dbg_h) {
+            a.dbg_h[(size_t)moe_sorted<SMALL>(a, rt, pos) * a.De + col] = hb;
+          }
+        }
+      }
+      __syncthreads();   // red and xl are reused by the next batch
+    }
+  }
+}
+
+// Items: nseg * (D / 32 / rpw_r) routed row groups, then the shared ones; ks
+// waves split a tile row's chunks, rpw = 4 / ks rows per workgroup.
+template <int KIND, int TB, bool SMALL>
+__global__ __launch_bounds__(256) void k_moe_down_s(MoeArgs a, int ks_r, int ks_s) {
+  extern __shared__ __attribute__((aligned(16))) uint32_t xl[];
+  __shared__ float red[4][32][TB];
+  __shared__ MoeSmallRoute rt;
+  if constexpr (SMALL) moe_route_small(a, rt);
+  const int nseg = SMALL ? rt.nseg : (int)a.hdr[1];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int rows = a.D / 32, P = a.T * a.k;
+  const int gr = rows / (4 / ks_r), gs = a.Ds ? rows / (4 / ks_s) : 0;
+  const int n_items = nseg * gr + gs;
+  uint32_t kMask = 0x000F000Fu, kMagic = 0x43004300u;
+  asm volatile("" : "+s"(kMask));
+  asm volatile("" : "+v"(kMagic));
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    const bool shared = item >= nseg * gr;
+    int e = 0, start = 0, cnt = a.T, grp;
+    if (!shared) {
+      const int u = item / gr;
+      grp = item - u * gr;
+      moe_seg<SMALL>(a, rt, u, e, start, cnt);
+    } else {
+      grp = item - nseg * gr;
+    }
+    const int ks = shared ? ks_s : ks_r, rpw = 4 / ks;
+    const int TC = (shared ? a.Ds : a.De) / 256;
+    const int slot = wave / ks, part = wave % ks;
+    const int tr0 = grp * rpw, tr = tr0 + slot;
+    const int c0 = part * TC / ks, nc = (part + 1) * TC / ks - c0;
+    const uint8_t* row = (shared ? a.sdown : a.down + (size_t)e * a.down_stride) +
+                         (size_t)tr * TC * ChunkBytes<KIND>::value;
+    constexpr int CPW = kMoeCpwDown;
+    Q4Chunk<KIND> ch[CPW];
+    for (int b0 = 0; b0 < cnt; b0 += TB) {
+      const int ntok = min(TB, cnt - b0);
+      const uint16_t* src[TB];
+#pragma unroll
+      for (int m = 0; m < TB; ++m) {
+        const int mm = m < ntok ? m : 0;
+        const int pos = shared ? P + b0 + mm : start + b0 + mm;
+        src[m] = a.hbuf + (size_t)pos * a.hstride;
+      }
+      float acc[4][TB];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int m = 0; m < TB; ++m) acc[i][m] = 0.f;
+      // weights first (held across batches when the wave's run fits), then this batch's rows
+      if (b0 == 0 && nc <= CPW) moe_load<KIND, CPW>(row, c0, nc, lane, ch);
+      moe_stage<TB>(src, TC, xl);
+      __syncthreads();
+      for (int r0 = 0; r0 < nc; r0 += CPW) {
+        if (nc > CPW) moe_load<KIND, CPW>(row, c0 + r0, min(CPW, nc - r0), lane, ch);
+        moe_chunks<KIND, TB, CPW>(ch, min(CPW, nc - r0), c0 + r0, TC, xl, kMask, kMagic, acc);
+      }
+      q4_lane_reduce<TB>(acc);
+      if ((lane & 7) == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int m = 0; m < TB; ++m) red[wave][8 * i + (lane >> 3)][m] = acc[i][m];
+      }
+      __syncthreads();
+      for (int idx = threadIdx.x; idx < rpw * 32 * TB; idx += 256) {
+        const int s2 = idx / (32 * TB), rem = idx - s2 * 32 * TB;
+        const int r = rem / TB, m = rem - r * TB;
+        const int t_row = tr0 + s2;
+        if (m < ntok) {
+          float v = 0.f;
+          for (int p2 = 0; p2 < ks; ++p2) v += red[s2 * ks + p2][r][m];
+          const int dst = shared ? P + b0 + m : moe_sorted<SMALL>(a, rt, start + b0 + m);
+          a.dbuf[(size_t)dst * a.D + 32 * t_row + r] = v;
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // combine
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_moe_combine(MoeArgs a) {
@@ -315,16 +635,34 @@ template <int KIND, int TB>
 static hipError_t moe_run(const MoeArgs& a, hipStream_t s) {
   const int P = a.T * a.k;
   const int nseg_max = P < a.n_experts ? P : a.n_experts;
+  const int tcr = a.De / 256, tcs = a.Ds ? a.Ds / 256 : 1;
+  const int ks_r = tcr >= 4 ? 4 : (tcr >= 2 ? 2 : 1);
+  const int ks_s = tcs >= 4 ? 4 : (tcs >= 2 ? 2 : 1);
+  const int rows = a.D / 32;
+  // Few pairs (decode): weight-stationary kernels with routing in every
+  // workgroup, when a batch's prepared rows fit in 64 KB of LDS.  Many pairs
+  // (prompt blocks): the route kernel, then one work item per (token batch,
+  // tile row), which spreads a popular expert's batches over many CUs (holding
+  // its chunks in one workgroup serialises them, measured slower).
+  const int rec = 8 * 72 * TB;
+  const int xl_gu = rec * (a.D / 256);
+  const int xl_dn = rec * ((a.De > a.Ds ? a.De : a.Ds) / 256);
+  const bool small = P <= kMoeSmallPairs;
+  if (small && xl_gu <= 65536 && xl_dn <= 65536) {
+    const int gu_items = nseg_max * (a.De / 32) + a.Ds / 32;
+    const int dn_items = nseg_max * (rows / (4 / ks_r)) + (a.Ds ? rows / (4 / ks_s) : 0);
+    const dim3 g_gu(gu_items < 4096 ? gu_items : 4096), g_dn(dn_items < 4096 ? dn_items : 4096);
+    hipLaunchKernelGGL((k_moe_gateup_s<KIND, TB, true>), g_gu, dim3(256), xl_gu, s, a);
+    hipLaunchKernelGGL((k_moe_down_s<KIND, TB, true>), g_dn, dim3(256), xl_dn, s, a, ks_r, ks_s);
+    hipLaunchKernelGGL(k_moe_combine, dim3((a.D + 255) / 256, a.T), dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
   const int nb_r = (P + nseg_max * (TB - 1)) / TB;        // bound on routed batches
   const int nb_s = a.Ds ? (a.T + TB - 1) / TB : 0;
   hipLaunchKernelGGL(k_moe_route, dim3(1), dim3(1024), 0, s, a);
   const int gu_items = nb_r * (a.De / 32) + nb_s * (a.Ds / 32);
   hipLaunchKernelGGL((k_moe_gateup<KIND, TB>), dim3(gu_items < 4096 ? gu_items : 4096), dim3(256),
                      0, s, a);
-  const int tcr = a.De / 256, tcs = a.Ds ? a.Ds / 256 : 1;
-  const int ks_r = tcr >= 4 ? 4 : (tcr >= 2 ? 2 : 1);
-  const int ks_s = tcs >= 4 ? 4 : (tcs >= 2 ? 2 : 1);
-  const int rows = a.D / 32;
   const int dn_items = nb_r * (rows / (4 / ks_r)) + nb_s * (rows / (4 / ks_s));
   hipLaunchKernelGGL((k_moe_down<KIND, TB>), dim3(dn_items < 4096 ? dn_items : 4096), dim3(256),
                      0, s, a, ks_r, ks_s);
