@@ -126,13 +126,16 @@ __global__ __launch_bounds__(256) void k_plan(PlanArgs a) {
       int xoff[M];
 #pragma unroll
       for (int m = 0; m < M; ++m) xoff[m] = 2 * (m * J.ldx + 32 * g);
+      // all of the unit's activation loads at once: one round trip, not one per chunk
+      XRaw<M> xr[CPW];
+#pragma unroll
+      for (int i = 0; i < CPW; ++i)
+        x_raw_coherent<M>(xrs, xoff, 256 * (c0 + (i < nc ? i : 0)), xr[i]);
 #pragma unroll
       for (int i = 0; i < CPW; ++i) {
         if (i < nc) {
-          XRaw<M> xr;
-          x_raw_coherent<M>(xrs, xoff, 256 * (c0 + i), xr);
           XPrep<M> xp;
-          x_prep_raw<M>(xr, xp);
+          x_prep_raw<M>(xr[i], xp);
           q4_compute<KIND, M>(ch[i], xp, kMask, kMagic, acc);
         }
       }
