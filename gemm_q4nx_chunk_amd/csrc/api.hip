@@ -274,7 +274,9 @@ int gemm_launch(q4nx::GemmArgs& a, int kind, void* ws, size_t ws_bytes, void* st
   a.cnt = need ? static_cast<uint32_t*>(ws) : nullptr;
   a.partial = need ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + q4nx::gemm_cnt_bytes(a.NB))
                    : nullptr;
-  const hipError_t e = q4nx::launch_gemm(kind, a, static_cast<hipStream_t>(stream));
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool local = a.S > 1 && q4nx::xcd_round_robin(st) == 1;
+  const hipError_t e = q4nx::launch_gemm(kind, a, local, st);
   return hip_status(e, name);
 }
 

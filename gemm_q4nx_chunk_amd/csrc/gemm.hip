@@ -118,12 +118,20 @@ __device__ __forceinline__ bf16x8 dequant8(uint32_t w, float s, float z_lo, floa
 // wait counts stay exact: a step waits only for its own chunk and, at its
 // end, for the next X tile.  Waves past the last tile row and X rows past M
 // read clamped, in-bounds data whose results are not stored.
-template <int KIND, bool TWO, int D>
-#ifndef Q4NX_GEMM_WAVES_PER_EU
-#define Q4NX_GEMM_WAVES_PER_EU 4
+#ifndef Q4NX_GEMM_QBARRIER
+#define Q4NX_GEMM_QBARRIER 0
 #endif
-// Two workgroups per CU (4 waves per SIMD, at most 128 VGPRs each).
-__global__ __launch_bounds__(64 * kGemmWaves) __attribute__((amdgpu_waves_per_eu(Q4NX_GEMM_WAVES_PER_EU, Q4NX_GEMM_WAVES_PER_EU)))
+// Waves per SIMD the kernel is compiled for: M > 32 (two accumulator tiles)
+// one workgroup per CU, M <= 32 two (at most 128 VGPRs).
+#ifndef Q4NX_GEMM_WPE_TWO
+#define Q4NX_GEMM_WPE_TWO 2
+#endif
+#ifndef Q4NX_GEMM_WPE_ONE
+#define Q4NX_GEMM_WPE_ONE 4
+#endif
+template <int KIND, bool TWO, int D, bool LOCAL>
+__global__ __launch_bounds__(64 * kGemmWaves)
+__attribute__((amdgpu_waves_per_eu(TWO ? Q4NX_GEMM_WPE_TWO : Q4NX_GEMM_WPE_ONE, TWO ? Q4NX_GEMM_WPE_TWO : Q4NX_GEMM_WPE_ONE)))
 void k_gemm_q4(GemmArgs a) {
   constexpr int CB = ChunkBytes<KIND>::value;
   constexpr int NT = 64 * kGemmWaves;
@@ -134,7 +142,23 @@ void k_gemm_q4(GemmArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave: row data in SGPRs
   const int h = lane >> 5, n = lane & 31;
-  const int nb = blockIdx.x, part = blockIdx.y;
+  // LOCAL: a 1-D grid laid out so that every K part of workgroup row nb has a
+  // linear id = nb (mod 8), i.e. runs on XCD nb % 8 (workgroups are dealt to
+  // the 8 XCDs round-robin by linear id; the host checks this once per device
+  // and the kernel flags any workgroup that finds itself elsewhere).  Then the
+  // parts' partial tiles and arrival counter only ever meet in that XCD's L2.
+  int nb, part;
+  if constexpr (LOCAL) {
+    const int L = blockIdx.x, r = L >> 3;
+    nb = 8 * (r / a.S) + (L & 7);
+    part = r % a.S;
+    if (nb >= a.NB) return;
+    if (tid == 0 && (int)(__builtin_amdgcn_s_getreg((3 << 11) | 20) & 15) != (L & 7))   // HW_REG_XCC_ID
+      __hip_atomic_fetch_or(a.cnt + a.NB, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    nb = blockIdx.x;
+    part = blockIdx.y;
+  }
   int ji = 0;
   for (int i = 1; i < a.n_jobs; ++i)
     if (nb >= a.job[i].nb0) ji = i;
@@ -163,17 +187,19 @@ void k_gemm_q4(GemmArgs a) {
     const int piece = tid + NT * p, row = piece >> 5, c16 = piece & 31;
     xoff[p] = (uint32_t)((row < M ? row : M - 1) * K + c16 * 8) * 2;
   }
-  u32x4 xr[XP];
-  auto xload = [&](int tc) {
+  // X tiles are loaded two tile columns ahead: xr[b] holds the tile whose
+  // column has parity b (relative to tc0) until it is written to xs[b].
+  u32x4 xr[2][XP];
+  auto xload = [&](int b, int tc) {
 #pragma unroll
     for (int p = 0; p < XP; ++p)
-      xr[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs, xoff[p] + tc * 512, 0, 0));
+      xr[b][p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs, xoff[p] + tc * 512, 0, 0));
   };
-  auto xstore = [&](int buf) {
+  auto xstore = [&](int b) {
 #pragma unroll
     for (int p = 0; p < XP; ++p) {
       const int piece = tid + NT * p, row = piece >> 5, c16 = piece & 31;
-      *reinterpret_cast<u32x4*>(&xs[buf][row * kXs + c16 * 8]) = xr[p];
+      *reinterpret_cast<u32x4*>(&xs[b][row * kXs + c16 * 8]) = xr[b][p];
     }
   };
 
@@ -182,20 +208,25 @@ void k_gemm_q4(GemmArgs a) {
   for (int v = 0; v < 16; ++v) { acc0[v] = 0.f; acc1[v] = 0.f; }
 
   GemmChunk<KIND> c[D];
-  xload(tc0);
+  xload(0, tc0);
 #pragma unroll
   for (int j = 0; j < D; ++j) gemm_load<KIND>(wrs, j * CB, n, h, c[j]);
   xstore(0);
+  xload(1, tc0 + 1);
 
-  // One tile column: t's X tile is in xs[(t - tc0) & 1] and its chunk in c[j].
+  // One tile column t (parity j relative to tc0): its X tile is in xs[j], its
+  // chunk in c[j]; the tile of t + 1 is in flight in xr[j ^ 1].
+  static_assert(D % 2 == 0, "the X double buffer follows the chunk ring's parity");
   auto step = [&](int j, int t) {
-    const int buf = (t - tc0) & 1;
-    __syncthreads();                       // X tile t is in xs[buf]; xs[buf ^ 1] is free
-    xload(t + 1);
+    __syncthreads();                       // X tile t is in xs[j]; xs[j ^ 1] is free
+    xload(j, t + 2);                       // xr[j] went to LDS at the end of step t - 1
     __builtin_amdgcn_sched_barrier(0);     // issue the X loads before the products
-    const uint16_t* xb = xs[buf] + n * kXs + 128 * h;
+    const uint16_t* xb = xs[j] + n * kXs + 128 * h;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
+#if Q4NX_GEMM_QBARRIER
+      __builtin_amdgcn_sched_barrier(0);   // bound how far operand reads are hoisted (registers)
+#endif
       float s, z;
       group_sz<KIND>(c[j], q, s, z);
       const float z_lo = fmaf(-1024.f, s, z), s16 = s * 0.0625f, z_hi = fmaf(-64.f, s, z);
@@ -212,7 +243,7 @@ void k_gemm_q4(GemmArgs a) {
       }
     }
     gemm_load<KIND>(wrs, (uint32_t)(t + D - tc0) * CB, n, h, c[j]);
-    xstore(buf ^ 1);
+    xstore(j ^ 1);                         // tile t + 1, loaded during step t - 1
   };
   // Full groups of D tile columns, then the last (tc1 - tc0) % D: no branch
   // inside a group, so every wait is for the chunk D tile columns back.
@@ -254,14 +285,20 @@ void k_gemm_q4(GemmArgs a) {
   const uint32_t part_bytes = (uint32_t)(kPartBytes * a.S);
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.partial + (size_t)nb * a.S * (kPartBytes / 4), part_bytes);
   const uint32_t lane_off = (uint32_t)(wave * 8 * 64 + lane) * 16;
+  // LOCAL: plain stores (they complete in this XCD's L2) and L2 atomics;
+  // otherwise device-scope (sc1) stores, loads and atomics.
+  constexpr int kStPol = LOCAL ? 0 : kCpolSc1;
+  constexpr int kLdPol = LOCAL ? 1 : kCpolSc1;   // sc0: past this CU's L1
 #pragma unroll
   for (int g = 0; g < G; ++g)
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, mine[g]), rs,
-                                           lane_off + part * (uint32_t)kPartBytes + g * 1024, 0, kCpolSc1);
+                                           lane_off + part * (uint32_t)kPartBytes + g * 1024, 0, kStPol);
   wait_stores();
   __syncthreads();
-  if (tid == 0)
-    s_old = __hip_atomic_fetch_add(a.cnt + nb, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) {
+    if constexpr (LOCAL) s_old = __hip_atomic_fetch_add(a.cnt + nb, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    else s_old = __hip_atomic_fetch_add(a.cnt + nb, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   __syncthreads();
   if (s_old != (uint32_t)a.S - 1) return;
 
@@ -276,7 +313,7 @@ void k_gemm_q4(GemmArgs a) {
 #pragma unroll
       for (int g = 0; g < G; ++g)
         in[j][g] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                 rs, lane_off + (p0 + j) * (uint32_t)kPartBytes + g * 1024, 0, kCpolSc1));
+                                                 rs, lane_off + (p0 + j) * (uint32_t)kPartBytes + g * 1024, 0, kLdPol));
 #pragma unroll
     for (int j = 0; j < PB; ++j)
       if (p0 + j < a.S)
@@ -284,22 +321,62 @@ void k_gemm_q4(GemmArgs a) {
         for (int g = 0; g < G; ++g) sum[g] += in[j][g];
   }
   if (active) store_y(sum);
-  if (tid == 0) __hip_atomic_store(a.cnt + nb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) {
+    if constexpr (LOCAL) __hip_atomic_store(a.cnt + nb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    else __hip_atomic_store(a.cnt + nb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
-hipError_t launch_gemm(int kind, const GemmArgs& a, hipStream_t s) {
-  const dim3 grid(a.NB, a.S), block(64 * kGemmWaves);
-  const bool two = a.M > 32;
-  if (kind == KIND_Q4_1) {
-    if (two) hipLaunchKernelGGL((k_gemm_q4<KIND_Q4_1, true, kGemmDepth>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_gemm_q4<KIND_Q4_1, false, kGemmDepth>), grid, block, 0, s, a);
-  } else if (kind == KIND_Q4_K) {
-    if (two) hipLaunchKernelGGL((k_gemm_q4<KIND_Q4_K, true, kGemmDepth>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_gemm_q4<KIND_Q4_K, false, kGemmDepth>), grid, block, 0, s, a);
+template <int KIND, bool TWO>
+static hipError_t launch_kind(const GemmArgs& a, bool local, hipStream_t s) {
+  const dim3 block(64 * kGemmWaves);
+  if (local && a.S > 1) {
+    const dim3 grid(8 * ((a.NB + 7) / 8) * a.S);
+    hipLaunchKernelGGL((k_gemm_q4<KIND, TWO, kGemmDepth, true>), grid, block, 0, s, a);
   } else {
-    return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k_gemm_q4<KIND, TWO, kGemmDepth, false>), dim3(a.NB, a.S), block, 0, s, a);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_gemm(int kind, const GemmArgs& a, bool local, hipStream_t s) {
+  const bool two = a.M > 32;
+  if (kind == KIND_Q4_1) return two ? launch_kind<KIND_Q4_1, true>(a, local, s) : launch_kind<KIND_Q4_1, false>(a, local, s);
+  if (kind == KIND_Q4_K) return two ? launch_kind<KIND_Q4_K, true>(a, local, s) : launch_kind<KIND_Q4_K, false>(a, local, s);
+  return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------------------
+// XCD placement probe
+// ---------------------------------------------------------------------------
+constexpr int kProbeWgs = 64;
+__device__ uint32_t g_xcc_probe[kProbeWgs];
+
+__global__ void k_xcc_probe() {
+  if (threadIdx.x == 0) g_xcc_probe[blockIdx.x] = __builtin_amdgcn_s_getreg((3 << 11) | 20) & 15;
+}
+
+int xcd_round_robin(hipStream_t s) {
+  static int cached[64];
+  static bool init = false;
+  if (!init) {
+    for (int& c : cached) c = -1;
+    init = true;
+  }
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cached[dev] >= 0) return cached[dev];
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return 0;
+  hipLaunchKernelGGL(k_xcc_probe, dim3(kProbeWgs), dim3(64), 0, s);
+  uint32_t ids[kProbeWgs];
+  if (hipGetLastError() != hipSuccess || hipStreamSynchronize(s) != hipSuccess ||
+      hipMemcpyFromSymbol(ids, HIP_SYMBOL(g_xcc_probe), sizeof ids, 0, hipMemcpyDeviceToHost) != hipSuccess)
+    return 0;
+  int ok = 1;
+  for (int i = 0; i < kProbeWgs; ++i) ok &= ids[i] == (uint32_t)(i % 8);
+  cached[dev] = ok;
+  return ok;
 }
 
 }  // namespace q4nx

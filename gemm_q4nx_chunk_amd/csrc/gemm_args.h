@@ -29,11 +29,11 @@ struct GemmArgs {
 // Tile rows per workgroup of the block GEMM.
 constexpr int kGemmRowsPerWg = 8;
 
-// Workgroups a launch aims for (two per CU), and the fewest tile columns a K
+// Workgroups a launch aims for (one per CU), and the fewest tile columns a K
 // part may hold (so the fp32 partial tiles stay small next to the weights
 // they summarise).
 #ifndef Q4NX_GEMM_WG_TARGET
-#define Q4NX_GEMM_WG_TARGET 512
+#define Q4NX_GEMM_WG_TARGET 256
 #endif
 #ifndef Q4NX_GEMM_MIN_COLS
 #define Q4NX_GEMM_MIN_COLS 4
@@ -53,13 +53,19 @@ inline int gemm_parts(int nb, int TC) {
 }
 
 // Bytes of the arrival counters (256-byte aligned) and of the partial tiles.
-inline size_t gemm_cnt_bytes(int nb) { return ((size_t)nb * 4 + 255) & ~(size_t)255; }
+// Counter region: nb arrival counters, then one flag word (set when a
+// workgroup of an XCD-local launch ran on another XCD than laid out).
+inline size_t gemm_cnt_bytes(int nb) { return ((size_t)(nb + 1) * 4 + 255) & ~(size_t)255; }
 inline size_t gemm_ws_bytes(int nb, int TC) {
   const int S = gemm_parts(nb, TC);
   if (S == 1) return 0;
   return gemm_cnt_bytes(nb) + (size_t)nb * S * 64 * kGemmRowsPerWg * 32 * 4;
 }
 
-hipError_t launch_gemm(int kind, const GemmArgs& a, hipStream_t s);
+// local: lay the K parts of each workgroup row on one XCD (see gemm.hip).
+hipError_t launch_gemm(int kind, const GemmArgs& a, bool local, hipStream_t s);
+// 1 when this device deals workgroups to 8 XCDs round-robin by linear id
+// (checked once per device with a 64-workgroup probe, outside graph capture).
+int xcd_round_robin(hipStream_t s);
 
 }  // namespace q4nx
