@@ -189,6 +189,136 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_q4x(const GemvBatch b) {
   }
 }
 
+// Q8 with the workgroup's activations staged once in LDS (raw bf16 rows) and
+// an unconditional buffer-load chunk ring: the same structure as k_gemv_q4x,
+// so a step waits only for its own chunk.  The chunk's 512-byte scale region
+// is fetched with one 8-byte load per lane and turned around in a per-wave
+// LDS slot ([group][row]), from which each lane reads its 16 scales (rows
+// 16h .. 16h+15 of its group) as two 16-byte reads, instead of 16 two-byte
+// global loads.  Used when the activation rows fit four 16-byte pieces per
+// thread and the LDS budget.
+struct Q8ChunkX {
+  u32x4 pc[8];
+  u32x2 dp;   // scales d(r, g) with 8r + g = 4 lane .. 4 lane + 3
+};
+
+template <int KIND>
+__device__ __forceinline__ void q8x_load_rs(__amdgpu_buffer_rsrc_t rs, uint32_t off, int lane, Q8ChunkX& c) {
+  constexpr int kNt = 2;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    c.pc[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + q8_piece<KIND>(lane, i), 0, kNt));
+  c.dp = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, off + 8192 + 8 * lane, 0, 0));
+}
+
+template <int KIND, int M, int WAVES, int D>
+__global__ __launch_bounds__(64 * WAVES) void k_gemv_q8x(const GemvBatch b) {
+  constexpr int NT = 64 * WAVES;
+  constexpr int XRP8 = 4;
+  constexpr int CB = 8704;
+  extern __shared__ __attribute__((aligned(16))) uint32_t xl[];
+  __shared__ __attribute__((aligned(16))) uint16_t dsl[WAVES][8 * 32];
+  __shared__ float red[WAVES][32][M];
+  const GemvJob& J = b.job[find_job(b, blockIdx.x)];
+  const int ks = J.ks, rpw = WAVES / ks;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int slot = wave / ks, part = wave % ks;
+  const int tr0 = (blockIdx.x - J.wg_begin) * rpw;
+  const int tr = tr0 + slot < J.TR ? tr0 + slot : J.TR - 1;
+  const int TC = J.TC, K = TC * 256;
+  const int c0 = part * TC / ks, c1 = (part + 1) * TC / ks;
+  const int h = (lane >> 2) & 1, g = lane >> 3;
+  const int NP = M * TC * 32;   // 16-byte pieces of the M activation rows
+
+  // 1. activations: piece p of row m at x[m][8 p'] (p' = p - 32 TC m)
+  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(J.x, (uint32_t)(((M - 1) * J.ldx + K) * 2));
+  u32x4 xr[XRP8];
+#pragma unroll
+  for (int p = 0; p < XRP8; ++p) {
+    const int pc = tid + NT * p, m = pc / (TC * 32), pp = pc - m * TC * 32;
+    xr[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                          xrs, (uint32_t)(m * J.ldx + 8 * pp) * 2, 0, 0));
+  }
+  // 2. the first D chunks of the wave's run
+  const __amdgpu_buffer_rsrc_t wrs =
+      make_rsrc(J.w + ((size_t)tr * TC + c0) * CB, (uint32_t)((c1 - c0) * CB));
+  Q8ChunkX ring[D];
+#pragma unroll
+  for (int j = 0; j < D; ++j) q8x_load_rs<KIND>(wrs, j * CB, lane, ring[j]);
+  // 3. rows to LDS: row m at xl[m * K / 2 .. ] (bf16 pairs)
+#pragma unroll
+  for (int p = 0; p < XRP8; ++p) {
+    const int pc = tid + NT * p;
+    if (pc < NP) *reinterpret_cast<u32x4*>(xl + 4 * pc) = xr[p];
+  }
+  __syncthreads();
+
+  float acc[16][M];
+#pragma unroll
+  for (int r = 0; r < 16; ++r)
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[r][m] = 0.f;
+  uint16_t* ds = dsl[wave];
+  const int dr = lane >> 1, dg0 = 4 * (lane & 1);
+  auto step = [&](int j, int c) {
+    __builtin_amdgcn_sched_barrier(0);
+    // scales: (row dr, groups dg0 .. dg0+3) -> slot [group][row]; the wave's
+    // LDS operations run in order, so the reads below see every lane's writes
+    const u32x2 dp = ring[j].dp;
+    ds[(dg0 + 0) * 32 + dr] = (uint16_t)(dp.x & 0xFFFFu);
+    ds[(dg0 + 1) * 32 + dr] = (uint16_t)(dp.x >> 16);
+    ds[(dg0 + 2) * 32 + dr] = (uint16_t)(dp.y & 0xFFFFu);
+    ds[(dg0 + 3) * 32 + dr] = (uint16_t)(dp.y >> 16);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    Q8Chunk ch;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ch.pc[i] = ring[j].pc[i];
+    const u32x4 d0 = *reinterpret_cast<const u32x4*>(ds + g * 32 + 16 * h);
+    const u32x4 d1 = *reinterpret_cast<const u32x4*>(ds + g * 32 + 16 * h + 8);
+    ch.dv[0] = d0.x; ch.dv[1] = d0.y; ch.dv[2] = d0.z; ch.dv[3] = d0.w;
+    ch.dv[4] = d1.x; ch.dv[5] = d1.y; ch.dv[6] = d1.z; ch.dv[7] = d1.w;
+    Q8XRaw<M> xv;
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+      xv.v[m] = *reinterpret_cast<const u32x4*>(xl + (m * K + q8_xcol(lane, c)) / 2);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");   // the slot's reads come before
+    __builtin_amdgcn_wave_barrier();                          // the next step's writes
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    q8_compute_raw<M>(ch, xv, acc);
+    q8x_load_rs<KIND>(wrs, (uint32_t)(c + D - c0) * CB, lane, ring[j]);
+  };
+  int base = c0;
+  for (; base + D <= c1; base += D) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) step(j, base + j);
+  }
+#pragma unroll
+  for (int j = 0; j + 1 < D; ++j)
+    if (base + j < c1) step(j, base + j);
+
+  q8_lane_reduce<M>(acc);
+  if ((lane & ~4) == 0) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+#pragma unroll
+      for (int m = 0; m < M; ++m) red[wave][16 * h + r][m] = acc[r][m];
+  }
+  __syncthreads();
+  for (int idx = tid; idx < rpw * 32 * M; idx += NT) {
+    const int s = idx / (32 * M), rem = idx - s * 32 * M;
+    const int r = rem / M, m = rem - r * M;
+    const int t = tr0 + s;
+    if (t < J.TR) {
+      float v = 0.f;
+      for (int p = 0; p < ks; ++p) v += red[s * ks + p][r][m];
+      J.y[(size_t)m * J.ldy + 32 * t + r] = v;
+    }
+  }
+}
+
 template <int KIND, int M, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void k_gemv_q8(const GemvBatch b) {
   constexpr int CB = 8704;
@@ -254,7 +384,11 @@ static hipError_t launch_one(const GemvBatch& b, int n_wg, int xl_bytes, hipStre
     else
       hipLaunchKernelGGL((k_gemv_q4<KIND, M, WAVES>), dim3(n_wg), dim3(64 * WAVES), 0, s, b);
   } else {
-    hipLaunchKernelGGL((k_gemv_q8<KIND, M, WAVES>), dim3(n_wg), dim3(64 * WAVES), 0, s, b);
+    if (xl_bytes > 0)
+      hipLaunchKernelGGL((k_gemv_q8x<KIND, M, WAVES, M == 1 ? 2 : 1>), dim3(n_wg),
+                         dim3(64 * WAVES), xl_bytes, s, b);
+    else
+      hipLaunchKernelGGL((k_gemv_q8<KIND, M, WAVES>), dim3(n_wg), dim3(64 * WAVES), 0, s, b);
   }
   return hipGetLastError();
 }
@@ -279,8 +413,8 @@ static hipError_t launch_w(int kind, int M, const GemvBatch& b, int n_wg, int xl
   switch (kind) {
     case KIND_Q4_1: return launch_m<KIND_Q4_1, WAVES>(M, b, n_wg, xl, s);
     case KIND_Q4_K: return launch_m<KIND_Q4_K, WAVES>(M, b, n_wg, xl, s);
-    case KIND_Q8_A: return launch_m<KIND_Q8_A, WAVES>(M, b, n_wg, 0, s);
-    case KIND_Q8_B: return launch_m<KIND_Q8_B, WAVES>(M, b, n_wg, 0, s);
+    case KIND_Q8_A: return launch_m<KIND_Q8_A, WAVES>(M, b, n_wg, xl, s);
+    case KIND_Q8_B: return launch_m<KIND_Q8_B, WAVES>(M, b, n_wg, xl, s);
   }
   return hipErrorInvalidValue;
 }
@@ -296,6 +430,11 @@ int gemv_xl_bytes(int kind, int M, int waves, int max_tc) {
 #if defined(Q4NX_GEMV_NO_XLDS)
   return 0;
 #endif
+  if (kind == KIND_Q8_A || kind == KIND_Q8_B) {   // raw rows, four 16-byte pieces per thread
+    const int NP = M * max_tc * 32;
+    if (NP > 4 * 64 * waves) return 0;
+    return NP * 16 <= 65536 ? NP * 16 : 0;
+  }
   if (kind != KIND_Q4_1 && kind != KIND_Q4_K) return 0;
   const int R = M * max_tc * 8;
   if (R > 2 * 64 * waves) return 0;          // two records per thread
@@ -312,8 +451,8 @@ hipError_t launch_gemv(int kind, int M, int waves, const GemvBatch& b, int n_wg,
     switch (kind) {
       case KIND_Q4_1: return launch_small<KIND_Q4_1>(M, b, n_wg, xl_bytes, s);
       case KIND_Q4_K: return launch_small<KIND_Q4_K>(M, b, n_wg, xl_bytes, s);
-      case KIND_Q8_A: return launch_small<KIND_Q8_A>(M, b, n_wg, 0, s);
-      case KIND_Q8_B: return launch_small<KIND_Q8_B>(M, b, n_wg, 0, s);
+      case KIND_Q8_A: return launch_small<KIND_Q8_A>(M, b, n_wg, xl_bytes, s);
+      case KIND_Q8_B: return launch_small<KIND_Q8_B>(M, b, n_wg, xl_bytes, s);
     }
   }
   return hipErrorInvalidValue;

@@ -209,6 +209,23 @@ __device__ __forceinline__ void q8_load(const uint8_t* __restrict__ ck, int lane
   }
 }
 
+// q8_load through a buffer resource over a run of chunks (off = the chunk's
+// byte offset in the run; past the run every load reads zero, no traffic).
+template <int KIND>
+__device__ __forceinline__ void q8_load_rs(__amdgpu_buffer_rsrc_t rs, uint32_t off, int lane, Q8Chunk& c) {
+  constexpr int kNt = 2;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    c.pc[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + q8_piece<KIND>(lane, i), 0, kNt));
+  const uint32_t dbase = off + q8_dbase(lane);
+#pragma unroll
+  for (int rr = 0; rr < 8; ++rr) {
+    const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(rs, dbase + 32 * rr, 0, 0);
+    const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(rs, dbase + 32 * rr + 16, 0, 0);
+    c.dv[rr] = lo | (hi << 16);
+  }
+}
+
 // The lane's 8 activations of one Q8 chunk (k = 32g + 8j .. +7), as loaded.
 template <int M>
 struct Q8XRaw {
