@@ -80,6 +80,7 @@ _lib.q4nx_moe_experts.argtypes = [ctypes.POINTER(MoeLayer), _P, _P, _P, _I, _I, 
                                   ctypes.POINTER(MoeDebug), _P, ctypes.c_size_t, _P]
 _lib.q4nx_unpack.argtypes = [ctypes.POINTER(Weight), _P, _P, _P, _P, _P]
 _lib.q4nx_decode.argtypes = [ctypes.POINTER(Weight), _P, _P]
+_lib.q4nx_repack_q4k_to_q41.argtypes = [ctypes.POINTER(Weight), _P, ctypes.c_size_t, _P]
 _lib.q4nx_plan_create.argtypes = [ctypes.POINTER(GemvJob), ctypes.POINTER(ctypes.c_int32), _I, _I,
                                   ctypes.POINTER(ctypes.c_void_p)]
 _lib.q4nx_plan_run.argtypes = [_P, _P]
@@ -92,7 +93,7 @@ _lib.q4nx_status_str.argtypes = [_I]
 _lib.q4nx_status_str.restype = ctypes.c_char_p
 _lib.q4nx_last_error.restype = ctypes.c_char_p
 for _f in ("q4nx_weight_check", "q4nx_gemv", "q4nx_gemv_batched", "q4nx_gemm_block", "q4nx_gemm_batched",
-           "q4nx_moe_experts", "q4nx_unpack", "q4nx_decode", "q4nx_version", "q4nx_plan_create",
+           "q4nx_moe_experts", "q4nx_unpack", "q4nx_decode", "q4nx_repack_q4k_to_q41", "q4nx_version", "q4nx_plan_create",
            "q4nx_plan_run", "q4nx_plan_errors"):
     getattr(_lib, _f).restype = ctypes.c_int
 
@@ -280,6 +281,13 @@ def moe_experts(L: MoeLayer, X, ids, p, Y, T: int, k: int, ws, dbg: dict | None 
                                  ctypes.byref(d) if d is not None else None, _ptr(ws),
                                  _nbytes(ws) if ws_bytes is None else ws_bytes,
                                  _stream(stream)))
+
+
+def repack_q4k_to_q41(w: Weight, out, stream=None, out_bytes: int | None = None) -> None:
+    """Q4_K weight -> q4_1 chunks in `out` (tiles * 5120 bytes), same tile order."""
+    _check(_lib.q4nx_repack_q4k_to_q41(ctypes.byref(w), _ptr(out),
+                                       _nbytes(out) if out_bytes is None else out_bytes,
+                                       _stream(stream)))
 
 
 def unpack(w: Weight, codes, meta0, meta1=None, row_meta=None, stream=None) -> None:

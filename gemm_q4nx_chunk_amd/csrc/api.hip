@@ -675,6 +675,23 @@ int q4nx_unpack(const q4nx_weight* w, uint8_t* codes, uint16_t* meta0, uint16_t*
   return hip_status(e, "unpack launch");
 }
 
+int q4nx_repack_q4k_to_q41(const q4nx_weight* w, void* out, size_t out_bytes, void* stream) {
+  int st = check_weight(w, "repack");
+  if (st) return st;
+  if (w->chunk_bytes != Q4NX_Q4_K_BYTES)
+    return fail(Q4NX_E_CHUNK_KIND, "repack: input must be Q4_K (4736-byte chunks), got %d", w->chunk_bytes);
+  if (!out) return fail(Q4NX_E_ARG, "repack: null output");
+  if (!aligned(out, 16)) return fail(Q4NX_E_ALIGN, "repack: output not 16-byte aligned");
+  const int64_t tiles = (int64_t)(w->rows / 32) * (w->cols / 256);
+  if (out_bytes < (size_t)tiles * Q4NX_Q4_1_BYTES)
+    return fail(Q4NX_E_SHORT, "repack: output holds %zu bytes, %lld needed", out_bytes,
+                (long long)(tiles * Q4NX_Q4_1_BYTES));
+  if (tiles > 0x7FFFFFFF) return fail(Q4NX_E_SHAPE, "repack: too many tiles");
+  const hipError_t e = q4nx::launch_repack_q4k(static_cast<const uint8_t*>(w->chunks), (int)tiles,
+                                               static_cast<uint8_t*>(out), static_cast<hipStream_t>(stream));
+  return hip_status(e, "repack launch");
+}
+
 int q4nx_decode(const q4nx_weight* w, float* out, void* stream) {
   int st = check_weight(w, "decode");
   if (st) return st;

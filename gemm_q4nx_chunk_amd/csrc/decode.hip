@@ -118,4 +118,33 @@ hipError_t launch_decode(int kind, const uint8_t* w, int TR, int TC, float* out,
   return launch_any(kind, w, TR, TC, nullptr, nullptr, nullptr, nullptr, out, s);
 }
 
+// ---------------------------------------------------------------------------
+// Q4_K -> q4_1 repack (1bit engine docs, page "NPU engine", section "Q4NX
+// chunks": Q4_K weights are repacked to q4_1, exactly apart from rounding
+// S * scale and M * min to bf16, so a q4_1 kernel serves both kinds).
+// One workgroup per chunk: the 4096 code bytes are copied unchanged (256
+// threads x 16 bytes) and thread t = 8r + g writes (scale', zero') of row r,
+// group g: S * sc and M * mn are exact in fp32 (8 x 8 significant bits) and
+// are rounded once, to nearest even, to bf16.  Products outside the fp32
+// range are outside the repack's domain.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_repack_q4k(const uint8_t* __restrict__ w, uint8_t* __restrict__ out) {
+  const int t = threadIdx.x, r = t >> 3, g = t & 7;
+  const uint8_t* ck = w + (size_t)blockIdx.x * 4736;
+  uint8_t* oc = out + (size_t)blockIdx.x * 5120;
+  *reinterpret_cast<u32x4*>(oc + 16 * t) = *reinterpret_cast<const u32x4*>(ck + 16 * t);
+  const uint32_t scmn = *reinterpret_cast<const uint16_t*>(ck + 4096 + 2 * (8 * r + g));
+  const uint32_t sm = *reinterpret_cast<const uint32_t*>(ck + 4608 + 4 * r);
+  const float s = bf16lo(sm) * (float)(scmn & 0xFFu);
+  const float z = bf16hi(sm) * (float)(scmn >> 8);
+  const uint32_t sb = __builtin_bit_cast(uint16_t, (__bf16)s);
+  const uint32_t zb = __builtin_bit_cast(uint16_t, (__bf16)z);
+  *reinterpret_cast<uint32_t*>(oc + 4096 + 4 * (8 * r + g)) = sb | (zb << 16);
+}
+
+hipError_t launch_repack_q4k(const uint8_t* w, int tiles, uint8_t* out, hipStream_t s) {
+  hipLaunchKernelGGL(k_repack_q4k, dim3(tiles), dim3(256), 0, s, w, out);
+  return hipGetLastError();
+}
+
 }  // namespace q4nx

@@ -116,5 +116,6 @@ hipError_t launch_gemv(int kind, int M, int waves, const GemvBatch& b, int n_wg,
 hipError_t launch_unpack(int kind, const uint8_t* w, int TR, int TC, uint8_t* codes,
                          uint16_t* meta0, uint16_t* meta1, uint16_t* row_meta, hipStream_t s);
 hipError_t launch_decode(int kind, const uint8_t* w, int TR, int TC, float* out, hipStream_t s);
+hipError_t launch_repack_q4k(const uint8_t* w, int tiles, uint8_t* out, hipStream_t s);
 
 }  // namespace q4nx

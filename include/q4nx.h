@@ -279,6 +279,21 @@ int q4nx_moe_experts(const q4nx_moe_layer* L, const uint16_t* X, const int32_t* 
                      void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Q4_K -> q4_1 repack (NPU engine page, "Q4NX chunks": Q4_K repacks into
+ * q4_1 exactly apart from rounding S * scale and M * min to bf16, so one
+ * q4_1 kernel serves both kinds).  Writes tiles = (rows/32) * (cols/256)
+ * q4_1 chunks of 5120 bytes in the same tile order: codes unchanged,
+ * scale'(r, g) = bf16(S(r) * sc(r, g)) and zero'(r, g) = bf16(M(r) * mn(r, g)),
+ * each product exact in fp32 and rounded once to nearest even.  Products
+ * that overflow fp32 are outside the repack's domain (they give +-Inf).
+ *   w          host descriptor of a Q4_K weight (E_CHUNK_KIND otherwise)
+ *   out        DEVICE, 16-byte aligned, out_bytes >= tiles * 5120 (E_SHORT)
+ * The result is a q4_1 weight of the same rows and cols; describe it with
+ * chunk_bytes = 5120 to use it.  Asynchronous on stream.
+ */
+int q4nx_repack_q4k_to_q41(const q4nx_weight* w, void* out, size_t out_bytes, void* stream);
+
+/*
  * Test surface of the decoders (NPU engine page, "Q4NX chunks": the decoders
  * of all three kinds are checked bit for bit).  Writes the fields of every
  * chunk in logical [rows][cols] order:

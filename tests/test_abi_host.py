@@ -182,6 +182,15 @@ def test_unpack_decode_checks(q):
     _expect(q, q.E_ALIGN, q.decode, _w(q), 0x1002, stream=0)
 
 
+def test_repack_checks(q):
+    wk = _w(q, rows=64, cols=512, kind="q4_k")
+    need = 2 * 2 * 5120
+    _expect(q, q.E_CHUNK_KIND, q.repack_q4k_to_q41, _w(q), 0x200000, stream=0, out_bytes=need)
+    _expect(q, q.E_ARG, q.repack_q4k_to_q41, wk, 0, stream=0, out_bytes=need)
+    _expect(q, q.E_ALIGN, q.repack_q4k_to_q41, wk, 0x200008, stream=0, out_bytes=need)
+    _expect(q, q.E_SHORT, q.repack_q4k_to_q41, wk, 0x200000, stream=0, out_bytes=need - 1)
+
+
 def test_plan_create_checks(q):
     good = (_w(q), 0x2000, 0x3000)
     lib = q.lib()
