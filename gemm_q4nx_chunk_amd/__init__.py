@@ -81,6 +81,8 @@ _lib.q4nx_moe_experts.argtypes = [ctypes.POINTER(MoeLayer), _P, _P, _P, _I, _I, 
 _lib.q4nx_unpack.argtypes = [ctypes.POINTER(Weight), _P, _P, _P, _P, _P]
 _lib.q4nx_decode.argtypes = [ctypes.POINTER(Weight), _P, _P]
 _lib.q4nx_repack_q4k_to_q41.argtypes = [ctypes.POINTER(Weight), _P, ctypes.c_size_t, _P]
+_lib.q4nx_q8_rows.argtypes = [ctypes.POINTER(Weight), _P, _I, _P, _P]
+_lib.q4nx_argmax.argtypes = [_P, _I, _I, _I, _P, _P, _P]
 _lib.q4nx_plan_create.argtypes = [ctypes.POINTER(GemvJob), ctypes.POINTER(ctypes.c_int32), _I, _I,
                                   ctypes.POINTER(ctypes.c_void_p)]
 _lib.q4nx_plan_run.argtypes = [_P, _P]
@@ -93,7 +95,7 @@ _lib.q4nx_status_str.argtypes = [_I]
 _lib.q4nx_status_str.restype = ctypes.c_char_p
 _lib.q4nx_last_error.restype = ctypes.c_char_p
 for _f in ("q4nx_weight_check", "q4nx_gemv", "q4nx_gemv_batched", "q4nx_gemm_block", "q4nx_gemm_batched",
-           "q4nx_moe_experts", "q4nx_unpack", "q4nx_decode", "q4nx_repack_q4k_to_q41", "q4nx_version", "q4nx_plan_create",
+           "q4nx_moe_experts", "q4nx_unpack", "q4nx_decode", "q4nx_repack_q4k_to_q41", "q4nx_q8_rows", "q4nx_argmax", "q4nx_version", "q4nx_plan_create",
            "q4nx_plan_run", "q4nx_plan_errors"):
     getattr(_lib, _f).restype = ctypes.c_int
 
@@ -288,6 +290,17 @@ def repack_q4k_to_q41(w: Weight, out, stream=None, out_bytes: int | None = None)
     _check(_lib.q4nx_repack_q4k_to_q41(ctypes.byref(w), _ptr(out),
                                        _nbytes(out) if out_bytes is None else out_bytes,
                                        _stream(stream)))
+
+
+def q8_rows(w: Weight, ids, T: int, out, stream=None) -> None:
+    """out[t] = decoded row ids[t] of the Q8 weight w (fp32 [T][cols])."""
+    _check(_lib.q4nx_q8_rows(ctypes.byref(w), _ptr(ids), T, _ptr(out), _stream(stream)))
+
+
+def argmax(y, n: int, M: int, idx, val=None, ldy: int | None = None, stream=None) -> None:
+    """idx[m] = index of the largest of y[m][:n] (lowest on ties, NaNs skipped)."""
+    _check(_lib.q4nx_argmax(_ptr(y), n, n if ldy is None else ldy, M, _ptr(idx), _ptr(val),
+                            _stream(stream)))
 
 
 def unpack(w: Weight, codes, meta0, meta1=None, row_meta=None, stream=None) -> None:

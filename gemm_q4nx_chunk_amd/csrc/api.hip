@@ -692,6 +692,29 @@ int q4nx_repack_q4k_to_q41(const q4nx_weight* w, void* out, size_t out_bytes, vo
   return hip_status(e, "repack launch");
 }
 
+int q4nx_q8_rows(const q4nx_weight* w, const int32_t* ids, int T, float* out, void* stream) {
+  int st = check_weight(w, "q8_rows");
+  if (st) return st;
+  if (w->chunk_bytes != Q4NX_Q8_BYTES)
+    return fail(Q4NX_E_CHUNK_KIND, "q8_rows: weight must be Q8 (8704-byte chunks), got %d", w->chunk_bytes);
+  if (!ids || !out) return fail(Q4NX_E_ARG, "q8_rows: null ids or output");
+  if (T < 1 || T > 65535) return fail(Q4NX_E_ARG, "q8_rows: T = %d outside 1..65535", T);
+  if (!aligned(ids, 4) || !aligned(out, 4)) return fail(Q4NX_E_ALIGN, "q8_rows: ids and out must be 4-byte aligned");
+  const hipError_t e = q4nx::launch_q8_rows(kind_of(w), static_cast<const uint8_t*>(w->chunks), w->rows,
+                                            w->cols / 256, ids, T, out, static_cast<hipStream_t>(stream));
+  return hip_status(e, "q8_rows launch");
+}
+
+int q4nx_argmax(const float* y, int n, int ldy, int M, int32_t* idx, float* val, void* stream) {
+  if (!y || !idx) return fail(Q4NX_E_ARG, "argmax: null y or idx");
+  if (n < 1 || ldy < n || M < 1 || M > 65535)
+    return fail(Q4NX_E_ARG, "argmax: n = %d, ldy = %d, M = %d (need 1 <= n <= ldy, 1 <= M <= 65535)", n, ldy, M);
+  if (!aligned(y, 4) || !aligned(idx, 4) || (val && !aligned(val, 4)))
+    return fail(Q4NX_E_ALIGN, "argmax: y, idx and val must be 4-byte aligned");
+  const hipError_t e = q4nx::launch_argmax(y, n, ldy, M, idx, val, static_cast<hipStream_t>(stream));
+  return hip_status(e, "argmax launch");
+}
+
 int q4nx_decode(const q4nx_weight* w, float* out, void* stream) {
   int st = check_weight(w, "decode");
   if (st) return st;

@@ -147,4 +147,85 @@ hipError_t launch_repack_q4k(const uint8_t* w, int tiles, uint8_t* out, hipStrea
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Q8 row gather: rows of a Q8 weight (a tied embedding) decoded to fp32
+// (1bit engine docs, page "NPU engine", section "Q4NX chunks": the Q8 kind
+// stores the embedding / lm_head, code (r, k) of a tile at byte k*32 + r in
+// layout A or (r/16)*4096 + (k/32)*512 + (k%32)*16 + r%16 in layout B).
+// One workgroup per requested row; thread k takes column k of every tile
+// column.  d * code is exact in fp32.  An id outside [0, rows) gives a row of
+// zeros and touches no weight byte.
+// ---------------------------------------------------------------------------
+template <int KIND>
+__global__ __launch_bounds__(256) void k_q8_rows(const uint8_t* __restrict__ w, int rows, int TC,
+                                                 const int32_t* __restrict__ ids, float* __restrict__ out) {
+  const int t = blockIdx.x, k = threadIdx.x;
+  const int id = ids[t];
+  float* o = out + (size_t)t * TC * 256;
+  if (id < 0 || id >= rows) {
+    for (int tc = 0; tc < TC; ++tc) o[256 * tc + k] = 0.f;
+    return;
+  }
+  const int tr = id >> 5, r = id & 31, g = k >> 5;
+  const int off = KIND == KIND_Q8_A ? k * 32 + r : (r >> 4) * 4096 + (k >> 5) * 512 + (k & 31) * 16 + (r & 15);
+  for (int tc = 0; tc < TC; ++tc) {
+    const uint8_t* ck = w + ((size_t)tr * TC + tc) * 8704;
+    const float c = (float)(int8_t)ck[off];
+    const float d = bf16lo(*reinterpret_cast<const uint16_t*>(ck + 8192 + 2 * (8 * r + g)));
+    o[256 * tc + k] = d * c;
+  }
+}
+
+hipError_t launch_q8_rows(int kind, const uint8_t* w, int rows, int TC, const int32_t* ids, int T,
+                          float* out, hipStream_t s) {
+  if (kind == KIND_Q8_A) hipLaunchKernelGGL((k_q8_rows<KIND_Q8_A>), dim3(T), dim3(256), 0, s, w, rows, TC, ids, out);
+  else if (kind == KIND_Q8_B) hipLaunchKernelGGL((k_q8_rows<KIND_Q8_B>), dim3(T), dim3(256), 0, s, w, rows, TC, ids, out);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// argmax over logits (greedy decode after the lm_head GEMV): per row m of
+// y [M][n], the largest value and its index, the lowest index among equal
+// values; NaNs are skipped (index -1 when a row holds only NaNs).  One
+// workgroup per row; each thread scans a strided slice, then a fixed-order
+// tree in LDS.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ bool am_better(float v, int i, float bv, int bi) {
+  return bi < 0 || v > bv || (v == bv && i < bi);
+}
+
+__global__ __launch_bounds__(1024) void k_argmax(const float* __restrict__ y, int n, int ldy,
+                                                 int32_t* __restrict__ idx, float* __restrict__ val) {
+  __shared__ float sv[1024];
+  __shared__ int si[1024];
+  const int m = blockIdx.x, t = threadIdx.x;
+  const float* row = y + (size_t)m * ldy;
+  float bv = 0.f;
+  int bi = -1;
+  for (int i = t; i < n; i += 1024) {
+    const float v = row[i];
+    if (v == v && am_better(v, i, bv, bi)) { bv = v; bi = i; }
+  }
+  sv[t] = bv;
+  si[t] = bi;
+  __syncthreads();
+  for (int h = 512; h > 0; h >>= 1) {
+    if (t < h && si[t + h] >= 0 && am_better(sv[t + h], si[t + h], sv[t], si[t])) {
+      sv[t] = sv[t + h];
+      si[t] = si[t + h];
+    }
+    __syncthreads();
+  }
+  if (t == 0) {
+    idx[m] = si[0];
+    if (val) val[m] = si[0] >= 0 ? sv[0] : __builtin_nanf("");
+  }
+}
+
+hipError_t launch_argmax(const float* y, int n, int ldy, int M, int32_t* idx, float* val, hipStream_t s) {
+  hipLaunchKernelGGL(k_argmax, dim3(M), dim3(1024), 0, s, y, n, ldy, idx, val);
+  return hipGetLastError();
+}
+
 }  // namespace q4nx

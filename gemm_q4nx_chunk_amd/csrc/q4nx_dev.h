@@ -117,5 +117,8 @@ hipError_t launch_unpack(int kind, const uint8_t* w, int TR, int TC, uint8_t* co
                          uint16_t* meta0, uint16_t* meta1, uint16_t* row_meta, hipStream_t s);
 hipError_t launch_decode(int kind, const uint8_t* w, int TR, int TC, float* out, hipStream_t s);
 hipError_t launch_repack_q4k(const uint8_t* w, int tiles, uint8_t* out, hipStream_t s);
+hipError_t launch_q8_rows(int kind, const uint8_t* w, int rows, int TC, const int32_t* ids, int T,
+                          float* out, hipStream_t s);
+hipError_t launch_argmax(const float* y, int n, int ldy, int M, int32_t* idx, float* val, hipStream_t s);
 
 }  // namespace q4nx

@@ -294,6 +294,26 @@ int q4nx_moe_experts(const q4nx_moe_layer* L, const uint16_t* X, const int32_t* 
 int q4nx_repack_q4k_to_q41(const q4nx_weight* w, void* out, size_t out_bytes, void* stream);
 
 /*
+ * Rows of a Q8 weight decoded to fp32: the token-embedding lookup of a tied
+ * Q8 embedding / lm_head (NPU engine page, "Q4NX chunks": Q8 chunks hold that
+ * tensor, in either code layout).  out[t][k] = d(r, k/32) * code(r, k) with
+ * r = ids[t]; every value is exact in fp32.
+ *   w    host descriptor of a Q8 weight (E_CHUNK_KIND otherwise)
+ *   ids  DEVICE int32 [T]; an id outside [0, w->rows) yields a row of zeros
+ *   out  DEVICE fp32 [T][w->cols]
+ *   T    1..65535
+ */
+int q4nx_q8_rows(const q4nx_weight* w, const int32_t* ids, int T, float* out, void* stream);
+
+/*
+ * Greedy pick after the lm_head GEMV: for each row m of y (fp32, row stride
+ * ldy), the index of the largest of its first n values, the lowest index
+ * among equal maxima; NaNs are skipped, and a row of only NaNs gives -1.
+ *   idx  DEVICE int32 [M];  val DEVICE fp32 [M] or NULL (the maximum)
+ */
+int q4nx_argmax(const float* y, int n, int ldy, int M, int32_t* idx, float* val, void* stream);
+
+/*
  * Test surface of the decoders (NPU engine page, "Q4NX chunks": the decoders
  * of all three kinds are checked bit for bit).  Writes the fields of every
  * chunk in logical [rows][cols] order:

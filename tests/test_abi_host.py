@@ -191,6 +191,18 @@ def test_repack_checks(q):
     _expect(q, q.E_SHORT, q.repack_q4k_to_q41, wk, 0x200000, stream=0, out_bytes=need - 1)
 
 
+def test_rows_and_argmax_checks(q):
+    w8 = _w(q, kind="q8", layout="A")
+    _expect(q, q.E_CHUNK_KIND, q.q8_rows, _w(q), 0x2000, 4, 0x3000, stream=0)
+    _expect(q, q.E_ARG, q.q8_rows, w8, 0, 4, 0x3000, stream=0)
+    _expect(q, q.E_ARG, q.q8_rows, w8, 0x2000, 0, 0x3000, stream=0)
+    _expect(q, q.E_ALIGN, q.q8_rows, w8, 0x2002, 4, 0x3000, stream=0)
+    _expect(q, q.E_ARG, q.argmax, 0, 10, 1, 0x3000, stream=0)
+    _expect(q, q.E_ARG, q.argmax, 0x2000, 10, 1, 0x3000, ldy=9, stream=0)
+    _expect(q, q.E_ARG, q.argmax, 0x2000, 10, 0, 0x3000, stream=0)
+    _expect(q, q.E_ALIGN, q.argmax, 0x2002, 10, 1, 0x3000, stream=0)
+
+
 def test_plan_create_checks(q):
     good = (_w(q), 0x2000, 0x3000)
     lib = q.lib()
