@@ -9,7 +9,8 @@ the HIP kernels.  It is plain, slow and written to be checked by eye:
   a pure-Python scalar decoder used as brute force on tiny grids;
 * ``ref``     -- float64 products y = W x with the per-output error scale
   a = sum |w x|, the tolerance test, SwiGLU, the MoE layer and its combine,
-  and the Q4_K -> q4_1 repack with its rounding bound.
+  the router (logits, softmax, top-k, renormalisation), and the Q4_K -> q4_1
+  repack with its rounding bound.
 
 What it follows: the 1bit engine docs, page "NPU engine", section "Q4NX chunks"
 (tile grid, chunk kinds, decode formulas, the two Q8 code layouts) and the
@@ -24,10 +25,11 @@ do not reuse this code's formulas (tests/test_oracle_pins.py).
 from .decode import (KIND_BYTES, decode_fields, weights_exact, weights_f32, unpack_expected,
                      scalar_decode_chunk)
 from .ref import (gemv_ref, check_tol, tol_ratio, silu, swiglu, moe_layer_ref, moe_combine_ref,
-                  repack_q4k_to_q41, repack_bound)
+                  repack_q4k_to_q41, repack_bound, router_topk, router_logits_ref)
 
 __all__ = [
     "KIND_BYTES", "decode_fields", "weights_exact", "weights_f32", "unpack_expected",
     "scalar_decode_chunk", "gemv_ref", "check_tol", "tol_ratio", "silu", "swiglu",
-    "moe_layer_ref", "moe_combine_ref", "repack_q4k_to_q41", "repack_bound",
+    "moe_layer_ref", "moe_combine_ref", "repack_q4k_to_q41", "repack_bound", "router_topk",
+    "router_logits_ref",
 ]

@@ -160,3 +160,37 @@ def repack_bound(chunks, N: int, K: int) -> np.ndarray:
     sc = np.repeat(f["sc"].astype(np.float64), 32, axis=1)
     mn = np.repeat(f["mn"].astype(np.float64), 32, axis=1)
     return 2.0 ** -8 * (f["codes"] * np.abs(S * sc) + np.abs(M * mn))
+
+
+def router_topk(logits, k: int, renormalize: bool = True):
+    """Top-k routing from router logits (Strata article, section 2: the router
+    picks 10 of 512 experts per token; the weights are the softmax
+    probabilities of the picked experts, rescaled to sum to one unless the
+    tail-skip variant of section 4.3 keeps them as they are).
+
+    logits [T, E] (any float dtype; the ranking is taken on these values as
+    given).  Returns ids [T, k] int32 in decreasing logit order, the lower id
+    first among equal logits, and p [T, k] float64 (softmax in float64).
+    """
+    L = np.asarray(logits)
+    T, E = L.shape
+    ids = np.zeros((T, k), dtype=np.int32)
+    p = np.zeros((T, k), dtype=np.float64)
+    for t in range(T):
+        row = L[t]
+        order = sorted(range(E), key=lambda e: (-float(row[e]), e))[:k]
+        ids[t] = order
+        z = row.astype(np.float64)
+        w = np.exp(z - z.max())
+        prob = w / w.sum()
+        sel = prob[order]
+        p[t] = sel / sel.sum() if renormalize else sel
+    return ids, p
+
+
+def router_logits_ref(R_bits, X_bits):
+    """Router logits z[t, e] = sum_d R[e, d] * X[t, d] in float64 from bf16 bits,
+    with the error scale a[t, e] = sum_d |R[e, d] X[t, d]|."""
+    R = _x64(R_bits)
+    X = _x64(X_bits)
+    return X @ R.T, np.abs(X) @ np.abs(R).T

@@ -193,3 +193,19 @@ def test_mixed_q4k_layer_and_q8_lm_head_full_size(layout):
         yr, a = oracle.gemv_ref(W, x)
         ysub = np.concatenate([y[:, 32 * t:32 * t + 32] for t in tr], axis=1)
         assert oracle.tol_ratio(ysub, yr, a) <= 1.0, spec.name
+
+
+@pytest.mark.parametrize("kind,layout", KINDS)
+@pytest.mark.parametrize("M", [2, 3, 4])
+def test_verify_window_slot_invariance(kind, layout, M):
+    """A verify window of M tokens (Strata article, section 6.2, batch slots):
+    a token's result does not depend on the slot it occupies -- permuting the
+    rows of x permutes the rows of y bit for bit."""
+    N, K = 2560, 2560
+    ch = _gen(kind, layout, N, K, "slots")
+    d = dev_u8(ch)
+    x = synth.gen_x(synth.rng("gpu-gemv", "slots", kind, M), M, K)
+    perm = np.roll(np.arange(M), 1)
+    y = gemv(d, N, K, kind, x, layout)
+    yp = gemv(d, N, K, kind, x[perm], layout)
+    np.testing.assert_array_equal(yp.view(np.uint32), y[perm].view(np.uint32))

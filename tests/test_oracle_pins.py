@@ -390,3 +390,44 @@ def test_moe_out_of_range_ids_contribute_nothing():
     p_ok = np.array([[0.5, 0.0], [0.0, 0.5]], np.float32)
     np.testing.assert_allclose(y, oracle.moe_layer_ref(X, ids_ok, p_ok, W, None, n_experts=4),
                                rtol=1e-13, atol=1e-13)
+
+
+# ----------------------------------------------------------------------------
+# router (top-k of the softmax, renormalised)
+# ----------------------------------------------------------------------------
+def test_router_topk_brute_force_and_invariants():
+    """Brute force on a tiny router: every k-subset is scored by its smallest
+    logit (then by ids), the best subset must be the oracle's, and the weights
+    must be the subset's softmax mass rescaled to one."""
+    import itertools
+    g = np.random.default_rng(3)
+    E, k = 7, 3
+    for trial in range(20):
+        z = g.integers(-3, 4, E).astype(np.float32) * 0.5     # many ties
+        ids, p = oracle.router_topk(z[None, :], k)
+        best = None
+        for sub in itertools.combinations(range(E), k):
+            key = (sorted((-float(z[e]), e) for e in sub))
+            if best is None or key < best[0]:
+                best = (key, sub)
+        want_order = [e for _, e in best[0]]
+        assert list(ids[0]) == want_order, (z, ids, want_order)
+        ex = [math.exp(float(v) - float(z.max())) for v in z]
+        tot = math.fsum(ex)
+        mass = [ex[e] / tot for e in want_order]
+        assert np.allclose(p[0], np.array(mass) / math.fsum(mass), rtol=1e-14, atol=0)
+        ids2, p2 = oracle.router_topk(z[None, :], k, renormalize=False)
+        assert list(ids2[0]) == want_order and np.allclose(p2[0], mass, rtol=1e-14, atol=0)
+        assert abs(math.fsum(p[0]) - 1.0) < 1e-14
+
+
+def test_router_logits_one_hot_column():
+    """One-hot activation picks one column of the router matrix exactly."""
+    g = synth.rng("pin", "router-onehot")
+    E, D = 16, 64
+    R = synth.bf16_bits(g.standard_normal((E, D)).astype(np.float32))
+    X = np.zeros((1, D), dtype=np.uint16)
+    X[0, 13] = 0x3F80   # 1.0
+    z, a = oracle.router_logits_ref(R, X)
+    np.testing.assert_array_equal(z[0], synth.bf16_to_f32(R[:, 13]).astype(np.float64))
+    np.testing.assert_array_equal(a[0], np.abs(z[0]))
