@@ -83,6 +83,7 @@ _lib.q4nx_decode.argtypes = [ctypes.POINTER(Weight), _P, _P]
 _lib.q4nx_repack_q4k_to_q41.argtypes = [ctypes.POINTER(Weight), _P, ctypes.c_size_t, _P]
 _lib.q4nx_q8_rows.argtypes = [ctypes.POINTER(Weight), _P, _I, _P, _P]
 _lib.q4nx_argmax.argtypes = [_P, _I, _I, _I, _P, _P, _P]
+_lib.q4nx_moe_router.argtypes = [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P]
 _lib.q4nx_plan_create.argtypes = [ctypes.POINTER(GemvJob), ctypes.POINTER(ctypes.c_int32), _I, _I,
                                   ctypes.POINTER(ctypes.c_void_p)]
 _lib.q4nx_plan_run.argtypes = [_P, _P]
@@ -95,7 +96,7 @@ _lib.q4nx_status_str.argtypes = [_I]
 _lib.q4nx_status_str.restype = ctypes.c_char_p
 _lib.q4nx_last_error.restype = ctypes.c_char_p
 for _f in ("q4nx_weight_check", "q4nx_gemv", "q4nx_gemv_batched", "q4nx_gemm_block", "q4nx_gemm_batched",
-           "q4nx_moe_experts", "q4nx_unpack", "q4nx_decode", "q4nx_repack_q4k_to_q41", "q4nx_q8_rows", "q4nx_argmax", "q4nx_version", "q4nx_plan_create",
+           "q4nx_moe_experts", "q4nx_unpack", "q4nx_decode", "q4nx_repack_q4k_to_q41", "q4nx_q8_rows", "q4nx_argmax", "q4nx_moe_router", "q4nx_version", "q4nx_plan_create",
            "q4nx_plan_run", "q4nx_plan_errors"):
     getattr(_lib, _f).restype = ctypes.c_int
 
@@ -301,6 +302,13 @@ def argmax(y, n: int, M: int, idx, val=None, ldy: int | None = None, stream=None
     """idx[m] = index of the largest of y[m][:n] (lowest on ties, NaNs skipped)."""
     _check(_lib.q4nx_argmax(_ptr(y), n, n if ldy is None else ldy, M, _ptr(idx), _ptr(val),
                             _stream(stream)))
+
+
+def moe_router(R, X, T: int, D: int, E: int, k: int, ids, p, logits=None, renorm: bool = True,
+               stream=None) -> None:
+    """Router on the device: ids [T][k] int32, p [T][k] fp32 from bf16 R [E][D] and X [T][D]."""
+    _check(_lib.q4nx_moe_router(_ptr(R), _ptr(X), T, D, E, k, 1 if renorm else 0, _ptr(ids),
+                                _ptr(p), _ptr(logits), _stream(stream)))
 
 
 def unpack(w: Weight, codes, meta0, meta1=None, row_meta=None, stream=None) -> None:

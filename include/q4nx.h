@@ -314,6 +314,24 @@ int q4nx_q8_rows(const q4nx_weight* w, const int32_t* ids, int T, float* out, vo
 int q4nx_argmax(const float* y, int n, int ldy, int M, int32_t* idx, float* val, void* stream);
 
 /*
+ * MoE router on the device (Strata article, section 2: per token the router
+ * picks k = 10 of 512 experts by the softmax of its logits and weights them by
+ * those probabilities rescaled to sum to one; section 4.3 "tail skip" keeps
+ * them unrescaled).  Produces the ids / p that q4nx_moe_experts takes.
+ *   R       DEVICE bf16 [E][D] router weights (row e contiguous), 16-byte aligned
+ *   X       DEVICE bf16 [T][D] activations, 16-byte aligned
+ *   D       512, 1024, 2048 or 4096 (E_SHAPE otherwise); E 1..1024; k 1..min(16, E)
+ *   renorm  nonzero: p rescaled to sum to one over the k picks
+ *   ids     DEVICE int32 [T][k]: picks in decreasing logit order, the lower id
+ *           first among equal fp32 logits
+ *   p       DEVICE fp32 [T][k]: expf(z - max z) / sum, rescaled when renorm
+ *   logits  DEVICE fp32 [T][E] or NULL: the fp32 logits the picks were made on
+ * Logits accumulate in fp32 in a fixed order; they must be finite.
+ */
+int q4nx_moe_router(const uint16_t* R, const uint16_t* X, int T, int D, int E, int k, int renorm,
+                    int32_t* ids, float* p, float* logits, void* stream);
+
+/*
  * Test surface of the decoders (NPU engine page, "Q4NX chunks": the decoders
  * of all three kinds are checked bit for bit).  Writes the fields of every
  * chunk in logical [rows][cols] order:

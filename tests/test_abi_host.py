@@ -203,6 +203,16 @@ def test_rows_and_argmax_checks(q):
     _expect(q, q.E_ALIGN, q.argmax, 0x2002, 10, 1, 0x3000, stream=0)
 
 
+def test_router_checks(q):
+    ok = dict(stream=0)
+    _expect(q, q.E_ARG, q.moe_router, 0, 0x2000, 1, 2048, 512, 10, 0x3000, 0x4000, **ok)
+    _expect(q, q.E_SHAPE, q.moe_router, 0x1000, 0x2000, 1, 2000, 512, 10, 0x3000, 0x4000, **ok)
+    _expect(q, q.E_ARG, q.moe_router, 0x1000, 0x2000, 1, 2048, 2000, 10, 0x3000, 0x4000, **ok)
+    _expect(q, q.E_ARG, q.moe_router, 0x1000, 0x2000, 1, 2048, 8, 10, 0x3000, 0x4000, **ok)
+    _expect(q, q.E_ARG, q.moe_router, 0x1000, 0x2000, 0, 2048, 512, 10, 0x3000, 0x4000, **ok)
+    _expect(q, q.E_ALIGN, q.moe_router, 0x1008, 0x2000, 1, 2048, 512, 10, 0x3000, 0x4000, **ok)
+
+
 def test_plan_create_checks(q):
     good = (_w(q), 0x2000, 0x3000)
     lib = q.lib()
