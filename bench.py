@@ -508,7 +508,25 @@ def moe_leg(steps, warmup, graph):
                         "pct_hbm_peak": 100 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                         "TFLOP_s": flops / (ms * 1e-3) / 1e12,
                         "launches": (3 if T * k <= 64 else 4) * L}
-        del wss, X, ids, ps, Ys
+        # the router on the device in front of the layer (bf16 router rows 512 x 2048 per layer)
+        Rs = [bf16_dev(synth.bf16_bits((synth.rng("moe_512x10", l, "R").standard_normal((E, D)) * 0.05)
+                                       .astype(np.float32))) for l in range(L)]
+        ids_d = [torch.empty((T, k), dtype=torch.int32, device=DEV) for _ in range(L)]
+        p_d = [torch.empty((T, k), dtype=torch.float32, device=DEV) for _ in range(L)]
+        lg_d = torch.empty((T, E), dtype=torch.float32, device=DEV)
+
+        def run_router(T=T, Rs=Rs, X=X, ids_d=ids_d, p_d=p_d, lg_d=lg_d):
+            st = torch.cuda.current_stream().cuda_stream
+            for l in range(L):
+                r = lib.q4nx_moe_router(Rs[l].data_ptr(), X[l].data_ptr(), T, D, E, k, 1,
+                                        ids_d[l].data_ptr(), p_d[l].data_ptr(), lg_d.data_ptr(), st)
+                if r:
+                    raise q.Q4nxError(r, q.last_error())
+        msr, _ = time_calls(run_router, steps, warmup, graph)
+        rbytes = L * E * D * 2
+        res[f"T{T}"]["router"] = {"ms_per_step": msr, "router_bytes": rbytes,
+                                  "GB_s": rbytes / (msr * 1e-3) / 1e9, "launches": 2 * L}
+        del wss, X, ids, ps, Ys, Rs, ids_d, p_d, lg_d
     del layers
     torch.cuda.empty_cache()
     return res

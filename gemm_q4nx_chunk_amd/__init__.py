@@ -304,9 +304,10 @@ def argmax(y, n: int, M: int, idx, val=None, ldy: int | None = None, stream=None
                             _stream(stream)))
 
 
-def moe_router(R, X, T: int, D: int, E: int, k: int, ids, p, logits=None, renorm: bool = True,
+def moe_router(R, X, T: int, D: int, E: int, k: int, ids, p, logits, renorm: bool = True,
                stream=None) -> None:
-    """Router on the device: ids [T][k] int32, p [T][k] fp32 from bf16 R [E][D] and X [T][D]."""
+    """Router on the device: ids [T][k] int32, p [T][k] fp32 (and the fp32 logits [T][E]
+    they are picked from) from bf16 R [E][D] and X [T][D]."""
     _check(_lib.q4nx_moe_router(_ptr(R), _ptr(X), T, D, E, k, 1 if renorm else 0, _ptr(ids),
                                 _ptr(p), _ptr(logits), _stream(stream)))
 

@@ -717,13 +717,13 @@ int q4nx_argmax(const float* y, int n, int ldy, int M, int32_t* idx, float* val,
 
 int q4nx_moe_router(const uint16_t* R, const uint16_t* X, int T, int D, int E, int k, int renorm,
                     int32_t* ids, float* p, float* logits, void* stream) {
-  if (!R || !X || !ids || !p) return fail(Q4NX_E_ARG, "router: null R, X, ids or p");
+  if (!R || !X || !ids || !p || !logits) return fail(Q4NX_E_ARG, "router: null R, X, ids, p or logits");
   if (T < 1 || T > 65535) return fail(Q4NX_E_ARG, "router: T = %d outside 1..65535", T);
   if (!(D == 512 || D == 1024 || D == 2048 || D == 4096))
     return fail(Q4NX_E_SHAPE, "router: D = %d is not 512, 1024, 2048 or 4096", D);
   if (E < 1 || E > 1024) return fail(Q4NX_E_ARG, "router: E = %d outside 1..1024", E);
   if (k < 1 || k > 16 || k > E) return fail(Q4NX_E_ARG, "router: k = %d outside 1..min(16, E)", k);
-  if (!aligned(R, 16) || !aligned(X, 16) || !aligned(ids, 4) || !aligned(p, 4) || (logits && !aligned(logits, 4)))
+  if (!aligned(R, 16) || !aligned(X, 16) || !aligned(ids, 4) || !aligned(p, 4) || !aligned(logits, 4))
     return fail(Q4NX_E_ALIGN, "router: R and X must be 16-byte, ids/p/logits 4-byte aligned");
   const hipError_t e = q4nx::launch_moe_router(R, X, T, D, E, k, renorm ? 1 : 0, ids, p, logits,
                                                static_cast<hipStream_t>(stream));

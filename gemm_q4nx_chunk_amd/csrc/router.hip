@@ -7,14 +7,13 @@
 // runs on the device, so ids and weights feed q4nx_moe_experts without a
 // host round trip.
 //
-// One workgroup per token.  Router weights are bf16 [E][D] (row e
-// contiguous).  Lane l of a wave holds the token's activations
-// x[512 b + 8 l .. +7] for every 512-column block b; wave w takes rows
-// e = w, w + 4, ...: 16-byte loads of the row, v_dot2_f32_bf16 against the
-// held pairs, and a fixed-order xor reduction over the 64 lanes, so a logit's
-// bits depend only on the data.  The top-k is taken on those fp32 logits (the
-// larger first, the lower id among equals) by k rounds of a fixed-order
-// workgroup reduction; the weights are expf(z - max) / sum in fp32.
+// Two kernels.  Router weights are bf16 [E][D] (row e contiguous); lane l of
+// a wave holds columns 512 b + 8 l .. +7 of each 512-column block b, forms
+// v_dot2_f32_bf16 products in a fixed order and the 64 lanes meet in a
+// fixed-order xor reduction, so a logit's bits depend only on the data.  The
+// top-k is then taken per token on those fp32 logits (the larger first, the
+// lower id among equals) by k rounds of a fixed-order workgroup reduction;
+// the weights are expf(z - max) / sum in fp32.
 #include "q4nx_dev.h"
 
 namespace q4nx {
@@ -26,37 +25,64 @@ __device__ __forceinline__ bool rt_better(float v, int i, float bv, int bi) {
   return bi < 0 || v > bv || (v == bv && i < bi);
 }
 
+// Logits: workgroup (bx, by) takes router rows 8 bx .. 8 bx + 7 (two per
+// wave, held in registers) against tokens 8 by .. 8 by + 7, so the router
+// weights stream through many CUs at once (one workgroup per token would
+// pull them through a single CU).
 template <int DB>
-__global__ __launch_bounds__(256) void k_moe_router(const uint16_t* __restrict__ R,
-                                                    const uint16_t* __restrict__ X, int E, int k,
-                                                    int renorm, int32_t* __restrict__ ids,
-                                                    float* __restrict__ p, float* __restrict__ logits) {
+__global__ __launch_bounds__(256) void k_router_logits(const uint16_t* __restrict__ R,
+                                                       const uint16_t* __restrict__ X, int T, int E,
+                                                       float* __restrict__ logits) {
   constexpr int D = 512 * DB;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r0 = 8 * blockIdx.x + 2 * wave;
+  u32x4 ra[DB], rb[DB];
+  const int ea = r0 < E ? r0 : E - 1, eb = r0 + 1 < E ? r0 + 1 : E - 1;
+#pragma unroll
+  for (int b = 0; b < DB; ++b) {
+    ra[b] = load16(R + (size_t)ea * D + 512 * b + 8 * lane);
+    rb[b] = load16(R + (size_t)eb * D + 512 * b + 8 * lane);
+  }
+  for (int tk = 0; tk < 8; ++tk) {
+    const int t = 8 * blockIdx.y + tk;
+    if (t >= T) break;
+    u32x4 xv[DB];
+#pragma unroll
+    for (int b = 0; b < DB; ++b) xv[b] = load16(X + (size_t)t * D + 512 * b + 8 * lane);
+    float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a0 = dot2bf16(ra[b][i], xv[b][i], a0);
+        a1 = dot2bf16(rb[b][i], xv[b][i], a1);
+      }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      a0 += __shfl_xor(a0, off);
+      a1 += __shfl_xor(a1, off);
+    }
+    if (lane == 0) {
+      if (r0 < E) logits[(size_t)t * E + r0] = a0;
+      if (r0 + 1 < E) logits[(size_t)t * E + r0 + 1] = a1;
+    }
+  }
+}
+
+// Picks and weights: one workgroup per token over its E logits.
+__global__ __launch_bounds__(256) void k_router_topk(const float* __restrict__ logits, int E, int k,
+                                                     int renorm, int32_t* __restrict__ ids,
+                                                     float* __restrict__ p) {
   __shared__ float lg[kRouterMaxE];
   __shared__ uint8_t taken[kRouterMaxE];
   __shared__ float rv[256];
   __shared__ int ri[256];
   __shared__ int sel[kRouterMaxK];
-  const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-
-  u32x4 xv[DB];
-#pragma unroll
-  for (int b = 0; b < DB; ++b) xv[b] = load16(X + (size_t)t * D + 512 * b + 8 * lane);
-  for (int e = wave; e < E; e += 4) {
-    const uint16_t* row = R + (size_t)e * D + 8 * lane;
-    u32x4 rr[DB];
-#pragma unroll
-    for (int b = 0; b < DB; ++b) rr[b] = load16(row + 512 * b);
-    float acc = 0.f;
-#pragma unroll
-    for (int b = 0; b < DB; ++b)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc = dot2bf16(rr[b][i], xv[b][i], acc);
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-    if (lane == 0) lg[e] = acc;
+  const int t = blockIdx.x, tid = threadIdx.x;
+  for (int e = tid; e < E; e += 256) {
+    lg[e] = logits[(size_t)t * E + e];
+    taken[e] = 0;
   }
-  for (int e = tid; e < E; e += 256) taken[e] = 0;
   __syncthreads();
 
   // max and sum of expf(z - max), each a fixed-order reduction
@@ -115,20 +141,19 @@ __global__ __launch_bounds__(256) void k_moe_router(const uint16_t* __restrict__
       p[(size_t)t * k + j] = renorm ? w[j] / tot : w[j];
     }
   }
-  if (logits)
-    for (int e = tid; e < E; e += 256) logits[(size_t)t * E + e] = lg[e];
 }
 
 hipError_t launch_moe_router(const uint16_t* R, const uint16_t* X, int T, int D, int E, int k,
                              int renorm, int32_t* ids, float* p, float* logits, hipStream_t s) {
-  const dim3 g(T), b(256);
+  const dim3 g((E + 7) / 8, (T + 7) / 8), b(256);
   switch (D / 512) {
-    case 1: hipLaunchKernelGGL((k_moe_router<1>), g, b, 0, s, R, X, E, k, renorm, ids, p, logits); break;
-    case 2: hipLaunchKernelGGL((k_moe_router<2>), g, b, 0, s, R, X, E, k, renorm, ids, p, logits); break;
-    case 4: hipLaunchKernelGGL((k_moe_router<4>), g, b, 0, s, R, X, E, k, renorm, ids, p, logits); break;
-    case 8: hipLaunchKernelGGL((k_moe_router<8>), g, b, 0, s, R, X, E, k, renorm, ids, p, logits); break;
+    case 1: hipLaunchKernelGGL((k_router_logits<1>), g, b, 0, s, R, X, T, E, logits); break;
+    case 2: hipLaunchKernelGGL((k_router_logits<2>), g, b, 0, s, R, X, T, E, logits); break;
+    case 4: hipLaunchKernelGGL((k_router_logits<4>), g, b, 0, s, R, X, T, E, logits); break;
+    case 8: hipLaunchKernelGGL((k_router_logits<8>), g, b, 0, s, R, X, T, E, logits); break;
     default: return hipErrorInvalidValue;
   }
+  hipLaunchKernelGGL(k_router_topk, dim3(T), b, 0, s, logits, E, k, renorm, ids, p);
   return hipGetLastError();
 }
 

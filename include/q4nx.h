@@ -325,7 +325,7 @@ int q4nx_argmax(const float* y, int n, int ldy, int M, int32_t* idx, float* val,
  *   ids     DEVICE int32 [T][k]: picks in decreasing logit order, the lower id
  *           first among equal fp32 logits
  *   p       DEVICE fp32 [T][k]: expf(z - max z) / sum, rescaled when renorm
- *   logits  DEVICE fp32 [T][E] or NULL: the fp32 logits the picks were made on
+ *   logits  DEVICE fp32 [T][E]: receives the fp32 logits the picks are made on
  * Logits accumulate in fp32 in a fixed order; they must be finite.
  */
 int q4nx_moe_router(const uint16_t* R, const uint16_t* X, int T, int D, int E, int k, int renorm,

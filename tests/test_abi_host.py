@@ -205,12 +205,13 @@ def test_rows_and_argmax_checks(q):
 
 def test_router_checks(q):
     ok = dict(stream=0)
-    _expect(q, q.E_ARG, q.moe_router, 0, 0x2000, 1, 2048, 512, 10, 0x3000, 0x4000, **ok)
-    _expect(q, q.E_SHAPE, q.moe_router, 0x1000, 0x2000, 1, 2000, 512, 10, 0x3000, 0x4000, **ok)
-    _expect(q, q.E_ARG, q.moe_router, 0x1000, 0x2000, 1, 2048, 2000, 10, 0x3000, 0x4000, **ok)
-    _expect(q, q.E_ARG, q.moe_router, 0x1000, 0x2000, 1, 2048, 8, 10, 0x3000, 0x4000, **ok)
-    _expect(q, q.E_ARG, q.moe_router, 0x1000, 0x2000, 0, 2048, 512, 10, 0x3000, 0x4000, **ok)
-    _expect(q, q.E_ALIGN, q.moe_router, 0x1008, 0x2000, 1, 2048, 512, 10, 0x3000, 0x4000, **ok)
+    _expect(q, q.E_ARG, q.moe_router, 0, 0x2000, 1, 2048, 512, 10, 0x3000, 0x4000, 0x5000, **ok)
+    _expect(q, q.E_SHAPE, q.moe_router, 0x1000, 0x2000, 1, 2000, 512, 10, 0x3000, 0x4000, 0x5000, **ok)
+    _expect(q, q.E_ARG, q.moe_router, 0x1000, 0x2000, 1, 2048, 2000, 10, 0x3000, 0x4000, 0x5000, **ok)
+    _expect(q, q.E_ARG, q.moe_router, 0x1000, 0x2000, 1, 2048, 8, 10, 0x3000, 0x4000, 0x5000, **ok)
+    _expect(q, q.E_ARG, q.moe_router, 0x1000, 0x2000, 0, 2048, 512, 10, 0x3000, 0x4000, 0x5000, **ok)
+    _expect(q, q.E_ALIGN, q.moe_router, 0x1008, 0x2000, 1, 2048, 512, 10, 0x3000, 0x4000, 0x5000, **ok)
+    _expect(q, q.E_ARG, q.moe_router, 0x1000, 0x2000, 1, 2048, 512, 10, 0x3000, 0x4000, None, **ok)
 
 
 def test_plan_create_checks(q):

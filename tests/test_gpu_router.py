@@ -73,7 +73,8 @@ def test_router_feeds_moe_on_device():
     ids_d = torch.empty((T, k), dtype=torch.int32, device="cuda")
     p_d = torch.empty((T, k), dtype=torch.float32, device="cuda")
     Xd = dev_bf16(X)
-    q().moe_router(dev_bf16(R), Xd, T, D, E, k, ids_d, p_d)
+    lg = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    q().moe_router(dev_bf16(R), Xd, T, D, E, k, ids_d, p_d, lg)
     ws = torch.zeros(q().moe_ws(layer.L, T, k), dtype=torch.uint8, device="cuda")
     Y1 = torch.empty((T, D), dtype=torch.float32, device="cuda")
     q().moe_experts(layer.L, Xd, ids_d, p_d, Y1, T, k, ws)
