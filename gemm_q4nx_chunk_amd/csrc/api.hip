@@ -272,7 +272,7 @@ int gemm_launch(q4nx::GemmArgs& a, int kind, void* ws, size_t ws_bytes, void* st
     return fail(Q4NX_E_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", name, ws_bytes, need);
   if (need && !aligned(ws, 256)) return fail(Q4NX_E_ALIGN, "%s: workspace not 256-byte aligned", name);
   a.cnt = need ? static_cast<uint32_t*>(ws) : nullptr;
-  a.partial = need ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + q4nx::gemm_cnt_bytes(a.NB))
+  a.partial = need ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + q4nx::kGemmCntBytes)
                    : nullptr;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const bool local = a.S > 1 && q4nx::xcd_round_robin(st) == 1;

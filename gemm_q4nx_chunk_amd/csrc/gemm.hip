@@ -142,19 +142,20 @@ void k_gemm_q4(GemmArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave: row data in SGPRs
   const int h = lane >> 5, n = lane & 31;
-  // LOCAL: a 1-D grid laid out so that every K part of workgroup row nb has a
-  // linear id = nb (mod 8), i.e. runs on XCD nb % 8 (workgroups are dealt to
-  // the 8 XCDs round-robin by linear id; the host checks this once per device
-  // and the kernel flags any workgroup that finds itself elsewhere).  Then the
-  // parts' partial tiles and arrival counter only ever meet in that XCD's L2.
+  // LOCAL: workgroups are dealt to the 8 XCDs round-robin by linear id,
+  // starting at an XCD that varies between launches (XCD = (id + c) mod 8 for
+  // one c per launch; the host checks the pattern once per device).  So the 8
+  // workgroups of each group r = id / 8 sit on 8 different XCDs, and a
+  // workgroup that takes row nb = 8 (r / S) + (its XCD) and part r % S puts
+  // every K part of row nb on one XCD: their partial tiles and arrival counter
+  // only ever meet in that XCD's L2.
   int nb, part;
   if constexpr (LOCAL) {
-    const int L = blockIdx.x, r = L >> 3;
-    nb = 8 * (r / a.S) + (L & 7);
+    const int r = blockIdx.x >> 3;
+    const int xcc = (int)(__builtin_amdgcn_s_getreg((3 << 11) | 20) & 7);   // HW_REG_XCC_ID
+    nb = 8 * (r / a.S) + xcc;
     part = r % a.S;
     if (nb >= a.NB) return;
-    if (tid == 0 && (int)(__builtin_amdgcn_s_getreg((3 << 11) | 20) & 15) != (L & 7))   // HW_REG_XCC_ID
-      __hip_atomic_fetch_or(a.cnt + a.NB, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   } else {
     nb = blockIdx.x;
     part = blockIdx.y;
@@ -356,6 +357,7 @@ __global__ void k_xcc_probe() {
   if (threadIdx.x == 0) g_xcc_probe[blockIdx.x] = __builtin_amdgcn_s_getreg((3 << 11) | 20) & 15;
 }
 
+// 1 when a 64-workgroup launch lands as XCD = (id + c) mod 8 for one c.
 int xcd_round_robin(hipStream_t s) {
   static int cached[64];
   static bool init = false;
@@ -373,8 +375,8 @@ int xcd_round_robin(hipStream_t s) {
   if (hipGetLastError() != hipSuccess || hipStreamSynchronize(s) != hipSuccess ||
       hipMemcpyFromSymbol(ids, HIP_SYMBOL(g_xcc_probe), sizeof ids, 0, hipMemcpyDeviceToHost) != hipSuccess)
     return 0;
-  int ok = 1;
-  for (int i = 0; i < kProbeWgs; ++i) ok &= ids[i] == (uint32_t)(i % 8);
+  int ok = ids[0] < 8;
+  for (int i = 0; i < kProbeWgs; ++i) ok &= ids[i] == (ids[0] + (uint32_t)i) % 8;
   cached[dev] = ok;
   return ok;
 }

@@ -22,7 +22,7 @@ struct GemmArgs {
   int32_t n_jobs;
   const uint16_t* X;
   float* partial;   // [NB][S][8 waves][8 groups][64 lanes][4] fp32 when S > 1
-  uint32_t* cnt;    // [NB] parts arrived; zero between calls
+  uint32_t* cnt;    // [NB] parts arrived (of kGemmCntWords); zero between calls
   int32_t TC, M, S, NB;
 };
 
@@ -52,20 +52,23 @@ inline int gemm_parts(int nb, int TC) {
   return S;
 }
 
-// Bytes of the arrival counters (256-byte aligned) and of the partial tiles.
-// Counter region: nb arrival counters, then one flag word (set when a
-// workgroup of an XCD-local launch ran on another XCD than laid out).
-inline size_t gemm_cnt_bytes(int nb) { return ((size_t)(nb + 1) * 4 + 255) & ~(size_t)255; }
+// Workspace: kGemmCntWords arrival counters (K is split only when nb * 2 <=
+// the workgroup target, so nb stays below it), padded to 256 bytes, then the
+// partial tiles.  The counter region has the same size for every call, so one
+// zeroed buffer of the largest size any call needs serves calls of any shape.
+constexpr int kGemmCntWords = Q4NX_GEMM_WG_TARGET;
+constexpr size_t kGemmCntBytes = ((size_t)kGemmCntWords * 4 + 255) & ~(size_t)255;
 inline size_t gemm_ws_bytes(int nb, int TC) {
   const int S = gemm_parts(nb, TC);
   if (S == 1) return 0;
-  return gemm_cnt_bytes(nb) + (size_t)nb * S * 64 * kGemmRowsPerWg * 32 * 4;
+  return kGemmCntBytes + (size_t)nb * S * 64 * kGemmRowsPerWg * 32 * 4;
 }
 
 // local: lay the K parts of each workgroup row on one XCD (see gemm.hip).
 hipError_t launch_gemm(int kind, const GemmArgs& a, bool local, hipStream_t s);
-// 1 when this device deals workgroups to 8 XCDs round-robin by linear id
-// (checked once per device with a 64-workgroup probe, outside graph capture).
+// 1 when this device deals a launch's workgroups to its 8 XCDs round-robin by
+// linear id, from a starting XCD that may vary per launch (checked once per
+// device with a 64-workgroup probe, outside graph capture).
 int xcd_round_robin(hipStream_t s);
 
 }  // namespace q4nx

@@ -186,8 +186,10 @@ void q4nx_plan_destroy(q4nx_plan plan);
  *   M  1..Q4NX_GEMM_MAX_M
  *   ws DEVICE workspace of q4nx_gemm_block_ws(w) bytes, 256-byte aligned (may
  *      be NULL when that size is 0).  It must hold zeros before its first use;
- *      every call leaves it ready for the next one.  One workspace serves one
- *      call at a time.  (K is split over several workgroups when the tile rows
+ *      every call leaves it ready for the next one.  Its layout does not
+ *      depend on the call (256 counter words, then the partial tiles), so one
+ *      buffer of the largest size any call needs serves calls of any shape,
+ *      one call at a time.  (K is split over several workgroups when the tile rows
  *      alone would leave CUs idle; the workspace holds their partial tiles.)
  * The bf16 rounding of each weight moves it by at most 2^-8 of its size; with
  * random signs the error of a sum over K stays well inside 2e-3 * sum |w x|.

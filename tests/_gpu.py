@@ -47,3 +47,24 @@ def gemv(chunks_dev, N, K, kind, x_bits, layout=None):
     y = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
     q().gemv(weight(chunks_dev, N, K, kind, layout), x, y, M)
     return host(y)
+
+
+_SHIFT = {}
+
+
+def shift_xcd_start(n_wg: int = 1):
+    """Launch n_wg one-workgroup GEMVs (q4nx_gemv of a 32 x 256 weight).
+
+    Workgroups are dealt to the XCDs round-robin from a starting XCD that
+    carries over between launches, so launches of odd workgroup counts move
+    where the next launch's workgroup 0 lands.  Tests of the XCD-local
+    exchanges put these between calls.
+    """
+    if "w" not in _SHIFT:
+        import numpy as np
+        _SHIFT["w"] = torch.zeros(5120, dtype=torch.uint8, device="cuda")
+        _SHIFT["x"] = torch.zeros(256, dtype=torch.int16, device="cuda")
+        _SHIFT["y"] = torch.empty(32, dtype=torch.float32, device="cuda")
+    w = q().weight(_SHIFT["w"], 32, 256, "q4_1")
+    for _ in range(n_wg):
+        q().gemv(w, _SHIFT["x"], _SHIFT["y"], 1)
