@@ -409,7 +409,7 @@ def gemm_leg(steps, warmup, graph):
     ach = nbytes / (ms * 1e-3) / 1e9
     res["M64"]["roofline"] = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                               "frac": ach / HBM_PEAK_GBS, "traffic": profiled_traffic("k_gemm_q4"),
-                              "kernel": "k_gemm_q4<q4_1, M=64>",
+                              "kernel": "k_gemm_q4h<q4_1> (M = 64)",
                               "avg_launch_us": ms * 1e3 / n_launch,
                               "bytes_per_launch": nbytes / n_launch,
                               "mfma_frac": flops / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS}

@@ -254,7 +254,7 @@ int gemm_setup(const q4nx_weight* const* w, float* const* Y, int n, const uint16
     a.job[i].Y = Y[i];
     a.job[i].TR = (int32_t)(w[i]->rows / 32);
     a.job[i].nb0 = nb;
-    nb += q4nx::gemm_blocks(a.job[i].TR);
+    nb += q4nx::gemm_blocks(a.job[i].TR, M);
   }
   a.n_jobs = n;
   a.X = X;
@@ -267,7 +267,7 @@ int gemm_setup(const q4nx_weight* const* w, float* const* Y, int n, const uint16
 
 int gemm_launch(q4nx::GemmArgs& a, int kind, void* ws, size_t ws_bytes, void* stream,
                 const char* name) {
-  const size_t need = q4nx::gemm_ws_bytes(a.NB, a.TC);
+  const size_t need = q4nx::gemm_ws_bytes(a.NB, a.TC, a.M);
   if (need && (!ws || ws_bytes < need))
     return fail(Q4NX_E_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", name, ws_bytes, need);
   if (need && !aligned(ws, 256)) return fail(Q4NX_E_ALIGN, "%s: workspace not 256-byte aligned", name);
@@ -295,7 +295,8 @@ int q4nx_gemm_block(const q4nx_weight* w, const uint16_t* X, float* Y, int M, vo
 
 size_t q4nx_gemm_block_ws(const q4nx_weight* w) {
   if (check_weight(w, "gemm_block_ws")) return 0;
-  return q4nx::gemm_ws_bytes(q4nx::gemm_blocks((int)(w->rows / 32)), (int)(w->cols / 256));
+  const int TR = (int)(w->rows / 32);
+  return q4nx::gemm_ws_bytes_any_m(&TR, 1, (int)(w->cols / 256));
 }
 
 int q4nx_gemm_batched(const q4nx_gemm_job* jobs, int n_jobs, const uint16_t* X, int M, void* ws,
@@ -321,12 +322,12 @@ size_t q4nx_gemm_batched_ws(const q4nx_gemm_job* jobs, int n_jobs) {
     fail(Q4NX_E_ARG, "gemm_batched_ws: bad job array");
     return 0;
   }
-  int nb = 0;
+  int TR[Q4NX_GEMM_BATCH_MAX_JOBS];
   for (int i = 0; i < n_jobs; ++i) {
     if (check_weight(&jobs[i].w, "gemm_batched_ws")) return 0;
-    nb += q4nx::gemm_blocks((int)(jobs[i].w.rows / 32));
+    TR[i] = (int)(jobs[i].w.rows / 32);
   }
-  return q4nx::gemm_ws_bytes(nb, (int)(jobs[0].w.cols / 256));
+  return q4nx::gemm_ws_bytes_any_m(TR, n_jobs, (int)(jobs[0].w.cols / 256));
 }
 
 // ---------------------------------------------------------------------------

@@ -328,14 +328,231 @@ void k_gemm_q4(GemmArgs a) {
   }
 }
 
+// The M > 32 variant: 8 waves = 4 tile rows x 2 halves of the workgroup's K
+// range.  Wave (row rho, half pi) multiplies tile row rho's chunks of its
+// half; the halves meet in LDS at the end (fixed order: first + second).  A
+// workgroup covers 4 tile rows, so twice as many workgroups fill the chip
+// before K has to be split across workgroups, whose fp32 partial tiles (64
+// tokens x 32 outputs per row) cost as many bytes as a few tile columns of
+// weights.  The X columns of both halves' current tile columns (2 x 64 x 256
+// bf16) sit in LDS, double buffered: the tiles two steps ahead are loaded into
+// registers at the start of a step and written to the other buffer at the end
+// of the next.  Chunk loads run D steps ahead in a ring of D register sets; as
+// above, every load is unconditional and every branch uniform.
+template <int KIND, int D, bool LOCAL>
+__global__ __launch_bounds__(64 * kGemmWaves)
+__attribute__((amdgpu_waves_per_eu(Q4NX_GEMM_WPE_TWO, Q4NX_GEMM_WPE_TWO)))
+void k_gemm_q4h(GemmArgs a) {
+  constexpr int CB = ChunkBytes<KIND>::value;
+  constexpr int XR = 64, G = 8, R = kGemmRowsHalves;
+  constexpr int NH = 64 * kGemmWaves / 2;    // threads of one half
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][2][XR * kXs];   // [buffer][half]
+  __shared__ uint32_t s_old;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave: row data in SGPRs
+  const int rho = wave & (R - 1), pi = wave / R;
+  const int h = lane >> 5, n = lane & 31;
+  int nb, part;   // workgroup row and K part, laid out as in k_gemm_q4
+  if constexpr (LOCAL) {
+    const int r = blockIdx.x >> 3;
+    const int xcc = (int)(__builtin_amdgcn_s_getreg((3 << 11) | 20) & 7);   // HW_REG_XCC_ID
+    nb = 8 * (r / a.S) + xcc;
+    part = r % a.S;
+    if (nb >= a.NB) return;
+  } else {
+    nb = blockIdx.x;
+    part = blockIdx.y;
+  }
+  int ji = 0;
+  for (int i = 1; i < a.n_jobs; ++i)
+    if (nb >= a.job[i].nb0) ji = i;
+  const GemmJob& job = a.job[ji];
+  const int tr_raw = (nb - job.nb0) * R + rho;
+  const bool active = tr_raw < job.TR;
+  const int tr = active ? tr_raw : job.TR - 1;
+  const int K = a.TC * 256, N = job.TR * 32, M = a.M;
+  // the workgroup's K part [tc0, tc1), cut into halves [tc0, mid) and [mid, tc1)
+  const int tc0 = part * a.TC / a.S, tc1 = (part + 1) * a.TC / a.S;
+  const int mid = tc0 + (tc1 - tc0 + 1) / 2;
+  const int nsteps = mid - tc0;                          // steps of the first (longer) half
+  const int hc0 = pi ? mid : tc0, hc1 = pi ? tc1 : mid;  // this wave's half
+  const __amdgpu_buffer_rsrc_t wrs =
+      make_rsrc(job.w + ((size_t)tr * a.TC + hc0) * CB, (uint32_t)((hc1 - hc0) * CB));
+
+  uint32_t kMaskLo = 0x000F000Fu, kMaskHi = 0x00F000F0u, kMagic = 0x64006400u;
+  asm volatile("" : "+s"(kMaskLo));
+  asm volatile("" : "+s"(kMaskHi));
+  asm volatile("" : "+v"(kMagic));
+
+  // X tile loader: the threads of half pi load that half's tile, 64 rows x 32
+  // pieces of 16 B; thread th takes rows th / 32 + 8 p.  Rows past M fall
+  // outside the buffer resource and read zero; past the end of the half the
+  // loads read other columns of X or zeros.  Those values are never stored.
+  constexpr int XP = XR * 32 / NH;
+  const int th = tid - pi * NH;
+  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(a.X, (uint32_t)(M * K * 2));
+  const uint32_t xoff = (uint32_t)((th >> 5) * K + (th & 31) * 8) * 2;
+  const uint32_t xrow8 = (uint32_t)(8 * K * 2);          // 8 rows of X, bytes
+  u32x4 xr[2][XP];
+  auto xload = [&](int b, int t) {   // t: step index (tile column hc0 + t)
+    const uint32_t col = (uint32_t)(hc0 + t) * 512;
+#pragma unroll
+    for (int p = 0; p < XP; ++p)
+      xr[b][p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs, xoff + col, p * xrow8, 0));
+  };
+  auto xstore = [&](int b) {
+#pragma unroll
+    for (int p = 0; p < XP; ++p) {
+      const int piece = th + NH * p, row = piece >> 5, c16 = piece & 31;
+      *reinterpret_cast<u32x4*>(&xs[b][pi][row * kXs + c16 * 8]) = xr[b][p];
+    }
+  };
+
+  f32x16 acc0, acc1;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) { acc0[v] = 0.f; acc1[v] = 0.f; }
+
+  GemmChunk<KIND> c[D];
+  xload(0, 0);
+#pragma unroll
+  for (int j = 0; j < D; ++j) gemm_load<KIND>(wrs, j * CB, n, h, c[j]);
+  xstore(0);
+  xload(1, 1);
+
+  // Step t (parity j): this half's X tile is in xs[j][pi], its chunk in c[j];
+  // the tiles of step t + 1 are in flight in xr[j ^ 1].  The second half may
+  // have one step fewer: its waves skip the products of that step.
+  static_assert(D % 2 == 0, "the X double buffer follows the chunk ring's parity");
+  auto step = [&](int j, int t) {
+    __syncthreads();                       // the tiles of step t are in xs[j]; xs[j ^ 1] is free
+    xload(j, t + 2);                       // xr[j] went to LDS at the end of step t - 1
+    __builtin_amdgcn_sched_barrier(0);     // issue the X loads before the products
+    if (hc0 + t < hc1) {
+      const uint16_t* xb = xs[j][pi] + n * kXs + 128 * h;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float s, z;
+        group_sz<KIND>(c[j], q, s, z);
+        const float z_lo = fmaf(-1024.f, s, z), s16 = s * 0.0625f, z_hi = fmaf(-64.f, s, z);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int st = 4 * q + e;
+          const bf16x8 B = dequant8(c[j].q[q][e], s, z_lo, s16, z_hi, kMaskLo, kMaskHi, kMagic);
+          const bf16x8 A0 = *reinterpret_cast<const bf16x8*>(xb + 8 * st);
+          const bf16x8 A1 = *reinterpret_cast<const bf16x8*>(xb + 32 * kXs + 8 * st);
+          acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A0, B, acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A1, B, acc1, 0, 0, 0);
+        }
+      }
+    }
+    gemm_load<KIND>(wrs, (uint32_t)(t + D) * CB, n, h, c[j]);
+    xstore(j ^ 1);                         // tiles of step t + 1, loaded during step t - 1
+  };
+  int base = 0;
+  for (; base + D <= nsteps; base += D) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) step(j, base + j);
+  }
+#pragma unroll
+  for (int j = 0; j + 1 < D; ++j)
+    if (base + j < nsteps) step(j, base + j);
+
+  // 32x32 accumulator: register v of lane holds token row 8*(v/4) + 4*h + v%4, output column n.
+  f32x4 mine[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mine[g][i] = g < 4 ? acc0[4 * g + i] : acc1[4 * (g - 4) + i];
+
+  // The halves meet in LDS: the second half's waves leave their sums in the
+  // X buffers, the first half's add them (first + second).
+  __syncthreads();
+  f32x4* red = reinterpret_cast<f32x4*>(&xs[0][0][0]);   // [R rows][G][64 lanes]
+  static_assert(sizeof(xs) >= sizeof(f32x4) * R * G * 64, "LDS for the halves' sums");
+  if (pi == 1) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) red[(rho * G + g) * 64 + lane] = mine[g];
+  }
+  __syncthreads();
+  if (pi == 0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) mine[g] += red[(rho * G + g) * 64 + lane];
+  }
+
+  auto store_y = [&](const f32x4* r) {
+    float* yc = job.Y + 32 * tr + n;
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = 32 * (g >> 2) + 8 * (g & 3) + 4 * h + i;
+        if (m < M) yc[(size_t)m * N] = r[g][i];
+      }
+  };
+  if (a.S == 1) {
+    if (pi == 0 && active) store_y(mine);
+    return;
+  }
+
+  // Split K as in k_gemm_q4, over R rows per workgroup row: the first half's
+  // waves hold the sums; the second half's only take part in the barriers.
+  constexpr size_t kPartBytes = (size_t)R * 8 * 64 * 16;
+  const uint32_t part_bytes = (uint32_t)(kPartBytes * a.S);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.partial + (size_t)nb * a.S * (kPartBytes / 4), part_bytes);
+  const uint32_t lane_off = (uint32_t)(rho * 8 * 64 + lane) * 16;
+  constexpr int kStPol = LOCAL ? 0 : kCpolSc1;
+  constexpr int kLdPol = LOCAL ? 1 : kCpolSc1;   // sc0: past this CU's L1
+  if (pi == 0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, mine[g]), rs,
+                                             lane_off + part * (uint32_t)kPartBytes + g * 1024, 0, kStPol);
+  }
+  wait_stores();
+  __syncthreads();
+  if (tid == 0) {
+    if constexpr (LOCAL) s_old = __hip_atomic_fetch_add(a.cnt + nb, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    else s_old = __hip_atomic_fetch_add(a.cnt + nb, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (s_old != (uint32_t)a.S - 1 || pi == 1) return;
+
+  constexpr int PB = 2;                      // parts loaded per round trip (64 registers)
+  f32x4 sum[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) sum[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int p0 = 0; p0 < a.S; p0 += PB) {
+    f32x4 in[PB][G];
+#pragma unroll
+    for (int jj = 0; jj < PB; ++jj)
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+        in[jj][g] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  rs, lane_off + (p0 + jj) * (uint32_t)kPartBytes + g * 1024, 0, kLdPol));
+#pragma unroll
+    for (int jj = 0; jj < PB; ++jj)
+      if (p0 + jj < a.S)
+#pragma unroll
+        for (int g = 0; g < G; ++g) sum[g] += in[jj][g];
+  }
+  if (active) store_y(sum);
+  if (tid == 0) {
+    if constexpr (LOCAL) __hip_atomic_store(a.cnt + nb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    else __hip_atomic_store(a.cnt + nb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 template <int KIND, bool TWO>
 static hipError_t launch_kind(const GemmArgs& a, bool local, hipStream_t s) {
   const dim3 block(64 * kGemmWaves);
-  if (local && a.S > 1) {
-    const dim3 grid(8 * ((a.NB + 7) / 8) * a.S);
-    hipLaunchKernelGGL((k_gemm_q4<KIND, TWO, kGemmDepth, true>), grid, block, 0, s, a);
+  const bool lc = local && a.S > 1;
+  const dim3 grid = lc ? dim3(8 * ((a.NB + 7) / 8) * a.S) : dim3(a.NB, a.S);
+  if constexpr (TWO) {
+    if (lc) hipLaunchKernelGGL((k_gemm_q4h<KIND, kGemmDepth, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_gemm_q4h<KIND, kGemmDepth, false>), grid, block, 0, s, a);
   } else {
-    hipLaunchKernelGGL((k_gemm_q4<KIND, TWO, kGemmDepth, false>), dim3(a.NB, a.S), block, 0, s, a);
+    if (lc) hipLaunchKernelGGL((k_gemm_q4<KIND, false, kGemmDepth, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_gemm_q4<KIND, false, kGemmDepth, false>), grid, block, 0, s, a);
   }
   return hipGetLastError();
 }

@@ -26,8 +26,11 @@ struct GemmArgs {
   int32_t TC, M, S, NB;
 };
 
-// Tile rows per workgroup of the block GEMM.
+// Tile rows per workgroup of the block GEMM: 8 for M <= 32 (a wave per row),
+// 4 for M > 32 (a wave per row and K half).
 constexpr int kGemmRowsPerWg = 8;
+constexpr int kGemmRowsHalves = 4;
+inline int gemm_rows(int M) { return M > 32 ? kGemmRowsHalves : kGemmRowsPerWg; }
 
 // Workgroups a launch aims for (one per CU), and the fewest tile columns a K
 // part may hold (so the fp32 partial tiles stay small next to the weights
@@ -39,7 +42,7 @@ constexpr int kGemmRowsPerWg = 8;
 #define Q4NX_GEMM_MIN_COLS 4
 #endif
 
-inline int gemm_blocks(int TR) { return (TR + kGemmRowsPerWg - 1) / kGemmRowsPerWg; }
+inline int gemm_blocks(int TR, int M) { return (TR + gemm_rows(M) - 1) / gemm_rows(M); }
 
 // K parts for a launch of nb workgroup rows over TC tile columns: as many as
 // keep all workgroups resident at once (nb * S <= the target), at most one
@@ -58,10 +61,21 @@ inline int gemm_parts(int nb, int TC) {
 // zeroed buffer of the largest size any call needs serves calls of any shape.
 constexpr int kGemmCntWords = Q4NX_GEMM_WG_TARGET;
 constexpr size_t kGemmCntBytes = ((size_t)kGemmCntWords * 4 + 255) & ~(size_t)255;
-inline size_t gemm_ws_bytes(int nb, int TC) {
+inline size_t gemm_ws_bytes(int nb, int TC, int M) {
   const int S = gemm_parts(nb, TC);
   if (S == 1) return 0;
-  return kGemmCntBytes + (size_t)nb * S * 64 * kGemmRowsPerWg * 32 * 4;
+  return kGemmCntBytes + (size_t)nb * S * 64 * gemm_rows(M) * 32 * 4;
+}
+// Workspace for a launch over weights of tile rows TR[0..n-1] at any M.
+inline size_t gemm_ws_bytes_any_m(const int* TR, int n, int TC) {
+  size_t best = 0;
+  for (int M : {32, 64}) {
+    int nb = 0;
+    for (int i = 0; i < n; ++i) nb += gemm_blocks(TR[i], M);
+    const size_t b = gemm_ws_bytes(nb, TC, M);
+    if (b > best) best = b;
+  }
+  return best;
 }
 
 // local: lay the K parts of each workgroup row on one XCD (see gemm.hip).
