@@ -101,6 +101,16 @@ int pow2_at_least(int v, int cap) {
 #define Q4NX_SMALL_MIN_TC 17
 #endif
 
+// Launches of at most Q4NX_ROWSPLIT_TR tile rows (q4 kinds, prepared
+// activations) split each tile's rows into two units of 16, and of at most
+// Q4NX_ROWSPLIT4_TR into four units of 8, so they reach more CUs.
+#ifndef Q4NX_ROWSPLIT_TR
+#define Q4NX_ROWSPLIT_TR 1024
+#endif
+#ifndef Q4NX_ROWSPLIT4_TR
+#define Q4NX_ROWSPLIT4_TR 0
+#endif
+
 int pick_waves(int64_t total_tr, int M, int max_tc) {
   return (total_tr >= Q4NX_SMALL_ROWS || M > 2 || max_tc < Q4NX_SMALL_MIN_TC) ? 4 : 16;
 }
@@ -122,10 +132,15 @@ int run_batch(int kind, const q4nx_gemv_job* const* jobs, int n, int M, hipStrea
     max_tc = std::max(max_tc, jobs[i]->w.cols / 256);
   }
   const int waves = pick_waves(total_tr, M, max_tc);
+  const int xl = q4nx::gemv_xl_bytes(kind, M, waves, max_tc);
+  const bool q4 = kind == q4nx::KIND_Q4_1 || kind == q4nx::KIND_Q4_K;
+  const int parts = !(q4 && xl > 0) ? 1                                     // units per tile row
+                    : total_tr <= Q4NX_ROWSPLIT4_TR ? 4 : total_tr <= Q4NX_ROWSPLIT_TR ? 2 : 1;
   for (int i0 = 0; i0 < n; i0 += q4nx::kMaxBatch) {
     const int cnt = n - i0 < q4nx::kMaxBatch ? n - i0 : q4nx::kMaxBatch;
     q4nx::GemvBatch b;
     memset(&b, 0, sizeof b);
+    b.sl = 4 / parts;
     int wg = 0;
     for (int t = 0; t < cnt; ++t) {
       const q4nx_gemv_job* j = jobs[i0 + t];
@@ -140,11 +155,10 @@ int run_batch(int kind, const q4nx_gemv_job* const* jobs, int n, int M, hipStrea
       g.ks = pick_ks(waves, total_tr, g.TC);
       g.wg_begin = wg;
       const int rpw = waves / g.ks;
-      wg += (g.TR + rpw - 1) / rpw;
+      wg += (g.TR * parts + rpw - 1) / rpw;
     }
     b.n_jobs = cnt;
-    const hipError_t e =
-        q4nx::launch_gemv(kind, M, waves, b, wg, q4nx::gemv_xl_bytes(kind, M, waves, max_tc), s);
+    const hipError_t e = q4nx::launch_gemv(kind, M, waves, b, wg, xl, s);
     if (e != hipSuccess) return hip_status(e, "gemv launch");
   }
   return Q4NX_OK;

@@ -76,20 +76,30 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_q4(const GemvBatch b) {
 // every wait is for the chunk D steps back.  The host uses this kernel when
 // the prepared records (M * TC * 8 per job, 72 bytes each) fit XRP per thread
 // and the LDS budget; otherwise k_gemv_q4.
-template <int KIND, int M, int WAVES, int D>
+//
+// SL = 2 (or 1) splits each tile's 32 rows into two units of 16 (chunk slices
+// 0-1 and 2-3: 2 KB of codes and 512 B of scales each), or four of 8, so a
+// launch of few tile rows spreads over more compute units with no partial
+// sums to combine.  (One CU draws only a few tens of GB/s from HBM, so a 2560-row
+// projection, 80 tile rows, otherwise streams from 80 CUs.)
+template <int KIND, int M, int WAVES, int D, int SL = 4>
 __global__ __launch_bounds__(64 * WAVES) void k_gemv_q4x(const GemvBatch b) {
   constexpr int NT = 64 * WAVES;
   constexpr int XRP = 2;
   constexpr int CB = ChunkBytes<KIND>::value;
+  constexpr int PARTS = 4 / SL;       // units per tile row
+  constexpr int UR = 8 * SL;          // output rows per unit
   extern __shared__ __attribute__((aligned(16))) uint32_t xl[];
-  __shared__ float red[WAVES][32][M];
+  __shared__ float red[WAVES][UR][M];
   const GemvJob& J = b.job[find_job(b, blockIdx.x)];
   const int ks = J.ks, rpw = WAVES / ks;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int slot = wave / ks, part = wave % ks;
-  const int tr0 = (blockIdx.x - J.wg_begin) * rpw;
-  const int tr = tr0 + slot < J.TR ? tr0 + slot : J.TR - 1;   // spare waves redo the last row, unstored
+  const int NU = J.TR * PARTS;        // units of the job
+  const int u0 = (blockIdx.x - J.wg_begin) * rpw;
+  const int u = u0 + slot < NU ? u0 + slot : NU - 1;          // spare waves redo the last unit, unstored
+  const int tr = u / PARTS, i0 = (u - tr * PARTS) * SL;
   const int TC = J.TC, g = lane & 7;
   const int c0 = part * TC / ks, c1 = (part + 1) * TC / ks;
   const int R = M * TC * 8;
@@ -108,9 +118,9 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_q4x(const GemvBatch b) {
   // 2. the first D chunks of the wave's run
   const __amdgpu_buffer_rsrc_t wrs =
       make_rsrc(J.w + ((size_t)tr * TC + c0) * CB, (uint32_t)((c1 - c0) * CB));
-  Q4Chunk<KIND> ring[D];
+  Q4Chunk<KIND, SL> ring[D];
 #pragma unroll
-  for (int j = 0; j < D; ++j) q4_load_rs<KIND>(wrs, j * CB, lane, ring[j]);
+  for (int j = 0; j < D; ++j) q4_load_rs<KIND>(wrs, j * CB, lane, ring[j], i0);
   // 3. prepared records to LDS: pairs at xl[16 r], (d136, sum) at xl[16 R + 2 r]
   float* sums = reinterpret_cast<float*>(xl + 16 * R);
 #pragma unroll
@@ -135,9 +145,9 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_q4x(const GemvBatch b) {
   uint32_t kMask = 0x000F000Fu, kMagic = 0x43004300u;
   asm volatile("" : "+s"(kMask));
   asm volatile("" : "+v"(kMagic));
-  float acc[4][M];
+  float acc[SL][M];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < SL; ++i)
 #pragma unroll
     for (int m = 0; m < M; ++m) acc[i][m] = 0.f;
   auto step = [&](int j, int c) {
@@ -158,7 +168,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_q4x(const GemvBatch b) {
       xp.sum[m] = sums[2 * r + 1];
     }
     q4_compute<KIND, M>(ring[j], xp, kMask, kMagic, acc);
-    q4_load_rs<KIND>(wrs, (uint32_t)(c + D - c0) * CB, lane, ring[j]);
+    q4_load_rs<KIND>(wrs, (uint32_t)(c + D - c0) * CB, lane, ring[j], i0);
   };
   int base = c0;
   for (; base + D <= c1; base += D) {
@@ -172,19 +182,19 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_q4x(const GemvBatch b) {
   q4_lane_reduce<M>(acc);
   if (g == 0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < SL; ++i)
 #pragma unroll
       for (int m = 0; m < M; ++m) red[wave][8 * i + (lane >> 3)][m] = acc[i][m];
   }
   __syncthreads();
-  for (int idx = tid; idx < rpw * 32 * M; idx += NT) {
-    const int s = idx / (32 * M), rem = idx - s * 32 * M;
+  for (int idx = tid; idx < rpw * UR * M; idx += NT) {
+    const int s = idx / (UR * M), rem = idx - s * UR * M;
     const int r = rem / M, m = rem - r * M;
-    const int t = tr0 + s;
-    if (t < J.TR) {
+    const int t = u0 + s;   // unit: tile row t / PARTS, rows UR * (t % PARTS) + r of it
+    if (t < NU) {
       float v = 0.f;
       for (int p = 0; p < ks; ++p) v += red[s * ks + p][r][m];
-      J.y[(size_t)m * J.ldy + 32 * t + r] = v;
+      J.y[(size_t)m * J.ldy + UR * t + r] = v;
     }
   }
 }
@@ -379,7 +389,11 @@ template <int KIND, int M, int WAVES>
 static hipError_t launch_one(const GemvBatch& b, int n_wg, int xl_bytes, hipStream_t s) {
   if constexpr (KIND == KIND_Q4_1 || KIND == KIND_Q4_K) {
     constexpr int D = GemvXDepth<M, WAVES>::value;
-    if (xl_bytes > 0)
+    if (xl_bytes > 0 && b.sl == 2)
+      hipLaunchKernelGGL((k_gemv_q4x<KIND, M, WAVES, D, 2>), dim3(n_wg), dim3(64 * WAVES), xl_bytes, s, b);
+    else if (xl_bytes > 0 && b.sl == 1)
+      hipLaunchKernelGGL((k_gemv_q4x<KIND, M, WAVES, D, 1>), dim3(n_wg), dim3(64 * WAVES), xl_bytes, s, b);
+    else if (xl_bytes > 0)
       hipLaunchKernelGGL((k_gemv_q4x<KIND, M, WAVES, D>), dim3(n_wg), dim3(64 * WAVES), xl_bytes, s, b);
     else
       hipLaunchKernelGGL((k_gemv_q4<KIND, M, WAVES>), dim3(n_wg), dim3(64 * WAVES), 0, s, b);

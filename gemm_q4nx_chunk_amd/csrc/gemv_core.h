@@ -23,11 +23,13 @@ namespace q4nx {
 // identical operand bits give identical chain results).  For Q4_K, s = S*scale
 // and z = M*min (both products exact in fp32).
 
-template <int KIND>
+// SL slices of a chunk (all 4, or 2 for launches that split a tile's rows
+// between workgroups: slices i0 .. i0 + SL - 1 are rows 8 i0 .. 8 (i0 + SL) - 1).
+template <int KIND, int SL = 4>
 struct Q4Chunk {
-  u32x4 q[4];
-  uint32_t meta[4];   // q4_1: (scale, zero) bf16 pair;  Q4_K: (sc | mn << 8)
-  uint32_t rowsm[4];  // Q4_K: (S, M) bf16 pair of the lane's row
+  u32x4 q[SL];
+  uint32_t meta[SL];   // q4_1: (scale, zero) bf16 pair;  Q4_K: (sc | mn << 8)
+  uint32_t rowsm[SL];  // Q4_K: (S, M) bf16 pair of the lane's row
 };
 
 template <int KIND>
@@ -49,21 +51,22 @@ __device__ __forceinline__ void q4_load(const uint8_t* __restrict__ ck, int lane
 // q4_load through a buffer resource over a run of chunks: off is the chunk's
 // byte offset in the run.  Offsets past the run read zero without touching
 // memory, so a prefetch past the last chunk needs no branch.
-template <int KIND>
+template <int KIND, int SL = 4>
 __device__ __forceinline__ void q4_load_rs(__amdgpu_buffer_rsrc_t rs, uint32_t off, int lane,
-                                           Q4Chunk<KIND>& c) {
+                                           Q4Chunk<KIND, SL>& c, int i0 = 0) {
   constexpr int kNt = 2;   // nontemporal: weights are read once
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    c.q[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 1024 * i + 16 * lane, 0, kNt));
+  for (int i = 0; i < SL; ++i)
+    c.q[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 1024 * (i0 + i) + 16 * lane, 0, kNt));
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < SL; ++i) {
+    const int si = i0 + i;
     if constexpr (KIND == KIND_Q4_1) {
-      c.meta[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, off + 4096 + 256 * i + 4 * lane, 0, 0);
+      c.meta[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, off + 4096 + 256 * si + 4 * lane, 0, 0);
       c.rowsm[i] = 0;
     } else {
-      c.meta[i] = __builtin_amdgcn_raw_buffer_load_b16(rs, off + 4096 + 128 * i + 2 * lane, 0, 0);
-      c.rowsm[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, off + 4608 + 32 * i + 4 * (lane >> 3), 0, 0);
+      c.meta[i] = __builtin_amdgcn_raw_buffer_load_b16(rs, off + 4096 + 128 * si + 2 * lane, 0, 0);
+      c.rowsm[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, off + 4608 + 32 * si + 4 * (lane >> 3), 0, 0);
     }
   }
 }
@@ -135,11 +138,11 @@ __device__ __forceinline__ void x_prep(const uint16_t* const (&xrow)[M], int col
   x_prep_raw<M>(r, xp);
 }
 
-template <int KIND, int M>
-__device__ __forceinline__ void q4_compute(const Q4Chunk<KIND>& c, const XPrep<M>& xp,
-                                           uint32_t kMask, uint32_t kMagic, float (&acc)[4][M]) {
+template <int KIND, int M, int SL = 4>
+__device__ __forceinline__ void q4_compute(const Q4Chunk<KIND, SL>& c, const XPrep<M>& xp,
+                                           uint32_t kMask, uint32_t kMagic, float (&acc)[SL][M]) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < SL; ++i) {
     float s, zz;
     if constexpr (KIND == KIND_Q4_1) {
       s = bf16lo(c.meta[i]);
@@ -370,10 +373,10 @@ __device__ __forceinline__ void q4_row_partial(const uint8_t* __restrict__ row, 
 
 // Sum a lane's partials over the 8 groups; afterwards every lane of the 8
 // holds the row sum of rows 8i + lane/8.
-template <int M>
-__device__ __forceinline__ void q4_lane_reduce(float (&acc)[4][M]) {
+template <int M, int SL = 4>
+__device__ __forceinline__ void q4_lane_reduce(float (&acc)[SL][M]) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < SL; ++i)
 #pragma unroll
     for (int m = 0; m < M; ++m) acc[i][m] = sum_lanes_xor7(acc[i][m]);
 }

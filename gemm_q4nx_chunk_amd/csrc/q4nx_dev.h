@@ -50,6 +50,10 @@ constexpr int kMaxBatch = 64;
 struct GemvBatch {
   GemvJob job[kMaxBatch];
   int32_t n_jobs;
+  // chunk slices per unit of work: 4 (a unit is a tile row), or 2 (a unit is
+  // 16 rows of a tile; q4 kinds with prepared activations only).  The jobs'
+  // wg_begin and ks then count units.
+  int32_t sl;
 };
 
 // ---------------------------------------------------------------------------
