@@ -12,8 +12,8 @@
 // v_dot2_f32_bf16 products in a fixed order and the 64 lanes meet in a
 // fixed-order xor reduction, so a logit's bits depend only on the data.  The
 // top-k is then taken per token on those fp32 logits (the larger first, the
-// lower id among equals) by k rounds of a fixed-order workgroup reduction;
-// the weights are expf(z - max) / sum in fp32.
+// lower id among equals) by k rounds of a wave-wide selection; the weights are
+// expf(z - max) / sum in fp32.
 #include "q4nx_dev.h"
 
 namespace q4nx {
@@ -25,17 +25,17 @@ __device__ __forceinline__ bool rt_better(float v, int i, float bv, int bi) {
   return bi < 0 || v > bv || (v == bv && i < bi);
 }
 
-// Logits: workgroup (bx, by) takes router rows 8 bx .. 8 bx + 7 (two per
-// wave, held in registers) against tokens 8 by .. 8 by + 7, so the router
-// weights stream through many CUs at once (one workgroup per token would
-// pull them through a single CU).
+// Logits: workgroup (bx, by), one wave, takes router rows 2 bx and 2 bx + 1
+// (held in registers) against tokens 8 by .. 8 by + 7, so the router weights
+// stream through as many CUs as there are row pairs (a CU draws only a few
+// tens of GB/s; one workgroup per token would pull them through one CU).
 template <int DB>
-__global__ __launch_bounds__(256) void k_router_logits(const uint16_t* __restrict__ R,
-                                                       const uint16_t* __restrict__ X, int T, int E,
-                                                       float* __restrict__ logits) {
+__global__ __launch_bounds__(64) void k_router_logits(const uint16_t* __restrict__ R,
+                                                      const uint16_t* __restrict__ X, int T, int E,
+                                                      float* __restrict__ logits) {
   constexpr int D = 512 * DB;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int r0 = 8 * blockIdx.x + 2 * wave;
+  const int lane = threadIdx.x & 63;
+  const int r0 = 2 * blockIdx.x;
   u32x4 ra[DB], rb[DB];
   const int ea = r0 < E ? r0 : E - 1, eb = r0 + 1 < E ? r0 + 1 : E - 1;
 #pragma unroll
@@ -69,83 +69,81 @@ __global__ __launch_bounds__(256) void k_router_logits(const uint16_t* __restric
   }
 }
 
-// Picks and weights: one workgroup per token over its E logits.
-__global__ __launch_bounds__(256) void k_router_topk(const float* __restrict__ logits, int E, int k,
-                                                     int renorm, int32_t* __restrict__ ids,
+// Picks and weights: one wave per token (4 tokens per workgroup).  Lane l
+// holds logits l + 64 i (i < 16, E <= 1024) in registers; the max, the sum of
+// expf(z - max) (each lane's terms in i order, then a fixed xor pattern over
+// the lanes) and each of the k picks (the lane's best untaken candidate, then
+// an xor-butterfly selection under the (value desc, id asc) order, which picks
+// the same expert whatever the pairing) need no LDS and no barrier.
+__global__ __launch_bounds__(256) void k_router_topk(const float* __restrict__ logits, int T, int E,
+                                                     int k, int renorm, int32_t* __restrict__ ids,
                                                      float* __restrict__ p) {
-  __shared__ float lg[kRouterMaxE];
-  __shared__ uint8_t taken[kRouterMaxE];
-  __shared__ float rv[256];
-  __shared__ int ri[256];
-  __shared__ int sel[kRouterMaxK];
-  const int t = blockIdx.x, tid = threadIdx.x;
-  for (int e = tid; e < E; e += 256) {
-    lg[e] = logits[(size_t)t * E + e];
-    taken[e] = 0;
+  constexpr int EL = kRouterMaxE / 64;
+  const int lane = threadIdx.x & 63;
+  const int t = 4 * blockIdx.x + (threadIdx.x >> 6);
+  if (t >= T) return;
+  float v[EL];
+#pragma unroll
+  for (int i = 0; i < EL; ++i) {
+    const int e = lane + 64 * i;
+    v[i] = e < E ? logits[(size_t)t * E + e] : 0.f;
   }
-  __syncthreads();
-
-  // max and sum of expf(z - max), each a fixed-order reduction
   float m = -__builtin_inff();
-  for (int e = tid; e < E; e += 256) m = fmaxf(m, lg[e]);
-  rv[tid] = m;
-  __syncthreads();
-  for (int h = 128; h > 0; h >>= 1) {
-    if (tid < h) rv[tid] = fmaxf(rv[tid], rv[tid + h]);
-    __syncthreads();
-  }
-  const float mx = rv[0];
-  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < EL; ++i)
+    if (lane + 64 * i < E) m = fmaxf(m, v[i]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
   float sacc = 0.f;
-  for (int e = tid; e < E; e += 256) sacc += expf(lg[e] - mx);
-  rv[tid] = sacc;
-  __syncthreads();
-  for (int h = 128; h > 0; h >>= 1) {
-    if (tid < h) rv[tid] += rv[tid + h];
-    __syncthreads();
-  }
-  const float ssum = rv[0];
-  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < EL; ++i)
+    if (lane + 64 * i < E) sacc += expf(v[i] - m);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) sacc += __shfl_xor(sacc, off);
 
-  // top-k: k rounds of a (value desc, index asc) reduction over untaken experts
+  uint32_t taken = 0;   // bit i: expert lane + 64 i already picked
+  int my_id = -1;       // lane j < k: the j-th pick
+  float my_v = 0.f;
   for (int j = 0; j < k; ++j) {
     float bv = 0.f;
     int bi = -1;
-    for (int e = tid; e < E; e += 256)
-      if (!taken[e] && rt_better(lg[e], e, bv, bi)) { bv = lg[e]; bi = e; }
-    rv[tid] = bv;
-    ri[tid] = bi;
-    __syncthreads();
-    for (int h = 128; h > 0; h >>= 1) {
-      if (tid < h && ri[tid + h] >= 0 && rt_better(rv[tid + h], ri[tid + h], rv[tid], ri[tid])) {
-        rv[tid] = rv[tid + h];
-        ri[tid] = ri[tid + h];
+#pragma unroll
+    for (int i = 0; i < EL; ++i) {
+      const int e = lane + 64 * i;
+      if (e < E && !((taken >> i) & 1u) && rt_better(v[i], e, bv, bi)) {
+        bv = v[i];
+        bi = e;
       }
-      __syncthreads();
     }
-    if (tid == 0) {
-      sel[j] = ri[0];
-      taken[ri[0]] = 1;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      const float ov = __shfl_xor(bv, off);
+      const int oi = __shfl_xor(bi, off);
+      if (oi >= 0 && rt_better(ov, oi, bv, bi)) {
+        bv = ov;
+        bi = oi;
+      }
     }
-    __syncthreads();
+    if (bi >= 0 && (bi & 63) == lane) taken |= 1u << (bi >> 6);
+    if (lane == j) {
+      my_id = bi;
+      my_v = bv;
+    }
   }
-  if (tid == 0) {
-    float w[kRouterMaxK];
-    float tot = 0.f;
-    for (int j = 0; j < k; ++j) {
-      w[j] = expf(lg[sel[j]] - mx) / ssum;
-      tot += w[j];
-    }
-    for (int j = 0; j < k; ++j) {
-      ids[(size_t)t * k + j] = sel[j];
-      p[(size_t)t * k + j] = renorm ? w[j] / tot : w[j];
-    }
+  // weights: lane j < k holds pick j; the renormalising total is a fixed-order
+  // sum of the k weights (lanes 0 .. k - 1 in order, via a broadcast loop)
+  const float w = lane < k ? expf(my_v - m) / sacc : 0.f;
+  float tot = 0.f;
+  for (int j = 0; j < k; ++j) tot += __shfl(w, j);
+  if (lane < k) {
+    ids[(size_t)t * k + lane] = my_id;
+    p[(size_t)t * k + lane] = renorm ? w / tot : w;
   }
 }
 
 hipError_t launch_moe_router(const uint16_t* R, const uint16_t* X, int T, int D, int E, int k,
                              int renorm, int32_t* ids, float* p, float* logits, hipStream_t s) {
-  const dim3 g((E + 7) / 8, (T + 7) / 8), b(256);
+  const dim3 g((E + 1) / 2, (T + 7) / 8), b(64);
   switch (D / 512) {
     case 1: hipLaunchKernelGGL((k_router_logits<1>), g, b, 0, s, R, X, T, E, logits); break;
     case 2: hipLaunchKernelGGL((k_router_logits<2>), g, b, 0, s, R, X, T, E, logits); break;
@@ -153,7 +151,7 @@ hipError_t launch_moe_router(const uint16_t* R, const uint16_t* X, int T, int D,
     case 8: hipLaunchKernelGGL((k_router_logits<8>), g, b, 0, s, R, X, T, E, logits); break;
     default: return hipErrorInvalidValue;
   }
-  hipLaunchKernelGGL(k_router_topk, dim3(T), b, 0, s, logits, E, k, renorm, ids, p);
+  hipLaunchKernelGGL(k_router_topk, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k, renorm, ids, p);
   return hipGetLastError();
 }
 
