@@ -21,10 +21,6 @@ namespace q4nx {
 constexpr int kRouterMaxE = 1024;
 constexpr int kRouterMaxK = 16;
 
-__device__ __forceinline__ bool rt_better(float v, int i, float bv, int bi) {
-  return bi < 0 || v > bv || (v == bv && i < bi);
-}
-
 // Logits: workgroup (bx, by), one wave, takes router rows 2 bx and 2 bx + 1
 // (held in registers) against tokens 8 by .. 8 by + 7, so the router weights
 // stream through as many CUs as there are row pairs (a CU draws only a few
@@ -69,72 +65,110 @@ __global__ __launch_bounds__(64) void k_router_logits(const uint16_t* __restrict
   }
 }
 
+// Order-preserving 32-bit key of a logit: larger logits give larger keys;
+// NaN maps below every number, so it is never picked before a number.
+__device__ __forceinline__ uint32_t rt_key(float v) {
+  const uint32_t b = __float_as_uint(v);
+  if (v != v) return 0u;
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// (key, ~id) pairs ordered lexicographically: the larger key first, the lower
+// id among equal keys.  Moves a pair within rows of 16 lanes by DPP.
+__device__ __forceinline__ void rt_max_step(uint32_t& k, uint32_t& i, int ctrl_sel) {
+  uint32_t ok, oi;
+  switch (ctrl_sel) {   // constant after inlining
+    case 0: ok = __builtin_amdgcn_mov_dpp(k, 0xB1, 0xF, 0xF, false); oi = __builtin_amdgcn_mov_dpp(i, 0xB1, 0xF, 0xF, false); break;   // quad_perm [1,0,3,2]
+    case 1: ok = __builtin_amdgcn_mov_dpp(k, 0x4E, 0xF, 0xF, false); oi = __builtin_amdgcn_mov_dpp(i, 0x4E, 0xF, 0xF, false); break;   // quad_perm [2,3,0,1]
+    case 2: ok = __builtin_amdgcn_mov_dpp(k, 0x141, 0xF, 0xF, false); oi = __builtin_amdgcn_mov_dpp(i, 0x141, 0xF, 0xF, false); break; // row_half_mirror
+    default: ok = __builtin_amdgcn_mov_dpp(k, 0x140, 0xF, 0xF, false); oi = __builtin_amdgcn_mov_dpp(i, 0x140, 0xF, 0xF, false); break; // row_mirror
+  }
+  const bool take = ok > k || (ok == k && oi > i);
+  k = take ? ok : k;
+  i = take ? oi : i;
+}
+
 // Picks and weights: one wave per token (4 tokens per workgroup).  Lane l
-// holds logits l + 64 i (i < 16, E <= 1024) in registers; the max, the sum of
-// expf(z - max) (each lane's terms in i order, then a fixed xor pattern over
-// the lanes) and each of the k picks (the lane's best untaken candidate, then
-// an xor-butterfly selection under the (value desc, id asc) order, which picks
-// the same expert whatever the pairing) need no LDS and no barrier.
+// holds logits l + 64 i (i < 16, E <= 1024) in registers.  The max and the
+// sum of expf(z - max) (each lane's terms in i order, then a fixed pattern:
+// pairs, quads, eights and rows of 16 within a row by DPP, then rows 0..3 in
+// order) and each of the k picks (the lane's best untaken candidate, the best
+// of each row by DPP, then of the 4 rows) need no LDS and no barrier; a pick
+// is a maximum under a total order, so it does not depend on the pairing.
 __global__ __launch_bounds__(256) void k_router_topk(const float* __restrict__ logits, int T, int E,
                                                      int k, int renorm, int32_t* __restrict__ ids,
                                                      float* __restrict__ p) {
   constexpr int EL = kRouterMaxE / 64;
   const int lane = threadIdx.x & 63;
-  const int t = 4 * blockIdx.x + (threadIdx.x >> 6);
+  const int t = 4 * blockIdx.x + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
   if (t >= T) return;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(logits + (size_t)t * E, (uint32_t)E * 4);
   float v[EL];
 #pragma unroll
-  for (int i = 0; i < EL; ++i) {
-    const int e = lane + 64 * i;
-    v[i] = e < E ? logits[(size_t)t * E + e] : 0.f;
-  }
+  for (int i = 0; i < EL; ++i)   // past E: zero, and never a candidate
+    v[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (uint32_t)(lane + 64 * i) * 4, 0, 0));
   float m = -__builtin_inff();
 #pragma unroll
-  for (int i = 0; i < EL; ++i)
-    if (lane + 64 * i < E) m = fmaxf(m, v[i]);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  for (int i = 0; i < EL; ++i) m = fmaxf(m, lane + 64 * i < E ? v[i] : -__builtin_inff());
+  m = fmaxf(m, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__float_as_int(m), 0xB1, 0xF, 0xF, false)));
+  m = fmaxf(m, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__float_as_int(m), 0x4E, 0xF, 0xF, false)));
+  m = fmaxf(m, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__float_as_int(m), 0x141, 0xF, 0xF, false)));
+  m = fmaxf(m, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__float_as_int(m), 0x140, 0xF, 0xF, false)));
+  m = fmaxf(fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(m), 0)),
+                  __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(m), 16))),
+            fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(m), 32)),
+                  __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(m), 48))));
   float sacc = 0.f;
 #pragma unroll
-  for (int i = 0; i < EL; ++i)
-    if (lane + 64 * i < E) sacc += expf(v[i] - m);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) sacc += __shfl_xor(sacc, off);
+  for (int i = 0; i < EL; ++i) sacc += expf(lane + 64 * i < E ? v[i] - m : -__builtin_inff());   // exp(-inf) = 0
+  sacc += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__float_as_int(sacc), 0xB1, 0xF, 0xF, false));
+  sacc += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__float_as_int(sacc), 0x4E, 0xF, 0xF, false));
+  sacc += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__float_as_int(sacc), 0x141, 0xF, 0xF, false));
+  sacc += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__float_as_int(sacc), 0x140, 0xF, 0xF, false));
+  const float ssum = ((__builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(sacc), 0)) +
+                       __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(sacc), 16))) +
+                      __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(sacc), 32))) +
+                     __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(sacc), 48));
 
+  uint32_t key[EL];
+#pragma unroll
+  for (int i = 0; i < EL; ++i) key[i] = lane + 64 * i < E ? rt_key(v[i]) : 0u;
   uint32_t taken = 0;   // bit i: expert lane + 64 i already picked
   int my_id = -1;       // lane j < k: the j-th pick
   float my_v = 0.f;
   for (int j = 0; j < k; ++j) {
-    float bv = 0.f;
-    int bi = -1;
+    // the lane's best untaken candidate; (0, 0) when it has none
+    uint32_t bk = 0, bi = 0;
 #pragma unroll
     for (int i = 0; i < EL; ++i) {
-      const int e = lane + 64 * i;
-      if (e < E && !((taken >> i) & 1u) && rt_better(v[i], e, bv, bi)) {
-        bv = v[i];
-        bi = e;
-      }
+      const uint32_t e = (uint32_t)(lane + 64 * i);
+      const uint32_t ni = ~e;
+      const bool ok = e < (uint32_t)E && !((taken >> i) & 1u);
+      const bool take = ok && (key[i] > bk || (key[i] == bk && ni > bi) || bi == 0);
+      bk = take ? key[i] : bk;
+      bi = take ? ni : bi;
     }
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const int oi = __shfl_xor(bi, off);
-      if (oi >= 0 && rt_better(ov, oi, bv, bi)) {
-        bv = ov;
-        bi = oi;
+    for (int c = 0; c < 4; ++c) rt_max_step(bk, bi, c);
+    // rows 0..3: the best of the four row leaders (uniform)
+    uint32_t wk = __builtin_amdgcn_readlane(bk, 0), wi = __builtin_amdgcn_readlane(bi, 0);
+#pragma unroll
+    for (int r = 1; r < 4; ++r) {
+      const uint32_t rk = __builtin_amdgcn_readlane(bk, 16 * r), ri = __builtin_amdgcn_readlane(bi, 16 * r);
+      if (rk > wk || (rk == wk && ri > wi)) {
+        wk = rk;
+        wi = ri;
       }
     }
-    if (bi >= 0 && (bi & 63) == lane) taken |= 1u << (bi >> 6);
-    if (lane == j) {
-      my_id = bi;
-      my_v = bv;
-    }
+    const int pick = (int)~wi;
+    if ((pick & 63) == lane) taken |= 1u << (pick >> 6);
+    if (lane == j) my_id = pick;
   }
-  // weights: lane j < k holds pick j; the renormalising total is a fixed-order
-  // sum of the k weights (lanes 0 .. k - 1 in order, via a broadcast loop)
-  const float w = lane < k ? expf(my_v - m) / sacc : 0.f;
+  // the picked logits and weights: lane j < k holds pick j
+  if (lane < k) my_v = logits[(size_t)t * E + my_id];
+  const float w = lane < k ? expf(my_v - m) / ssum : 0.f;
   float tot = 0.f;
-  for (int j = 0; j < k; ++j) tot += __shfl(w, j);
+  for (int j = 0; j < k; ++j) tot += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(w), j));
   if (lane < k) {
     ids[(size_t)t * k + lane] = my_id;
     p[(size_t)t * k + lane] = renorm ? w / tot : w;
