@@ -625,6 +625,15 @@ int q4nx_moe_experts(const q4nx_moe_layer* L, const uint16_t* X, const int32_t* 
                 q4nx::kMoeMaxPairs);
   if (!aligned(X, 16) || !aligned(ids, 4) || !aligned(p, 4) || !aligned(Y, 4))
     return fail(Q4NX_E_ALIGN, "moe: X must be 16-byte, ids/p/Y 4-byte aligned");
+  {
+    // a batch's prepared activation rows (72 bytes per row, tile column and
+    // group) are staged in at most 64 KB of LDS
+    const int tb = T == 1 ? 1 : 4;
+    const int widest = std::max(L->d_model, std::max(L->d_expert, L->d_shared));
+    if ((int64_t)tb * 8 * 72 * (widest / 256) > 65536)
+      return fail(Q4NX_E_SHAPE, "moe: d_model, d_expert and d_shared must be at most %d for T = %d",
+                  65536 / (tb * 8 * 72) * 256, T);
+  }
   const q4nx::MoeWsLayout lay = q4nx::moe_ws_layout(T * k, T, L->d_model, moe_hstride(L));
   if (!ws || ws_bytes < lay.total)
     return fail(Q4NX_E_WORKSPACE, "moe: workspace of %zu bytes, %zu needed", ws_bytes, lay.total);

@@ -170,120 +170,6 @@ __device__ __forceinline__ bool moe_item(const MoeArgs& a, int item, int rows_r,
 }
 
 // ---------------------------------------------------------------------------
-// gate / up / SwiGLU
-// ---------------------------------------------------------------------------
-// Waves 0-1 run the gate tile row, waves 2-3 the up tile row, each pair
-// splitting the D/256 chunks in two halves.
-template <int KIND, int TB>
-__global__ __launch_bounds__(256) void k_moe_gateup(MoeArgs a) {
-  constexpr int CB = ChunkBytes<KIND>::value;
-  __shared__ float red[4][32][TB];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int TC = a.D / 256;
-  const int rows_r = a.De / 32, rows_s = a.Ds / 32;
-  const int P = a.T * a.k;
-  for (int item = blockIdx.x;; item += gridDim.x) {
-    MoeItem it;
-    if (!moe_item<TB>(a, item, rows_r, rows_s, 1, 1, false, it)) break;
-    const uint16_t* xrow[TB];
-#pragma unroll
-    for (int m = 0; m < TB; ++m) {
-      const int mm = m < it.ntok ? m : 0;
-      const int t = it.shared ? it.pos0 - P + mm : a.sorted[it.pos0 + mm] / a.k;
-      xrow[m] = a.X + (size_t)t * a.D;
-    }
-    const uint8_t* w = (wave < 2 ? it.w0 : it.w1) + (size_t)it.tr * TC * CB;
-    const int half = wave & 1;
-    float acc[4][TB];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int m = 0; m < TB; ++m) acc[i][m] = 0.f;
-    q4_row_partial<KIND, TB>(w, half * TC / 2, (half + 1) * TC / 2, xrow, lane, acc);
-    q4_lane_reduce<TB>(acc);
-    if ((lane & 7) == 0) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int m = 0; m < TB; ++m) red[wave][8 * i + (lane >> 3)][m] = acc[i][m];
-    }
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < 32 * TB; idx += 256) {
-      const int r = idx / TB, m = idx - r * TB;
-      if (m < it.ntok) {
-        const float g = red[0][r][m] + red[1][r][m];
-        const float u = red[2][r][m] + red[3][r][m];
-        const float hv = g / (1.0f + expf(-g)) * u;
-        const uint16_t hb = __builtin_bit_cast(uint16_t, (__bf16)hv);
-        const int col = 32 * it.tr + r;
-        a.hbuf[(size_t)(it.pos0 + m) * a.hstride + col] = hb;
-        if (it.shared) {
-          if (a.dbg_h_shared) a.dbg_h_shared[(size_t)(it.pos0 - P + m) * a.Ds + col] = hb;
-        } else if (a.dbg_h) {
-          a.dbg_h[(size_t)a.sorted[it.pos0 + m] * a.De + col] = hb;
-        }
-      }
-    }
-    __syncthreads();
-  }
-}
-
-// ---------------------------------------------------------------------------
-// down
-// ---------------------------------------------------------------------------
-// ks waves split one tile row's chunks; 4/ks tile rows per workgroup.
-template <int KIND, int TB>
-__global__ __launch_bounds__(256) void k_moe_down(MoeArgs a, int ks_r, int ks_s) {
-  constexpr int CB = ChunkBytes<KIND>::value;
-  __shared__ float red[4][32][TB];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int rows = a.D / 32;
-  const int P = a.T * a.k;
-  for (int item = blockIdx.x;; item += gridDim.x) {
-    MoeItem it;
-    if (!moe_item<TB>(a, item, rows, rows, 4 / ks_r, 4 / ks_s, true, it)) break;
-    const int ks = it.shared ? ks_s : ks_r, rpw = 4 / ks;
-    const int TC = (it.shared ? a.Ds : a.De) / 256;
-    const int slot = wave / ks, part = wave % ks;
-    const int tr = it.tr + slot;
-    const uint16_t* xrow[TB];
-#pragma unroll
-    for (int m = 0; m < TB; ++m) {
-      const int mm = m < it.ntok ? m : 0;
-      xrow[m] = a.hbuf + (size_t)(it.pos0 + mm) * a.hstride;
-    }
-    float acc[4][TB];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int m = 0; m < TB; ++m) acc[i][m] = 0.f;
-    if (tr < rows)
-      q4_row_partial<KIND, TB>(it.w0 + (size_t)tr * TC * CB, part * TC / ks, (part + 1) * TC / ks,
-                               xrow, lane, acc);
-    q4_lane_reduce<TB>(acc);
-    if ((lane & 7) == 0) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int m = 0; m < TB; ++m) red[wave][8 * i + (lane >> 3)][m] = acc[i][m];
-    }
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < rpw * 32 * TB; idx += 256) {
-      const int s = idx / (32 * TB), rem = idx - s * 32 * TB;
-      const int r = rem / TB, m = rem - r * TB;
-      const int t_row = it.tr + s;
-      if (m < it.ntok && t_row < rows) {
-        float v = 0.f;
-        for (int p = 0; p < ks; ++p) v += red[s * ks + p][r][m];
-        const int dst = it.shared ? it.pos0 + m : a.sorted[it.pos0 + m];
-        a.dbuf[(size_t)dst * a.D + 32 * t_row + r] = v;
-      }
-    }
-    __syncthreads();
-  }
-}
-
-// ---------------------------------------------------------------------------
 // weight-stationary gate/up and down
 // ---------------------------------------------------------------------------
 // One work item is one tile row of one selected expert (or of the shared
@@ -604,6 +490,146 @@ __global__ __launch_bounds__(256) void k_moe_down_s(MoeArgs a, int ks_r, int ks_
 }
 
 // ---------------------------------------------------------------------------
+// prompt blocks: one work item per (token batch, tile row or row group)
+// ---------------------------------------------------------------------------
+// Many pairs (after the route kernel): an item is one batch of up to TB tokens
+// of one segment against one tile row (gate/up) or row group (down), so a
+// popular expert's batches spread over many CUs.  Each item issues its weight
+// loads first, then prepares its batch's activation rows in LDS as the
+// weight-stationary kernels do, and runs the same arithmetic (chunk split,
+// chunk order, reduction order), so a token's bits do not depend on its batch.
+
+// Waves 0-1 run the gate tile row, waves 2-3 the up tile row, each pair
+// splitting the D/256 chunks in two halves.
+template <int KIND, int TB>
+__global__ __launch_bounds__(256) void k_moe_gateup(MoeArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint32_t xl[];
+  __shared__ float red[4][32][TB];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int TC = a.D / 256;
+  const int rows_r = a.De / 32, rows_s = a.Ds / 32;
+  const int P = a.T * a.k;
+  const int half = wave & 1;
+  const int c0 = half * TC / 2, nc = (half + 1) * TC / 2 - c0;
+  constexpr int CPW = kMoeCpwGateUp;
+  uint32_t kMask = 0x000F000Fu, kMagic = 0x43004300u;
+  asm volatile("" : "+s"(kMask));
+  asm volatile("" : "+v"(kMagic));
+  for (int item = blockIdx.x;; item += gridDim.x) {
+    MoeItem it;
+    if (!moe_item<TB>(a, item, rows_r, rows_s, 1, 1, false, it)) break;
+    const uint8_t* row = (wave < 2 ? it.w0 : it.w1) + (size_t)it.tr * TC * ChunkBytes<KIND>::value;
+    Q4Chunk<KIND> ch[CPW];
+    if (nc <= CPW) moe_load<KIND, CPW>(row, c0, nc, lane, ch);   // weights first
+    const uint16_t* src[TB];
+#pragma unroll
+    for (int m = 0; m < TB; ++m) {
+      const int mm = m < it.ntok ? m : 0;
+      const int t = it.shared ? it.pos0 - P + mm : a.sorted[it.pos0 + mm] / a.k;
+      src[m] = a.X + (size_t)t * a.D;
+    }
+    float acc[4][TB];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int m = 0; m < TB; ++m) acc[i][m] = 0.f;
+    moe_stage<TB>(src, TC, xl);
+    __syncthreads();
+    for (int r0 = 0; r0 < nc; r0 += CPW) {
+      if (nc > CPW) moe_load<KIND, CPW>(row, c0 + r0, min(CPW, nc - r0), lane, ch);
+      moe_chunks<KIND, TB, CPW>(ch, min(CPW, nc - r0), c0 + r0, TC, xl, kMask, kMagic, acc);
+    }
+    q4_lane_reduce<TB>(acc);
+    if ((lane & 7) == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int m = 0; m < TB; ++m) red[wave][8 * i + (lane >> 3)][m] = acc[i][m];
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < 32 * TB; idx += 256) {
+      const int r = idx / TB, m = idx - r * TB;
+      if (m < it.ntok) {
+        const float g = red[0][r][m] + red[1][r][m];
+        const float u = red[2][r][m] + red[3][r][m];
+        const float hv = g / (1.0f + expf(-g)) * u;
+        const uint16_t hb = __builtin_bit_cast(uint16_t, (__bf16)hv);
+        const int col = 32 * it.tr + r;
+        a.hbuf[(size_t)(it.pos0 + m) * a.hstride + col] = hb;
+        if (it.shared) {
+          if (a.dbg_h_shared) a.dbg_h_shared[(size_t)(it.pos0 - P + m) * a.Ds + col] = hb;
+        } else if (a.dbg_h) {
+          a.dbg_h[(size_t)a.sorted[it.pos0 + m] * a.De + col] = hb;
+        }
+      }
+    }
+    __syncthreads();   // red and xl are reused by the next item
+  }
+}
+
+// ks waves split one tile row's chunks; 4/ks tile rows per workgroup.
+template <int KIND, int TB>
+__global__ __launch_bounds__(256) void k_moe_down(MoeArgs a, int ks_r, int ks_s) {
+  extern __shared__ __attribute__((aligned(16))) uint32_t xl[];
+  __shared__ float red[4][32][TB];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int rows = a.D / 32;
+  constexpr int CPW = kMoeCpwDown;
+  uint32_t kMask = 0x000F000Fu, kMagic = 0x43004300u;
+  asm volatile("" : "+s"(kMask));
+  asm volatile("" : "+v"(kMagic));
+  for (int item = blockIdx.x;; item += gridDim.x) {
+    MoeItem it;
+    if (!moe_item<TB>(a, item, rows, rows, 4 / ks_r, 4 / ks_s, true, it)) break;
+    const int ks = it.shared ? ks_s : ks_r, rpw = 4 / ks;
+    const int TC = (it.shared ? a.Ds : a.De) / 256;
+    const int slot = wave / ks, part = wave % ks;
+    const int tr = it.tr + slot < rows ? it.tr + slot : rows - 1;   // past the last row: redone, unstored
+    const int c0 = part * TC / ks, nc = (part + 1) * TC / ks - c0;
+    const uint8_t* row = it.w0 + (size_t)tr * TC * ChunkBytes<KIND>::value;
+    Q4Chunk<KIND> ch[CPW];
+    if (nc <= CPW) moe_load<KIND, CPW>(row, c0, nc, lane, ch);   // weights first
+    const uint16_t* src[TB];
+#pragma unroll
+    for (int m = 0; m < TB; ++m) {
+      const int mm = m < it.ntok ? m : 0;
+      src[m] = a.hbuf + (size_t)(it.pos0 + mm) * a.hstride;
+    }
+    float acc[4][TB];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int m = 0; m < TB; ++m) acc[i][m] = 0.f;
+    moe_stage<TB>(src, TC, xl);
+    __syncthreads();
+    for (int r0 = 0; r0 < nc; r0 += CPW) {
+      if (nc > CPW) moe_load<KIND, CPW>(row, c0 + r0, min(CPW, nc - r0), lane, ch);
+      moe_chunks<KIND, TB, CPW>(ch, min(CPW, nc - r0), c0 + r0, TC, xl, kMask, kMagic, acc);
+    }
+    q4_lane_reduce<TB>(acc);
+    if ((lane & 7) == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int m = 0; m < TB; ++m) red[wave][8 * i + (lane >> 3)][m] = acc[i][m];
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < rpw * 32 * TB; idx += 256) {
+      const int s2 = idx / (32 * TB), rem = idx - s2 * 32 * TB;
+      const int r = rem / TB, m = rem - r * TB;
+      const int t_row = it.tr + s2;
+      if (m < it.ntok && t_row < rows) {
+        float v = 0.f;
+        for (int p2 = 0; p2 < ks; ++p2) v += red[s2 * ks + p2][r][m];
+        const int dst = it.shared ? it.pos0 + m : a.sorted[it.pos0 + m];
+        a.dbuf[(size_t)dst * a.D + 32 * t_row + r] = v;
+      }
+    }
+    __syncthreads();   // red and xl are reused by the next item
+  }
+}
+
+// ---------------------------------------------------------------------------
 // combine
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_moe_combine(MoeArgs a) {
@@ -662,10 +688,10 @@ static hipError_t moe_run(const MoeArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(k_moe_route, dim3(1), dim3(1024), 0, s, a);
   const int gu_items = nb_r * (a.De / 32) + nb_s * (a.Ds / 32);
   hipLaunchKernelGGL((k_moe_gateup<KIND, TB>), dim3(gu_items < 4096 ? gu_items : 4096), dim3(256),
-                     0, s, a);
+                     xl_gu, s, a);
   const int dn_items = nb_r * (rows / (4 / ks_r)) + nb_s * (rows / (4 / ks_s));
   hipLaunchKernelGGL((k_moe_down<KIND, TB>), dim3(dn_items < 4096 ? dn_items : 4096), dim3(256),
-                     0, s, a, ks_r, ks_s);
+                     xl_dn, s, a, ks_r, ks_s);
   hipLaunchKernelGGL(k_moe_combine, dim3((a.D + 255) / 256, a.T), dim3(256), 0, s, a);
   return hipGetLastError();
 }

@@ -269,7 +269,9 @@ size_t q4nx_moe_ws(const q4nx_moe_layer* L, int T, int k);
  * expert, in fp32, with no atomics.
  *   X    DEVICE bf16 [T][D]; ids DEVICE int32 [T][k]; p DEVICE fp32 [T][k]
  *   Y    DEVICE fp32 [T][D], fully overwritten
- *   T    1..4096, k 1..16, T*k <= 4096
+ *   T    1..4096, k 1..16, T*k <= 4096; for T > 1, d_model, d_expert and
+ *        d_shared at most 7168 (a batch of 4 tokens' prepared activations is
+ *        staged in 64 KB of LDS), else E_SHAPE
  *   dbg  NULL, or stage outputs to fill (any member may be NULL)
  *   ws   DEVICE workspace of at least q4nx_moe_ws(L, T, k) bytes, 256-byte aligned
  * An id outside [0, n_experts) is never dereferenced: its slot contributes 0
