@@ -675,6 +675,7 @@ int q4nx_moe_experts(const q4nx_moe_layer* L, const uint16_t* X, const int32_t* 
   a.sorted = reinterpret_cast<int32_t*>(w + lay.sorted);
   a.seg = reinterpret_cast<int32_t*>(w + lay.seg);
   a.batch0 = reinterpret_cast<int32_t*>(w + lay.batch0);
+  a.btab = reinterpret_cast<int32_t*>(w + lay.btab);
   a.hbuf = reinterpret_cast<uint16_t*>(w + lay.hbuf);
   a.dbuf = reinterpret_cast<float*>(w + lay.dbuf);
   const hipError_t e = q4nx::launch_moe(L->chunk_bytes == Q4NX_Q4_1_BYTES ? q4nx::KIND_Q4_1

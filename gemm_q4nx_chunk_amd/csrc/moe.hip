@@ -95,6 +95,20 @@ __global__ __launch_bounds__(1024) void k_moe_route(MoeArgs a) {
       a.seg[3 * u + 1] = s;
       a.seg[3 * u + 2] = cnt;
       a.batch0[u] = bstart;
+      // the segment's batch records, so a work item finds its batch in one load
+      for (int bi = 0; bi < nb; ++bi) {
+        int32_t* r = a.btab + (size_t)(bstart + bi) * kMoeBatchInts;
+        const int pos0 = s + bi * a.tb, ntok = min(a.tb, cnt - bi * a.tb);
+        r[0] = e;
+        r[1] = pos0;
+        r[2] = ntok;
+        r[3] = 0;
+        for (int m = 0; m < 4; ++m) {
+          const int pair = (int)(key[pos0 + (m < ntok ? m : 0)] & 0xFFFu);
+          r[4 + m] = pair / a.k;
+          r[8 + m] = pair;
+        }
+      }
     }
     base_seg += scan[1023] >> 20;
     base_batch += scan[1023] & 0xFFFFF;
@@ -108,16 +122,6 @@ __global__ __launch_bounds__(1024) void k_moe_route(MoeArgs a) {
   }
 }
 
-// Segment of routed batch b: the last u with batch0[u] <= b.
-__device__ __forceinline__ int find_seg(const int32_t* batch0, int nseg, int b) {
-  int lo = 0, hi = nseg - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (batch0[mid] <= b) lo = mid; else hi = mid - 1;
-  }
-  return lo;
-}
-
 // Work item of a (batch, tile-row group) launch: which expert, which tokens.
 struct MoeItem {
   const uint8_t* w0;    // gate (gateup) or down (down) chunks of the expert
@@ -126,25 +130,37 @@ struct MoeItem {
   int ntok;             // tokens in this batch (1..TB)
   int pos0;             // first sorted position (routed) or P + first token (shared)
   bool shared;
+  const int32_t* rec;   // routed: the batch's record (tokens at [4], pairs at [8])
 };
+
+// Token of row m < TB of an item (past ntok: the first again), and its pair
+// index (routed) or P + token (shared).
+__device__ __forceinline__ int moe_item_tok(const MoeArgs& a, const MoeItem& it, int m) {
+  if (!it.shared) return it.rec[4 + m];
+  return it.pos0 - a.T * a.k + (m < it.ntok ? m : 0);
+}
+__device__ __forceinline__ int moe_item_pair(const MoeArgs& a, const MoeItem& it, int m) {
+  if (!it.shared) return it.rec[8 + m];
+  return it.pos0 + (m < it.ntok ? m : 0);
+}
 
 // Items are numbered routed first (every routed batch times its tile-row
 // groups), then shared.  rpw = tile rows per workgroup for each kind of item.
 template <int TB>
-__device__ __forceinline__ bool moe_item(const MoeArgs& a, int item, int rows_r, int rows_s,
+__device__ __forceinline__ bool moe_item(const MoeArgs& a, int nbr, int item, int rows_r, int rows_s,
                                          int rpw_r, int rpw_s, bool down, MoeItem& it) {
-  const int nseg = (int)a.hdr[1], nbr = (int)a.hdr[2];
+  static_assert(TB <= 4, "batch records hold 4 tokens");
   const int P = a.T * a.k;
   const int gr = rows_r / rpw_r, gs = rows_s / rpw_s;
   if (item < nbr * gr) {
     const int b = item / gr;
-    const int u = find_seg(a.batch0, nseg, b);
-    const int e = a.seg[3 * u + 0], start = a.seg[3 * u + 1], cnt = a.seg[3 * u + 2];
-    const int bi = b - a.batch0[u];
+    const int32_t* r = a.btab + (size_t)b * kMoeBatchInts;
+    const int e = r[0];
     it.tr = (item - b * gr) * rpw_r;
-    it.pos0 = start + bi * TB;
-    it.ntok = min(TB, cnt - bi * TB);
+    it.pos0 = r[1];
+    it.ntok = r[2];
     it.shared = false;
+    it.rec = r;
     if (down) {
       it.w0 = a.down + (size_t)e * a.down_stride;
       it.w1 = nullptr;
@@ -162,6 +178,7 @@ __device__ __forceinline__ bool moe_item(const MoeArgs& a, int item, int rows_r,
     it.pos0 = P + b * TB;
     it.ntok = min(TB, a.T - b * TB);
     it.shared = true;
+    it.rec = nullptr;
     it.w0 = down ? a.sdown : a.sgate;
     it.w1 = down ? nullptr : a.sup;
     return true;
@@ -189,6 +206,12 @@ constexpr int kMoeSmallPairs = 64;
 // (4 chunks at d_model 2048), down waves one or two chunks.
 constexpr int kMoeCpwGateUp = 4;
 constexpr int kMoeCpwDown = 2;
+// Chunks a wave of the prompt-block gate/up kernel holds at once (fewer
+// registers, so more of its workgroups fit on a CU).
+#ifndef Q4NX_MOE_CPW_BATCH
+#define Q4NX_MOE_CPW_BATCH 2
+#endif
+constexpr int kMoeCpwBatch = Q4NX_MOE_CPW_BATCH;
 
 struct MoeSmallRoute {
   int32_t sorted[kMoeSmallPairs];   // pair index at each sorted position
@@ -237,19 +260,19 @@ __device__ __forceinline__ void moe_route_small(const MoeArgs& a, MoeSmallRoute&
   __syncthreads();
 }
 
-// Prepared activation records of TB rows (row m at src[m]) over TC tile
-// columns, record (m * TC + c) * 8 + g at xl[16 r] and its (d136, sum) at
-// xl[16 R + 2 r]; all threads of the workgroup take part.
+// Prepared activation records of TB rows (row m at base + rows[m], rows in
+// LDS) over TC tile columns, record (m * TC + c) * 8 + g at xl[16 r] and its
+// (d136, sum) at xl[16 R + 2 r]; all threads of the workgroup take part.  (A
+// thread's row comes from LDS: picking it from a register array by a lane-
+// varying index would put the array in private memory, whose loads wait for
+// every weight load in flight.)
 template <int TB>
-__device__ __forceinline__ void moe_stage(const uint16_t* const (&src)[TB], int TC, uint32_t* xl) {
+__device__ __forceinline__ void moe_stage(const uint16_t* base, const int64_t* rows, int TC, uint32_t* xl) {
   const int R = TB * TC * 8;
   float* sums = reinterpret_cast<float*>(xl + 16 * R);
   for (int r = threadIdx.x; r < R; r += 256) {
     const int m = r / (TC * 8), rem = r - m * TC * 8;
-    const uint16_t* p = src[0];
-#pragma unroll
-    for (int i = 1; i < TB; ++i)
-      if (m == i) p = src[i];
+    const uint16_t* p = base + rows[m];
     XRaw<1> raw;
 #pragma unroll
     for (int d = 0; d < 4; ++d) raw.v[0][d] = load16(p + 32 * rem + 8 * d);
@@ -326,6 +349,7 @@ template <int KIND, int TB, bool SMALL>
 __global__ __launch_bounds__(256) void k_moe_gateup_s(MoeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint32_t xl[];
   __shared__ float red[4][32][TB];
+  __shared__ int64_t s_rows[TB];   // the batch's activation rows (element offsets)
   __shared__ MoeSmallRoute rt;
   if constexpr (SMALL) {
     moe_route_small(a, rt);
@@ -358,12 +382,10 @@ __global__ __launch_bounds__(256) void k_moe_gateup_s(MoeArgs a) {
     Q4Chunk<KIND> ch[CPW];
     for (int b0 = 0; b0 < cnt; b0 += TB) {
       const int ntok = min(TB, cnt - b0);
-      const uint16_t* src[TB];
-#pragma unroll
-      for (int m = 0; m < TB; ++m) {
-        const int mm = m < ntok ? m : 0;
+      if (threadIdx.x < TB) {
+        const int mm = (int)threadIdx.x < ntok ? (int)threadIdx.x : 0;
         const int t = shared ? b0 + mm : moe_sorted<SMALL>(a, rt, start + b0 + mm) / a.k;
-        src[m] = a.X + (size_t)t * a.D;
+        s_rows[threadIdx.x] = (int64_t)t * a.D;
       }
       float acc[4][TB];
 #pragma unroll
@@ -372,7 +394,8 @@ __global__ __launch_bounds__(256) void k_moe_gateup_s(MoeArgs a) {
         for (int m = 0; m < TB; ++m) acc[i][m] = 0.f;
       // weights first (held across batches when the wave's run fits), then this batch's rows
       if (b0 == 0 && nc <= CPW) moe_load<KIND, CPW>(row, c0, nc, lane, ch);
-      moe_stage<TB>(src, TC, xl);
+      __syncthreads();
+      moe_stage<TB>(a.X, s_rows, TC, xl);
       __syncthreads();
       for (int r0 = 0; r0 < nc; r0 += CPW) {
         if (nc > CPW) moe_load<KIND, CPW>(row, c0 + r0, min(CPW, nc - r0), lane, ch);
@@ -414,6 +437,7 @@ template <int KIND, int TB, bool SMALL>
 __global__ __launch_bounds__(256) void k_moe_down_s(MoeArgs a, int ks_r, int ks_s) {
   extern __shared__ __attribute__((aligned(16))) uint32_t xl[];
   __shared__ float red[4][32][TB];
+  __shared__ int64_t s_rows[TB];   // the batch's activation rows (element offsets)
   __shared__ MoeSmallRoute rt;
   if constexpr (SMALL) moe_route_small(a, rt);
   const int nseg = SMALL ? rt.nseg : (int)a.hdr[1];
@@ -445,12 +469,10 @@ __global__ __launch_bounds__(256) void k_moe_down_s(MoeArgs a, int ks_r, int ks_
     Q4Chunk<KIND> ch[CPW];
     for (int b0 = 0; b0 < cnt; b0 += TB) {
       const int ntok = min(TB, cnt - b0);
-      const uint16_t* src[TB];
-#pragma unroll
-      for (int m = 0; m < TB; ++m) {
-        const int mm = m < ntok ? m : 0;
+      if (threadIdx.x < TB) {
+        const int mm = (int)threadIdx.x < ntok ? (int)threadIdx.x : 0;
         const int pos = shared ? P + b0 + mm : start + b0 + mm;
-        src[m] = a.hbuf + (size_t)pos * a.hstride;
+        s_rows[threadIdx.x] = (int64_t)pos * a.hstride;
       }
       float acc[4][TB];
 #pragma unroll
@@ -459,7 +481,8 @@ __global__ __launch_bounds__(256) void k_moe_down_s(MoeArgs a, int ks_r, int ks_
         for (int m = 0; m < TB; ++m) acc[i][m] = 0.f;
       // weights first (held across batches when the wave's run fits), then this batch's rows
       if (b0 == 0 && nc <= CPW) moe_load<KIND, CPW>(row, c0, nc, lane, ch);
-      moe_stage<TB>(src, TC, xl);
+      __syncthreads();
+      moe_stage<TB>(a.hbuf, s_rows, TC, xl);
       __syncthreads();
       for (int r0 = 0; r0 < nc; r0 += CPW) {
         if (nc > CPW) moe_load<KIND, CPW>(row, c0 + r0, min(CPW, nc - r0), lane, ch);
@@ -505,35 +528,32 @@ template <int KIND, int TB>
 __global__ __launch_bounds__(256) void k_moe_gateup(MoeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint32_t xl[];
   __shared__ float red[4][32][TB];
+  __shared__ int64_t s_rows[TB];   // the batch's activation rows (element offsets)
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int TC = a.D / 256;
   const int rows_r = a.De / 32, rows_s = a.Ds / 32;
   const int P = a.T * a.k;
   const int half = wave & 1;
   const int c0 = half * TC / 2, nc = (half + 1) * TC / 2 - c0;
-  constexpr int CPW = kMoeCpwGateUp;
+  constexpr int CPW = kMoeCpwBatch;
   uint32_t kMask = 0x000F000Fu, kMagic = 0x43004300u;
   asm volatile("" : "+s"(kMask));
   asm volatile("" : "+v"(kMagic));
+  const int nbr = (int)a.hdr[2];
   for (int item = blockIdx.x;; item += gridDim.x) {
     MoeItem it;
-    if (!moe_item<TB>(a, item, rows_r, rows_s, 1, 1, false, it)) break;
+    if (!moe_item<TB>(a, nbr, item, rows_r, rows_s, 1, 1, false, it)) break;
     const uint8_t* row = (wave < 2 ? it.w0 : it.w1) + (size_t)it.tr * TC * ChunkBytes<KIND>::value;
     Q4Chunk<KIND> ch[CPW];
     if (nc <= CPW) moe_load<KIND, CPW>(row, c0, nc, lane, ch);   // weights first
-    const uint16_t* src[TB];
-#pragma unroll
-    for (int m = 0; m < TB; ++m) {
-      const int mm = m < it.ntok ? m : 0;
-      const int t = it.shared ? it.pos0 - P + mm : a.sorted[it.pos0 + mm] / a.k;
-      src[m] = a.X + (size_t)t * a.D;
-    }
+    if (threadIdx.x < TB) s_rows[threadIdx.x] = (int64_t)moe_item_tok(a, it, threadIdx.x) * a.D;
     float acc[4][TB];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int m = 0; m < TB; ++m) acc[i][m] = 0.f;
-    moe_stage<TB>(src, TC, xl);
+    __syncthreads();
+    moe_stage<TB>(a.X, s_rows, TC, xl);
     __syncthreads();
     for (int r0 = 0; r0 < nc; r0 += CPW) {
       if (nc > CPW) moe_load<KIND, CPW>(row, c0 + r0, min(CPW, nc - r0), lane, ch);
@@ -559,7 +579,7 @@ __global__ __launch_bounds__(256) void k_moe_gateup(MoeArgs a) {
         if (it.shared) {
           if (a.dbg_h_shared) a.dbg_h_shared[(size_t)(it.pos0 - P + m) * a.Ds + col] = hb;
         } else if (a.dbg_h) {
-          a.dbg_h[(size_t)a.sorted[it.pos0 + m] * a.De + col] = hb;
+          a.dbg_h[(size_t)moe_item_pair(a, it, m) * a.De + col] = hb;
         }
       }
     }
@@ -572,15 +592,17 @@ template <int KIND, int TB>
 __global__ __launch_bounds__(256) void k_moe_down(MoeArgs a, int ks_r, int ks_s) {
   extern __shared__ __attribute__((aligned(16))) uint32_t xl[];
   __shared__ float red[4][32][TB];
+  __shared__ int64_t s_rows[TB];   // the batch's activation rows (element offsets)
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int rows = a.D / 32;
   constexpr int CPW = kMoeCpwDown;
   uint32_t kMask = 0x000F000Fu, kMagic = 0x43004300u;
   asm volatile("" : "+s"(kMask));
   asm volatile("" : "+v"(kMagic));
+  const int nbr = (int)a.hdr[2];
   for (int item = blockIdx.x;; item += gridDim.x) {
     MoeItem it;
-    if (!moe_item<TB>(a, item, rows, rows, 4 / ks_r, 4 / ks_s, true, it)) break;
+    if (!moe_item<TB>(a, nbr, item, rows, rows, 4 / ks_r, 4 / ks_s, true, it)) break;
     const int ks = it.shared ? ks_s : ks_r, rpw = 4 / ks;
     const int TC = (it.shared ? a.Ds : a.De) / 256;
     const int slot = wave / ks, part = wave % ks;
@@ -589,18 +611,17 @@ __global__ __launch_bounds__(256) void k_moe_down(MoeArgs a, int ks_r, int ks_s)
     const uint8_t* row = it.w0 + (size_t)tr * TC * ChunkBytes<KIND>::value;
     Q4Chunk<KIND> ch[CPW];
     if (nc <= CPW) moe_load<KIND, CPW>(row, c0, nc, lane, ch);   // weights first
-    const uint16_t* src[TB];
-#pragma unroll
-    for (int m = 0; m < TB; ++m) {
-      const int mm = m < it.ntok ? m : 0;
-      src[m] = a.hbuf + (size_t)(it.pos0 + mm) * a.hstride;
+    if (threadIdx.x < TB) {
+      const int mm = (int)threadIdx.x < it.ntok ? (int)threadIdx.x : 0;
+      s_rows[threadIdx.x] = (int64_t)(it.pos0 + mm) * a.hstride;
     }
     float acc[4][TB];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int m = 0; m < TB; ++m) acc[i][m] = 0.f;
-    moe_stage<TB>(src, TC, xl);
+    __syncthreads();
+    moe_stage<TB>(a.hbuf, s_rows, TC, xl);
     __syncthreads();
     for (int r0 = 0; r0 < nc; r0 += CPW) {
       if (nc > CPW) moe_load<KIND, CPW>(row, c0 + r0, min(CPW, nc - r0), lane, ch);
@@ -621,8 +642,7 @@ __global__ __launch_bounds__(256) void k_moe_down(MoeArgs a, int ks_r, int ks_s)
       if (m < it.ntok && t_row < rows) {
         float v = 0.f;
         for (int p2 = 0; p2 < ks; ++p2) v += red[s2 * ks + p2][r][m];
-        const int dst = it.shared ? it.pos0 + m : a.sorted[it.pos0 + m];
-        a.dbuf[(size_t)dst * a.D + 32 * t_row + r] = v;
+        a.dbuf[(size_t)moe_item_pair(a, it, m) * a.D + 32 * t_row + r] = v;
       }
     }
     __syncthreads();   // red and xl are reused by the next item

@@ -7,6 +7,7 @@
 namespace q4nx {
 
 constexpr int kMoeMaxPairs = 4096;   // T * k per call (the route kernel sorts them in LDS)
+constexpr int kMoeBatchInts = 12;    // ints per routed-batch record (batches of at most 4 tokens)
 
 struct MoeArgs {
   // routed experts: expert e's chunks at base + e * stride
@@ -37,6 +38,8 @@ struct MoeArgs {
   int32_t* sorted;   // [P] pair index at each sorted position
   int32_t* seg;      // [P][3] (expert, first sorted position, count)
   int32_t* batch0;   // [P + 1] first routed batch of each segment
+  int32_t* btab;     // [P][kMoeBatchInts] per routed batch: expert, first sorted position,
+                     // tokens, -, then its tokens' ids and pair indices (4 each)
   uint16_t* hbuf;    // [P + T][hstride] bf16 h (routed by sorted position, shared at P + t)
   float* dbuf;       // [P + T][D] fp32 d (routed by pair index, shared at P + t)
 };
@@ -44,7 +47,7 @@ struct MoeArgs {
 // Workspace layout for P pairs and T tokens; returns the total bytes and fills
 // the offsets (each 256-byte aligned).
 struct MoeWsLayout {
-  size_t hdr, sorted, seg, batch0, hbuf, dbuf, total;
+  size_t hdr, sorted, seg, batch0, btab, hbuf, dbuf, total;
 };
 
 inline MoeWsLayout moe_ws_layout(int P, int T, int D, int hstride) {
@@ -55,6 +58,7 @@ inline MoeWsLayout moe_ws_layout(int P, int T, int D, int hstride) {
   l.sorted = o; o = up(o + (size_t)P * 4);
   l.seg = o;    o = up(o + (size_t)P * 12);
   l.batch0 = o; o = up(o + (size_t)(P + 1) * 4);
+  l.btab = o;   o = up(o + (size_t)P * kMoeBatchInts * 4);
   l.hbuf = o;   o = up(o + (size_t)(P + T) * hstride * 2);
   l.dbuf = o;   o = up(o + (size_t)(P + T) * D * 4);
   l.total = o;
