@@ -145,7 +145,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--legs", default="all",
-                    help="comma list of: decode, mixed, gemm, moe, single, cpu, copyref "
+                    help="comma list of: decode, mixed, gemm, moe, single, repack, greedy, cpu, copyref "
                          "(default all but copyref)")
     ap.add_argument("--no-graph", action="store_true", help="launch the step without a HIP graph")
     return ap.parse_args()
@@ -167,7 +167,7 @@ import torch  # noqa: E402
 import gemm_q4nx_chunk_amd as q  # noqa: E402
 import synth  # noqa: E402
 
-LEGS = set(["decode", "mixed", "gemm", "moe", "single", "cpu"] if args.legs == "all"
+LEGS = set(["decode", "mixed", "gemm", "moe", "single", "repack", "greedy", "cpu"] if args.legs == "all"
            else args.legs.split(","))
 DEV = torch.device("cuda:0")
 torch.cuda.set_device(DEV)
@@ -490,7 +490,7 @@ def moe_leg(steps, warmup, graph):
         ps = [torch.from_numpy(routes[T][l][1]).to(DEV) for l in range(L)]
         Ys = [torch.empty((T, D), dtype=torch.float32, device=DEV) for _ in range(L)]
 
-        def run(T=T, wss=wss, X=X, ids=ids, ps=ps, Ys=Ys, ws_b=ws_b):
+        def run(T=T, wss=wss, X=X, ids=ids, ps=ps, Ys=Ys, ws_b=ws_b, k=k):
             st = torch.cuda.current_stream().cuda_stream
             for l in range(L):
                 r = lib.q4nx_moe_experts(ctypes.byref(layers[l][0]), X[l].data_ptr(), ids[l].data_ptr(),
@@ -499,6 +499,7 @@ def moe_leg(steps, warmup, graph):
                 if r:
                     raise q.Q4nxError(r, q.last_error())
         ms, wall = time_calls(run, steps, warmup, graph)
+        y_full = [y.clone() for y in Ys]
         # algorithmic bytes: every selected expert read once per layer, plus the shared expert
         uniq = sum(len(np.unique(routes[T][l][0])) for l in range(L))
         nbytes = uniq * (2 * gu + dn) + L * 3 * (Ds // 32) * (D // 256) * 5120
@@ -508,6 +509,20 @@ def moe_leg(steps, warmup, graph):
                         "pct_hbm_peak": 100 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                         "TFLOP_s": flops / (ms * 1e-3) / 1e12,
                         "launches": (3 if T * k <= 64 else 4) * L}
+        # tail skip: the picks ranked 7..10 dropped, the first six keep their weights
+        # (no renormalisation); the layer outputs move by rel_l2 against all ten picks
+        ks = 6
+        ids6 = [i[:, :ks].contiguous() for i in ids]
+        ps6 = [p_[:, :ks].contiguous() for p_ in ps]
+        ms6, _ = time_calls(lambda: run(ids=ids6, ps=ps6, k=ks), steps, warmup, graph)
+        uniq6 = sum(len(np.unique(routes[T][l][0][:, :ks])) for l in range(L))
+        b6 = uniq6 * (2 * gu + dn) + L * 3 * (Ds // 32) * (D // 256) * 5120
+        rel = [float(torch.linalg.vector_norm(y - yf) / torch.linalg.vector_norm(yf))
+               for y, yf in zip(Ys, y_full)]
+        res[f"T{T}"]["tail_skip_top6"] = {"ms_per_step": ms6, "speedup": ms / ms6, "weight_bytes": b6,
+                                          "GB_s": b6 / (ms6 * 1e-3) / 1e9,
+                                          "rel_l2_vs_top10_mean": sum(rel) / L, "rel_l2_vs_top10_max": max(rel)}
+        del ids6, ps6, y_full
         # the router on the device in front of the layer (bf16 router rows 512 x 2048 per layer)
         Rs = [bf16_dev(synth.bf16_bits((synth.rng("moe_512x10", l, "R").standard_normal((E, D)) * 0.05)
                                        .astype(np.float32))) for l in range(L)]
@@ -528,6 +543,65 @@ def moe_leg(steps, warmup, graph):
                                   "GB_s": rbytes / (msr * 1e-3) / 1e9, "launches": 2 * L}
         del wss, X, ids, ps, Ys, Rs, ids_d, p_d, lg_d
     del layers
+    torch.cuda.empty_cache()
+    return res
+
+
+# ----------------------------------------------------------------------------
+# weight preparation and the Q8 tied head's two ends
+# ----------------------------------------------------------------------------
+def repack_leg(steps, warmup, graph):
+    """Q4_K -> q4_1 repack of one 8B-dense gate|up-sized weight (28672 x 4096)."""
+    N, K = 2 * 14336, 4096
+    spec = synth.TensorSpec("gate_up", "q4_k", N, K, ("repack_q4k", 0))
+    src = to_dev(spec.generate())
+    w = q.weight(src, N, K, "q4_k")
+    out = torch.empty((N // 32) * (K // 256) * 5120, dtype=torch.uint8, device=DEV)
+    ms, _ = time_calls(lambda: q.repack_q4k_to_q41(w, out), steps, warmup, graph)
+    moved = src.numel() + out.numel()
+    return {"shape": [N, K], "bytes_read": src.numel(), "bytes_written": out.numel(), "ms": ms,
+            "GB_s_read_plus_write": moved / (ms * 1e-3) / 1e9,
+            "pct_hbm_peak": 100 * moved / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+
+def greedy_leg(steps, warmup, graph):
+    """The Q8 tied 151936 x 2560 head in both code layouts: embedding row gather
+    for 1 and 64 tokens, and greedy decode's lm_head GEMV + argmax (M = 1)."""
+    name, N, K = synth.QWEN3_4B_LM_HEAD
+    chA = synth.TensorSpec(name, "q8", N, K, ("mixed_decode", 10_000, name), q8_layout="A").generate()
+    reps = 50
+    res = {}
+    for lay in ("A", "B"):
+        d = to_dev(chA if lay == "A" else synth.q8_relayout(chA, "A", "B"))
+        w = q.weight(d, N, K, "q8", lay)
+        r = {}
+        for T in (1, 64):
+            ids = [torch.from_numpy(synth.rng("greedy", "ids", T, i).integers(0, N, T).astype(np.int32)).to(DEV)
+                   for i in range(reps)]
+            out = torch.empty((T, K), dtype=torch.float32, device=DEV)
+
+            def rows(ids=ids, out=out, T=T):
+                for i in ids:
+                    q.q8_rows(w, i, T, out)
+            ms, _ = time_calls(rows, steps, warmup, graph)
+            r[f"rows_T{T}_us"] = ms * 1e3 / reps
+        x = bf16_dev(synth.gen_x(synth.rng("greedy", "x"), 1, K))
+        y = torch.empty((1, N), dtype=torch.float32, device=DEV)
+        idx = torch.empty(1, dtype=torch.int32, device=DEV)
+
+        def head():
+            q.gemv(w, x, y, 1)
+            q.argmax(y, N, 1, idx)
+
+        def argmax_only():
+            for _ in range(reps):
+                q.argmax(y, N, 1, idx)
+        ms, _ = time_calls(head, steps, warmup, graph)
+        msa, _ = time_calls(argmax_only, steps, warmup, graph)
+        r.update({"head_gemv_argmax_us": ms * 1e3, "head_GB_s": d.numel() / (ms * 1e-3) / 1e9,
+                  "argmax_us": msa * 1e3 / reps})
+        res[f"layout_{lay}"] = r
+        del d
     torch.cuda.empty_cache()
     return res
 
@@ -627,6 +701,10 @@ def main():
         legs["moe_512x10"] = moe_leg(max(3, args.steps // 2), 2, graph)
     if "single" in LEGS:
         legs["single_gemv_1024"] = single_leg()
+    if "repack" in LEGS:
+        legs["repack_q4k_8b_gate_up"] = repack_leg(args.steps, 2, graph)
+    if "greedy" in LEGS:
+        legs["q8_head_151936x2560"] = greedy_leg(max(3, args.steps // 2), 2, graph)
     if "copyref" in LEGS:
         # a plain device copy of known size, for scaling the HBM byte counters
         a = torch.empty(1 << 30, dtype=torch.uint8, device=DEV)

@@ -195,31 +195,61 @@ __device__ __forceinline__ bool am_better(float v, int i, float bv, int bi) {
   return bi < 0 || v > bv || (v == bv && i < bi);
 }
 
+__device__ __forceinline__ void am_take(float v, int i, float& bv, int& bi) {
+  if (v == v && am_better(v, i, bv, bi)) { bv = v; bi = i; }
+}
+
+// One workgroup per row.  "Larger value, then lower index" is a total order
+// on the non-NaN values, so the pick does not depend on which thread saw which
+// element.  A 16-byte aligned row is streamed in 16-byte pieces, eight in
+// flight per thread (unconditional buffer loads; pieces past the row read zero
+// and are not taken); the last n % 4 elements, or the whole of an unaligned
+// row, are read one by one.  Waves meet through lane shuffles, then the 16
+// wave results in LDS.
 __global__ __launch_bounds__(1024) void k_argmax(const float* __restrict__ y, int n, int ldy,
                                                  int32_t* __restrict__ idx, float* __restrict__ val) {
-  __shared__ float sv[1024];
-  __shared__ int si[1024];
+  __shared__ float sv[16];
+  __shared__ int si[16];
+  constexpr int U = 8;
   const int m = blockIdx.x, t = threadIdx.x;
   const float* row = y + (size_t)m * ldy;
   float bv = 0.f;
   int bi = -1;
-  for (int i = t; i < n; i += 1024) {
-    const float v = row[i];
-    if (v == v && am_better(v, i, bv, bi)) { bv = v; bi = i; }
-  }
-  sv[t] = bv;
-  si[t] = bi;
-  __syncthreads();
-  for (int h = 512; h > 0; h >>= 1) {
-    if (t < h && si[t + h] >= 0 && am_better(sv[t + h], si[t + h], sv[t], si[t])) {
-      sv[t] = sv[t + h];
-      si[t] = si[t + h];
+  const bool vec = (reinterpret_cast<uintptr_t>(row) & 15) == 0 && n < (1 << 28);
+  const int n4 = vec ? n >> 2 : 0;
+  if (n4 > 0) {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(row, (uint32_t)n4 * 16u);
+    for (int b = 0; b < n4; b += 1024 * U) {
+      f32x4 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        v[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                             rs, (uint32_t)(b + 1024 * u + t) * 16u, 0, 0));
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int pc = b + 1024 * u + t;
+        if (pc < n4)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) am_take(v[u][c], 4 * pc + c, bv, bi);
+      }
     }
-    __syncthreads();
   }
+  for (int i = 4 * n4 + t; i < n; i += 1024) am_take(row[i], i, bv, bi);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const float ov = __shfl_xor(bv, off);
+    const int oi = __shfl_xor(bi, off);
+    if (oi >= 0 && am_better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+  }
+  if ((t & 63) == 0) { sv[t >> 6] = bv; si[t >> 6] = bi; }
+  __syncthreads();
   if (t == 0) {
-    idx[m] = si[0];
-    if (val) val[m] = si[0] >= 0 ? sv[0] : __builtin_nanf("");
+    bv = sv[0];
+    bi = si[0];
+    for (int w = 1; w < 16; ++w)
+      if (si[w] >= 0 && am_better(sv[w], si[w], bv, bi)) { bv = sv[w]; bi = si[w]; }
+    idx[m] = bi;
+    if (val) val[m] = bi >= 0 ? bv : __builtin_nanf("");
   }
 }
 

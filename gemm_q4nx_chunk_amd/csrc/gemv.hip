@@ -199,14 +199,49 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_q4x(const GemvBatch b) {
   }
 }
 
-// Q8 with the workgroup's activations staged once in LDS (raw bf16 rows) and
-// an unconditional buffer-load chunk ring: the same structure as k_gemv_q4x,
-// so a step waits only for its own chunk.  The chunk's 512-byte scale region
-// is fetched with one 8-byte load per lane and turned around in a per-wave
-// LDS slot ([group][row]), from which each lane reads its 16 scales (rows
-// 16h .. 16h+15 of its group) as two 16-byte reads, instead of 16 two-byte
-// global loads.  Used when the activation rows fit four 16-byte pieces per
-// thread and the LDS budget.
+// Q8 with the workgroup's activations staged once in LDS and an unconditional
+// buffer-load chunk ring: the same structure as k_gemv_q4x, so a step waits
+// only for its own chunk.
+//
+// Lane mapping: each 16-byte load instruction of a wave reads eight whole
+// 128-byte lines of the code region (lanes 8a .. 8a+7 one line each), so no
+// line is fetched into the CU more than once.
+//   layout A (byte 32k + r), lane 8g + s, load i: byte 1024g + 128i + 16s =
+//     column 32g + 4i + s/2, rows 16(s&1) .. +15.  The lane keeps group g and
+//     row half s&1.
+//   layout B, lane 8a + s, load i: byte 4096h + 512(g0 + i/4) + 128(i%4) + 16s
+//     with h = a&1, g0 = 2(a>>1) = column 32(g0 + i/4) + 8(i%4) + s, rows
+//     16h .. +15.  The lane keeps row half h and groups g0 (loads 0-3) and
+//     g0 + 1 (loads 4-7).
+// The activation rows sit in LDS permuted inside every 256-column span so that
+// a lane's eight columns, in load order, are one 16-byte read.  The chunk's
+// 512-byte scale region is fetched with one 8-byte load per lane and turned
+// around in a per-wave LDS slot ([group][row]), from which a lane reads the 16
+// scales of each of its groups (rows of its half) as two 16-byte reads.
+template <int KIND>
+struct Q8Lines {
+  static constexpr bool kA = KIND == KIND_Q8_A;
+  static constexpr int kGroups = kA ? 1 : 2;        // groups per lane
+  static constexpr int kHalfBit = kA ? 0 : 3;       // lane bit that selects the row half
+  __device__ static __forceinline__ uint32_t piece(int lane, int i) {
+    const int a = lane >> 3, s = lane & 7;
+    if constexpr (kA) return 1024 * a + 128 * i + 16 * s;
+    else return 4096 * (a & 1) + 512 * (2 * (a >> 1) + (i >> 2)) + 128 * (i & 3) + 16 * s;
+  }
+  __device__ static __forceinline__ int half(int lane) { return (lane >> kHalfBit) & 1; }
+  __device__ static __forceinline__ int group0(int lane) { return kA ? lane >> 3 : 2 * (lane >> 4); }
+  // LDS position (bf16 units, inside the span) of the lane's eight columns
+  __device__ static __forceinline__ int xread(int lane) {
+    return kA ? 32 * (lane >> 3) + 8 * ((lane >> 1) & 3) : 64 * (lane >> 4) + 8 * (lane & 7);
+  }
+  // LDS position of column u (0..255) of a span
+  __device__ static __forceinline__ int xperm(int u) {
+    const int g = u >> 5, w = u & 31;
+    if constexpr (kA) return 32 * g + 8 * (w & 3) + (w >> 2);
+    else return 64 * (g >> 1) + 8 * (w & 7) + 4 * (g & 1) + (w >> 3);
+  }
+};
+
 struct Q8ChunkX {
   u32x4 pc[8];
   u32x2 dp;   // scales d(r, g) with 8r + g = 4 lane .. 4 lane + 3
@@ -217,12 +252,54 @@ __device__ __forceinline__ void q8x_load_rs(__amdgpu_buffer_rsrc_t rs, uint32_t 
   constexpr int kNt = 2;
 #pragma unroll
   for (int i = 0; i < 8; ++i)
-    c.pc[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + q8_piece<KIND>(lane, i), 0, kNt));
+    c.pc[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            rs, off + Q8Lines<KIND>::piece(lane, i), 0, kNt));
   c.dp = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, off + 8192 + 8 * lane, 0, 0));
+}
+
+// acc[rho][m] += sum over the lane's groups q of d(16h + rho, g0 + q) *
+// sum over the group's loads i of code(16h + rho, column of load i) * x[m][i].
+// Every product of an int8 code and a bf16 is exact in fp32.
+template <int NG, int M>
+__device__ __forceinline__ void q8x_compute(const u32x4 (&pc)[8], const uint32_t (&dv)[NG][8],
+                                            const Q8XRaw<M>& xr, float (&acc)[16][M]) {
+  float xf[M][8];
+#pragma unroll
+  for (int m = 0; m < M; ++m)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      xf[m][2 * t] = bf16lo(xr.v[m][t]);
+      xf[m][2 * t + 1] = bf16hi(xr.v[m][t]);
+    }
+  constexpr int L = 8 / NG;   // loads per group
+#pragma unroll
+  for (int q = 0; q < NG; ++q) {
+    float part[16][M];
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+#pragma unroll
+      for (int m = 0; m < M; ++m) part[r][m] = 0.f;
+#pragma unroll
+    for (int i = q * L; i < (q + 1) * L; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float cf = (float)(int8_t)(pc[i][r >> 2] >> (8 * (r & 3)));
+#pragma unroll
+        for (int m = 0; m < M; ++m) part[r][m] = fmaf(cf, xf[m][i], part[r][m]);
+      }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float d = (r & 1) ? bf16hi(dv[q][r >> 1]) : bf16lo(dv[q][r >> 1]);
+#pragma unroll
+      for (int m = 0; m < M; ++m) acc[r][m] = fmaf(d, part[r][m], acc[r][m]);
+    }
+  }
 }
 
 template <int KIND, int M, int WAVES, int D>
 __global__ __launch_bounds__(64 * WAVES) void k_gemv_q8x(const GemvBatch b) {
+  using Map = Q8Lines<KIND>;
+  constexpr int NG = Map::kGroups, HB = Map::kHalfBit;
   constexpr int NT = 64 * WAVES;
   constexpr int XRP8 = 4;
   constexpr int CB = 8704;
@@ -238,10 +315,10 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_q8x(const GemvBatch b) {
   const int tr = tr0 + slot < J.TR ? tr0 + slot : J.TR - 1;
   const int TC = J.TC, K = TC * 256;
   const int c0 = part * TC / ks, c1 = (part + 1) * TC / ks;
-  const int h = (lane >> 2) & 1, g = lane >> 3;
+  const int h = Map::half(lane), g0 = Map::group0(lane);
   const int NP = M * TC * 32;   // 16-byte pieces of the M activation rows
 
-  // 1. activations: piece p of row m at x[m][8 p'] (p' = p - 32 TC m)
+  // 1. activations: piece p of row m holds x[m][8 p' .. 8 p' + 7] (p' = p - 32 TC m)
   const __amdgpu_buffer_rsrc_t xrs = make_rsrc(J.x, (uint32_t)(((M - 1) * J.ldx + K) * 2));
   u32x4 xr[XRP8];
 #pragma unroll
@@ -256,11 +333,20 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_q8x(const GemvBatch b) {
   Q8ChunkX ring[D];
 #pragma unroll
   for (int j = 0; j < D; ++j) q8x_load_rs<KIND>(wrs, j * CB, lane, ring[j]);
-  // 3. rows to LDS: row m at xl[m * K / 2 .. ] (bf16 pairs)
+  // 3. rows to LDS, permuted inside each 256-column span: row m at bf16 m * K
+  uint16_t* xh = reinterpret_cast<uint16_t*>(xl);
 #pragma unroll
   for (int p = 0; p < XRP8; ++p) {
     const int pc = tid + NT * p;
-    if (pc < NP) *reinterpret_cast<u32x4*>(xl + 4 * pc) = xr[p];
+    if (pc < NP) {
+      const int m = pc / (TC * 32), pp = pc - m * TC * 32;
+      const int span = m * K + 256 * (pp >> 5), u0 = 8 * (pp & 31);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t w = xr[p][e >> 1];
+        xh[span + Map::xperm(u0 + e)] = (uint16_t)((e & 1) ? (w >> 16) : (w & 0xFFFFu));
+      }
+    }
   }
   __syncthreads();
 
@@ -271,6 +357,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_q8x(const GemvBatch b) {
     for (int m = 0; m < M; ++m) acc[r][m] = 0.f;
   uint16_t* ds = dsl[wave];
   const int dr = lane >> 1, dg0 = 4 * (lane & 1);
+  const int xoff = Map::xread(lane);
   auto step = [&](int j, int c) {
     __builtin_amdgcn_sched_barrier(0);
     // scales: (row dr, groups dg0 .. dg0+3) -> slot [group][row]; the wave's
@@ -283,21 +370,25 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_q8x(const GemvBatch b) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    Q8Chunk ch;
+    u32x4 pcs[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) ch.pc[i] = ring[j].pc[i];
-    const u32x4 d0 = *reinterpret_cast<const u32x4*>(ds + g * 32 + 16 * h);
-    const u32x4 d1 = *reinterpret_cast<const u32x4*>(ds + g * 32 + 16 * h + 8);
-    ch.dv[0] = d0.x; ch.dv[1] = d0.y; ch.dv[2] = d0.z; ch.dv[3] = d0.w;
-    ch.dv[4] = d1.x; ch.dv[5] = d1.y; ch.dv[6] = d1.z; ch.dv[7] = d1.w;
+    for (int i = 0; i < 8; ++i) pcs[i] = ring[j].pc[i];
+    uint32_t dv[NG][8];
+#pragma unroll
+    for (int q = 0; q < NG; ++q) {
+      const u32x4 d0 = *reinterpret_cast<const u32x4*>(ds + (g0 + q) * 32 + 16 * h);
+      const u32x4 d1 = *reinterpret_cast<const u32x4*>(ds + (g0 + q) * 32 + 16 * h + 8);
+      dv[q][0] = d0.x; dv[q][1] = d0.y; dv[q][2] = d0.z; dv[q][3] = d0.w;
+      dv[q][4] = d1.x; dv[q][5] = d1.y; dv[q][6] = d1.z; dv[q][7] = d1.w;
+    }
     Q8XRaw<M> xv;
 #pragma unroll
     for (int m = 0; m < M; ++m)
-      xv.v[m] = *reinterpret_cast<const u32x4*>(xl + (m * K + q8_xcol(lane, c)) / 2);
+      xv.v[m] = *reinterpret_cast<const u32x4*>(xh + m * K + 256 * c + xoff);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");   // the slot's reads come before
     __builtin_amdgcn_wave_barrier();                          // the next step's writes
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    q8_compute_raw<M>(ch, xv, acc);
+    q8x_compute<NG, M>(pcs, dv, xv, acc);
     q8x_load_rs<KIND>(wrs, (uint32_t)(c + D - c0) * CB, lane, ring[j]);
   };
   int base = c0;
@@ -309,8 +400,18 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_q8x(const GemvBatch b) {
   for (int j = 0; j + 1 < D; ++j)
     if (base + j < c1) step(j, base + j);
 
-  q8_lane_reduce<M>(acc);
-  if ((lane & ~4) == 0) {
+  // sum over the 32 lanes of each row half (every lane bit but HB)
+#pragma unroll
+  for (int r = 0; r < 16; ++r)
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      float v = acc[r][m];
+#pragma unroll
+      for (int bit = 0; bit < 6; ++bit)
+        if (bit != HB) v += __shfl_xor(v, 1 << bit);
+      acc[r][m] = v;
+    }
+  if ((lane & ~(1 << HB)) == 0) {
 #pragma unroll
     for (int r = 0; r < 16; ++r)
 #pragma unroll
@@ -399,7 +500,9 @@ static hipError_t launch_one(const GemvBatch& b, int n_wg, int xl_bytes, hipStre
       hipLaunchKernelGGL((k_gemv_q4<KIND, M, WAVES>), dim3(n_wg), dim3(64 * WAVES), 0, s, b);
   } else {
     if (xl_bytes > 0)
-      hipLaunchKernelGGL((k_gemv_q8x<KIND, M, WAVES, M == 1 ? 2 : 1>), dim3(n_wg),
+      // two chunks in flight per wave at M = 1, except layout B's 16-wave
+      // variant, whose two scale groups per lane leave no registers for it
+      hipLaunchKernelGGL((k_gemv_q8x<KIND, M, WAVES, M == 1 && !(KIND == KIND_Q8_B && WAVES == 16) ? 2 : 1>), dim3(n_wg),
                          dim3(64 * WAVES), xl_bytes, s, b);
     else
       hipLaunchKernelGGL((k_gemv_q8<KIND, M, WAVES>), dim3(n_wg), dim3(64 * WAVES), 0, s, b);

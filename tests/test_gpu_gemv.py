@@ -60,15 +60,23 @@ def test_gemv_other_m(M):
     _check(gemv(dev_u8(ch), N, K, "q4_1", x), ch, "q4_1", N, K, x, None)
 
 
-def test_q8_layouts_give_identical_bits():
+@pytest.mark.parametrize("M", [1, 2, 4])
+def test_q8_layouts_of_one_weight(M):
+    """The same codes stored in layout A and in layout B: each result is within
+    the bar of the oracle and repeats bit for bit.  The two layouts put
+    different columns in a lane, so their sums run in different orders and
+    may differ in the last bits."""
     N, K = 2048, 2560
     A = synth.gen_q8(synth.rng("gpu-gemv", "q8ab"), N, K, "A")
     B = synth.q8_relayout(A, "A", "B")
-    x = synth.gen_x(synth.rng("gpu-gemv", "q8ab-x"), 1, K)
-    ya = gemv(dev_u8(A), N, K, "q8", x, "A")
-    yb = gemv(dev_u8(B), N, K, "q8", x, "B")
-    np.testing.assert_array_equal(ya.view(np.uint32), yb.view(np.uint32))
+    x = synth.gen_x(synth.rng("gpu-gemv", "q8ab-x", M), M, K)
+    dA, dB = dev_u8(A), dev_u8(B)
+    ya = gemv(dA, N, K, "q8", x, "A")
+    yb = gemv(dB, N, K, "q8", x, "B")
     _check(ya, A, "q8", N, K, x, "A")
+    _check(yb, A, "q8", N, K, x, "A")
+    np.testing.assert_array_equal(gemv(dA, N, K, "q8", x, "A").view(np.uint32), ya.view(np.uint32))
+    np.testing.assert_array_equal(gemv(dB, N, K, "q8", x, "B").view(np.uint32), yb.view(np.uint32))
 
 
 @pytest.mark.parametrize("kind,layout", KINDS)

@@ -76,3 +76,24 @@ def test_greedy_head_q8(layout):
     for m in range(2):
         assert got[m] == _argmax_ref(yh[m])
         assert yr[m, got[m]] >= yr[m].max() - 2 * 2e-3 * a[m, got[m]] - 2 * 2e-3 * a[m, np.argmax(yr[m])]
+
+
+@pytest.mark.parametrize("n,ldy", [(3001, 3003), (3001, 3004), (5, 5), (1, 1), (151936, 151936)])
+def test_argmax_tail_and_unaligned_rows(n, ldy):
+    """Rows whose length is not a multiple of 4, rows that start off a 16-byte
+    boundary, and the full 151936-wide head: maxima in the last element and a
+    tie between the first and last elements."""
+    g = np.random.default_rng(n + ldy)
+    M = 3
+    y = g.standard_normal((M, ldy)).astype(np.float32)
+    y[0, n - 1] = 50.0
+    y[1, 0] = 60.0
+    y[1, n - 1] = 60.0
+    y[2, g.integers(0, n)] = 70.0
+    idx = torch.zeros(M, dtype=torch.int32, device="cuda")
+    val = torch.zeros(M, dtype=torch.float32, device="cuda")
+    q().argmax(dev_f32(y), n, M, idx, val, ldy=ldy)
+    got, gv = host(idx), host(val)
+    for m in range(M):
+        assert got[m] == _argmax_ref(y[m, :n]), m
+        assert gv[m] == y[m, got[m]]
