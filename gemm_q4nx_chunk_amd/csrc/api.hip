@@ -579,6 +579,9 @@ static int check_moe_layer(const q4nx_moe_layer* L) {
       L->d_shared < 0 || L->d_shared % 256)
     return fail(Q4NX_E_SHAPE, "moe: d_model, d_expert, d_shared must be multiples of 256 "
                 "(d_shared may be 0), got %d, %d, %d", L->d_model, L->d_expert, L->d_shared);
+  if (L->d_model > (1 << 20) || L->d_expert > (1 << 20) || L->d_shared > (1 << 20))
+    return fail(Q4NX_E_SHAPE, "moe: d_model, d_expert, d_shared must be at most 1048576, got %d, %d, %d",
+                L->d_model, L->d_expert, L->d_shared);
   const int64_t cb = L->chunk_bytes;
   const int64_t gu = (int64_t)(L->d_expert / 32) * (L->d_model / 256) * cb;
   const int64_t dn = (int64_t)(L->d_model / 32) * (L->d_expert / 256) * cb;
@@ -609,7 +612,7 @@ static int moe_hstride(const q4nx_moe_layer* L) {
 }
 
 size_t q4nx_moe_ws(const q4nx_moe_layer* L, int T, int k) {
-  if (check_moe_layer(L) || T < 1 || k < 1 || T > 4096 || k > 16 || T * k > q4nx::kMoeMaxPairs)
+  if (check_moe_layer(L) || T < 1 || k < 1 || T > 4096 || k > q4nx::kMoeMaxK || T * k > q4nx::kMoeMaxPairs)
     return 0;
   return q4nx::moe_ws_layout(T * k, T, L->d_model, moe_hstride(L)).total;
 }
@@ -620,7 +623,7 @@ int q4nx_moe_experts(const q4nx_moe_layer* L, const uint16_t* X, const int32_t* 
   int st = check_moe_layer(L);
   if (st) return st;
   if (!X || !ids || !p || !Y) return fail(Q4NX_E_ARG, "moe: null X, ids, p or Y");
-  if (T < 1 || T > 4096 || k < 1 || k > 16 || T * k > q4nx::kMoeMaxPairs)
+  if (T < 1 || T > 4096 || k < 1 || k > q4nx::kMoeMaxK || T * k > q4nx::kMoeMaxPairs)
     return fail(Q4NX_E_ARG, "moe: T = %d, k = %d outside T 1..4096, k 1..16, T*k <= %d", T, k,
                 q4nx::kMoeMaxPairs);
   if (!aligned(X, 16) || !aligned(ids, 4) || !aligned(p, 4) || !aligned(Y, 4))

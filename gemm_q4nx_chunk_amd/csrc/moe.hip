@@ -652,22 +652,38 @@ __global__ __launch_bounds__(256) void k_moe_down(MoeArgs a, int ks_r, int ks_s)
 // ---------------------------------------------------------------------------
 // combine
 // ---------------------------------------------------------------------------
+// Every load of a thread is issued before the first product: ids, weights and
+// the k partial rows come through buffer resources, so slots past k read zero
+// without a branch, and the sum runs in slot order once they have arrived.
 __global__ __launch_bounds__(256) void k_moe_combine(MoeArgs a) {
+  constexpr int KM = kMoeMaxK;
   const int t = blockIdx.y;
   const int n = blockIdx.x * 256 + threadIdx.x;
   if (n >= a.D) return;
   const int P = a.T * a.k;
+  const __amdgpu_buffer_rsrc_t ir = make_rsrc(a.ids + (size_t)t * a.k, (uint32_t)a.k * 4u);
+  const __amdgpu_buffer_rsrc_t pr = make_rsrc(a.p + (size_t)t * a.k, (uint32_t)a.k * 4u);
+  const __amdgpu_buffer_rsrc_t dr = make_rsrc(a.dbuf + (size_t)t * a.k * a.D, (uint32_t)(a.k * a.D) * 4u);
+  int e[KM];
+  float pj[KM], d[KM];
+#pragma unroll
+  for (int j = 0; j < KM; ++j) {
+    e[j] = (int)__builtin_amdgcn_raw_buffer_load_b32(ir, 4u * j, 0, 0);
+    pj[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(pr, 4u * j, 0, 0));
+    d[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(dr, (uint32_t)(j * a.D + n) * 4u, 0, 0));
+  }
+  const float ds = a.Ds ? a.dbuf[(size_t)(P + t) * a.D + n] : 0.f;
   float y = 0.f;
-  for (int j = 0; j < a.k; ++j) {
-    const int pair = t * a.k + j;
-    const int e = a.ids[pair];
-    const bool ok = e >= 0 && e < a.n_experts;
-    const float d = ok ? a.dbuf[(size_t)pair * a.D + n] : 0.f;
-    if (ok) y = fmaf(a.p[pair], d, y);
-    if (a.dbg_d) a.dbg_d[(size_t)pair * a.D + n] = d;
+#pragma unroll
+  for (int j = 0; j < KM; ++j) {
+    if (j < a.k) {
+      const bool ok = e[j] >= 0 && e[j] < a.n_experts;
+      const float dj = ok ? d[j] : 0.f;
+      if (ok) y = fmaf(pj[j], dj, y);
+      if (a.dbg_d) a.dbg_d[(size_t)(t * a.k + j) * a.D + n] = dj;
+    }
   }
   if (a.Ds) {
-    const float ds = a.dbuf[(size_t)(P + t) * a.D + n];
     y += ds;
     if (a.dbg_d_shared) a.dbg_d_shared[(size_t)t * a.D + n] = ds;
   }

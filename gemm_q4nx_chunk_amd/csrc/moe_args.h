@@ -7,6 +7,7 @@
 namespace q4nx {
 
 constexpr int kMoeMaxPairs = 4096;   // T * k per call (the route kernel sorts them in LDS)
+constexpr int kMoeMaxK = 16;         // picks per token
 constexpr int kMoeBatchInts = 12;    // ints per routed-batch record (batches of at most 4 tokens)
 
 struct MoeArgs {

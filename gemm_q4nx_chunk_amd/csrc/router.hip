@@ -73,6 +73,11 @@ __device__ __forceinline__ uint32_t rt_key(float v) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
+// The logit of a key (a NaN for key 0).
+__device__ __forceinline__ float rt_logit(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+}
+
 // (key, ~id) pairs ordered lexicographically: the larger key first, the lower
 // id among equal keys.  Moves a pair within rows of 16 lanes by DPP.
 __device__ __forceinline__ void rt_max_step(uint32_t& k, uint32_t& i, int ctrl_sel) {
@@ -89,16 +94,16 @@ __device__ __forceinline__ void rt_max_step(uint32_t& k, uint32_t& i, int ctrl_s
 }
 
 // Picks and weights: one wave per token (4 tokens per workgroup).  Lane l
-// holds logits l + 64 i (i < 16, E <= 1024) in registers.  The max and the
+// holds logits l + 64 i (i < EL, E <= 64 EL) in registers.  The max and the
 // sum of expf(z - max) (each lane's terms in i order, then a fixed pattern:
 // pairs, quads, eights and rows of 16 within a row by DPP, then rows 0..3 in
 // order) and each of the k picks (the lane's best untaken candidate, the best
 // of each row by DPP, then of the 4 rows) need no LDS and no barrier; a pick
 // is a maximum under a total order, so it does not depend on the pairing.
+template <int EL>   // logits per lane: E <= 64 EL
 __global__ __launch_bounds__(256) void k_router_topk(const float* __restrict__ logits, int T, int E,
                                                      int k, int renorm, int32_t* __restrict__ ids,
                                                      float* __restrict__ p) {
-  constexpr int EL = kRouterMaxE / 64;
   const int lane = threadIdx.x & 63;
   const int t = 4 * blockIdx.x + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
   if (t >= T) return;
@@ -162,10 +167,12 @@ __global__ __launch_bounds__(256) void k_router_topk(const float* __restrict__ l
     }
     const int pick = (int)~wi;
     if ((pick & 63) == lane) taken |= 1u << (pick >> 6);
-    if (lane == j) my_id = pick;
+    if (lane == j) {
+      my_id = pick;
+      my_v = rt_logit(wk);
+    }
   }
-  // the picked logits and weights: lane j < k holds pick j
-  if (lane < k) my_v = logits[(size_t)t * E + my_id];
+  // the weights: lane j < k holds pick j
   const float w = lane < k ? expf(my_v - m) / ssum : 0.f;
   float tot = 0.f;
   for (int j = 0; j < k; ++j) tot += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(w), j));
@@ -185,7 +192,10 @@ hipError_t launch_moe_router(const uint16_t* R, const uint16_t* X, int T, int D,
     case 8: hipLaunchKernelGGL((k_router_logits<8>), g, b, 0, s, R, X, T, E, logits); break;
     default: return hipErrorInvalidValue;
   }
-  hipLaunchKernelGGL(k_router_topk, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k, renorm, ids, p);
+  const dim3 gt((T + 3) / 4), bt(256);
+  if (E <= 256) hipLaunchKernelGGL(k_router_topk<4>, gt, bt, 0, s, logits, T, E, k, renorm, ids, p);
+  else if (E <= 512) hipLaunchKernelGGL(k_router_topk<8>, gt, bt, 0, s, logits, T, E, k, renorm, ids, p);
+  else hipLaunchKernelGGL(k_router_topk<kRouterMaxE / 64>, gt, bt, 0, s, logits, T, E, k, renorm, ids, p);
   return hipGetLastError();
 }
 

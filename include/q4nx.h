@@ -232,9 +232,9 @@ size_t q4nx_gemm_batched_ws(const q4nx_gemm_job* jobs, int n_jobs);
  */
 typedef struct q4nx_moe_layer {
   int32_t n_experts;     /* routed experts in the arena, >= 1 */
-  int32_t d_model;       /* model width D: gate/up cols, down rows (mult. of 256) */
-  int32_t d_expert;      /* routed intermediate width: gate/up rows, down cols (mult. of 256) */
-  int32_t d_shared;      /* shared intermediate width (mult. of 256), or 0 for none */
+  int32_t d_model;       /* model width D: gate/up cols, down rows (mult. of 256, <= 1048576) */
+  int32_t d_expert;      /* routed intermediate width: gate/up rows, down cols (mult. of 256, <= 1048576) */
+  int32_t d_shared;      /* shared intermediate width (mult. of 256, <= 1048576), or 0 for none */
   int32_t chunk_bytes;   /* kind of every expert weight: 5120 (q4_1) or 4736 (Q4_K) */
   int32_t reserved;      /* must be 0 */
   const void* gate;      /* DEVICE, expert e at gate + e*gate_stride, [d_expert/32][D/256] chunks */
