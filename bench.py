@@ -145,7 +145,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--legs", default="all",
-                    help="comma list of: decode, mixed, gemm, moe, single, repack, greedy, cpu, copyref "
+                    help="comma list of: decode, mixed, gemm, moe, single, kinds, repack, greedy, cpu, copyref "
                          "(default all but copyref)")
     ap.add_argument("--no-graph", action="store_true", help="launch the step without a HIP graph")
     return ap.parse_args()
@@ -167,7 +167,8 @@ import torch  # noqa: E402
 import gemm_q4nx_chunk_amd as q  # noqa: E402
 import synth  # noqa: E402
 
-LEGS = set(["decode", "mixed", "gemm", "moe", "single", "repack", "greedy", "cpu"] if args.legs == "all"
+LEGS = set(["decode", "mixed", "gemm", "moe", "single", "kinds", "repack", "greedy", "cpu"]
+           if args.legs == "all"
            else args.legs.split(","))
 DEV = torch.device("cuda:0")
 torch.cuda.set_device(DEV)
@@ -564,6 +565,40 @@ def repack_leg(steps, warmup, graph):
             "pct_hbm_peak": 100 * moved / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
 
+def kinds_leg(steps, warmup, graph):
+    """One large decode GEMV per chunk kind at the lm_head shape (151936 x 2560,
+    M = 1): q4_1, Q4_K and Q8 in both code layouts, HIP events around each call."""
+    name, N, K = synth.QWEN3_4B_LM_HEAD
+    x = bf16_dev(synth.gen_x(synth.rng("kinds", "x"), 1, K))
+    y = torch.empty((1, N), dtype=torch.float32, device=DEV)
+    res = {}
+    for kind, lay, key in (("q4_1", None, ("qwen3_4b_decode", 10_000, name)),
+                           ("q4_k", None, ("kinds", "q4_k")),
+                           ("q8", "A", ("mixed_decode", 10_000, name)),
+                           ("q8", "B", ("mixed_decode", 10_000, name))):
+        spec = synth.TensorSpec(name, kind, N, K, key, q8_layout=lay or "A",
+                                opts={"zero": "normal"} if kind == "q4_1" else {})
+        ch = spec.generate()
+        if lay == "B":
+            ch = synth.q8_relayout(ch, "A", "B")
+        d = to_dev(ch)
+        del ch
+        w = q.weight(d, N, K, kind, lay)
+        calls = 10
+
+        def run(w=w):
+            for _ in range(calls):
+                q.gemv(w, x, y, 1)
+        ms, _ = time_calls(run, steps, warmup, graph)
+        us = ms * 1e3 / calls
+        res[kind if lay is None else f"q8_{lay}"] = {"bytes": d.numel(), "us_per_call": us,
+                                                      "GB_s": d.numel() / (us * 1e-6) / 1e9,
+                                                      "pct_hbm_peak": 100 * d.numel() / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+        del d
+    torch.cuda.empty_cache()
+    return res
+
+
 def greedy_leg(steps, warmup, graph):
     """The Q8 tied 151936 x 2560 head in both code layouts: embedding row gather
     for 1 and 64 tokens, and greedy decode's lm_head GEMV + argmax (M = 1)."""
@@ -635,10 +670,29 @@ def single_leg():
         for _ in range(copies):
             lib.q4nx_gemv(ctypes.byref(hot), x.data_ptr(), y.data_ptr(), 1, st)
     msh, _ = time_calls(run_hot, 3, 1, graph=True)
+    # the same GEMVs, 64 independent ones (own weight copy, x and y) per batched launch
+    nj = 64
+    xs = bf16_dev(np.tile(synth.gen_x(synth.rng("q4_1_gemv_1024", 0, "x"), 1, spec.K), (nj, 1)))
+    ys = torch.empty((nj, spec.N), dtype=torch.float32, device=DEV)
+    arrs = []
+    for b0 in range(0, copies, nj):
+        arrs.append((q.GemvJob * nj)(*[q.GemvJob(descs[b0 + j], q._ptr(xs[j]), q._ptr(ys[j]))
+                                       for j in range(nj)]))
+
+    def run_batched():
+        st = torch.cuda.current_stream().cuda_stream
+        for arr in arrs:
+            r = lib.q4nx_gemv_batched(arr, nj, 1, st)
+            if r:
+                raise q.Q4nxError(r, q.last_error())
+    msb, _ = time_calls(run_batched, 5, 2, graph=True)
+    perb = msb / copies * 1e3
     return {"weight_bytes": spec.nbytes, "rotated_copies": copies,
             "us_per_call_stream": per, "us_per_call_graph": perg,
             "GB_s_graph_rotated": spec.nbytes / (perg * 1e-6) / 1e9,
-            "us_per_call_graph_hot": msh / copies * 1e3}
+            "us_per_call_graph_hot": msh / copies * 1e3,
+            "batched_64_per_launch": {"us_per_gemv": perb, "GB_s": spec.nbytes / (perb * 1e-6) / 1e9,
+                                      "pct_hbm_peak": 100 * spec.nbytes / (perb * 1e-6) / 1e9 / HBM_PEAK_GBS}}
 
 
 # ----------------------------------------------------------------------------
@@ -701,6 +755,8 @@ def main():
         legs["moe_512x10"] = moe_leg(max(3, args.steps // 2), 2, graph)
     if "single" in LEGS:
         legs["single_gemv_1024"] = single_leg()
+    if "kinds" in LEGS:
+        legs["lm_head_shape_per_kind"] = kinds_leg(max(3, args.steps // 2), 2, graph)
     if "repack" in LEGS:
         legs["repack_q4k_8b_gate_up"] = repack_leg(args.steps, 2, graph)
     if "greedy" in LEGS:
