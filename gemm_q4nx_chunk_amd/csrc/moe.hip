@@ -26,10 +26,124 @@ namespace q4nx {
 // ---------------------------------------------------------------------------
 // route
 // ---------------------------------------------------------------------------
+// Blocks of at most 64 tokens over at most 1024 experts whose ids are all in
+// range and whose tokens name distinct experts need no sort: bit t of mask[e]
+// says token t picked expert e.  A token's slots name distinct experts, so an
+// expert's pairs in token order are its pairs in pair-index order, and a
+// pair's place in its segment is the number of earlier tokens in the mask.
+// Counts, batch counts and segment flags are one prefix sum over the experts
+// (one per thread); each routed batch's record is then written by its own
+// thread.  The tables are the ones the sort below produces.  Returns false,
+// having written nothing, when the block does not qualify.
+constexpr int kRouteMaskTokens = 64, kRouteMaskExperts = 1024;
+
+__device__ __forceinline__ uint64_t block_incl_scan64(uint64_t v, uint64_t* wsum) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint64_t o = __shfl_up(v, off);
+    if (lane >= off) v += o;
+  }
+  if (lane == 63) wsum[w] = v;
+  __syncthreads();
+  if (w == 0) {
+    uint64_t t = lane < 16 ? wsum[lane] : 0;
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+      const uint64_t o = __shfl_up(t, off);
+      if (lane >= off) t += o;
+    }
+    if (lane < 16) wsum[lane] = t;
+  }
+  __syncthreads();
+  return w > 0 ? v + wsum[w - 1] : v;
+}
+
+__device__ __forceinline__ bool moe_route_masks(const MoeArgs& a, uint32_t* lds16k, int32_t* sorted_lds,
+                                                uint64_t* wsum, int32_t* flags) {
+  const int T = a.T, k = a.k, P = T * k, E = a.n_experts, tid = threadIdx.x;
+  if (T > kRouteMaskTokens || E > kRouteMaskExperts) return false;
+  uint64_t* mask = reinterpret_cast<uint64_t*>(lds16k);           // [1024]
+  int32_t* s_start = reinterpret_cast<int32_t*>(mask + 1024);     // [1024]
+  int32_t* s_bstart = s_start + 1024;                             // [1024]
+  mask[tid] = 0;
+  if (tid == 0) { flags[0] = 0; flags[1] = 0; }
+  __syncthreads();
+  int e_mine = -1;
+  if (tid < P) {   // P <= 64 * 16 = 1024
+    const int e = a.ids[tid];
+    if (e < 0 || e >= E) atomicOr(&flags[0], 1);
+    else {
+      atomicOr(reinterpret_cast<unsigned long long*>(&mask[e]), 1ull << (tid / k));
+      e_mine = e;
+    }
+  }
+  __syncthreads();
+  const uint64_t m = tid < E ? mask[tid] : 0;
+  const int cnt = __popcll(m);
+  if (cnt) atomicAdd(&flags[1], cnt);
+  __syncthreads();
+  if (flags[0] || flags[1] != P) return false;   // an id out of range, or a token naming an expert twice
+  const int nb = (cnt + a.tb - 1) / a.tb;
+  const uint64_t own = (uint64_t)cnt | ((uint64_t)nb << 16) | ((uint64_t)(cnt > 0) << 32);
+  const uint64_t inc = block_incl_scan64(own, wsum);
+  const uint64_t ex = inc - own;
+  const int start = (int)(ex & 0xFFFFu), bstart = (int)((ex >> 16) & 0xFFFFu), u = (int)(ex >> 32);
+  s_start[tid] = start;
+  s_bstart[tid] = bstart;
+  if (cnt) {
+    a.seg[3 * u + 0] = tid;
+    a.seg[3 * u + 1] = start;
+    a.seg[3 * u + 2] = cnt;
+    a.batch0[u] = bstart;
+  }
+  if (tid == 1023) {
+    const int nseg = (int)(inc >> 32), nbatch = (int)((inc >> 16) & 0xFFFFu);
+    a.hdr[0] = 0u;
+    a.hdr[1] = (uint32_t)nseg;
+    a.hdr[2] = (uint32_t)nbatch;
+    a.batch0[nseg] = nbatch;
+    flags[2] = nbatch;
+  }
+  __syncthreads();
+  if (e_mine >= 0) {
+    const int t = tid / k;
+    const int pos = s_start[e_mine] + __popcll(mask[e_mine] & ((1ull << t) - 1));
+    sorted_lds[pos] = tid;
+    a.sorted[pos] = tid;
+  }
+  __syncthreads();
+  if (tid < flags[2]) {   // batch tid: the last expert whose first batch is at or before it
+    int lo = 0, hi = E - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_bstart[mid] <= tid) lo = mid; else hi = mid - 1;
+    }
+    const int e = lo, bi = tid - s_bstart[e], c = __popcll(mask[e]);
+    const int pos0 = s_start[e] + bi * a.tb, ntok = min(a.tb, c - bi * a.tb);
+    int32_t* r = a.btab + (size_t)tid * kMoeBatchInts;
+    r[0] = e;
+    r[1] = pos0;
+    r[2] = ntok;
+    r[3] = 0;
+    for (int mm = 0; mm < 4; ++mm) {
+      const int pair = sorted_lds[pos0 + (mm < ntok ? mm : 0)];
+      r[4 + mm] = pair / k;
+      r[8 + mm] = pair;
+    }
+  }
+  return true;
+}
+
 __global__ __launch_bounds__(1024) void k_moe_route(MoeArgs a) {
   __shared__ uint32_t key[kMoeMaxPairs];
   __shared__ int32_t scan[1024];
   __shared__ int32_t nbad;
+  __shared__ uint64_t wsum[16];
+  __shared__ int32_t flags[4];
+  static_assert(kMoeMaxPairs * 4 >= 1024 * 16, "the masks and prefix tables fit the key array");
+  if (moe_route_masks(a, key, scan, wsum, flags)) return;
+  __syncthreads();   // the masks' LDS is the sort's
   const int P = a.T * a.k;
   int NP = 1;
   while (NP < P) NP <<= 1;

@@ -157,7 +157,7 @@ def _check_stages(layer, X, ids, p, r):
 
 
 @pytest.mark.parametrize("kind", ["q4_1", "q4_k"])
-@pytest.mark.parametrize("T", [1, 3, 17, 64])
+@pytest.mark.parametrize("T", [1, 3, 17, 64, 65])
 def test_small_moe_stagewise(kind, T):
     layer = Layer("small", kind, 16, 512, 256, 256)
     g = synth.rng("gpu-moe", "route", kind, T)
@@ -195,6 +195,27 @@ def test_out_of_range_ids_flagged_and_skipped():
     assert r2["err"] == 0
     np.testing.assert_array_equal(r["y"].view(np.uint32), r2["y"].view(np.uint32))
     _check_stages(layer, X, bad, p, r)
+
+
+@pytest.mark.parametrize("case", ["repeat", "bad"])
+def test_block_routing_with_repeated_or_bad_ids(case):
+    """A 20-token block (routed through the route kernel) where one token names
+    the same expert in two slots, or where ids are out of range: the same
+    results as the oracle's slot-by-slot sum, and for bad ids the error flag."""
+    layer = Layer("blockroute", "q4_1", 16, 512, 256, 256)
+    g = synth.rng("gpu-moe", "route-block", case)
+    ids, p = synth.gen_router(g, 20, 16, 4, 1.1)
+    X = synth.gen_x(g, 20, 512)
+    ids = ids.copy()
+    if case == "repeat":
+        ids[3, 1] = ids[3, 0]
+        ids[11, 3] = ids[11, 2]
+    else:
+        ids[2, 1] = -3
+        ids[17, 0] = 16
+    r = layer.run(X, ids, p)
+    assert r["err"] == (1 if case == "bad" else 0)
+    _check_stages(layer, X, ids, p, r)
 
 
 def test_token_result_does_not_depend_on_its_batch():
