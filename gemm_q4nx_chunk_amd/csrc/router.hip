@@ -78,19 +78,27 @@ __device__ __forceinline__ float rt_logit(uint32_t key) {
   return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
 }
 
-// (key, ~id) pairs ordered lexicographically: the larger key first, the lower
-// id among equal keys.  Moves a pair within rows of 16 lanes by DPP.
-__device__ __forceinline__ void rt_max_step(uint32_t& k, uint32_t& i, int ctrl_sel) {
-  uint32_t ok, oi;
+// A candidate as one 64-bit value, key << 32 | ~id: the larger value is the
+// better candidate (the larger key, then the lower id), and 0 is "none".
+// Takes the larger of the lane's value and its partner's within rows of 16
+// lanes, by DPP on both halves.
+__device__ __forceinline__ uint64_t rt_max_step(uint64_t v, int ctrl_sel) {
+  const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  uint32_t olo, ohi;
   switch (ctrl_sel) {   // constant after inlining
-    case 0: ok = __builtin_amdgcn_mov_dpp(k, 0xB1, 0xF, 0xF, false); oi = __builtin_amdgcn_mov_dpp(i, 0xB1, 0xF, 0xF, false); break;   // quad_perm [1,0,3,2]
-    case 1: ok = __builtin_amdgcn_mov_dpp(k, 0x4E, 0xF, 0xF, false); oi = __builtin_amdgcn_mov_dpp(i, 0x4E, 0xF, 0xF, false); break;   // quad_perm [2,3,0,1]
-    case 2: ok = __builtin_amdgcn_mov_dpp(k, 0x141, 0xF, 0xF, false); oi = __builtin_amdgcn_mov_dpp(i, 0x141, 0xF, 0xF, false); break; // row_half_mirror
-    default: ok = __builtin_amdgcn_mov_dpp(k, 0x140, 0xF, 0xF, false); oi = __builtin_amdgcn_mov_dpp(i, 0x140, 0xF, 0xF, false); break; // row_mirror
+    case 0: olo = __builtin_amdgcn_mov_dpp(lo, 0xB1, 0xF, 0xF, false); ohi = __builtin_amdgcn_mov_dpp(hi, 0xB1, 0xF, 0xF, false); break;   // quad_perm [1,0,3,2]
+    case 1: olo = __builtin_amdgcn_mov_dpp(lo, 0x4E, 0xF, 0xF, false); ohi = __builtin_amdgcn_mov_dpp(hi, 0x4E, 0xF, 0xF, false); break;   // quad_perm [2,3,0,1]
+    case 2: olo = __builtin_amdgcn_mov_dpp(lo, 0x141, 0xF, 0xF, false); ohi = __builtin_amdgcn_mov_dpp(hi, 0x141, 0xF, 0xF, false); break; // row_half_mirror
+    default: olo = __builtin_amdgcn_mov_dpp(lo, 0x140, 0xF, 0xF, false); ohi = __builtin_amdgcn_mov_dpp(hi, 0x140, 0xF, 0xF, false); break; // row_mirror
   }
-  const bool take = ok > k || (ok == k && oi > i);
-  k = take ? ok : k;
-  i = take ? oi : i;
+  const uint64_t o = ((uint64_t)ohi << 32) | olo;
+  return o > v ? o : v;
+}
+
+__device__ __forceinline__ uint64_t rt_readlane(uint64_t v, int l) {
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((uint32_t)(v >> 32), l);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((uint32_t)v, l);   // no sign extension
+  return ((uint64_t)hi << 32) | lo;
 }
 
 // Picks and weights: one wave per token (4 tokens per workgroup).  Lane l
@@ -135,41 +143,35 @@ __global__ __launch_bounds__(256) void k_router_topk(const float* __restrict__ l
                       __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(sacc), 32))) +
                      __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(sacc), 48));
 
-  uint32_t key[EL];
+  uint64_t cand[EL];   // the lane's untaken candidates (0 once taken or past E)
 #pragma unroll
-  for (int i = 0; i < EL; ++i) key[i] = lane + 64 * i < E ? rt_key(v[i]) : 0u;
-  uint32_t taken = 0;   // bit i: expert lane + 64 i already picked
+  for (int i = 0; i < EL; ++i) {
+    const int e = lane + 64 * i;
+    cand[i] = e < E ? ((uint64_t)rt_key(v[i]) << 32) | (uint32_t)~e : 0ull;
+  }
   int my_id = -1;       // lane j < k: the j-th pick
   float my_v = 0.f;
   for (int j = 0; j < k; ++j) {
-    // the lane's best untaken candidate; (0, 0) when it has none
-    uint32_t bk = 0, bi = 0;
+    uint64_t best = 0;
 #pragma unroll
-    for (int i = 0; i < EL; ++i) {
-      const uint32_t e = (uint32_t)(lane + 64 * i);
-      const uint32_t ni = ~e;
-      const bool ok = e < (uint32_t)E && !((taken >> i) & 1u);
-      const bool take = ok && (key[i] > bk || (key[i] == bk && ni > bi) || bi == 0);
-      bk = take ? key[i] : bk;
-      bi = take ? ni : bi;
-    }
+    for (int i = 0; i < EL; ++i) best = cand[i] > best ? cand[i] : best;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) rt_max_step(bk, bi, c);
+    for (int c = 0; c < 4; ++c) best = rt_max_step(best, c);
     // rows 0..3: the best of the four row leaders (uniform)
-    uint32_t wk = __builtin_amdgcn_readlane(bk, 0), wi = __builtin_amdgcn_readlane(bi, 0);
+    uint64_t w = rt_readlane(best, 0);
 #pragma unroll
     for (int r = 1; r < 4; ++r) {
-      const uint32_t rk = __builtin_amdgcn_readlane(bk, 16 * r), ri = __builtin_amdgcn_readlane(bi, 16 * r);
-      if (rk > wk || (rk == wk && ri > wi)) {
-        wk = rk;
-        wi = ri;
-      }
+      const uint64_t o = rt_readlane(best, 16 * r);
+      w = o > w ? o : w;
     }
-    const int pick = (int)~wi;
-    if ((pick & 63) == lane) taken |= 1u << (pick >> 6);
+    const int pick = (int)~(uint32_t)w;
+    const bool mine = (pick & 63) == lane;
+#pragma unroll
+    for (int i = 0; i < EL; ++i)
+      if (mine && (pick >> 6) == i) cand[i] = 0;
     if (lane == j) {
       my_id = pick;
-      my_v = rt_logit(wk);
+      my_v = rt_logit((uint32_t)(w >> 32));
     }
   }
   // the weights: lane j < k holds pick j
