@@ -623,18 +623,24 @@ def greedy_leg(steps, warmup, graph):
         x = bf16_dev(synth.gen_x(synth.rng("greedy", "x"), 1, K))
         y = torch.empty((1, N), dtype=torch.float32, device=DEV)
         idx = torch.empty(1, dtype=torch.int32, device=DEV)
+        aws = torch.empty(q.argmax_ws(N, 1), dtype=torch.uint8, device=DEV)
 
         def head():
             q.gemv(w, x, y, 1)
-            q.argmax(y, N, 1, idx)
+            q.argmax(y, N, 1, idx, ws=aws)
 
-        def argmax_only():
+        def argmax_split():
+            for _ in range(reps):
+                q.argmax(y, N, 1, idx, ws=aws)
+
+        def argmax_one_wg():
             for _ in range(reps):
                 q.argmax(y, N, 1, idx)
         ms, _ = time_calls(head, steps, warmup, graph)
-        msa, _ = time_calls(argmax_only, steps, warmup, graph)
+        msa, _ = time_calls(argmax_split, steps, warmup, graph)
+        ms1, _ = time_calls(argmax_one_wg, steps, warmup, graph)
         r.update({"head_gemv_argmax_us": ms * 1e3, "head_GB_s": d.numel() / (ms * 1e-3) / 1e9,
-                  "argmax_us": msa * 1e3 / reps})
+                  "argmax_us": msa * 1e3 / reps, "argmax_one_workgroup_us": ms1 * 1e3 / reps})
         res[f"layout_{lay}"] = r
         del d
     torch.cuda.empty_cache()

@@ -82,7 +82,9 @@ _lib.q4nx_unpack.argtypes = [ctypes.POINTER(Weight), _P, _P, _P, _P, _P]
 _lib.q4nx_decode.argtypes = [ctypes.POINTER(Weight), _P, _P]
 _lib.q4nx_repack_q4k_to_q41.argtypes = [ctypes.POINTER(Weight), _P, ctypes.c_size_t, _P]
 _lib.q4nx_q8_rows.argtypes = [ctypes.POINTER(Weight), _P, _I, _P, _P]
-_lib.q4nx_argmax.argtypes = [_P, _I, _I, _I, _P, _P, _P]
+_lib.q4nx_argmax.argtypes = [_P, _I, _I, _I, _P, _P, _P, ctypes.c_size_t, _P]
+_lib.q4nx_argmax_ws.argtypes = [_I, _I]
+_lib.q4nx_argmax_ws.restype = ctypes.c_size_t
 _lib.q4nx_moe_router.argtypes = [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P]
 _lib.q4nx_plan_create.argtypes = [ctypes.POINTER(GemvJob), ctypes.POINTER(ctypes.c_int32), _I, _I,
                                   ctypes.POINTER(ctypes.c_void_p)]
@@ -298,9 +300,16 @@ def q8_rows(w: Weight, ids, T: int, out, stream=None) -> None:
     _check(_lib.q4nx_q8_rows(ctypes.byref(w), _ptr(ids), T, _ptr(out), _stream(stream)))
 
 
-def argmax(y, n: int, M: int, idx, val=None, ldy: int | None = None, stream=None) -> None:
-    """idx[m] = index of the largest of y[m][:n] (lowest on ties, NaNs skipped)."""
-    _check(_lib.q4nx_argmax(_ptr(y), n, n if ldy is None else ldy, M, _ptr(idx), _ptr(val),
+def argmax_ws(n: int, M: int) -> int:
+    return _lib.q4nx_argmax_ws(n, M)
+
+
+def argmax(y, n: int, M: int, idx, val=None, ldy: int | None = None, ws=None, stream=None,
+           ws_bytes: int | None = None) -> None:
+    """idx[m] = index of the largest of y[m][:n] (lowest on ties, NaNs skipped);
+    with a workspace (argmax_ws bytes) the rows are split over many workgroups."""
+    _check(_lib.q4nx_argmax(_ptr(y), n, n if ldy is None else ldy, M, _ptr(idx), _ptr(val), _ptr(ws),
+                            (_nbytes(ws) if ws is not None else 0) if ws_bytes is None else ws_bytes,
                             _stream(stream)))
 
 

@@ -733,13 +733,25 @@ int q4nx_q8_rows(const q4nx_weight* w, const int32_t* ids, int T, float* out, vo
   return hip_status(e, "q8_rows launch");
 }
 
-int q4nx_argmax(const float* y, int n, int ldy, int M, int32_t* idx, float* val, void* stream) {
+size_t q4nx_argmax_ws(int n, int M) {
+  if (n < 1 || M < 1 || M > 65535) return 0;
+  return (size_t)M * q4nx::argmax_parts(n) * 8;
+}
+
+int q4nx_argmax(const float* y, int n, int ldy, int M, int32_t* idx, float* val, void* ws,
+                size_t ws_bytes, void* stream) {
   if (!y || !idx) return fail(Q4NX_E_ARG, "argmax: null y or idx");
   if (n < 1 || ldy < n || M < 1 || M > 65535)
     return fail(Q4NX_E_ARG, "argmax: n = %d, ldy = %d, M = %d (need 1 <= n <= ldy, 1 <= M <= 65535)", n, ldy, M);
   if (!aligned(y, 4) || !aligned(idx, 4) || (val && !aligned(val, 4)))
     return fail(Q4NX_E_ALIGN, "argmax: y, idx and val must be 4-byte aligned");
-  const hipError_t e = q4nx::launch_argmax(y, n, ldy, M, idx, val, static_cast<hipStream_t>(stream));
+  if (ws) {
+    const size_t need = q4nx_argmax_ws(n, M);
+    if (ws_bytes < need)
+      return fail(Q4NX_E_WORKSPACE, "argmax: workspace of %zu bytes, %zu needed", ws_bytes, need);
+    if (!aligned(ws, 8)) return fail(Q4NX_E_ALIGN, "argmax: workspace not 8-byte aligned");
+  }
+  const hipError_t e = q4nx::launch_argmax(y, n, ldy, M, idx, val, ws, static_cast<hipStream_t>(stream));
   return hip_status(e, "argmax launch");
 }
 

@@ -253,8 +253,106 @@ __global__ __launch_bounds__(1024) void k_argmax(const float* __restrict__ y, in
   }
 }
 
-hipError_t launch_argmax(const float* y, int n, int ldy, int M, int32_t* idx, float* val, hipStream_t s) {
-  hipLaunchKernelGGL(k_argmax, dim3(M), dim3(1024), 0, s, y, n, ldy, idx, val);
+// Split form: a row is cut into slices of kArgmaxSlice values, one 256-thread
+// workgroup each (so a logits row streams through many CUs; one CU draws only
+// a few tens of GB/s), whose best candidate goes to the workspace as one
+// 64-bit key; a second launch takes the largest key of each row.  Key of value
+// v at index i: the order-preserving bits of v (zeros of either sign alike) in
+// the high word, ~i in the low one, so the larger key is the larger value and,
+// among equal values, the lower index; 0 means no candidate (NaN or none).
+__device__ __forceinline__ uint64_t am_key(float v, int i) {
+  if (v != v) return 0ull;
+  const uint32_t b = v == 0.f ? 0u : __float_as_uint(v);
+  const uint32_t k = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((uint64_t)k << 32) | (uint32_t)~i;
+}
+
+__device__ __forceinline__ uint64_t am_wave_max(uint64_t v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const uint64_t o = __shfl_xor(v, off);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+__global__ __launch_bounds__(256) void k_argmax_part(const float* __restrict__ y, int n, int ldy,
+                                                     uint64_t* __restrict__ ws) {
+  constexpr int PP = kArgmaxSlice / 4 / 256;   // 16-byte pieces per thread
+  __shared__ uint64_t wbest[4];
+  const int g = blockIdx.x, m = blockIdx.y, t = threadIdx.x;
+  const float* row = y + (size_t)m * ldy;
+  uint64_t best = 0;
+  const int i0 = g * kArgmaxSlice;
+  if ((reinterpret_cast<uintptr_t>(row) & 15) == 0 && n < (1 << 28)) {
+    // pieces wholly inside the row; the one that crosses its end is read by value
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(row, (uint32_t)n * 4u);
+    f32x4 v[PP];
+#pragma unroll
+    for (int u = 0; u < PP; ++u)
+      v[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                           rs, (uint32_t)(i0 + 4 * (t + 256 * u)) * 4u, 0, 0));
+#pragma unroll
+    for (int u = 0; u < PP; ++u) {
+      const int e0 = i0 + 4 * (t + 256 * u);
+      if (e0 + 3 < n) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const uint64_t kk = am_key(v[u][c], e0 + c);
+          best = kk > best ? kk : best;
+        }
+      } else {
+        for (int e = e0; e < n; ++e) {
+          const uint64_t kk = am_key(row[e], e);
+          best = kk > best ? kk : best;
+        }
+      }
+    }
+  } else {
+    const int i1 = min(n, i0 + kArgmaxSlice);
+    for (int e = i0 + t; e < i1; e += 256) {
+      const uint64_t kk = am_key(row[e], e);
+      best = kk > best ? kk : best;
+    }
+  }
+  best = am_wave_max(best);
+  if ((t & 63) == 0) wbest[t >> 6] = best;
+  __syncthreads();
+  if (t == 0) {
+    uint64_t b = wbest[0];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) b = wbest[w] > b ? wbest[w] : b;
+    ws[(size_t)m * gridDim.x + g] = b;
+  }
+}
+
+__global__ __launch_bounds__(64) void k_argmax_final(const float* __restrict__ y, int ldy, int parts,
+                                                     const uint64_t* __restrict__ ws,
+                                                     int32_t* __restrict__ idx, float* __restrict__ val) {
+  const int m = blockIdx.x, lane = threadIdx.x;
+  uint64_t best = 0;
+  for (int g = lane; g < parts; g += 64) {
+    const uint64_t kk = ws[(size_t)m * parts + g];
+    best = kk > best ? kk : best;
+  }
+  best = am_wave_max(best);
+  if (lane == 0) {
+    const int i = best ? (int)~(uint32_t)best : -1;
+    idx[m] = i;
+    if (val) val[m] = i >= 0 ? y[(size_t)m * ldy + i] : __builtin_nanf("");
+  }
+}
+
+hipError_t launch_argmax(const float* y, int n, int ldy, int M, int32_t* idx, float* val, void* ws,
+                         hipStream_t s) {
+  if (!ws) {
+    hipLaunchKernelGGL(k_argmax, dim3(M), dim3(1024), 0, s, y, n, ldy, idx, val);
+    return hipGetLastError();
+  }
+  const int parts = argmax_parts(n);
+  hipLaunchKernelGGL(k_argmax_part, dim3(parts, M), dim3(256), 0, s, y, n, ldy, static_cast<uint64_t*>(ws));
+  hipLaunchKernelGGL(k_argmax_final, dim3(M), dim3(64), 0, s, y, ldy, parts, static_cast<const uint64_t*>(ws),
+                     idx, val);
   return hipGetLastError();
 }
 

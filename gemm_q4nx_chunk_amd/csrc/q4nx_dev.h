@@ -123,7 +123,12 @@ hipError_t launch_decode(int kind, const uint8_t* w, int TR, int TC, float* out,
 hipError_t launch_repack_q4k(const uint8_t* w, int tiles, uint8_t* out, hipStream_t s);
 hipError_t launch_q8_rows(int kind, const uint8_t* w, int rows, int TC, const int32_t* ids, int T,
                           float* out, hipStream_t s);
-hipError_t launch_argmax(const float* y, int n, int ldy, int M, int32_t* idx, float* val, hipStream_t s);
+// Split argmax: slices of this many values per workgroup, one 8-byte key each
+// in the workspace.
+constexpr int kArgmaxSlice = 4096;
+inline int argmax_parts(int n) { return (n + kArgmaxSlice - 1) / kArgmaxSlice; }
+hipError_t launch_argmax(const float* y, int n, int ldy, int M, int32_t* idx, float* val, void* ws,
+                         hipStream_t s);
 hipError_t launch_moe_router(const uint16_t* R, const uint16_t* X, int T, int D, int E, int k,
                              int renorm, int32_t* ids, float* p, float* logits, hipStream_t s);
 

@@ -312,10 +312,19 @@ int q4nx_q8_rows(const q4nx_weight* w, const int32_t* ids, int T, float* out, vo
 /*
  * Greedy pick after the lm_head GEMV: for each row m of y (fp32, row stride
  * ldy), the index of the largest of its first n values, the lowest index
- * among equal maxima; NaNs are skipped, and a row of only NaNs gives -1.
- *   idx  DEVICE int32 [M];  val DEVICE fp32 [M] or NULL (the maximum)
+ * among equal maxima (zeros of either sign are equal); NaNs are skipped, and
+ * a row of only NaNs gives -1.
+ *   y    DEVICE fp32, 4-byte aligned; 1 <= n <= ldy, 1 <= M <= 65535
+ *   idx  DEVICE int32 [M];  val DEVICE fp32 [M] or NULL (y at the pick)
+ *   ws   DEVICE workspace of at least q4nx_argmax_ws(n, M) bytes, 8-byte
+ *        aligned, or NULL.  With it each row is cut into slices of 4096
+ *        values, one workgroup each, and a second launch combines the slices;
+ *        without it one workgroup reads the whole row.  Same result either way.
+ *        Nothing in it needs initialising; calls that share it must not overlap.
  */
-int q4nx_argmax(const float* y, int n, int ldy, int M, int32_t* idx, float* val, void* stream);
+size_t q4nx_argmax_ws(int n, int M);
+int q4nx_argmax(const float* y, int n, int ldy, int M, int32_t* idx, float* val, void* ws,
+                size_t ws_bytes, void* stream);
 
 /*
  * MoE router on the device (Strata article, section 2: per token the router

@@ -201,6 +201,12 @@ def test_rows_and_argmax_checks(q):
     _expect(q, q.E_ARG, q.argmax, 0x2000, 10, 1, 0x3000, ldy=9, stream=0)
     _expect(q, q.E_ARG, q.argmax, 0x2000, 10, 0, 0x3000, stream=0)
     _expect(q, q.E_ALIGN, q.argmax, 0x2002, 10, 1, 0x3000, stream=0)
+    # split form: one 8-byte key per 4096-value slice per row
+    assert q.argmax_ws(151936, 1) == 38 * 8
+    assert q.argmax_ws(4096, 3) == 3 * 8 and q.argmax_ws(4097, 3) == 6 * 8
+    assert q.argmax_ws(0, 1) == 0 and q.argmax_ws(10, 0) == 0
+    _expect(q, q.E_WORKSPACE, q.argmax, 0x2000, 5000, 1, 0x3000, ws=0x4000, ws_bytes=15, stream=0)
+    _expect(q, q.E_ALIGN, q.argmax, 0x2000, 5000, 1, 0x3000, ws=0x4004, ws_bytes=16, stream=0)
 
 
 def test_router_checks(q):

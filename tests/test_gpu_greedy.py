@@ -39,7 +39,16 @@ def _argmax_ref(y):
     return int(np.nanargmax(y))
 
 
-def test_argmax_ties_nans_and_rows():
+def _argmax(y, n, M, idx, val=None, ldy=None, split=False):
+    """q4nx_argmax with (split) or without a workspace."""
+    ws = None
+    if split:
+        ws = torch.full((q().argmax_ws(n, M),), 0xAB, dtype=torch.uint8, device="cuda")  # stale contents
+    q().argmax(y, n, M, idx, val, ldy=ldy, ws=ws)
+
+
+@pytest.mark.parametrize("split", [False, True])
+def test_argmax_ties_nans_and_rows(split):
     g = np.random.default_rng(7)
     M, n, ldy = 5, 3000, 3072
     y = g.standard_normal((M, ldy)).astype(np.float32)
@@ -51,7 +60,7 @@ def test_argmax_ties_nans_and_rows():
     y[4, n:] = 100.0                   # past n: ignored
     idx = torch.zeros(M, dtype=torch.int32, device="cuda")
     val = torch.zeros(M, dtype=torch.float32, device="cuda")
-    q().argmax(dev_f32(y), n, M, idx, val, ldy=ldy)
+    _argmax(dev_f32(y), n, M, idx, val, ldy=ldy, split=split)
     got = host(idx)
     for m in range(M):
         assert got[m] == _argmax_ref(y[m, :n]), m
@@ -70,16 +79,21 @@ def test_greedy_head_q8(layout):
     y = torch.empty((2, N), dtype=torch.float32, device="cuda")
     q().gemv(w, dev_bf16(x), y, 2)
     idx = torch.zeros(2, dtype=torch.int32, device="cuda")
+    idx2 = torch.zeros(2, dtype=torch.int32, device="cuda")
     q().argmax(y, N, 2, idx)
+    _argmax(y, N, 2, idx2, split=True)
     yh, got = host(y), host(idx)
+    np.testing.assert_array_equal(host(idx2), got)
     yr, a = oracle.gemv_ref(oracle.weights_exact(ch, "q8", N, K, layout), x)
     for m in range(2):
         assert got[m] == _argmax_ref(yh[m])
         assert yr[m, got[m]] >= yr[m].max() - 2 * 2e-3 * a[m, got[m]] - 2 * 2e-3 * a[m, np.argmax(yr[m])]
 
 
-@pytest.mark.parametrize("n,ldy", [(3001, 3003), (3001, 3004), (5, 5), (1, 1), (151936, 151936)])
-def test_argmax_tail_and_unaligned_rows(n, ldy):
+@pytest.mark.parametrize("split", [False, True])
+@pytest.mark.parametrize("n,ldy", [(3001, 3003), (3001, 3004), (5, 5), (1, 1), (4096, 4096), (4099, 4100),
+                                   (151936, 151936)])
+def test_argmax_tail_and_unaligned_rows(n, ldy, split):
     """Rows whose length is not a multiple of 4, rows that start off a 16-byte
     boundary, and the full 151936-wide head: maxima in the last element and a
     tie between the first and last elements."""
@@ -92,8 +106,24 @@ def test_argmax_tail_and_unaligned_rows(n, ldy):
     y[2, g.integers(0, n)] = 70.0
     idx = torch.zeros(M, dtype=torch.int32, device="cuda")
     val = torch.zeros(M, dtype=torch.float32, device="cuda")
-    q().argmax(dev_f32(y), n, M, idx, val, ldy=ldy)
+    _argmax(dev_f32(y), n, M, idx, val, ldy=ldy, split=split)
     got, gv = host(idx), host(val)
     for m in range(M):
         assert got[m] == _argmax_ref(y[m, :n]), m
         assert gv[m] == y[m, got[m]]
+
+
+@pytest.mark.parametrize("split", [False, True])
+def test_argmax_signed_zeros_are_equal(split):
+    """A row whose maximum is zero, held as -0.0 before +0.0 (and the reverse):
+    the first of them wins, and val is the value stored there."""
+    n = 9000
+    y = -np.abs(np.random.default_rng(3).standard_normal((2, n))).astype(np.float32) - 1.0
+    y[0, 4500], y[0, 8000] = -0.0, 0.0
+    y[1, 100], y[1, 5000] = 0.0, -0.0
+    idx = torch.zeros(2, dtype=torch.int32, device="cuda")
+    val = torch.zeros(2, dtype=torch.float32, device="cuda")
+    _argmax(dev_f32(y), n, 2, idx, val, split=split)
+    got, gv = host(idx), host(val)
+    assert got.tolist() == [4500, 100]
+    assert np.signbit(gv[0]) and not np.signbit(gv[1])
