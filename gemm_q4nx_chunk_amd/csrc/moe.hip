@@ -346,13 +346,15 @@ __device__ __forceinline__ void moe_route_small(const MoeArgs& a, MoeSmallRoute&
       key = ((uint32_t)(ok ? e : a.n_experts) << 12) | (uint32_t)lane;
     }
     int rank = 0;
-    for (int j = 0; j < P; ++j) rank += __shfl(key, j) < key ? 1 : 0;
+    for (int j = 0; j < P; ++j) rank += (uint32_t)__builtin_amdgcn_readlane(key, j) < key ? 1 : 0;
     const uint64_t bad = __ballot(lane < P && !ok);
     if (lane < P) rt.sorted[rank] = lane;
-    // From here lane s describes sorted position s (LDS is in order within a wave).
+    // From here lane s describes sorted position s (LDS is in order within a wave);
+    // its pair's id comes from the lane that loaded it.
     __builtin_amdgcn_wave_barrier();
     const int pi = lane < P ? rt.sorted[lane] : 0;
-    const int es = lane < P ? a.ids[pi] : -1;
+    const int e_of_pi = __shfl(e, pi);
+    const int es = lane < P ? e_of_pi : -1;
     const bool vs = lane < P && es >= 0 && es < a.n_experts;
     const int eprev = __shfl_up(es, 1);
     const bool start = vs && (lane == 0 || eprev != es);
