@@ -66,12 +66,12 @@ __device__ __forceinline__ void gemm_load(__amdgpu_buffer_rsrc_t rs, uint32_t of
     c.q[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                            rs, off + 128 * n + 64 * h + 16 * q, 0, kNt));
   if constexpr (KIND == KIND_Q4_1) {
-    c.meta = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 4096 + 32 * n + 16 * h, 0, 0));
+    c.meta = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 4096 + 32 * n + 16 * h, 0, kNt));
   } else {
-    const u32x2 scmn = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, off + 4096 + 16 * n + 8 * h, 0, 0));
+    const u32x2 scmn = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, off + 4096 + 16 * n + 8 * h, 0, kNt));
     c.meta.x = scmn.x;
     c.meta.y = scmn.y;
-    c.meta.z = __builtin_amdgcn_raw_buffer_load_b32(rs, off + 4608 + 4 * n, 0, 0);
+    c.meta.z = __builtin_amdgcn_raw_buffer_load_b32(rs, off + 4608 + 4 * n, 0, kNt);
     c.meta.w = 0;
   }
 }

@@ -254,7 +254,7 @@ __device__ __forceinline__ void q8x_load_rs(__amdgpu_buffer_rsrc_t rs, uint32_t 
   for (int i = 0; i < 8; ++i)
     c.pc[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                             rs, off + Q8Lines<KIND>::piece(lane, i), 0, kNt));
-  c.dp = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, off + 8192 + 8 * lane, 0, 0));
+  c.dp = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, off + 8192 + 8 * lane, 0, kNt));
 }
 
 // acc[rho][m] += sum over the lane's groups q of d(16h + rho, g0 + q) *

@@ -37,13 +37,13 @@ __device__ __forceinline__ void q4_load(const uint8_t* __restrict__ ck, int lane
 #pragma unroll
   for (int i = 0; i < 4; ++i) c.q[i] = load_nt16(ck + 1024 * i + 16 * lane);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 4; ++i) {   // metadata nontemporal too: weights are read once
     if constexpr (KIND == KIND_Q4_1) {
-      c.meta[i] = *reinterpret_cast<const uint32_t*>(ck + 4096 + 256 * i + 4 * lane);
+      c.meta[i] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(ck + 4096 + 256 * i + 4 * lane));
       c.rowsm[i] = 0;
     } else {
-      c.meta[i] = *reinterpret_cast<const uint16_t*>(ck + 4096 + 128 * i + 2 * lane);
-      c.rowsm[i] = *reinterpret_cast<const uint32_t*>(ck + 4608 + 32 * i + 4 * (lane >> 3));
+      c.meta[i] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(ck + 4096 + 128 * i + 2 * lane));
+      c.rowsm[i] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(ck + 4608 + 32 * i + 4 * (lane >> 3)));
     }
   }
 }
@@ -54,7 +54,7 @@ __device__ __forceinline__ void q4_load(const uint8_t* __restrict__ ck, int lane
 template <int KIND, int SL = 4>
 __device__ __forceinline__ void q4_load_rs(__amdgpu_buffer_rsrc_t rs, uint32_t off, int lane,
                                            Q4Chunk<KIND, SL>& c, int i0 = 0) {
-  constexpr int kNt = 2;   // nontemporal: weights are read once
+  constexpr int kNt = 2;   // nontemporal, codes and metadata alike: weights are read once
 #pragma unroll
   for (int i = 0; i < SL; ++i)
     c.q[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 1024 * (i0 + i) + 16 * lane, 0, kNt));
@@ -62,11 +62,11 @@ __device__ __forceinline__ void q4_load_rs(__amdgpu_buffer_rsrc_t rs, uint32_t o
   for (int i = 0; i < SL; ++i) {
     const int si = i0 + i;
     if constexpr (KIND == KIND_Q4_1) {
-      c.meta[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, off + 4096 + 256 * si + 4 * lane, 0, 0);
+      c.meta[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, off + 4096 + 256 * si + 4 * lane, 0, kNt);
       c.rowsm[i] = 0;
     } else {
-      c.meta[i] = __builtin_amdgcn_raw_buffer_load_b16(rs, off + 4096 + 128 * si + 2 * lane, 0, 0);
-      c.rowsm[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, off + 4608 + 32 * si + 4 * (lane >> 3), 0, 0);
+      c.meta[i] = __builtin_amdgcn_raw_buffer_load_b16(rs, off + 4096 + 128 * si + 2 * lane, 0, kNt);
+      c.rowsm[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, off + 4608 + 32 * si + 4 * (lane >> 3), 0, kNt);
     }
   }
 }
@@ -223,8 +223,8 @@ __device__ __forceinline__ void q8_load_rs(__amdgpu_buffer_rsrc_t rs, uint32_t o
   const uint32_t dbase = off + q8_dbase(lane);
 #pragma unroll
   for (int rr = 0; rr < 8; ++rr) {
-    const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(rs, dbase + 32 * rr, 0, 0);
-    const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(rs, dbase + 32 * rr + 16, 0, 0);
+    const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(rs, dbase + 32 * rr, 0, kNt);
+    const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(rs, dbase + 32 * rr + 16, 0, kNt);
     c.dv[rr] = lo | (hi << 16);
   }
 }
