@@ -58,7 +58,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_q4(const GemvBatch b) {
     if (t < J.TR) {
       float v = 0.f;
       for (int p = 0; p < ks; ++p) v += red[s * ks + p][r][m];
-      J.y[(size_t)m * J.ldy + 32 * t + r] = v;
+      __builtin_nontemporal_store(v, &J.y[(size_t)m * J.ldy + 32 * t + r]);   // written once
     }
   }
 }
@@ -194,7 +194,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_q4x(const GemvBatch b) {
     if (t < NU) {
       float v = 0.f;
       for (int p = 0; p < ks; ++p) v += red[s * ks + p][r][m];
-      J.y[(size_t)m * J.ldy + UR * t + r] = v;
+      __builtin_nontemporal_store(v, &J.y[(size_t)m * J.ldy + UR * t + r]);   // written once
     }
   }
 }
@@ -425,7 +425,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_q8x(const GemvBatch b) {
     if (t < J.TR) {
       float v = 0.f;
       for (int p = 0; p < ks; ++p) v += red[s * ks + p][r][m];
-      J.y[(size_t)m * J.ldy + 32 * t + r] = v;
+      __builtin_nontemporal_store(v, &J.y[(size_t)m * J.ldy + 32 * t + r]);   // written once
     }
   }
 }
@@ -467,7 +467,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_q8(const GemvBatch b) {
     if (t < J.TR) {
       float v = 0.f;
       for (int p = 0; p < ks; ++p) v += red[s * ks + p][r][m];
-      J.y[(size_t)m * J.ldy + 32 * t + r] = v;
+      __builtin_nontemporal_store(v, &J.y[(size_t)m * J.ldy + 32 * t + r]);   // written once
     }
   }
 }
