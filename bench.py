@@ -400,6 +400,10 @@ def gemm_leg(steps, warmup, graph):
     res = {"M64": {"ms_per_block": ms, "TFLOP_s": flops / (ms * 1e-3) / 1e12, "flops": flops,
                    "weight_bytes": nbytes, "GB_s": nbytes / (ms * 1e-3) / 1e9,
                    "pct_mfma_peak": 100 * flops / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+                   # attainable = min(MFMA peak, flops per weight byte x HBM peak)
+                   "attainable_TFLOP_s": min(BF16_MFMA_PEAK_TFLOPS, flops / nbytes * HBM_PEAK_GBS / 1e3),
+                   "pct_attainable": 100 * flops / (ms * 1e-3) / 1e12
+                   / min(BF16_MFMA_PEAK_TFLOPS, flops / nbytes * HBM_PEAK_GBS / 1e3),
                    "pct_hbm_peak": 100 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                    "launches": len(launches)}}
     # roofline of the block GEMM kernel: its launches run back to back, so the timed
