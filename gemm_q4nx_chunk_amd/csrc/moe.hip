@@ -386,7 +386,7 @@ template <int TB>
 __device__ __forceinline__ void moe_stage(const uint16_t* base, const int64_t* rows, int TC, uint32_t* xl) {
   const int R = TB * TC * 8;
   float* sums = reinterpret_cast<float*>(xl + 16 * R);
-  for (int r = threadIdx.x; r < R; r += 256) {
+  for (int r = threadIdx.x; r < R; r += blockDim.x) {
     const int m = r / (TC * 8), rem = r - m * TC * 8;
     const uint16_t* p = base + rows[m];
     XRaw<1> raw;
@@ -548,18 +548,18 @@ __global__ __launch_bounds__(256) void k_moe_gateup_s(MoeArgs a) {
 }
 
 // Items: nseg * (D / 32 / rpw_r) routed row groups, then the shared ones; ks
-// waves split a tile row's chunks, rpw = 4 / ks rows per workgroup.
-template <int KIND, int TB, bool SMALL>
-__global__ __launch_bounds__(256) void k_moe_down_s(MoeArgs a, int ks_r, int ks_s) {
+// waves split a tile row's chunks, rpw = WAVES / ks rows per workgroup.
+template <int KIND, int TB, bool SMALL, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void k_moe_down_s(MoeArgs a, int ks_r, int ks_s) {
   extern __shared__ __attribute__((aligned(16))) uint32_t xl[];
-  __shared__ float red[4][32][TB];
+  __shared__ float red[WAVES][32][TB];
   __shared__ int64_t s_rows[TB];   // the batch's activation rows (element offsets)
   __shared__ MoeSmallRoute rt;
   if constexpr (SMALL) moe_route_small(a, rt);
   const int nseg = SMALL ? rt.nseg : (int)a.hdr[1];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int rows = a.D / 32, P = a.T * a.k;
-  const int gr = rows / (4 / ks_r), gs = a.Ds ? rows / (4 / ks_s) : 0;
+  const int gr = rows / (WAVES / ks_r), gs = a.Ds ? rows / (WAVES / ks_s) : 0;
   const int n_items = nseg * gr + gs;
   uint32_t kMask = 0x000F000Fu, kMagic = 0x43004300u;
   asm volatile("" : "+s"(kMask));
@@ -574,7 +574,7 @@ __global__ __launch_bounds__(256) void k_moe_down_s(MoeArgs a, int ks_r, int ks_
     } else {
       grp = item - nseg * gr;
     }
-    const int ks = shared ? ks_s : ks_r, rpw = 4 / ks;
+    const int ks = shared ? ks_s : ks_r, rpw = WAVES / ks;
     const int TC = (shared ? a.Ds : a.De) / 256;
     const int slot = wave / ks, part = wave % ks;
     const int tr0 = grp * rpw, tr = tr0 + slot;
@@ -612,7 +612,7 @@ __global__ __launch_bounds__(256) void k_moe_down_s(MoeArgs a, int ks_r, int ks_
           for (int m = 0; m < TB; ++m) red[wave][8 * i + (lane >> 3)][m] = acc[i][m];
       }
       __syncthreads();
-      for (int idx = threadIdx.x; idx < rpw * 32 * TB; idx += 256) {
+      for (int idx = threadIdx.x; idx < rpw * 32 * TB; idx += 64 * WAVES) {
         const int s2 = idx / (32 * TB), rem = idx - s2 * 32 * TB;
         const int r = rem / TB, m = rem - r * TB;
         const int t_row = tr0 + s2;
@@ -703,11 +703,11 @@ __global__ __launch_bounds__(256) void k_moe_gateup(MoeArgs a) {
   }
 }
 
-// ks waves split one tile row's chunks; 4/ks tile rows per workgroup.
-template <int KIND, int TB>
-__global__ __launch_bounds__(256) void k_moe_down(MoeArgs a, int ks_r, int ks_s) {
+// ks waves split one tile row's chunks; WAVES/ks tile rows per workgroup.
+template <int KIND, int TB, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void k_moe_down(MoeArgs a, int ks_r, int ks_s) {
   extern __shared__ __attribute__((aligned(16))) uint32_t xl[];
-  __shared__ float red[4][32][TB];
+  __shared__ float red[WAVES][32][TB];
   __shared__ int64_t s_rows[TB];   // the batch's activation rows (element offsets)
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int rows = a.D / 32;
@@ -718,8 +718,8 @@ __global__ __launch_bounds__(256) void k_moe_down(MoeArgs a, int ks_r, int ks_s)
   const int nbr = (int)a.hdr[2];
   for (int item = blockIdx.x;; item += gridDim.x) {
     MoeItem it;
-    if (!moe_item<TB>(a, nbr, item, rows, rows, 4 / ks_r, 4 / ks_s, true, it)) break;
-    const int ks = it.shared ? ks_s : ks_r, rpw = 4 / ks;
+    if (!moe_item<TB>(a, nbr, item, rows, rows, WAVES / ks_r, WAVES / ks_s, true, it)) break;
+    const int ks = it.shared ? ks_s : ks_r, rpw = WAVES / ks;
     const int TC = (it.shared ? a.Ds : a.De) / 256;
     const int slot = wave / ks, part = wave % ks;
     const int tr = it.tr + slot < rows ? it.tr + slot : rows - 1;   // past the last row: redone, unstored
@@ -751,7 +751,7 @@ __global__ __launch_bounds__(256) void k_moe_down(MoeArgs a, int ks_r, int ks_s)
         for (int m = 0; m < TB; ++m) red[wave][8 * i + (lane >> 3)][m] = acc[i][m];
     }
     __syncthreads();
-    for (int idx = threadIdx.x; idx < rpw * 32 * TB; idx += 256) {
+    for (int idx = threadIdx.x; idx < rpw * 32 * TB; idx += 64 * WAVES) {
       const int s2 = idx / (32 * TB), rem = idx - s2 * 32 * TB;
       const int r = rem / TB, m = rem - r * TB;
       const int t_row = it.tr + s2;
@@ -814,8 +814,12 @@ static hipError_t moe_run(const MoeArgs& a, hipStream_t s) {
   const int P = a.T * a.k;
   const int nseg_max = P < a.n_experts ? P : a.n_experts;
   const int tcr = a.De / 256, tcs = a.Ds ? a.Ds / 256 : 1;
-  const int ks_r = tcr >= 4 ? 4 : (tcr >= 2 ? 2 : 1);
-  const int ks_s = tcs >= 4 ? 4 : (tcs >= 2 ? 2 : 1);
+  // Waves per tile row in the down kernels: about two chunks per wave.  (One
+  // chunk per wave, ks = TC up to 4, measured 10% slower at T = 64 and 4%
+  // faster at T = 1.  Both paths must use the same split for a token's bits
+  // not to depend on T.)
+  const int ks_r = tcr >= 8 ? 4 : (tcr >= 4 ? 2 : 1);
+  const int ks_s = tcs >= 8 ? 4 : (tcs >= 4 ? 2 : 1);
   const int rows = a.D / 32;
   // Few pairs (decode): weight-stationary kernels with routing in every
   // workgroup, when a batch's prepared rows fit in 64 KB of LDS.  Many pairs
@@ -828,10 +832,16 @@ static hipError_t moe_run(const MoeArgs& a, hipStream_t s) {
   const bool small = P <= kMoeSmallPairs;
   if (small && xl_gu <= 65536 && xl_dn <= 65536) {
     const int gu_items = nseg_max * (a.De / 32) + a.Ds / 32;
-    const int dn_items = nseg_max * (rows / (4 / ks_r)) + (a.Ds ? rows / (4 / ks_s) : 0);
+    // decode-sized down: two-wave workgroups when a tile row takes at most two waves
+    // (more, smaller workgroups for a latency-bound launch), else four
+    const int dn_waves = (ks_r <= 2 && ks_s <= 2) ? 2 : 4;
+    const int dn_items = nseg_max * (rows / (dn_waves / ks_r)) + (a.Ds ? rows / (dn_waves / ks_s) : 0);
     const dim3 g_gu(gu_items < 4096 ? gu_items : 4096), g_dn(dn_items < 4096 ? dn_items : 4096);
     hipLaunchKernelGGL((k_moe_gateup_s<KIND, TB, true>), g_gu, dim3(256), xl_gu, s, a);
-    hipLaunchKernelGGL((k_moe_down_s<KIND, TB, true>), g_dn, dim3(256), xl_dn, s, a, ks_r, ks_s);
+    if (dn_waves == 2)
+      hipLaunchKernelGGL((k_moe_down_s<KIND, TB, true, 2>), g_dn, dim3(128), xl_dn, s, a, ks_r, ks_s);
+    else
+      hipLaunchKernelGGL((k_moe_down_s<KIND, TB, true, 4>), g_dn, dim3(256), xl_dn, s, a, ks_r, ks_s);
     hipLaunchKernelGGL(k_moe_combine, dim3((a.D + 255) / 256, a.T), dim3(256), 0, s, a);
     return hipGetLastError();
   }
@@ -841,8 +851,11 @@ static hipError_t moe_run(const MoeArgs& a, hipStream_t s) {
   const int gu_items = nb_r * (a.De / 32) + nb_s * (a.Ds / 32);
   hipLaunchKernelGGL((k_moe_gateup<KIND, TB>), dim3(gu_items < 4096 ? gu_items : 4096), dim3(256),
                      xl_gu, s, a);
-  const int dn_items = nb_r * (rows / (4 / ks_r)) + nb_s * (rows / (4 / ks_s));
-  hipLaunchKernelGGL((k_moe_down<KIND, TB>), dim3(dn_items < 4096 ? dn_items : 4096), dim3(256),
+  // prompt-block down: four-wave workgroups (two fit a CU at this register
+  // count; eight-wave ones, one per CU, measured 20% slower)
+  constexpr int kDnWaves = 4;
+  const int dn_items = nb_r * (rows / (kDnWaves / ks_r)) + nb_s * (rows / (kDnWaves / ks_s));
+  hipLaunchKernelGGL((k_moe_down<KIND, TB, kDnWaves>), dim3(dn_items < 4096 ? dn_items : 4096), dim3(64 * kDnWaves),
                      xl_dn, s, a, ks_r, ks_s);
   hipLaunchKernelGGL(k_moe_combine, dim3((a.D + 255) / 256, a.T), dim3(256), 0, s, a);
   return hipGetLastError();
