@@ -3,9 +3,11 @@
 // Decode reads every weight once per token and does two flops with it, so the
 // kernel is bound by HBM bandwidth (Strata article, section 1: decode speed is
 // set by the bytes of weights read per token).  The design keeps the weight
-// stream as wide 16-byte nontemporal loads of whole chunks, keeps x in
-// registers, unpacks and scales in registers, and leaves the ALU work per
-// weight small enough to hide under the stream.
+// stream as wide 16-byte nontemporal loads of whole chunks (metadata included),
+// keeps x in registers (k_gemv_q4) or prepared once per workgroup in LDS (the
+// default k_gemv_q4x / k_gemv_q8x), unpacks and scales in registers, leaves
+// the ALU work per weight small enough to hide under the stream, and writes y
+// with nontemporal stores (it is read by a later launch, never by this one).
 //
 // Work split: a workgroup of WAVES waves (4 for launches with many tile rows,
 // 16 for small ones, where latency rather than bandwidth sets the time) owns
