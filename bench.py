@@ -758,6 +758,8 @@ def main():
             legs[f"mixed_q4k_q8{lay}"] = r
             del st
             torch.cuda.empty_cache()
+    if "kinds" in LEGS:   # before the MoE leg, whose 48 GB of arenas come and go
+        legs["lm_head_shape_per_kind"] = kinds_leg(max(3, args.steps // 2), 2, graph)
     if "gemm" in LEGS:
         legs["block_gemm_8b"] = gemm_leg(max(3, args.steps // 4), 2, graph)
         torch.cuda.empty_cache()
@@ -765,8 +767,6 @@ def main():
         legs["moe_512x10"] = moe_leg(max(3, args.steps // 2), 2, graph)
     if "single" in LEGS:
         legs["single_gemv_1024"] = single_leg()
-    if "kinds" in LEGS:
-        legs["lm_head_shape_per_kind"] = kinds_leg(max(3, args.steps // 2), 2, graph)
     if "repack" in LEGS:
         legs["repack_q4k_8b_gate_up"] = repack_leg(args.steps, 2, graph)
     if "greedy" in LEGS:
