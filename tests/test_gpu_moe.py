@@ -252,3 +252,22 @@ def test_moe_512x10_layer_full_size(T):
     sel = [0] if T == 1 else [0, 31, 63]
     sub = {name: (v[sel] if name not in ("err",) else v) for name, v in r.items()}
     _check_stages(layer, X[sel], ids[sel], p[sel], sub)
+
+
+@pytest.mark.parametrize("T,k", [(1024, 4), (4096, 1)])
+def test_maximum_pairs(T, k):
+    """T * k at its limit of 4096 pairs (the sort in one workgroup's LDS): every
+    token's output against the oracle's slot-by-slot sum on a sample of tokens,
+    and a token's bits equal to the same token routed alone."""
+    layer = Layer("maxpairs", "q4_1", 16, 512, 256, 256)
+    g = synth.rng("gpu-moe", "maxpairs", T, k)
+    ids, p = synth.gen_router(g, T, 16, k, 1.1)
+    X = synth.gen_x(g, T, 512)
+    r = layer.run(X, ids, p)
+    assert r["err"] == 0
+    sel = [0, 1, T // 2, T - 1]
+    sub = {name: (v[sel] if name != "err" else v) for name, v in r.items()}
+    _check_stages(layer, X[sel], ids[sel], p[sel], sub)
+    for t in (0, T - 1):
+        one = layer.run(X[t:t + 1], ids[t:t + 1], p[t:t + 1], dbg=False)
+        np.testing.assert_array_equal(one["y"][0].view(np.uint32), r["y"][t].view(np.uint32))
