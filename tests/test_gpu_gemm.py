@@ -217,3 +217,19 @@ def test_split_k_graph_replays_with_new_inputs():
         torch.cuda.synchronize()
         np.testing.assert_array_equal(host(Y).view(np.uint32), eager[i].view(np.uint32))
     assert torch.count_nonzero(ws[:4 * 256]).item() == 0
+
+
+@pytest.mark.parametrize("M", [5, 64])
+def test_gemm_batched_at_the_job_limit(M):
+    """Eight jobs in one call (the API's limit) with rows from 32 to 512: each against the oracle."""
+    K = 768
+    shapes = [32, 512, 64, 96, 256, 32, 160, 128]
+    chs = [_gen("q4_k", N, K, f"lim{i}") for i, N in enumerate(shapes)]
+    X = synth.gen_x(synth.rng("gpu-gemm", "limX", M), M, K)
+    ws_ = [weight(dev_u8(c), N, K, "q4_k") for c, N in zip(chs, shapes)]
+    Ys = [torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda") for N in shapes]
+    jobs = list(zip(ws_, Ys))
+    q().gemm_batched(jobs, dev_bf16(X), M, _ws_bytes(q().gemm_batched_ws(jobs)))
+    for c, N, Y in zip(chs, shapes, Ys):
+        yr, a = oracle.gemv_ref(oracle.weights_exact(c, "q4_k", N, K), X)
+        assert oracle.tol_ratio(host(Y), yr, a) <= 1.0, N

@@ -217,3 +217,23 @@ def test_verify_window_slot_invariance(kind, layout, M):
     y = gemv(d, N, K, kind, x, layout)
     yp = gemv(d, N, K, kind, x[perm], layout)
     np.testing.assert_array_equal(yp.view(np.uint32), y[perm].view(np.uint32))
+
+
+@pytest.mark.parametrize("M", [1, 2])
+def test_batched_at_the_job_limit(M):
+    """64 jobs in one call (the API's limit), all three kinds and both Q8 layouts
+    mixed, of varied shapes: each job's result against the oracle."""
+    g = np.random.default_rng(64 + M)
+    kinds = [("q4_1", None), ("q4_k", None), ("q8", "A"), ("q8", "B")]
+    jobs, refs = [], []
+    for i in range(64):
+        kind, lay = kinds[i % 4]
+        N, K = 32 * int(g.integers(1, 5)), 256 * int(g.integers(1, 4))
+        ch = _gen(kind, lay, N, K, f"lim{M}-{i}")
+        x = synth.gen_x(synth.rng("gpu-gemv", "limx", M, i), M, K)
+        y = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+        jobs.append((weight(dev_u8(ch), N, K, kind, lay), dev_bf16(x), y))
+        refs.append((ch, kind, lay, N, K, x, y))
+    q().gemv_batched(jobs, M)
+    for ch, kind, lay, N, K, x, y in refs:
+        _check(host(y), ch, kind, N, K, x, lay)
