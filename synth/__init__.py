@@ -161,6 +161,33 @@ def gen_x(g: np.random.Generator, M: int, K: int, std: float = 1.0) -> np.ndarra
     return bf16_bits(g.standard_normal((M, K), dtype=np.float32) * np.float32(std))
 
 
+def gen_gguf(g: np.random.Generator, gtype: int, N: int, K: int, d_std: float = 0.02) -> np.ndarray:
+    """A GGUF 4-bit tensor [N, K] as raw bytes (uint8): Q4_0 (type 2, 18-byte
+    blocks of 32), Q4_1 (3, 20-byte blocks) or Q4_K (12, 144-byte super-blocks
+    of 256), each row K/32 (K/256) consecutive blocks, fields little-endian.
+    Codes and Q4_K's packed 6-bit scales are uniform random bytes; the fp16
+    fields are drawn: Q4_0 d ~ N(0, d_std); Q4_1 d ~ |N(0, d_std)|, m ~ N(-8 d_std,
+    d_std); Q4_K d, dmin ~ |N(0, d_std / 16)|."""
+    bb, bc = {2: (18, 32), 3: (20, 32), 12: (144, 256)}[gtype]
+    if N <= 0 or K <= 0 or K % bc:
+        raise ValueError(f"shape {N}x{K} is not a whole number of GGUF blocks")
+    nb = N * (K // bc)
+    b = _random_bytes(g, (nb, bb)).copy()
+
+    def put_f16(off, v):
+        b[:, off:off + 2] = np.asarray(v, dtype=np.float16).view(np.uint8).reshape(nb, 2)
+
+    if gtype == 2:
+        put_f16(0, g.standard_normal(nb) * d_std)
+    elif gtype == 3:
+        put_f16(0, np.abs(g.standard_normal(nb)) * d_std)
+        put_f16(2, g.standard_normal(nb) * d_std - 8 * d_std)
+    else:
+        put_f16(0, np.abs(g.standard_normal(nb)) * d_std / 16)
+        put_f16(2, np.abs(g.standard_normal(nb)) * d_std / 16)
+    return b.reshape(-1)
+
+
 # ----------------------------------------------------------------------------
 # packers from logical fields (tests build structured cases with these)
 # ----------------------------------------------------------------------------
