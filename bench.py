@@ -145,7 +145,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--legs", default="all",
-                    help="comma list of: decode, mixed, gemm, moe, single, kinds, repack, greedy, cpu, copyref "
+                    help="comma list of: decode, mixed, gemm, moe, single, kinds, repack, gguf, greedy, cpu, copyref "
                          "(default all but copyref)")
     ap.add_argument("--no-graph", action="store_true", help="launch the step without a HIP graph")
     return ap.parse_args()
@@ -167,7 +167,7 @@ import torch  # noqa: E402
 import gemm_q4nx_chunk_amd as q  # noqa: E402
 import synth  # noqa: E402
 
-LEGS = set(["decode", "mixed", "gemm", "moe", "single", "kinds", "repack", "greedy", "cpu"]
+LEGS = set(["decode", "mixed", "gemm", "moe", "single", "kinds", "repack", "gguf", "greedy", "cpu"]
            if args.legs == "all"
            else args.legs.split(","))
 DEV = torch.device("cuda:0")
@@ -569,6 +569,23 @@ def repack_leg(steps, warmup, graph):
             "pct_hbm_peak": 100 * moved / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
 
+def gguf_leg(steps, warmup, graph):
+    """GGUF Q4_0 / Q4_1 / Q4_K -> q4_1 conversion of one 8B-dense gate|up-sized
+    tensor (28672 x 4096) each: bytes read plus written per second."""
+    N, K = 2 * 14336, 4096
+    out = torch.empty((N // 32) * (K // 256) * 5120, dtype=torch.uint8, device=DEV)
+    res = {}
+    for name, gtype in (("q4_0", q.GGUF_Q4_0), ("q4_1", q.GGUF_Q4_1), ("q4_k", q.GGUF_Q4_K)):
+        src = to_dev(synth.gen_gguf(synth.rng("gguf", name), gtype, N, K))
+        ms, _ = time_calls(lambda: q.gguf_to_q41(gtype, src, N, K, out), steps, warmup, graph)
+        moved = src.numel() + out.numel()
+        res[name] = {"bytes_read": src.numel(), "bytes_written": out.numel(), "ms": ms,
+                     "GB_s_read_plus_write": moved / (ms * 1e-3) / 1e9,
+                     "pct_hbm_peak": 100 * moved / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        del src
+    return {"shape": [N, K], **res}
+
+
 def kinds_leg(steps, warmup, graph):
     """One large decode GEMV per chunk kind at the lm_head shape (151936 x 2560,
     M = 1): q4_1, Q4_K and Q8 in both code layouts, HIP events around each call."""
@@ -769,6 +786,8 @@ def main():
         legs["single_gemv_1024"] = single_leg()
     if "repack" in LEGS:
         legs["repack_q4k_8b_gate_up"] = repack_leg(args.steps, 2, graph)
+    if "gguf" in LEGS:
+        legs["gguf_to_q41_8b_gate_up"] = gguf_leg(args.steps, 2, graph)
     if "greedy" in LEGS:
         legs["q8_head_151936x2560"] = greedy_leg(max(3, args.steps // 2), 2, graph)
     if "copyref" in LEGS:

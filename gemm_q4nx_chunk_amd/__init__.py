@@ -82,6 +82,9 @@ _lib.q4nx_unpack.argtypes = [ctypes.POINTER(Weight), _P, _P, _P, _P, _P]
 _lib.q4nx_decode.argtypes = [ctypes.POINTER(Weight), _P, _P]
 _lib.q4nx_repack_q4k_to_q41.argtypes = [ctypes.POINTER(Weight), _P, ctypes.c_size_t, _P]
 _lib.q4nx_q8_rows.argtypes = [ctypes.POINTER(Weight), _P, _I, _P, _P]
+_lib.q4nx_gguf_to_q41.argtypes = [_I, _P, ctypes.c_size_t, _I, _I, _P, ctypes.c_size_t, _P]
+_lib.q4nx_gguf_bytes.argtypes = [_I, _I, _I]
+_lib.q4nx_gguf_bytes.restype = ctypes.c_size_t
 _lib.q4nx_argmax.argtypes = [_P, _I, _I, _I, _P, _P, _P, ctypes.c_size_t, _P]
 _lib.q4nx_argmax_ws.argtypes = [_I, _I]
 _lib.q4nx_argmax_ws.restype = ctypes.c_size_t
@@ -98,7 +101,7 @@ _lib.q4nx_status_str.argtypes = [_I]
 _lib.q4nx_status_str.restype = ctypes.c_char_p
 _lib.q4nx_last_error.restype = ctypes.c_char_p
 for _f in ("q4nx_weight_check", "q4nx_gemv", "q4nx_gemv_batched", "q4nx_gemm_block", "q4nx_gemm_batched",
-           "q4nx_moe_experts", "q4nx_unpack", "q4nx_decode", "q4nx_repack_q4k_to_q41", "q4nx_q8_rows", "q4nx_argmax", "q4nx_moe_router", "q4nx_version", "q4nx_plan_create",
+           "q4nx_moe_experts", "q4nx_unpack", "q4nx_decode", "q4nx_repack_q4k_to_q41", "q4nx_gguf_to_q41", "q4nx_q8_rows", "q4nx_argmax", "q4nx_moe_router", "q4nx_version", "q4nx_plan_create",
            "q4nx_plan_run", "q4nx_plan_errors"):
     getattr(_lib, _f).restype = ctypes.c_int
 
@@ -285,6 +288,22 @@ def moe_experts(L: MoeLayer, X, ids, p, Y, T: int, k: int, ws, dbg: dict | None 
     _check(_lib.q4nx_moe_experts(ctypes.byref(L), _ptr(X), _ptr(ids), _ptr(p), T, k, _ptr(Y),
                                  ctypes.byref(d) if d is not None else None, _ptr(ws),
                                  _nbytes(ws) if ws_bytes is None else ws_bytes,
+                                 _stream(stream)))
+
+
+GGUF_Q4_0, GGUF_Q4_1, GGUF_Q4_K = 2, 3, 12
+
+
+def gguf_bytes(gguf_type: int, rows: int, cols: int) -> int:
+    """Bytes of a rows x cols GGUF tensor of that type (0 if the type or cols is invalid)."""
+    return int(_lib.q4nx_gguf_bytes(gguf_type, rows, cols))
+
+
+def gguf_to_q41(gguf_type: int, src, rows: int, cols: int, out, stream=None,
+                src_bytes: int | None = None, out_bytes: int | None = None) -> None:
+    """GGUF Q4_0 / Q4_1 / Q4_K tensor bytes (device) -> q4_1 chunks in `out`."""
+    _check(_lib.q4nx_gguf_to_q41(gguf_type, _ptr(src), _nbytes(src) if src_bytes is None else src_bytes,
+                                 rows, cols, _ptr(out), _nbytes(out) if out_bytes is None else out_bytes,
                                  _stream(stream)))
 
 

@@ -720,6 +720,44 @@ int q4nx_repack_q4k_to_q41(const q4nx_weight* w, void* out, size_t out_bytes, vo
   return hip_status(e, "repack launch");
 }
 
+static int gguf_geometry(int gtype, int* block_bytes, int* block_cols, int* align) {
+  switch (gtype) {
+    case Q4NX_GGUF_Q4_0: *block_bytes = 18; *block_cols = 32; *align = 2; return 1;
+    case Q4NX_GGUF_Q4_1: *block_bytes = 20; *block_cols = 32; *align = 4; return 1;
+    case Q4NX_GGUF_Q4_K: *block_bytes = 144; *block_cols = 256; *align = 16; return 1;
+    default: return 0;
+  }
+}
+
+size_t q4nx_gguf_bytes(int gguf_type, int rows, int cols) {
+  int bb, bc, al;
+  if (!gguf_geometry(gguf_type, &bb, &bc, &al) || rows <= 0 || cols <= 0 || cols % bc) return 0;
+  return (size_t)rows * (size_t)(cols / bc) * (size_t)bb;
+}
+
+int q4nx_gguf_to_q41(int gguf_type, const void* src, size_t src_bytes, int rows, int cols, void* out,
+                     size_t out_bytes, void* stream) {
+  int bb, bc, al;
+  if (!gguf_geometry(gguf_type, &bb, &bc, &al))
+    return fail(Q4NX_E_ARG, "gguf: type %d is not Q4_0 (2), Q4_1 (3) or Q4_K (12)", gguf_type);
+  if (!src || !out) return fail(Q4NX_E_ARG, "gguf: null source or output");
+  if (rows <= 0 || cols <= 0 || rows % 32 || cols % 256)
+    return fail(Q4NX_E_SHAPE, "gguf: %d x %d is not a whole number of 32 x 256 tiles", rows, cols);
+  const int64_t tiles = (int64_t)(rows / 32) * (cols / 256);
+  if (tiles > 0x7FFFFFFF) return fail(Q4NX_E_SHAPE, "gguf: too many tiles");
+  if (!aligned(src, al)) return fail(Q4NX_E_ALIGN, "gguf: source not %d-byte aligned", al);
+  if (!aligned(out, 16)) return fail(Q4NX_E_ALIGN, "gguf: output not 16-byte aligned");
+  const size_t need = q4nx_gguf_bytes(gguf_type, rows, cols);
+  if (src_bytes < need)
+    return fail(Q4NX_E_SHORT, "gguf: source holds %zu bytes, %zu needed", src_bytes, need);
+  if (out_bytes < (size_t)tiles * Q4NX_Q4_1_BYTES)
+    return fail(Q4NX_E_SHORT, "gguf: output holds %zu bytes, %lld needed", out_bytes,
+                (long long)(tiles * Q4NX_Q4_1_BYTES));
+  const hipError_t e = q4nx::launch_gguf_q41(gguf_type, static_cast<const uint8_t*>(src), rows / 32, cols / 256,
+                                             static_cast<uint8_t*>(out), static_cast<hipStream_t>(stream));
+  return hip_status(e, "gguf launch");
+}
+
 int q4nx_q8_rows(const q4nx_weight* w, const int32_t* ids, int T, float* out, void* stream) {
   int st = check_weight(w, "q8_rows");
   if (st) return st;

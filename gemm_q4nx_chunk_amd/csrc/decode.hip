@@ -148,6 +148,111 @@ hipError_t launch_repack_q4k(const uint8_t* w, int tiles, uint8_t* out, hipStrea
 }
 
 // ---------------------------------------------------------------------------
+// GGUF 4-bit tensors -> q4_1 chunks (1bit engine docs, page "NPU engine",
+// section "From a GGUF": Q4_0 maps to scale d, zero -8d; Q4_1 to scale d,
+// zero m; Q4_K, per 32-column sub-block, to scale d*sc, zero -dmin*mn, a
+// super-block being one tile row's 256 columns; codes unchanged, and rounding
+// the scale and zero to bf16 the only error).  The GGUF blocks are the public
+// format's: Q4_0 = fp16 d + 16 code bytes (18 B, 32 weights), Q4_1 = fp16 d,
+// fp16 m + 16 code bytes (20 B), weight j < 16 in the low nibble of byte j and
+// weight j + 16 in its high nibble; Q4_K = fp16 d, fp16 dmin, 12 bytes of
+// 6-bit (sc, mn) pairs, 128 code bytes (144 B, 256 weights), sub-block j in the
+// low (j even) or high (j odd) nibbles of code bytes 32 (j/2) .. 32 (j/2) + 31.
+// Each row of the tensor is its K/32 (K/256) blocks in column order.
+//
+// One workgroup per tile; thread t = 8r + g builds row r, group g: it reads
+// the one GGUF block (Q4_K: the sub-block) covering those 32 weights
+// (staging a tile's blocks in LDS with whole 16-byte loads measured slower),
+// reorders the codes into the chunk's order (even column in the low nibble),
+// and writes its 16 code bytes and its (scale, zero) pair.  fp16 -> fp32 and
+// the products d*sc, dmin*mn (11 x 6 significant bits) are exact; each field is
+// rounded once, to nearest even.  Non-finite fp16 fields are outside the
+// conversion's domain.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float f16_to_f32(uint32_t h) {
+  return (float)__builtin_bit_cast(_Float16, (unsigned short)(h & 0xFFFFu));
+}
+
+// Four codes (one per byte of a and of b, in column order) -> 4 chunk bytes:
+// columns 2i in the low nibble, 2i + 1 in the high one.
+__device__ __forceinline__ uint32_t pack_code_pairs(uint32_t a, uint32_t b) {
+  const uint32_t a2 = a | (a >> 4), b2 = b | (b >> 4);   // bytes 0 and 2 hold the pairs
+  return (a2 & 0xFFu) | ((a2 >> 8) & 0xFF00u) | ((b2 & 0xFFu) << 16) | ((b2 << 8) & 0xFF000000u);
+}
+
+template <int GT>
+__global__ __launch_bounds__(256) void k_gguf_q41(const uint8_t* __restrict__ src, int TC,
+                                                  uint8_t* __restrict__ out) {
+  const int t = threadIdx.x, r = t >> 3, g = t & 7;
+  const int tile = blockIdx.x, tr = tile / TC, tc = tile - tr * TC;
+  const size_t R = (size_t)tr * 32 + r;
+  uint32_t c[4];
+  float scale, zero;
+  if constexpr (GT == 12) {   // Q4_K: super-block (R, tc), sub-block g
+    const uint8_t* sb = src + (R * TC + tc) * 144;
+    const u32x4 h = *reinterpret_cast<const u32x4*>(sb);
+    const u32x4 q0 = *reinterpret_cast<const u32x4*>(sb + 16 + 32 * (g >> 1));
+    const u32x4 q1 = *reinterpret_cast<const u32x4*>(sb + 32 + 32 * (g >> 1));
+    const int sh = 4 * (g & 1);
+    const uint32_t q[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+#pragma unroll
+    for (int o = 0; o < 4; ++o)
+      c[o] = pack_code_pairs((q[2 * o] >> sh) & 0x0F0F0F0Fu, (q[2 * o + 1] >> sh) & 0x0F0F0F0Fu);
+    const uint32_t sw[3] = {h.y, h.z, h.w};   // the 12 scale bytes
+    auto sbyte = [&](int j) { return (sw[j >> 2] >> (8 * (j & 3))) & 0xFFu; };
+    uint32_t sc, mn;
+    if (g < 4) {
+      sc = sbyte(g) & 63u;
+      mn = sbyte(g + 4) & 63u;
+    } else {
+      sc = (sbyte(g + 4) & 15u) | ((sbyte(g - 4) >> 6) << 4);
+      mn = (sbyte(g + 4) >> 4) | ((sbyte(g) >> 6) << 4);
+    }
+    scale = f16_to_f32(h.x) * (float)sc;
+    zero = -(f16_to_f32(h.x >> 16) * (float)mn);
+  } else {                    // Q4_0 / Q4_1: block (R, 8 tc + g)
+    constexpr int BB = GT == 2 ? 18 : 20;
+    const uint8_t* bk = src + (R * TC * 8 + 8 * tc + g) * BB;
+    uint32_t d, m = 0, q[4];
+    if constexpr (GT == 2) {  // 2-byte aligned
+      const uint16_t* h = reinterpret_cast<const uint16_t*>(bk);
+      d = h[0];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) q[i] = (uint32_t)h[1 + 2 * i] | ((uint32_t)h[2 + 2 * i] << 16);
+    } else {                  // 4-byte aligned
+      const uint32_t* w = reinterpret_cast<const uint32_t*>(bk);
+      d = w[0] & 0xFFFFu;
+      m = w[0] >> 16;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) q[i] = w[1 + i];
+    }
+    // low nibbles are columns 0..15, high nibbles 16..31
+    c[0] = pack_code_pairs(q[0] & 0x0F0F0F0Fu, q[1] & 0x0F0F0F0Fu);
+    c[1] = pack_code_pairs(q[2] & 0x0F0F0F0Fu, q[3] & 0x0F0F0F0Fu);
+    c[2] = pack_code_pairs((q[0] >> 4) & 0x0F0F0F0Fu, (q[1] >> 4) & 0x0F0F0F0Fu);
+    c[3] = pack_code_pairs((q[2] >> 4) & 0x0F0F0F0Fu, (q[3] >> 4) & 0x0F0F0F0Fu);
+    scale = f16_to_f32(d);
+    zero = GT == 2 ? -8.f * scale : f16_to_f32(m);
+  }
+  uint8_t* oc = out + (size_t)tile * 5120;
+  *reinterpret_cast<u32x4*>(oc + 16 * t) = u32x4{c[0], c[1], c[2], c[3]};
+  const uint32_t sb16 = __builtin_bit_cast(uint16_t, (__bf16)scale);
+  const uint32_t zb16 = __builtin_bit_cast(uint16_t, (__bf16)zero);
+  *reinterpret_cast<uint32_t*>(oc + 4096 + 4 * t) = sb16 | (zb16 << 16);
+}
+
+hipError_t launch_gguf_q41(int gtype, const uint8_t* src, int TR, int TC, uint8_t* out, hipStream_t s) {
+  const dim3 grid(TR * TC);
+  switch (gtype) {
+    case 2: hipLaunchKernelGGL(k_gguf_q41<2>, grid, dim3(256), 0, s, src, TC, out); break;
+    case 3: hipLaunchKernelGGL(k_gguf_q41<3>, grid, dim3(256), 0, s, src, TC, out); break;
+    case 12: hipLaunchKernelGGL(k_gguf_q41<12>, grid, dim3(256), 0, s, src, TC, out); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Q8 row gather: rows of a Q8 weight (a tied embedding) decoded to fp32
 // (1bit engine docs, page "NPU engine", section "Q4NX chunks": the Q8 kind
 // stores the embedding / lm_head, code (r, k) of a tile at byte k*32 + r in

@@ -121,6 +121,7 @@ hipError_t launch_unpack(int kind, const uint8_t* w, int TR, int TC, uint8_t* co
                          uint16_t* meta0, uint16_t* meta1, uint16_t* row_meta, hipStream_t s);
 hipError_t launch_decode(int kind, const uint8_t* w, int TR, int TC, float* out, hipStream_t s);
 hipError_t launch_repack_q4k(const uint8_t* w, int tiles, uint8_t* out, hipStream_t s);
+hipError_t launch_gguf_q41(int gtype, const uint8_t* src, int TR, int TC, uint8_t* out, hipStream_t s);
 hipError_t launch_q8_rows(int kind, const uint8_t* w, int rows, int TC, const int32_t* ids, int T,
                           float* out, hipStream_t s);
 // Split argmax: slices of this many values per workgroup, one 8-byte key each

@@ -298,6 +298,39 @@ int q4nx_moe_experts(const q4nx_moe_layer* L, const uint16_t* X, const int32_t* 
 int q4nx_repack_q4k_to_q41(const q4nx_weight* w, void* out, size_t out_bytes, void* stream);
 
 /*
+ * GGUF 4-bit tensors -> q4_1 chunks (NPU engine page, section "From a GGUF":
+ * the exact GGUF types map to q4_1 with codes unchanged, Q4_0 as scale d and
+ * zero -8d, Q4_1 as scale d and zero m, Q4_K per 32-column sub-block as scale
+ * d*sc and zero -dmin*mn, a Q4_K super-block covering one tile row's 256
+ * columns; the only error is rounding scale and zero to bf16).  The type
+ * numbers are GGUF's own.  The blocks are the GGUF format's, little-endian:
+ *   Q4_0  18 B per 32 weights: fp16 d, 16 code bytes (weight j < 16 in the low
+ *         nibble of byte j, weight j + 16 in its high nibble); w = d (q - 8)
+ *   Q4_1  20 B per 32 weights: fp16 d, fp16 m, 16 code bytes as Q4_0; w = d q + m
+ *   Q4_K  144 B per 256 weights: fp16 d, fp16 dmin, 12 bytes of 6-bit (sc, mn)
+ *         for 8 sub-blocks, 128 code bytes (sub-block j in the low (j even) or
+ *         high (j odd) nibbles of bytes 32 (j/2) .. 32 (j/2) + 31);
+ *         w = d sc q - dmin mn
+ * and the tensor is rows x cols weights, each row its cols/32 (Q4_K cols/256)
+ * blocks in column order.  Each scale and zero is formed exactly in fp32 and
+ * rounded once to nearest even bf16; non-finite fp16 fields are outside the
+ * conversion's domain.
+ *   gguf_type  Q4NX_GGUF_Q4_0, _Q4_1 or _Q4_K (E_ARG otherwise)
+ *   src        DEVICE, src_bytes >= q4nx_gguf_bytes(type, rows, cols) (E_SHORT);
+ *              2-byte (Q4_0), 4-byte (Q4_1) or 16-byte (Q4_K) aligned (E_ALIGN)
+ *   rows, cols positive multiples of 32 and 256 (E_SHAPE)
+ *   out        DEVICE, 16-byte aligned, out_bytes >= (rows/32)*(cols/256)*5120
+ * The result is a q4_1 weight of the same shape (chunk_bytes = 5120), tiles in
+ * the usual row-major order.  Asynchronous on stream.
+ * q4nx_gguf_bytes returns the tensor's byte size, or 0 for an unknown type or
+ * a cols that is not a whole number of blocks.
+ */
+enum { Q4NX_GGUF_Q4_0 = 2, Q4NX_GGUF_Q4_1 = 3, Q4NX_GGUF_Q4_K = 12 };
+size_t q4nx_gguf_bytes(int gguf_type, int rows, int cols);
+int q4nx_gguf_to_q41(int gguf_type, const void* src, size_t src_bytes, int rows, int cols, void* out,
+                     size_t out_bytes, void* stream);
+
+/*
  * Rows of a Q8 weight decoded to fp32: the token-embedding lookup of a tied
  * Q8 embedding / lm_head (NPU engine page, "Q4NX chunks": Q8 chunks hold that
  * tensor, in either code layout).  out[t][k] = d(r, k/32) * code(r, k) with

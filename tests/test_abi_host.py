@@ -191,6 +191,28 @@ def test_repack_checks(q):
     _expect(q, q.E_SHORT, q.repack_q4k_to_q41, wk, 0x200000, stream=0, out_bytes=need - 1)
 
 
+def test_gguf_sizes_and_checks(q):
+    assert q.gguf_bytes(q.GGUF_Q4_0, 64, 512) == 64 * 16 * 18
+    assert q.gguf_bytes(q.GGUF_Q4_1, 64, 512) == 64 * 16 * 20
+    assert q.gguf_bytes(q.GGUF_Q4_K, 64, 512) == 64 * 2 * 144
+    assert q.gguf_bytes(q.GGUF_Q4_K, 64, 500) == 0 and q.gguf_bytes(8, 64, 512) == 0
+    need_out = 2 * 2 * 5120
+    for t, al in ((q.GGUF_Q4_0, 2), (q.GGUF_Q4_1, 4), (q.GGUF_Q4_K, 16)):
+        n = q.gguf_bytes(t, 64, 512)
+        ok = dict(stream=0, src_bytes=n, out_bytes=need_out)
+        _expect(q, q.E_ARG, q.gguf_to_q41, 6, 0x100000, 64, 512, 0x200000, **ok)       # Q5_0: not taken
+        _expect(q, q.E_ARG, q.gguf_to_q41, t, 0, 64, 512, 0x200000, **ok)
+        _expect(q, q.E_ARG, q.gguf_to_q41, t, 0x100000, 64, 512, 0, **ok)
+        _expect(q, q.E_SHAPE, q.gguf_to_q41, t, 0x100000, 48, 512, 0x200000, **ok)
+        _expect(q, q.E_SHAPE, q.gguf_to_q41, t, 0x100000, 64, 384, 0x200000, **ok)
+        _expect(q, q.E_ALIGN, q.gguf_to_q41, t, 0x100000 + al // 2, 64, 512, 0x200000, **ok)
+        _expect(q, q.E_ALIGN, q.gguf_to_q41, t, 0x100000, 64, 512, 0x200004, **ok)
+        _expect(q, q.E_SHORT, q.gguf_to_q41, t, 0x100000, 64, 512, 0x200000, stream=0,
+                src_bytes=n - 1, out_bytes=need_out)
+        _expect(q, q.E_SHORT, q.gguf_to_q41, t, 0x100000, 64, 512, 0x200000, stream=0,
+                src_bytes=n, out_bytes=need_out - 1)
+
+
 def test_rows_and_argmax_checks(q):
     w8 = _w(q, kind="q8", layout="A")
     _expect(q, q.E_CHUNK_KIND, q.q8_rows, _w(q), 0x2000, 4, 0x3000, stream=0)
