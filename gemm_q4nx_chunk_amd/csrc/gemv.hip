@@ -93,6 +93,8 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_q4x(const GemvBatch b) {
   constexpr int UR = 8 * SL;          // output rows per unit
   extern __shared__ __attribute__((aligned(16))) uint32_t xl[];
   __shared__ float red[WAVES][UR][M];
+  constexpr bool kTurn = KIND == KIND_Q4_K;   // Q4_K metadata through an LDS slot per wave
+  __shared__ __attribute__((aligned(16))) uint8_t tsl[kTurn ? WAVES : 1][kTurn ? 160 * SL : 16];
   const GemvJob& J = b.job[find_job(b, blockIdx.x)];
   const int ks = J.ks, rpw = WAVES / ks;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -122,7 +124,10 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_q4x(const GemvBatch b) {
       make_rsrc(J.w + ((size_t)tr * TC + c0) * CB, (uint32_t)((c1 - c0) * CB));
   Q4Chunk<KIND, SL> ring[D];
 #pragma unroll
-  for (int j = 0; j < D; ++j) q4_load_rs<KIND>(wrs, j * CB, lane, ring[j], i0);
+  for (int j = 0; j < D; ++j) {
+    if constexpr (kTurn) q4k_load_rs_whole<SL>(wrs, j * CB, lane, ring[j], i0);
+    else q4_load_rs<KIND>(wrs, j * CB, lane, ring[j], i0);
+  }
   // 3. prepared records to LDS: pairs at xl[16 r], (d136, sum) at xl[16 R + 2 r]
   float* sums = reinterpret_cast<float*>(xl + 16 * R);
 #pragma unroll
@@ -169,8 +174,14 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_q4x(const GemvBatch b) {
       xp.d136[m] = sums[2 * r];
       xp.sum[m] = sums[2 * r + 1];
     }
-    q4_compute<KIND, M>(ring[j], xp, kMask, kMagic, acc);
-    q4_load_rs<KIND>(wrs, (uint32_t)(c + D - c0) * CB, lane, ring[j], i0);
+    if constexpr (kTurn) {
+      q4k_turn<SL>(tsl[wave], lane, ring[j]);
+      q4_compute<KIND, M>(ring[j], xp, kMask, kMagic, acc);
+      q4k_load_rs_whole<SL>(wrs, (uint32_t)(c + D - c0) * CB, lane, ring[j], i0);
+    } else {
+      q4_compute<KIND, M>(ring[j], xp, kMask, kMagic, acc);
+      q4_load_rs<KIND>(wrs, (uint32_t)(c + D - c0) * CB, lane, ring[j], i0);
+    }
   };
   int base = c0;
   for (; base + D <= c1; base += D) {

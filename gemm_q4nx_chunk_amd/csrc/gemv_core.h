@@ -71,6 +71,53 @@ __device__ __forceinline__ void q4_load_rs(__amdgpu_buffer_rsrc_t rs, uint32_t o
   }
 }
 
+// Q4_K with the metadata fetched whole: the unit's (sc, mn) bytes (128 per
+// slice) as one load per lane, 2 SL bytes each, into meta[0..1], and its rows'
+// (S, M) pairs into rowsm[0] of lanes 0 .. 8 SL - 1: two small loads per chunk
+// instead of 2 SL.  q4k_turn hands each lane its own entries through a
+// per-wave LDS slot of 160 SL bytes.
+template <int SL>
+__device__ __forceinline__ void q4k_load_rs_whole(__amdgpu_buffer_rsrc_t rs, uint32_t off, int lane,
+                                                  Q4Chunk<KIND_Q4_K, SL>& c, int i0) {
+  constexpr int kNt = 2;
+#pragma unroll
+  for (int i = 0; i < SL; ++i)
+    c.q[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 1024 * (i0 + i) + 16 * lane, 0, kNt));
+  const uint32_t mb = off + 4096 + 128 * i0;
+  if constexpr (SL == 4) {
+    const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, mb + 8 * lane, 0, kNt));
+    c.meta[0] = v.x;
+    c.meta[1] = v.y;
+  } else if constexpr (SL == 2) {
+    c.meta[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, mb + 4 * lane, 0, kNt);
+  } else {
+    c.meta[0] = __builtin_amdgcn_raw_buffer_load_b16(rs, mb + 2 * lane, 0, kNt);
+  }
+  c.rowsm[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, off + 4608 + 32 * i0 + 4 * (lane & (8 * SL - 1)), 0, kNt);
+}
+
+// ts: the wave's slot.  Afterwards c holds, per slice i, the lane's (sc | mn << 8)
+// and its row's (S, M), as q4_load_rs leaves them.  The wave's LDS operations
+// run in order; the fences keep the compiler from moving them across each other.
+template <int SL>
+__device__ __forceinline__ void q4k_turn(uint8_t* ts, int lane, Q4Chunk<KIND_Q4_K, SL>& c) {
+  if constexpr (SL == 4) *reinterpret_cast<u32x2*>(ts + 8 * lane) = u32x2{c.meta[0], c.meta[1]};
+  else if constexpr (SL == 2) *reinterpret_cast<uint32_t*>(ts + 4 * lane) = c.meta[0];
+  else *reinterpret_cast<uint16_t*>(ts + 2 * lane) = (uint16_t)c.meta[0];
+  if (lane < 8 * SL) *reinterpret_cast<uint32_t*>(ts + 128 * SL + 4 * lane) = c.rowsm[0];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+  for (int i = 0; i < SL; ++i) {
+    c.meta[i] = *reinterpret_cast<const uint16_t*>(ts + 128 * i + 2 * lane);
+    c.rowsm[i] = *reinterpret_cast<const uint32_t*>(ts + 128 * SL + 32 * i + 4 * (lane >> 3));
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");   // these reads come before
+  __builtin_amdgcn_wave_barrier();                          // the next chunk's writes
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Activation pairs (x[k], x[k+4]) of the lane's group for one tile column, in
 // the order the code chain uses them, the 136-chain, and sum x taken as that
 // chain / 136 (a few fp32 roundings; it is only ever multiplied by z + 8s, and
