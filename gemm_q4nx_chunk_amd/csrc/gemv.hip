@@ -159,6 +159,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_q4x(const GemvBatch b) {
     for (int m = 0; m < M; ++m) acc[i][m] = 0.f;
   auto step = [&](int j, int c) {
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (kTurn) q4k_turn<SL>(tsl[wave], lane, ring[j]);
     XPrep<M> xp;
 #pragma unroll
     for (int m = 0; m < M; ++m) {
@@ -175,7 +176,6 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_q4x(const GemvBatch b) {
       xp.sum[m] = sums[2 * r + 1];
     }
     if constexpr (kTurn) {
-      q4k_turn<SL>(tsl[wave], lane, ring[j]);
       q4_compute<KIND, M>(ring[j], xp, kMask, kMagic, acc);
       q4k_load_rs_whole<SL>(wrs, (uint32_t)(c + D - c0) * CB, lane, ring[j], i0);
     } else {
