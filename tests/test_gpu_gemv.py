@@ -237,3 +237,18 @@ def test_batched_at_the_job_limit(M):
     q().gemv_batched(jobs, M)
     for ch, kind, lay, N, K, x, y in refs:
         _check(host(y), ch, kind, N, K, x, lay)
+
+
+@pytest.mark.parametrize("N,M", [(151936, 1), (151936, 2), (40960, 1), (40960, 3)])
+def test_q4k_whole_tile_launches_sampled(N, M):
+    """Q4_K launches of more than 1024 tile rows (whole-tile units, metadata
+    handed out through the per-wave LDS slot): sampled rows against the oracle."""
+    K = 2560
+    ch = synth.gen_q4_k(synth.rng("gpu-gemv", "q4k-whole", N), N, K)
+    x = synth.gen_x(synth.rng("gpu-gemv", "q4k-whole-x", N, M), M, K)
+    y = gemv(dev_u8(ch), N, K, "q4_k", x)
+    tr = np.unique(_sampled_rows(N, 7 + M) // 32)
+    W = oracle.weights_exact(ch[tr], "q4_k", 32 * len(tr), K)
+    yr, a = oracle.gemv_ref(W, x)
+    ysub = np.concatenate([y[:, 32 * t:32 * t + 32] for t in tr], axis=1)
+    assert oracle.tol_ratio(ysub, yr, a) <= 1.0
