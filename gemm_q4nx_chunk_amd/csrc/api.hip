@@ -629,13 +629,16 @@ int q4nx_moe_experts(const q4nx_moe_layer* L, const uint16_t* X, const int32_t* 
   if (!aligned(X, 16) || !aligned(ids, 4) || !aligned(p, 4) || !aligned(Y, 4))
     return fail(Q4NX_E_ALIGN, "moe: X must be 16-byte, ids/p/Y 4-byte aligned");
   {
-    // a batch's prepared activation rows (72 bytes per row, tile column and
-    // group) are staged in at most 64 KB of LDS
+    // a batch's prepared activation records are staged in at most 64 KB of
+    // LDS: per token and tile column 576 bytes of x (gate/up) and 1056 bytes
+    // of h (down)
     const int tb = T == 1 ? 1 : 4;
-    const int widest = std::max(L->d_model, std::max(L->d_expert, L->d_shared));
-    if ((int64_t)tb * 8 * 72 * (widest / 256) > 65536)
-      return fail(Q4NX_E_SHAPE, "moe: d_model, d_expert and d_shared must be at most %d for T = %d",
-                  65536 / (tb * 8 * 72) * 256, T);
+    const int inner = std::max(L->d_expert, L->d_shared);
+    const int max_d = 65536 / (tb * q4nx::kMoeRecGateUp) * 256;
+    const int max_inner = 65536 / (tb * q4nx::kMoeRecDown) * 256;
+    if (L->d_model > max_d || inner > max_inner)
+      return fail(Q4NX_E_SHAPE, "moe: for T = %d, d_model must be at most %d and d_expert, d_shared at most %d",
+                  T, max_d, max_inner);
   }
   const q4nx::MoeWsLayout lay = q4nx::moe_ws_layout(T * k, T, L->d_model, moe_hstride(L));
   if (!ws || ws_bytes < lay.total)
@@ -679,7 +682,7 @@ int q4nx_moe_experts(const q4nx_moe_layer* L, const uint16_t* X, const int32_t* 
   a.seg = reinterpret_cast<int32_t*>(w + lay.seg);
   a.batch0 = reinterpret_cast<int32_t*>(w + lay.batch0);
   a.btab = reinterpret_cast<int32_t*>(w + lay.btab);
-  a.hbuf = reinterpret_cast<uint16_t*>(w + lay.hbuf);
+  a.hbuf = reinterpret_cast<float*>(w + lay.hbuf);
   a.dbuf = reinterpret_cast<float*>(w + lay.dbuf);
   const hipError_t e = q4nx::launch_moe(L->chunk_bytes == Q4NX_Q4_1_BYTES ? q4nx::KIND_Q4_1
                                                                           : q4nx::KIND_Q4_K,

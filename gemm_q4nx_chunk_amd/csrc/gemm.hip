@@ -20,11 +20,11 @@
 // Dequantisation: a 4-bit code c placed in an fp16 mantissa under the exponent
 // of 1024 reads as 1024 + c (low nibble) or 1024 + 16c (high nibble of a
 // byte), both exact, so one v_and_or makes two weights' codes into an fp16
-// pair and one v_fma_mix_f32 per weight forms c*s + z in fp32:
-//   w = (1024 + c) * s + (z - 1024 s) = (1024 + 16c) * (s/16) + (z - 64 s).
-// v_cvt_pk_bf16_f32 then rounds two weights to the bf16 pair the MFMA takes.
-// z - 1024 s carries one fp32 rounding (about 2^-24 of 1024 s), far below the
-// bf16 rounding of the weight itself (2^-8 of its size).
+// pair; one v_pk_add_f16 of -1024 (or one v_pk_fma_f16 by 1/16 with -64) turns
+// the pair into the exact codes (c, c'), and one v_fma_mix_f32 per weight forms
+// w = c * s + z in fp32: the exact value rounded once, which is the decoded
+// weight bit for bit.  v_cvt_pk_bf16_f32 then rounds two weights to the bf16
+// pair the MFMA takes (at most 2^-8 of the weight's size).
 //
 // k-slot assignment: in MFMA step s (16 per tile column) lane (h = lane/32,
 // n = lane%32) feeds the 8 products k = 128h + 8s + 0..7 -- for the B operand
@@ -90,22 +90,25 @@ __device__ __forceinline__ void group_sz(const GemmChunk<KIND>& c, int q, float&
 }
 
 // Eight weights of one code word (k = 0..7, even k in the low nibble) as bf16.
-__device__ __forceinline__ bf16x8 dequant8(uint32_t w, float s, float z_lo, float s16, float z_hi,
-                                           uint32_t kMaskLo, uint32_t kMaskHi, uint32_t kMagic) {
+__device__ __forceinline__ bf16x8 dequant8(uint32_t w, float s, float z, uint32_t kMaskLo,
+                                           uint32_t kMaskHi, uint32_t kMagic) {
+  const f16x2 m1024 = {(_Float16)-1024.f, (_Float16)-1024.f};
+  const f16x2 m64 = {(_Float16)-64.f, (_Float16)-64.f};
+  const f16x2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
   const uint32_t w8 = w >> 8;
-  const f16x2 p0 = __builtin_bit_cast(f16x2, (w & kMaskLo) | kMagic);    // (c0, c4)
-  const f16x2 p1 = __builtin_bit_cast(f16x2, (w & kMaskHi) | kMagic);    // (16 c1, 16 c5)
-  const f16x2 p2 = __builtin_bit_cast(f16x2, (w8 & kMaskLo) | kMagic);   // (c2, c6)
-  const f16x2 p3 = __builtin_bit_cast(f16x2, (w8 & kMaskHi) | kMagic);   // (16 c3, 16 c7)
+  const f16x2 p0 = __builtin_bit_cast(f16x2, (w & kMaskLo) | kMagic) + m1024;    // (c0, c4)
+  const f16x2 p1 = __builtin_elementwise_fma(__builtin_bit_cast(f16x2, (w & kMaskHi) | kMagic), sixteenth, m64);    // (c1, c5)
+  const f16x2 p2 = __builtin_bit_cast(f16x2, (w8 & kMaskLo) | kMagic) + m1024;   // (c2, c6)
+  const f16x2 p3 = __builtin_elementwise_fma(__builtin_bit_cast(f16x2, (w8 & kMaskHi) | kMagic), sixteenth, m64);   // (c3, c7)
   bf16x8 b;
-  b[0] = (__bf16)fmaf((float)p0.x, s, z_lo);
-  b[1] = (__bf16)fmaf((float)p1.x, s16, z_hi);
-  b[2] = (__bf16)fmaf((float)p2.x, s, z_lo);
-  b[3] = (__bf16)fmaf((float)p3.x, s16, z_hi);
-  b[4] = (__bf16)fmaf((float)p0.y, s, z_lo);
-  b[5] = (__bf16)fmaf((float)p1.y, s16, z_hi);
-  b[6] = (__bf16)fmaf((float)p2.y, s, z_lo);
-  b[7] = (__bf16)fmaf((float)p3.y, s16, z_hi);
+  b[0] = (__bf16)fmaf((float)p0.x, s, z);
+  b[1] = (__bf16)fmaf((float)p1.x, s, z);
+  b[2] = (__bf16)fmaf((float)p2.x, s, z);
+  b[3] = (__bf16)fmaf((float)p3.x, s, z);
+  b[4] = (__bf16)fmaf((float)p0.y, s, z);
+  b[5] = (__bf16)fmaf((float)p1.y, s, z);
+  b[6] = (__bf16)fmaf((float)p2.y, s, z);
+  b[7] = (__bf16)fmaf((float)p3.y, s, z);
   return b;
 }
 
@@ -230,11 +233,10 @@ void k_gemm_q4(GemmArgs a) {
 #endif
       float s, z;
       group_sz<KIND>(c[j], q, s, z);
-      const float z_lo = fmaf(-1024.f, s, z), s16 = s * 0.0625f, z_hi = fmaf(-64.f, s, z);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int st = 4 * q + e;
-        const bf16x8 B = dequant8(c[j].q[q][e], s, z_lo, s16, z_hi, kMaskLo, kMaskHi, kMagic);
+        const bf16x8 B = dequant8(c[j].q[q][e], s, z, kMaskLo, kMaskHi, kMagic);
         const bf16x8 A0 = *reinterpret_cast<const bf16x8*>(xb + 8 * st);
         acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A0, B, acc0, 0, 0, 0);
         if constexpr (TWO) {
@@ -433,11 +435,10 @@ void k_gemm_q4h(GemmArgs a) {
       for (int q = 0; q < 4; ++q) {
         float s, z;
         group_sz<KIND>(c[j], q, s, z);
-        const float z_lo = fmaf(-1024.f, s, z), s16 = s * 0.0625f, z_hi = fmaf(-64.f, s, z);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int st = 4 * q + e;
-          const bf16x8 B = dequant8(c[j].q[q][e], s, z_lo, s16, z_hi, kMaskLo, kMaskHi, kMagic);
+          const bf16x8 B = dequant8(c[j].q[q][e], s, z, kMaskLo, kMaskHi, kMagic);
           const bf16x8 A0 = *reinterpret_cast<const bf16x8*>(xb + 8 * st);
           const bf16x8 A1 = *reinterpret_cast<const bf16x8*>(xb + 32 * kXs + 8 * st);
           acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A0, B, acc0, 0, 0, 0);

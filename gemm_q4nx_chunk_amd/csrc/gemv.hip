@@ -67,17 +67,17 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_q4(const GemvBatch b) {
 
 // The same GEMV with the workgroup's activations prepared once in LDS.
 //
-// Per (activation row m, tile column c, group g) the 16 bf16 pairs the dot
-// chain takes and the group's (136-chain, sum x) are computed once per
+// Per (activation row m, tile column c, group g) the record the dot chain takes
+// (16 fp16 pairs, the scale f and sum x; gemv_core.h) is built once per
 // workgroup instead of once per lane and chunk, and a wave's loop then reads
-// them from LDS (lgkmcnt) while its chunk loads are counted alone on vmcnt.
+// it from LDS (lgkmcnt) while its chunk loads are counted alone on vmcnt.
 // The activation loads are issued before the first chunk loads, so waiting for
 // them never waits for a chunk; chunk loads are unconditional buffer loads
 // (past the wave's run they read zero without memory traffic) running D chunks
 // ahead of the products, and there is no branch inside a group of D steps, so
 // every wait is for the chunk D steps back.  The host uses this kernel when
-// the prepared records (M * TC * 8 per job, 72 bytes each) fit XRP per thread
-// and the LDS budget; otherwise k_gemv_q4.
+// the prepared records (M * TC * 8 per job, 72 bytes each) fit the LDS budget;
+// otherwise k_gemv_q4.
 //
 // SL = 2 (or 1) splits each tile's 32 rows into two units of 16 (chunk slices
 // 0-1 and 2-3: 2 KB of codes and 512 B of scales each), or four of 8, so a
@@ -128,30 +128,35 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_q4x(const GemvBatch b) {
     if constexpr (kTurn) q4k_load_rs_whole<SL>(wrs, j * CB, lane, ring[j], i0);
     else q4_load_rs<KIND>(wrs, j * CB, lane, ring[j], i0);
   }
-  // 3. prepared records to LDS: pairs at xl[16 r], (d136, sum) at xl[16 R + 2 r]
+  // 3. records to LDS: pairs at xl[16 r], (f, X) at xl[16 R + 2 r]
   float* sums = reinterpret_cast<float*>(xl + 16 * R);
-#pragma unroll
-  for (int p = 0; p < XRP; ++p) {
-    const int r = tid + NT * p;
-    XRaw<1> raw;
-#pragma unroll
-    for (int d = 0; d < 4; ++d) raw.v[0][d] = xr[p][d];
-    XPrep<1> xp;
-    x_prep_raw<1>(raw, xp);
+  auto put = [&](int r, const u32x4 (&v)[4]) {
+    uint32_t pr[16];
+    float f, X;
+    x_record(v, pr, f, X);
     if (r < R) {
 #pragma unroll
       for (int d = 0; d < 4; ++d)
-        *reinterpret_cast<u32x4*>(xl + 16 * r + 4 * d) =
-            u32x4{xp.p[0][4 * d], xp.p[0][4 * d + 1], xp.p[0][4 * d + 2], xp.p[0][4 * d + 3]};
-      sums[2 * r] = xp.d136[0];
-      sums[2 * r + 1] = xp.sum[0];
+        *reinterpret_cast<u32x4*>(xl + 16 * r + 4 * d) = u32x4{pr[4 * d], pr[4 * d + 1], pr[4 * d + 2], pr[4 * d + 3]};
+      sums[2 * r] = f;
+      sums[2 * r + 1] = X;
     }
+  };
+#pragma unroll
+  for (int p = 0; p < XRP; ++p) put(tid + NT * p, xr[p]);
+  // long-K launches: the records past the first XRP per thread, loaded and prepared in turn
+  for (int r = tid + NT * XRP; r < R; r += NT) {
+    const int m = r / (TC * 8), rem = r - m * TC * 8;
+    const uint32_t off = (uint32_t)(m * J.ldx + 32 * rem) * 2;
+    u32x4 v[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+      v[d] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs, off + 16 * d, 0, 0));
+    put(r, v);
   }
   __syncthreads();
 
-  uint32_t kMask = 0x000F000Fu, kMagic = 0x43004300u;
-  asm volatile("" : "+s"(kMask));
-  asm volatile("" : "+v"(kMagic));
+  const Q4Consts k = q4_consts();
   float acc[SL][M];
 #pragma unroll
   for (int i = 0; i < SL; ++i)
@@ -160,7 +165,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_q4x(const GemvBatch b) {
   auto step = [&](int j, int c) {
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (kTurn) q4k_turn<SL>(tsl[wave], lane, ring[j]);
-    XPrep<M> xp;
+    XRec<M> xp;
 #pragma unroll
     for (int m = 0; m < M; ++m) {
       const int r = (m * TC + c) * 8 + g;
@@ -172,16 +177,12 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_q4x(const GemvBatch b) {
         xp.p[m][4 * d + 2] = v.z;
         xp.p[m][4 * d + 3] = v.w;
       }
-      xp.d136[m] = sums[2 * r];
-      xp.sum[m] = sums[2 * r + 1];
+      xp.f[m] = sums[2 * r];
+      xp.X[m] = sums[2 * r + 1];
     }
-    if constexpr (kTurn) {
-      q4_compute<KIND, M>(ring[j], xp, kMask, kMagic, acc);
-      q4k_load_rs_whole<SL>(wrs, (uint32_t)(c + D - c0) * CB, lane, ring[j], i0);
-    } else {
-      q4_compute<KIND, M>(ring[j], xp, kMask, kMagic, acc);
-      q4_load_rs<KIND>(wrs, (uint32_t)(c + D - c0) * CB, lane, ring[j], i0);
-    }
+    q4_compute<KIND, M, SL>(ring[j], xp, k, acc);
+    if constexpr (kTurn) q4k_load_rs_whole<SL>(wrs, (uint32_t)(c + D - c0) * CB, lane, ring[j], i0);
+    else q4_load_rs<KIND>(wrs, (uint32_t)(c + D - c0) * CB, lane, ring[j], i0);
   };
   int base = c0;
   for (; base + D <= c1; base += D) {
@@ -499,16 +500,25 @@ struct GemvXDepth {
   static constexpr int value = (WAVES == 16 && M > 1) ? 1 : Q4NX_GEMVX_DEPTH;
 };
 
+// Launch of a prepared-activation kernel; more than 64 KB of dynamic LDS is
+// declared to the runtime first.
+template <typename F>
+static void launch_xl(F* kern, int n_wg, int threads, int xl_bytes, hipStream_t s, const GemvBatch& b) {
+  if (xl_bytes > 65536)
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, xl_bytes);
+  hipLaunchKernelGGL(kern, dim3(n_wg), dim3(threads), xl_bytes, s, b);
+}
+
 template <int KIND, int M, int WAVES>
 static hipError_t launch_one(const GemvBatch& b, int n_wg, int xl_bytes, hipStream_t s) {
   if constexpr (KIND == KIND_Q4_1 || KIND == KIND_Q4_K) {
     constexpr int D = GemvXDepth<M, WAVES>::value;
     if (xl_bytes > 0 && b.sl == 2)
-      hipLaunchKernelGGL((k_gemv_q4x<KIND, M, WAVES, D, 2>), dim3(n_wg), dim3(64 * WAVES), xl_bytes, s, b);
+      launch_xl(k_gemv_q4x<KIND, M, WAVES, D, 2>, n_wg, 64 * WAVES, xl_bytes, s, b);
     else if (xl_bytes > 0 && b.sl == 1)
-      hipLaunchKernelGGL((k_gemv_q4x<KIND, M, WAVES, D, 1>), dim3(n_wg), dim3(64 * WAVES), xl_bytes, s, b);
+      launch_xl(k_gemv_q4x<KIND, M, WAVES, D, 1>, n_wg, 64 * WAVES, xl_bytes, s, b);
     else if (xl_bytes > 0)
-      hipLaunchKernelGGL((k_gemv_q4x<KIND, M, WAVES, D>), dim3(n_wg), dim3(64 * WAVES), xl_bytes, s, b);
+      launch_xl(k_gemv_q4x<KIND, M, WAVES, D, 4>, n_wg, 64 * WAVES, xl_bytes, s, b);
     else
       hipLaunchKernelGGL((k_gemv_q4<KIND, M, WAVES>), dim3(n_wg), dim3(64 * WAVES), 0, s, b);
   } else {
@@ -556,6 +566,19 @@ static hipError_t launch_small(int M, const GemvBatch& b, int n_wg, int xl, hipS
   return hipErrorInvalidValue;
 }
 
+// Dynamic LDS a workgroup may take: the device's limit (160 KB on gfx950)
+// less the kernels' static arrays (at most 8 KB).
+static int gemv_lds_budget() {
+  static const int budget = [] {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+      v = 65536;
+    return v - 8192 > 65536 ? v - 8192 : 65536;
+  }();
+  return budget;
+}
+
 int gemv_xl_bytes(int kind, int M, int waves, int max_tc) {
 #if defined(Q4NX_GEMV_NO_XLDS)
   return 0;
@@ -566,10 +589,8 @@ int gemv_xl_bytes(int kind, int M, int waves, int max_tc) {
     return NP * 16 <= 65536 ? NP * 16 : 0;
   }
   if (kind != KIND_Q4_1 && kind != KIND_Q4_K) return 0;
-  const int R = M * max_tc * 8;
-  if (R > 2 * 64 * waves) return 0;          // two records per thread
-  const int bytes = R * 72;
-  return bytes <= 65536 ? bytes : 0;
+  const int bytes = M * max_tc * 8 * 72;
+  return bytes <= (waves == 4 ? gemv_lds_budget() : 65536) ? bytes : 0;
 }
 
 // 16-wave workgroups hold at most 128 registers per lane, so they are used

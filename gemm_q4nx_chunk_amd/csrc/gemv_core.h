@@ -11,17 +11,44 @@ namespace q4nx {
 // Lane l reads, in slice i = 0..3 of a chunk, the 16 bytes at 1024*i + 16*l:
 // the 32 codes of tile row r = 8i + l/8 in group g = l%8.  Every slice of every
 // chunk gives lane l the same group g, so the lane's 32 activations of a tile
-// column are loaded once per chunk.
+// column are prepared once per chunk.
 //
-// Unpack: the bf16 with bits 0x4300 | c is exactly 128 + c for a 4-bit c, so
-// (w >> 4j) & 0x000F000F | 0x43004300 makes nibbles j and j+4 of a 32-bit code
-// word into a bf16 pair, which v_dot2_f32_bf16 multiplies with the pair
-// (x[k], x[k+4]).  The same dot chain run with 136 (= 128 + 8) in place of each
-// code is subtracted, so with s the scale, z the zero of the 32-column group:
-//     sum_k (c s + z) x = s * (D - D136) + (z + 8 s) * sum_k x
-// where D - D136 = sum (c - 8) x, bit-exactly 0 when every code is 8 (the
-// identical operand bits give identical chain results).  For Q4_K, s = S*scale
-// and z = M*min (both products exact in fp32).
+// A group's weights are w_k = s c_k + z (q4_1: scale s, zero z; Q4_K:
+// s = S*scale, z = M*min, both products exact in fp32).  With any integer c0,
+//     sum_k w_k x_k = s * sum_k (c_k - c0) x_k + (z + c0 s) * sum_k x_k.
+// The library takes c0 = clamp(round(-z/s), 0, 15), the code nearest the
+// group's zero crossing, so that |z + c0 s| <= |s|/2 whenever the crossing lies
+// inside the code range, and z + c0 s has the sign of every s (c_k - c0) term
+// otherwise.  Then |s| |c_k - c0| + |z + c0 s| <= 3 |w_k| for every k: the two
+// parts of the sum never cancel more than their own terms, so the error of the
+// factored sum stays a small multiple of sum |w x| (the bound the oracle
+// checks), for any codes and any (s, z).  (Any c0 gives the same exact value;
+// the choice only bounds the rounding.)  The pair z + c0 s is exact in fp32
+// when the crossing is inside the code range (Sterbenz), so a one-hot x gives
+// back fl(s c + z), the decoded weight, bit for bit.
+//
+// Signed codes: (w & 0x000F000F) | 0x64006400 makes nibbles 0 and 4 of a code
+// word into the fp16 pair (1024 + c, 1024 + c'), and (w & 0x00F000F0) | ...
+// nibbles 1 and 5 into (1024 + 16 c, 1024 + 16 c'); one v_pk_add_f16 with
+// -(1024 + c0) (one v_pk_fma_f16 by 1/16 with -(64 + c0)) then gives the exact
+// pair (c - c0, c' - c0).  v_dot2_f32_f16 multiplies it with the activation
+// pair (x[k], x[k+4]); every product (5-bit code times 11-bit fp16) is exact.
+//
+// Activations are fp16 "records": the 32 values of one (row, tile column,
+// group), each pair in the chain's order, scaled by 2^sigma so that the
+// largest lands in [2^15, 2^16).  A bf16 value is exact in fp16 from 2^-17 up,
+// so a record is exact whenever its nonzero values span at most 2^32; the
+// record keeps f = 2^-sigma and X = sum x.  A record that is not exact (values
+// spanning more, subnormal or huge bf16s) keeps its raw bf16 pairs and f = -1
+// instead, and the lanes that own such a record run the same chain in bf16,
+// with the signed codes converted to bf16 pairs (exact small integers).
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2f16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c, false);
+}
 
 // SL slices of a chunk (all 4, or 2 for launches that split a tile's rows
 // between workgroups: slices i0 .. i0 + SL - 1 are rows 8 i0 .. 8 (i0 + SL) - 1).
@@ -118,17 +145,9 @@ __device__ __forceinline__ void q4k_turn(uint8_t* ts, int lane, Q4Chunk<KIND_Q4_
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Activation pairs (x[k], x[k+4]) of the lane's group for one tile column, in
-// the order the code chain uses them, the 136-chain, and sum x taken as that
-// chain / 136 (a few fp32 roundings; it is only ever multiplied by z + 8s, and
-// it is exact when a single x of the group is nonzero).
-template <int M>
-struct XPrep {
-  uint32_t p[M][16];
-  float sum[M];
-  float d136[M];
-};
-
+// --------------------------------------------------------------------------
+// activation records
+// --------------------------------------------------------------------------
 // The lane's 32 activations of one tile column, as loaded (bf16 pairs, k order).
 template <int M>
 struct XRaw {
@@ -157,63 +176,238 @@ __device__ __forceinline__ void x_raw_coherent(__amdgpu_buffer_rsrc_t rsrc, cons
                                                 rsrc, xoff[m] + 2 * (col + 8 * d), 0, kCpolSc1));
 }
 
-template <int M>
-__device__ __forceinline__ void x_prep_raw(const XRaw<M>& r, XPrep<M>& xp) {
+// The 16 bf16 pairs of a group in chain order: pair 4d + j is (x[8d + j], x[8d + j + 4]).
+__device__ __forceinline__ void bf16_chain_pairs(const u32x4 (&v)[4], uint32_t (&p)[16]) {
 #pragma unroll
-  for (int m = 0; m < M; ++m) {
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      const u32x4 v = r.v[m][d];   // x[8d .. 8d+7] of the group, bf16 pairs
-      // v_perm_b32 byte select: 0..3 pick bytes of the second operand, 4..7 of the first.
-      xp.p[m][4 * d + 0] = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);   // (x0, x4)
-      xp.p[m][4 * d + 1] = __builtin_amdgcn_perm(v.z, v.x, 0x07060302u);   // (x1, x5)
-      xp.p[m][4 * d + 2] = __builtin_amdgcn_perm(v.w, v.y, 0x05040100u);   // (x2, x6)
-      xp.p[m][4 * d + 3] = __builtin_amdgcn_perm(v.w, v.y, 0x07060302u);   // (x3, x7)
-    }
-    float e = 0.f;
-#pragma unroll
-    for (int t = 0; t < 16; ++t) e = dot2bf16(0x43084308u, xp.p[m][t], e);   // (136, 136)
-    xp.d136[m] = e;
-    xp.sum[m] = e / 136.0f;
+  for (int d = 0; d < 4; ++d) {
+    // v_perm_b32 byte select: 0..3 pick bytes of the second operand, 4..7 of the first.
+    p[4 * d + 0] = __builtin_amdgcn_perm(v[d].z, v[d].x, 0x05040100u);   // (x0, x4)
+    p[4 * d + 1] = __builtin_amdgcn_perm(v[d].z, v[d].x, 0x07060302u);   // (x1, x5)
+    p[4 * d + 2] = __builtin_amdgcn_perm(v[d].w, v[d].y, 0x05040100u);   // (x2, x6)
+    p[4 * d + 3] = __builtin_amdgcn_perm(v[d].w, v[d].y, 0x07060302u);   // (x3, x7)
   }
 }
 
-template <int M>
-__device__ __forceinline__ void x_prep(const uint16_t* const (&xrow)[M], int col, XPrep<M>& xp) {
-  XRaw<M> r;
-  x_raw<M>(xrow, col, r);
-  x_prep_raw<M>(r, xp);
+// sum of the 32 values of a group of bf16 pairs (fixed order, fp32)
+__device__ __forceinline__ float bf16_pairs_sum(const uint32_t (&p)[16]) {
+  float e = 0.f;
+#pragma unroll
+  for (int t = 0; t < 16; ++t) e = dot2bf16(0x3F803F80u, p[t], e);   // (1, 1)
+  return e;
 }
 
-template <int KIND, int M, int SL = 4>
-__device__ __forceinline__ void q4_compute(const Q4Chunk<KIND, SL>& c, const XPrep<M>& xp,
-                                           uint32_t kMask, uint32_t kMagic, float (&acc)[SL][M]) {
+// One fp16 record from the 32 bf16 activations of a group (see above).
+// p: pairs in chain order; f: 2^-sigma (fp16 record) or -1 (bf16 record);
+// X: sum of the 32 values.
+__device__ __forceinline__ void x_record(const u32x4 (&v)[4], uint32_t (&p)[16], float& f, float& X) {
+  // largest magnitude (as bits) and a lower bound on the smallest nonzero
+  // exponent: (b - 1) & 0x7F80 is the exponent field of b, one less when the
+  // mantissa is zero (conservative), 0 for a subnormal, and 0x7F80 for a zero
+  // (which then never wins the minimum).
+  u16x2 mx = {0, 0}, mn = {0x7F80, 0x7F80};
 #pragma unroll
-  for (int i = 0; i < SL; ++i) {
-    float s, zz;
-    if constexpr (KIND == KIND_Q4_1) {
-      s = bf16lo(c.meta[i]);
-      zz = fmaf(8.f, s, bf16hi(c.meta[i]));
-    } else {
-      const float S = bf16lo(c.rowsm[i]), Mn = bf16hi(c.rowsm[i]);
-      s = S * (float)(c.meta[i] & 0xFFu);
-      zz = fmaf(8.f, s, Mn * (float)((c.meta[i] >> 8) & 0xFFu));
+  for (int d = 0; d < 4; ++d)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const u16x2 a = __builtin_bit_cast(u16x2, v[d][t] & 0x7FFF7FFFu);
+      mx = __builtin_elementwise_max(mx, a);
+      const u16x2 e = __builtin_bit_cast(u16x2, __builtin_bit_cast(uint32_t, a - u16x2{1, 1}) & 0x7F807F80u);
+      mn = __builtin_elementwise_min(mn, e);
     }
-    uint32_t cp[16];
+  const uint32_t top = mx.x > mx.y ? mx.x : mx.y;        // bits of max |x|
+  const int E = (int)(top >> 7);                        // its exponent field
+  const int Emin = (int)((mn.x < mn.y ? mn.x : mn.y) >> 7);
+  // exact in fp16 after scaling: max in [2^15, 2^16), every nonzero value
+  // >= 2^-17 (exponent field >= E - 32); keep 2^sigma within 2^64 either way
+  const bool fast = top == 0 || (E >= 78 && E <= 206 && Emin >= E - 32);
+  if (fast) {
+    const float up = top == 0 ? 1.f : __uint_as_float((uint32_t)(269 - E) << 23);   // 2^sigma, sigma = 142 - E
+    f = top == 0 ? 1.f : __uint_as_float((uint32_t)(E - 15) << 23);                // 2^-sigma
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      const uint32_t w = c.q[i][d];
-      cp[4 * d + 0] = (w & kMask) | kMagic;
-      cp[4 * d + 1] = ((w >> 4) & kMask) | kMagic;
-      cp[4 * d + 2] = ((w >> 8) & kMask) | kMagic;
-      cp[4 * d + 3] = ((w >> 12) & kMask) | kMagic;
+      const u32x4 w = v[d];
+      p[4 * d + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(bf16lo(w.x) * up, bf16lo(w.z) * up));
+      p[4 * d + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(bf16hi(w.x) * up, bf16hi(w.z) * up));
+      p[4 * d + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(bf16lo(w.y) * up, bf16lo(w.w) * up));
+      p[4 * d + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(bf16hi(w.y) * up, bf16hi(w.w) * up));
     }
+    float e = 0.f;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) e = dot2f16(0x3C003C00u, p[t], e);   // (1, 1)
+    X = e * f;
+  } else {
+    bf16_chain_pairs(v, p);
+    f = -1.f;
+    X = bf16_pairs_sum(p);
+  }
+}
+
+// M prepared records of one tile column (one per activation row).
+template <int M>
+struct XRec {
+  uint32_t p[M][16];
+  float f[M];
+  float X[M];
+};
+
+template <int M>
+__device__ __forceinline__ void x_records(const XRaw<M>& r, XRec<M>& xp) {
+#pragma unroll
+  for (int m = 0; m < M; ++m) x_record(r.v[m], xp.p[m], xp.f[m], xp.X[m]);
+}
+
+// bf16-only records (the exact fallback form, used where records are built per
+// lane and per chunk): raw pairs, f = -1.  PL planes: a fp32 activation is
+// carried as the sum of PL bf16 values (plane 0 = bf16(x), plane 1 = bf16(x -
+// plane 0)).
+template <int M, int PL = 1>
+struct XRecB {
+  uint32_t p[M][PL][16];
+  float X[M];
+};
+
+template <int M>
+__device__ __forceinline__ void x_records_b(const XRaw<M>& r, XRecB<M>& xp) {
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    bf16_chain_pairs(r.v[m], xp.p[m][0]);
+    xp.X[m] = bf16_pairs_sum(xp.p[m][0]);
+  }
+}
+
+// --------------------------------------------------------------------------
+// products
+// --------------------------------------------------------------------------
+// A slice's group: scale, zero, center code and its fp16 constants.
+struct Q4Group {
+  float s, delta;      // delta = z + c0 s
+  uint32_t pkl, pkh;   // fp16 pairs -(1024 + c0), -(64 + c0)
+};
+
+template <int KIND, int SL>
+__device__ __forceinline__ Q4Group q4_group(const Q4Chunk<KIND, SL>& c, int i) {
+  float s, z;
+  if constexpr (KIND == KIND_Q4_1) {
+    s = bf16lo(c.meta[i]);
+    z = bf16hi(c.meta[i]);
+  } else {
+    s = bf16lo(c.rowsm[i]) * (float)(c.meta[i] & 0xFFu);
+    z = bf16hi(c.rowsm[i]) * (float)((c.meta[i] >> 8) & 0xFFu);
+  }
+  // c0 = clamp(round(-z / s), 0, 15); the reciprocal's rounding only moves
+  // the choice near half-integers, which keeps |z + c0 s| within 0.5 |s| plus a
+  // few ulps.  s = 0 or a NaN lands on 0 or 15: any c0 is exact.
+  const float t = fminf(fmaxf(fmaf(-z, __builtin_amdgcn_rcpf(s), 0.5f), 0.f), 15.5f);
+  const uint32_t c0 = (uint32_t)t;
+  Q4Group gp;
+  gp.s = s;
+  gp.delta = fmaf((float)c0, s, z);
+  gp.pkl = 0xE400E400u | (c0 * 0x00010001u);
+  gp.pkh = 0xD400D400u | (c0 * 0x00100010u);
+  return gp;
+}
+
+// Unpack constants kept in registers: gfx9 VOP3 instructions take no literal,
+// so a mask in an SGPR and the magic in a VGPR let one v_and_or_b32 build a pair.
+struct Q4Consts {
+  uint32_t mlo, mhi, magic;
+};
+
+__device__ __forceinline__ Q4Consts q4_consts() {
+  uint32_t a = 0x000F000Fu, b = 0x00F000F0u, c = 0x64006400u;
+  asm volatile("" : "+s"(a));
+  asm volatile("" : "+s"(b));
+  asm volatile("" : "+v"(c));
+  return Q4Consts{a, b, c};
+}
+
+// The 16 signed code pairs of one 32-code run, in chain order.
+__device__ __forceinline__ void q4_signed(const u32x4& q, const Q4Group& gp, const Q4Consts& k,
+                                          uint32_t (&cp)[16]) {
+  const f16x2 lo = __builtin_bit_cast(f16x2, gp.pkl), hi = __builtin_bit_cast(f16x2, gp.pkh);
+  const f16x2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const uint32_t w = q[d], w8 = w >> 8;
+    const f16x2 a0 = __builtin_bit_cast(f16x2, (w & k.mlo) | k.magic);    // (1024 + c, 1024 + c')
+    const f16x2 a1 = __builtin_bit_cast(f16x2, (w & k.mhi) | k.magic);    // (1024 + 16 c, ...)
+    const f16x2 a2 = __builtin_bit_cast(f16x2, (w8 & k.mlo) | k.magic);
+    const f16x2 a3 = __builtin_bit_cast(f16x2, (w8 & k.mhi) | k.magic);
+    cp[4 * d + 0] = __builtin_bit_cast(uint32_t, a0 + lo);
+    cp[4 * d + 1] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(a1, sixteenth, hi));
+    cp[4 * d + 2] = __builtin_bit_cast(uint32_t, a2 + lo);
+    cp[4 * d + 3] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(a3, sixteenth, hi));
+  }
+}
+
+// fp16 signed code pair -> bf16 pair (small integers: exact).
+__device__ __forceinline__ uint32_t f16pair_to_bf16(uint32_t c) {
+  const f16x2 h = __builtin_bit_cast(f16x2, c);
+  const bf16x2 b = {(__bf16)(float)h.x, (__bf16)(float)h.y};
+  return __builtin_bit_cast(uint32_t, b);
+}
+
+// acc[i][m] += the slices' products with the fp16 records (bf16 records on
+// the lanes that hold one).
+template <int KIND, int M, int SL = 4>
+__device__ __forceinline__ void q4_compute(const Q4Chunk<KIND, SL>& c, const XRec<M>& xp,
+                                           const Q4Consts& k, float (&acc)[SL][M]) {
+  bool slow = false;
+#pragma unroll
+  for (int m = 0; m < M; ++m) slow |= xp.f[m] < 0.f;
+  const bool wslow = __builtin_amdgcn_ballot_w64(slow) != 0;   // uniform
+#pragma unroll
+  for (int i = 0; i < SL; ++i) {
+    const Q4Group gp = q4_group<KIND, SL>(c, i);
+    uint32_t cp[16];
+    q4_signed(c.q[i], gp, k, cp);
+    float D[M];
 #pragma unroll
     for (int m = 0; m < M; ++m) {
-      float D = 0.f;
+      float e = 0.f;
 #pragma unroll
-      for (int t = 0; t < 16; ++t) D = dot2bf16(cp[t], xp.p[m][t], D);
-      acc[i][m] = fmaf(s, D - xp.d136[m], fmaf(zz, xp.sum[m], acc[i][m]));
+      for (int t = 0; t < 16; ++t) e = dot2f16(cp[t], xp.p[m][t], e);
+      D[m] = e;
+    }
+    if (wslow) {
+      uint32_t cb[16];
+#pragma unroll
+      for (int t = 0; t < 16; ++t) cb[t] = f16pair_to_bf16(cp[t]);
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        if (xp.f[m] < 0.f) {
+          float e = 0.f;
+#pragma unroll
+          for (int t = 0; t < 16; ++t) e = dot2bf16(cb[t], xp.p[m][t], e);
+          D[m] = e;
+        }
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+      acc[i][m] = fmaf(gp.s * fabsf(xp.f[m]), D[m], fmaf(gp.delta, xp.X[m], acc[i][m]));
+  }
+}
+
+// The same products with bf16-only records of PL planes.
+template <int KIND, int M, int PL, int SL = 4>
+__device__ __forceinline__ void q4_compute_b(const Q4Chunk<KIND, SL>& c, const XRecB<M, PL>& xp,
+                                             const Q4Consts& k, float (&acc)[SL][M]) {
+#pragma unroll
+  for (int i = 0; i < SL; ++i) {
+    const Q4Group gp = q4_group<KIND, SL>(c, i);
+    uint32_t cp[16];
+    q4_signed(c.q[i], gp, k, cp);
+#pragma unroll
+    for (int t = 0; t < 16; ++t) cp[t] = f16pair_to_bf16(cp[t]);
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      float e = 0.f;
+#pragma unroll
+      for (int pl = 0; pl < PL; ++pl)
+#pragma unroll
+        for (int t = 0; t < 16; ++t) e = dot2bf16(cp[t], xp.p[m][pl][t], e);
+      acc[i][m] = fmaf(gp.s, e, fmaf(gp.delta, xp.X[m], acc[i][m]));
     }
   }
 }
@@ -375,13 +569,16 @@ __device__ __forceinline__ void q8_lane_reduce(float (&acc)[16][M]) {
 
 // Partial sums of one tile row over chunks [c0, c1) for M activation rows.
 // acc[i][m] of lane l belongs to row 8i + l/8, group l%8 (sum over the groups
-// with q4_lane_reduce).  xrow[m] points at activation row m, column 0.
+// with q4_lane_reduce).  xrow[m] points at activation row m, column 0.  The
+// activations are loaded per lane and chunk, so they are taken as bf16 records.
 template <int KIND, int M>
 __device__ __forceinline__ void q4_step(const Q4Chunk<KIND>& ch, const uint16_t* const (&xrow)[M],
-                                        int c, uint32_t kMask, uint32_t kMagic, float (&acc)[4][M]) {
-  XPrep<M> xp;
-  x_prep<M>(xrow, 256 * c, xp);
-  q4_compute<KIND, M>(ch, xp, kMask, kMagic, acc);
+                                        int c, const Q4Consts& k, float (&acc)[4][M]) {
+  XRaw<M> r;
+  x_raw<M>(xrow, 256 * c, r);
+  XRecB<M> xb;
+  x_records_b<M>(r, xb);
+  q4_compute_b<KIND, M, 1>(ch, xb, k, acc);
 }
 
 // Chunks kept in flight per wave by q4_row_partial: a ring of this many chunk
@@ -398,10 +595,7 @@ __device__ __forceinline__ void q4_row_partial(const uint8_t* __restrict__ row, 
   const uint16_t* xrow[M];
 #pragma unroll
   for (int m = 0; m < M; ++m) xrow[m] = xrow_in[m] + 32 * g;
-  // Register operands let the unpack use one v_and_or_b32 (gfx9 VOP3 takes no literal).
-  uint32_t kMask = 0x000F000Fu, kMagic = 0x43004300u;
-  asm volatile("" : "+s"(kMask));
-  asm volatile("" : "+v"(kMagic));
+  const Q4Consts k = q4_consts();
   const int n = c1 - c0;
   Q4Chunk<KIND> ring[D];
 #pragma unroll
@@ -411,7 +605,7 @@ __device__ __forceinline__ void q4_row_partial(const uint8_t* __restrict__ row, 
 #pragma unroll
     for (int b = 0; b < D; ++b) {
       if (i + b < n) {
-        q4_step<KIND, M>(ring[b], xrow, c0 + i + b, kMask, kMagic, acc);
+        q4_step<KIND, M>(ring[b], xrow, c0 + i + b, k, acc);
         if (i + b + D < n) q4_load<KIND>(row + (size_t)(c0 + i + b + D) * CB, lane, ring[b]);
       }
     }

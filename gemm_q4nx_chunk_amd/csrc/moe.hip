@@ -14,8 +14,10 @@
 //           per-expert segments; batch counts.  Ids outside [0, n_experts) go
 //           to the end, are never dereferenced, and set bit 0 of the error word.
 //   gateup  per (token batch, tile row): gate and up rows of the expert for up
-//           to TB tokens, h = silu(g) * u, rounded to bf16.
-//   down    per (token batch, group of tile rows): d = Down h, fp32.
+//           to TB tokens, h = silu(g) * u in fp32.
+//   down    per (token batch, group of tile rows): d = Down h, fp32; each h
+//           is taken as the sum of two bf16 values (its bf16 rounding and the
+//           bf16 rounding of the rest), 16 significant bits.
 //   combine y[t] = sum_j p[t][j] d[t][j] in slot order, then + the shared d.
 // No floating-point atomics anywhere; every sum has a fixed order.
 #include "gemv_core.h"
@@ -377,11 +379,11 @@ __device__ __forceinline__ void moe_route_small(const MoeArgs& a, MoeSmallRoute&
 }
 
 // Prepared activation records of TB rows (row m at base + rows[m], rows in
-// LDS) over TC tile columns, record (m * TC + c) * 8 + g at xl[16 r] and its
-// (d136, sum) at xl[16 R + 2 r]; all threads of the workgroup take part.  (A
-// thread's row comes from LDS: picking it from a register array by a lane-
-// varying index would put the array in private memory, whose loads wait for
-// every weight load in flight.)
+// LDS) over TC tile columns: record r = (m * TC + c) * 8 + g at xl[16 r], its
+// (f, X) at xl[16 R + 2 r] (gemv_core.h); all threads of the workgroup take
+// part.  (A thread's row comes from LDS: picking it from a register array by a
+// lane-varying index would put the array in private memory, whose loads wait
+// for every weight load in flight.)
 template <int TB>
 __device__ __forceinline__ void moe_stage(const uint16_t* base, const int64_t* rows, int TC, uint32_t* xl) {
   const int R = TB * TC * 8;
@@ -389,31 +391,62 @@ __device__ __forceinline__ void moe_stage(const uint16_t* base, const int64_t* r
   for (int r = threadIdx.x; r < R; r += blockDim.x) {
     const int m = r / (TC * 8), rem = r - m * TC * 8;
     const uint16_t* p = base + rows[m];
-    XRaw<1> raw;
+    u32x4 v[4];
 #pragma unroll
-    for (int d = 0; d < 4; ++d) raw.v[0][d] = load16(p + 32 * rem + 8 * d);
-    XPrep<1> xp;
-    x_prep_raw<1>(raw, xp);
+    for (int d = 0; d < 4; ++d) v[d] = load16(p + 32 * rem + 8 * d);
+    uint32_t pr[16];
+    float f, X;
+    x_record(v, pr, f, X);
 #pragma unroll
     for (int d = 0; d < 4; ++d)
-      *reinterpret_cast<u32x4*>(xl + 16 * r + 4 * d) =
-          u32x4{xp.p[0][4 * d], xp.p[0][4 * d + 1], xp.p[0][4 * d + 2], xp.p[0][4 * d + 3]};
-    sums[2 * r] = xp.d136[0];
-    sums[2 * r + 1] = xp.sum[0];
+      *reinterpret_cast<u32x4*>(xl + 16 * r + 4 * d) = u32x4{pr[4 * d], pr[4 * d + 1], pr[4 * d + 2], pr[4 * d + 3]};
+    sums[2 * r] = f;
+    sums[2 * r + 1] = X;
+  }
+}
+
+// Two-plane bf16 records of TB rows of fp32 h: record r at xl[32 r] (plane 0
+// pairs, then plane 1 pairs, chain order), its sum of h at xl[32 R + r].
+// Plane 0 is bf16(h) and plane 1 bf16(h - plane 0), both rounded to nearest
+// even, so each h is carried to 16 significant bits.
+template <int TB>
+__device__ __forceinline__ void moe_stage_h(const float* base, const int64_t* rows, int TC, uint32_t* xl) {
+  const int R = TB * TC * 8;
+  float* sums = reinterpret_cast<float*>(xl + 32 * R);
+  for (int r = threadIdx.x; r < R; r += blockDim.x) {
+    const int m = r / (TC * 8), rem = r - m * TC * 8;
+    const float* p = base + rows[m] + 32 * rem;
+    float h[32];
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(p + 4 * d);
+      h[4 * d] = v.x; h[4 * d + 1] = v.y; h[4 * d + 2] = v.z; h[4 * d + 3] = v.w;
+    }
+    float X = 0.f;
+#pragma unroll
+    for (int k = 0; k < 32; ++k) X += h[k];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const int k0 = 8 * (t >> 2) + (t & 3), k1 = k0 + 4;   // chain pair t: (x[k0], x[k0 + 4])
+      const __bf16 a0 = (__bf16)h[k0], a1 = (__bf16)h[k1];
+      const __bf16 b0 = (__bf16)(h[k0] - (float)a0), b1 = (__bf16)(h[k1] - (float)a1);
+      xl[32 * r + t] = __builtin_bit_cast(uint32_t, bf16x2{a0, a1});
+      xl[32 * r + 16 + t] = __builtin_bit_cast(uint32_t, bf16x2{b0, b1});
+    }
+    sums[r] = X;
   }
 }
 
 // acc += the held chunks [0, nc) (tile columns c0 + j) against the staged rows.
 template <int KIND, int TB, int CPW>
 __device__ __forceinline__ void moe_chunks(const Q4Chunk<KIND> (&ch)[CPW], int nc, int c0, int TC,
-                                           const uint32_t* xl, uint32_t kMask, uint32_t kMagic,
-                                           float (&acc)[4][TB]) {
+                                           const uint32_t* xl, const Q4Consts& k, float (&acc)[4][TB]) {
   const int R = TB * TC * 8, g = threadIdx.x & 7;
   const float* sums = reinterpret_cast<const float*>(xl + 16 * R);
 #pragma unroll
   for (int j = 0; j < CPW; ++j) {
     if (j < nc) {
-      XPrep<TB> xp;
+      XRec<TB> xp;
 #pragma unroll
       for (int m = 0; m < TB; ++m) {
         const int r = (m * TC + c0 + j) * 8 + g;
@@ -425,10 +458,40 @@ __device__ __forceinline__ void moe_chunks(const Q4Chunk<KIND> (&ch)[CPW], int n
           xp.p[m][4 * d + 2] = v.z;
           xp.p[m][4 * d + 3] = v.w;
         }
-        xp.d136[m] = sums[2 * r];
-        xp.sum[m] = sums[2 * r + 1];
+        xp.f[m] = sums[2 * r];
+        xp.X[m] = sums[2 * r + 1];
       }
-      q4_compute<KIND, TB>(ch[j], xp, kMask, kMagic, acc);
+      q4_compute<KIND, TB>(ch[j], xp, k, acc);
+    }
+  }
+}
+
+// The same against two-plane records of h (moe_stage_h).
+template <int KIND, int TB, int CPW>
+__device__ __forceinline__ void moe_chunks_h(const Q4Chunk<KIND> (&ch)[CPW], int nc, int c0, int TC,
+                                             const uint32_t* xl, const Q4Consts& k, float (&acc)[4][TB]) {
+  const int R = TB * TC * 8, g = threadIdx.x & 7;
+  const float* sums = reinterpret_cast<const float*>(xl + 32 * R);
+#pragma unroll
+  for (int j = 0; j < CPW; ++j) {
+    if (j < nc) {
+      XRecB<TB, 2> xp;
+#pragma unroll
+      for (int m = 0; m < TB; ++m) {
+        const int r = (m * TC + c0 + j) * 8 + g;
+#pragma unroll
+        for (int pl = 0; pl < 2; ++pl)
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(xl + 32 * r + 16 * pl + 4 * d);
+            xp.p[m][pl][4 * d] = v.x;
+            xp.p[m][pl][4 * d + 1] = v.y;
+            xp.p[m][pl][4 * d + 2] = v.z;
+            xp.p[m][pl][4 * d + 3] = v.w;
+          }
+        xp.X[m] = sums[r];
+      }
+      q4_compute_b<KIND, TB, 2>(ch[j], xp, k, acc);
     }
   }
 }
@@ -476,9 +539,7 @@ __global__ __launch_bounds__(256) void k_moe_gateup_s(MoeArgs a) {
   const int TC = a.D / 256, P = a.T * a.k;
   const int rows_r = a.De / 32, rows_s = a.Ds / 32;
   const int n_items = nseg * rows_r + rows_s;
-  uint32_t kMask = 0x000F000Fu, kMagic = 0x43004300u;
-  asm volatile("" : "+s"(kMask));
-  asm volatile("" : "+v"(kMagic));
+  const Q4Consts kc = q4_consts();
   const int half = wave & 1;
   const int c0 = half * TC / 2, nc = (half + 1) * TC / 2 - c0;
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
@@ -515,7 +576,7 @@ __global__ __launch_bounds__(256) void k_moe_gateup_s(MoeArgs a) {
       __syncthreads();
       for (int r0 = 0; r0 < nc; r0 += CPW) {
         if (nc > CPW) moe_load<KIND, CPW>(row, c0 + r0, min(CPW, nc - r0), lane, ch);
-        moe_chunks<KIND, TB, CPW>(ch, min(CPW, nc - r0), c0 + r0, TC, xl, kMask, kMagic, acc);
+        moe_chunks<KIND, TB, CPW>(ch, min(CPW, nc - r0), c0 + r0, TC, xl, kc, acc);
       }
       q4_lane_reduce<TB>(acc);
       if ((lane & 7) == 0) {
@@ -531,14 +592,13 @@ __global__ __launch_bounds__(256) void k_moe_gateup_s(MoeArgs a) {
           const float g = red[0][r][m] + red[1][r][m];
           const float u = red[2][r][m] + red[3][r][m];
           const float hv = g / (1.0f + expf(-g)) * u;
-          const uint16_t hb = __builtin_bit_cast(uint16_t, (__bf16)hv);
           const int col = 32 * tr + r;
           const int pos = shared ? P + b0 + m : start + b0 + m;
-          a.hbuf[(size_t)pos * a.hstride + col] = hb;
+          a.hbuf[(size_t)pos * a.hstride + col] = hv;
           if (shared) {
-            if (a.dbg_h_shared) a.dbg_h_shared[(size_t)(b0 + m) * a.Ds + col] = hb;
+            if (a.dbg_h_shared) a.dbg_h_shared[(size_t)(b0 + m) * a.Ds + col] = hv;
           } else if (a.dbg_h) {
-            a.dbg_h[(size_t)moe_sorted<SMALL>(a, rt, pos) * a.De + col] = hb;
+            a.dbg_h[(size_t)moe_sorted<SMALL>(a, rt, pos) * a.De + col] = hv;
           }
         }
       }
@@ -561,9 +621,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_moe_down_s(MoeArgs a, int ks_r, 
   const int rows = a.D / 32, P = a.T * a.k;
   const int gr = rows / (WAVES / ks_r), gs = a.Ds ? rows / (WAVES / ks_s) : 0;
   const int n_items = nseg * gr + gs;
-  uint32_t kMask = 0x000F000Fu, kMagic = 0x43004300u;
-  asm volatile("" : "+s"(kMask));
-  asm volatile("" : "+v"(kMagic));
+  const Q4Consts kc = q4_consts();
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
     const bool shared = item >= nseg * gr;
     int e = 0, start = 0, cnt = a.T, grp;
@@ -598,11 +656,11 @@ __global__ __launch_bounds__(64 * WAVES) void k_moe_down_s(MoeArgs a, int ks_r, 
       // weights first (held across batches when the wave's run fits), then this batch's rows
       if (b0 == 0 && nc <= CPW) moe_load<KIND, CPW>(row, c0, nc, lane, ch);
       __syncthreads();
-      moe_stage<TB>(a.hbuf, s_rows, TC, xl);
+      moe_stage_h<TB>(a.hbuf, s_rows, TC, xl);
       __syncthreads();
       for (int r0 = 0; r0 < nc; r0 += CPW) {
         if (nc > CPW) moe_load<KIND, CPW>(row, c0 + r0, min(CPW, nc - r0), lane, ch);
-        moe_chunks<KIND, TB, CPW>(ch, min(CPW, nc - r0), c0 + r0, TC, xl, kMask, kMagic, acc);
+        moe_chunks_h<KIND, TB, CPW>(ch, min(CPW, nc - r0), c0 + r0, TC, xl, kc, acc);
       }
       q4_lane_reduce<TB>(acc);
       if ((lane & 7) == 0) {
@@ -652,9 +710,7 @@ __global__ __launch_bounds__(256) void k_moe_gateup(MoeArgs a) {
   const int half = wave & 1;
   const int c0 = half * TC / 2, nc = (half + 1) * TC / 2 - c0;
   constexpr int CPW = kMoeCpwBatch;
-  uint32_t kMask = 0x000F000Fu, kMagic = 0x43004300u;
-  asm volatile("" : "+s"(kMask));
-  asm volatile("" : "+v"(kMagic));
+  const Q4Consts kc = q4_consts();
   const int nbr = (int)a.hdr[2];
   for (int item = blockIdx.x;; item += gridDim.x) {
     MoeItem it;
@@ -673,7 +729,7 @@ __global__ __launch_bounds__(256) void k_moe_gateup(MoeArgs a) {
     __syncthreads();
     for (int r0 = 0; r0 < nc; r0 += CPW) {
       if (nc > CPW) moe_load<KIND, CPW>(row, c0 + r0, min(CPW, nc - r0), lane, ch);
-      moe_chunks<KIND, TB, CPW>(ch, min(CPW, nc - r0), c0 + r0, TC, xl, kMask, kMagic, acc);
+      moe_chunks<KIND, TB, CPW>(ch, min(CPW, nc - r0), c0 + r0, TC, xl, kc, acc);
     }
     q4_lane_reduce<TB>(acc);
     if ((lane & 7) == 0) {
@@ -689,13 +745,12 @@ __global__ __launch_bounds__(256) void k_moe_gateup(MoeArgs a) {
         const float g = red[0][r][m] + red[1][r][m];
         const float u = red[2][r][m] + red[3][r][m];
         const float hv = g / (1.0f + expf(-g)) * u;
-        const uint16_t hb = __builtin_bit_cast(uint16_t, (__bf16)hv);
         const int col = 32 * it.tr + r;
-        a.hbuf[(size_t)(it.pos0 + m) * a.hstride + col] = hb;
+        a.hbuf[(size_t)(it.pos0 + m) * a.hstride + col] = hv;
         if (it.shared) {
-          if (a.dbg_h_shared) a.dbg_h_shared[(size_t)(it.pos0 - P + m) * a.Ds + col] = hb;
+          if (a.dbg_h_shared) a.dbg_h_shared[(size_t)(it.pos0 - P + m) * a.Ds + col] = hv;
         } else if (a.dbg_h) {
-          a.dbg_h[(size_t)moe_item_pair(a, it, m) * a.De + col] = hb;
+          a.dbg_h[(size_t)moe_item_pair(a, it, m) * a.De + col] = hv;
         }
       }
     }
@@ -712,9 +767,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_moe_down(MoeArgs a, int ks_r, in
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int rows = a.D / 32;
   constexpr int CPW = kMoeCpwDown;
-  uint32_t kMask = 0x000F000Fu, kMagic = 0x43004300u;
-  asm volatile("" : "+s"(kMask));
-  asm volatile("" : "+v"(kMagic));
+  const Q4Consts kc = q4_consts();
   const int nbr = (int)a.hdr[2];
   for (int item = blockIdx.x;; item += gridDim.x) {
     MoeItem it;
@@ -737,11 +790,11 @@ __global__ __launch_bounds__(64 * WAVES) void k_moe_down(MoeArgs a, int ks_r, in
 #pragma unroll
       for (int m = 0; m < TB; ++m) acc[i][m] = 0.f;
     __syncthreads();
-    moe_stage<TB>(a.hbuf, s_rows, TC, xl);
+    moe_stage_h<TB>(a.hbuf, s_rows, TC, xl);
     __syncthreads();
     for (int r0 = 0; r0 < nc; r0 += CPW) {
       if (nc > CPW) moe_load<KIND, CPW>(row, c0 + r0, min(CPW, nc - r0), lane, ch);
-      moe_chunks<KIND, TB, CPW>(ch, min(CPW, nc - r0), c0 + r0, TC, xl, kMask, kMagic, acc);
+      moe_chunks_h<KIND, TB, CPW>(ch, min(CPW, nc - r0), c0 + r0, TC, xl, kc, acc);
     }
     q4_lane_reduce<TB>(acc);
     if ((lane & 7) == 0) {
@@ -826,9 +879,8 @@ static hipError_t moe_run(const MoeArgs& a, hipStream_t s) {
   // (prompt blocks): the route kernel, then one work item per (token batch,
   // tile row), which spreads a popular expert's batches over many CUs (holding
   // its chunks in one workgroup serialises them, measured slower).
-  const int rec = 8 * 72 * TB;
-  const int xl_gu = rec * (a.D / 256);
-  const int xl_dn = rec * ((a.De > a.Ds ? a.De : a.Ds) / 256);
+  const int xl_gu = kMoeRecGateUp * TB * (a.D / 256);
+  const int xl_dn = kMoeRecDown * TB * ((a.De > a.Ds ? a.De : a.Ds) / 256);
   const bool small = P <= kMoeSmallPairs;
   if (small && xl_gu <= 65536 && xl_dn <= 65536) {
     const int gu_items = nseg_max * (a.De / 32) + a.Ds / 32;

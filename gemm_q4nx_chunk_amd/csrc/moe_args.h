@@ -30,9 +30,9 @@ struct MoeArgs {
   int32_t tb;        // tokens per work item (1 or 4)
   int32_t hstride;   // row stride of hbuf, max(De, Ds)
   // optional stage outputs
-  uint16_t* dbg_h;
+  float* dbg_h;
   float* dbg_d;
-  uint16_t* dbg_h_shared;
+  float* dbg_h_shared;
   float* dbg_d_shared;
   // workspace
   uint32_t* hdr;     // [0] error word, [1] segments, [2] routed batches
@@ -41,7 +41,7 @@ struct MoeArgs {
   int32_t* batch0;   // [P + 1] first routed batch of each segment
   int32_t* btab;     // [P][kMoeBatchInts] per routed batch: expert, first sorted position,
                      // tokens, -, then its tokens' ids and pair indices (4 each)
-  uint16_t* hbuf;    // [P + T][hstride] bf16 h (routed by sorted position, shared at P + t)
+  float* hbuf;       // [P + T][hstride] fp32 h (routed by sorted position, shared at P + t)
   float* dbuf;       // [P + T][D] fp32 d (routed by pair index, shared at P + t)
 };
 
@@ -60,11 +60,17 @@ inline MoeWsLayout moe_ws_layout(int P, int T, int D, int hstride) {
   l.seg = o;    o = up(o + (size_t)P * 12);
   l.batch0 = o; o = up(o + (size_t)(P + 1) * 4);
   l.btab = o;   o = up(o + (size_t)P * kMoeBatchInts * 4);
-  l.hbuf = o;   o = up(o + (size_t)(P + T) * hstride * 2);
+  l.hbuf = o;   o = up(o + (size_t)(P + T) * hstride * 4);
   l.dbuf = o;   o = up(o + (size_t)(P + T) * D * 4);
   l.total = o;
   return l;
 }
+
+// Prepared-record bytes per (token, tile column) in LDS: gate/up take fp16
+// records of bf16 activations (8 groups x 72 B), down takes two-plane bf16
+// records of the fp32 h (8 groups x 132 B).
+constexpr int kMoeRecGateUp = 8 * 72;
+constexpr int kMoeRecDown = 8 * 132;
 
 hipError_t launch_moe(int kind, const MoeArgs& a, hipStream_t s);
 

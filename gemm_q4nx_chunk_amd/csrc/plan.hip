@@ -58,9 +58,7 @@ __global__ __launch_bounds__(256) void k_plan(PlanArgs a) {
   __shared__ float red[4][32][M];
   __shared__ uint32_t s_old;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  uint32_t kMask = 0x000F000Fu, kMagic = 0x43004300u;
-  asm volatile("" : "+s"(kMask));
-  asm volatile("" : "+v"(kMagic));
+  const Q4Consts kc = q4_consts();
   int confirmed = 0;   // every phase below this one is known to be finished
 
   for (int u = blockIdx.x; u < a.n_units; u += gridDim.x) {
@@ -134,9 +132,9 @@ __global__ __launch_bounds__(256) void k_plan(PlanArgs a) {
 #pragma unroll
       for (int i = 0; i < CPW; ++i) {
         if (i < nc) {
-          XPrep<M> xp;
-          x_prep_raw<M>(xr[i], xp);
-          q4_compute<KIND, M>(ch[i], xp, kMask, kMagic, acc);
+          XRecB<M> xp;   // activations per lane and chunk: bf16 records
+          x_records_b<M>(xr[i], xp);
+          q4_compute_b<KIND, M, 1>(ch[i], xp, kc, acc);
         }
       }
       q4_lane_reduce<M>(acc);

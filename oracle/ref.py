@@ -94,20 +94,25 @@ def moe_combine_ref(d, p, d_shared=None, a_d=None, a_shared=None):
     return y, a
 
 
-def moe_layer_ref(X_bits, ids, p, expert_w, shared_w=None, n_experts: int | None = None):
+def moe_layer_ref(X_bits, ids, p, expert_w, shared_w=None, n_experts: int | None = None,
+                  with_scale: bool = False):
     """The whole MoE layer in float64.
 
     X_bits [T, D] bf16 bits; ids [T, k] int; p [T, k] float; expert_w(e) returns
     (G, U, Dn) float64 weights of expert e; shared_w is (G, U, Dn) or None.
     Slots whose id is outside [0, n_experts) contribute nothing.
-    Returns y [T, D] float64.
+    Returns y [T, D] float64, and with ``with_scale`` also the layer's error
+    scale a = sum_j |p| (|Dn_e| |h_e|) + |Dn_s| |h_s| (the combine's scale with
+    each down projection's sum |w h|).
     """
     X = _x64(X_bits)
     T = X.shape[0]
     y = np.zeros((T, X.shape[1]))
+    a = np.zeros((T, X.shape[1]))
     cache = {}
     for t in range(T):
         acc = np.zeros(X.shape[1])
+        sc = np.zeros(X.shape[1])
         for j in range(ids.shape[1]):
             e = int(ids[t, j])
             if n_experts is not None and not (0 <= e < n_experts):
@@ -117,11 +122,15 @@ def moe_layer_ref(X_bits, ids, p, expert_w, shared_w=None, n_experts: int | None
             G, U, Dn = cache[e]
             h = swiglu(G @ X[t], U @ X[t])
             acc += float(p[t, j]) * (Dn @ h)
+            sc += abs(float(p[t, j])) * (np.abs(Dn) @ np.abs(h))
         if shared_w is not None:
             G, U, Dn = shared_w
-            acc += Dn @ swiglu(G @ X[t], U @ X[t])
+            h = swiglu(G @ X[t], U @ X[t])
+            acc += Dn @ h
+            sc += np.abs(Dn) @ np.abs(h)
         y[t] = acc
-    return y
+        a[t] = sc
+    return (y, a) if with_scale else y
 
 
 # ----------------------------------------------------------------------------

@@ -79,12 +79,8 @@ def test_q8_layouts_of_one_weight(M):
     np.testing.assert_array_equal(gemv(dB, N, K, "q8", x, "B").view(np.uint32), yb.view(np.uint32))
 
 
-@pytest.mark.parametrize("kind,layout", KINDS)
-def test_one_hot_activation_gives_the_column(kind, layout):
-    N, K = 64, 512
-    ch = _gen(kind, layout, N, K, "onehot")
+def _one_hot_check(ch, kind, layout, N, K, cols):
     W32 = oracle.weights_f32(ch, kind, N, K, layout)
-    cols = [0, 5, 31, 32, 255, 256, 511]
     x = np.zeros((len(cols), K), np.uint16)
     for i, k in enumerate(cols):
         x[i, k] = 0x3F80
@@ -92,11 +88,30 @@ def test_one_hot_activation_gives_the_column(kind, layout):
         xs = x[i0:i0 + 4]
         y = gemv(dev_u8(ch), N, K, kind, xs, layout)
         for j in range(xs.shape[0]):
-            k = cols[i0 + j]
-            if kind in ("q8",):
-                np.testing.assert_array_equal(y[j], W32[:, k])          # d*c exact
-            else:
-                np.testing.assert_allclose(y[j], W32[:, k], rtol=2e-3, atol=0)
+            np.testing.assert_array_equal(y[j].view(np.uint32), W32[:, cols[i0 + j]].view(np.uint32))
+
+
+@pytest.mark.parametrize("kind,layout", KINDS)
+def test_one_hot_activation_gives_the_column(kind, layout):
+    """x = e_k returns column k of the decoded weights bit for bit: the signed
+    codes and their center make s (c - c0) + (z + c0 s) one rounding of s c + z."""
+    N, K = 64, 512
+    _one_hot_check(_gen(kind, layout, N, K, "onehot"), kind, layout, N, K, [0, 5, 31, 32, 255, 256, 511])
+
+
+def test_one_hot_q4_k_signed_metadata():
+    """The same pin on Q4_K with S of either sign and M = -dmin <= 0 (as a GGUF
+    Q4_K maps), sc/mn over 0..255, at moderate |M mn / (S sc)| (below 2^8, so
+    z + c0 s is exact in fp32)."""
+    N, K = 64, 512
+    g = synth.rng("gpu-gemv", "onehot-q4k-signed")
+    codes = g.integers(0, 16, (N, K), dtype=np.uint8)
+    sc = g.integers(16, 256, (N, K // 32), dtype=np.uint8)
+    mn = g.integers(0, 256, (N, K // 32), dtype=np.uint8)
+    S = synth.bf16_bits((g.standard_normal((N, K // 256)) * 1e-3).astype(np.float32))
+    Mv = synth.bf16_bits((-np.abs(g.standard_normal((N, K // 256))) * 1e-3).astype(np.float32))
+    ch = synth.pack_q4_k(codes, sc, mn, S, Mv)
+    _one_hot_check(ch, "q4_k", None, N, K, [0, 7, 33, 300, 511])
 
 
 def test_q4_0_style_zero_rows_are_exactly_zero():

@@ -1,12 +1,13 @@
 """GPU routed-expert MoE layer (q4nx_moe_experts) vs the float64 oracle.
 
 Stage-wise checks:
-  h  vs silu(G x) * (U x) from the oracle, within the propagated GEMV bar plus
-     the bf16 rounding of h (2^-8 |h|);
-  d  vs the oracle's Down applied to the GPU's own h, within 2e-3 * sum |w h|;
+  h  vs silu(G x) * (U x) from the oracle, within the GEMV bar of g and u
+     propagated through silu(g) * u;
+  d  vs the oracle's Down applied to the GPU's own h (fp32), within
+     2e-3 * sum |w h|;
   y  vs the oracle combine of the GPU's own d (fp32 sum of k+1 terms);
-and the end-to-end error against the all-float64 layer is bounded loosely
-(it carries the bf16 rounding of h).
+and end to end against the all-float64 layer within 2e-3 * a with
+a = sum_j |p| sum |Down| |h| + the shared expert's sum |Down_s| |h_s|.
 """
 import numpy as np
 import pytest
@@ -78,10 +79,10 @@ class Layer:
         Y = torch.full((T, self.D), float("nan"), dtype=torch.float32, device="cuda")
         out = {}
         if dbg:
-            out = {"h": torch.zeros((T, k, self.De), dtype=torch.int16, device="cuda"),
+            out = {"h": torch.zeros((T, k, self.De), dtype=torch.float32, device="cuda"),
                    "d": torch.zeros((T, k, self.D), dtype=torch.float32, device="cuda")}
             if self.Ds:
-                out["h_shared"] = torch.zeros((T, self.Ds), dtype=torch.int16, device="cuda")
+                out["h_shared"] = torch.zeros((T, self.Ds), dtype=torch.float32, device="cuda")
                 out["d_shared"] = torch.zeros((T, self.D), dtype=torch.float32, device="cuda")
         q().moe_experts(self.L, dev_bf16(X), dev_i32(ids), dev_f32(p), Y, T, k, ws, dbg=out or None)
         res = {name: host(t) for name, t in out.items()}
@@ -111,8 +112,8 @@ def _check_stages(layer, X, ids, p, r):
             ag, au = np.abs(G) @ np.abs(xs[t]), np.abs(U) @ np.abs(xs[t])
             h_ref = oracle.swiglu(g, u)
             sil = oracle.silu(g)
-            bound = 2e-3 * (1.1 * np.abs(u) * ag + np.abs(sil) * au) + 2.0 ** -8 * np.abs(h_ref) + 1e-30
-            hg = _x64(r["h"][t, j].view(np.uint16))
+            bound = 2e-3 * (1.1 * np.abs(u) * ag + np.abs(sil) * au) + 1e-30
+            hg = r["h"][t, j].astype(np.float64)
             worst["h"] = max(worst["h"], float(np.max(np.abs(hg - h_ref) / bound)))
             dref, ad = oracle.gemv_ref(Dn, hg[None, :], x_is_bits=False)
             worst["d"] = max(worst["d"], oracle.tol_ratio(r["d"][t, j][None, :], dref, ad))
@@ -123,9 +124,8 @@ def _check_stages(layer, X, ids, p, r):
             g, u = G @ xs[t], U @ xs[t]
             ag, au = np.abs(G) @ np.abs(xs[t]), np.abs(U) @ np.abs(xs[t])
             h_ref = oracle.swiglu(g, u)
-            bound = (2e-3 * (1.1 * np.abs(u) * ag + np.abs(oracle.silu(g)) * au)
-                     + 2.0 ** -8 * np.abs(h_ref) + 1e-30)
-            hg = _x64(r["h_shared"][t].view(np.uint16))
+            bound = 2e-3 * (1.1 * np.abs(u) * ag + np.abs(oracle.silu(g)) * au) + 1e-30
+            hg = r["h_shared"][t].astype(np.float64)
             worst["h"] = max(worst["h"], float(np.max(np.abs(hg - h_ref) / bound)))
             dref, ad = oracle.gemv_ref(Dn, hg[None, :], x_is_bits=False)
             worst["d"] = max(worst["d"], oracle.tol_ratio(r["d_shared"][t][None, :], dref, ad))
@@ -138,21 +138,10 @@ def _check_stages(layer, X, ids, p, r):
     if layer.Ds:
         scale += np.abs(r["d_shared"])
     assert np.all(np.abs(r["y"] - y_ref) <= (k + 2) * 2.0 ** -24 * scale + 1e-30)
-    # end to end against the all-float64 layer (bf16 h inside: loose bound)
-    ye = oracle.moe_layer_ref(X, ids, p, layer.W, layer.Wsh(), n_experts=layer.n)
-    ae = np.zeros_like(ye)
-    for t in range(T):
-        for j in range(k):
-            e = int(ids[t, j])
-            if 0 <= e < layer.n:
-                G, U, Dn = layer.W(e)
-                hh = np.abs(oracle.swiglu(G @ xs[t], U @ xs[t]))
-                ae[t] += abs(float(p[t, j])) * (np.abs(Dn) @ hh)
-        if layer.Ds:
-            G, U, Dn = layer.Wsh()
-            ae[t] += np.abs(Dn) @ np.abs(oracle.swiglu(G @ xs[t], U @ xs[t]))
-    e2e = float(np.max(np.abs(r["y"] - ye) / (ae + 1e-30)))
-    assert e2e <= 2e-2, e2e
+    # end to end against the all-float64 layer
+    ye, ae = oracle.moe_layer_ref(X, ids, p, layer.W, layer.Wsh(), n_experts=layer.n, with_scale=True)
+    e2e = oracle.tol_ratio(r["y"], ye, ae)
+    assert e2e <= 1.0, e2e
     return worst, e2e
 
 
