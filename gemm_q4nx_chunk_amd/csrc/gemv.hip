@@ -108,17 +108,18 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_q4x(const GemvBatch b) {
   const int c0 = part * TC / ks, c1 = (part + 1) * TC / ks;
   const int R = M * TC * 8;
 
-  // 1. activations of record r = (m * TC + c) * 8 + g: 32 bf16 at x[m][32 * (8c + g)]
+  // 1. activations: record r = (m * TC + c) * 8 + g holds the 32 bf16 at
+  // x[m][32 * (8c + g)]; four consecutive lanes build it, part d = q & 3 of
+  // part index q taking x[m][32 * (8c + g) + 8d .. + 7] (16 bytes)
   const __amdgpu_buffer_rsrc_t xrs = make_rsrc(J.x, (uint32_t)(((M - 1) * J.ldx + TC * 256) * 2));
-  u32x4 xr[XRP][4];
+  auto xpart_off = [&](int q) {
+    const int r = q >> 2, m = r / (TC * 8), rem = r - m * TC * 8;
+    return (uint32_t)(m * J.ldx + 32 * rem + 8 * (q & 3)) * 2;   // q >= 4R: m >= M, past the resource
+  };
+  u32x4 xr[XRP];
 #pragma unroll
-  for (int p = 0; p < XRP; ++p) {
-    const int r = tid + NT * p, m = r / (TC * 8), rem = r - m * TC * 8;
-    const uint32_t off = (uint32_t)(m * J.ldx + 32 * rem) * 2;   // r >= R: m >= M, past the resource
-#pragma unroll
-    for (int d = 0; d < 4; ++d)
-      xr[p][d] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs, off + 16 * d, 0, 0));
-  }
+  for (int i = 0; i < XRP; ++i)
+    xr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs, xpart_off(tid + NT * i), 0, 0));
   // 2. the first D chunks of the wave's run
   const __amdgpu_buffer_rsrc_t wrs =
       make_rsrc(J.w + ((size_t)tr * TC + c0) * CB, (uint32_t)((c1 - c0) * CB));
@@ -130,30 +131,24 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_q4x(const GemvBatch b) {
   }
   // 3. records to LDS: pairs at xl[16 r], (f, X) at xl[16 R + 2 r]
   float* sums = reinterpret_cast<float*>(xl + 16 * R);
-  auto put = [&](int r, const u32x4 (&v)[4]) {
-    uint32_t pr[16];
+  auto put = [&](int q, const u32x4 v) {   // the four lanes of a record come together
+    uint32_t pr[4];
     float f, X;
-    x_record(v, pr, f, X);
+    x_record_part(v, pr, f, X);
+    const int r = q >> 2;
     if (r < R) {
-#pragma unroll
-      for (int d = 0; d < 4; ++d)
-        *reinterpret_cast<u32x4*>(xl + 16 * r + 4 * d) = u32x4{pr[4 * d], pr[4 * d + 1], pr[4 * d + 2], pr[4 * d + 3]};
-      sums[2 * r] = f;
-      sums[2 * r + 1] = X;
+      *reinterpret_cast<u32x4*>(xl + 16 * r + 4 * (q & 3)) = u32x4{pr[0], pr[1], pr[2], pr[3]};
+      if ((q & 3) == 0) {
+        sums[2 * r] = f;
+        sums[2 * r + 1] = X;
+      }
     }
   };
 #pragma unroll
-  for (int p = 0; p < XRP; ++p) put(tid + NT * p, xr[p]);
-  // long-K launches: the records past the first XRP per thread, loaded and prepared in turn
-  for (int r = tid + NT * XRP; r < R; r += NT) {
-    const int m = r / (TC * 8), rem = r - m * TC * 8;
-    const uint32_t off = (uint32_t)(m * J.ldx + 32 * rem) * 2;
-    u32x4 v[4];
-#pragma unroll
-    for (int d = 0; d < 4; ++d)
-      v[d] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs, off + 16 * d, 0, 0));
-    put(r, v);
-  }
+  for (int i = 0; i < XRP; ++i) put(tid + NT * i, xr[i]);
+  // long-K launches: the parts past the first XRP per thread, loaded and built in turn
+  for (int q = tid + NT * XRP; q < 4 * R; q += NT)
+    put(q, __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs, xpart_off(q), 0, 0)));
   __syncthreads();
 
   const Q4Consts k = q4_consts();

@@ -196,14 +196,79 @@ __device__ __forceinline__ float bf16_pairs_sum(const uint32_t (&p)[16]) {
   return e;
 }
 
-// One fp16 record from the 32 bf16 activations of a group (see above).
-// p: pairs in chain order; f: 2^-sigma (fp16 record) or -1 (bf16 record);
-// X: sum of the 32 values.
-__device__ __forceinline__ void x_record(const u32x4 (&v)[4], uint32_t (&p)[16], float& f, float& X) {
+// Quad reductions: the 4 consecutive lanes of a record meet through DPP
+// quad permutations (xor 1, then xor 2), so every lane ends with the result.
+// Each permuted value is read once, outside any branch: a DPP read from a lane
+// that is switched off in the exec mask does not return its value.
+__device__ __forceinline__ uint32_t quad_xor1(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+}
+__device__ __forceinline__ uint32_t quad_xor2(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+}
+__device__ __forceinline__ uint32_t quad_max_u32(uint32_t v) {
+  v = __builtin_elementwise_max(v, quad_xor1(v));
+  return __builtin_elementwise_max(v, quad_xor2(v));
+}
+__device__ __forceinline__ float quad_sum(float v) {
+  v += __uint_as_float(quad_xor1(__float_as_uint(v)));
+  return v + __uint_as_float(quad_xor2(__float_as_uint(v)));
+}
+
+// One quarter of an fp16 record (see above), built by the 4 consecutive lanes
+// that share the record: this lane holds v = x[8d .. 8d+7] of the group (d =
+// its place in the quad) and gets the chain pairs 4d .. 4d+3, p[j] = (x[8d+j],
+// x[8d+j+4]), plus the record's f = 2^-sigma (or -1 for a bf16 record) and
+// X = sum of the 32 values.  Every lane of the quad must call it.
+__device__ __forceinline__ void x_record_part(const u32x4 v, uint32_t (&p)[4], float& f, float& X) {
   // largest magnitude (as bits) and a lower bound on the smallest nonzero
   // exponent: (b - 1) & 0x7F80 is the exponent field of b, one less when the
   // mantissa is zero (conservative), 0 for a subnormal, and 0x7F80 for a zero
   // (which then never wins the minimum).
+  u16x2 mx = {0, 0}, mn = {0x7F80, 0x7F80};
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const u16x2 a = __builtin_bit_cast(u16x2, v[t] & 0x7FFF7FFFu);
+    mx = __builtin_elementwise_max(mx, a);
+    mn = __builtin_elementwise_min(mn, a - u16x2{1, 1});
+  }
+  const uint32_t top = quad_max_u32(mx.x > mx.y ? mx.x : mx.y);   // bits of max |x|
+  // min over the quad through max of the complement
+  const uint32_t mnl = (mn.x < mn.y ? mn.x : mn.y) & 0x7F80u;
+  const uint32_t low = 0x7F80u - quad_max_u32(0x7F80u - mnl);
+  const int E = (int)(top >> 7), Emin = (int)(low >> 7);
+  // exact in fp16 after scaling: max in [2^15, 2^16), every nonzero value
+  // >= 2^-17 (exponent field >= E - 32); keep 2^sigma within 2^64 either way
+  const bool fast = top == 0 || (E >= 78 && E <= 206 && Emin >= E - 32);
+  float xs;
+  if (fast) {
+    const float up = top == 0 ? 1.f : __uint_as_float((uint32_t)(269 - E) << 23);   // 2^sigma, sigma = 142 - E
+    f = top == 0 ? 1.f : __uint_as_float((uint32_t)(E - 15) << 23);                // 2^-sigma
+    p[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(bf16lo(v.x) * up, bf16lo(v.z) * up));
+    p[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(bf16hi(v.x) * up, bf16hi(v.z) * up));
+    p[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(bf16lo(v.y) * up, bf16lo(v.w) * up));
+    p[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(bf16hi(v.y) * up, bf16hi(v.w) * up));
+    float e = 0.f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) e = dot2f16(0x3C003C00u, p[t], e);   // (1, 1)
+    xs = e * f;
+  } else {
+    // v_perm_b32 byte select: 0..3 pick bytes of the second operand, 4..7 of the first.
+    p[0] = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);   // (x0, x4)
+    p[1] = __builtin_amdgcn_perm(v.z, v.x, 0x07060302u);   // (x1, x5)
+    p[2] = __builtin_amdgcn_perm(v.w, v.y, 0x05040100u);   // (x2, x6)
+    p[3] = __builtin_amdgcn_perm(v.w, v.y, 0x07060302u);   // (x3, x7)
+    f = -1.f;
+    float e = 0.f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) e = dot2bf16(0x3F803F80u, p[t], e);   // (1, 1)
+    xs = e;
+  }
+  X = quad_sum(xs);
+}
+
+// The same record built by one lane from all 32 values (v[d] = x[8d .. 8d+7]).
+__device__ __forceinline__ void x_record(const u32x4 (&v)[4], uint32_t (&p)[16], float& f, float& X) {
   u16x2 mx = {0, 0}, mn = {0x7F80, 0x7F80};
 #pragma unroll
   for (int d = 0; d < 4; ++d)
@@ -211,18 +276,15 @@ __device__ __forceinline__ void x_record(const u32x4 (&v)[4], uint32_t (&p)[16],
     for (int t = 0; t < 4; ++t) {
       const u16x2 a = __builtin_bit_cast(u16x2, v[d][t] & 0x7FFF7FFFu);
       mx = __builtin_elementwise_max(mx, a);
-      const u16x2 e = __builtin_bit_cast(u16x2, __builtin_bit_cast(uint32_t, a - u16x2{1, 1}) & 0x7F807F80u);
-      mn = __builtin_elementwise_min(mn, e);
+      mn = __builtin_elementwise_min(mn, a - u16x2{1, 1});
     }
-  const uint32_t top = mx.x > mx.y ? mx.x : mx.y;        // bits of max |x|
-  const int E = (int)(top >> 7);                        // its exponent field
-  const int Emin = (int)((mn.x < mn.y ? mn.x : mn.y) >> 7);
-  // exact in fp16 after scaling: max in [2^15, 2^16), every nonzero value
-  // >= 2^-17 (exponent field >= E - 32); keep 2^sigma within 2^64 either way
+  const uint32_t top = mx.x > mx.y ? mx.x : mx.y;
+  const int E = (int)(top >> 7);
+  const int Emin = (int)(((mn.x < mn.y ? mn.x : mn.y) & 0x7F80u) >> 7);
   const bool fast = top == 0 || (E >= 78 && E <= 206 && Emin >= E - 32);
   if (fast) {
-    const float up = top == 0 ? 1.f : __uint_as_float((uint32_t)(269 - E) << 23);   // 2^sigma, sigma = 142 - E
-    f = top == 0 ? 1.f : __uint_as_float((uint32_t)(E - 15) << 23);                // 2^-sigma
+    const float up = top == 0 ? 1.f : __uint_as_float((uint32_t)(269 - E) << 23);
+    f = top == 0 ? 1.f : __uint_as_float((uint32_t)(E - 15) << 23);
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
       const u32x4 w = v[d];
@@ -299,11 +361,12 @@ __device__ __forceinline__ Q4Group q4_group(const Q4Chunk<KIND, SL>& c, int i) {
   // few ulps.  s = 0 or a NaN lands on 0 or 15: any c0 is exact.
   const float t = fminf(fmaxf(fmaf(-z, __builtin_amdgcn_rcpf(s), 0.5f), 0.f), 15.5f);
   const uint32_t c0 = (uint32_t)t;
+  const uint32_t c2 = (c0 << 16) | c0;   // c0 in both halves
   Q4Group gp;
   gp.s = s;
   gp.delta = fmaf((float)c0, s, z);
-  gp.pkl = 0xE400E400u | (c0 * 0x00010001u);
-  gp.pkh = 0xD400D400u | (c0 * 0x00100010u);
+  gp.pkl = 0xE400E400u | c2;
+  gp.pkh = (c2 << 4) | 0xD400D400u;
   return gp;
 }
 

@@ -388,20 +388,19 @@ template <int TB>
 __device__ __forceinline__ void moe_stage(const uint16_t* base, const int64_t* rows, int TC, uint32_t* xl) {
   const int R = TB * TC * 8;
   float* sums = reinterpret_cast<float*>(xl + 16 * R);
-  for (int r = threadIdx.x; r < R; r += blockDim.x) {
-    const int m = r / (TC * 8), rem = r - m * TC * 8;
-    const uint16_t* p = base + rows[m];
-    u32x4 v[4];
-#pragma unroll
-    for (int d = 0; d < 4; ++d) v[d] = load16(p + 32 * rem + 8 * d);
-    uint32_t pr[16];
+  // four consecutive lanes per record (blockDim is a multiple of 4, so a
+  // record's lanes run each iteration together); part d = q & 3 takes 8 values
+  for (int q = threadIdx.x; q < 4 * R; q += blockDim.x) {
+    const int r = q >> 2, m = r / (TC * 8), rem = r - m * TC * 8;
+    const u32x4 v = load16(base + rows[m] + 32 * rem + 8 * (q & 3));
+    uint32_t pr[4];
     float f, X;
-    x_record(v, pr, f, X);
-#pragma unroll
-    for (int d = 0; d < 4; ++d)
-      *reinterpret_cast<u32x4*>(xl + 16 * r + 4 * d) = u32x4{pr[4 * d], pr[4 * d + 1], pr[4 * d + 2], pr[4 * d + 3]};
-    sums[2 * r] = f;
-    sums[2 * r + 1] = X;
+    x_record_part(v, pr, f, X);
+    *reinterpret_cast<u32x4*>(xl + 16 * r + 4 * (q & 3)) = u32x4{pr[0], pr[1], pr[2], pr[3]};
+    if ((q & 3) == 0) {
+      sums[2 * r] = f;
+      sums[2 * r + 1] = X;
+    }
   }
 }
 
