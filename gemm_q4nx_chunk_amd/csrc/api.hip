@@ -629,9 +629,9 @@ int q4nx_moe_experts(const q4nx_moe_layer* L, const uint16_t* X, const int32_t* 
   if (!aligned(X, 16) || !aligned(ids, 4) || !aligned(p, 4) || !aligned(Y, 4))
     return fail(Q4NX_E_ALIGN, "moe: X must be 16-byte, ids/p/Y 4-byte aligned");
   {
-    // a batch's prepared activation records are staged in at most 64 KB of
-    // LDS: per token and tile column 576 bytes of x (gate/up) and 1056 bytes
-    // of h (down)
+    // a batch's prepared activation records (576 bytes per token and tile
+    // column, of x for gate/up and of h for down) are staged in at most 64 KB
+    // of LDS
     const int tb = T == 1 ? 1 : 4;
     const int inner = std::max(L->d_expert, L->d_shared);
     const int max_d = 65536 / (tb * q4nx::kMoeRecGateUp) * 256;

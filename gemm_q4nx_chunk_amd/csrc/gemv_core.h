@@ -267,6 +267,34 @@ __device__ __forceinline__ void x_record_part(const u32x4 v, uint32_t (&p)[4], f
   X = quad_sum(xs);
 }
 
+// One quarter of an fp16 record of fp32 activations (the MoE intermediate h),
+// built by four consecutive lanes: this lane holds a = h[8d .. 8d+3] and
+// b = h[8d+4 .. 8d+7].  The values are scaled by 2^sigma (largest in
+// [2^14, 2^15), sigma kept within +-64: an fp32 value just under 2^16 would
+// round to the fp16 infinity) and rounded to nearest fp16: each moves by at
+// most 2^-12 of its size, or, below the fp16 normal range (values under 2^-28
+// of the group's largest), by at most 2^-25 scaled units.
+// X is the fp32 sum of the 32 unrounded values.
+__device__ __forceinline__ void h_record_part(const f32x4 a, const f32x4 b, uint32_t (&p)[4], float& f,
+                                              float& X) {
+  const float m = fmaxf(fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))),
+                        fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w))));
+  const uint32_t top = quad_max_u32(__float_as_uint(m));   // |values| compare as their bits
+  int E = (int)(top >> 23);
+  E = E < 77 ? 77 : (E > 205 ? 205 : E);
+  const float up = __uint_as_float((uint32_t)(268 - E) << 23);   // 2^sigma, sigma = 141 - E
+  f = __uint_as_float((uint32_t)(E - 14) << 23);                // 2^-sigma
+  const f16x2 q0 = {(_Float16)(a.x * up), (_Float16)(b.x * up)};   // (h0, h4)
+  const f16x2 q1 = {(_Float16)(a.y * up), (_Float16)(b.y * up)};   // (h1, h5)
+  const f16x2 q2 = {(_Float16)(a.z * up), (_Float16)(b.z * up)};   // (h2, h6)
+  const f16x2 q3 = {(_Float16)(a.w * up), (_Float16)(b.w * up)};   // (h3, h7)
+  p[0] = __builtin_bit_cast(uint32_t, q0);
+  p[1] = __builtin_bit_cast(uint32_t, q1);
+  p[2] = __builtin_bit_cast(uint32_t, q2);
+  p[3] = __builtin_bit_cast(uint32_t, q3);
+  X = quad_sum(((a.x + a.y) + (a.z + a.w)) + ((b.x + b.y) + (b.z + b.w)));
+}
+
 // The same record built by one lane from all 32 values (v[d] = x[8d .. 8d+7]).
 __device__ __forceinline__ void x_record(const u32x4 (&v)[4], uint32_t (&p)[16], float& f, float& X) {
   u16x2 mx = {0, 0}, mn = {0x7F80, 0x7F80};

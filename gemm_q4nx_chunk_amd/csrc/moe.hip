@@ -15,9 +15,9 @@
 //           to the end, are never dereferenced, and set bit 0 of the error word.
 //   gateup  per (token batch, tile row): gate and up rows of the expert for up
 //           to TB tokens, h = silu(g) * u in fp32.
-//   down    per (token batch, group of tile rows): d = Down h, fp32; each h
-//           is taken as the sum of two bf16 values (its bf16 rounding and the
-//           bf16 rounding of the rest), 16 significant bits.
+//   down    per (token batch, group of tile rows): d = Down h, fp32; h is
+//           read as fp16 records with a power-of-two scale per 32 values
+//           (each h to 2^-12 of its size).
 //   combine y[t] = sum_j p[t][j] d[t][j] in slot order, then + the shared d.
 // No floating-point atomics anywhere; every sum has a fixed order.
 #include "gemv_core.h"
@@ -404,35 +404,24 @@ __device__ __forceinline__ void moe_stage(const uint16_t* base, const int64_t* r
   }
 }
 
-// Two-plane bf16 records of TB rows of fp32 h: record r at xl[32 r] (plane 0
-// pairs, then plane 1 pairs, chain order), its sum of h at xl[32 R + r].
-// Plane 0 is bf16(h) and plane 1 bf16(h - plane 0), both rounded to nearest
-// even, so each h is carried to 16 significant bits.
+// fp16 records of TB rows of fp32 h (h_record_part), in the layout of
+// moe_stage: four consecutive lanes per record.
 template <int TB>
 __device__ __forceinline__ void moe_stage_h(const float* base, const int64_t* rows, int TC, uint32_t* xl) {
   const int R = TB * TC * 8;
-  float* sums = reinterpret_cast<float*>(xl + 32 * R);
-  for (int r = threadIdx.x; r < R; r += blockDim.x) {
-    const int m = r / (TC * 8), rem = r - m * TC * 8;
-    const float* p = base + rows[m] + 32 * rem;
-    float h[32];
-#pragma unroll
-    for (int d = 0; d < 8; ++d) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(p + 4 * d);
-      h[4 * d] = v.x; h[4 * d + 1] = v.y; h[4 * d + 2] = v.z; h[4 * d + 3] = v.w;
+  float* sums = reinterpret_cast<float*>(xl + 16 * R);
+  for (int q = threadIdx.x; q < 4 * R; q += blockDim.x) {
+    const int r = q >> 2, m = r / (TC * 8), rem = r - m * TC * 8;
+    const float* p = base + rows[m] + 32 * rem + 8 * (q & 3);
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
+    uint32_t pr[4];
+    float f, X;
+    h_record_part(a, b, pr, f, X);
+    *reinterpret_cast<u32x4*>(xl + 16 * r + 4 * (q & 3)) = u32x4{pr[0], pr[1], pr[2], pr[3]};
+    if ((q & 3) == 0) {
+      sums[2 * r] = f;
+      sums[2 * r + 1] = X;
     }
-    float X = 0.f;
-#pragma unroll
-    for (int k = 0; k < 32; ++k) X += h[k];
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const int k0 = 8 * (t >> 2) + (t & 3), k1 = k0 + 4;   // chain pair t: (x[k0], x[k0 + 4])
-      const __bf16 a0 = (__bf16)h[k0], a1 = (__bf16)h[k1];
-      const __bf16 b0 = (__bf16)(h[k0] - (float)a0), b1 = (__bf16)(h[k1] - (float)a1);
-      xl[32 * r + t] = __builtin_bit_cast(uint32_t, bf16x2{a0, a1});
-      xl[32 * r + 16 + t] = __builtin_bit_cast(uint32_t, bf16x2{b0, b1});
-    }
-    sums[r] = X;
   }
 }
 
@@ -461,36 +450,6 @@ __device__ __forceinline__ void moe_chunks(const Q4Chunk<KIND> (&ch)[CPW], int n
         xp.X[m] = sums[2 * r + 1];
       }
       q4_compute<KIND, TB>(ch[j], xp, k, acc);
-    }
-  }
-}
-
-// The same against two-plane records of h (moe_stage_h).
-template <int KIND, int TB, int CPW>
-__device__ __forceinline__ void moe_chunks_h(const Q4Chunk<KIND> (&ch)[CPW], int nc, int c0, int TC,
-                                             const uint32_t* xl, const Q4Consts& k, float (&acc)[4][TB]) {
-  const int R = TB * TC * 8, g = threadIdx.x & 7;
-  const float* sums = reinterpret_cast<const float*>(xl + 32 * R);
-#pragma unroll
-  for (int j = 0; j < CPW; ++j) {
-    if (j < nc) {
-      XRecB<TB, 2> xp;
-#pragma unroll
-      for (int m = 0; m < TB; ++m) {
-        const int r = (m * TC + c0 + j) * 8 + g;
-#pragma unroll
-        for (int pl = 0; pl < 2; ++pl)
-#pragma unroll
-          for (int d = 0; d < 4; ++d) {
-            const u32x4 v = *reinterpret_cast<const u32x4*>(xl + 32 * r + 16 * pl + 4 * d);
-            xp.p[m][pl][4 * d] = v.x;
-            xp.p[m][pl][4 * d + 1] = v.y;
-            xp.p[m][pl][4 * d + 2] = v.z;
-            xp.p[m][pl][4 * d + 3] = v.w;
-          }
-        xp.X[m] = sums[r];
-      }
-      q4_compute_b<KIND, TB, 2>(ch[j], xp, k, acc);
     }
   }
 }
@@ -659,7 +618,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_moe_down_s(MoeArgs a, int ks_r, 
       __syncthreads();
       for (int r0 = 0; r0 < nc; r0 += CPW) {
         if (nc > CPW) moe_load<KIND, CPW>(row, c0 + r0, min(CPW, nc - r0), lane, ch);
-        moe_chunks_h<KIND, TB, CPW>(ch, min(CPW, nc - r0), c0 + r0, TC, xl, kc, acc);
+        moe_chunks<KIND, TB, CPW>(ch, min(CPW, nc - r0), c0 + r0, TC, xl, kc, acc);
       }
       q4_lane_reduce<TB>(acc);
       if ((lane & 7) == 0) {
@@ -793,7 +752,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_moe_down(MoeArgs a, int ks_r, in
     __syncthreads();
     for (int r0 = 0; r0 < nc; r0 += CPW) {
       if (nc > CPW) moe_load<KIND, CPW>(row, c0 + r0, min(CPW, nc - r0), lane, ch);
-      moe_chunks_h<KIND, TB, CPW>(ch, min(CPW, nc - r0), c0 + r0, TC, xl, kc, acc);
+      moe_chunks<KIND, TB, CPW>(ch, min(CPW, nc - r0), c0 + r0, TC, xl, kc, acc);
     }
     q4_lane_reduce<TB>(acc);
     if ((lane & 7) == 0) {

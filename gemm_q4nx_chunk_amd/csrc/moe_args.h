@@ -66,11 +66,10 @@ inline MoeWsLayout moe_ws_layout(int P, int T, int D, int hstride) {
   return l;
 }
 
-// Prepared-record bytes per (token, tile column) in LDS: gate/up take fp16
-// records of bf16 activations (8 groups x 72 B), down takes two-plane bf16
-// records of the fp32 h (8 groups x 132 B).
+// Prepared-record bytes per (token, tile column) in LDS: fp16 records of the
+// bf16 activations (gate/up) or of the fp32 h (down), 8 groups x 72 B.
 constexpr int kMoeRecGateUp = 8 * 72;
-constexpr int kMoeRecDown = 8 * 132;
+constexpr int kMoeRecDown = 8 * 72;
 
 hipError_t launch_moe(int kind, const MoeArgs& a, hipStream_t s);
 

@@ -264,16 +264,16 @@ size_t q4nx_moe_ws(const q4nx_moe_layer* L, int T, int k);
  * device so that each selected expert's weights are read once per call
  * however many tokens chose it (onw technical notes, "computing MoE prompts
  * together": tokens grouped by expert, each expert read once per prompt).
- * The intermediate h stays fp32: the down projection takes each h as the sum
- * of two bf16 values (16 significant bits, relative error at most 2^-17); the
- * weighted sum over slots runs in slot order, then the shared expert, in
- * fp32, with no atomics.
+ * The intermediate h stays fp32; the down projection reads it as fp16 with
+ * a power-of-two scale per 32 values (round to nearest: each h moves by at
+ * most 2^-12 of its size while it lies within 2^29 of the largest of its 32,
+ * so d is within 2^-12 * sum |w h| plus the fp32 sums); the weighted sum over
+ * slots runs in slot order, then the shared expert, in fp32, with no atomics.
  *   X    DEVICE bf16 [T][D]; ids DEVICE int32 [T][k]; p DEVICE fp32 [T][k]
  *   Y    DEVICE fp32 [T][D], fully overwritten
  *   T    1..4096, k 1..16, T*k <= 4096.  A batch's prepared activations are
- *        staged in 64 KB of LDS, so d_model is at most 28928 (T = 1) or 7168
- *        (T > 1), and d_expert, d_shared at most 15872 (T = 1) or 3840
- *        (T > 1), else E_SHAPE
+ *        staged in 64 KB of LDS, so d_model, d_expert and d_shared are at most
+ *        28928 (T = 1) or 7168 (T > 1), else E_SHAPE
  *   dbg  NULL, or stage outputs to fill (any member may be NULL)
  *   ws   DEVICE workspace of at least q4nx_moe_ws(L, T, k) bytes, 256-byte aligned
  * An id outside [0, n_experts) is never dereferenced: its slot contributes 0
