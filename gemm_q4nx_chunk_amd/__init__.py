@@ -74,6 +74,7 @@ _lib.q4nx_gemm_block_ws.restype = ctypes.c_size_t
 _lib.q4nx_gemm_batched.argtypes = [ctypes.POINTER(GemmJob), _I, _P, _I, _P, ctypes.c_size_t, _P]
 _lib.q4nx_gemm_batched_ws.argtypes = [ctypes.POINTER(GemmJob), _I]
 _lib.q4nx_gemm_batched_ws.restype = ctypes.c_size_t
+_lib.q4nx_gemm_exchange_mode.argtypes = [_I]
 _lib.q4nx_moe_ws.argtypes = [ctypes.POINTER(MoeLayer), _I, _I]
 _lib.q4nx_moe_ws.restype = ctypes.c_size_t
 _lib.q4nx_moe_experts.argtypes = [ctypes.POINTER(MoeLayer), _P, _P, _P, _I, _I, _P,
@@ -102,7 +103,7 @@ _lib.q4nx_status_str.restype = ctypes.c_char_p
 _lib.q4nx_last_error.restype = ctypes.c_char_p
 for _f in ("q4nx_weight_check", "q4nx_gemv", "q4nx_gemv_batched", "q4nx_gemm_block", "q4nx_gemm_batched",
            "q4nx_moe_experts", "q4nx_unpack", "q4nx_decode", "q4nx_repack_q4k_to_q41", "q4nx_gguf_to_q41", "q4nx_q8_rows", "q4nx_argmax", "q4nx_moe_router", "q4nx_version", "q4nx_plan_create",
-           "q4nx_plan_run", "q4nx_plan_errors"):
+           "q4nx_plan_run", "q4nx_plan_errors", "q4nx_gemm_exchange_mode"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -236,6 +237,15 @@ def gemm_block(w: Weight, X, Y, M: int, ws=None, stream=None, ws_bytes: int | No
     """
     _check(_lib.q4nx_gemm_block(ctypes.byref(w), _ptr(X), _ptr(Y), M, _ptr(ws),
                                 _nbytes(ws) if ws_bytes is None else ws_bytes, _stream(stream)))
+
+
+def gemm_exchange_mode(mode: int) -> None:
+    """Split-K exchange of every later block GEMM: 0 default, 1 odd groups act
+    displaced (tests), 2 device-coherent exchange (tests)."""
+    _check(_lib.q4nx_gemm_exchange_mode(mode))
+
+
+GEMM_WS_DIAG_OFFSET = 3072   # uint32 in the GEMM workspace: workgroups that found their XCD slot taken
 
 
 def _gemm_jobs(jobs):

@@ -6,6 +6,7 @@
 // (section "Q4NX chunks": the chunk size names the kind, the two Q8 layouts
 // cannot be told apart; section "From a GGUF": a checker refuses an unknown
 // chunk size or a tensor shorter than its layout needs).
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <algorithm>
@@ -241,6 +242,9 @@ int q4nx_gemv_batched(const q4nx_gemv_job* jobs, int n_jobs, int M, void* stream
 
 namespace {
 
+// q4nx_gemm_exchange_mode: 0 default, 1 odd groups act displaced, 2 device-coherent exchange.
+std::atomic<int> g_gemm_exchange_mode{0};
+
 // Checks a block-GEMM launch over weights w[0..n-1] sharing X and fills the
 // kernel arguments (all but the workspace).  Returns a status.
 int gemm_setup(const q4nx_weight* const* w, float* const* Y, int n, const uint16_t* X, int M,
@@ -285,11 +289,16 @@ int gemm_launch(q4nx::GemmArgs& a, int kind, void* ws, size_t ws_bytes, void* st
   if (need && (!ws || ws_bytes < need))
     return fail(Q4NX_E_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", name, ws_bytes, need);
   if (need && !aligned(ws, 256)) return fail(Q4NX_E_ALIGN, "%s: workspace not 256-byte aligned", name);
-  a.cnt = need ? static_cast<uint32_t*>(ws) : nullptr;
-  a.partial = need ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + q4nx::kGemmCntBytes)
-                   : nullptr;
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  a.cnt = need ? reinterpret_cast<uint32_t*>(w) : nullptr;
+  a.claim = need ? reinterpret_cast<uint32_t*>(w + q4nx::kGemmClaimOff) : nullptr;
+  a.rescued = need ? reinterpret_cast<uint32_t*>(w + q4nx::kGemmRescueOff) : nullptr;
+  a.diag = need ? reinterpret_cast<uint32_t*>(w + q4nx::kGemmDiagOff) : nullptr;
+  a.partial = need ? reinterpret_cast<float*>(w + q4nx::kGemmCntBytes) : nullptr;
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  const bool local = a.S > 1 && q4nx::xcd_round_robin(st) == 1;
+  const int mode = g_gemm_exchange_mode.load(std::memory_order_relaxed);
+  a.test_mode = mode == 1 ? 1 : 0;
+  const bool local = a.S > 1 && mode != 2 && q4nx::xcd_round_robin(st) == 1;
   const hipError_t e = q4nx::launch_gemm(kind, a, local, st);
   return hip_status(e, name);
 }
@@ -329,6 +338,12 @@ int q4nx_gemm_batched(const q4nx_gemm_job* jobs, int n_jobs, const uint16_t* X, 
   if (st) return st;
   const int r = gemm_launch(a, kind_of(w[0]), ws, ws_bytes, stream, "gemm_batched");
   return r ? r : ok();
+}
+
+int q4nx_gemm_exchange_mode(int mode) {
+  if (mode < 0 || mode > 2) return fail(Q4NX_E_ARG, "gemm_exchange_mode: %d is not 0, 1 or 2", mode);
+  g_gemm_exchange_mode.store(mode, std::memory_order_relaxed);
+  return ok();
 }
 
 size_t q4nx_gemm_batched_ws(const q4nx_gemm_job* jobs, int n_jobs) {

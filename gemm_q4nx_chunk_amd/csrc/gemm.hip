@@ -32,6 +32,9 @@
 // use the same slots, so the order of k inside a step does not change the sum.
 // With this order a lane's weights are one contiguous 64-byte run of its row's
 // codes, and their scale records one 16-byte load.
+#include <atomic>
+#include <mutex>
+
 #include "gemm_args.h"
 #include "q4nx_dev.h"
 
@@ -132,6 +135,65 @@ __device__ __forceinline__ bf16x8 dequant8(uint32_t w, float s, float z, uint32_
 #ifndef Q4NX_GEMM_WPE_ONE
 #define Q4NX_GEMM_WPE_ONE 4
 #endif
+// XCD-local placement.  Workgroups are dealt to the 8 XCDs round-robin by
+// linear id from a starting XCD that varies between launches (XCD = (id + c)
+// mod 8 for one c per launch), so the 8 workgroups of group r = id / 8 land on
+// 8 different XCDs, and the workgroup on XCD x takes workgroup row
+// nb = 8 (r / S) + x and part r % S: every K part of row nb runs on XCD
+// nb % 8, where its partial tiles and arrival counter meet in one L2.
+//
+// That placement is checked, not assumed: each workgroup claims its XCD's slot
+// of its group with an atomic OR.  If the slot is taken (another workgroup of
+// the group landed on the same XCD, as concurrent dispatches from other
+// streams can cause), it takes the first free slot instead -- 8 workgroups, 8
+// slots: each ends with one -- and is "displaced": its unit's home XCD is not
+// its own.  A displaced workgroup computes its rows over the whole K range and
+// writes Y itself, raises the row's rescue flag and then counts its part in;
+// the home parts of that row see the flag and skip their combine.  The last
+// claimer of a group clears the group's word for the next call.
+struct GemmUnit {
+  int nb, part;
+  bool displaced;
+};
+
+__device__ __forceinline__ GemmUnit gemm_claim(const GemmArgs& a, uint32_t* s_slot) {
+  const int r = blockIdx.x >> 3;
+  const uint32_t xcc = __builtin_amdgcn_s_getreg((3 << 11) | 20) & 7;   // HW_REG_XCC_ID
+  if (threadIdx.x == 0) {
+    const bool force = a.test_mode == 1 && (r & 1);   // tests: odd groups act displaced
+    uint32_t x = xcc, bit = 1u << xcc, old = 0;
+    if (!force) old = __hip_atomic_fetch_or(a.claim + r, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (force || (old & bit)) {
+      if (!force) __hip_atomic_fetch_add(a.diag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t start = force ? xcc + 1 : 0;
+      for (uint32_t i = 0; i < 8; ++i) {
+        x = (start + i) & 7;
+        bit = 1u << x;
+        old = __hip_atomic_fetch_or(a.claim + r, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (!(old & bit)) break;
+      }
+    }
+    if ((old | bit) == 0xFFu) __hip_atomic_store(a.claim + r, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *s_slot = x;
+  }
+  __syncthreads();
+  const uint32_t x = *s_slot;
+  return GemmUnit{8 * (r / a.S) + (int)x, r % a.S, x != xcc};
+}
+
+// A displaced workgroup's row is complete in Y: raise the row's rescue flag,
+// then count the part in (the flag is out before the count moves); the last
+// of the row's parts clears both.
+__device__ __forceinline__ void gemm_rescued_part(const GemmArgs& a, int nb) {
+  __hip_atomic_store(a.rescued + nb, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  wait_stores();
+  const uint32_t old = __hip_atomic_fetch_add(a.cnt + nb, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (old == (uint32_t)a.S - 1) {
+    __hip_atomic_store(a.cnt + nb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(a.rescued + nb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 template <int KIND, bool TWO, int D, bool LOCAL>
 __global__ __launch_bounds__(64 * kGemmWaves)
 __attribute__((amdgpu_waves_per_eu(TWO ? Q4NX_GEMM_WPE_TWO : Q4NX_GEMM_WPE_ONE, TWO ? Q4NX_GEMM_WPE_TWO : Q4NX_GEMM_WPE_ONE)))
@@ -141,23 +203,18 @@ void k_gemm_q4(GemmArgs a) {
   constexpr int XR = TWO ? 64 : 32;          // token rows staged in LDS
   constexpr int G = TWO ? 8 : 4;             // f32x4 groups of the accumulators
   __shared__ __attribute__((aligned(16))) uint16_t xs[2][XR * kXs];
-  __shared__ uint32_t s_old;
+  __shared__ uint32_t s_old, s_flag;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave: row data in SGPRs
   const int h = lane >> 5, n = lane & 31;
-  // LOCAL: workgroups are dealt to the 8 XCDs round-robin by linear id,
-  // starting at an XCD that varies between launches (XCD = (id + c) mod 8 for
-  // one c per launch; the host checks the pattern once per device).  So the 8
-  // workgroups of each group r = id / 8 sit on 8 different XCDs, and a
-  // workgroup that takes row nb = 8 (r / S) + (its XCD) and part r % S puts
-  // every K part of row nb on one XCD: their partial tiles and arrival counter
-  // only ever meet in that XCD's L2.
+  // LOCAL: all K parts of a row on one XCD, claimed as gemm_claim describes.
   int nb, part;
+  bool displaced = false;
   if constexpr (LOCAL) {
-    const int r = blockIdx.x >> 3;
-    const int xcc = (int)(__builtin_amdgcn_s_getreg((3 << 11) | 20) & 7);   // HW_REG_XCC_ID
-    nb = 8 * (r / a.S) + xcc;
-    part = r % a.S;
+    const GemmUnit u = gemm_claim(a, &s_old);
+    nb = u.nb;
+    part = u.part;
+    displaced = u.displaced;
     if (nb >= a.NB) return;
   } else {
     nb = blockIdx.x;
@@ -171,7 +228,8 @@ void k_gemm_q4(GemmArgs a) {
   const bool active = tr_raw < job.TR;
   const int tr = active ? tr_raw : job.TR - 1;
   const int K = a.TC * 256, N = job.TR * 32, M = a.M;
-  const int tc0 = part * a.TC / a.S, tc1 = (part + 1) * a.TC / a.S;
+  // a displaced workgroup takes its rows' whole K range
+  const int tc0 = displaced ? 0 : part * a.TC / a.S, tc1 = displaced ? a.TC : (part + 1) * a.TC / a.S;
   const __amdgpu_buffer_rsrc_t wrs =
       make_rsrc(job.w + ((size_t)tr * a.TC + tc0) * CB, (uint32_t)((tc1 - tc0) * CB));
 
@@ -275,15 +333,21 @@ void k_gemm_q4(GemmArgs a) {
   for (int g = 0; g < G; ++g)
 #pragma unroll
     for (int i = 0; i < 4; ++i) mine[g][i] = g < 4 ? acc0[4 * g + i] : acc1[4 * (g - 4) + i];
-  if (a.S == 1) {
+  if (a.S == 1 || displaced) {
     if (active) store_y(mine);
+    if (displaced) {
+      wait_stores();
+      __syncthreads();
+      if (tid == 0) gemm_rescued_part(a, nb);
+    }
     return;
   }
 
   // Split K: each part stores its accumulators in register order (16 B per
-  // lane and group, device-coherent), and the last part of the block to
-  // arrive adds all parts, its own read back too, in part order.  Loads past
-  // the last part fall outside the buffer resource and read zero.
+  // lane and group), and the last part of the block to arrive adds all parts,
+  // its own read back too, in part order (unless a displaced workgroup has
+  // already written the row whole).  Loads past the last part fall outside the
+  // buffer resource and read zero.
   constexpr size_t kPartBytes = (size_t)kGemmWaves * 8 * 64 * 16;
   const uint32_t part_bytes = (uint32_t)(kPartBytes * a.S);
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.partial + (size_t)nb * a.S * (kPartBytes / 4), part_bytes);
@@ -299,11 +363,18 @@ void k_gemm_q4(GemmArgs a) {
   wait_stores();
   __syncthreads();
   if (tid == 0) {
-    if constexpr (LOCAL) s_old = __hip_atomic_fetch_add(a.cnt + nb, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    else s_old = __hip_atomic_fetch_add(a.cnt + nb, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_old = __hip_atomic_fetch_add(a.cnt + nb, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_flag = 0;
+    if (s_old == (uint32_t)a.S - 1) {
+      s_flag = __hip_atomic_load(a.rescued + nb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (s_flag) {   // the row is already whole in Y: clear for the next call
+        __hip_atomic_store(a.cnt + nb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(a.rescued + nb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
   }
   __syncthreads();
-  if (s_old != (uint32_t)a.S - 1) return;
+  if (s_old != (uint32_t)a.S - 1 || s_flag) return;
 
   constexpr int PB = 16 / G;                 // parts loaded per round trip (64 registers)
   f32x4 sum[G];
@@ -324,10 +395,7 @@ void k_gemm_q4(GemmArgs a) {
         for (int g = 0; g < G; ++g) sum[g] += in[j][g];
   }
   if (active) store_y(sum);
-  if (tid == 0) {
-    if constexpr (LOCAL) __hip_atomic_store(a.cnt + nb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    else __hip_atomic_store(a.cnt + nb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  if (tid == 0) __hip_atomic_store(a.cnt + nb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // The M > 32 variant: 8 waves = 4 tile rows x 2 halves of the workgroup's K
@@ -349,17 +417,18 @@ void k_gemm_q4h(GemmArgs a) {
   constexpr int XR = 64, G = 8, R = kGemmRowsHalves;
   constexpr int NH = 64 * kGemmWaves / 2;    // threads of one half
   __shared__ __attribute__((aligned(16))) uint16_t xs[2][2][XR * kXs];   // [buffer][half]
-  __shared__ uint32_t s_old;
+  __shared__ uint32_t s_old, s_flag;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave: row data in SGPRs
   const int rho = wave & (R - 1), pi = wave / R;
   const int h = lane >> 5, n = lane & 31;
   int nb, part;   // workgroup row and K part, laid out as in k_gemm_q4
+  bool displaced = false;
   if constexpr (LOCAL) {
-    const int r = blockIdx.x >> 3;
-    const int xcc = (int)(__builtin_amdgcn_s_getreg((3 << 11) | 20) & 7);   // HW_REG_XCC_ID
-    nb = 8 * (r / a.S) + xcc;
-    part = r % a.S;
+    const GemmUnit u = gemm_claim(a, &s_old);
+    nb = u.nb;
+    part = u.part;
+    displaced = u.displaced;
     if (nb >= a.NB) return;
   } else {
     nb = blockIdx.x;
@@ -373,8 +442,9 @@ void k_gemm_q4h(GemmArgs a) {
   const bool active = tr_raw < job.TR;
   const int tr = active ? tr_raw : job.TR - 1;
   const int K = a.TC * 256, N = job.TR * 32, M = a.M;
-  // the workgroup's K part [tc0, tc1), cut into halves [tc0, mid) and [mid, tc1)
-  const int tc0 = part * a.TC / a.S, tc1 = (part + 1) * a.TC / a.S;
+  // the workgroup's K part [tc0, tc1) (all of K when displaced), cut into
+  // halves [tc0, mid) and [mid, tc1)
+  const int tc0 = displaced ? 0 : part * a.TC / a.S, tc1 = displaced ? a.TC : (part + 1) * a.TC / a.S;
   const int mid = tc0 + (tc1 - tc0 + 1) / 2;
   const int nsteps = mid - tc0;                          // steps of the first (longer) half
   const int hc0 = pi ? mid : tc0, hc1 = pi ? tc1 : mid;  // this wave's half
@@ -490,8 +560,13 @@ void k_gemm_q4h(GemmArgs a) {
         if (m < M) yc[(size_t)m * N] = r[g][i];
       }
   };
-  if (a.S == 1) {
+  if (a.S == 1 || displaced) {
     if (pi == 0 && active) store_y(mine);
+    if (displaced) {
+      wait_stores();
+      __syncthreads();
+      if (tid == 0) gemm_rescued_part(a, nb);
+    }
     return;
   }
 
@@ -512,11 +587,18 @@ void k_gemm_q4h(GemmArgs a) {
   wait_stores();
   __syncthreads();
   if (tid == 0) {
-    if constexpr (LOCAL) s_old = __hip_atomic_fetch_add(a.cnt + nb, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    else s_old = __hip_atomic_fetch_add(a.cnt + nb, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_old = __hip_atomic_fetch_add(a.cnt + nb, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_flag = 0;
+    if (s_old == (uint32_t)a.S - 1) {
+      s_flag = __hip_atomic_load(a.rescued + nb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (s_flag) {   // the row is already whole in Y: clear for the next call
+        __hip_atomic_store(a.cnt + nb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(a.rescued + nb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
   }
   __syncthreads();
-  if (s_old != (uint32_t)a.S - 1 || pi == 1) return;
+  if (s_old != (uint32_t)a.S - 1 || s_flag || pi == 1) return;
 
   constexpr int PB = 2;                      // parts loaded per round trip (64 registers)
   f32x4 sum[G];
@@ -537,10 +619,7 @@ void k_gemm_q4h(GemmArgs a) {
         for (int g = 0; g < G; ++g) sum[g] += in[jj][g];
   }
   if (active) store_y(sum);
-  if (tid == 0) {
-    if constexpr (LOCAL) __hip_atomic_store(a.cnt + nb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    else __hip_atomic_store(a.cnt + nb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  if (tid == 0) __hip_atomic_store(a.cnt + nb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int KIND, bool TWO>
@@ -575,28 +654,39 @@ __global__ void k_xcc_probe() {
   if (threadIdx.x == 0) g_xcc_probe[blockIdx.x] = __builtin_amdgcn_s_getreg((3 << 11) | 20) & 15;
 }
 
-// 1 when a 64-workgroup launch lands as XCD = (id + c) mod 8 for one c.
-int xcd_round_robin(hipStream_t s) {
-  static int cached[64];
-  static bool init = false;
-  if (!init) {
-    for (int& c : cached) c = -1;
-    init = true;
+// 1 when a 64-workgroup launch lands as XCD = (id + c) mod 8 for one c.  The
+// probe runs once per device, on a non-blocking stream of the library's own,
+// and its copy back is asynchronous on that stream: the caller's stream is
+// never waited on.  While the caller's stream is being captured into a graph
+// nothing is launched (the answer is 0 until the probe has run).
+static std::once_flag g_probe_once[64];
+static std::atomic<int> g_probe_result[64];
+
+static int run_xcc_probe() {
+  hipStream_t ps = nullptr;
+  if (hipStreamCreateWithFlags(&ps, hipStreamNonBlocking) != hipSuccess) return 0;
+  uint32_t* dev_ids = nullptr;
+  int ok = 0;
+  uint32_t ids[kProbeWgs];
+  hipLaunchKernelGGL(k_xcc_probe, dim3(kProbeWgs), dim3(64), 0, ps);
+  if (hipGetLastError() == hipSuccess && hipGetSymbolAddress((void**)&dev_ids, HIP_SYMBOL(g_xcc_probe)) == hipSuccess &&
+      hipMemcpyAsync(ids, dev_ids, sizeof ids, hipMemcpyDeviceToHost, ps) == hipSuccess &&
+      hipStreamSynchronize(ps) == hipSuccess) {
+    ok = ids[0] < 8;
+    for (int i = 0; i < kProbeWgs; ++i) ok &= ids[i] == (ids[0] + (uint32_t)i) % 8;
   }
+  (void)hipStreamDestroy(ps);
+  return ok;
+}
+
+int xcd_round_robin(hipStream_t caller) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cached[dev] >= 0) return cached[dev];
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-  if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return 0;
-  hipLaunchKernelGGL(k_xcc_probe, dim3(kProbeWgs), dim3(64), 0, s);
-  uint32_t ids[kProbeWgs];
-  if (hipGetLastError() != hipSuccess || hipStreamSynchronize(s) != hipSuccess ||
-      hipMemcpyFromSymbol(ids, HIP_SYMBOL(g_xcc_probe), sizeof ids, 0, hipMemcpyDeviceToHost) != hipSuccess)
-    return 0;
-  int ok = ids[0] < 8;
-  for (int i = 0; i < kProbeWgs; ++i) ok &= ids[i] == (ids[0] + (uint32_t)i) % 8;
-  cached[dev] = ok;
-  return ok;
+  if (hipStreamIsCapturing(caller, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone)
+    return g_probe_result[dev].load() == 1 ? 1 : 0;
+  std::call_once(g_probe_once[dev], [dev] { g_probe_result[dev].store(run_xcc_probe() ? 1 : 2); });
+  return g_probe_result[dev].load() == 1 ? 1 : 0;
 }
 
 }  // namespace q4nx

@@ -23,7 +23,11 @@ struct GemmArgs {
   const uint16_t* X;
   float* partial;   // [NB][S][8 waves][8 groups][64 lanes][4] fp32 when S > 1
   uint32_t* cnt;    // [NB] parts arrived (of kGemmCntWords); zero between calls
+  uint32_t* claim;  // [groups] XCD slots taken in each group of 8 workgroups; zero between calls
+  uint32_t* rescued;   // [NB] 1 when a row was computed whole by a displaced workgroup; zero between calls
+  uint32_t* diag;   // [0]: workgroups that found their XCD slot taken (never reset by the kernels)
   int32_t TC, M, S, NB;
+  int32_t test_mode;   // 0; 1: every odd group's workgroups act as displaced (tests of that path)
 };
 
 // Tile rows per workgroup of the block GEMM: 8 for M <= 32 (a wave per row),
@@ -55,12 +59,18 @@ inline int gemm_parts(int nb, int TC) {
   return S;
 }
 
-// Workspace: kGemmCntWords arrival counters (K is split only when nb * 2 <=
-// the workgroup target, so nb stays below it), padded to 256 bytes, then the
-// partial tiles.  The counter region has the same size for every call, so one
-// zeroed buffer of the largest size any call needs serves calls of any shape.
+// Workspace: a 4 KB header -- kGemmCntWords arrival counters (K is split only
+// when nb * 2 <= the workgroup target, so nb stays below it), as many XCD
+// claim words (one per group of 8 workgroups: ceil(NB / 8) * S <= 256 groups,
+// since NB * S <= 256), as many rescue flags, then diagnostic words -- and
+// then the partial tiles.  The header has the same size for every call, so one zeroed buffer of
+// the largest size any call needs serves calls of any shape.
 constexpr int kGemmCntWords = Q4NX_GEMM_WG_TARGET;
-constexpr size_t kGemmCntBytes = ((size_t)kGemmCntWords * 4 + 255) & ~(size_t)255;
+constexpr size_t kGemmClaimOff = (size_t)kGemmCntWords * 4;
+constexpr size_t kGemmRescueOff = kGemmClaimOff + (size_t)kGemmCntWords * 4;
+constexpr size_t kGemmDiagOff = kGemmRescueOff + (size_t)kGemmCntWords * 4;
+constexpr size_t kGemmCntBytes = 4096;
+static_assert(kGemmDiagOff + 256 <= kGemmCntBytes, "GEMM workspace header");
 inline size_t gemm_ws_bytes(int nb, int TC, int M) {
   const int S = gemm_parts(nb, TC);
   if (S == 1) return 0;
@@ -81,8 +91,10 @@ inline size_t gemm_ws_bytes_any_m(const int* TR, int n, int TC) {
 // local: lay the K parts of each workgroup row on one XCD (see gemm.hip).
 hipError_t launch_gemm(int kind, const GemmArgs& a, bool local, hipStream_t s);
 // 1 when this device deals a launch's workgroups to its 8 XCDs round-robin by
-// linear id, from a starting XCD that may vary per launch (checked once per
-// device with a 64-workgroup probe, outside graph capture).
-int xcd_round_robin(hipStream_t s);
+// linear id, from a starting XCD that may vary per launch.  Checked once per
+// device with a 64-workgroup probe on a stream of the library's own, never on
+// the caller's stream and never while the caller's stream is being captured
+// (0 until the probe has run).
+int xcd_round_robin(hipStream_t caller);
 
 }  // namespace q4nx

@@ -187,10 +187,16 @@ void q4nx_plan_destroy(q4nx_plan plan);
  *   ws DEVICE workspace of q4nx_gemm_block_ws(w) bytes, 256-byte aligned (may
  *      be NULL when that size is 0).  It must hold zeros before its first use;
  *      every call leaves it ready for the next one.  Its layout does not
- *      depend on the call (256 counter words, then the partial tiles), so one
- *      buffer of the largest size any call needs serves calls of any shape,
- *      one call at a time.  (K is split over several workgroups when the tile rows
- *      alone would leave CUs idle; the workspace holds their partial tiles.)
+ *      depend on the call (a 4 KB header of counters, claim words and flags,
+ *      then the partial tiles), so one buffer of the largest size any call
+ *      needs serves calls of any shape, one call at a time.  (K is split over
+ *      several workgroups when the tile rows alone would leave CUs idle; the
+ *      workspace holds their partial tiles.  The parts of a row are placed on
+ *      one XCD so they meet in its L2; a workgroup that lands elsewhere, as
+ *      concurrent work on other streams can cause, detects it and computes its
+ *      rows whole, so the result is the same wherever workgroups land.  The
+ *      uint32 at byte 3072 of the workspace counts such workgroups; the
+ *      library never resets it.)
  * The bf16 rounding of each weight moves it by at most 2^-8 of its size; with
  * random signs the error of a sum over K stays well inside 2e-3 * sum |w x|.
  */
@@ -198,6 +204,18 @@ int q4nx_gemm_block(const q4nx_weight* w, const uint16_t* X, float* Y, int M, vo
                     size_t ws_bytes, void* stream);
 /* Workspace bytes q4nx_gemm_block needs for this weight (0 = none). */
 size_t q4nx_gemm_block_ws(const q4nx_weight* w);
+
+/*
+ * Test and tuning switch of the block GEMM's split-K exchange, for every later
+ * call in the process: 0 (default) puts the K parts of a row on one XCD when a
+ * one-time probe of the device shows workgroups dealt to XCDs round-robin;
+ * 1 does the same but makes the workgroups of every odd group act displaced
+ * (the path a workgroup takes when another of its group landed on its XCD);
+ * 2 always uses the device-coherent exchange (partials through device-scope
+ * stores and loads).  The results are the same in every mode.  Returns
+ * Q4NX_OK or E_ARG.
+ */
+int q4nx_gemm_exchange_mode(int mode);
 
 /*
  * The block GEMM of several weights that read the same X (the q, k and v
