@@ -622,7 +622,8 @@ def kinds_leg(steps, warmup, graph):
 
 def greedy_leg(steps, warmup, graph):
     """The Q8 tied 151936 x 2560 head in both code layouts: embedding row gather
-    for 1 and 64 tokens, and greedy decode's lm_head GEMV + argmax (M = 1)."""
+    for 1 and 64 tokens, greedy decode's lm_head GEMV + argmax (M = 1) as two
+    launches, and the same head as one launch with its top-k pick (k = 1, 10)."""
     name, N, K = synth.QWEN3_4B_LM_HEAD
     chA = synth.TensorSpec(name, "q8", N, K, ("mixed_decode", 10_000, name), q8_layout="A").generate()
     reps = 50
@@ -657,10 +658,26 @@ def greedy_leg(steps, warmup, graph):
         def argmax_one_wg():
             for _ in range(reps):
                 q.argmax(y, N, 1, idx)
+        # the same head in one launch: GEMV with its top-k pick, no logits written
+        tk = {}
+        for k in (1, 10):
+            tids = torch.empty((1, k), dtype=torch.int32, device=DEV)
+            tws = torch.zeros(q.gemv_topk_ws(w, 1, k), dtype=torch.uint8, device=DEV)
+
+            def fused(tids=tids, tws=tws, k=k):
+                q.gemv_topk(w, x, 1, k, tids, tws)
+            msk, _ = time_calls(fused, steps, warmup, graph)
+            tk[f"k{k}_us"] = msk * 1e3
+            tk[f"k{k}_GB_s"] = d.numel() / (msk * 1e-3) / 1e9
+
+        def gemv_only():
+            q.gemv(w, x, y, 1)
         ms, _ = time_calls(head, steps, warmup, graph)
+        msg, _ = time_calls(gemv_only, steps, warmup, graph)
         msa, _ = time_calls(argmax_split, steps, warmup, graph)
         ms1, _ = time_calls(argmax_one_wg, steps, warmup, graph)
         r.update({"head_gemv_argmax_us": ms * 1e3, "head_GB_s": d.numel() / (ms * 1e-3) / 1e9,
+                  "gemv_alone_us": msg * 1e3, "head_one_launch_topk": tk,
                   "argmax_us": msa * 1e3 / reps, "argmax_one_workgroup_us": ms1 * 1e3 / reps})
         res[f"layout_{lay}"] = r
         del d

@@ -75,6 +75,9 @@ _lib.q4nx_gemm_batched.argtypes = [ctypes.POINTER(GemmJob), _I, _P, _I, _P, ctyp
 _lib.q4nx_gemm_batched_ws.argtypes = [ctypes.POINTER(GemmJob), _I]
 _lib.q4nx_gemm_batched_ws.restype = ctypes.c_size_t
 _lib.q4nx_gemm_exchange_mode.argtypes = [_I]
+_lib.q4nx_gemv_topk_ws.argtypes = [ctypes.POINTER(Weight), _I, _I]
+_lib.q4nx_gemv_topk_ws.restype = ctypes.c_size_t
+_lib.q4nx_gemv_topk.argtypes = [ctypes.POINTER(Weight), _P, _I, _I, _P, _P, _P, _P, ctypes.c_size_t, _P]
 _lib.q4nx_moe_ws.argtypes = [ctypes.POINTER(MoeLayer), _I, _I]
 _lib.q4nx_moe_ws.restype = ctypes.c_size_t
 _lib.q4nx_moe_experts.argtypes = [ctypes.POINTER(MoeLayer), _P, _P, _P, _I, _I, _P,
@@ -103,7 +106,7 @@ _lib.q4nx_status_str.restype = ctypes.c_char_p
 _lib.q4nx_last_error.restype = ctypes.c_char_p
 for _f in ("q4nx_weight_check", "q4nx_gemv", "q4nx_gemv_batched", "q4nx_gemm_block", "q4nx_gemm_batched",
            "q4nx_moe_experts", "q4nx_unpack", "q4nx_decode", "q4nx_repack_q4k_to_q41", "q4nx_gguf_to_q41", "q4nx_q8_rows", "q4nx_argmax", "q4nx_moe_router", "q4nx_version", "q4nx_plan_create",
-           "q4nx_plan_run", "q4nx_plan_errors", "q4nx_gemm_exchange_mode"):
+           "q4nx_plan_run", "q4nx_plan_errors", "q4nx_gemm_exchange_mode", "q4nx_gemv_topk"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -237,6 +240,19 @@ def gemm_block(w: Weight, X, Y, M: int, ws=None, stream=None, ws_bytes: int | No
     """
     _check(_lib.q4nx_gemm_block(ctypes.byref(w), _ptr(X), _ptr(Y), M, _ptr(ws),
                                 _nbytes(ws) if ws_bytes is None else ws_bytes, _stream(stream)))
+
+
+def gemv_topk_ws(w: Weight, M: int, k: int) -> int:
+    """Workspace bytes of gemv_topk (0 = the shape does not fit it)."""
+    return int(_lib.q4nx_gemv_topk_ws(ctypes.byref(w), M, k))
+
+
+def gemv_topk(w: Weight, x, M: int, k: int, ids, ws, y=None, vals=None, stream=None,
+              ws_bytes: int | None = None) -> None:
+    """ids[M, k] (int32, best first) and optionally vals[M, k] and the logits y[M, rows]
+    of y = x @ W^T, in one launch.  ws: zero-initialised, gemv_topk_ws(w, M, k) bytes."""
+    _check(_lib.q4nx_gemv_topk(ctypes.byref(w), _ptr(x), M, k, _ptr(y), _ptr(ids), _ptr(vals),
+                               _ptr(ws), _nbytes(ws) if ws_bytes is None else ws_bytes, _stream(stream)))
 
 
 def gemm_exchange_mode(mode: int) -> None:

@@ -19,6 +19,7 @@
 #include "moe_args.h"
 #include "plan_args.h"
 #include "q4nx_dev.h"
+#include "topk.h"
 
 static_assert(Q4NX_GEMM_BATCH_MAX_JOBS == q4nx::kGemmMaxJobs, "GEMM job table size");
 
@@ -165,6 +166,44 @@ int run_batch(int kind, const q4nx_gemv_job* const* jobs, int n, int M, hipStrea
   return Q4NX_OK;
 }
 
+// Launch shape of the top-k GEMV (one job, 4-wave workgroups, the rules of
+// run_batch otherwise).  Returns false when the shape does not fit it.
+struct TopkShape {
+  q4nx::GemvBatch b;
+  int n_wg, xl;
+  size_t ws_bytes;
+};
+
+constexpr size_t kTopkCntBytes = 256;   // n_grp + 1 <= 65 counters
+
+bool topk_shape(const q4nx_weight* w, int M, int k, TopkShape& t) {
+  const int kind = kind_of(w);
+  const int TR = w->rows / 32, TC = w->cols / 256;
+  t.xl = q4nx::gemv_xl_bytes(kind, M, 4, TC);
+  if (t.xl <= 0) return false;
+  const bool q4 = kind == q4nx::KIND_Q4_1 || kind == q4nx::KIND_Q4_K;
+  const int parts = !q4 ? 1 : TR <= Q4NX_ROWSPLIT4_TR ? 4 : TR <= Q4NX_ROWSPLIT_TR ? 2 : 1;
+  memset(&t.b, 0, sizeof t.b);
+  t.b.sl = 4 / parts;
+  q4nx::GemvJob& g = t.b.job[0];
+  g.w = static_cast<const uint8_t*>(w->chunks);
+  g.TR = TR;
+  g.TC = TC;
+  g.ldx = w->cols;
+  g.ldy = w->rows;
+  g.ks = pick_ks(4, TR, TC);
+  g.wg_begin = 0;
+  t.b.n_jobs = 1;
+  const int rpw = 4 / g.ks;
+  t.n_wg = (TR * parts + rpw - 1) / rpw;
+  if (t.n_wg > q4nx::kTopkMaxWg) return false;
+  t.b.tk.k = k;
+  t.b.tk.n_wg = t.n_wg;
+  t.b.tk.n_grp = (t.n_wg + q4nx::kTopkGroup - 1) / q4nx::kTopkGroup;
+  t.ws_bytes = kTopkCntBytes + (size_t)(t.n_wg + t.b.tk.n_grp) * M * k * 8;
+  return true;
+}
+
 int check_gemv_io(const q4nx_weight* w, const void* x, const float* y, int M, const char* name) {
   int st = check_weight(w, name);
   if (st) return st;
@@ -236,6 +275,43 @@ int q4nx_gemv_batched(const q4nx_gemv_job* jobs, int n_jobs, int M, void* stream
     if (r) return r;
   }
   return ok();
+}
+
+size_t q4nx_gemv_topk_ws(const q4nx_weight* w, int M, int k) {
+  TopkShape t;
+  if (check_weight(w, "gemv_topk_ws") || M < 1 || M > 4 || k < 1 || k > q4nx::kTopkMax ||
+      !topk_shape(w, M, k, t))
+    return 0;
+  return t.ws_bytes;
+}
+
+int q4nx_gemv_topk(const q4nx_weight* w, const uint16_t* x, int M, int k, float* y, int32_t* ids,
+                   float* vals, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_weight(w, "gemv_topk");
+  if (st) return st;
+  if (!x || !ids) return fail(Q4NX_E_ARG, "gemv_topk: null x or ids");
+  if (M < 1 || M > 4) return fail(Q4NX_E_ARG, "gemv_topk: M = %d outside 1..4", M);
+  if (k < 1 || k > q4nx::kTopkMax || k > w->rows)
+    return fail(Q4NX_E_ARG, "gemv_topk: k = %d outside 1..min(%d, rows)", k, q4nx::kTopkMax);
+  if (!aligned(x, 16)) return fail(Q4NX_E_ALIGN, "gemv_topk: x not 16-byte aligned");
+  if ((y && !aligned(y, 4)) || !aligned(ids, 4) || (vals && !aligned(vals, 4)))
+    return fail(Q4NX_E_ALIGN, "gemv_topk: y, ids and vals must be 4-byte aligned");
+  TopkShape t;
+  if (!topk_shape(w, M, k, t))
+    return fail(Q4NX_E_SHAPE, "gemv_topk: %d x %d at M = %d does not fit the prepared-activation GEMV "
+                "with at most %d workgroups", w->rows, w->cols, M, q4nx::kTopkMaxWg);
+  if (!ws || ws_bytes < t.ws_bytes)
+    return fail(Q4NX_E_WORKSPACE, "gemv_topk: workspace of %zu bytes, %zu needed", ws_bytes, t.ws_bytes);
+  if (!aligned(ws, 256)) return fail(Q4NX_E_ALIGN, "gemv_topk: workspace not 256-byte aligned");
+  uint8_t* wsb = static_cast<uint8_t*>(ws);
+  t.b.job[0].x = x;
+  t.b.job[0].y = y;
+  t.b.tk.cnt = reinterpret_cast<uint32_t*>(wsb);
+  t.b.tk.cand = reinterpret_cast<uint64_t*>(wsb + kTopkCntBytes);
+  t.b.tk.ids = ids;
+  t.b.tk.vals = vals;
+  const hipError_t e = q4nx::launch_gemv_topk(kind_of(w), M, t.b, t.n_wg, t.xl, static_cast<hipStream_t>(stream));
+  return hip_status(e, "gemv_topk launch");
 }
 
 }  // extern "C"

@@ -15,6 +15,7 @@
 // chunks, and their partial row sums meet in LDS, where one pass adds them in
 // wave order.  No atomics: the result bits do not depend on timing.
 #include "gemv_core.h"
+#include "topk.h"
 
 namespace q4nx {
 
@@ -84,7 +85,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_q4(const GemvBatch b) {
 // launch of few tile rows spreads over more compute units with no partial
 // sums to combine.  (One CU draws only a few tens of GB/s from HBM, so a 2560-row
 // projection, 80 tile rows, otherwise streams from 80 CUs.)
-template <int KIND, int M, int WAVES, int D, int SL = 4>
+template <int KIND, int M, int WAVES, int D, int SL = 4, bool TOPK = false>
 __global__ __launch_bounds__(64 * WAVES) void k_gemv_q4x(const GemvBatch b) {
   constexpr int NT = 64 * WAVES;
   constexpr int XRP = 2;
@@ -196,6 +197,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_q4x(const GemvBatch b) {
       for (int m = 0; m < M; ++m) red[wave][8 * i + (lane >> 3)][m] = acc[i][m];
   }
   __syncthreads();
+  __shared__ float tv[TOPK ? M : 1][TOPK ? kTopkRows : 1];
   for (int idx = tid; idx < rpw * UR * M; idx += NT) {
     const int s = idx / (UR * M), rem = idx - s * UR * M;
     const int r = rem / M, m = rem - r * M;
@@ -203,8 +205,19 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_q4x(const GemvBatch b) {
     if (t < NU) {
       float v = 0.f;
       for (int p = 0; p < ks; ++p) v += red[s * ks + p][r][m];
-      __builtin_nontemporal_store(v, &J.y[(size_t)m * J.ldy + UR * t + r]);   // written once
+      if constexpr (TOPK) {
+        tv[m][s * UR + r] = v;
+        if (J.y) J.y[(size_t)m * J.ldy + UR * t + r] = v;
+      } else {
+        __builtin_nontemporal_store(v, &J.y[(size_t)m * J.ldy + UR * t + r]);   // written once
+      }
     }
+  }
+  if constexpr (TOPK) {
+    __shared__ uint32_t s_flag;
+    __syncthreads();
+    const int nr = (NU - u0 < rpw ? NU - u0 : rpw) * UR;
+    topk_epilogue<M, WAVES>(b.tk, tv, nr, (uint32_t)(UR * u0), &s_flag);
   }
 }
 
@@ -305,7 +318,7 @@ __device__ __forceinline__ void q8x_compute(const u32x4 (&pc)[8], const uint32_t
   }
 }
 
-template <int KIND, int M, int WAVES, int D>
+template <int KIND, int M, int WAVES, int D, bool TOPK = false>
 __global__ __launch_bounds__(64 * WAVES) void k_gemv_q8x(const GemvBatch b) {
   using Map = Q8Lines<KIND>;
   constexpr int NG = Map::kGroups, HB = Map::kHalfBit;
@@ -427,6 +440,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_q8x(const GemvBatch b) {
       for (int m = 0; m < M; ++m) red[wave][16 * h + r][m] = acc[r][m];
   }
   __syncthreads();
+  __shared__ float tv[TOPK ? M : 1][TOPK ? kTopkRows : 1];
   for (int idx = tid; idx < rpw * 32 * M; idx += NT) {
     const int s = idx / (32 * M), rem = idx - s * 32 * M;
     const int r = rem / M, m = rem - r * M;
@@ -434,8 +448,19 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_q8x(const GemvBatch b) {
     if (t < J.TR) {
       float v = 0.f;
       for (int p = 0; p < ks; ++p) v += red[s * ks + p][r][m];
-      __builtin_nontemporal_store(v, &J.y[(size_t)m * J.ldy + 32 * t + r]);   // written once
+      if constexpr (TOPK) {
+        tv[m][s * 32 + r] = v;
+        if (J.y) J.y[(size_t)m * J.ldy + 32 * t + r] = v;
+      } else {
+        __builtin_nontemporal_store(v, &J.y[(size_t)m * J.ldy + 32 * t + r]);   // written once
+      }
     }
+  }
+  if constexpr (TOPK) {
+    __shared__ uint32_t s_flag;
+    __syncthreads();
+    const int nr = (J.TR - tr0 < rpw ? J.TR - tr0 : rpw) * 32;
+    topk_epilogue<M, WAVES>(b.tk, tv, nr, (uint32_t)(32 * tr0), &s_flag);
   }
 }
 
@@ -502,6 +527,42 @@ static void launch_xl(F* kern, int n_wg, int threads, int xl_bytes, hipStream_t 
   if (xl_bytes > 65536)
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, xl_bytes);
   hipLaunchKernelGGL(kern, dim3(n_wg), dim3(threads), xl_bytes, s, b);
+}
+
+// The top-k GEMV: 4-wave workgroups, prepared activations, M <= 4.
+template <int KIND, int M>
+static hipError_t launch_topk(const GemvBatch& b, int n_wg, int xl_bytes, hipStream_t s) {
+  constexpr int D = GemvXDepth<M, 4>::value;
+  if constexpr (KIND == KIND_Q4_1 || KIND == KIND_Q4_K) {
+    if (b.sl == 2) launch_xl(k_gemv_q4x<KIND, M, 4, D, 2, true>, n_wg, 256, xl_bytes, s, b);
+    else if (b.sl == 1) launch_xl(k_gemv_q4x<KIND, M, 4, D, 1, true>, n_wg, 256, xl_bytes, s, b);
+    else launch_xl(k_gemv_q4x<KIND, M, 4, D, 4, true>, n_wg, 256, xl_bytes, s, b);
+  } else {
+    hipLaunchKernelGGL((k_gemv_q8x<KIND, M, 4, M == 1 ? 2 : 1, true>), dim3(n_wg), dim3(256), xl_bytes, s, b);
+  }
+  return hipGetLastError();
+}
+
+template <int KIND>
+static hipError_t launch_topk_m(int M, const GemvBatch& b, int n_wg, int xl, hipStream_t s) {
+  switch (M) {
+    case 1: return launch_topk<KIND, 1>(b, n_wg, xl, s);
+    case 2: return launch_topk<KIND, 2>(b, n_wg, xl, s);
+    case 3: return launch_topk<KIND, 3>(b, n_wg, xl, s);
+    case 4: return launch_topk<KIND, 4>(b, n_wg, xl, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemv_topk(int kind, int M, const GemvBatch& b, int n_wg, int xl_bytes, hipStream_t s) {
+  if (xl_bytes <= 0) return hipErrorInvalidValue;
+  switch (kind) {
+    case KIND_Q4_1: return launch_topk_m<KIND_Q4_1>(M, b, n_wg, xl_bytes, s);
+    case KIND_Q4_K: return launch_topk_m<KIND_Q4_K>(M, b, n_wg, xl_bytes, s);
+    case KIND_Q8_A: return launch_topk_m<KIND_Q8_A>(M, b, n_wg, xl_bytes, s);
+    case KIND_Q8_B: return launch_topk_m<KIND_Q8_B>(M, b, n_wg, xl_bytes, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 template <int KIND, int M, int WAVES>

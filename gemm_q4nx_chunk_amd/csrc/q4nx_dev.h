@@ -47,6 +47,16 @@ struct GemvJob {
 
 constexpr int kMaxBatch = 64;
 
+// Top-k of the outputs in the same launch (topk.h); k = 0 for a plain GEMV.
+struct TopkArgs {
+  int32_t k;           // 0: no top-k (plain GEMV)
+  int32_t n_wg, n_grp;
+  uint64_t* cand;      // [n_wg + n_grp][M][k] keys: level 0, then level 1
+  uint32_t* cnt;       // [n_grp + 1] arrival counters (zero between calls)
+  int32_t* ids;        // [M][k] rows, best first; -1 past the last number
+  float* vals;         // [M][k] or null
+};
+
 struct GemvBatch {
   GemvJob job[kMaxBatch];
   int32_t n_jobs;
@@ -54,6 +64,7 @@ struct GemvBatch {
   // 16 rows of a tile; q4 kinds with prepared activations only).  The jobs'
   // wg_begin and ks then count units.
   int32_t sl;
+  TopkArgs tk;   // one job, 4-wave workgroups, M <= 4; job[0].y may be null
 };
 
 // ---------------------------------------------------------------------------
@@ -117,6 +128,8 @@ __device__ __forceinline__ int find_job(const GemvBatch& b, int wg) {
 int gemv_xl_bytes(int kind, int M, int waves, int max_tc);
 hipError_t launch_gemv(int kind, int M, int waves, const GemvBatch& b, int n_wg, int xl_bytes,
                        hipStream_t s);
+// The GEMV of b.job[0] with the top-k of its outputs (b.tk), 4-wave workgroups, M <= 4.
+hipError_t launch_gemv_topk(int kind, int M, const GemvBatch& b, int n_wg, int xl_bytes, hipStream_t s);
 hipError_t launch_unpack(int kind, const uint8_t* w, int TR, int TC, uint8_t* codes,
                          uint16_t* meta0, uint16_t* meta1, uint16_t* row_meta, hipStream_t s);
 hipError_t launch_decode(int kind, const uint8_t* w, int TR, int TC, float* out, hipStream_t s);

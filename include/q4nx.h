@@ -363,7 +363,34 @@ int q4nx_gguf_to_q41(int gguf_type, const void* src, size_t src_bytes, int rows,
 int q4nx_q8_rows(const q4nx_weight* w, const int32_t* ids, int T, float* out, void* stream);
 
 /*
- * Greedy pick after the lm_head GEMV: for each row m of y (fp32, row stride
+ * The lm_head GEMV with its greedy / top-k pick in the same launch (NPU
+ * engine page, "Q4NX chunks": the Q8 tied embedding / lm_head; onw technical
+ * notes, "host work of one step": a decode step ends by picking tokens from
+ * the head's logits).  For every activation row m: the k largest of
+ * y[m] = W x[m] in decreasing order, the lower row first among equal values
+ * (zeros of either sign are equal); NaNs are skipped, and past the last
+ * number ids are -1 and vals NaN.  The products are q4nx_gemv's (same bits).
+ *   w     any chunk kind; the prepared-activation GEMV must fit it (cols at
+ *         most 7168 at M = 4 ... 28672 at M = 1) and the launch must take at
+ *         most 4096 workgroups, else E_SHAPE
+ *   x     DEVICE bf16 [M][cols], 16-byte aligned;  M 1..4;  k 1..min(16, rows)
+ *   y     DEVICE fp32 [M][rows] to receive the logits, or NULL (not written)
+ *   ids   DEVICE int32 [M][k];  vals DEVICE fp32 [M][k] or NULL
+ *   ws    DEVICE workspace of q4nx_gemv_topk_ws(w, M, k) bytes, 256-byte
+ *         aligned, holding zeros before its first use; every call leaves it
+ *         ready for the next one; calls that share it must not overlap.
+ * Every workgroup picks the top k of its own rows; the last workgroup of each
+ * group of 64 merges its group's lists, and the last group merges the groups'
+ * (device-scope stores and counters in the workspace).
+ */
+size_t q4nx_gemv_topk_ws(const q4nx_weight* w, int M, int k);
+int q4nx_gemv_topk(const q4nx_weight* w, const uint16_t* x, int M, int k, float* y, int32_t* ids,
+                   float* vals, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Greedy pick over logits already in memory (the same ordering as
+ * q4nx_gemv_topk with k = 1; NPU engine page, "Q4NX chunks", the tied Q8
+ * lm_head whose logits it reads): for each row m of y (fp32, row stride
  * ldy), the index of the largest of its first n values, the lowest index
  * among equal maxima (zeros of either sign are equal); NaNs are skipped, and
  * a row of only NaNs gives -1.

@@ -9,8 +9,9 @@ the HIP kernels.  It is plain, slow and written to be checked by eye:
   a pure-Python scalar decoder used as brute force on tiny grids;
 * ``ref``     -- float64 products y = W x with the per-output error scale
   a = sum |w x|, the tolerance test, SwiGLU, the MoE layer and its combine,
-  the router (logits, softmax, top-k, renormalisation), and the Q4_K -> q4_1
-  repack with its rounding bound;
+  the router (logits, softmax, top-k, renormalisation), the greedy / top-k
+  pick from the head's logits, and the Q4_K -> q4_1 repack with its rounding
+  bound;
 * ``gguf``    -- GGUF Q4_0 / Q4_1 / Q4_K blocks decoded from their own
   definition, and the q4_1 fields the GGUF -> q4_1 conversion must give.
 
@@ -30,7 +31,7 @@ do not reuse this code's formulas (tests/test_oracle_pins.py).
 from .decode import (KIND_BYTES, decode_fields, weights_exact, weights_f32, unpack_expected,
                      scalar_decode_chunk)
 from .ref import (gemv_ref, check_tol, tol_ratio, silu, swiglu, moe_layer_ref, moe_combine_ref,
-                  repack_q4k_to_q41, repack_bound, router_topk, router_logits_ref)
+                  repack_q4k_to_q41, repack_bound, router_topk, router_logits_ref, head_topk)
 from .gguf import (GGUF_Q4_0, GGUF_Q4_1, GGUF_Q4_K, gguf_bytes, gguf_fields, gguf_dequant,
                    gguf_to_q41, gguf_to_q41_bound)
 
@@ -38,6 +39,6 @@ __all__ = [
     "KIND_BYTES", "decode_fields", "weights_exact", "weights_f32", "unpack_expected",
     "scalar_decode_chunk", "gemv_ref", "check_tol", "tol_ratio", "silu", "swiglu",
     "moe_layer_ref", "moe_combine_ref", "repack_q4k_to_q41", "repack_bound", "router_topk",
-    "router_logits_ref", "GGUF_Q4_0", "GGUF_Q4_1", "GGUF_Q4_K", "gguf_bytes", "gguf_fields",
+    "router_logits_ref", "head_topk", "GGUF_Q4_0", "GGUF_Q4_1", "GGUF_Q4_K", "gguf_bytes", "gguf_fields",
     "gguf_dequant", "gguf_to_q41", "gguf_to_q41_bound",
 ]

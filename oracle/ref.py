@@ -203,3 +203,25 @@ def router_logits_ref(R_bits, X_bits):
     R = _x64(R_bits)
     X = _x64(X_bits)
     return X @ R.T, np.abs(X) @ np.abs(R).T
+
+
+def head_topk(y, k: int):
+    """The greedy / top-k pick from the lm_head's logits (NPU engine page, "Q4NX
+    chunks": the tied Q8 embedding / lm_head; onw technical notes, the host
+    work of one step picks the next token from the head's outputs).
+
+    y [M, N] (taken as given, in its own precision).  Returns ids [M, k] int32:
+    per row the indices of the k largest values in decreasing order, the lower
+    index first among equal values (-0 and +0 are equal); NaNs are never
+    picked, and past the last number the ids are -1.
+    """
+    Y = np.atleast_2d(np.asarray(y))
+    M, N = Y.shape
+    out = np.full((M, k), -1, dtype=np.int32)
+    for m in range(M):
+        row = Y[m]
+        order = sorted((i for i in range(N) if not math.isnan(float(row[i]))),
+                       key=lambda i: (-float(row[i]), i))
+        for j, i in enumerate(order[:k]):
+            out[m, j] = i
+    return out

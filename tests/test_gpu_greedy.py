@@ -13,7 +13,7 @@ import pytest
 import oracle
 import synth
 
-from _gpu import dev_bf16, dev_f32, dev_i32, dev_u8, have_gpu, host, q, torch, weight
+from _gpu import dev_bf16, dev_f32, dev_i32, dev_u8, gemv, have_gpu, host, q, torch, weight
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not have_gpu(), reason="needs a GPU")]
 
@@ -127,3 +127,127 @@ def test_argmax_signed_zeros_are_equal(split):
     got, gv = host(idx), host(val)
     assert got.tolist() == [4500, 100]
     assert np.signbit(gv[0]) and not np.signbit(gv[1])
+
+
+# ----------------------------------------------------------------------------
+# q4nx_gemv_topk: the head GEMV with its top-k pick in the same launch
+# ----------------------------------------------------------------------------
+def _head(kind, layout, N, K, tag):
+    g = synth.rng("gpu-topk", tag, kind, layout or "-", N, K)
+    if kind == "q4_1":
+        return synth.gen_q4_1(g, N, K, zero="normal")
+    if kind == "q4_k":
+        return synth.gen_q4_k(g, N, K)
+    return synth.gen_q8(g, N, K, layout)
+
+
+def _topk(w, x, M, k, with_y=True, with_vals=True, ws=None):
+    N = w.rows
+    ids = torch.full((M, k), -7, dtype=torch.int32, device="cuda")
+    vals = torch.full((M, k), float("nan"), dtype=torch.float32, device="cuda") if with_vals else None
+    y = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda") if with_y else None
+    if ws is None:
+        ws = torch.zeros(q().gemv_topk_ws(w, M, k), dtype=torch.uint8, device="cuda")
+    q().gemv_topk(w, dev_bf16(x), M, k, ids, ws, y=y, vals=vals)
+    return host(ids), (host(vals) if with_vals else None), (host(y) if with_y else None), ws
+
+
+@pytest.mark.parametrize("kind,layout", [("q8", "A"), ("q8", "B"), ("q4_1", None), ("q4_k", None)])
+@pytest.mark.parametrize("k", [1, 10])
+def test_gemv_topk_full_size_head(kind, layout, k):
+    """151936 x 2560 head (the tied embedding / lm_head shape): the logits equal
+    q4nx_gemv's bit for bit, the picks equal the oracle's on those logits, the
+    values are the logits at the picks, and the workspace counters are back to
+    zero after every call."""
+    N, K, M = 151936, 2560, 1
+    ch = _head(kind, layout, N, K, "full")
+    w = weight(dev_u8(ch), N, K, kind, layout)
+    x = synth.gen_x(synth.rng("gpu-topk", "x", kind, k), M, K)
+    y_plain = gemv(dev_u8(ch), N, K, kind, x, layout)
+    ws = None
+    for rep in range(2):
+        ids, vals, y, ws = _topk(w, x, M, k, ws=ws)
+        np.testing.assert_array_equal(y.view(np.uint32), y_plain.view(np.uint32))
+        np.testing.assert_array_equal(ids, oracle.head_topk(y, k))
+        np.testing.assert_array_equal(vals.view(np.uint32), y[0, ids[0]].view(np.uint32)[None, :])
+        assert torch.count_nonzero(ws[:256]).item() == 0
+    # the picked logits against the float64 reference of those rows
+    rows = ids[0]
+    W = oracle.weights_exact(ch[rows // 32], kind, 32 * len(rows), K, layout)
+    sel = (rows % 32) + 32 * np.arange(len(rows))
+    yr, a = oracle.gemv_ref(W[sel], x)
+    assert oracle.tol_ratio(vals, yr, a) <= 1.0
+
+
+@pytest.mark.parametrize("M", [1, 2, 3])
+def test_gemv_topk_without_logits_rows_and_m(M):
+    """No logits written (y = NULL), M activation rows, k = 16, a 40960-row q4_1
+    head split into 16-row units: the picks equal the oracle's on q4nx_gemv's logits."""
+    N, K, k = 40960, 2560, 16
+    ch = _head("q4_1", None, N, K, "rows")
+    w = weight(dev_u8(ch), N, K, "q4_1")
+    x = synth.gen_x(synth.rng("gpu-topk", "xm", M), M, K)
+    y_plain = gemv(dev_u8(ch), N, K, "q4_1", x)
+    ids, vals, _, _ = _topk(w, x, M, k, with_y=False)
+    np.testing.assert_array_equal(ids, oracle.head_topk(y_plain, k))
+    for m in range(M):
+        np.testing.assert_array_equal(vals[m].view(np.uint32), y_plain[m, ids[m]].view(np.uint32))
+
+
+def test_gemv_topk_ties_nans_and_small_heads():
+    """Equal rows (identical chunks give identical logits: the lower row wins),
+    rows poisoned by a NaN scale (never picked), a head of one tile row with
+    k larger than its numbers (then -1), and a Q8 head."""
+    N, K = 96, 512
+    ch = _head("q4_1", None, N, K, "ties")
+    ch[1] = ch[0]                       # tile row 1 repeats tile row 0: rows 32..63 tie with 0..31
+    # NaN scale in tile row 2, row r = 5, group 0 of every chunk: row 69 is NaN
+    for tc in range(K // 256):
+        ch[2, tc, 4096 + 4 * (8 * 5):4096 + 4 * (8 * 5) + 2] = np.frombuffer(np.uint16(0x7FC0).tobytes(), np.uint8)
+    w = weight(dev_u8(ch), N, K, "q4_1")
+    x = synth.gen_x(synth.rng("gpu-topk", "xt"), 2, K)
+    ids, vals, y, _ = _topk(w, x, 2, 16)
+    assert np.isnan(y[:, 69]).all()
+    np.testing.assert_array_equal(ids, oracle.head_topk(y, 16))
+    assert 69 not in ids
+    # one tile row, every row NaN but 3: k = 8 gives 3 picks, then -1
+    ch1 = _head("q4_1", None, 32, 256, "one")
+    for r in range(32):
+        if r not in (4, 17, 30):
+            ch1[0, 0, 4096 + 4 * (8 * r):4096 + 4 * (8 * r) + 2] = np.frombuffer(np.uint16(0x7FC0).tobytes(), np.uint8)
+    w1 = weight(dev_u8(ch1), 32, 256, "q4_1")
+    x1 = synth.gen_x(synth.rng("gpu-topk", "x1"), 1, 256)
+    ids1, vals1, y1, _ = _topk(w1, x1, 1, 8)
+    np.testing.assert_array_equal(ids1, oracle.head_topk(y1, 8))
+    assert list(ids1[0, 3:]) == [-1] * 5 and np.isnan(vals1[0, 3:]).all()
+    # a Q8 head of 2048 rows in layout B
+    ch8 = _head("q8", "B", 2048, 1024, "q8small")
+    w8 = weight(dev_u8(ch8), 2048, 1024, "q8", "B")
+    x8 = synth.gen_x(synth.rng("gpu-topk", "x8"), 3, 1024)
+    ids8, _, y8, _ = _topk(w8, x8, 3, 5)
+    np.testing.assert_array_equal(ids8, oracle.head_topk(y8, 5))
+
+
+def test_gemv_topk_graph_replays():
+    """The one-launch head captured in a graph and replayed on new activations."""
+    N, K, k = 151936, 2560, 4
+    ch = _head("q8", "A", N, K, "graph")
+    w = weight(dev_u8(ch), N, K, "q8", "A")
+    xs = [synth.gen_x(synth.rng("gpu-topk", "gx", i), 1, K) for i in range(3)]
+    xd = dev_bf16(xs[0])
+    ids = torch.full((1, k), -7, dtype=torch.int32, device="cuda")
+    ws = torch.zeros(q().gemv_topk_ws(w, 1, k), dtype=torch.uint8, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        q().gemv_topk(w, xd, 1, k, ids, ws)
+    torch.cuda.synchronize()
+    for rep, i in enumerate((1, 2, 0, 1)):
+        xd.copy_(dev_bf16(xs[i]))
+        ids.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        want = oracle.head_topk(gemv(dev_u8(ch), N, K, "q8", xs[i], "A"), k)
+        np.testing.assert_array_equal(host(ids), want)

@@ -431,3 +431,35 @@ def test_router_logits_one_hot_column():
     z, a = oracle.router_logits_ref(R, X)
     np.testing.assert_array_equal(z[0], synth.bf16_to_f32(R[:, 13]).astype(np.float64))
     np.testing.assert_array_equal(a[0], np.abs(z[0]))
+
+
+def test_head_topk_hand_worked_and_brute_force():
+    """The head's pick: hand-worked rows with ties, signed zeros and NaNs, then
+    brute force (repeated argmax over what is left, a different method) on
+    random rows with many repeated values."""
+    nan = float("nan")
+    y = np.array([[1.0, 3.0, 3.0, -0.0, 0.0, nan, 2.0],
+                  [nan, nan, -1.0, nan, -1.0, -2.0, -0.0]], dtype=np.float32)
+    ids = oracle.head_topk(y, 5)
+    np.testing.assert_array_equal(ids[0], [1, 2, 6, 0, 3])     # 3, 3 (lower index first), 2, 1, then -0 (index 3) ahead of +0
+    np.testing.assert_array_equal(ids[1], [6, 2, 4, 5, -1])    # -0, -1, -1, -2, then nothing (NaNs never picked)
+    rng = np.random.default_rng(7)
+    for trial in range(20):
+        M, N, k = 2, int(rng.integers(1, 40)), int(rng.integers(1, 9))
+        v = rng.integers(-4, 5, (M, N)).astype(np.float32)
+        v[rng.random((M, N)) < 0.1] = np.nan
+        got = oracle.head_topk(v, k)
+        for m in range(M):
+            left = [i for i in range(N) if not np.isnan(v[m, i])]
+            want = []
+            for _ in range(k):
+                if not left:
+                    want.append(-1)
+                    continue
+                best = left[0]
+                for i in left[1:]:
+                    if v[m, i] > v[m, best]:
+                        best = i
+                want.append(best)
+                left.remove(best)
+            np.testing.assert_array_equal(got[m], want)
