@@ -63,6 +63,14 @@ class MoeDebug(ctypes.Structure):
                 ("d_shared", ctypes.c_void_p)]
 
 
+class ChunkLayout(ctypes.Structure):
+    """q4nx_chunk_layout: where a q4_1 / Q4_K chunk keeps each field (see include/q4nx.h)."""
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "chunk_bytes", "code_off", "code_row", "code_group", "code_step", "code_pairing",
+        "code_high_first", "f0_off", "f0_row", "f0_group", "f1_off", "f1_row", "f1_group",
+        "s_off", "s_row", "m_off", "m_row")]
+
+
 _P = ctypes.c_void_p
 _I = ctypes.c_int
 _lib.q4nx_weight_check.argtypes = [ctypes.POINTER(Weight)]
@@ -75,6 +83,9 @@ _lib.q4nx_gemm_batched.argtypes = [ctypes.POINTER(GemmJob), _I, _P, _I, _P, ctyp
 _lib.q4nx_gemm_batched_ws.argtypes = [ctypes.POINTER(GemmJob), _I]
 _lib.q4nx_gemm_batched_ws.restype = ctypes.c_size_t
 _lib.q4nx_gemm_exchange_mode.argtypes = [_I]
+_lib.q4nx_chunk_layout_default.argtypes = [_I, ctypes.POINTER(ChunkLayout)]
+_lib.q4nx_chunk_layout_check.argtypes = [ctypes.POINTER(ChunkLayout)]
+_lib.q4nx_relayout.argtypes = [ctypes.POINTER(ChunkLayout), ctypes.POINTER(Weight), _P, ctypes.c_size_t, _P]
 _lib.q4nx_gemv_topk_ws.argtypes = [ctypes.POINTER(Weight), _I, _I]
 _lib.q4nx_gemv_topk_ws.restype = ctypes.c_size_t
 _lib.q4nx_gemv_topk.argtypes = [ctypes.POINTER(Weight), _P, _I, _I, _P, _P, _P, _P, ctypes.c_size_t, _P]
@@ -106,7 +117,8 @@ _lib.q4nx_status_str.restype = ctypes.c_char_p
 _lib.q4nx_last_error.restype = ctypes.c_char_p
 for _f in ("q4nx_weight_check", "q4nx_gemv", "q4nx_gemv_batched", "q4nx_gemm_block", "q4nx_gemm_batched",
            "q4nx_moe_experts", "q4nx_unpack", "q4nx_decode", "q4nx_repack_q4k_to_q41", "q4nx_gguf_to_q41", "q4nx_q8_rows", "q4nx_argmax", "q4nx_moe_router", "q4nx_version", "q4nx_plan_create",
-           "q4nx_plan_run", "q4nx_plan_errors", "q4nx_gemm_exchange_mode", "q4nx_gemv_topk"):
+           "q4nx_plan_run", "q4nx_plan_errors", "q4nx_gemm_exchange_mode", "q4nx_gemv_topk",
+           "q4nx_chunk_layout_default", "q4nx_chunk_layout_check", "q4nx_relayout"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -253,6 +265,30 @@ def gemv_topk(w: Weight, x, M: int, k: int, ids, ws, y=None, vals=None, stream=N
     of y = x @ W^T, in one launch.  ws: zero-initialised, gemv_topk_ws(w, M, k) bytes."""
     _check(_lib.q4nx_gemv_topk(ctypes.byref(w), _ptr(x), M, k, _ptr(y), _ptr(ids), _ptr(vals),
                                _ptr(ws), _nbytes(ws) if ws_bytes is None else ws_bytes, _stream(stream)))
+
+
+def chunk_layout_default(kind) -> ChunkLayout:
+    """The library's own in-chunk layout of q4_1 (5120) or Q4_K (4736) chunks."""
+    L = ChunkLayout()
+    _check(_lib.q4nx_chunk_layout_default(CHUNK_BYTES[kind] if isinstance(kind, str) else int(kind),
+                                          ctypes.byref(L)))
+    return L
+
+
+def chunk_layout(**fields) -> ChunkLayout:
+    """A layout descriptor from its field values (see include/q4nx.h)."""
+    return ChunkLayout(**fields)
+
+
+def chunk_layout_check(L: ChunkLayout) -> int:
+    """Host-only check of a layout; returns the status code (0 = valid)."""
+    return _lib.q4nx_chunk_layout_check(ctypes.byref(L))
+
+
+def relayout(L: ChunkLayout, src: Weight, out, stream=None, out_bytes: int | None = None) -> None:
+    """Chunks of src (in layout L) -> the same weight in the library's layout, into out."""
+    _check(_lib.q4nx_relayout(ctypes.byref(L), ctypes.byref(src), _ptr(out),
+                              _nbytes(out) if out_bytes is None else out_bytes, _stream(stream)))
 
 
 def gemm_exchange_mode(mode: int) -> None:

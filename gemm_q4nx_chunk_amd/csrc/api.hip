@@ -814,6 +814,94 @@ int q4nx_repack_q4k_to_q41(const q4nx_weight* w, void* out, size_t out_bytes, vo
   return hip_status(e, "repack launch");
 }
 
+static_assert(sizeof(q4nx_chunk_layout) == sizeof(q4nx::ChunkLayout), "layout descriptor");
+
+int q4nx_chunk_layout_default(int chunk_bytes, q4nx_chunk_layout* out) {
+  if (!out) return fail(Q4NX_E_ARG, "chunk_layout_default: null output");
+  if (chunk_bytes != Q4NX_Q4_1_BYTES && chunk_bytes != Q4NX_Q4_K_BYTES)
+    return fail(Q4NX_E_CHUNK_KIND, "chunk_layout_default: %d is not 5120 (q4_1) or 4736 (Q4_K)", chunk_bytes);
+  q4nx_chunk_layout L;
+  memset(&L, 0, sizeof L);
+  L.chunk_bytes = chunk_bytes;
+  L.code_off = 0; L.code_row = 128; L.code_group = 16; L.code_step = 1;
+  L.code_pairing = 0; L.code_high_first = 0;
+  if (chunk_bytes == Q4NX_Q4_1_BYTES) {
+    L.f0_off = 4096; L.f0_row = 32; L.f0_group = 4;
+    L.f1_off = 4098; L.f1_row = 32; L.f1_group = 4;
+  } else {
+    L.f0_off = 4096; L.f0_row = 16; L.f0_group = 2;
+    L.f1_off = 4097; L.f1_row = 16; L.f1_group = 2;
+    L.s_off = 4608; L.s_row = 4;
+    L.m_off = 4610; L.m_row = 4;
+  }
+  *out = L;
+  return ok();
+}
+
+int q4nx_chunk_layout_check(const q4nx_chunk_layout* L) {
+  if (!L) return fail(Q4NX_E_ARG, "chunk_layout_check: null layout");
+  const int CB = L->chunk_bytes;
+  if (CB != Q4NX_Q4_1_BYTES && CB != Q4NX_Q4_K_BYTES)
+    return fail(Q4NX_E_CHUNK_KIND, "chunk_layout: chunk size %d is not 5120 (q4_1) or 4736 (Q4_K)", CB);
+  if (L->code_pairing != 0 && L->code_pairing != 1)
+    return fail(Q4NX_E_ARG, "chunk_layout: code_pairing %d is not 0 or 1", L->code_pairing);
+  std::vector<uint8_t> used(CB, 0);
+  // a field of `len` bytes at `off`: inside the chunk and on bytes nothing else uses
+  auto mark = [&](int64_t off, int len, const char* what, int r, int g) -> int {
+    if (off < 0 || off + len > CB)
+      return fail(Q4NX_E_ARG, "chunk_layout: %s of row %d, group %d at byte %lld leaves the %d-byte chunk",
+                  what, r, g, (long long)off, CB);
+    for (int i = 0; i < len; ++i)
+      if (used[off + i]++)
+        return fail(Q4NX_E_ARG, "chunk_layout: %s of row %d, group %d shares byte %lld with another field",
+                    what, r, g, (long long)(off + i));
+    return Q4NX_OK;
+  };
+  for (int r = 0; r < 32; ++r)
+    for (int g = 0; g < 8; ++g) {
+      for (int b = 0; b < 16; ++b) {   // each code byte holds two codes: mark it once
+        const int st = mark((int64_t)L->code_off + (int64_t)r * L->code_row + (int64_t)g * L->code_group +
+                                (int64_t)b * L->code_step, 1, "a code byte", r, g);
+        if (st) return st;
+      }
+      const int fl = CB == Q4NX_Q4_1_BYTES ? 2 : 1;
+      int st = mark((int64_t)L->f0_off + (int64_t)r * L->f0_row + (int64_t)g * L->f0_group, fl, "field 0", r, g);
+      if (!st) st = mark((int64_t)L->f1_off + (int64_t)r * L->f1_row + (int64_t)g * L->f1_group, fl, "field 1", r, g);
+      if (st) return st;
+    }
+  if (CB == Q4NX_Q4_K_BYTES)
+    for (int r = 0; r < 32; ++r) {
+      int st = mark((int64_t)L->s_off + (int64_t)r * L->s_row, 2, "S", r, 0);
+      if (!st) st = mark((int64_t)L->m_off + (int64_t)r * L->m_row, 2, "M", r, 0);
+      if (st) return st;
+    }
+  for (int i = 0; i < CB; ++i)
+    if (!used[i]) return fail(Q4NX_E_ARG, "chunk_layout: byte %d of the chunk belongs to no field", i);
+  return ok();
+}
+
+int q4nx_relayout(const q4nx_chunk_layout* L, const q4nx_weight* src, void* out, size_t out_bytes, void* stream) {
+  int st = q4nx_chunk_layout_check(L);
+  if (st) return st;
+  st = check_weight(src, "relayout");
+  if (st) return st;
+  if (src->chunk_bytes != L->chunk_bytes)
+    return fail(Q4NX_E_CHUNK_KIND, "relayout: weight chunks of %d bytes, layout for %d", src->chunk_bytes,
+                L->chunk_bytes);
+  if (!out) return fail(Q4NX_E_ARG, "relayout: null output");
+  if (!aligned(out, 16)) return fail(Q4NX_E_ALIGN, "relayout: output not 16-byte aligned");
+  const int64_t tiles = (int64_t)(src->rows / 32) * (src->cols / 256);
+  if (out_bytes < (size_t)(tiles * L->chunk_bytes))
+    return fail(Q4NX_E_SHORT, "relayout: output holds %zu bytes, %lld needed", out_bytes,
+                (long long)(tiles * L->chunk_bytes));
+  if (tiles > 0x7FFFFFFF) return fail(Q4NX_E_SHAPE, "relayout: too many tiles");
+  q4nx::ChunkLayout d;
+  memcpy(&d, L, sizeof d);
+  const hipError_t e = q4nx::launch_relayout(d, static_cast<const uint8_t*>(src->chunks), (int)tiles,
+                                             static_cast<uint8_t*>(out), static_cast<hipStream_t>(stream));
+  return hip_status(e, "relayout launch");
+}
+
 static int gguf_geometry(int gtype, int* block_bytes, int* block_cols, int* align) {
   switch (gtype) {
     case Q4NX_GGUF_Q4_0: *block_bytes = 18; *block_cols = 32; *align = 2; return 1;

@@ -142,6 +142,63 @@ __global__ __launch_bounds__(256) void k_repack_q4k(const uint8_t* __restrict__ 
   *reinterpret_cast<uint32_t*>(oc + 4096 + 4 * (8 * r + g)) = sb | (zb << 16);
 }
 
+// ---------------------------------------------------------------------------
+// relayout: chunks in a described in-chunk layout -> the library's layout
+// ---------------------------------------------------------------------------
+// One workgroup per chunk: the source chunk comes into LDS with 16-byte loads,
+// then each thread assembles 16 bytes of the output chunk (code bytes r*128 +
+// k/2 hold codes k, k+1 of row r; then the metadata records) and stores them.
+__device__ __forceinline__ uint32_t rl_code(const uint8_t* c, const ChunkLayout& L, int r, int k) {
+  const int g = k >> 5, j = k & 31;
+  const int b = L.code_pairing ? (j & 15) : (j >> 1);
+  const int n = (L.code_pairing ? (j >> 4) : (j & 1)) ^ (L.code_high_first ? 1 : 0);
+  const uint8_t v = c[L.code_off + r * L.code_row + g * L.code_group + b * L.code_step];
+  return n ? (uint32_t)(v >> 4) : (uint32_t)(v & 15u);
+}
+
+__device__ __forceinline__ uint32_t rl_u16(const uint8_t* c, int off) {
+  return (uint32_t)c[off] | ((uint32_t)c[off + 1] << 8);
+}
+
+__global__ __launch_bounds__(256) void k_relayout(ChunkLayout L, const uint8_t* __restrict__ src,
+                                                  uint8_t* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) uint8_t c[5120];
+  const int CB = L.chunk_bytes, tid = threadIdx.x;
+  const uint8_t* s = src + (size_t)blockIdx.x * CB;
+  uint8_t* o = out + (size_t)blockIdx.x * CB;
+  for (int p = tid; p < CB / 16; p += 256)
+    *reinterpret_cast<u32x4*>(c + 16 * p) = *reinterpret_cast<const u32x4*>(s + 16 * p);
+  __syncthreads();
+  for (int p = tid; p < CB / 16; p += 256) {
+    uint32_t w[4] = {0, 0, 0, 0};
+    for (int e = 0; e < 16; ++e) {
+      const int ob = 16 * p + e;   // output byte
+      uint32_t v;
+      if (ob < 4096) {
+        const int r = ob >> 7, k = 2 * (ob & 127);
+        v = rl_code(c, L, r, k) | (rl_code(c, L, r, k + 1) << 4);
+      } else if (CB == 5120) {    // q4_1 (scale, zero) of (r, g) at 4096 + 4 (8r + g)
+        const int q = ob - 4096, rg = q >> 2, r = rg >> 3, g = rg & 7, f = q & 3;
+        const int off = f < 2 ? L.f0_off + r * L.f0_row + g * L.f0_group : L.f1_off + r * L.f1_row + g * L.f1_group;
+        v = c[off + (f & 1)];
+      } else if (ob < 4608) {      // Q4_K (scale, min) of (r, g) at 4096 + 2 (8r + g)
+        const int q = ob - 4096, rg = q >> 1, r = rg >> 3, g = rg & 7;
+        v = (q & 1) ? c[L.f1_off + r * L.f1_row + g * L.f1_group] : c[L.f0_off + r * L.f0_row + g * L.f0_group];
+      } else {                     // Q4_K (S, M) of row r at 4608 + 4r
+        const int q = ob - 4608, r = q >> 2, f = q & 3;
+        v = rl_u16(c, f < 2 ? L.s_off + r * L.s_row : L.m_off + r * L.m_row) >> (8 * (f & 1)) & 0xFFu;
+      }
+      w[e >> 2] |= (v & 0xFFu) << (8 * (e & 3));
+    }
+    *reinterpret_cast<u32x4*>(o + 16 * p) = u32x4{w[0], w[1], w[2], w[3]};
+  }
+}
+
+hipError_t launch_relayout(const ChunkLayout& L, const uint8_t* src, int tiles, uint8_t* out, hipStream_t s) {
+  hipLaunchKernelGGL(k_relayout, dim3(tiles), dim3(256), 0, s, L, src, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_repack_q4k(const uint8_t* w, int tiles, uint8_t* out, hipStream_t s) {
   hipLaunchKernelGGL(k_repack_q4k, dim3(tiles), dim3(256), 0, s, w, out);
   return hipGetLastError();

@@ -134,6 +134,15 @@ hipError_t launch_unpack(int kind, const uint8_t* w, int TR, int TC, uint8_t* co
                          uint16_t* meta0, uint16_t* meta1, uint16_t* row_meta, hipStream_t s);
 hipError_t launch_decode(int kind, const uint8_t* w, int TR, int TC, float* out, hipStream_t s);
 hipError_t launch_repack_q4k(const uint8_t* w, int tiles, uint8_t* out, hipStream_t s);
+// A described in-chunk layout (the fields of q4nx_chunk_layout), checked on the host.
+struct ChunkLayout {
+  int32_t chunk_bytes;
+  int32_t code_off, code_row, code_group, code_step, code_pairing, code_high_first;
+  int32_t f0_off, f0_row, f0_group;
+  int32_t f1_off, f1_row, f1_group;
+  int32_t s_off, s_row, m_off, m_row;
+};
+hipError_t launch_relayout(const ChunkLayout& L, const uint8_t* src, int tiles, uint8_t* out, hipStream_t s);
 hipError_t launch_gguf_q41(int gtype, const uint8_t* src, int TR, int TC, uint8_t* out, hipStream_t s);
 hipError_t launch_q8_rows(int kind, const uint8_t* w, int rows, int TC, const int32_t* ids, int T,
                           float* out, hipStream_t s);

@@ -318,6 +318,55 @@ int q4nx_moe_experts(const q4nx_moe_layer* L, const uint16_t* X, const int32_t* 
 int q4nx_repack_q4k_to_q41(const q4nx_weight* w, void* out, size_t out_bytes, void* stream);
 
 /*
+ * In-chunk layout of a q4_1 or Q4_K chunk (NPU engine page, "Q4NX chunks":
+ * the chunk sizes and what each kind holds are printed there, the byte order
+ * inside a chunk is left to a header that is not published).  The library's
+ * own order is the one at the top of this file; a layout descriptor says where
+ * another producer's chunks keep each field, so its tensors can be converted
+ * (q4nx_relayout) and then used by every call.  For row r (0..31), group
+ * g = k/32 (0..7) and j = k%32 of a tile:
+ *   code (r, k): byte code_off + r*code_row + g*code_group + b*code_step, with
+ *     code_pairing 0: b = j/2, the codes j and j+1 share a byte, nibble n = j%2;
+ *     code_pairing 1: b = j%16, the codes j and j+16 share a byte, n = j/16;
+ *     nibble n = 0 is the low one, or the high one when code_high_first != 0.
+ *   per (r, g): field 0 at f0_off + r*f0_row + g*f0_group, field 1 likewise:
+ *     q4_1: bf16 scale, bf16 zero;  Q4_K: u8 scale, u8 min.
+ *   per row r (Q4_K only): bf16 S at s_off + r*s_row, bf16 M at m_off + r*m_row.
+ * Multi-byte fields are little-endian.  A valid layout puts every field inside
+ * the chunk and uses each of its bytes exactly once (4096 code bytes plus the
+ * metadata fill the chunk size exactly).
+ */
+typedef struct q4nx_chunk_layout {
+  int32_t chunk_bytes;   /* 5120 (q4_1) or 4736 (Q4_K) */
+  int32_t code_off, code_row, code_group, code_step, code_pairing, code_high_first;
+  int32_t f0_off, f0_row, f0_group;
+  int32_t f1_off, f1_row, f1_group;
+  int32_t s_off, s_row;  /* Q4_K only */
+  int32_t m_off, m_row;  /* Q4_K only */
+} q4nx_chunk_layout;
+
+/* The library's own layout for 5120 or 4736 (E_CHUNK_KIND otherwise). */
+int q4nx_chunk_layout_default(int chunk_bytes, q4nx_chunk_layout* out);
+
+/*
+ * Host-only check of a layout: E_CHUNK_KIND for another chunk size, E_ARG when
+ * a field leaves the chunk, two fields share a byte or a byte is unused (the
+ * detail names the first such field and tile position).
+ */
+int q4nx_chunk_layout_check(const q4nx_chunk_layout* L);
+
+/*
+ * Chunks in layout L -> the same weight in the library's layout, bit for bit
+ * (codes and metadata are moved, never changed).  src describes the input
+ * tensor (its chunk_bytes must equal L->chunk_bytes); out receives
+ * (rows/32)*(cols/256) chunks of the same size, 16-byte aligned (E_SHORT when
+ * out_bytes is smaller).  One workgroup per chunk, staged through LDS.
+ * Asynchronous on stream; src and out must not overlap.
+ */
+int q4nx_relayout(const q4nx_chunk_layout* L, const q4nx_weight* src, void* out, size_t out_bytes,
+                  void* stream);
+
+/*
  * GGUF 4-bit tensors -> q4_1 chunks (NPU engine page, section "From a GGUF":
  * the exact GGUF types map to q4_1 with codes unchanged, Q4_0 as scale d and
  * zero -8d, Q4_1 as scale d and zero m, Q4_K per 32-column sub-block as scale

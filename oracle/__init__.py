@@ -6,7 +6,8 @@ library's own path never does, and it shares no code, table or constant with
 the HIP kernels.  It is plain, slow and written to be checked by eye:
 
 * ``decode``  -- chunk bytes -> logical fields -> exact weights (float64), plus
-  a pure-Python scalar decoder used as brute force on tiny grids;
+  a pure-Python scalar decoder used as brute force on tiny grids, and the same
+  decode for chunks in another described in-chunk layout;
 * ``ref``     -- float64 products y = W x with the per-output error scale
   a = sum |w x|, the tolerance test, SwiGLU, the MoE layer and its combine,
   the router (logits, softmax, top-k, renormalisation), the greedy / top-k
@@ -29,7 +30,7 @@ file (none is available; hand-worked blocks pin the reading instead).  Everythin
 do not reuse this code's formulas (tests/test_oracle_pins.py).
 """
 from .decode import (KIND_BYTES, decode_fields, weights_exact, weights_f32, unpack_expected,
-                     scalar_decode_chunk)
+                     scalar_decode_chunk, default_layout, decode_fields_layout, weights_exact_layout)
 from .ref import (gemv_ref, check_tol, tol_ratio, silu, swiglu, moe_layer_ref, moe_combine_ref,
                   repack_q4k_to_q41, repack_bound, router_topk, router_logits_ref, head_topk)
 from .gguf import (GGUF_Q4_0, GGUF_Q4_1, GGUF_Q4_K, gguf_bytes, gguf_fields, gguf_dequant,
@@ -37,6 +38,7 @@ from .gguf import (GGUF_Q4_0, GGUF_Q4_1, GGUF_Q4_K, gguf_bytes, gguf_fields, ggu
 
 __all__ = [
     "KIND_BYTES", "decode_fields", "weights_exact", "weights_f32", "unpack_expected",
+    "default_layout", "decode_fields_layout", "weights_exact_layout",
     "scalar_decode_chunk", "gemv_ref", "check_tol", "tol_ratio", "silu", "swiglu",
     "moe_layer_ref", "moe_combine_ref", "repack_q4k_to_q41", "repack_bound", "router_topk",
     "router_logits_ref", "head_topk", "GGUF_Q4_0", "GGUF_Q4_1", "GGUF_Q4_K", "gguf_bytes", "gguf_fields",

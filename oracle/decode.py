@@ -211,3 +211,67 @@ def scalar_decode_chunk(chunk: bytes, kind: str, q8_layout: str | None = None):
                 code = struct.unpack("<b", b[pos:pos + 1])[0]
                 out[r][k] = _bf16(b, 8192 + 2 * (8 * r + grp)) * code
     return out
+
+
+# ----------------------------------------------------------------------------
+# other in-chunk layouts (q4_1 / Q4_K): the byte order inside a chunk is left
+# by the NPU engine page ("Q4NX chunks") to an unpublished header, so a layout
+# is described field by field (the same description as q4nx_chunk_layout):
+#   code (r, g, j): byte code_off + r*code_row + g*code_group + b*code_step,
+#     b = j//2 and nibble j%2 (code_pairing 0) or b = j%16 and nibble j//16
+#     (code_pairing 1); nibble 0 is the low one unless code_high_first;
+#   per (r, g): field 0 / field 1 at f*_off + r*f*_row + g*f*_group
+#     (q4_1: bf16 scale / zero; Q4_K: u8 scale / min);
+#   per row (Q4_K): bf16 S at s_off + r*s_row, bf16 M at m_off + r*m_row.
+# ----------------------------------------------------------------------------
+def default_layout(kind: str) -> dict:
+    """The project's own layout (the one decode_fields reads) as a description."""
+    L = {"code_off": 0, "code_row": 128, "code_group": 16, "code_step": 1, "code_pairing": 0,
+         "code_high_first": 0}
+    if kind == "q4_1":
+        L.update(f0_off=4096, f0_row=32, f0_group=4, f1_off=4098, f1_row=32, f1_group=4)
+    elif kind == "q4_k":
+        L.update(f0_off=4096, f0_row=16, f0_group=2, f1_off=4097, f1_row=16, f1_group=2,
+                 s_off=4608, s_row=4, m_off=4610, m_row=4)
+    else:
+        raise ValueError("layouts describe q4_1 and Q4_K chunks")
+    return L
+
+
+def decode_fields_layout(chunks, kind: str, N: int, K: int, L: dict) -> dict:
+    """decode_fields for chunks stored in the described layout L."""
+    if kind not in ("q4_1", "q4_k"):
+        raise ValueError("layouts describe q4_1 and Q4_K chunks")
+    g = _grid(chunks, kind, N, K)
+    r = _R[:, None, None]
+    gg = np.arange(8)[None, :, None]
+    j = np.arange(32)[None, None, :]
+    if L["code_pairing"] == 0:
+        b, nib = j // 2, j % 2
+    else:
+        b, nib = j % 16, j // 16
+    if L["code_high_first"]:
+        nib = 1 - nib
+    off = L["code_off"] + r * L["code_row"] + gg * L["code_group"] + b * L["code_step"]   # [32, 8, 32]
+    byte = g[..., off.reshape(32, 256)]                                                  # [TR, TC, 32, 256]
+    shift = (4 * np.broadcast_to(nib, (32, 8, 32))).reshape(32, 256).astype(np.uint8)
+    codes = _to_matrix((byte >> shift) & np.uint8(15))
+    rg0 = L["f0_off"] + _R[:, None] * L["f0_row"] + np.arange(8)[None, :] * L["f0_group"]
+    rg1 = L["f1_off"] + _R[:, None] * L["f1_row"] + np.arange(8)[None, :] * L["f1_group"]
+    if kind == "q4_1":
+        return {"codes": codes, "scale": _to_matrix(_u16_at(g, rg0)), "zero": _to_matrix(_u16_at(g, rg1))}
+    srow = L["s_off"] + _R * L["s_row"]
+    mrow = L["m_off"] + _R * L["m_row"]
+    return {"codes": codes, "sc": _to_matrix(g[..., rg0]), "mn": _to_matrix(g[..., rg1]),
+            "S": _to_matrix(_u16_at(g, srow)[..., None]), "M": _to_matrix(_u16_at(g, mrow)[..., None])}
+
+
+def weights_exact_layout(chunks, kind: str, N: int, K: int, L: dict) -> np.ndarray:
+    """weights_exact for chunks stored in the described layout L (same formulas)."""
+    f = decode_fields_layout(chunks, kind, N, K, L)
+    c = f["codes"].astype(np.float64)
+    if kind == "q4_1":
+        return c * _expand(_bf16_to_f64(f["scale"]), 32) + _expand(_bf16_to_f64(f["zero"]), 32)
+    S = _expand(_bf16_to_f64(f["S"]), 256)
+    M = _expand(_bf16_to_f64(f["M"]), 256)
+    return (S * _expand(f["sc"].astype(np.float64), 32)) * c + M * _expand(f["mn"].astype(np.float64), 32)

@@ -246,6 +246,52 @@ def pack_q4_k(codes, sc, mn, S_bits, M_bits) -> np.ndarray:
     return out
 
 
+def pack_q4_layout(kind: str, fields: dict, L: dict) -> np.ndarray:
+    """Logical q4_1 / Q4_K fields -> chunks [TR, TC, CB] in the described in-chunk
+    layout L (the keys of q4nx_chunk_layout; every byte of a chunk must belong
+    to exactly one field).  fields: codes [N, K]; q4_1 scale, zero [N, K/32]
+    bf16 bits; Q4_K sc, mn [N, K/32] u8, S, M [N, K/256] bf16 bits."""
+    codes = np.asarray(fields["codes"], dtype=np.uint8)
+    N, K = codes.shape
+    TR, TC = _check_shape(N, K)
+    CB = Q4_1_BYTES if kind == "q4_1" else Q4_K_BYTES
+    out = np.zeros((TR, TC, CB), dtype=np.uint8)
+    ct = codes.reshape(TR, 32, TC, 8, 32).transpose(0, 2, 1, 3, 4)        # [TR, TC, r, g, j]
+    for r in range(32):
+        for g in range(8):
+            for j in range(32):
+                if L["code_pairing"] == 0:
+                    b, nib = j // 2, j % 2
+                else:
+                    b, nib = j % 16, j // 16
+                if L["code_high_first"]:
+                    nib = 1 - nib
+                off = L["code_off"] + r * L["code_row"] + g * L["code_group"] + b * L["code_step"]
+                out[:, :, off] |= (ct[:, :, r, g, j] << (4 * nib)).astype(np.uint8)
+
+    def put16(off, bits):              # bits [TR, TC]
+        b = np.asarray(bits, dtype=np.uint16)
+        out[:, :, off] = (b & 0xFF).astype(np.uint8)
+        out[:, :, off + 1] = (b >> 8).astype(np.uint8)
+
+    names = ("scale", "zero") if kind == "q4_1" else ("sc", "mn")
+    per = [np.asarray(fields[n]).reshape(TR, 32, TC, 8).transpose(0, 2, 1, 3) for n in names]
+    for r in range(32):
+        for g in range(8):
+            for fi, name in enumerate(("f0", "f1")):
+                off = L[name + "_off"] + r * L[name + "_row"] + g * L[name + "_group"]
+                if kind == "q4_1":
+                    put16(off, per[fi][:, :, r, g])
+                else:
+                    out[:, :, off] = per[fi][:, :, r, g].astype(np.uint8)
+    if kind == "q4_k":
+        for name, key in (("S", "s"), ("M", "m")):
+            rows = np.asarray(fields[name]).reshape(TR, 32, TC).transpose(0, 2, 1)
+            for r in range(32):
+                put16(L[key + "_off"] + r * L[key + "_row"], rows[:, :, r])
+    return out
+
+
 def q8_code_region(tile_codes: np.ndarray, layout: str) -> np.ndarray:
     """Tile codes [..., 32 r, 256 k] int8 -> code region [..., 8192] in the named layout."""
     t = np.asarray(tile_codes)

@@ -268,3 +268,37 @@ def test_descriptor_keeps_its_tensor_alive(q):
     t = torch.zeros(2 * 2 * 5120, dtype=torch.uint8)
     w = q.weight(t, 64, 512, "q4_1")
     assert w._owner is t and q.weight_check(w) == q.Q4NX_OK
+
+
+def test_chunk_layout_default_and_check(q):
+    """The library's own layout passes its check; layouts that leave the chunk
+    or overlap are refused with E_ARG (the fields' sizes add up to the chunk
+    size, so no valid layout leaves a byte unused), other chunk sizes with
+    E_CHUNK_KIND; relayout refuses before launching."""
+    for kind in ("q4_1", "q4_k"):
+        L = q.chunk_layout_default(kind)
+        assert q.chunk_layout_check(L) == 0
+    with pytest.raises(q.Q4nxError) as e:
+        q.chunk_layout_default(8704)
+    assert e.value.status == 2
+    blocks = dict(chunk_bytes=5120, code_off=4, code_row=160, code_group=20, code_step=1, code_pairing=1,
+                  code_high_first=0, f0_off=0, f0_row=160, f0_group=20, f1_off=2, f1_row=160, f1_group=20)
+    assert q.chunk_layout_check(q.chunk_layout(**blocks)) == 0
+    bad = [dict(blocks, f1_off=1),                 # zero overlaps the scale
+           dict(blocks, code_off=5),               # codes leave the chunk
+           dict(blocks, code_step=2),              # overlaps and leaves the chunk
+           dict(blocks, code_pairing=2),           # not a pairing
+           dict(blocks, chunk_bytes=4736)]         # a Q4_K chunk described with q4_1 records
+    for b in bad:
+        assert q.chunk_layout_check(q.chunk_layout(**b)) in (1, 2), b
+    assert q.chunk_layout_check(q.chunk_layout(**dict(blocks, chunk_bytes=8704))) == 2
+    w = _w(q, 64, 512, "q4_1")
+    with pytest.raises(q.Q4nxError) as e:
+        q.relayout(q.chunk_layout(**dict(blocks, f1_off=1)), w, 0x200000, stream=0, out_bytes=1 << 20)
+    assert e.value.status == 1
+    with pytest.raises(q.Q4nxError) as e:
+        q.relayout(q.chunk_layout(**blocks), w, 0x200000, stream=0, out_bytes=100)
+    assert e.value.status == 4
+    with pytest.raises(q.Q4nxError) as e:
+        q.relayout(q.chunk_layout_default("q4_k"), w, 0x200000, stream=0, out_bytes=1 << 20)
+    assert e.value.status == 2

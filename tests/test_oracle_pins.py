@@ -463,3 +463,69 @@ def test_head_topk_hand_worked_and_brute_force():
                 want.append(best)
                 left.remove(best)
             np.testing.assert_array_equal(got[m], want)
+
+
+# ----------------------------------------------------------------------------
+# described in-chunk layouts
+# ----------------------------------------------------------------------------
+def test_layout_hand_worked_block_chunk(golden_dir):
+    """A q4_1 chunk in a 20-byte-record layout, weights worked out by hand."""
+    import json
+    import os
+    doc = json.load(open(os.path.join(golden_dir, "layout_blocks_hand.json")))
+    ch = np.zeros(5120, np.uint8)
+    for off, v in doc["bytes"].items():
+        ch[int(off)] = v
+    W = oracle.weights_exact_layout(ch, "q4_1", 32, 256, doc["layout"])
+    for e in doc["expected"]:
+        assert W[e["r"], e["k"]] == e["w"], e
+
+
+@pytest.mark.parametrize("kind", ["q4_1", "q4_k"])
+def test_layout_default_description_reads_like_the_fixed_decoder(kind):
+    g = synth.rng("pin-layout", kind)
+    N, K = 64, 512
+    ch = synth.gen_q4_1(g, N, K, zero="normal") if kind == "q4_1" else synth.gen_q4_k(g, N, K)
+    a = oracle.decode_fields(ch, kind, N, K)
+    b = oracle.decode_fields_layout(ch, kind, N, K, oracle.default_layout(kind))
+    for name in a:
+        np.testing.assert_array_equal(a[name], b[name])
+
+
+LAYOUTS = {
+    "q4_1": {
+        "blocks": dict(code_off=4, code_row=160, code_group=20, code_step=1, code_pairing=1, code_high_first=0,
+                       f0_off=0, f0_row=160, f0_group=20, f1_off=2, f1_row=160, f1_group=20),
+        "columns": dict(code_off=0, code_row=1, code_group=512, code_step=32, code_pairing=0, code_high_first=1,
+                        f0_off=4096, f0_row=2, f0_group=64, f1_off=4608, f1_row=2, f1_group=64),
+    },
+    "q4_k": {
+        "blocks": dict(code_off=2, code_row=144, code_group=18, code_step=1, code_pairing=1, code_high_first=0,
+                       f0_off=0, f0_row=144, f0_group=18, f1_off=1, f1_row=144, f1_group=18,
+                       s_off=4608, s_row=4, m_off=4610, m_row=4),
+        "columns": dict(code_off=0, code_row=1, code_group=512, code_step=32, code_pairing=0, code_high_first=1,
+                        f0_off=4096, f0_row=1, f0_group=32, f1_off=4352, f1_row=1, f1_group=32,
+                        s_off=4608, s_row=2, m_off=4672, m_row=2),
+    },
+}
+
+
+@pytest.mark.parametrize("kind", ["q4_1", "q4_k"])
+@pytest.mark.parametrize("name", ["blocks", "columns"])
+def test_layout_pack_and_decode_round_trip(kind, name):
+    """Fields packed by the input generator in a described layout come back from
+    the oracle's decode of that layout unchanged (two independent readings of
+    the same description), and the weights equal those of the same fields in
+    the project's own layout."""
+    g = synth.rng("pin-layout-rt", kind, name)
+    N, K = 64, 512
+    ch = synth.gen_q4_1(g, N, K, zero="normal") if kind == "q4_1" else synth.gen_q4_k(g, N, K)
+    f = oracle.decode_fields(ch, kind, N, K)
+    L = LAYOUTS[kind][name]
+    other = synth.pack_q4_layout(kind, f, L)
+    assert not np.array_equal(other, ch)
+    back = oracle.decode_fields_layout(other, kind, N, K, L)
+    for key in f:
+        np.testing.assert_array_equal(back[key], f[key])
+    np.testing.assert_array_equal(oracle.weights_exact_layout(other, kind, N, K, L),
+                                  oracle.weights_exact(ch, kind, N, K))
