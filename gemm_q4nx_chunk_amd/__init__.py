@@ -79,6 +79,9 @@ _lib.q4nx_gemv_batched.argtypes = [ctypes.POINTER(GemvJob), _I, _I, _P]
 _lib.q4nx_gemm_block.argtypes = [ctypes.POINTER(Weight), _P, _P, _I, _P, ctypes.c_size_t, _P]
 _lib.q4nx_gemm_block_ws.argtypes = [ctypes.POINTER(Weight)]
 _lib.q4nx_gemm_block_ws.restype = ctypes.c_size_t
+_lib.q4nx_gemm_block_noalloc.argtypes = [ctypes.POINTER(Weight), _P, _P, _I, _P]
+_lib.q4nx_gemm_block_noalloc_max.argtypes = []
+_lib.q4nx_gemm_block_noalloc_max.restype = ctypes.c_size_t
 _lib.q4nx_gemm_batched.argtypes = [ctypes.POINTER(GemmJob), _I, _P, _I, _P, ctypes.c_size_t, _P]
 _lib.q4nx_gemm_batched_ws.argtypes = [ctypes.POINTER(GemmJob), _I]
 _lib.q4nx_gemm_batched_ws.restype = ctypes.c_size_t
@@ -252,6 +255,17 @@ def gemm_block(w: Weight, X, Y, M: int, ws=None, stream=None, ws_bytes: int | No
     """
     _check(_lib.q4nx_gemm_block(ctypes.byref(w), _ptr(X), _ptr(Y), M, _ptr(ws),
                                 _nbytes(ws) if ws_bytes is None else ws_bytes, _stream(stream)))
+
+
+def gemm_block_noalloc(w: Weight, X, Y, M: int, stream=None) -> None:
+    """gemm_block with the library's static workspace: allocates nothing.
+    Calls that may overlap on one GPU race (the workspace is shared)."""
+    _check(_lib.q4nx_gemm_block_noalloc(ctypes.byref(w), _ptr(X), _ptr(Y), M, _stream(stream)))
+
+
+def gemm_block_noalloc_max() -> int:
+    """Bytes of gemm_block_noalloc's static workspace."""
+    return int(_lib.q4nx_gemm_block_noalloc_max())
 
 
 def gemv_topk_ws(w: Weight, M: int, k: int) -> int:

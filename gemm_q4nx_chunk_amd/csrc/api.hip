@@ -11,6 +11,7 @@
 #include <cstdio>
 #include <algorithm>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -360,7 +361,7 @@ int gemm_setup(const q4nx_weight* const* w, float* const* Y, int n, const uint16
 }
 
 int gemm_launch(q4nx::GemmArgs& a, int kind, void* ws, size_t ws_bytes, void* stream,
-                const char* name) {
+                const char* name, bool may_probe = true) {
   const size_t need = q4nx::gemm_ws_bytes(a.NB, a.TC, a.M);
   if (need && (!ws || ws_bytes < need))
     return fail(Q4NX_E_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", name, ws_bytes, need);
@@ -374,7 +375,8 @@ int gemm_launch(q4nx::GemmArgs& a, int kind, void* ws, size_t ws_bytes, void* st
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const int mode = g_gemm_exchange_mode.load(std::memory_order_relaxed);
   a.test_mode = mode == 1 ? 1 : 0;
-  const bool local = a.S > 1 && mode != 2 && q4nx::xcd_round_robin(st) == 1;
+  const bool local = a.S > 1 && mode != 2 &&
+                     (may_probe ? q4nx::xcd_round_robin(st) : q4nx::xcd_round_robin_known()) == 1;
   const hipError_t e = q4nx::launch_gemm(kind, a, local, st);
   return hip_status(e, name);
 }
@@ -389,6 +391,80 @@ int q4nx_gemm_block(const q4nx_weight* w, const uint16_t* X, float* Y, int M, vo
   const int st = gemm_setup(&w, &Y, 1, X, M, "gemm_block", a);
   if (st) return st;
   const int r = gemm_launch(a, kind_of(w), ws, ws_bytes, stream, "gemm_block");
+  return r ? r : ok();
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// the allocation-free block GEMM
+// ---------------------------------------------------------------------------
+// Its workspace is `scratch`, in the code object: every GPU the library runs
+// on holds one until the process ends.  Each call clears the header words
+// that must start at zero (arrival counters, claim words, rescue flags) with a
+// small kernel on the caller's stream before the GEMM; the partial tiles are
+// written before they are read.  Calls that overlap on one GPU share the array
+// and race.  Host code never passes the array's name to a kernel: its device
+// address comes from hipGetSymbolAddress, once per device, with that device
+// current.
+constexpr size_t kNoAllocGemmBytes = q4nx::kGemmCntBytes + ((size_t)16 << 20);
+static_assert(kNoAllocGemmBytes >= q4nx::kGemmCntBytes + (size_t)Q4NX_GEMM_WG_TARGET * 64 *
+                                       q4nx::kGemmRowsPerWg * 32 * 4,
+              "scratch holds the largest split any call makes (workgroup rows x parts <= the target)");
+
+static __device__ __align__(256) uint8_t scratch[kNoAllocGemmBytes];
+
+namespace {
+
+constexpr int kHeaderZeroWords = (int)(q4nx::kGemmDiagOff / 4);
+
+__global__ void __launch_bounds__(256) k_clear_words(uint32_t* p, int n) {
+  for (int i = threadIdx.x; i < n; i += 256) p[i] = 0u;
+}
+
+std::once_flag g_scratch_once[64];
+void* g_scratch_ptr[64];
+hipError_t g_scratch_err[64];
+
+int scratch_address(void** out) {
+  int dev = 0;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "gemm_block_noalloc: current device");
+  if (dev < 0 || dev >= 64) return fail(Q4NX_E_HIP, "gemm_block_noalloc: device %d beyond 63", dev);
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+  });
+  if (g_scratch_err[dev] != hipSuccess) return hip_status(g_scratch_err[dev], "gemm_block_noalloc: scratch address");
+  if (!g_scratch_ptr[dev]) return fail(Q4NX_E_HIP, "gemm_block_noalloc: scratch address is null");
+  *out = g_scratch_ptr[dev];
+  return Q4NX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t q4nx_gemm_block_noalloc_max(void) { return kNoAllocGemmBytes; }
+
+int q4nx_gemm_block_noalloc(const q4nx_weight* w, const uint16_t* X, float* Y, int M, void* stream) {
+  q4nx::GemmArgs a;
+  const int st = gemm_setup(&w, &Y, 1, X, M, "gemm_block_noalloc", a);
+  if (st) return st;
+  const size_t need = q4nx::gemm_ws_bytes(a.NB, a.TC, a.M);
+  if (need > kNoAllocGemmBytes)
+    return fail(Q4NX_E_WORKSPACE, "gemm_block_noalloc: this call needs %zu bytes of scratch, the static "
+                "array holds %zu", need, kNoAllocGemmBytes);
+  void* ws = nullptr;
+  if (need) {
+    const int s2 = scratch_address(&ws);
+    if (s2) return s2;
+    k_clear_words<<<1, 256, 0, static_cast<hipStream_t>(stream)>>>(static_cast<uint32_t*>(ws), kHeaderZeroWords);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_status(e, "gemm_block_noalloc: clearing the scratch header");
+  }
+  const int r = gemm_launch(a, kind_of(w), ws, need, stream, "gemm_block_noalloc", false);
   return r ? r : ok();
 }
 

@@ -679,6 +679,12 @@ static int run_xcc_probe() {
   return ok;
 }
 
+int xcd_round_robin_known() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  return g_probe_result[dev].load() == 1 ? 1 : 0;
+}
+
 int xcd_round_robin(hipStream_t caller) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;

@@ -96,5 +96,7 @@ hipError_t launch_gemm(int kind, const GemmArgs& a, bool local, hipStream_t s);
 // the caller's stream and never while the caller's stream is being captured
 // (0 until the probe has run).
 int xcd_round_robin(hipStream_t caller);
+// The probe's answer if it has already run on this device, else 0; launches nothing.
+int xcd_round_robin_known();
 
 }  // namespace q4nx

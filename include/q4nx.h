@@ -206,6 +206,26 @@ int q4nx_gemm_block(const q4nx_weight* w, const uint16_t* X, float* Y, int M, vo
 size_t q4nx_gemm_block_ws(const q4nx_weight* w);
 
 /*
+ * q4nx_gemm_block without a workspace argument and without allocating, for
+ * callers that cannot allocate device memory: code under stream capture,
+ * tight serving loops, hosts that forbid hipMalloc.  Same arguments, result
+ * and errors as q4nx_gemm_block; its workspace is a static array of
+ * q4nx_gemm_block_noalloc_max() bytes (a 4 KB header + 16 MiB, enough for
+ * every split the GEMM makes) that each GPU the library runs on holds until
+ * the process ends.  Each call first clears the array's header with a small
+ * kernel on `stream` (no memset node), then runs the GEMM.  The array keeps
+ * the last call's contents and is shared by every call on one GPU: calls that
+ * may overlap on one GPU (other streams, other host threads) race and must be
+ * serialised by the caller.  A call whose split would need more than the array
+ * returns Q4NX_E_WORKSPACE.  The XCD placement of the K parts is used only
+ * when an earlier allocating call has already probed the device; otherwise
+ * the parts exchange through device-coherent stores (the same result).
+ */
+int q4nx_gemm_block_noalloc(const q4nx_weight* w, const uint16_t* X, float* Y, int M, void* stream);
+/* Bytes of the static workspace of q4nx_gemm_block_noalloc. */
+size_t q4nx_gemm_block_noalloc_max(void);
+
+/*
  * Test and tuning switch of the block GEMM's split-K exchange, for every later
  * call in the process: 0 (default) puts the K parts of a row on one XCD when a
  * one-time probe of the device shows workgroups dealt to XCDs round-robin;
