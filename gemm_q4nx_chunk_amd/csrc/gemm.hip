@@ -6,8 +6,8 @@
 // registers, to bf16 (round to nearest even); no bf16 copy of a weight is ever
 // written.  All M rows share one pass over the weights: splitting the token
 // rows over several passes would read the weights again (Strata article,
-// section 5.1, on an overlap attempt that lost speed by reading dense weights
-// twice).
+// section 3.2, the work split inside one layer: an overlap attempt lost speed
+// by reading the dense weights twice).
 //
 // Workgroup: 8 waves, one tile row (32 outputs) each, over a range of tile
 // columns.  The X columns of the current tile column (M x 256 bf16) sit in
