@@ -329,18 +329,26 @@ def decode_leg(specs, tag, steps, warmup, graph, M=1):
 # ----------------------------------------------------------------------------
 # CPU oracle baseline (bounded sample)
 # ----------------------------------------------------------------------------
-def cpu_baseline(specs, budget_s=15.0):
-    import oracle
+def _cpu_model() -> str:
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
-    done_bytes, t_dec, t_dot, names = 0, 0.0, 0.0, []
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_gemv_sample(specs, M, budget_s, tag):
+    """float64 decode + product of the oracle over specs until budget_s; returns
+    (bytes of chunks, decode s, product s, names, flops)."""
+    import oracle
+    done, t_dec, t_dot, names, flops = 0, 0.0, 0.0, [], 0
     t_start = time.time()
     for s in specs:
         ch = s.generate()
-        x = synth.gen_x(synth.rng("cpu", s.name), 1, s.K)
+        x = synth.gen_x(synth.rng("cpu", tag, s.name), M, s.K)
         t0 = time.perf_counter()
         W = oracle.weights_exact(ch, s.kind, s.N, s.K, s.q8_layout if s.kind == "q8" else None)
         t1 = time.perf_counter()
@@ -348,17 +356,70 @@ def cpu_baseline(specs, budget_s=15.0):
         t2 = time.perf_counter()
         t_dec += t1 - t0
         t_dot += t2 - t1
-        done_bytes += s.nbytes
+        done += s.nbytes
+        flops += 2 * M * s.N * s.K
         names.append(s.name)
         del W, ch
         if time.time() - t_start > budget_s:
             break
+    return done, t_dec, t_dot, names, flops
+
+
+def cpu_baseline(specs, moe_check=None, budget_s=15.0):
+    """The oracle, as it stands, on bounded samples of the workloads (host cores)."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threadpool_limits = None
+        threads = 1
+    done, t_dec, t_dot, names, _ = _oracle_gemv_sample(specs, 1, budget_s, "c2")
     tot = t_dec + t_dot
-    return {"value": done_bytes / tot / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"float64 decode + dot of {len(names)} q4_1 tensors of the decode step "
-                      f"({names[0]}..{names[-1]}, {done_bytes / 1e6:.0f} MB of chunks)",
-            "decode_s": t_dec, "dot_s": t_dot,
-            "host_cpus": len(os.sched_getaffinity(0))}
+    out = {"value": done / tot / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+           "sample": f"float64 decode + dot of {len(names)} q4_1 tensors of the decode step "
+                     f"({names[0]}..{names[-1]}, {done / 1e6:.0f} MB of chunks)",
+           "decode_s": t_dec, "dot_s": t_dot,
+           "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": _cpu_model(),
+           "threads_note": "cores = the BLAS thread pool, which runs the products; the "
+                           "oracle's decode is numpy elementwise work on one thread"}
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            d1, a1, b1, n1, _ = _oracle_gemv_sample(specs, 1, 5.0, "c2")
+        out["one_thread"] = {"value": d1 / (a1 + b1) / 1e9, "unit": "GB/s", "cores": 1,
+                             "sample": f"the first {len(n1)} tensors of the same step, {d1 / 1e6:.0f} MB"}
+    # mixed-kind decode (Q4_K projections of the first layers)
+    mixed = [s for s in synth.mixed_decode_specs(q8_layout="A") if s.kind == "q4_k"]
+    d3, a3, b3, n3, _ = _oracle_gemv_sample(mixed, 1, 5.0, "c3")
+    out["mixed_decode_q4k"] = {"GB_s": d3 / (a3 + b3) / 1e9, "tensors": len(n3), "bytes": d3,
+                               "s": a3 + b3}
+    # 64-token block GEMM: one 8B-dense layer at M = 64, extrapolated to the 32-layer block
+    dense = synth.dense_8b_block_specs(layers=1)
+    d4, a4, b4, n4, f4 = _oracle_gemv_sample(dense, 64, 30.0, "c4")
+    full = sum(s.nbytes for s in synth.dense_8b_block_specs())
+    out["block_gemm_8b_m64"] = {"TFLOP_s": f4 / (a4 + b4) / 1e12, "layer_s": a4 + b4,
+                                "tensors": len(n4),
+                                "block_s_extrapolated": (a4 + b4) * full / d4,
+                                "note": "one layer measured; the 32-layer figure is extrapolated by bytes"}
+    # MoE layer 0 at T = 1 and T = 64: the oracle's time, and the GPU layer output
+    # of the MoE leg against it (|y - y_ref| / (2e-3 * a), a = the layer's error scale)
+    if moe_check:
+        D, De, Ds = synth.MOE_D_MODEL, synth.MOE_D_EXPERT, synth.MOE_D_SHARED
+
+        def wt(p_, e):
+            sp = synth.moe_expert_spec(0, p_, e) if e != "shared" else synth.moe_shared_spec(0, p_)
+            return oracle.weights_exact(sp.generate(), "q4_1", sp.N, sp.K)
+        res5 = {}
+        for T, (Xb, ids, pr, Yg) in sorted(moe_check.items()):
+            t0 = time.perf_counter()
+            ye, ae = oracle.moe_layer_ref(Xb, ids, pr, lambda e: (wt("gate", e), wt("up", e), wt("down", e)),
+                                          (wt("gate", "shared"), wt("up", "shared"), wt("down", "shared")),
+                                          n_experts=synth.MOE_EXPERTS, with_scale=True)
+            dt = time.perf_counter() - t0
+            res5[f"T{T}"] = {"oracle_layer_s": dt, "oracle_48_layers_s_extrapolated": 48 * dt,
+                             "gpu_layer0_tol_ratio": oracle.tol_ratio(Yg, ye, ae)}
+        out["moe_512x10"] = res5
+    return out
 
 
 # ----------------------------------------------------------------------------
@@ -446,6 +507,9 @@ def gemm_leg(steps, warmup, graph):
 # ----------------------------------------------------------------------------
 # MoE
 # ----------------------------------------------------------------------------
+MOE_CHECK = {}   # layer 0's inputs and GPU output per T, checked against the oracle in the cpu leg
+
+
 def moe_leg(steps, warmup, graph):
     D, De, Ds, E, L = synth.MOE_D_MODEL, synth.MOE_D_EXPERT, synth.MOE_D_SHARED, synth.MOE_EXPERTS, synth.MOE_LAYERS
     gu = (De // 32) * (D // 256) * 5120
@@ -504,6 +568,8 @@ def moe_leg(steps, warmup, graph):
                 if r:
                     raise q.Q4nxError(r, q.last_error())
         ms, wall = time_calls(run, steps, warmup, graph)
+        MOE_CHECK[T] = (X[0].cpu().numpy().view(np.uint16), routes[T][0][0], routes[T][0][1],
+                        Ys[0].cpu().numpy())
         y_full = [y.clone() for y in Ys]
         # algorithmic bytes: every selected expert read once per layer, plus the shared expert
         uniq = sum(len(np.unique(routes[T][l][0])) for l in range(L))
@@ -559,36 +625,68 @@ def repack_leg(steps, warmup, graph):
     """Q4_K -> q4_1 repack of one 8B-dense gate|up-sized weight (28672 x 4096)."""
     N, K = 2 * 14336, 4096
     spec = synth.TensorSpec("gate_up", "q4_k", N, K, ("repack_q4k", 0))
-    src = to_dev(spec.generate())
-    w = q.weight(src, N, K, "q4_k")
-    out = torch.empty((N // 32) * (K // 256) * 5120, dtype=torch.uint8, device=DEV)
-    ms, _ = time_calls(lambda: q.repack_q4k_to_q41(w, out), steps, warmup, graph)
-    moved = src.numel() + out.numel()
-    return {"shape": [N, K], "bytes_read": src.numel(), "bytes_written": out.numel(), "ms": ms,
-            "GB_s_read_plus_write": moved / (ms * 1e-3) / 1e9,
-            "pct_hbm_peak": 100 * moved / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    src0 = to_dev(spec.generate())
+    out_bytes = (N // 32) * (K // 256) * 5120
+    n = n_copies(src0.numel() + out_bytes)   # source and destination pairs cycled past the cache
+    srcs = [src0] + [src0.clone() for _ in range(n - 1)]
+    ws = [q.weight(s_, N, K, "q4_k") for s_ in srcs]
+    outs = [torch.empty(out_bytes, dtype=torch.uint8, device=DEV) for _ in range(n)]
+
+    def run():
+        for w, o in zip(ws, outs):
+            q.repack_q4k_to_q41(w, o)
+    ms, _ = time_calls(run, steps, warmup, graph)
+    ms /= n
+    moved = src0.numel() + out_bytes
+    res = {"shape": [N, K], "bytes_read": src0.numel(), "bytes_written": out_bytes, "ms": ms,
+           "copies_cycled": n, "working_set_bytes": n * moved,
+           "GB_s_read_plus_write": moved / (ms * 1e-3) / 1e9,
+           "pct_hbm_peak": 100 * moved / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    del srcs, ws, outs, src0
+    torch.cuda.empty_cache()
+    return res
 
 
 def gguf_leg(steps, warmup, graph):
     """GGUF Q4_0 / Q4_1 / Q4_K -> q4_1 conversion of one 8B-dense gate|up-sized
     tensor (28672 x 4096) each: bytes read plus written per second."""
     N, K = 2 * 14336, 4096
-    out = torch.empty((N // 32) * (K // 256) * 5120, dtype=torch.uint8, device=DEV)
+    out_bytes = (N // 32) * (K // 256) * 5120
     res = {}
     for name, gtype in (("q4_0", q.GGUF_Q4_0), ("q4_1", q.GGUF_Q4_1), ("q4_k", q.GGUF_Q4_K)):
-        src = to_dev(synth.gen_gguf(synth.rng("gguf", name), gtype, N, K))
-        ms, _ = time_calls(lambda: q.gguf_to_q41(gtype, src, N, K, out), steps, warmup, graph)
-        moved = src.numel() + out.numel()
-        res[name] = {"bytes_read": src.numel(), "bytes_written": out.numel(), "ms": ms,
+        src0 = to_dev(synth.gen_gguf(synth.rng("gguf", name), gtype, N, K))
+        n = n_copies(src0.numel() + out_bytes)
+        srcs = [src0] + [src0.clone() for _ in range(n - 1)]
+        outs = [torch.empty(out_bytes, dtype=torch.uint8, device=DEV) for _ in range(n)]
+
+        def run(srcs=srcs, outs=outs, gtype=gtype):
+            for s_, o in zip(srcs, outs):
+                q.gguf_to_q41(gtype, s_, N, K, o)
+        ms, _ = time_calls(run, steps, warmup, graph)
+        ms /= n
+        moved = src0.numel() + out_bytes
+        res[name] = {"bytes_read": src0.numel(), "bytes_written": out_bytes, "ms": ms,
+                     "copies_cycled": n, "working_set_bytes": n * moved,
                      "GB_s_read_plus_write": moved / (ms * 1e-3) / 1e9,
                      "pct_hbm_peak": 100 * moved / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
-        del src
+        del srcs, outs, src0
+        torch.cuda.empty_cache()
     return {"shape": [N, K], **res}
+
+
+ROTATE_BYTES = 1100 * 1000 * 1000   # working sets past the 256 MB Infinity Cache
+
+
+def n_copies(nbytes: int) -> int:
+    """Distinct device copies of a weight so that cycling through them moves at least ROTATE_BYTES."""
+    return max(1, -(-ROTATE_BYTES // nbytes))
 
 
 def kinds_leg(steps, warmup, graph):
     """One large decode GEMV per chunk kind at the lm_head shape (151936 x 2560,
-    M = 1): q4_1, Q4_K and Q8 in both code layouts, HIP events around each call."""
+    M = 1): q4_1, Q4_K and Q8 in both code layouts, HIP events around each call.
+    Each timed run cycles through enough distinct copies of the weight (over
+    1.1 GB) that every call reads HBM, not the Infinity Cache."""
     name, N, K = synth.QWEN3_4B_LM_HEAD
     x = bf16_dev(synth.gen_x(synth.rng("kinds", "x"), 1, K))
     y = torch.empty((1, N), dtype=torch.float32, device=DEV)
@@ -602,21 +700,24 @@ def kinds_leg(steps, warmup, graph):
         ch = spec.generate()
         if lay == "B":
             ch = synth.q8_relayout(ch, "A", "B")
-        d = to_dev(ch)
+        d0 = to_dev(ch)
         del ch
-        w = q.weight(d, N, K, kind, lay)
-        calls = 10
+        calls = n_copies(d0.numel())
+        ds = [d0] + [d0.clone() for _ in range(calls - 1)]
+        ws = [q.weight(d, N, K, kind, lay) for d in ds]
 
-        def run(w=w):
-            for _ in range(calls):
+        def run(ws=ws):
+            for w in ws:
                 q.gemv(w, x, y, 1)
         ms, _ = time_calls(run, steps, warmup, graph)
         us = ms * 1e3 / calls
-        res[kind if lay is None else f"q8_{lay}"] = {"bytes": d.numel(), "us_per_call": us,
-                                                      "GB_s": d.numel() / (us * 1e-6) / 1e9,
-                                                      "pct_hbm_peak": 100 * d.numel() / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
-        del d
-    torch.cuda.empty_cache()
+        res[kind if lay is None else f"q8_{lay}"] = {"bytes": d0.numel(), "us_per_call": us,
+                                                      "copies_cycled": calls,
+                                                      "working_set_bytes": calls * d0.numel(),
+                                                      "GB_s": d0.numel() / (us * 1e-6) / 1e9,
+                                                      "pct_hbm_peak": 100 * d0.numel() / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+        del ds, ws, d0
+        torch.cuda.empty_cache()
     return res
 
 
@@ -731,7 +832,18 @@ def single_leg():
                 raise q.Q4nxError(r, q.last_error())
     msb, _ = time_calls(run_batched, 5, 2, graph=True)
     perb = msb / copies * 1e3
+    # all 2048 distinct copies in ONE launch: a plan whose single phase holds every GEMV
+    yp = torch.empty((copies, spec.N), dtype=torch.float32, device=DEV)
+    plan = q.Plan([(descs[i], x, yp[i]) for i in range(copies)], [0] * copies, 1)
+    msp, _ = time_calls(plan.run, 5, 2, graph=True)
+    if plan.errors():
+        raise RuntimeError("plan of the 2048 copies reported an error flag")
+    perp = msp / copies * 1e3
+    plan.close()
     return {"weight_bytes": spec.nbytes, "rotated_copies": copies,
+            "one_launch_2048_copies": {"launches": 1, "ms": msp, "us_per_gemv": perp,
+                                       "GB_s": spec.nbytes / (perp * 1e-6) / 1e9,
+                                       "pct_hbm_peak": 100 * spec.nbytes / (perp * 1e-6) / 1e9 / HBM_PEAK_GBS},
             "us_per_call_stream": per, "us_per_call_graph": perg,
             "GB_s_graph_rotated": spec.nbytes / (perg * 1e-6) / 1e9,
             "us_per_call_graph_hot": msh / copies * 1e3,
@@ -775,8 +887,6 @@ def main():
         legs["decode"] = res
         del step
         torch.cuda.empty_cache()
-    if "cpu" in LEGS:
-        out["cpu_baseline"] = cpu_baseline(specs)
     if "mixed" in LEGS:
         for lay in ("A", "B"):
             ms = synth.mixed_decode_specs(q8_layout=lay)
@@ -815,6 +925,8 @@ def main():
         legs["copy_1GiB"] = {"bytes_read": 1 << 30, "bytes_written": 1 << 30, "ms": ms,
                              "GB_s_read_plus_write": 2 * (1 << 30) / (ms * 1e-3) / 1e9}
         del a, b
+    if "cpu" in LEGS:
+        out["cpu_baseline"] = cpu_baseline(specs, MOE_CHECK)
     out["legs"] = legs
     print(json.dumps(out))
 
