@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libq4nx.so")
 OBJDIR = os.path.join(os.path.dirname(HERE), "_build")
-SOURCES = ["api.hip", "gemv.hip", "plan.hip", "gemm.hip", "decode.hip", "moe.hip", "router.hip"]
+SOURCES = ["api.hip", "gemv.hip", "plan.hip", "step.hip", "gemm.hip", "decode.hip", "moe.hip", "router.hip"]
 ARCH = os.environ.get("Q4NX_OFFLOAD_ARCH", "gfx950")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -12,6 +12,8 @@
 #include <algorithm>
 #include <cstring>
 #include <mutex>
+#include <queue>
+#include <tuple>
 #include <string>
 #include <vector>
 
@@ -519,7 +521,10 @@ size_t q4nx_gemm_batched_ws(const q4nx_gemm_job* jobs, int n_jobs) {
 struct q4nx_plan_s {
   struct Seg {
     int kind, grid;
+    bool step = false;   // the step kernel (static schedule) instead of the unit-dealing one
+    size_t lds = 0;
     q4nx::PlanArgs args;
+    q4nx::StepArgs sargs;
   };
   int M = 1;
   std::vector<Seg> segs;
@@ -581,6 +586,90 @@ int q4nx_plan_create(const q4nx_gemv_job* jobs, const int32_t* phase, int n_jobs
     ++sg.n_phases;
     t = e;
   }
+  int n_cu = 0;
+  {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_status(e, "plan device query");
+  }
+  // q4 segments whose activations fit the step kernel's LDS run on it
+  struct StepT {
+    bool use = false;
+    size_t lds = 0, rec = 0;
+    int ns = 0;
+    std::vector<q4nx::StepJob> sj;
+    std::vector<q4nx::StepUnit> units;
+    std::vector<int32_t> first;
+    size_t o_jobs = 0, o_units = 0, o_first = 0, o_sync = 0, o_ctl = 0;
+  };
+  std::vector<StepT> steps(segs.size());
+  for (size_t si = 0; si < segs.size(); ++si) {
+    SegH& sg = segs[si];
+    if (sg.kind != q4nx::KIND_Q4_1 && sg.kind != q4nx::KIND_Q4_K) continue;
+    int max_tc = 0;
+    for (int ji : sg.jobs) max_tc = std::max(max_tc, (int)(jobs[ji].w.cols / 256));
+    const q4nx::StepLds lds = q4nx::step_lds(M, max_tc);
+    if (lds.ns < 2) continue;
+    StepT& S = steps[si];
+    S.use = true;
+    S.lds = lds.total;
+    S.rec = lds.rec;
+    S.ns = lds.ns;
+    for (int ji : sg.jobs) {
+      const q4nx_gemv_job& j = jobs[ji];
+      S.sj.push_back({static_cast<const uint8_t*>(j.w.chunks), j.x, j.y, (int32_t)(j.w.rows / 32),
+                      (int32_t)(j.w.cols / 256), (int32_t)j.w.cols, (int32_t)j.w.rows});
+    }
+    // whole tile rows to workgroups, largest first, each to the least loaded in
+    // its phase (then overall); a workgroup's rows in (job, row) order, cut into
+    // pieces of at most kStepPieceCols chunk columns
+    const int cap = q4nx::kStepPieceCols;
+    std::vector<std::vector<q4nx::StepUnit>> per(n_cu);
+    std::vector<long long> total(n_cu, 0);
+    for (int ph = 0; ph < sg.n_phases; ++ph) {
+      struct Row { int cost, job, tr; };
+      std::vector<Row> rows;
+      for (size_t i = 0; i < sg.jobs.size(); ++i)
+        if (sg.phase_of[i] == ph)
+          for (int tr = 0; tr < S.sj[i].TR; ++tr) rows.push_back({S.sj[i].TC, (int)i, tr});
+      std::stable_sort(rows.begin(), rows.end(), [](const Row& a, const Row& b) { return a.cost > b.cost; });
+      typedef std::tuple<long long, long long, int> Key;
+      std::priority_queue<Key, std::vector<Key>, std::greater<Key>> heap;
+      for (int b = 0; b < n_cu; ++b) heap.push(Key(0, total[b], b));
+      std::vector<std::vector<Row>> mine(n_cu);
+      for (const Row& r : rows) {
+        Key k = heap.top();
+        heap.pop();
+        const int b = std::get<2>(k);
+        mine[b].push_back(r);
+        total[b] += r.cost;
+        heap.push(Key(std::get<0>(k) + r.cost, total[b], b));
+      }
+      for (int b = 0; b < n_cu; ++b) {
+        std::sort(mine[b].begin(), mine[b].end(),
+                  [](const Row& a, const Row& c) { return a.job != c.job ? a.job < c.job : a.tr < c.tr; });
+        for (const Row& r : mine[b]) {
+          const int TC = S.sj[r.job].TC, n_sub = (TC + cap - 1) / cap;
+          for (int t = 0; t < n_sub; ++t) {
+            q4nx::StepUnit u;
+            u.job = r.job;
+            u.tr = r.tr;
+            u.c0 = (int16_t)(t * TC / n_sub);
+            u.c1 = (int16_t)((t + 1) * TC / n_sub);
+            u.phase = (int16_t)ph;
+            u.flags = (int16_t)((t == 0 ? q4nx::kStepFirst : 0) | (t == n_sub - 1 ? q4nx::kStepLast : 0));
+            per[b].push_back(u);
+          }
+        }
+      }
+    }
+    S.first.push_back(0);
+    for (int b = 0; b < n_cu; ++b) {
+      S.units.insert(S.units.end(), per[b].begin(), per[b].end());
+      S.first.push_back((int32_t)S.units.size());
+    }
+  }
   // host tables and device layout
   struct SegT {
     std::vector<q4nx::PlanJob> pj;
@@ -628,6 +717,14 @@ int q4nx_plan_create(const q4nx_gemv_job* jobs, const int32_t* phase, int n_jobs
     T.o_cnt = total;   total = align256(total + (size_t)std::max(T.n_slots, 1) * 4);
     T.o_part = total;  total = align256(total + (size_t)T.n_slots * T.smax * 32 * M * 4);
     T.o_ctl = total;   total = align256(total + 16);
+    StepT& S = steps[si];
+    if (S.use) {
+      S.o_jobs = total;  total = align256(total + S.sj.size() * sizeof(q4nx::StepJob));
+      S.o_units = total; total = align256(total + S.units.size() * sizeof(q4nx::StepUnit));
+      S.o_first = total; total = align256(total + S.first.size() * 4);
+      S.o_sync = total;  total = align256(total + q4nx::step_sync_words(segs[si].n_phases) * 4);
+      S.o_ctl = total;   total = align256(total + 16);
+    }
   }
   // check every kernel can be resident before allocating anything
   std::vector<int> grids(segs.size());
@@ -647,6 +744,12 @@ int q4nx_plan_create(const q4nx_gemv_job* jobs, const int32_t* phase, int n_jobs
     memcpy(host.data() + T.o_jobs, T.pj.data(), T.pj.size() * sizeof(q4nx::PlanJob));
     memcpy(host.data() + T.o_unit, T.unit_job.data(), T.unit_job.size() * 4);
     memcpy(host.data() + T.o_need, T.need.data(), T.need.size() * 4);
+    const StepT& S = steps[si];
+    if (S.use) {
+      memcpy(host.data() + S.o_jobs, S.sj.data(), S.sj.size() * sizeof(q4nx::StepJob));
+      memcpy(host.data() + S.o_units, S.units.data(), S.units.size() * sizeof(q4nx::StepUnit));
+      memcpy(host.data() + S.o_first, S.first.data(), S.first.size() * 4);
+    }
   }
   e = hipMemcpy(dev, host.data(), total, hipMemcpyHostToDevice);
   if (e != hipSuccess) {
@@ -674,6 +777,22 @@ int q4nx_plan_create(const q4nx_gemv_job* jobs, const int32_t* phase, int n_jobs
     s.args.n_phases = segs[si].n_phases;
     s.args.spin_limit = kPlanSpinLimit;
     s.args.smax = T.smax;
+    const StepT& S = steps[si];
+    if (S.use) {
+      s.step = true;
+      s.grid = n_cu;
+      s.lds = S.lds;
+      s.sargs.jobs = reinterpret_cast<const q4nx::StepJob*>(d + S.o_jobs);
+      s.sargs.units = reinterpret_cast<const q4nx::StepUnit*>(d + S.o_units);
+      s.sargs.wg_first = reinterpret_cast<const int32_t*>(d + S.o_first);
+      s.sargs.sync = reinterpret_cast<uint32_t*>(d + S.o_sync);
+      s.sargs.ctl = reinterpret_cast<uint32_t*>(d + S.o_ctl);
+      s.sargs.n_phases = segs[si].n_phases;
+      s.sargs.spin_limit = kPlanSpinLimit;
+      s.sargs.ring_off = (int32_t)S.rec;
+      s.sargs.ns = S.ns;
+      s.args.ctl = s.sargs.ctl;
+    }
     plan->segs.push_back(s);
     plan->ctl.push_back(s.args.ctl);
   }
@@ -684,8 +803,10 @@ int q4nx_plan_create(const q4nx_gemv_job* jobs, const int32_t* phase, int n_jobs
 int q4nx_plan_run(q4nx_plan plan, void* stream) {
   if (!plan) return fail(Q4NX_E_ARG, "plan_run: null plan");
   for (const auto& s : plan->segs) {
-    const hipError_t e = q4nx::launch_plan(s.kind, plan->M, s.args, s.grid,
-                                           static_cast<hipStream_t>(stream));
+    const hipError_t e = s.step ? q4nx::launch_step(s.kind, plan->M, s.sargs, s.grid, s.lds,
+                                                    static_cast<hipStream_t>(stream))
+                                : q4nx::launch_plan(s.kind, plan->M, s.args, s.grid,
+                                                    static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_status(e, "plan launch");
   }
   return ok();

@@ -144,9 +144,13 @@ int q4nx_gemv_batched(const q4nx_gemv_job* jobs, int n_jobs, int M, void* stream
  * each short kernel pays its own start and drain and the weight stream stalls
  * between them (Strata article, section 3.2, runs its whole 48-layer pass as
  * one captured graph for this reason).  A plan runs every job of phase p only
- * after every job of phase p-1 has written its y, but issues each unit's
- * weight loads before that wait, so weight streaming continues across the
- * phase boundaries.
+ * after every job of phase p-1 has written its y, but issues the weight loads
+ * of the next phase before that wait, so weight streaming continues across the
+ * phase boundaries.  (q4_1 and Q4_K runs whose activations fit in LDS use one
+ * workgroup per CU with a static schedule; other runs, and Q8, deal units of
+ * one tile row to a resident grid.  On MI355X a device-wide hand-off costs
+ * more than a kernel boundary, so for a decode step the same phases captured
+ * as separate q4nx_gemv_batched launches in a HIP graph are faster.)
  *
  *   jobs    HOST array of n_jobs GEMVs (copied into the plan; the weights, x
  *           and y they point at must stay allocated while the plan is used)
