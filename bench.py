@@ -42,10 +42,14 @@ def log(*a):
 # Kernel sources whose rocprofv3 counter summary (under profiles/) stays valid
 # while they are unchanged.
 KERNEL_SOURCES = {
-    "k_gemv_q4": ["gemv.hip", "gemv_core.h", "q4nx_dev.h"],
+    "k_gemv_q4": ["gemv.hip", "gemv_core.h", "q4nx_dev.h", "topk.h"],
+    "k_gemv_q8": ["gemv.hip", "gemv_core.h", "q4nx_dev.h", "topk.h"],
     "k_gemm_q4": ["gemm.hip", "gemm_args.h", "q4nx_dev.h"],
+    "k_moe": ["moe.hip", "moe_args.h", "gemv_core.h", "q4nx_dev.h"],
+    "k_router": ["router.hip", "q4nx_dev.h"],
+    "k_step": ["step.hip", "plan_args.h", "gemv_core.h", "q4nx_dev.h"],
 }
-PROFILE_FILES = {
+PROFILE_FILES = {   # the summaries whose FETCH/WRITE figures feed a roofline's "traffic"
     "k_gemv_q4": "k_gemv_q4__qwen3_4b_decode_step.md",
     "k_gemm_q4": "k_gemm_q4__dense_8b_block_m64.md",
 }
@@ -76,7 +80,7 @@ def profiled_traffic(kernel: str):
     return float(vals["traffic_bytes_per_launch"])
 
 
-def summarize(trace_db, fetch_db, write_db, kernel, title, commands):
+def summarize(trace_db, fetch_db, write_db, kernel, title, commands, counters_db=None):
     """Markdown summary of rocprofv3 results (kernel trace + FETCH_SIZE / WRITE_SIZE
     passes) for one kernel family; the counters are scaled by what they read for
     the 1 GiB copy of the copyref leg."""
@@ -128,8 +132,23 @@ def summarize(trace_db, fetch_db, write_db, kernel, title, commands):
         tf += vf; nf += cf; tw += vw; nw += cw
     per_launch = (tf / nf * sf + tw / nw * sw) * 1024
     out += ["", f"Scaled HBM bytes per {kernel} dispatch (fetch + write, averaged over "
-                f"{nf} dispatches): {per_launch / 1e6:.3f} MB", "",
-            f"traffic_bytes_per_launch: {per_launch:.0f}",
+                f"{nf} dispatches): {per_launch / 1e6:.3f} MB"]
+    if counters_db:
+        c = sqlite3.connect(counters_db)
+        rows = c.execute("select kernel_name, grid_size_x, counter_name, value from counters_collection").fetchall()
+        names = sorted({r[2] for r in rows})
+        acc = defaultdict(lambda: defaultdict(list))
+        for n, g, cn, v in rows:
+            if kernel in n:
+                acc[(n, g)][cn].append(v)
+        out += ["", "## Other counters (one --pmc pass; average per dispatch)", "",
+                "| kernel | grid (threads) | dispatches | " + " | ".join(names) + " |",
+                "|---|---:|---:|" + "---:|" * len(names)]
+        for (n, g), d in sorted(acc.items(), key=lambda kv: -len(next(iter(kv[1].values())))):
+            cnt = max(len(v) for v in d.values())
+            out.append(f"| `{n[:60]}` | {g} | {cnt} | " +
+                       " | ".join(f"{sum(d[cn]) / len(d[cn]):.4g}" if d.get(cn) else "" for cn in names) + " |")
+    out += ["", f"traffic_bytes_per_launch: {per_launch:.0f}",
             f"source_sha1: `{source_sha1(kernel)}`"]
     return "\n".join(out) + "\n"
 
@@ -141,6 +160,7 @@ def parse():
     ap.add_argument("--kernel", default="k_gemv_q4", choices=sorted(KERNEL_SOURCES))
     ap.add_argument("--title", default="")
     ap.add_argument("--commands", default="", help="the rocprofv3 commands, separated by ';'")
+    ap.add_argument("--counters", default=None, help="a further --pmc results database to tabulate")
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
@@ -154,7 +174,7 @@ def parse():
 args = parse()
 if args.summarize:
     print(summarize(*args.summarize, args.kernel, args.title,
-                    [c.strip() for c in args.commands.split(";") if c.strip()]), end="")
+                    [c.strip() for c in args.commands.split(";") if c.strip()], args.counters), end="")
     sys.exit(0)
 if args.gpus != 1:
     print(json.dumps({"error": "one GPU only: the library has no multi-GPU path; --gpus must be 1",
