@@ -333,7 +333,10 @@ def decode_leg(specs, tag, steps, warmup, graph, M=1):
     step = DecodeStep(specs, tag, M)
     ms, wall = time_calls(step.run, steps, warmup, graph)
     gbs = step.bytes / (ms * 1e-3) / 1e9
-    msp, _ = time_calls(step.plan.run, steps, warmup, graph)
+    msp, _ = time_calls(step.plan.run, steps, warmup, graph)          # mode 0: one launch per phase
+    step.plan.set_mode(1)
+    msp1, _ = time_calls(step.plan.run, steps, warmup, graph)         # mode 1: persistent launches
+    step.plan.set_mode(0)
     errs = step.plan.errors()
     if errs:
         raise RuntimeError(f"plan reported error flags {errs}")
@@ -341,7 +344,9 @@ def decode_leg(specs, tag, steps, warmup, graph, M=1):
            "GB_s": gbs, "pct_hbm_peak": 100 * gbs / HBM_PEAK_GBS,
            "launches": len(step.calls), "graph": graph,
            "plan": {"ms_per_step": msp, "GB_s": step.bytes / (msp * 1e-3) / 1e9,
-                    "launches": 1 + sum(1 for a, b in zip(specs, specs[1:]) if a.kind != b.kind),
+                    "launches": max(step.plan_phases) + 1, "mode": "one launch per phase (device job tables)",
+                    "persistent": {"ms_per_step": msp1, "GB_s": step.bytes / (msp1 * 1e-3) / 1e9,
+                                   "launches": 1 + sum(1 for a, b in zip(specs, specs[1:]) if a.kind != b.kind)},
                     "phases": max(step.plan_phases) + 1, "device_bytes": step.plan.nbytes()}}
     return step, res
 

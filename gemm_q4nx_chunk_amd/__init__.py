@@ -79,6 +79,7 @@ _lib.q4nx_gemv_batched.argtypes = [ctypes.POINTER(GemvJob), _I, _I, _P]
 _lib.q4nx_gemm_block.argtypes = [ctypes.POINTER(Weight), _P, _P, _I, _P, ctypes.c_size_t, _P]
 _lib.q4nx_gemm_block_ws.argtypes = [ctypes.POINTER(Weight)]
 _lib.q4nx_gemm_block_ws.restype = ctypes.c_size_t
+_lib.q4nx_plan_set_mode.argtypes = [_P, _I]
 _lib.q4nx_gemm_block_noalloc.argtypes = [ctypes.POINTER(Weight), _P, _P, _I, _P]
 _lib.q4nx_gemm_block_noalloc_max.argtypes = []
 _lib.q4nx_gemm_block_noalloc_max.restype = ctypes.c_size_t
@@ -121,7 +122,8 @@ _lib.q4nx_last_error.restype = ctypes.c_char_p
 for _f in ("q4nx_weight_check", "q4nx_gemv", "q4nx_gemv_batched", "q4nx_gemm_block", "q4nx_gemm_batched",
            "q4nx_moe_experts", "q4nx_unpack", "q4nx_decode", "q4nx_repack_q4k_to_q41", "q4nx_gguf_to_q41", "q4nx_q8_rows", "q4nx_argmax", "q4nx_moe_router", "q4nx_version", "q4nx_plan_create",
            "q4nx_plan_run", "q4nx_plan_errors", "q4nx_gemm_exchange_mode", "q4nx_gemv_topk",
-           "q4nx_chunk_layout_default", "q4nx_chunk_layout_check", "q4nx_relayout"):
+           "q4nx_chunk_layout_default", "q4nx_chunk_layout_check", "q4nx_relayout", "q4nx_plan_set_mode",
+           "q4nx_gemm_block_noalloc"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -221,6 +223,10 @@ class Plan:
 
     def run(self, stream=None) -> None:
         _check(_lib.q4nx_plan_run(self.handle, _stream(stream)))
+
+    def set_mode(self, mode: int) -> None:
+        """0: one launch per phase (default); 1: persistent launches."""
+        _check(_lib.q4nx_plan_set_mode(self.handle, mode))
 
     def errors(self) -> int:
         f = ctypes.c_uint32()

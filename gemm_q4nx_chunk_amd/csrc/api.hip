@@ -127,6 +127,36 @@ int pick_ks(int waves, int64_t total_tr, int TC) {
   return ks < lim ? ks : lim;
 }
 
+// Launch shape of one kind's jobs (all valid, same M) in one launch.
+struct BatchShape {
+  int waves, xl, parts;   // parts: units per tile row
+};
+
+BatchShape batch_shape(int kind, int64_t total_tr, int max_tc, int M) {
+  BatchShape sh;
+  sh.waves = pick_waves(total_tr, M, max_tc);
+  sh.xl = q4nx::gemv_xl_bytes(kind, M, sh.waves, max_tc);
+  const bool q4 = kind == q4nx::KIND_Q4_1 || kind == q4nx::KIND_Q4_K;
+  sh.parts = !(q4 && sh.xl > 0) ? 1 : total_tr <= Q4NX_ROWSPLIT4_TR ? 4 : total_tr <= Q4NX_ROWSPLIT_TR ? 2 : 1;
+  return sh;
+}
+
+// Fills the kernel's job record of j, its workgroups starting at wg_begin;
+// returns its workgroup count.
+int fill_job(q4nx::GemvJob& g, const q4nx_gemv_job* j, const BatchShape& sh, int64_t total_tr, int wg_begin) {
+  g.w = static_cast<const uint8_t*>(j->w.chunks);
+  g.x = j->x;
+  g.y = j->y;
+  g.TR = j->w.rows / 32;
+  g.TC = j->w.cols / 256;
+  g.ldx = j->w.cols;
+  g.ldy = j->w.rows;
+  g.ks = pick_ks(sh.waves, total_tr, g.TC);
+  g.wg_begin = wg_begin;
+  const int rpw = sh.waves / g.ks;
+  return (g.TR * sh.parts + rpw - 1) / rpw;
+}
+
 // Launch one kind's jobs (all valid, same M) in as few launches as the job
 // table allows.
 int run_batch(int kind, const q4nx_gemv_job* const* jobs, int n, int M, hipStream_t s) {
@@ -136,34 +166,16 @@ int run_batch(int kind, const q4nx_gemv_job* const* jobs, int n, int M, hipStrea
     total_tr += jobs[i]->w.rows / 32;
     max_tc = std::max(max_tc, jobs[i]->w.cols / 256);
   }
-  const int waves = pick_waves(total_tr, M, max_tc);
-  const int xl = q4nx::gemv_xl_bytes(kind, M, waves, max_tc);
-  const bool q4 = kind == q4nx::KIND_Q4_1 || kind == q4nx::KIND_Q4_K;
-  const int parts = !(q4 && xl > 0) ? 1                                     // units per tile row
-                    : total_tr <= Q4NX_ROWSPLIT4_TR ? 4 : total_tr <= Q4NX_ROWSPLIT_TR ? 2 : 1;
+  const BatchShape sh = batch_shape(kind, total_tr, max_tc, M);
   for (int i0 = 0; i0 < n; i0 += q4nx::kMaxBatch) {
     const int cnt = n - i0 < q4nx::kMaxBatch ? n - i0 : q4nx::kMaxBatch;
     q4nx::GemvBatch b;
     memset(&b, 0, sizeof b);
-    b.sl = 4 / parts;
+    b.sl = 4 / sh.parts;
     int wg = 0;
-    for (int t = 0; t < cnt; ++t) {
-      const q4nx_gemv_job* j = jobs[i0 + t];
-      q4nx::GemvJob& g = b.job[t];
-      g.w = static_cast<const uint8_t*>(j->w.chunks);
-      g.x = j->x;
-      g.y = j->y;
-      g.TR = j->w.rows / 32;
-      g.TC = j->w.cols / 256;
-      g.ldx = j->w.cols;
-      g.ldy = j->w.rows;
-      g.ks = pick_ks(waves, total_tr, g.TC);
-      g.wg_begin = wg;
-      const int rpw = waves / g.ks;
-      wg += (g.TR * parts + rpw - 1) / rpw;
-    }
+    for (int t = 0; t < cnt; ++t) wg += fill_job(b.job[t], jobs[i0 + t], sh, total_tr, wg);
     b.n_jobs = cnt;
-    const hipError_t e = q4nx::launch_gemv(kind, M, waves, b, wg, xl, s);
+    const hipError_t e = q4nx::launch_gemv(kind, M, sh.waves, b, wg, sh.xl, s);
     if (e != hipSuccess) return hip_status(e, "gemv launch");
   }
   return Q4NX_OK;
@@ -527,7 +539,13 @@ struct q4nx_plan_s {
     q4nx::StepArgs sargs;
   };
   int M = 1;
+  int mode = 0;          // 0: one GEMV launch per phase; 1: one persistent launch per segment
   std::vector<Seg> segs;
+  struct Phase {         // mode 0: one batched GEMV launch over a device job table
+    int kind, waves, xl, n_wg;
+    q4nx::GemvBatch b;
+  };
+  std::vector<Phase> phases;
   void* dev = nullptr;
   size_t bytes = 0;
   std::vector<uint32_t*> ctl;   // per segment control words (device)
@@ -670,6 +688,43 @@ int q4nx_plan_create(const q4nx_gemv_job* jobs, const int32_t* phase, int n_jobs
       S.first.push_back((int32_t)S.units.size());
     }
   }
+  // mode 0: every phase as one batched GEMV launch whose jobs come from a
+  // device table (no limit on their number), shaped as q4nx_gemv_batched
+  // shapes one kind's jobs
+  struct PhaseT {
+    int kind;
+    BatchShape sh;
+    int n_wg;
+    std::vector<q4nx::GemvJob> jobs;
+    std::vector<int32_t> wg_job;
+    size_t o_jobs = 0, o_wg = 0;
+  };
+  std::vector<PhaseT> pts;
+  for (size_t t = 0; t < order.size();) {
+    const int ph = phase[order[t]];
+    size_t e = t;
+    int64_t total_tr = 0;
+    int max_tc = 0;
+    while (e < order.size() && phase[order[e]] == ph) {
+      total_tr += jobs[order[e]].w.rows / 32;
+      max_tc = std::max(max_tc, jobs[order[e]].w.cols / 256);
+      ++e;
+    }
+    PhaseT P;
+    P.kind = kind_of(&jobs[order[t]].w);
+    P.sh = batch_shape(P.kind, total_tr, max_tc, M);
+    int wg = 0;
+    for (size_t i = t; i < e; ++i) {
+      q4nx::GemvJob g;
+      const int n = fill_job(g, &jobs[order[i]], P.sh, total_tr, wg);
+      for (int b = 0; b < n; ++b) P.wg_job.push_back((int32_t)P.jobs.size());
+      P.jobs.push_back(g);
+      wg += n;
+    }
+    P.n_wg = wg;
+    pts.push_back(std::move(P));
+    t = e;
+  }
   // host tables and device layout
   struct SegT {
     std::vector<q4nx::PlanJob> pj;
@@ -726,6 +781,10 @@ int q4nx_plan_create(const q4nx_gemv_job* jobs, const int32_t* phase, int n_jobs
       S.o_ctl = total;   total = align256(total + 16);
     }
   }
+  for (PhaseT& P : pts) {
+    P.o_jobs = total; total = align256(total + P.jobs.size() * sizeof(q4nx::GemvJob));
+    P.o_wg = total;   total = align256(total + P.wg_job.size() * 4);
+  }
   // check every kernel can be resident before allocating anything
   std::vector<int> grids(segs.size());
   for (size_t si = 0; si < segs.size(); ++si) {
@@ -750,6 +809,10 @@ int q4nx_plan_create(const q4nx_gemv_job* jobs, const int32_t* phase, int n_jobs
       memcpy(host.data() + S.o_units, S.units.data(), S.units.size() * sizeof(q4nx::StepUnit));
       memcpy(host.data() + S.o_first, S.first.data(), S.first.size() * 4);
     }
+  }
+  for (const PhaseT& P : pts) {
+    memcpy(host.data() + P.o_jobs, P.jobs.data(), P.jobs.size() * sizeof(q4nx::GemvJob));
+    memcpy(host.data() + P.o_wg, P.wg_job.data(), P.wg_job.size() * 4);
   }
   e = hipMemcpy(dev, host.data(), total, hipMemcpyHostToDevice);
   if (e != hipSuccess) {
@@ -796,12 +859,39 @@ int q4nx_plan_create(const q4nx_gemv_job* jobs, const int32_t* phase, int n_jobs
     plan->segs.push_back(s);
     plan->ctl.push_back(s.args.ctl);
   }
+  for (const PhaseT& P : pts) {
+    q4nx_plan_s::Phase ph;
+    ph.kind = P.kind;
+    ph.waves = P.sh.waves;
+    ph.xl = P.sh.xl;
+    ph.n_wg = P.n_wg;
+    memset(&ph.b, 0, sizeof ph.b);
+    ph.b.sl = 4 / P.sh.parts;
+    ph.b.tab = reinterpret_cast<const q4nx::GemvJob*>(d + P.o_jobs);
+    ph.b.tab_wg = reinterpret_cast<const int32_t*>(d + P.o_wg);
+    plan->phases.push_back(ph);
+  }
   *out = plan;
+  return ok();
+}
+
+int q4nx_plan_set_mode(q4nx_plan plan, int mode) {
+  if (!plan) return fail(Q4NX_E_ARG, "plan_set_mode: null plan");
+  if (mode != 0 && mode != 1) return fail(Q4NX_E_ARG, "plan_set_mode: mode %d is neither 0 nor 1", mode);
+  plan->mode = mode;
   return ok();
 }
 
 int q4nx_plan_run(q4nx_plan plan, void* stream) {
   if (!plan) return fail(Q4NX_E_ARG, "plan_run: null plan");
+  if (plan->mode == 0) {
+    for (const auto& ph : plan->phases) {
+      const hipError_t e = q4nx::launch_gemv(ph.kind, plan->M, ph.waves, ph.b, ph.n_wg, ph.xl,
+                                             static_cast<hipStream_t>(stream));
+      if (e != hipSuccess) return hip_status(e, "plan phase launch");
+    }
+    return ok();
+  }
   for (const auto& s : plan->segs) {
     const hipError_t e = s.step ? q4nx::launch_step(s.kind, plan->M, s.sargs, s.grid, s.lds,
                                                     static_cast<hipStream_t>(stream))

@@ -24,7 +24,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_q4(const GemvBatch b) {
   constexpr int CB = ChunkBytes<KIND>::value;
   constexpr int D = WAVES == 4 ? Q4Depth<M>::value : (M == 1 ? 2 : 1);
   __shared__ float red[WAVES][32][M];
-  const GemvJob& J = b.job[find_job(b, blockIdx.x)];
+  const GemvJob J = gemv_job(b);
   const int ks = J.ks, rpw = WAVES / ks;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int slot = wave / ks, part = wave % ks;
@@ -96,7 +96,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_q4x(const GemvBatch b) {
   __shared__ float red[WAVES][UR][M];
   constexpr bool kTurn = KIND == KIND_Q4_K;   // Q4_K metadata through an LDS slot per wave
   __shared__ __attribute__((aligned(16))) uint8_t tsl[kTurn ? WAVES : 1][kTurn ? 160 * SL : 16];
-  const GemvJob& J = b.job[find_job(b, blockIdx.x)];
+  const GemvJob J = gemv_job(b);
   const int ks = J.ks, rpw = WAVES / ks;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -328,7 +328,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_q8x(const GemvBatch b) {
   extern __shared__ __attribute__((aligned(16))) uint32_t xl[];
   __shared__ __attribute__((aligned(16))) uint16_t dsl[WAVES][8 * 32];
   __shared__ float red[WAVES][32][M];
-  const GemvJob& J = b.job[find_job(b, blockIdx.x)];
+  const GemvJob J = gemv_job(b);
   const int ks = J.ks, rpw = WAVES / ks;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -468,7 +468,7 @@ template <int KIND, int M, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void k_gemv_q8(const GemvBatch b) {
   constexpr int CB = 8704;
   __shared__ float red[WAVES][32][M];
-  const GemvJob& J = b.job[find_job(b, blockIdx.x)];
+  const GemvJob J = gemv_job(b);
   const int ks = J.ks, rpw = WAVES / ks;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int slot = wave / ks, part_id = wave % ks;

@@ -59,6 +59,10 @@ struct TopkArgs {
 
 struct GemvBatch {
   GemvJob job[kMaxBatch];
+  // Or, when tab is set, the jobs come from device memory (any number of
+  // them): workgroup b runs job tab[tab_wg[b]], and job[] / n_jobs are unused.
+  const GemvJob* tab;
+  const int32_t* tab_wg;
   int32_t n_jobs;
   // chunk slices per unit of work: 4 (a unit is a tile row), or 2 (a unit is
   // 16 rows of a tile; q4 kinds with prepared activations only).  The jobs'
@@ -114,12 +118,33 @@ __device__ __forceinline__ float ld_coherent(const float* p) {
 // for sc1 stores), and keep the compiler from moving memory operations across.
 __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Tables that never change during a launch, read through the constant address
+// space so the loads are scalar and never wait behind vector memory traffic.
+template <typename T>
+__device__ __forceinline__ T ld_const(const T* p, int i) {
+  static_assert(sizeof(T) % 4 == 0, "whole words");
+  typedef const __attribute__((address_space(4))) uint32_t* cword;
+  const cword q = (cword)(p + i);
+  uint32_t w[sizeof(T) / 4];
+#pragma unroll
+  for (unsigned j = 0; j < sizeof(T) / 4; ++j) w[j] = q[j];
+  T v;
+  __builtin_memcpy(&v, w, sizeof(T));
+  return v;
+}
+
 // Pick the job of workgroup `wg`: the last one whose wg_begin <= wg.
 __device__ __forceinline__ int find_job(const GemvBatch& b, int wg) {
   int j = 0;
   for (int t = 1; t < b.n_jobs; ++t)
     if (wg >= b.job[t].wg_begin) j = t;
   return j;
+}
+
+// The job of this workgroup, from the kernel arguments or the device table.
+__device__ __forceinline__ GemvJob gemv_job(const GemvBatch& b) {
+  if (b.tab) return ld_const(b.tab, ld_const(b.tab_wg, (int)blockIdx.x));
+  return b.job[find_job(b, blockIdx.x)];
 }
 
 // Host-side launchers (gemv.hip, gemm.hip, decode.hip, moe.hip).

@@ -85,22 +85,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* p, ui
   return make_rsrc(reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo), __builtin_amdgcn_readfirstlane(n));
 }
 
-// The schedule tables never change during a launch: read them through the
-// constant address space, so the loads are scalar and never wait behind the
-// weight stream.
-template <typename T>
-__device__ __forceinline__ T ld_const(const T* p, int i) {
-  static_assert(sizeof(T) % 4 == 0, "whole words");
-  typedef const __attribute__((address_space(4))) uint32_t* cword;
-  const cword q = (cword)(p + i);
-  uint32_t w[sizeof(T) / 4];
-#pragma unroll
-  for (unsigned j = 0; j < sizeof(T) / 4; ++j) w[j] = q[j];
-  T v;
-  __builtin_memcpy(&v, w, sizeof(T));
-  return v;
-}
-
 // Device-scope store through a global-space pointer (a global store, which the
 // compiler does not hold back behind this wave's earlier memory operations).
 __device__ __forceinline__ void st_agent(float* p, float v) {

@@ -137,20 +137,27 @@ typedef struct q4nx_gemv_job {
 int q4nx_gemv_batched(const q4nx_gemv_job* jobs, int n_jobs, int M, void* stream);
 
 /*
- * A GEMV plan: a whole decode step in one launch (per chunk kind present).
+ * A GEMV plan: a whole decode step's GEMVs, prepared once, run many times.
  *
  * A decode step is a chain of GEMV groups that depend on each other (per
- * layer q|k|v, o, gate|up, down, then the lm_head); run as separate launches,
- * each short kernel pays its own start and drain and the weight stream stalls
- * between them (Strata article, section 3.2, runs its whole 48-layer pass as
- * one captured graph for this reason).  A plan runs every job of phase p only
- * after every job of phase p-1 has written its y, but issues the weight loads
- * of the next phase before that wait, so weight streaming continues across the
- * phase boundaries.  (q4_1 and Q4_K runs whose activations fit in LDS use one
- * workgroup per CU with a static schedule; other runs, and Q8, deal units of
- * one tile row to a resident grid.  On MI355X a device-wide hand-off costs
- * more than a kernel boundary, so for a decode step the same phases captured
- * as separate q4nx_gemv_batched launches in a HIP graph are faster.)
+ * layer q|k|v, o, gate|up, down, then the lm_head); the Strata article
+ * (section 3.2) runs its whole pass as one captured graph so that no step
+ * waits on the host.  A plan holds the step's job tables on the device and
+ * runs every job of phase p only after every job of phase p-1 has written its
+ * y.  Two ways to run it (q4nx_plan_set_mode):
+ *   0 (default)  one batched GEMV launch per phase, its jobs read from the
+ *                plan's device table (so a phase may hold any number of jobs:
+ *                thousands of independent GEMVs go in one launch), each launch
+ *                shaped as q4nx_gemv_batched shapes it.  Stream order makes
+ *                the phases wait for each other.
+ *   1            one persistent launch per run of same-kind phases: the
+ *                workgroups wait for each other on the device, and the weight
+ *                loads of phase p + 1 are issued before that wait.  (q4_1 and
+ *                Q4_K runs whose activations fit in LDS use one workgroup per
+ *                CU with a static schedule; other runs and Q8 deal tile rows
+ *                to a resident grid.)  On MI355X a device-wide hand-off costs
+ *                more than a kernel boundary, so mode 0 is the faster one for
+ *                a decode step.
  *
  *   jobs    HOST array of n_jobs GEMVs (copied into the plan; the weights, x
  *           and y they point at must stay allocated while the plan is used)
@@ -160,18 +167,20 @@ int q4nx_gemv_batched(const q4nx_gemv_job* jobs, int n_jobs, int M, void* stream
  *   out     receives the plan handle
  * q4nx_plan_create allocates the plan's device tables (hipMalloc) and copies
  * them (synchronously); it is the only allocating call of the library.
- * q4nx_plan_run enqueues one persistent launch per run of same-kind phases;
- * it allocates nothing and may be captured in a HIP graph.  Runs of one plan
- * must not overlap each other, and the launch assumes the whole GPU: it sizes
- * its grid to stay resident.  If a phase wait ever exceeds its spin limit (a
- * grid that could not become resident), the kernel sets an error flag instead
- * of hanging; q4nx_plan_errors reads and clears it (synchronous).
+ * q4nx_plan_run enqueues the plan's launches on `stream`; it allocates
+ * nothing and may be captured in a HIP graph.  Runs of one plan must not
+ * overlap each other.  In mode 1 a launch assumes the whole GPU (it sizes its
+ * grid to stay resident); if a wait ever exceeds its spin limit (a grid that
+ * could not become resident), the kernel sets an error flag instead of
+ * hanging; q4nx_plan_errors reads and clears it (synchronous).
  */
 typedef struct q4nx_plan_s* q4nx_plan;
 
 int q4nx_plan_create(const q4nx_gemv_job* jobs, const int32_t* phase, int n_jobs, int M,
                      q4nx_plan* out);
 int q4nx_plan_run(q4nx_plan plan, void* stream);
+/* mode 0: one launch per phase (default); 1: persistent launches.  E_ARG otherwise. */
+int q4nx_plan_set_mode(q4nx_plan plan, int mode);
 /* flags: bit 0 = a phase wait timed out.  Returns Q4NX_OK or Q4NX_E_HIP. */
 int q4nx_plan_errors(q4nx_plan plan, uint32_t* flags);
 /* Device bytes the plan holds (tables, counters, partial rows). */

@@ -259,6 +259,7 @@ def test_plan_create_checks(q):
     assert create([good, (_w(q, kind=77, nbytes=10 ** 6), 0x2000, 0x3000)], [0, 1])[0] == q.E_CHUNK_KIND
     assert lib.q4nx_plan_create(None, None, 0, 1, None) == q.E_ARG
     assert lib.q4nx_plan_run(None, None) == q.E_ARG
+    assert lib.q4nx_plan_set_mode(None, 0) == q.E_ARG
     assert q.lib().q4nx_plan_bytes(None) == 0
     lib.q4nx_plan_destroy(None)
 

@@ -1,9 +1,11 @@
 """GEMV plans (q4nx_plan_*): a decode step's dependent phases in one launch.
 
-Checked: every output against the float64 oracle; a real dependency (phase 1
-reads, as its activations, the bytes phase 0 writes); repeated runs and HIP
-graph replays (the counters reset themselves); several chunk kinds; no wait
-ever times out.
+Checked in both modes (0: one launch per phase over the plan's device job
+table; 1: persistent launches): every output against the float64 oracle; a
+real dependency (phase 1 reads, as its activations, the bytes phase 0 writes);
+repeated runs and HIP graph replays (the counters reset themselves); several
+chunk kinds; no wait ever times out; a phase of more jobs than one batched
+call takes, in one launch.
 """
 import numpy as np
 import pytest
@@ -46,13 +48,15 @@ class Job:
         return y
 
 
+@pytest.mark.parametrize("mode", [0, 1])
 @pytest.mark.parametrize("M", [1, 2, 4])
-def test_plan_matches_oracle_and_repeats(M):
+def test_plan_matches_oracle_and_repeats(M, mode):
     jobs = [Job("q4_1", 4096, 2560, "q", M), Job("q4_1", 1024, 2560, "k", M),
             Job("q4_1", 2560, 4096, "o", M), Job("q4_1", 1920, 9728, "down", M),
             Job("q4_1", 32, 256, "tiny", M), Job("q4_1", 8192, 2560, "big", M)]
     phases = [0, 0, 1, 2, 2, 3]
     plan = q().Plan([j.job() for j in jobs], phases, M)
+    plan.set_mode(mode)
     outs = []
     for _ in range(3):
         for j in jobs:
@@ -67,7 +71,8 @@ def test_plan_matches_oracle_and_repeats(M):
     plan.close()
 
 
-def test_plan_honours_the_phase_dependency():
+@pytest.mark.parametrize("mode", [0, 1])
+def test_plan_honours_the_phase_dependency(mode):
     """Phase 1's activations are the bytes phase 0 writes (bf16-exact outputs by construction)."""
     M, N0, K0 = 2, 4096, 2560
     g = synth.rng("gpu-plan", "dep")
@@ -94,6 +99,7 @@ def test_plan_honours_the_phase_dependency():
     y1 = torch.empty((M, N1), dtype=torch.float32, device="cuda")
     plan = q().Plan([(weight(d0, N0, K0, "q4_1"), dx0, y0), (weight(d1, N1, K1, "q4_1"), x1_view, y1)],
                     [0, 1], M)
+    plan.set_mode(mode)
     x1_bits = y0_expect.view(np.uint16).reshape(M, K1)
     yr, a = oracle.gemv_ref(oracle.weights_exact(ch1, "q4_1", N1, K1), x1_bits)
     stale = np.full((M, K1), 0x3F80, np.uint16)
@@ -109,10 +115,12 @@ def test_plan_honours_the_phase_dependency():
     assert plan.errors() == 0
 
 
-def test_plan_in_a_hip_graph_replays_correctly():
+@pytest.mark.parametrize("mode", [0, 1])
+def test_plan_in_a_hip_graph_replays_correctly(mode):
     M = 1
     jobs = [Job("q4_1", 2048, 2560, "gq", M), Job("q4_1", 2560, 9728, "gd", M)]
     plan = q().Plan([j.job() for j in jobs], [0, 1], M)
+    plan.set_mode(mode)
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
         plan.run()
@@ -134,12 +142,14 @@ def test_plan_in_a_hip_graph_replays_correctly():
     assert plan.errors() == 0
 
 
+@pytest.mark.parametrize("mode", [0, 1])
 @pytest.mark.parametrize("layout", ["A", "B"])
-def test_plan_mixed_kinds_in_segments(layout):
+def test_plan_mixed_kinds_in_segments(layout, mode):
     M = 1
     jobs = [Job("q4_k", 4096, 2560, "kq", M), Job("q4_k", 1024, 2560, "kk", M),
             Job("q4_k", 2560, 9728, "kd", M), Job("q8", 8192, 2560, "head", M, layout)]
     plan = q().Plan([j.job() for j in jobs], [0, 0, 1, 2], M)
+    plan.set_mode(mode)
     for _ in range(2):
         plan.run()
         torch.cuda.synchronize()
@@ -148,7 +158,8 @@ def test_plan_mixed_kinds_in_segments(layout):
     assert plan.errors() == 0
 
 
-def test_plan_of_a_qwen3_4b_layer_and_lm_head():
+@pytest.mark.parametrize("mode", [0, 1])
+def test_plan_of_a_qwen3_4b_layer_and_lm_head(mode):
     """The real decode-step shapes: one layer's four phases and the lm_head, M = 1."""
     specs = synth.qwen3_4b_decode_specs(1, True)
     jobs, phases = [], []
@@ -165,6 +176,7 @@ def test_plan_of_a_qwen3_4b_layer_and_lm_head():
         jobs.append(j)
         phases.append(ph[s.name.split(".")[-1]])
     plan = q().Plan([j.job() for j in jobs], phases, 1)
+    plan.set_mode(mode)
     plan.run()
     torch.cuda.synchronize()
     assert plan.errors() == 0
@@ -178,3 +190,26 @@ def test_plan_of_a_qwen3_4b_layer_and_lm_head():
             assert oracle.tol_ratio(ysub, yr, a) <= 1.0
         else:
             j.check()
+
+
+@pytest.mark.parametrize("kind", ["q4_1", "q4_k"])
+def test_one_phase_of_many_jobs_is_one_launch(kind):
+    """200 independent GEMVs (more than one batched call takes) in one phase:
+    mode 0 runs them as one launch over the device job table."""
+    M, N, K = 1, 64, 512
+    jobs = [Job(kind, N, K, f"many{i}", M) for i in range(200)]
+    plan = q().Plan([j.job() for j in jobs], [0] * len(jobs), M)
+    for _ in range(2):
+        for j in jobs:
+            j.dy.fill_(float("nan"))
+        plan.run()
+        torch.cuda.synchronize()
+        for j in jobs:
+            j.check()
+    assert plan.errors() == 0
+
+
+def test_plan_mode_is_checked():
+    plan = q().Plan([Job("q4_1", 64, 512, "modes", 1).job()], [0], 1)
+    with pytest.raises(q().Q4nxError):
+        plan.set_mode(2)
