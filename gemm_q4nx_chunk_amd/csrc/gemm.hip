@@ -405,10 +405,12 @@ void k_gemm_q4(GemmArgs a) {
 // before K has to be split across workgroups, whose fp32 partial tiles (64
 // tokens x 32 outputs per row) cost as many bytes as a few tile columns of
 // weights.  The X columns of both halves' current tile columns (2 x 64 x 256
-// bf16) sit in LDS, double buffered: the tiles two steps ahead are loaded into
-// registers at the start of a step and written to the other buffer at the end
-// of the next.  Chunk loads run D steps ahead in a ring of D register sets; as
-// above, every load is unconditional and every branch uniform.
+// bf16) sit in LDS, double buffered: the next step's tiles are loaded into
+// registers at the start of a step and written to the other buffer at its
+// end.  Chunk loads run D steps ahead in a ring of D register sets; as above,
+// every load is unconditional and every branch uniform.  Inside a step the
+// dequantisation of the next MFMA step's weights and the reads of its X
+// operands are interleaved with the current products.
 template <int KIND, int D, bool LOCAL>
 __global__ __launch_bounds__(64 * kGemmWaves)
 __attribute__((amdgpu_waves_per_eu(Q4NX_GEMM_WPE_TWO, Q4NX_GEMM_WPE_TWO)))
@@ -465,18 +467,18 @@ void k_gemm_q4h(GemmArgs a) {
   const __amdgpu_buffer_rsrc_t xrs = make_rsrc(a.X, (uint32_t)(M * K * 2));
   const uint32_t xoff = (uint32_t)((th >> 5) * K + (th & 31) * 8) * 2;
   const uint32_t xrow8 = (uint32_t)(8 * K * 2);          // 8 rows of X, bytes
-  u32x4 xr[2][XP];
-  auto xload = [&](int b, int t) {   // t: step index (tile column hc0 + t)
+  u32x4 xr[XP];
+  auto xload = [&](int t) {   // t: step index (tile column hc0 + t)
     const uint32_t col = (uint32_t)(hc0 + t) * 512;
 #pragma unroll
     for (int p = 0; p < XP; ++p)
-      xr[b][p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs, xoff + col, p * xrow8, 0));
+      xr[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs, xoff + col, p * xrow8, 0));
   };
-  auto xstore = [&](int b) {
+  auto xstore = [&](int buf) {
 #pragma unroll
     for (int p = 0; p < XP; ++p) {
       const int piece = th + NH * p, row = piece >> 5, c16 = piece & 31;
-      *reinterpret_cast<u32x4*>(&xs[b][pi][row * kXs + c16 * 8]) = xr[b][p];
+      *reinterpret_cast<u32x4*>(&xs[buf][pi][row * kXs + c16 * 8]) = xr[p];
     }
   };
 
@@ -485,39 +487,57 @@ void k_gemm_q4h(GemmArgs a) {
   for (int v = 0; v < 16; ++v) { acc0[v] = 0.f; acc1[v] = 0.f; }
 
   GemmChunk<KIND> c[D];
-  xload(0, 0);
+  xload(0);
 #pragma unroll
   for (int j = 0; j < D; ++j) gemm_load<KIND>(wrs, j * CB, n, h, c[j]);
   xstore(0);
-  xload(1, 1);
 
-  // Step t (parity j): this half's X tile is in xs[j][pi], its chunk in c[j];
-  // the tiles of step t + 1 are in flight in xr[j ^ 1].  The second half may
-  // have one step fewer: its waves skip the products of that step.
-  static_assert(D % 2 == 0, "the X double buffer follows the chunk ring's parity");
-  auto step = [&](int j, int t) {
+  // Step t: this half's X tile is in xs[t & 1][pi], its chunk in c[jc]
+  // (jc = t mod D).  The tiles of step t + 1 are loaded at the top of the
+  // step and stored to the other buffer at its end (one register set: the
+  // products cover their latency).  The second half may have one step fewer:
+  // its waves skip the products of that step.
+  auto step = [&](int jc, int t) {
+    const int j = t & 1;
     __syncthreads();                       // the tiles of step t are in xs[j]; xs[j ^ 1] is free
-    xload(j, t + 2);                       // xr[j] went to LDS at the end of step t - 1
+    xload(t + 1);
     __builtin_amdgcn_sched_barrier(0);     // issue the X loads before the products
     if (hc0 + t < hc1) {
+      // Software pipeline: the weights of MFMA step st + 1 are dequantised and
+      // its X operands read while the two products of step st run, in the
+      // order the group barriers fix (reads, VALU, product, VALU, product).
       const uint16_t* xb = xs[j][pi] + n * kXs + 128 * h;
+      float s, z;
+      group_sz<KIND>(c[jc], 0, s, z);
+      bf16x8 B = dequant8(c[jc].q[0][0], s, z, kMaskLo, kMaskHi, kMagic);
+      bf16x8 A0 = *reinterpret_cast<const bf16x8*>(xb);
+      bf16x8 A1 = *reinterpret_cast<const bf16x8*>(xb + 32 * kXs);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float s, z;
-        group_sz<KIND>(c[j], q, s, z);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int st = 4 * q + e;
-          const bf16x8 B = dequant8(c[j].q[q][e], s, z, kMaskLo, kMaskHi, kMagic);
-          const bf16x8 A0 = *reinterpret_cast<const bf16x8*>(xb + 8 * st);
-          const bf16x8 A1 = *reinterpret_cast<const bf16x8*>(xb + 32 * kXs + 8 * st);
-          acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A0, B, acc0, 0, 0, 0);
-          acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A1, B, acc1, 0, 0, 0);
+      for (int st = 0; st < 16; ++st) {
+        bf16x8 Bn = B, A0n = A0, A1n = A1;
+        if (st < 15) {
+          const int sn = st + 1;
+          if ((sn & 3) == 0) group_sz<KIND>(c[jc], sn >> 2, s, z);
+          Bn = dequant8(c[jc].q[sn >> 2][sn & 3], s, z, kMaskLo, kMaskHi, kMagic);
+          A0n = *reinterpret_cast<const bf16x8*>(xb + 8 * sn);
+          A1n = *reinterpret_cast<const bf16x8*>(xb + 32 * kXs + 8 * sn);
+        }
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A0, B, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A1, B, acc1, 0, 0, 0);
+        B = Bn;
+        A0 = A0n;
+        A1 = A1n;
+        if (st < 15) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);    // DS reads
+          __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);    // VALU
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 14, 0);   // VALU
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
         }
       }
     }
-    gemm_load<KIND>(wrs, (uint32_t)(t + D) * CB, n, h, c[j]);
-    xstore(j ^ 1);                         // tiles of step t + 1, loaded during step t - 1
+    gemm_load<KIND>(wrs, (uint32_t)(t + D) * CB, n, h, c[jc]);
+    xstore(j ^ 1);                         // tiles of step t + 1
   };
   int base = 0;
   for (; base + D <= nsteps; base += D) {
