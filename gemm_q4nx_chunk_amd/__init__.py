@@ -50,7 +50,7 @@ class GemmJob(ctypes.Structure):
 class MoeLayer(ctypes.Structure):
     _fields_ = [("n_experts", ctypes.c_int32), ("d_model", ctypes.c_int32),
                 ("d_expert", ctypes.c_int32), ("d_shared", ctypes.c_int32),
-                ("chunk_bytes", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("chunk_bytes", ctypes.c_int32), ("hot_tokens", ctypes.c_int32),
                 ("gate", ctypes.c_void_p), ("up", ctypes.c_void_p), ("down", ctypes.c_void_p),
                 ("gate_stride", ctypes.c_int64), ("up_stride", ctypes.c_int64),
                 ("down_stride", ctypes.c_int64), ("gate_bytes", ctypes.c_int64),
@@ -338,13 +338,13 @@ def gemm_batched(jobs, X, M: int, ws=None, stream=None, ws_bytes: int | None = N
 def moe_layer(n_experts: int, d_model: int, d_expert: int, kind: str, gate, up, down,
               gate_stride: int, up_stride: int, down_stride: int,
               shared=None, d_shared: int = 0, gate_bytes=None, up_bytes=None,
-              down_bytes=None) -> MoeLayer:
+              down_bytes=None, hot_tokens: int = 0) -> MoeLayer:
     """MoE layer descriptor.  ``shared`` = (Weight gate, Weight up, Weight down) or None."""
     L = MoeLayer()
     L.n_experts, L.d_model, L.d_expert = n_experts, d_model, d_expert
     L.d_shared = d_shared if shared is not None else 0
     L.chunk_bytes = CHUNK_BYTES[kind]
-    L.reserved = 0
+    L.hot_tokens = hot_tokens
     L.gate, L.up, L.down = _ptr(gate), _ptr(up), _ptr(down)
     L.gate_stride, L.up_stride, L.down_stride = gate_stride, up_stride, down_stride
     L.gate_bytes = _nbytes(gate) if gate_bytes is None else gate_bytes

@@ -947,7 +947,6 @@ static int check_arena(const void* base, int64_t stride, int64_t bytes, int n, i
 
 static int check_moe_layer(const q4nx_moe_layer* L) {
   if (!L) return fail(Q4NX_E_ARG, "moe: null layer");
-  if (L->reserved) return fail(Q4NX_E_ARG, "moe: reserved field must be 0");
   if (L->n_experts < 1 || L->n_experts >= (1 << 19))
     return fail(Q4NX_E_ARG, "moe: n_experts = %d outside 1..524287", L->n_experts);
   if (L->chunk_bytes != Q4NX_Q4_1_BYTES && L->chunk_bytes != Q4NX_Q4_K_BYTES)
@@ -1048,6 +1047,7 @@ int q4nx_moe_experts(const q4nx_moe_layer* L, const uint16_t* X, const int32_t* 
   a.k = k;
   a.tb = T == 1 ? 1 : 4;
   a.hstride = moe_hstride(L);
+  a.hot_min = L->hot_tokens > 0 ? L->hot_tokens : 0;
   if (dbg) {
     a.dbg_h = dbg->h;
     a.dbg_d = dbg->d;
@@ -1060,6 +1060,7 @@ int q4nx_moe_experts(const q4nx_moe_layer* L, const uint16_t* X, const int32_t* 
   a.seg = reinterpret_cast<int32_t*>(w + lay.seg);
   a.batch0 = reinterpret_cast<int32_t*>(w + lay.batch0);
   a.btab = reinterpret_cast<int32_t*>(w + lay.btab);
+  a.hot = reinterpret_cast<int32_t*>(w + lay.hot);
   a.hbuf = reinterpret_cast<float*>(w + lay.hbuf);
   a.dbuf = reinterpret_cast<float*>(w + lay.dbuf);
   const hipError_t e = q4nx::launch_moe(L->chunk_bytes == Q4NX_Q4_1_BYTES ? q4nx::KIND_Q4_1

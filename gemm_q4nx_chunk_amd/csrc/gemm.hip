@@ -15,105 +15,23 @@
 // too few workgroups to keep every CU's ALUs busy with dequantisation, K is
 // split over S workgroups; each writes its fp32 partial tile to the workspace
 // and the last of the S to arrive adds the parts in part order (no atomics on
-// data, so the result bits do not depend on timing).
-//
-// Dequantisation: a 4-bit code c placed in an fp16 mantissa under the exponent
-// of 1024 reads as 1024 + c (low nibble) or 1024 + 16c (high nibble of a
-// byte), both exact, so one v_and_or makes two weights' codes into an fp16
-// pair; one v_pk_add_f16 of -1024 (or one v_pk_fma_f16 by 1/16 with -64) turns
-// the pair into the exact codes (c, c'), and one v_fma_mix_f32 per weight forms
-// w = c * s + z in fp32: the exact value rounded once, which is the decoded
-// weight bit for bit.  v_cvt_pk_bf16_f32 then rounds two weights to the bf16
-// pair the MFMA takes (at most 2^-8 of the weight's size).
-//
-// k-slot assignment: in MFMA step s (16 per tile column) lane (h = lane/32,
-// n = lane%32) feeds the 8 products k = 128h + 8s + 0..7 -- for the B operand
-// (weights) of output row n, for the A operand (X) of token row n.  A and B
-// use the same slots, so the order of k inside a step does not change the sum.
-// With this order a lane's weights are one contiguous 64-byte run of its row's
-// codes, and their scale records one 16-byte load.
+// data, so the result bits do not depend on timing).  The dequantisation and
+// the order of k inside an MFMA step are described in mfma_q4.h.
 #include <atomic>
 #include <mutex>
 
 #include "gemm_args.h"
+#include "mfma_q4.h"
 #include "q4nx_dev.h"
 
 namespace q4nx {
 
-constexpr int kXs = 264;   // LDS row stride of an X tile in bf16 (256 + 8: 4-bank skew per row)
 constexpr int kGemmWaves = 8;
 #ifndef Q4NX_GEMM_DEPTH
 #define Q4NX_GEMM_DEPTH 2
 #endif
 constexpr int kGemmDepth = Q4NX_GEMM_DEPTH;   // chunk loads in flight per wave
 static_assert(kGemmWaves == kGemmRowsPerWg, "one tile row per wave");
-
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-
-template <int KIND>
-struct GemmChunk {
-  u32x4 q[4];   // codes k = 128h + 32q + 0..31 of row n
-  u32x4 meta;   // q4_1: (scale, zero) of groups 4h..4h+3; Q4_K: .x,.y = (sc,mn) bytes, .z = (S, M)
-};
-
-// Chunk of tile column t of the lane's row: rs covers the row's chunks of this
-// workgroup's K part, off = (t - first tile column) * chunk bytes.  Offsets past
-// the part read as zero without touching memory, so the prefetch past the last
-// tile column needs no branch.
-template <int KIND>
-__device__ __forceinline__ void gemm_load(__amdgpu_buffer_rsrc_t rs, uint32_t off, int n, int h,
-                                          GemmChunk<KIND>& c) {
-  constexpr int kNt = 2;   // nontemporal: weights are read once
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-    c.q[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                           rs, off + 128 * n + 64 * h + 16 * q, 0, kNt));
-  if constexpr (KIND == KIND_Q4_1) {
-    c.meta = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 4096 + 32 * n + 16 * h, 0, kNt));
-  } else {
-    const u32x2 scmn = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, off + 4096 + 16 * n + 8 * h, 0, kNt));
-    c.meta.x = scmn.x;
-    c.meta.y = scmn.y;
-    c.meta.z = __builtin_amdgcn_raw_buffer_load_b32(rs, off + 4608 + 4 * n, 0, kNt);
-    c.meta.w = 0;
-  }
-}
-
-// Scale and offset of group q (0..3) of the lane: w = code * s + z.
-template <int KIND>
-__device__ __forceinline__ void group_sz(const GemmChunk<KIND>& c, int q, float& s, float& z) {
-  if constexpr (KIND == KIND_Q4_1) {
-    s = bf16lo(c.meta[q]);
-    z = bf16hi(c.meta[q]);
-  } else {
-    const uint32_t pair = (q < 2 ? c.meta.x : c.meta.y) >> (16 * (q & 1));
-    s = bf16lo(c.meta.z) * (float)(pair & 0xFFu);
-    z = bf16hi(c.meta.z) * (float)((pair >> 8) & 0xFFu);
-  }
-}
-
-// Eight weights of one code word (k = 0..7, even k in the low nibble) as bf16.
-__device__ __forceinline__ bf16x8 dequant8(uint32_t w, float s, float z, uint32_t kMaskLo,
-                                           uint32_t kMaskHi, uint32_t kMagic) {
-  const f16x2 m1024 = {(_Float16)-1024.f, (_Float16)-1024.f};
-  const f16x2 m64 = {(_Float16)-64.f, (_Float16)-64.f};
-  const f16x2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
-  const uint32_t w8 = w >> 8;
-  const f16x2 p0 = __builtin_bit_cast(f16x2, (w & kMaskLo) | kMagic) + m1024;    // (c0, c4)
-  const f16x2 p1 = __builtin_elementwise_fma(__builtin_bit_cast(f16x2, (w & kMaskHi) | kMagic), sixteenth, m64);    // (c1, c5)
-  const f16x2 p2 = __builtin_bit_cast(f16x2, (w8 & kMaskLo) | kMagic) + m1024;   // (c2, c6)
-  const f16x2 p3 = __builtin_elementwise_fma(__builtin_bit_cast(f16x2, (w8 & kMaskHi) | kMagic), sixteenth, m64);   // (c3, c7)
-  bf16x8 b;
-  b[0] = (__bf16)fmaf((float)p0.x, s, z);
-  b[1] = (__bf16)fmaf((float)p1.x, s, z);
-  b[2] = (__bf16)fmaf((float)p2.x, s, z);
-  b[3] = (__bf16)fmaf((float)p3.x, s, z);
-  b[4] = (__bf16)fmaf((float)p0.y, s, z);
-  b[5] = (__bf16)fmaf((float)p1.y, s, z);
-  b[6] = (__bf16)fmaf((float)p2.y, s, z);
-  b[7] = (__bf16)fmaf((float)p3.y, s, z);
-  return b;
-}
 
 // The X columns of the current tile column (XR x 256 bf16) sit in LDS, double
 // buffered: the next tile column's X is loaded into registers at the start of
@@ -502,40 +420,8 @@ void k_gemm_q4h(GemmArgs a) {
     __syncthreads();                       // the tiles of step t are in xs[j]; xs[j ^ 1] is free
     xload(t + 1);
     __builtin_amdgcn_sched_barrier(0);     // issue the X loads before the products
-    if (hc0 + t < hc1) {
-      // Software pipeline: the weights of MFMA step st + 1 are dequantised and
-      // its X operands read while the two products of step st run, in the
-      // order the group barriers fix (reads, VALU, product, VALU, product).
-      const uint16_t* xb = xs[j][pi] + n * kXs + 128 * h;
-      float s, z;
-      group_sz<KIND>(c[jc], 0, s, z);
-      bf16x8 B = dequant8(c[jc].q[0][0], s, z, kMaskLo, kMaskHi, kMagic);
-      bf16x8 A0 = *reinterpret_cast<const bf16x8*>(xb);
-      bf16x8 A1 = *reinterpret_cast<const bf16x8*>(xb + 32 * kXs);
-#pragma unroll
-      for (int st = 0; st < 16; ++st) {
-        bf16x8 Bn = B, A0n = A0, A1n = A1;
-        if (st < 15) {
-          const int sn = st + 1;
-          if ((sn & 3) == 0) group_sz<KIND>(c[jc], sn >> 2, s, z);
-          Bn = dequant8(c[jc].q[sn >> 2][sn & 3], s, z, kMaskLo, kMaskHi, kMagic);
-          A0n = *reinterpret_cast<const bf16x8*>(xb + 8 * sn);
-          A1n = *reinterpret_cast<const bf16x8*>(xb + 32 * kXs + 8 * sn);
-        }
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A0, B, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A1, B, acc1, 0, 0, 0);
-        B = Bn;
-        A0 = A0n;
-        A1 = A1n;
-        if (st < 15) {
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);    // DS reads
-          __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);    // VALU
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x002, 14, 0);   // VALU
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
-        }
-      }
-    }
+    if (hc0 + t < hc1)
+      mfma_tile<KIND>(c[jc], xs[j][pi] + n * kXs + 128 * h, 32 * kXs, acc0, acc1, kMaskLo, kMaskHi, kMagic);
     gemm_load<KIND>(wrs, (uint32_t)(t + D) * CB, n, h, c[jc]);
     xstore(j ^ 1);                         // tiles of step t + 1
   };

@@ -20,7 +20,10 @@
 //           (each h to 2^-12 of its size).
 //   combine y[t] = sum_j p[t][j] d[t][j] in slot order, then + the shared d.
 // No floating-point atomics anywhere; every sum has a fixed order.
+#include <type_traits>
+
 #include "gemv_core.h"
+#include "mfma_q4.h"
 #include "moe_args.h"
 
 namespace q4nx {
@@ -38,6 +41,14 @@ namespace q4nx {
 // thread.  The tables are the ones the sort below produces.  Returns false,
 // having written nothing, when the block does not qualify.
 constexpr int kRouteMaskTokens = 64, kRouteMaskExperts = 1024;
+
+// A segment of cnt pairs runs on the matrix cores (and has no batches).
+__device__ __forceinline__ bool moe_hot(const MoeArgs& a, int cnt) {
+  return a.hot_min > 0 && cnt >= a.hot_min;
+}
+__device__ __forceinline__ bool moe_shared_hot(const MoeArgs& a) {
+  return a.Ds > 0 && a.hot_min > 0 && a.T >= a.hot_min;
+}
 
 __device__ __forceinline__ uint64_t block_incl_scan64(uint64_t v, uint64_t* wsum) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -86,7 +97,7 @@ __device__ __forceinline__ bool moe_route_masks(const MoeArgs& a, uint32_t* lds1
   if (cnt) atomicAdd(&flags[1], cnt);
   __syncthreads();
   if (flags[0] || flags[1] != P) return false;   // an id out of range, or a token naming an expert twice
-  const int nb = (cnt + a.tb - 1) / a.tb;
+  const int nb = moe_hot(a, cnt) ? 0 : (cnt + a.tb - 1) / a.tb;
   const uint64_t own = (uint64_t)cnt | ((uint64_t)nb << 16) | ((uint64_t)(cnt > 0) << 32);
   const uint64_t inc = block_incl_scan64(own, wsum);
   const uint64_t ex = inc - own;
@@ -137,6 +148,75 @@ __device__ __forceinline__ bool moe_route_masks(const MoeArgs& a, uint32_t* lds1
   return true;
 }
 
+// Matrix-core units: the segments of at least hot_min pairs in segment order,
+// then the shared expert when T >= hot_min; each with the first of its work
+// items in both item spaces (items of 64 token rows times groups of 2 gate/up
+// or 8 down tile rows).  Wave 0 walks the segment table the route kernel has
+// just written, 64 segments at a time.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(v, off);
+    if (lane >= off) v += o;
+  }
+  return v;
+}
+
+__device__ __forceinline__ void moe_route_hot(const MoeArgs& a) {
+  if (a.hot_min <= 0) return;
+  __syncthreads();   // the segment table and header are written
+  if (threadIdx.x >= 64) return;
+  const int lane = threadIdx.x;
+  const int nseg = (int)a.hdr[1];
+  const int g_gu = a.De / 64, g_dn = a.D / 256;   // row groups per token block
+  int nh = 0, igu = 0, idn = 0;
+  for (int s0 = 0; s0 < nseg; s0 += 64) {
+    const int sg = s0 + lane;
+    int e = 0, start = 0, cnt = 0;
+    if (sg < nseg) {
+      e = a.seg[3 * sg];
+      start = a.seg[3 * sg + 1];
+      cnt = a.seg[3 * sg + 2];
+    }
+    const bool hot = sg < nseg && moe_hot(a, cnt);
+    const int nblk = hot ? (cnt + kMoeHotTokens - 1) / kMoeHotTokens : 0;
+    const int ih = wave_incl_scan(hot ? 1 : 0);
+    const int ig = wave_incl_scan(nblk * g_gu);
+    const int id = wave_incl_scan(nblk * g_dn);
+    if (hot) {
+      int32_t* r = a.hot + (size_t)(nh + ih - 1) * kMoeHotInts;
+      r[0] = e;
+      r[1] = start;
+      r[2] = cnt;
+      r[3] = igu + ig - nblk * g_gu;
+      r[4] = idn + id - nblk * g_dn;
+    }
+    nh += __shfl(ih, 63);
+    igu += __shfl(ig, 63);
+    idn += __shfl(id, 63);
+  }
+  if (moe_shared_hot(a)) {
+    const int nblk = (a.T + kMoeHotTokens - 1) / kMoeHotTokens;
+    if (lane == 0) {
+      int32_t* r = a.hot + (size_t)nh * kMoeHotInts;
+      r[0] = -1;
+      r[1] = 0;
+      r[2] = a.T;
+      r[3] = igu;
+      r[4] = idn;
+    }
+    nh += 1;
+    igu += nblk * (a.Ds / 64);
+    idn += nblk * g_dn;
+  }
+  if (lane == 0) {
+    a.hdr[3] = (uint32_t)nh;
+    a.hdr[4] = (uint32_t)igu;
+    a.hdr[5] = (uint32_t)idn;
+  }
+}
+
 __global__ __launch_bounds__(1024) void k_moe_route(MoeArgs a) {
   __shared__ uint32_t key[kMoeMaxPairs];
   __shared__ int32_t scan[1024];
@@ -144,7 +224,10 @@ __global__ __launch_bounds__(1024) void k_moe_route(MoeArgs a) {
   __shared__ uint64_t wsum[16];
   __shared__ int32_t flags[4];
   static_assert(kMoeMaxPairs * 4 >= 1024 * 16, "the masks and prefix tables fit the key array");
-  if (moe_route_masks(a, key, scan, wsum, flags)) return;
+  if (moe_route_masks(a, key, scan, wsum, flags)) {
+    moe_route_hot(a);
+    return;
+  }
   __syncthreads();   // the masks' LDS is the sort's
   const int P = a.T * a.k;
   int NP = 1;
@@ -195,7 +278,7 @@ __global__ __launch_bounds__(1024) void k_moe_route(MoeArgs a) {
       a.sorted[s] = (int32_t)(key[s] & 0xFFFu);
     }
     // inclusive scans of start flags and of batch counts, packed in one int
-    const int nb = start ? (cnt + a.tb - 1) / a.tb : 0;
+    const int nb = start && !moe_hot(a, cnt) ? (cnt + a.tb - 1) / a.tb : 0;
     scan[tid] = (start << 20) | nb;
     __syncthreads();
     for (int off = 1; off < 1024; off <<= 1) {
@@ -236,6 +319,7 @@ __global__ __launch_bounds__(1024) void k_moe_route(MoeArgs a) {
     a.hdr[2] = (uint32_t)base_batch;  // routed token batches
     a.batch0[base_seg] = base_batch;
   }
+  moe_route_hot(a);
 }
 
 // Work item of a (batch, tile-row group) launch: which expert, which tokens.
@@ -287,7 +371,7 @@ __device__ __forceinline__ bool moe_item(const MoeArgs& a, int nbr, int item, in
     return true;
   }
   item -= nbr * gr;
-  const int nbs = a.Ds ? (a.T + TB - 1) / TB : 0;
+  const int nbs = a.Ds && !moe_shared_hot(a) ? (a.T + TB - 1) / TB : 0;
   if (item < nbs * gs) {
     const int b = item / gs;
     it.tr = (item - b * gs) * rpw_s;
@@ -777,6 +861,324 @@ __global__ __launch_bounds__(64 * WAVES) void k_moe_down(MoeArgs a, int ks_r, in
 }
 
 // ---------------------------------------------------------------------------
+// experts with many tokens: bf16 matrix-core tiles
+// ---------------------------------------------------------------------------
+// A unit (a segment of at least hot_min pairs, or the shared expert when
+// T >= hot_min) is cut into work items of 64 token rows times a group of tile
+// rows.  Each chunk of the group is read once per item and dequantised once to
+// two bf16 parts (hi = bf16(w), lo = bf16(w - hi): each weight to 2^-16 of
+// its size, so the per-output bound holds however the terms of a sum are
+// distributed), and v_mfma_f32_32x32x16 multiplies both against all 64 rows
+// at once, where the batched kernels above would re-read the expert per batch
+// of 4 tokens and spend a dot2 chain per token.  The token rows are gathered into an LDS tile per tile column,
+// double buffered, shared by the workgroup's 8 waves.  Rows past the unit's
+// count repeat its first token and are never stored.
+//
+// A token's bits depend on whether its expert reached hot_min pairs in the
+// call (a different order of sums and of roundings), within the same
+// per-output bound either way.
+
+// The unit of work item `item` (first items at field f of the unit records),
+// or -1 when none holds it.  *s_unit is -1 on entry; the caller sets it back
+// before the barrier that ends the item.
+__device__ __forceinline__ int moe_hot_unit(const MoeArgs& a, int item, int nh, int nitems, int f,
+                                            int32_t* s_unit) {
+  for (int u = threadIdx.x; u < nh; u += blockDim.x) {
+    const int f0 = a.hot[(size_t)u * kMoeHotInts + f];
+    const int f1 = u + 1 < nh ? a.hot[(size_t)(u + 1) * kMoeHotInts + f] : nitems;
+    if (f0 <= item && item < f1) *s_unit = u;
+  }
+  __syncthreads();
+  return __builtin_amdgcn_readfirstlane(*s_unit);
+}
+
+// Token slots of an item: X row (element offset, gate/up), h row (hbuf row,
+// down), destination (pair index routed, P + t shared), valid flag.
+struct MoeHotSlots {
+  int64_t xrow[kMoeHotTokens];
+  int32_t hrow[kMoeHotTokens];
+  int32_t dst[kMoeHotTokens];
+  int32_t valid[kMoeHotTokens];
+};
+
+__device__ __forceinline__ void moe_hot_slots(const MoeArgs& a, bool shared, int start, int m0, int nb,
+                                              MoeHotSlots& sl) {
+  const int P = a.T * a.k, t = threadIdx.x;
+  if (t < kMoeHotTokens) {
+    const int mm = m0 + (t < nb ? t : 0);
+    int tok, hrow, dst;
+    if (shared) {
+      tok = mm;
+      hrow = P + mm;
+      dst = P + mm;
+    } else {
+      dst = a.sorted[start + mm];
+      tok = dst / a.k;
+      hrow = start + mm;
+    }
+    sl.xrow[t] = (int64_t)tok * a.D;
+    sl.hrow[t] = hrow;
+    sl.dst[t] = dst;
+    sl.valid[t] = t < nb;
+  }
+}
+
+// gate/up: an item is 64 token rows times 2 tile rows of gate and the same 2
+// of up.  Wave w runs tile row 2g + (w & 1) of gate or up ((w >> 1) & 1) over
+// one half of K (w >> 2); the halves meet in LDS (first + second), then the
+// up waves hand their sums to the gate waves, which write h = silu(g) u in
+// fp32.  Items of at most 32 token rows skip the second token tile.
+template <int KIND>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void k_moe_hot_gu(MoeArgs a) {
+  constexpr int CB = ChunkBytes<KIND>::value, NH = 256, XR = kMoeHotTokens;
+  constexpr int XP = XR * 32 / NH;   // 16-byte X pieces per thread and tile of its half
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][2][XR * kXs];   // [buffer][half]
+  __shared__ MoeHotSlots sl;
+  __shared__ int32_t s_unit;
+  static_assert(sizeof(xs) >= (4 + 2) * 8 * 64 * 16, "LDS for the exchanges of sums");
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, n = lane & 31;
+  const int half = wave >> 2, proj = (wave >> 1) & 1, rsub = wave & 1;
+  const int th = tid & (NH - 1);
+  const int nh = (int)a.hdr[3], nitems = (int)a.hdr[4];
+  const int TC = a.D / 256, P = a.T * a.k;
+  const int mid = (TC + 1) / 2, hc0 = half ? mid : 0, hc1 = half ? TC : mid;
+  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(a.X, (uint32_t)((size_t)a.T * a.D * 2));
+  uint32_t kMaskLo = 0x000F000Fu, kMaskHi = 0x00F000F0u, kMagic = 0x64006400u;
+  asm volatile("" : "+s"(kMaskLo));
+  asm volatile("" : "+s"(kMaskHi));
+  asm volatile("" : "+v"(kMagic));
+  if (tid == 0) s_unit = -1;
+  __syncthreads();
+  for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
+    const int u = moe_hot_unit(a, item, nh, nitems, 3, &s_unit);
+    if (u < 0) {   // (a unit table that does not cover the item: nothing to do)
+      __syncthreads();   // every wave has read the unit before any writes the next
+      continue;
+    }
+    const int32_t* rec = a.hot + (size_t)u * kMoeHotInts;
+    const int e = rec[0], start = rec[1], cnt = rec[2], first = rec[3];
+    const bool shared = e < 0;
+    const int G = (shared ? a.Ds : a.De) / 64;
+    const int local = item - first, blk = local / G, g = local - blk * G;
+    const int tr = 2 * g + rsub;
+    const int m0 = blk * XR, nb = min(XR, cnt - m0);
+    moe_hot_slots(a, shared, start, m0, nb, sl);
+    const uint8_t* wbase = shared ? (proj ? a.sup : a.sgate)
+                                  : (proj ? a.up + (size_t)e * a.up_stride : a.gate + (size_t)e * a.gate_stride);
+    const __amdgpu_buffer_rsrc_t wrs =
+        make_rsrc(wbase + ((size_t)tr * TC + hc0) * CB, (uint32_t)((hc1 - hc0) * CB));
+    GemmChunk<KIND> c[2];
+    gemm_load<KIND>(wrs, 0, n, h, c[0]);
+    gemm_load<KIND>(wrs, CB, n, h, c[1]);
+    __syncthreads();   // the slots are in LDS
+    uint32_t xo[XP];
+#pragma unroll
+    for (int p = 0; p < XP; ++p) xo[p] = (uint32_t)(sl.xrow[(th >> 5) + 8 * p] + (th & 31) * 8) * 2;
+    u32x4 xr[XP];
+    auto xload = [&](int t) {   // tile column hc0 + t of this half
+#pragma unroll
+      for (int p = 0; p < XP; ++p)
+        xr[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs, xo[p] + (hc0 + t) * 512, 0, 0));
+    };
+    auto xstore = [&](int buf) {
+#pragma unroll
+      for (int p = 0; p < XP; ++p)
+        *reinterpret_cast<u32x4*>(&xs[buf][half][((th >> 5) + 8 * p) * kXs + (th & 31) * 8]) = xr[p];
+    };
+    f32x16 acc0, acc1;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) { acc0[v] = 0.f; acc1[v] = 0.f; }
+    if (hc0 < hc1) xload(0);
+    xstore(0);
+    // The second half may have one step fewer: its waves skip that step's
+    // loads and products but keep to the barriers.
+    auto run = [&](auto two_c) {
+      constexpr bool TWO = decltype(two_c)::value;
+      auto step = [&](int jc, int t) {
+        const int j = t & 1;
+        const bool mine = hc0 + t < hc1, next = hc0 + t + 1 < hc1;
+        __syncthreads();   // X tile t is in xs[j]; xs[j ^ 1] is free
+        if (next) xload(t + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        if (mine)
+          mfma_tile_w2<KIND, TWO>(c[jc], xs[j][half] + n * kXs + 128 * h, 32 * kXs, acc0, acc1, kMaskLo,
+                                  kMaskHi, kMagic);
+        gemm_load<KIND>(wrs, (uint32_t)(t + 2) * CB, n, h, c[jc]);   // past the half: zeros
+        if (next) xstore(j ^ 1);
+      };
+      for (int t = 0; t < mid; t += 2) {
+        step(0, t);
+        if (t + 1 < mid) step(1, t + 1);
+      }
+    };
+    if (nb > 32) run(std::true_type{});
+    else run(std::false_type{});
+    __syncthreads();   // every product is done: xs holds the exchanges now
+    f32x4* red = reinterpret_cast<f32x4*>(&xs[0][0][0]);   // [4 waves of half 1][8 groups][64 lanes]
+    f32x4* red2 = red + 4 * 8 * 64;                       // [2 up waves][8 groups][64 lanes]
+    // group g8 of a wave's sums: registers 4 g8 .. 4 g8 + 3 of acc0 (g8 < 4) or acc1
+    auto part = [&](int g8) -> f32x4 {
+      const f32x16& A = g8 < 4 ? acc0 : acc1;
+      const int b = 4 * (g8 & 3);
+      return f32x4{A[b], A[b + 1], A[b + 2], A[b + 3]};
+    };
+    auto add = [&](int g8, f32x4 v) {
+      f32x16& A = g8 < 4 ? acc0 : acc1;
+      const int b = 4 * (g8 & 3);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) A[b + i] += v[i];
+    };
+    if (half == 1) {
+#pragma unroll
+      for (int g8 = 0; g8 < 8; ++g8) red[((wave & 3) * 8 + g8) * 64 + lane] = part(g8);
+    }
+    __syncthreads();
+    if (half == 0) {
+#pragma unroll
+      for (int g8 = 0; g8 < 8; ++g8) add(g8, red[((wave & 3) * 8 + g8) * 64 + lane]);
+      if (proj == 1) {
+#pragma unroll
+        for (int g8 = 0; g8 < 8; ++g8) red2[(rsub * 8 + g8) * 64 + lane] = part(g8);
+      }
+    }
+    __syncthreads();
+    if (half == 0 && proj == 0) {
+      const int col = 32 * tr + n;
+#pragma unroll
+      for (int g8 = 0; g8 < 8; ++g8) {
+        const f32x4 uu = red2[(rsub * 8 + g8) * 64 + lane];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          // register v of a 32x32 tile: token row 8 (v / 4) + 4 h + v % 4
+          const int m = 32 * (g8 >> 2) + 8 * (g8 & 3) + 4 * h + i;
+          const float gv = (g8 < 4 ? acc0 : acc1)[4 * (g8 & 3) + i];
+          if (sl.valid[m]) {
+            const float hv = gv / (1.0f + expf(-gv)) * uu[i];
+            a.hbuf[(size_t)sl.hrow[m] * a.hstride + col] = hv;
+            if (shared) {
+              if (a.dbg_h_shared) a.dbg_h_shared[(size_t)(sl.dst[m] - P) * a.Ds + col] = hv;
+            } else if (a.dbg_h) {
+              a.dbg_h[(size_t)sl.dst[m] * a.De + col] = hv;
+            }
+          }
+        }
+      }
+    }
+    if (tid == 0) s_unit = -1;
+    __syncthreads();   // xs, the slots and the unit are reused by the next item
+  }
+}
+
+// down: an item is 64 token rows times 8 tile rows of down (one per wave) over
+// all of the unit's inner width (items of at most 32 token rows skip the
+// second token tile).  h (fp32) enters as two bf16 tiles,
+// hi = bf16(h) and lo = bf16(h - hi), which carry h to 2^-16 of its size;
+// d = whi hhi + wlo hhi + whi hlo in fp32, stored by pair for the combine.
+template <int KIND>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void k_moe_hot_dn(MoeArgs a) {
+  constexpr int CB = ChunkBytes<KIND>::value, NT = 512, XR = kMoeHotTokens;
+  constexpr int HP = XR * 64 / NT;   // 16-byte pieces of fp32 h per thread and tile
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][2][XR * kXs];   // [buffer][hi, lo]
+  __shared__ MoeHotSlots sl;
+  __shared__ int32_t s_unit;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, n = lane & 31;
+  const int nh = (int)a.hdr[3], nitems = (int)a.hdr[5];
+  const int G = a.D / 256;
+  const __amdgpu_buffer_rsrc_t hrs =
+      make_rsrc(a.hbuf, (uint32_t)((size_t)(a.T * a.k + a.T) * a.hstride * 4));
+  uint32_t kMaskLo = 0x000F000Fu, kMaskHi = 0x00F000F0u, kMagic = 0x64006400u;
+  asm volatile("" : "+s"(kMaskLo));
+  asm volatile("" : "+s"(kMaskHi));
+  asm volatile("" : "+v"(kMagic));
+  if (tid == 0) s_unit = -1;
+  __syncthreads();
+  for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
+    const int u = moe_hot_unit(a, item, nh, nitems, 4, &s_unit);
+    if (u < 0) {   // (a unit table that does not cover the item: nothing to do)
+      __syncthreads();   // every wave has read the unit before any writes the next
+      continue;
+    }
+    const int32_t* rec = a.hot + (size_t)u * kMoeHotInts;
+    const int e = rec[0], start = rec[1], cnt = rec[2], first = rec[4];
+    const bool shared = e < 0;
+    const int TC = (shared ? a.Ds : a.De) / 256;
+    const int local = item - first, blk = local / G, g = local - blk * G;
+    const int tr = 8 * g + wave;
+    const int m0 = blk * XR, nb = min(XR, cnt - m0);
+    moe_hot_slots(a, shared, start, m0, nb, sl);
+    const uint8_t* wbase = shared ? a.sdown : a.down + (size_t)e * a.down_stride;
+    const __amdgpu_buffer_rsrc_t wrs = make_rsrc(wbase + (size_t)tr * TC * CB, (uint32_t)(TC * CB));
+    GemmChunk<KIND> c[2];
+    gemm_load<KIND>(wrs, 0, n, h, c[0]);
+    gemm_load<KIND>(wrs, CB, n, h, c[1]);
+    __syncthreads();   // the slots are in LDS
+    uint32_t ho[HP];
+#pragma unroll
+    for (int p = 0; p < HP; ++p) ho[p] = (uint32_t)(sl.hrow[(tid >> 6) + 8 * p] * a.hstride + (tid & 63) * 4) * 4;
+    f32x4 hr[HP];
+    auto hload = [&](int t) {
+#pragma unroll
+      for (int p = 0; p < HP; ++p)
+        hr[p] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(hrs, ho[p] + t * 1024, 0, 0));
+    };
+    auto hstore = [&](int buf) {
+#pragma unroll
+      for (int p = 0; p < HP; ++p) {
+        const int off = ((tid >> 6) + 8 * p) * kXs + (tid & 63) * 4;
+        uint16_t hi[4], lo[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const __bf16 b = (__bf16)hr[p][i];
+          hi[i] = __builtin_bit_cast(uint16_t, b);
+          lo[i] = __builtin_bit_cast(uint16_t, (__bf16)(hr[p][i] - (float)b));
+        }
+        *reinterpret_cast<u32x2*>(&xs[buf][0][off]) = u32x2{hi[0] | ((uint32_t)hi[1] << 16), hi[2] | ((uint32_t)hi[3] << 16)};
+        *reinterpret_cast<u32x2*>(&xs[buf][1][off]) = u32x2{lo[0] | ((uint32_t)lo[1] << 16), lo[2] | ((uint32_t)lo[3] << 16)};
+      }
+    };
+    f32x16 acc0, acc1;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) { acc0[v] = 0.f; acc1[v] = 0.f; }
+    hload(0);
+    hstore(0);
+    auto run = [&](auto two_c) {
+      constexpr bool TWO = decltype(two_c)::value;
+      auto step = [&](int jc, int t) {
+        const int j = t & 1;
+        __syncthreads();   // h tiles of step t are in xs[j]; xs[j ^ 1] is free
+        if (t + 1 < TC) hload(t + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_tile_hl<KIND, TWO>(c[jc], xs[j][0] + n * kXs + 128 * h, 32 * kXs, XR * kXs, acc0, acc1, kMaskLo,
+                                kMaskHi, kMagic);
+        gemm_load<KIND>(wrs, (uint32_t)(t + 2) * CB, n, h, c[jc]);   // past the row: zeros
+        if (t + 1 < TC) hstore(j ^ 1);
+      };
+      for (int t = 0; t < TC; t += 2) {
+        step(0, t);
+        if (t + 1 < TC) step(1, t + 1);
+      }
+    };
+    if (nb > 32) run(std::true_type{});
+    else run(std::false_type{});
+    const int col = 32 * tr + n;
+#pragma unroll
+    for (int v = 0; v < 32; ++v) {
+      const int m = 32 * (v >> 4) + 8 * ((v & 15) >> 2) + 4 * h + (v & 3);
+      const float dv = v < 16 ? acc0[v] : acc1[v - 16];
+      if (sl.valid[m]) a.dbuf[(size_t)sl.dst[m] * a.D + col] = dv;
+    }
+    if (tid == 0) s_unit = -1;
+    __syncthreads();   // xs, the slots and the unit are reused by the next item
+  }
+}
+
+// ---------------------------------------------------------------------------
 // combine
 // ---------------------------------------------------------------------------
 // Every load of a thread is issued before the first product: ids, weights and
@@ -858,11 +1260,16 @@ static hipError_t moe_run(const MoeArgs& a, hipStream_t s) {
   const int nb_r = (P + nseg_max * (TB - 1)) / TB;        // bound on routed batches
   const int nb_s = a.Ds ? (a.T + TB - 1) / TB : 0;
   hipLaunchKernelGGL(k_moe_route, dim3(1), dim3(1024), 0, s, a);
+  // experts with at least hot_min pairs (and the shared expert when T >= hot_min)
+  // on the matrix cores; one persistent workgroup per CU walks their items
+  const bool hot = a.hot_min > 0;
+  if (hot) hipLaunchKernelGGL((k_moe_hot_gu<KIND>), dim3(256), dim3(512), 0, s, a);
   const int gu_items = nb_r * (a.De / 32) + nb_s * (a.Ds / 32);
   hipLaunchKernelGGL((k_moe_gateup<KIND, TB>), dim3(gu_items < 4096 ? gu_items : 4096), dim3(256),
                      xl_gu, s, a);
   // prompt-block down: four-wave workgroups (two fit a CU at this register
   // count; eight-wave ones, one per CU, measured 20% slower)
+  if (hot) hipLaunchKernelGGL((k_moe_hot_dn<KIND>), dim3(256), dim3(512), 0, s, a);
   constexpr int kDnWaves = 4;
   const int dn_items = nb_r * (rows / (kDnWaves / ks_r)) + nb_s * (rows / (kDnWaves / ks_s));
   hipLaunchKernelGGL((k_moe_down<KIND, TB, kDnWaves>), dim3(dn_items < 4096 ? dn_items : 4096), dim3(64 * kDnWaves),

@@ -287,7 +287,10 @@ typedef struct q4nx_moe_layer {
   int32_t d_expert;      /* routed intermediate width: gate/up rows, down cols (mult. of 256, <= 1048576) */
   int32_t d_shared;      /* shared intermediate width (mult. of 256, <= 1048576), or 0 for none */
   int32_t chunk_bytes;   /* kind of every expert weight: 5120 (q4_1) or 4736 (Q4_K) */
-  int32_t reserved;      /* must be 0 */
+  int32_t hot_tokens;    /* prompt-block calls (T * k > 64): an expert chosen by at least this
+                            many pairs, and the shared expert when T reaches it, runs on the
+                            bf16 matrix cores (see q4nx_moe_experts); 0 or negative: never
+                            (the default: measured faster at the 512-expert block) */
   const void* gate;      /* DEVICE, expert e at gate + e*gate_stride, [d_expert/32][D/256] chunks */
   const void* up;        /* DEVICE, same shape as gate */
   const void* down;      /* DEVICE, expert e at down + e*down_stride, [D/32][d_expert/256] chunks */
@@ -320,6 +323,14 @@ size_t q4nx_moe_ws(const q4nx_moe_layer* L, int T, int k);
  * most 2^-12 of its size while it lies within 2^29 of the largest of its 32,
  * so d is within 2^-12 * sum |w h| plus the fp32 sums); the weighted sum over
  * slots runs in slot order, then the shared expert, in fp32, with no atomics.
+ * In prompt-block calls (T * k > 64) an expert chosen by at least
+ * L->hot_tokens pairs, and the shared expert when T reaches it, runs on the
+ * bf16 matrix cores instead: each weight and each h carried as two bf16
+ * parts, hi = bf16(v) and lo = bf16(v - hi) (to 2^-16 of its size), fp32
+ * accumulation.  A token's bits then depend on
+ * whether its experts reached that count in the call; with hot_tokens <= 0
+ * (the default) they never do, and a token's bits do not depend on the other
+ * tokens.
  *   X    DEVICE bf16 [T][D]; ids DEVICE int32 [T][k]; p DEVICE fp32 [T][k]
  *   Y    DEVICE fp32 [T][D], fully overwritten
  *   T    1..4096, k 1..16, T*k <= 4096.  A batch's prepared activations are

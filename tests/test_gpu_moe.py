@@ -8,6 +8,13 @@ Stage-wise checks:
   y  vs the oracle combine of the GPU's own d (fp32 sum of k+1 terms);
 and end to end against the all-float64 layer within 2e-3 * a with
 a = sum_j |p| sum |Down| |h| + the shared expert's sum |Down_s| |h_s|.
+
+With hot_tokens > 0, experts of prompt-block calls chosen by at least that
+many pairs (and the shared expert when T reaches it) run on the bf16 matrix
+cores; the same checks hold there.  A token's bits are independent of the
+other tokens of the call only with that path off (the default), so the
+batch-invariance checks run with it off, and the matrix-core path is checked
+against the oracle.
 """
 import numpy as np
 import pytest
@@ -23,7 +30,7 @@ pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not have_gpu(), reason="needs 
 class Layer:
     """Routed experts in three device arenas plus a shared expert."""
 
-    def __init__(self, tag, kind, n_exp, D, De, Ds, experts_needed=None):
+    def __init__(self, tag, kind, n_exp, D, De, Ds, experts_needed=None, hot_tokens=0):
         self.kind, self.n, self.D, self.De, self.Ds = kind, n_exp, D, De, Ds
         cb = oracle.KIND_BYTES[kind]
         self.gu_bytes = (De // 32) * (D // 256) * cb
@@ -52,7 +59,8 @@ class Layer:
                 sw.append(weight(d, N, K, kind))
             shared = tuple(sw)
         self.L = q().moe_layer(n_exp, D, De, kind, self.dev["gate"], self.dev["up"], self.dev["down"],
-                               self.gu_bytes, self.gu_bytes, self.dn_bytes, shared=shared, d_shared=Ds)
+                               self.gu_bytes, self.gu_bytes, self.dn_bytes, shared=shared, d_shared=Ds,
+                               hot_tokens=hot_tokens)
 
     def _gen(self, tag, p, e, N, K):
         g = synth.rng("gpu-moe", tag, p, e)
@@ -208,7 +216,8 @@ def test_block_routing_with_repeated_or_bad_ids(case):
 
 
 def test_token_result_does_not_depend_on_its_batch():
-    """A token alone (T=1) and inside a 64-token block get the same bits."""
+    """With the matrix-core path off (the default), a token alone (T=1) and
+    inside a 64-token block get the same bits."""
     layer = Layer("batch", "q4_1", 16, 512, 256, 256)
     g = synth.rng("gpu-moe", "route-batch")
     ids, p = synth.gen_router(g, 64, 16, 4, 1.1)
@@ -252,11 +261,54 @@ def test_maximum_pairs(T, k):
     g = synth.rng("gpu-moe", "maxpairs", T, k)
     ids, p = synth.gen_router(g, T, 16, k, 1.1)
     X = synth.gen_x(g, T, 512)
-    r = layer.run(X, ids, p)
-    assert r["err"] == 0
     sel = [0, 1, T // 2, T - 1]
-    sub = {name: (v[sel] if name != "err" else v) for name, v in r.items()}
-    _check_stages(layer, X[sel], ids[sel], p[sel], sub)
+    for hot in (1, 0):   # every expert on the matrix cores, then none
+        layer.L.hot_tokens = hot
+        r = layer.run(X, ids, p)
+        assert r["err"] == 0
+        sub = {name: (v[sel] if name != "err" else v) for name, v in r.items()}
+        _check_stages(layer, X[sel], ids[sel], p[sel], sub)
     for t in (0, T - 1):
         one = layer.run(X[t:t + 1], ids[t:t + 1], p[t:t + 1], dbg=False)
         np.testing.assert_array_equal(one["y"][0].view(np.uint32), r["y"][t].view(np.uint32))
+
+
+@pytest.mark.parametrize("kind", ["q4_1", "q4_k"])
+@pytest.mark.parametrize("hot", [1, 9, -1])
+def test_matrix_core_experts(kind, hot):
+    """hot_tokens 1: every expert of a prompt block (and the shared expert) on
+    the matrix cores; 9: the popular ones only; -1: none (as 0, the default).  Stage-wise and end
+    to end against the oracle each time, with 70 tokens (two 64-row blocks for
+    the shared expert and the most popular experts) and a d_model of 768
+    (an odd number of tile columns)."""
+    layer = Layer("hot", kind, 24, 768, 256, 512, hot_tokens=hot)
+    g = synth.rng("gpu-moe", "hot", kind)
+    ids, p = synth.gen_router(g, 70, 24, 6, 1.1)
+    X = synth.gen_x(g, 70, 768)
+    r = layer.run(X, ids, p)
+    assert r["err"] == 0
+    counts = np.bincount(ids.ravel(), minlength=24)
+    assert counts.max() > 64 and (counts < 9).any() and (counts >= 9).any()
+    print(_check_stages(layer, X, ids, p, r))
+
+
+def test_matrix_core_experts_full_size_block():
+    """The 512-expert layer's 64-token block with experts of 8 or more pairs on
+    the matrix cores, and the same call with that path off: every sampled
+    output within the bar of the oracle's scale."""
+    T = 64
+    ids, p = synth.moe_router(0, T)
+    layer = Layer("full", "q4_1", synth.MOE_EXPERTS, synth.MOE_D_MODEL, synth.MOE_D_EXPERT,
+                  synth.MOE_D_SHARED, experts_needed=ids.ravel().tolist(), hot_tokens=8)
+    X = synth.gen_x(synth.rng("moe_512x10", 0, "X", T), T, synth.MOE_D_MODEL)
+    counts = np.bincount(ids.ravel(), minlength=synth.MOE_EXPERTS)
+    assert (counts >= 8).sum() >= 5
+    a = layer.run(X, ids, p, dbg=False)
+    layer.L.hot_tokens = 0
+    b = layer.run(X, ids, p, dbg=False)
+    sel = [0, 17, 40, 63]
+    ye, ae = oracle.moe_layer_ref(X[sel], ids[sel], p[sel], layer.W, layer.Wsh(), n_experts=layer.n,
+                                  with_scale=True)
+    assert oracle.tol_ratio(a["y"][sel], ye, ae) <= 1.0
+    assert oracle.tol_ratio(b["y"][sel], ye, ae) <= 1.0
+    assert not np.array_equal(a["y"], b["y"])   # the two paths did run
