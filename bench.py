@@ -44,8 +44,8 @@ def log(*a):
 KERNEL_SOURCES = {
     "k_gemv_q4": ["gemv.hip", "gemv_core.h", "q4nx_dev.h", "topk.h"],
     "k_gemv_q8": ["gemv.hip", "gemv_core.h", "q4nx_dev.h", "topk.h"],
-    "k_gemm_q4": ["gemm.hip", "gemm_args.h", "q4nx_dev.h"],
-    "k_moe": ["moe.hip", "moe_args.h", "gemv_core.h", "q4nx_dev.h"],
+    "k_gemm_q4": ["gemm.hip", "gemm_args.h", "mfma_q4.h", "q4nx_dev.h"],
+    "k_moe": ["moe.hip", "moe_args.h", "gemv_core.h", "mfma_q4.h", "q4nx_dev.h"],
     "k_router": ["router.hip", "q4nx_dev.h"],
     "k_step": ["step.hip", "plan_args.h", "gemv_core.h", "q4nx_dev.h"],
 }
