@@ -1179,6 +1179,197 @@ void k_moe_hot_dn(MoeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// decode-sized down projection and combine in one launch
+// ---------------------------------------------------------------------------
+// A workgroup owns 8 output rows (one slice of a tile row) for every token:
+// it computes d of those rows for every valid pair and for the shared expert,
+// then sums them per token in slot order, so d never goes through memory and
+// no second launch runs.  The arithmetic is that of k_moe_down_s and
+// k_moe_combine -- per row the same chunk split over ks waves, the same chunk
+// order, lane reduction, part order and slot order -- so the results are
+// those of the two-launch path bit for bit (a row's sum does not depend on how
+// many rows a lane holds).  With D / 8 workgroups every CU streams a share of
+// the selected experts' down rows.
+constexpr int kMoeDcSlices = 4;   // chunk slices a down task may hold (tile columns per wave)
+
+constexpr int kMoeDcWaves = 16;
+
+template <int KIND>
+__global__ __launch_bounds__(64 * kMoeDcWaves) void k_moe_down_c(MoeArgs a, int ks_r, int ks_s) {
+  extern __shared__ __attribute__((aligned(16))) uint32_t xl[];
+  __shared__ MoeSmallRoute rt;
+  __shared__ int32_t s_pos[kMoeSmallPairs];   // each pair's sorted position, -1 when invalid
+  __shared__ int32_t s_exp[kMoeSmallPairs];   // the expert of each valid sorted position
+  constexpr int CB = ChunkBytes<KIND>::value, W = kMoeDcWaves, NT = 64 * W;
+  moe_route_small(a, rt);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int P = a.T * a.k, T = a.T;
+  const int nseg = rt.nseg;
+  const int Pv = nseg ? rt.seg[nseg - 1][1] + rt.seg[nseg - 1][2] : 0;   // valid pairs sort first
+  const int TCr = a.De / 256, TCs = a.Ds / 256;
+  const int u = blockIdx.x, tr = u >> 2, i0 = u & 3;   // output rows 8u .. 8u + 7
+  const int NRr = Pv * TCr * 8, NR = NRr + T * TCs * 8;
+  float* sums = reinterpret_cast<float*>(xl + 16 * NR);
+  float* dpart = sums + 2 * NR;   // [task][8 rows]
+  const int n_r = Pv * ks_r, n_tasks = n_r + (a.Ds ? T * ks_s : 0);
+  for (int q = tid; q < P; q += NT) {
+    const int pr = rt.sorted[q];
+    s_pos[pr] = q < Pv ? q : -1;
+  }
+  if (tid < nseg)
+    for (int q = rt.seg[tid][1]; q < rt.seg[tid][1] + rt.seg[tid][2]; ++q) s_exp[q] = rt.seg[tid][0];
+  __syncthreads();
+
+  // A task: one wave's chunks [c0, c1) of one row (a valid pair's routed row,
+  // or a token's shared row), against that row's h records.
+  struct Task {
+    __amdgpu_buffer_rsrc_t rs;
+    int nc, c0, rbase, TC;
+  };
+  auto task = [&](int ti) {
+    Task tk;
+    const bool shared = ti >= n_r;
+    const int ks = shared ? ks_s : ks_r, TC = shared ? TCs : TCr;
+    const int idx = shared ? (ti - n_r) / ks_s : ti / ks_r, part = shared ? (ti - n_r) - idx * ks_s : ti - idx * ks_r;
+    const int c0 = part * TC / ks, c1 = (part + 1) * TC / ks;
+    const uint8_t* row = shared ? a.sdown : a.down + (size_t)s_exp[idx] * a.down_stride;
+    row += ((size_t)tr * TC + c0) * CB;
+    tk.rs = make_rsrc(row, (uint32_t)((c1 - c0) * CB));
+    tk.nc = c1 - c0;
+    tk.c0 = c0;
+    tk.rbase = shared ? NRr + idx * TCs * 8 : idx * TCr * 8;
+    tk.TC = TC;
+    return tk;
+  };
+  Q4Chunk<KIND, 1> ring[2][kMoeDcSlices];
+  auto load = [&](int b, const Task& tk) {
+#pragma unroll
+    for (int j = 0; j < kMoeDcSlices; ++j)
+      if (j < tk.nc) q4_load_rs<KIND, 1>(tk.rs, (uint32_t)(j * CB), lane, ring[b][j], i0);
+  };
+  const Q4Consts kc = q4_consts();
+  auto compute = [&](int b, const Task& tk, int ti) {
+    float acc[1][1] = {{0.f}};
+    const int g = lane & 7;
+#pragma unroll
+    for (int j = 0; j < kMoeDcSlices; ++j) {
+      if (j < tk.nc) {
+        const int r = tk.rbase + (tk.c0 + j) * 8 + g;
+        XRec<1> xp;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(xl + 16 * r + 4 * d);
+          xp.p[0][4 * d] = v.x;
+          xp.p[0][4 * d + 1] = v.y;
+          xp.p[0][4 * d + 2] = v.z;
+          xp.p[0][4 * d + 3] = v.w;
+        }
+        xp.f[0] = sums[2 * r];
+        xp.X[0] = sums[2 * r + 1];
+        q4_compute<KIND, 1, 1>(ring[b][j], xp, kc, acc);
+      }
+    }
+    q4_lane_reduce<1, 1>(acc);
+    if (g == 0) dpart[ti * 8 + (lane >> 3)] = acc[0][0];
+  };
+
+  // weights of the wave's first task first, then the h records of every row
+  int ti = wave;
+  Task cur;
+  if (ti < n_tasks) {
+    cur = task(ti);
+    load(0, cur);
+  }
+  // h records, four quarter records per thread per round: all four rounds'
+  // loads are issued before any is built (quarter records past 4 NR read a
+  // valid row again and are not stored)
+  auto hsrc = [&](int q4) {
+    const int r = min(q4 >> 2, NR - 1);
+    if (r < NRr) {
+      const int q = r / (TCr * 8), rem = r - q * TCr * 8;
+      return a.hbuf + (size_t)q * a.hstride + 32 * rem + 8 * (q4 & 3);
+    }
+    const int r2 = r - NRr, t = r2 / (TCs * 8), rem = r2 - t * TCs * 8;
+    return a.hbuf + (size_t)(P + t) * a.hstride + 32 * rem + 8 * (q4 & 3);
+  };
+  constexpr int HB = 4;
+  for (int q0 = tid; q0 < 4 * NR; q0 += NT * HB) {
+    f32x4 va[HB], vb[HB];
+#pragma unroll
+    for (int i = 0; i < HB; ++i) {
+      const float* src = hsrc(q0 + NT * i);
+      va[i] = *reinterpret_cast<const f32x4*>(src);
+      vb[i] = *reinterpret_cast<const f32x4*>(src + 4);
+    }
+#pragma unroll
+    for (int i = 0; i < HB; ++i) {
+      const int q4 = q0 + NT * i, r = q4 >> 2;
+      if (r < NR) {
+        uint32_t pr[4];
+        float f, X;
+        h_record_part(va[i], vb[i], pr, f, X);
+        *reinterpret_cast<u32x4*>(xl + 16 * r + 4 * (q4 & 3)) = u32x4{pr[0], pr[1], pr[2], pr[3]};
+        if ((q4 & 3) == 0) {
+          sums[2 * r] = f;
+          sums[2 * r + 1] = X;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  // the wave's tasks, the next one's chunks loaded while the current one runs
+  while (ti < n_tasks) {
+    Task nxt;
+    const bool more = ti + W < n_tasks;
+    if (more) {
+      nxt = task(ti + W);
+      load(1, nxt);
+    }
+    compute(0, cur, ti);
+    ti += W;
+    if (!more) break;
+    cur = nxt;
+    const bool more2 = ti + W < n_tasks;
+    if (more2) {
+      nxt = task(ti + W);
+      load(0, nxt);
+    }
+    compute(1, cur, ti);
+    ti += W;
+    if (!more2) break;
+    cur = nxt;
+  }
+  __syncthreads();
+  // y[t][row] = sum_j p[t][j] d[t][j][row] in slot order, then + the shared d
+  for (int idx = tid; idx < T * 8; idx += NT) {
+    const int t = idx >> 3, r = idx & 7, col = 8 * u + r;
+    float y = 0.f;
+    for (int j = 0; j < a.k; ++j) {
+      const int pair = t * a.k + j;
+      const int e = a.ids[pair];
+      const int pos = s_pos[pair];
+      const bool ok = e >= 0 && e < a.n_experts && pos >= 0;
+      float dj = 0.f;
+      if (ok) {
+        float v = 0.f;
+        for (int p2 = 0; p2 < ks_r; ++p2) v += dpart[(pos * ks_r + p2) * 8 + r];
+        dj = v;
+        y = fmaf(a.p[pair], dj, y);
+      }
+      if (a.dbg_d) a.dbg_d[(size_t)pair * a.D + col] = dj;
+    }
+    if (a.Ds) {
+      float ds = 0.f;
+      for (int p2 = 0; p2 < ks_s; ++p2) ds += dpart[(n_r + t * ks_s + p2) * 8 + r];
+      y += ds;
+      if (a.dbg_d_shared) a.dbg_d_shared[(size_t)t * a.D + col] = ds;
+    }
+    a.Y[(size_t)t * a.D + col] = y;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // combine
 // ---------------------------------------------------------------------------
 // Every load of a thread is issued before the first product: ids, weights and
@@ -1250,6 +1441,19 @@ static hipError_t moe_run(const MoeArgs& a, hipStream_t s) {
     const int dn_items = nseg_max * (rows / (dn_waves / ks_r)) + (a.Ds ? rows / (dn_waves / ks_s) : 0);
     const dim3 g_gu(gu_items < 4096 ? gu_items : 4096), g_dn(dn_items < 4096 ? dn_items : 4096);
     hipLaunchKernelGGL((k_moe_gateup_s<KIND, TB, true>), g_gu, dim3(256), xl_gu, s, a);
+    // down and combine in one launch when every row's h records fit in LDS and
+    // a wave's run of a row is at most kMoeDcSlices chunks
+    const int dc_rec = (P * tcr + (a.Ds ? a.T * tcs : 0)) * 8;
+    const int dc_bytes = dc_rec * 72 + (P * ks_r + (a.Ds ? a.T * ks_s : 0)) * 8 * 4;
+    const bool dc = dc_bytes <= 131072 && (tcr + ks_r - 1) / ks_r <= kMoeDcSlices &&
+                    (tcs + ks_s - 1) / ks_s <= kMoeDcSlices;
+    if (dc) {
+      if (dc_bytes > 65536)
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_moe_down_c<KIND>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, dc_bytes);
+      hipLaunchKernelGGL((k_moe_down_c<KIND>), dim3(a.D / 8), dim3(64 * kMoeDcWaves), dc_bytes, s, a, ks_r, ks_s);
+      return hipGetLastError();
+    }
     if (dn_waves == 2)
       hipLaunchKernelGGL((k_moe_down_s<KIND, TB, true, 2>), g_dn, dim3(128), xl_dn, s, a, ks_r, ks_s);
     else
