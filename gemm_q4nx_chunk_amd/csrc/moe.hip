@@ -538,6 +538,36 @@ __device__ __forceinline__ void moe_chunks(const Q4Chunk<KIND> (&ch)[CPW], int n
   }
 }
 
+// The same for units of 8 SL rows (slices i0 .. i0 + SL - 1 of every chunk):
+// a row's arithmetic does not depend on how many rows a lane holds.
+template <int KIND, int TB, int CPW, int SL>
+__device__ __forceinline__ void moe_chunks_sl(const Q4Chunk<KIND, SL> (&ch)[CPW], int nc, int c0, int TC,
+                                              const uint32_t* xl, const Q4Consts& k, float (&acc)[SL][TB]) {
+  const int R = TB * TC * 8, g = threadIdx.x & 7;
+  const float* sums = reinterpret_cast<const float*>(xl + 16 * R);
+#pragma unroll
+  for (int j = 0; j < CPW; ++j) {
+    if (j < nc) {
+      XRec<TB> xp;
+#pragma unroll
+      for (int m = 0; m < TB; ++m) {
+        const int r = (m * TC + c0 + j) * 8 + g;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(xl + 16 * r + 4 * d);
+          xp.p[m][4 * d] = v.x;
+          xp.p[m][4 * d + 1] = v.y;
+          xp.p[m][4 * d + 2] = v.z;
+          xp.p[m][4 * d + 3] = v.w;
+        }
+        xp.f[m] = sums[2 * r];
+        xp.X[m] = sums[2 * r + 1];
+      }
+      q4_compute<KIND, TB, SL>(ch[j], xp, k, acc);
+    }
+  }
+}
+
 template <int KIND, int CPW>
 __device__ __forceinline__ void moe_load(const uint8_t* row, int c0, int nc, int lane,
                                          Q4Chunk<KIND> (&ch)[CPW]) {
@@ -564,14 +594,17 @@ __device__ __forceinline__ int moe_sorted(const MoeArgs& a, const MoeSmallRoute&
   else return a.sorted[pos];
 }
 
-// Items: nseg * (De / 32) routed tile rows, then Ds / 32 shared ones.  Waves
-// 0-1 take the gate row, 2-3 the up row, each half of the row's chunks.
-template <int KIND, int TB, bool SMALL>
+// Items: nseg * (De / 32) routed tile rows, then Ds / 32 shared ones, each cut
+// into 4 / SL units of 8 SL rows (more, smaller workgroups for a launch bound
+// by each CU's share of the bytes).  Waves 0-1 take the gate rows, 2-3 the up
+// rows, each half of the row's chunks.
+template <int KIND, int TB, bool SMALL, int SL>
 __global__ __launch_bounds__(256) void k_moe_gateup_s(MoeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint32_t xl[];
-  __shared__ float red[4][32][TB];
+  __shared__ float red[4][8 * SL][TB];
   __shared__ int64_t s_rows[TB];   // the batch's activation rows (element offsets)
   __shared__ MoeSmallRoute rt;
+  constexpr int PARTS = 4 / SL, CB = ChunkBytes<KIND>::value;
   if constexpr (SMALL) {
     moe_route_small(a, rt);
     if (blockIdx.x == 0 && threadIdx.x == 0) a.hdr[0] = (uint32_t)rt.bad;
@@ -580,25 +613,32 @@ __global__ __launch_bounds__(256) void k_moe_gateup_s(MoeArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int TC = a.D / 256, P = a.T * a.k;
   const int rows_r = a.De / 32, rows_s = a.Ds / 32;
-  const int n_items = nseg * rows_r + rows_s;
+  const int n_items = (nseg * rows_r + rows_s) * PARTS;
   const Q4Consts kc = q4_consts();
   const int half = wave & 1;
   const int c0 = half * TC / 2, nc = (half + 1) * TC / 2 - c0;
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-    const bool shared = item >= nseg * rows_r;
+    const int unit = item / PARTS, i0 = SL * (item - unit * PARTS);
+    const bool shared = unit >= nseg * rows_r;
     int e = 0, start = 0, cnt = a.T, tr;
     if (!shared) {
-      const int u = item / rows_r;
-      tr = item - u * rows_r;
+      const int u = unit / rows_r;
+      tr = unit - u * rows_r;
       moe_seg<SMALL>(a, rt, u, e, start, cnt);
     } else {
-      tr = item - nseg * rows_r;
+      tr = unit - nseg * rows_r;
     }
     const uint8_t* w = shared ? (wave < 2 ? a.sgate : a.sup)
                               : (wave < 2 ? a.gate + (size_t)e * a.gate_stride : a.up + (size_t)e * a.up_stride);
-    const uint8_t* row = w + (size_t)tr * TC * ChunkBytes<KIND>::value;
+    const __amdgpu_buffer_rsrc_t wrs =
+        make_rsrc(w + ((size_t)tr * TC + c0) * CB, (uint32_t)(nc * CB));
     constexpr int CPW = kMoeCpwGateUp;
-    Q4Chunk<KIND> ch[CPW];
+    Q4Chunk<KIND, SL> ch[CPW];
+    auto load = [&](int r0) {
+#pragma unroll
+      for (int j = 0; j < CPW; ++j)
+        if (r0 + j < nc) q4_load_rs<KIND, SL>(wrs, (uint32_t)((r0 + j) * CB), lane, ch[j], i0);
+    };
     for (int b0 = 0; b0 < cnt; b0 += TB) {
       const int ntok = min(TB, cnt - b0);
       if (threadIdx.x < TB) {
@@ -606,35 +646,35 @@ __global__ __launch_bounds__(256) void k_moe_gateup_s(MoeArgs a) {
         const int t = shared ? b0 + mm : moe_sorted<SMALL>(a, rt, start + b0 + mm) / a.k;
         s_rows[threadIdx.x] = (int64_t)t * a.D;
       }
-      float acc[4][TB];
+      float acc[SL][TB];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < SL; ++i)
 #pragma unroll
         for (int m = 0; m < TB; ++m) acc[i][m] = 0.f;
       // weights first (held across batches when the wave's run fits), then this batch's rows
-      if (b0 == 0 && nc <= CPW) moe_load<KIND, CPW>(row, c0, nc, lane, ch);
+      if (b0 == 0 && nc <= CPW) load(0);
       __syncthreads();
       moe_stage<TB>(a.X, s_rows, TC, xl);
       __syncthreads();
       for (int r0 = 0; r0 < nc; r0 += CPW) {
-        if (nc > CPW) moe_load<KIND, CPW>(row, c0 + r0, min(CPW, nc - r0), lane, ch);
-        moe_chunks<KIND, TB, CPW>(ch, min(CPW, nc - r0), c0 + r0, TC, xl, kc, acc);
+        if (nc > CPW) load(r0);
+        moe_chunks_sl<KIND, TB, CPW, SL>(ch, min(CPW, nc - r0), c0 + r0, TC, xl, kc, acc);
       }
-      q4_lane_reduce<TB>(acc);
+      q4_lane_reduce<TB, SL>(acc);
       if ((lane & 7) == 0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < SL; ++i)
 #pragma unroll
           for (int m = 0; m < TB; ++m) red[wave][8 * i + (lane >> 3)][m] = acc[i][m];
       }
       __syncthreads();
-      for (int idx = threadIdx.x; idx < 32 * TB; idx += 256) {
+      for (int idx = threadIdx.x; idx < 8 * SL * TB; idx += 256) {
         const int r = idx / TB, m = idx - r * TB;
         if (m < ntok) {
           const float g = red[0][r][m] + red[1][r][m];
           const float u = red[2][r][m] + red[3][r][m];
           const float hv = g / (1.0f + expf(-g)) * u;
-          const int col = 32 * tr + r;
+          const int col = 32 * tr + 8 * i0 + r;
           const int pos = shared ? P + b0 + m : start + b0 + m;
           a.hbuf[(size_t)pos * a.hstride + col] = hv;
           if (shared) {
@@ -1434,13 +1474,14 @@ static hipError_t moe_run(const MoeArgs& a, hipStream_t s) {
   const int xl_dn = kMoeRecDown * TB * ((a.De > a.Ds ? a.De : a.Ds) / 256);
   const bool small = P <= kMoeSmallPairs;
   if (small && xl_gu <= 65536 && xl_dn <= 65536) {
-    const int gu_items = nseg_max * (a.De / 32) + a.Ds / 32;
+    constexpr int kGuSl = 1;   // 8-row units: four workgroups per gate/up tile row
+    const int gu_items = (nseg_max * (a.De / 32) + a.Ds / 32) * (4 / kGuSl);
     // decode-sized down: two-wave workgroups when a tile row takes at most two waves
     // (more, smaller workgroups for a latency-bound launch), else four
     const int dn_waves = (ks_r <= 2 && ks_s <= 2) ? 2 : 4;
     const int dn_items = nseg_max * (rows / (dn_waves / ks_r)) + (a.Ds ? rows / (dn_waves / ks_s) : 0);
     const dim3 g_gu(gu_items < 4096 ? gu_items : 4096), g_dn(dn_items < 4096 ? dn_items : 4096);
-    hipLaunchKernelGGL((k_moe_gateup_s<KIND, TB, true>), g_gu, dim3(256), xl_gu, s, a);
+    hipLaunchKernelGGL((k_moe_gateup_s<KIND, TB, true, kGuSl>), g_gu, dim3(256), xl_gu, s, a);
     // down and combine in one launch when every row's h records fit in LDS and
     // a wave's run of a row is at most kMoeDcSlices chunks
     const int dc_rec = (P * tcr + (a.Ds ? a.T * tcs : 0)) * 8;
