@@ -234,6 +234,24 @@ def test_verify_window_slot_invariance(kind, layout, M):
     np.testing.assert_array_equal(yp.view(np.uint32), y[perm].view(np.uint32))
 
 
+@pytest.mark.parametrize("kind", ["q4_1", "q4_k"])
+@pytest.mark.parametrize("N,K,M", [(64, 14336, 2), (64, 14336, 4), (96, 7424, 3), (32, 40960, 1), (160, 3328, 8)])
+def test_long_activation_rows(kind, N, K, M):
+    """Activation rows too long for one register load per thread (several
+    rows, long K, odd tile-column counts, 4- and 16-wave workgroups): against
+    the oracle, and a permutation of the rows of x permutes the rows of y bit
+    for bit."""
+    ch = _gen(kind, None, N, K, "longrows")
+    d = dev_u8(ch)
+    x = synth.gen_x(synth.rng("gpu-gemv", "longrows", kind, N, K, M), M, K)
+    y = gemv(d, N, K, kind, x)
+    _check(y, ch, kind, N, K, x, None)
+    if M > 1:
+        perm = np.roll(np.arange(M), 1)
+        yp = gemv(d, N, K, kind, x[perm])
+        np.testing.assert_array_equal(yp.view(np.uint32), y[perm].view(np.uint32))
+
+
 @pytest.mark.parametrize("M", [1, 2])
 def test_batched_at_the_job_limit(M):
     """64 jobs in one call (the API's limit), all three kinds and both Q8 layouts
