@@ -116,12 +116,27 @@ int pow2_at_least(int v, int cap) {
 #define Q4NX_ROWSPLIT4_TR 0
 #endif
 
-int pick_waves(int64_t total_tr, int M, int max_tc) {
+// Three or four activation rows (q4 kinds): 4-wave workgroups hold their
+// 168-235 registers three or two to a CU, so a launch of long K (at least
+// Q4NX_MID_MIN_TC tile columns) or of few tile rows (at most Q4NX_MID_MAX_TR)
+// would leave a wave alone on its SIMD with a long run of chunks; 8-wave
+// workgroups split K eight ways instead.
+#ifndef Q4NX_MID_MIN_TC
+#define Q4NX_MID_MIN_TC 17
+#endif
+#ifndef Q4NX_MID_MAX_TR
+#define Q4NX_MID_MAX_TR 0
+#endif
+
+int pick_waves(int kind, int64_t total_tr, int M, int max_tc) {
+  const bool q4 = kind == q4nx::KIND_Q4_1 || kind == q4nx::KIND_Q4_K;
+  if (q4 && (M == 3 || M == 4) && (max_tc >= Q4NX_MID_MIN_TC || total_tr <= Q4NX_MID_MAX_TR)) return 8;
   return (total_tr >= Q4NX_SMALL_ROWS || M > 2 || max_tc < Q4NX_SMALL_MIN_TC) ? 4 : 16;
 }
 
 int pick_ks(int waves, int64_t total_tr, int TC) {
   if (waves == 16) return pow2_at_least((TC + Q4NX_SMALL_CPW - 1) / Q4NX_SMALL_CPW, 16);
+  if (waves == 8) return pow2_at_least((TC + Q4NX_SMALL_CPW - 1) / Q4NX_SMALL_CPW, 8);
   int ks = total_tr >= 2048 ? 1 : (total_tr >= 1024 ? 2 : 4);
   const int lim = TC >= 4 ? 4 : (TC >= 2 ? 2 : 1);
   return ks < lim ? ks : lim;
@@ -134,8 +149,12 @@ struct BatchShape {
 
 BatchShape batch_shape(int kind, int64_t total_tr, int max_tc, int M) {
   BatchShape sh;
-  sh.waves = pick_waves(total_tr, M, max_tc);
+  sh.waves = pick_waves(kind, total_tr, M, max_tc);
   sh.xl = q4nx::gemv_xl_bytes(kind, M, sh.waves, max_tc);
+  if (sh.waves == 8 && sh.xl <= 0) {   // the 8-wave kernel stages its activations in LDS
+    sh.waves = 4;
+    sh.xl = q4nx::gemv_xl_bytes(kind, M, 4, max_tc);
+  }
   const bool q4 = kind == q4nx::KIND_Q4_1 || kind == q4nx::KIND_Q4_K;
   sh.parts = !(q4 && sh.xl > 0) ? 1 : total_tr <= Q4NX_ROWSPLIT4_TR ? 4 : total_tr <= Q4NX_ROWSPLIT_TR ? 2 : 1;
   return sh;

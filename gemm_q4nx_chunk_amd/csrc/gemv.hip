@@ -147,9 +147,18 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_q4x(const GemvBatch b) {
   };
 #pragma unroll
   for (int i = 0; i < XRP; ++i) put(tid + NT * i, xr[i]);
-  // long-K launches: the parts past the first XRP per thread, loaded and built in turn
-  for (int q = tid + NT * XRP; q < 4 * R; q += NT)
-    put(q, __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs, xpart_off(q), 0, 0)));
+  // long-K launches: the parts past the first XRP per thread, loaded and built
+  // in turn; NS at a time for three or more rows (whose staging is long enough
+  // for the round trips to add up; at one or two rows the registers cost more)
+  constexpr int NS = M >= 3 ? 4 : 1;
+  for (int q0 = tid + NT * XRP; q0 < 4 * R; q0 += NS * NT) {
+    u32x4 v[NS];
+#pragma unroll
+    for (int i = 0; i < NS; ++i)
+      v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs, xpart_off(q0 + NT * i), 0, 0));
+#pragma unroll
+    for (int i = 0; i < NS; ++i) put(q0 + NT * i, v[i]);
+  }
   __syncthreads();
 
   const Q4Consts k = q4_consts();
@@ -646,7 +655,16 @@ int gemv_xl_bytes(int kind, int M, int waves, int max_tc) {
   }
   if (kind != KIND_Q4_1 && kind != KIND_Q4_K) return 0;
   const int bytes = M * max_tc * 8 * 72;
-  return bytes <= (waves == 4 ? gemv_lds_budget() : 65536) ? bytes : 0;
+  return bytes <= (waves <= 8 ? gemv_lds_budget() : 65536) ? bytes : 0;
+}
+
+// Eight-wave workgroups (two waves per SIMD, up to 256 registers): q4 kinds
+// at M = 3 and 4.
+template <int KIND>
+static hipError_t launch_mid(int M, const GemvBatch& b, int n_wg, int xl, hipStream_t s) {
+  if (M == 3) return launch_one<KIND, 3, 8>(b, n_wg, xl, s);
+  if (M == 4) return launch_one<KIND, 4, 8>(b, n_wg, xl, s);
+  return hipErrorInvalidValue;
 }
 
 // 16-wave workgroups hold at most 128 registers per lane, so they are used
@@ -654,6 +672,10 @@ int gemv_xl_bytes(int kind, int M, int waves, int max_tc) {
 hipError_t launch_gemv(int kind, int M, int waves, const GemvBatch& b, int n_wg, int xl_bytes,
                        hipStream_t s) {
   if (waves == 4) return launch_w<4>(kind, M, b, n_wg, xl_bytes, s);
+  if (waves == 8 && xl_bytes > 0) {
+    if (kind == KIND_Q4_1) return launch_mid<KIND_Q4_1>(M, b, n_wg, xl_bytes, s);
+    if (kind == KIND_Q4_K) return launch_mid<KIND_Q4_K>(M, b, n_wg, xl_bytes, s);
+  }
   if (waves == 16 && M <= 2) {
     switch (kind) {
       case KIND_Q4_1: return launch_small<KIND_Q4_1>(M, b, n_wg, xl_bytes, s);

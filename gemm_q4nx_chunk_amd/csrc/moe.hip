@@ -473,17 +473,35 @@ __device__ __forceinline__ void moe_stage(const uint16_t* base, const int64_t* r
   const int R = TB * TC * 8;
   float* sums = reinterpret_cast<float*>(xl + 16 * R);
   // four consecutive lanes per record (blockDim is a multiple of 4, so a
-  // record's lanes run each iteration together); part d = q & 3 takes 8 values
-  for (int q = threadIdx.x; q < 4 * R; q += blockDim.x) {
-    const int r = q >> 2, m = r / (TC * 8), rem = r - m * TC * 8;
-    const u32x4 v = load16(base + rows[m] + 32 * rem + 8 * (q & 3));
-    uint32_t pr[4];
-    float f, X;
-    x_record_part(v, pr, f, X);
-    *reinterpret_cast<u32x4*>(xl + 16 * r + 4 * (q & 3)) = u32x4{pr[0], pr[1], pr[2], pr[3]};
-    if ((q & 3) == 0) {
-      sums[2 * r] = f;
-      sums[2 * r + 1] = X;
+  // record's lanes run each iteration together); part d = q & 3 takes 8 values.
+  // A thread's parts are loaded NB at a time and then built, so the staging
+  // waits for one round trip per NB parts rather than one per part (one row of
+  // d_model 2048 is one part per thread of 256).
+  constexpr int NB = TB < 4 ? TB : 4;
+  for (int q0 = threadIdx.x; q0 < 4 * R; q0 += NB * blockDim.x) {
+    u32x4 v[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int q = q0 + i * blockDim.x;
+      if (q < 4 * R) {
+        const int r = q >> 2, m = r / (TC * 8), rem = r - m * TC * 8;
+        v[i] = load16(base + rows[m] + 32 * rem + 8 * (q & 3));
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int q = q0 + i * blockDim.x;
+      if (q < 4 * R) {   // whole quads alike: 4 R and blockDim are multiples of 4
+        const int r = q >> 2;
+        uint32_t pr[4];
+        float f, X;
+        x_record_part(v[i], pr, f, X);
+        *reinterpret_cast<u32x4*>(xl + 16 * r + 4 * (q & 3)) = u32x4{pr[0], pr[1], pr[2], pr[3]};
+        if ((q & 3) == 0) {
+          sums[2 * r] = f;
+          sums[2 * r + 1] = X;
+        }
+      }
     }
   }
 }
