@@ -274,6 +274,27 @@ def test_batched_at_the_job_limit(M):
         _check(host(y), ch, kind, N, K, x, lay)
 
 
+@pytest.mark.parametrize("kind", ["q4_1", "q4_k"])
+@pytest.mark.parametrize("M", [1, 2, 4])
+def test_launch_of_several_rounds(kind, M):
+    """A launch of more workgroups than the CUs hold at once (the 28672 x 4096
+    gate|up of an 8B layer): sampled tile rows against the oracle, and its
+    first 256 tile rows bit for bit against the same rows as a launch that
+    fits in one round (the same K split and chunk order)."""
+    N, K = 28672, 4096
+    g = synth.rng("gpu-gemv", "upw", kind)
+    ch = synth.gen_q4_1(g, N, K, zero="normal") if kind == "q4_1" else synth.gen_q4_k(g, N, K)
+    x = synth.gen_x(synth.rng("gpu-gemv", "upw-x", kind, M), M, K)
+    y = gemv(dev_u8(ch), N, K, kind, x)
+    tr = np.unique(_sampled_rows(N, 31 + M) // 32)
+    W = oracle.weights_exact(ch[tr], kind, 32 * len(tr), K)
+    yr, a = oracle.gemv_ref(W, x)
+    ysub = np.concatenate([y[:, 32 * t:32 * t + 32] for t in tr], axis=1)
+    assert oracle.tol_ratio(ysub, yr, a) <= 1.0
+    part = gemv(dev_u8(np.ascontiguousarray(ch[:256])), 8192, K, kind, x)
+    np.testing.assert_array_equal(part.view(np.uint32), y[:, :8192].view(np.uint32))
+
+
 @pytest.mark.parametrize("N,M", [(151936, 1), (151936, 2), (40960, 1), (40960, 3)])
 def test_q4k_whole_tile_launches_sampled(N, M):
     """Q4_K launches of more than 1024 tile rows (whole-tile units, metadata
