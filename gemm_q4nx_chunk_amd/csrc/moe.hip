@@ -527,33 +527,37 @@ __device__ __forceinline__ void moe_stage_h(const float* base, const int64_t* ro
   }
 }
 
+// acc += one held chunk (tile column c) against the staged rows.
+template <int KIND, int TB>
+__device__ __forceinline__ void moe_chunk(const Q4Chunk<KIND>& ch, int c, int TC, const uint32_t* xl,
+                                          const Q4Consts& k, float (&acc)[4][TB]) {
+  const int R = TB * TC * 8, g = threadIdx.x & 7;
+  const float* sums = reinterpret_cast<const float*>(xl + 16 * R);
+  XRec<TB> xp;
+#pragma unroll
+  for (int m = 0; m < TB; ++m) {
+    const int r = (m * TC + c) * 8 + g;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(xl + 16 * r + 4 * d);
+      xp.p[m][4 * d] = v.x;
+      xp.p[m][4 * d + 1] = v.y;
+      xp.p[m][4 * d + 2] = v.z;
+      xp.p[m][4 * d + 3] = v.w;
+    }
+    xp.f[m] = sums[2 * r];
+    xp.X[m] = sums[2 * r + 1];
+  }
+  q4_compute<KIND, TB>(ch, xp, k, acc);
+}
+
 // acc += the held chunks [0, nc) (tile columns c0 + j) against the staged rows.
 template <int KIND, int TB, int CPW>
 __device__ __forceinline__ void moe_chunks(const Q4Chunk<KIND> (&ch)[CPW], int nc, int c0, int TC,
                                            const uint32_t* xl, const Q4Consts& k, float (&acc)[4][TB]) {
-  const int R = TB * TC * 8, g = threadIdx.x & 7;
-  const float* sums = reinterpret_cast<const float*>(xl + 16 * R);
 #pragma unroll
-  for (int j = 0; j < CPW; ++j) {
-    if (j < nc) {
-      XRec<TB> xp;
-#pragma unroll
-      for (int m = 0; m < TB; ++m) {
-        const int r = (m * TC + c0 + j) * 8 + g;
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const u32x4 v = *reinterpret_cast<const u32x4*>(xl + 16 * r + 4 * d);
-          xp.p[m][4 * d] = v.x;
-          xp.p[m][4 * d + 1] = v.y;
-          xp.p[m][4 * d + 2] = v.z;
-          xp.p[m][4 * d + 3] = v.w;
-        }
-        xp.f[m] = sums[2 * r];
-        xp.X[m] = sums[2 * r + 1];
-      }
-      q4_compute<KIND, TB>(ch[j], xp, k, acc);
-    }
-  }
+  for (int j = 0; j < CPW; ++j)
+    if (j < nc) moe_chunk<KIND, TB>(ch[j], c0 + j, TC, xl, k, acc);
 }
 
 // The same for units of 8 SL rows (slices i0 .. i0 + SL - 1 of every chunk):
@@ -817,7 +821,7 @@ __global__ __launch_bounds__(256) void k_moe_gateup(MoeArgs a) {
     if (!moe_item<TB>(a, nbr, item, rows_r, rows_s, 1, 1, false, it)) break;
     const uint8_t* row = (wave < 2 ? it.w0 : it.w1) + (size_t)it.tr * TC * ChunkBytes<KIND>::value;
     Q4Chunk<KIND> ch[CPW];
-    if (nc <= CPW) moe_load<KIND, CPW>(row, c0, nc, lane, ch);   // weights first
+    moe_load<KIND, CPW>(row, c0, min(CPW, nc), lane, ch);   // weights first: the first CPW chunks
     if (threadIdx.x < TB) s_rows[threadIdx.x] = (int64_t)moe_item_tok(a, it, threadIdx.x) * a.D;
     float acc[4][TB];
 #pragma unroll
@@ -827,9 +831,17 @@ __global__ __launch_bounds__(256) void k_moe_gateup(MoeArgs a) {
     __syncthreads();
     moe_stage<TB>(a.X, s_rows, TC, xl);
     __syncthreads();
-    for (int r0 = 0; r0 < nc; r0 += CPW) {
-      if (nc > CPW) moe_load<KIND, CPW>(row, c0 + r0, min(CPW, nc - r0), lane, ch);
-      moe_chunks<KIND, TB, CPW>(ch, min(CPW, nc - r0), c0 + r0, TC, xl, kc, acc);
+    // a ring of CPW slots: chunk j in slot j % CPW, and once its products are
+    // done, chunk j + CPW is issued into the slot (same chunk order as ever)
+    for (int j0 = 0; j0 < nc; j0 += CPW) {
+#pragma unroll
+      for (int jj = 0; jj < CPW; ++jj) {
+        const int j = j0 + jj;
+        if (j < nc) {
+          moe_chunk<KIND, TB>(ch[jj], c0 + j, TC, xl, kc, acc);
+          if (j + CPW < nc) q4_load<KIND>(row + (size_t)(c0 + j + CPW) * ChunkBytes<KIND>::value, lane, ch[jj]);
+        }
+      }
     }
     q4_lane_reduce<TB>(acc);
     if ((lane & 7) == 0) {
