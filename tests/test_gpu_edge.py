@@ -85,6 +85,22 @@ def test_gemv_sparse_rows(center, N, K, M):
     assert r <= 1.0, r
 
 
+@pytest.mark.parametrize("center", [8, 0])
+@pytest.mark.parametrize("M", [1, 3, 4])
+def test_gemv_sparse_rows_long_k(center, M):
+    """The same rows at the 4B step's down projection (38 tile columns: 16-wave
+    workgroups at M = 1, 8-wave ones at M = 3 and 4)."""
+    N, K = FULL_K
+    g = synth.rng("gpu-edge", "sparse-long", center, M)
+    rows = list(range(0, N, 7))
+    ch, cols = _sparse_q4_1(g, N, K, center, rows)
+    x = _x_spread(g, M, K, cols)
+    y = gemv(dev_u8(ch), N, K, "q4_1", x)
+    yr, a = _ref(ch, "q4_1", N, K, x)
+    r = oracle.tol_ratio(y, yr, a)
+    assert r <= 1.0, r
+
+
 @pytest.mark.parametrize("M", [1, 64])
 def test_gemm_sparse_rows(M):
     N, K = 256, 1024
