@@ -631,8 +631,9 @@ static hipError_t launch_small(int M, const GemvBatch& b, int n_wg, int xl, hipS
   return hipErrorInvalidValue;
 }
 
-// Dynamic LDS a workgroup may take: the device's limit (160 KB on gfx950)
-// less the kernels' static arrays (at most 8 KB).
+// Dynamic LDS a 4-wave workgroup may take: the device's limit (160 KB on
+// gfx950) less the kernels' static arrays (at most 8 KB; see gemv_xl_bytes for
+// 8 and 16 waves).
 static int gemv_lds_budget() {
   static const int budget = [] {
     int dev = 0, v = 0;
@@ -655,7 +656,10 @@ int gemv_xl_bytes(int kind, int M, int waves, int max_tc) {
   }
   if (kind != KIND_Q4_1 && kind != KIND_Q4_K) return 0;
   const int bytes = M * max_tc * 8 * 72;
-  return bytes <= (waves <= 8 ? gemv_lds_budget() : 65536) ? bytes : 0;
+  // 8-wave workgroups keep up to 9 KB of static arrays (the reduction buffer
+  // and Q4_K's metadata slots at M = 4, whole tiles): 4 KB more held back
+  const int lim = waves == 4 ? gemv_lds_budget() : waves == 8 ? gemv_lds_budget() - 4096 : 65536;
+  return bytes <= lim ? bytes : 0;
 }
 
 // Eight-wave workgroups (two waves per SIMD, up to 256 registers): q4 kinds
