@@ -402,6 +402,9 @@ __device__ __forceinline__ bool moe_item(const MoeArgs& a, int nbr, int item, in
 // itself (one wave, rank by comparison) and no route kernel runs.
 
 constexpr int kMoeSmallPairs = 64;
+#ifndef Q4NX_MOE_SPLIT_SINGLE
+#define Q4NX_MOE_SPLIT_SINGLE 1
+#endif
 // Chunks a wave keeps in registers: gate/up waves hold half a d_model row
 // (4 chunks at d_model 2048), down waves one or two chunks.
 constexpr int kMoeCpwGateUp = 4;
@@ -802,8 +805,11 @@ __global__ __launch_bounds__(64 * WAVES) void k_moe_down_s(MoeArgs a, int ks_r, 
 
 // Waves 0-1 run the gate tile row, waves 2-3 the up tile row, each pair
 // splitting the D/256 chunks in two halves.
+// cls 0: every item; 1: only routed batches of one token (then TB = 1, whose
+// registers let twice the workgroups share a CU); 2: every item but those.
+// A token's arithmetic is the same in either kernel, so its bits are too.
 template <int KIND, int TB>
-__global__ __launch_bounds__(256) void k_moe_gateup(MoeArgs a) {
+__global__ __launch_bounds__(256) void k_moe_gateup(MoeArgs a, int cls) {
   extern __shared__ __attribute__((aligned(16))) uint32_t xl[];
   __shared__ float red[4][32][TB];
   __shared__ int64_t s_rows[TB];   // the batch's activation rows (element offsets)
@@ -818,7 +824,9 @@ __global__ __launch_bounds__(256) void k_moe_gateup(MoeArgs a) {
   const int nbr = (int)a.hdr[2];
   for (int item = blockIdx.x;; item += gridDim.x) {
     MoeItem it;
+    if (cls == 1 && item >= nbr * rows_r) break;   // the routed items come first
     if (!moe_item<TB>(a, nbr, item, rows_r, rows_s, 1, 1, false, it)) break;
+    if ((cls == 1 && it.ntok != 1) || (cls == 2 && !it.shared && it.ntok == 1)) continue;
     const uint8_t* row = (wave < 2 ? it.w0 : it.w1) + (size_t)it.tr * TC * ChunkBytes<KIND>::value;
     Q4Chunk<KIND> ch[CPW];
     moe_load<KIND, CPW>(row, c0, min(CPW, nc), lane, ch);   // weights first: the first CPW chunks
@@ -871,8 +879,9 @@ __global__ __launch_bounds__(256) void k_moe_gateup(MoeArgs a) {
 }
 
 // ks waves split one tile row's chunks; WAVES/ks tile rows per workgroup.
+// cls as in k_moe_gateup.
 template <int KIND, int TB, int WAVES>
-__global__ __launch_bounds__(64 * WAVES) void k_moe_down(MoeArgs a, int ks_r, int ks_s) {
+__global__ __launch_bounds__(64 * WAVES) void k_moe_down(MoeArgs a, int ks_r, int ks_s, int cls) {
   extern __shared__ __attribute__((aligned(16))) uint32_t xl[];
   __shared__ float red[WAVES][32][TB];
   __shared__ int64_t s_rows[TB];   // the batch's activation rows (element offsets)
@@ -883,7 +892,9 @@ __global__ __launch_bounds__(64 * WAVES) void k_moe_down(MoeArgs a, int ks_r, in
   const int nbr = (int)a.hdr[2];
   for (int item = blockIdx.x;; item += gridDim.x) {
     MoeItem it;
+    if (cls == 1 && item >= nbr * (rows / (WAVES / ks_r))) break;   // the routed items come first
     if (!moe_item<TB>(a, nbr, item, rows, rows, WAVES / ks_r, WAVES / ks_s, true, it)) break;
+    if ((cls == 1 && it.ntok != 1) || (cls == 2 && !it.shared && it.ntok == 1)) continue;
     const int ks = it.shared ? ks_s : ks_r, rpw = WAVES / ks;
     const int TC = (it.shared ? a.Ds : a.De) / 256;
     const int slot = wave / ks, part = wave % ks;
@@ -1539,16 +1550,30 @@ static hipError_t moe_run(const MoeArgs& a, hipStream_t s) {
   // on the matrix cores; one persistent workgroup per CU walks their items
   const bool hot = a.hot_min > 0;
   if (hot) hipLaunchKernelGGL((k_moe_hot_gu<KIND>), dim3(256), dim3(512), 0, s, a);
+  // Batches of several tokens and the shared expert at TB; with TB = 4, the
+  // batches of one token (most of a prompt block's experts) in a TB = 1 launch
+  // of their own first.
+  const bool split = TB > 1 && Q4NX_MOE_SPLIT_SINGLE;
   const int gu_items = nb_r * (a.De / 32) + nb_s * (a.Ds / 32);
+  if (split) {
+    const int gu1 = nb_r * (a.De / 32);
+    hipLaunchKernelGGL((k_moe_gateup<KIND, 1>), dim3(gu1 < 4096 ? gu1 : 4096), dim3(256),
+                       kMoeRecGateUp * (a.D / 256), s, a, 1);
+  }
   hipLaunchKernelGGL((k_moe_gateup<KIND, TB>), dim3(gu_items < 4096 ? gu_items : 4096), dim3(256),
-                     xl_gu, s, a);
+                     xl_gu, s, a, split ? 2 : 0);
   // prompt-block down: four-wave workgroups (two fit a CU at this register
   // count; eight-wave ones, one per CU, measured 20% slower)
   if (hot) hipLaunchKernelGGL((k_moe_hot_dn<KIND>), dim3(256), dim3(512), 0, s, a);
   constexpr int kDnWaves = 4;
   const int dn_items = nb_r * (rows / (kDnWaves / ks_r)) + nb_s * (rows / (kDnWaves / ks_s));
+  if (split) {
+    const int dn1 = nb_r * (rows / (kDnWaves / ks_r));
+    hipLaunchKernelGGL((k_moe_down<KIND, 1, kDnWaves>), dim3(dn1 < 4096 ? dn1 : 4096), dim3(64 * kDnWaves),
+                       kMoeRecDown * ((a.De > a.Ds ? a.De : a.Ds) / 256), s, a, ks_r, ks_s, 1);
+  }
   hipLaunchKernelGGL((k_moe_down<KIND, TB, kDnWaves>), dim3(dn_items < 4096 ? dn_items : 4096), dim3(64 * kDnWaves),
-                     xl_dn, s, a, ks_r, ks_s);
+                     xl_dn, s, a, ks_r, ks_s, split ? 2 : 0);
   hipLaunchKernelGGL(k_moe_combine, dim3((a.D + 255) / 256, a.T), dim3(256), 0, s, a);
   return hipGetLastError();
 }
