@@ -604,7 +604,9 @@ def moe_leg(steps, warmup, graph):
                         "distinct_experts_per_layer": uniq / L, "GB_s": nbytes / (ms * 1e-3) / 1e9,
                         "pct_hbm_peak": 100 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                         "TFLOP_s": flops / (ms * 1e-3) / 1e12,
-                        "launches": (3 if T * k <= 64 else 4) * L}
+                        # per layer: decode-sized gate/up, down + combine; or route, gate/up and
+                        # down for one-token batches then for the rest, combine
+                        "launches": (2 if T * k <= 64 else 6) * L}
         # tail skip: the picks ranked 7..10 dropped, the first six keep their weights
         # (no renormalisation); the layer outputs move by rel_l2 against all ten picks
         ks = 6
