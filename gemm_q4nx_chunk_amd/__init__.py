@@ -12,7 +12,9 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libq4nx.so")
+# Q4NX_LIB names another build of the same library (the host-sanitised one of
+# build.py --sanitize); by default the in-tree libq4nx.so.
+LIB_PATH = os.environ.get("Q4NX_LIB") or os.path.join(HERE, "libq4nx.so")
 
 Q4NX_OK, E_ARG, E_CHUNK_KIND, E_SHAPE, E_SHORT, E_ALIGN, E_WORKSPACE, E_Q8_LAYOUT, E_HIP = range(9)
 CHUNK_BYTES = {"q4_1": 5120, "q4_k": 4736, "q8": 8704}

@@ -55,5 +55,46 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# The host-sanitised library: api.hip (every argument check of the C ABI) with
+# its host code built under AddressSanitizer and UndefinedBehaviorSanitizer,
+# linked with the other objects of build().  The device code is untouched
+# (sanitisers are asked for the host side only).  Loading it needs the shared
+# ASan runtime preloaded (asan_runtime()) and Q4NX_LIB set to its path.
+SAN_DIR = os.path.join(OBJDIR, "asan")
+SAN_LIB = os.path.join(SAN_DIR, "libq4nx.so")
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def asan_runtime() -> str:
+    """Path of clang's shared ASan runtime next to hipcc (may not exist)."""
+    clang = os.path.join(os.path.dirname(os.path.realpath(_hipcc())), "..", "lib", "llvm", "bin", "clang")
+    if not os.path.exists(clang):
+        clang = "/opt/rocm/llvm/bin/clang"
+    res = subprocess.run([clang, "-print-resource-dir"], capture_output=True, text=True).stdout.strip()
+    return os.path.join(res, "lib", "linux", "libclang_rt.asan-x86_64.so")
+
+
+def build_sanitized() -> str:
+    """Build SAN_LIB (needs the objects of build()); returns its path."""
+    os.makedirs(SAN_DIR, exist_ok=True)
+    cc = _hipcc()
+    others = [os.path.join(OBJDIR, s.replace(".hip", ".o")) for s in SOURCES if s != "api.hip"]
+    missing = [o for o in others if not os.path.exists(o)]
+    if missing:
+        raise RuntimeError(f"run build() first: {missing[0]} is missing")
+    obj = os.path.join(SAN_DIR, "api.o")
+    _run([cc, *[f for f in FLAGS if f != "-O3"], "-O1", "-g", *SAN_FLAGS, "-c", os.path.join(CSRC, "api.hip"),
+          "-o", obj])
+    tmp = SAN_LIB + ".tmp"
+    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *SAN_FLAGS[:4], "-shared-libasan", "-o", tmp, obj,
+          *others])
+    os.replace(tmp, SAN_LIB)
+    return SAN_LIB
+
+
 if __name__ == "__main__":
-    print(build(verbose=True))
+    if "--sanitize" in sys.argv:
+        print(build_sanitized())
+    else:
+        print(build(verbose=True))
