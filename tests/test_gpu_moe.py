@@ -228,6 +228,36 @@ def test_token_result_does_not_depend_on_its_batch():
         np.testing.assert_array_equal(one["y"][0].view(np.uint32), full["y"][t].view(np.uint32))
 
 
+def _weights(g, T, k):
+    p = g.random((T, k)).astype(np.float32) + np.float32(0.05)
+    return (p / p.sum(axis=1, keepdims=True)).astype(np.float32)
+
+
+@pytest.mark.parametrize("kind", ["q4_1", "q4_k"])
+@pytest.mark.parametrize("per_expert", [1, 2])
+def test_block_of_one_or_two_tokens_per_expert(kind, per_expert):
+    """An 80-pair block (routed through the route kernel) where every expert is
+    picked by exactly one token (all routed batches in the one-token launch) or
+    by exactly two (none there): against the oracle stage by stage, and each
+    sampled token's bits equal to the same token routed alone."""
+    T, k = 20, 4
+    n = T * k // per_expert
+    layer = Layer(f"pertok{per_expert}", kind, n, 512, 256, 256)
+    g = synth.rng("gpu-moe", "per-expert", kind, per_expert)
+    if per_expert == 1:
+        ids = g.permutation(n).astype(np.int32).reshape(T, k)
+    else:   # tokens 2i and 2i + 1 share experts 4i .. 4i + 3
+        ids = np.array([[4 * (t // 2) + j for j in range(k)] for t in range(T)], np.int32)
+    p = _weights(g, T, k)
+    X = synth.gen_x(g, T, 512)
+    r = layer.run(X, ids, p)
+    assert r["err"] == 0
+    print(_check_stages(layer, X, ids, p, r))
+    for t in (0, 7, T - 1):
+        one = layer.run(X[t:t + 1], ids[t:t + 1], p[t:t + 1], dbg=False)
+        np.testing.assert_array_equal(one["y"][0].view(np.uint32), r["y"][t].view(np.uint32))
+
+
 def test_repeat_bit_identical():
     layer = Layer("rep", "q4_k", 16, 512, 256, 256)
     g = synth.rng("gpu-moe", "route-rep")
