@@ -622,14 +622,15 @@ def moe_leg(steps, warmup, graph):
                                           "rel_l2_vs_top10_mean": sum(rel) / L, "rel_l2_vs_top10_max": max(rel)}
         del ids6, ps6, y_full
         if T * k > 64:
-            # the same call with experts of 8 or more pairs (and the shared expert) on
-            # the bf16 matrix cores instead of the batched dot2 kernels
+            # the same call with experts of 5 or more pairs (and the shared expert) on
+            # the bf16 matrix cores instead of the batched dot2 kernels (the best
+            # threshold measured at this block; the library's default keeps them off)
             for l in range(L):
-                layers[l][0].hot_tokens = 8
+                layers[l][0].hot_tokens = 5
             ms_hot, _ = time_calls(run, steps, warmup, graph)
             for l in range(L):
                 layers[l][0].hot_tokens = 0
-            res[f"T{T}"]["matrix_core_8"] = {"ms_per_step": ms_hot, "GB_s": nbytes / (ms_hot * 1e-3) / 1e9}
+            res[f"T{T}"]["matrix_core_5"] = {"ms_per_step": ms_hot, "GB_s": nbytes / (ms_hot * 1e-3) / 1e9}
         # the router on the device in front of the layer (bf16 router rows 512 x 2048 per layer)
         Rs = [bf16_dev(synth.bf16_bits((synth.rng("moe_512x10", l, "R").standard_normal((E, D)) * 0.05)
                                        .astype(np.float32))) for l in range(L)]
