@@ -322,17 +322,18 @@ def test_matrix_core_experts(kind, hot):
     print(_check_stages(layer, X, ids, p, r))
 
 
-def test_matrix_core_experts_full_size_block():
-    """The 512-expert layer's 64-token block with experts of 8 or more pairs on
-    the matrix cores, and the same call with that path off: every sampled
+@pytest.mark.parametrize("hot", [5, 8])
+def test_matrix_core_experts_full_size_block(hot):
+    """The 512-expert layer's 64-token block with experts of `hot` or more pairs
+    on the matrix cores, and the same call with that path off: every sampled
     output within the bar of the oracle's scale."""
     T = 64
     ids, p = synth.moe_router(0, T)
     layer = Layer("full", "q4_1", synth.MOE_EXPERTS, synth.MOE_D_MODEL, synth.MOE_D_EXPERT,
-                  synth.MOE_D_SHARED, experts_needed=ids.ravel().tolist(), hot_tokens=8)
+                  synth.MOE_D_SHARED, experts_needed=ids.ravel().tolist(), hot_tokens=hot)
     X = synth.gen_x(synth.rng("moe_512x10", 0, "X", T), T, synth.MOE_D_MODEL)
     counts = np.bincount(ids.ravel(), minlength=synth.MOE_EXPERTS)
-    assert (counts >= 8).sum() >= 5
+    assert (counts >= hot).sum() >= 5
     a = layer.run(X, ids, p, dbg=False)
     layer.L.hot_tokens = 0
     b = layer.run(X, ids, p, dbg=False)
