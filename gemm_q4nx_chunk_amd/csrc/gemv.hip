@@ -94,8 +94,9 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_q4x(const GemvBatch b) {
   constexpr int UR = 8 * SL;          // output rows per unit
   extern __shared__ __attribute__((aligned(16))) uint32_t xl[];
   __shared__ float red[WAVES][UR][M];
-  constexpr bool kTurn = KIND == KIND_Q4_K;   // Q4_K metadata through an LDS slot per wave
-  __shared__ __attribute__((aligned(16))) uint8_t tsl[kTurn ? WAVES : 1][kTurn ? 160 * SL : 16];
+  constexpr bool kTurn = KIND == KIND_Q4_K;   // Q4_K metadata fetched whole, then handed out to the lanes
+  constexpr bool kSlot = kTurn && SL == 4;    // the hand-out at 4 slices goes through an LDS slot per wave
+  __shared__ __attribute__((aligned(16))) uint8_t tsl[kSlot ? WAVES : 1][kSlot ? 160 * SL : 16];
   const GemvJob J = gemv_job(b);
   const int ks = J.ks, rpw = WAVES / ks;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -169,7 +170,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_q4x(const GemvBatch b) {
     for (int m = 0; m < M; ++m) acc[i][m] = 0.f;
   auto step = [&](int j, int c) {
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (kTurn) q4k_turn<SL>(tsl[wave], lane, ring[j]);
+    if constexpr (kTurn) q4k_turn<SL>(tsl[kSlot ? wave : 0], lane, ring[j]);
     XRec<M> xp;
 #pragma unroll
     for (int m = 0; m < M; ++m) {

@@ -101,8 +101,7 @@ __device__ __forceinline__ void q4_load_rs(__amdgpu_buffer_rsrc_t rs, uint32_t o
 // Q4_K with the metadata fetched whole: the unit's (sc, mn) bytes (128 per
 // slice) as one load per lane, 2 SL bytes each, into meta[0..1], and its rows'
 // (S, M) pairs into rowsm[0] of lanes 0 .. 8 SL - 1: two small loads per chunk
-// instead of 2 SL.  q4k_turn hands each lane its own entries through a
-// per-wave LDS slot of 160 SL bytes.
+// instead of 2 SL.  q4k_turn then hands each lane its own entries.
 template <int SL>
 __device__ __forceinline__ void q4k_load_rs_whole(__amdgpu_buffer_rsrc_t rs, uint32_t off, int lane,
                                                   Q4Chunk<KIND_Q4_K, SL>& c, int i0) {
@@ -123,26 +122,54 @@ __device__ __forceinline__ void q4k_load_rs_whole(__amdgpu_buffer_rsrc_t rs, uin
   c.rowsm[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, off + 4608 + 32 * i0 + 4 * (lane & (8 * SL - 1)), 0, kNt);
 }
 
-// ts: the wave's slot.  Afterwards c holds, per slice i, the lane's (sc | mn << 8)
-// and its row's (S, M), as q4_load_rs leaves them.  The wave's LDS operations
-// run in order; the fences keep the compiler from moving them across each other.
+// Afterwards c holds, per slice i, the lane's (sc | mn << 8) and its row's
+// (S, M), as q4_load_rs leaves them.  Lane l's entry of slice i is the 2 bytes
+// at 128 i + 2 l of the unit's (sc, mn) region, its row's pair the one in
+// rowsm[0] of lane 8 i + l / 8.
+//   SL <= 2: ds_bpermute fetches both from the lanes that hold them (for
+//   SL = 2 the entry is in the upper half of lane 32 i + l / 2's word when l
+//   is odd; for one slice it is the lane's own): no LDS memory, no barrier.
+//   SL = 4: the lanes hold 8 bytes each, and one permute per slice would need
+//   two plus a select; instead the wave writes its loads to ts, its slot of
+//   160 SL bytes, and reads its entries back.  The wave's LDS operations run
+//   in order; the fences keep the compiler from moving them across each other.
+// The split follows measurement: at SL = 4 the slot was faster, at SL <= 2
+// the permutes.
 template <int SL>
 __device__ __forceinline__ void q4k_turn(uint8_t* ts, int lane, Q4Chunk<KIND_Q4_K, SL>& c) {
-  if constexpr (SL == 4) *reinterpret_cast<u32x2*>(ts + 8 * lane) = u32x2{c.meta[0], c.meta[1]};
-  else if constexpr (SL == 2) *reinterpret_cast<uint32_t*>(ts + 4 * lane) = c.meta[0];
-  else *reinterpret_cast<uint16_t*>(ts + 2 * lane) = (uint16_t)c.meta[0];
-  if (lane < 8 * SL) *reinterpret_cast<uint32_t*>(ts + 128 * SL + 4 * lane) = c.rowsm[0];
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  if constexpr (SL == 4) {
+    *reinterpret_cast<u32x2*>(ts + 8 * lane) = u32x2{c.meta[0], c.meta[1]};
+    if (lane < 8 * SL) *reinterpret_cast<uint32_t*>(ts + 128 * SL + 4 * lane) = c.rowsm[0];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-  for (int i = 0; i < SL; ++i) {
-    c.meta[i] = *reinterpret_cast<const uint16_t*>(ts + 128 * i + 2 * lane);
-    c.rowsm[i] = *reinterpret_cast<const uint32_t*>(ts + 128 * SL + 32 * i + 4 * (lane >> 3));
+    for (int i = 0; i < SL; ++i) {
+      c.meta[i] = *reinterpret_cast<const uint16_t*>(ts + 128 * i + 2 * lane);
+      c.rowsm[i] = *reinterpret_cast<const uint32_t*>(ts + 128 * SL + 32 * i + 4 * (lane >> 3));
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");   // these reads come before
+    __builtin_amdgcn_wave_barrier();                          // the next chunk's writes
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  } else {
+    uint32_t meta[SL], row[SL];
+    const uint32_t rs = c.rowsm[0];
+#pragma unroll
+    for (int i = 0; i < SL; ++i) {
+      if constexpr (SL == 2) {
+        const uint32_t v = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * (32 * i + (lane >> 1)), (int)c.meta[0]);
+        meta[i] = (v >> (16 * (lane & 1))) & 0xFFFFu;
+      } else {
+        meta[i] = c.meta[0] & 0xFFFFu;
+      }
+      row[i] = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * (8 * i + (lane >> 3)), (int)rs);
+    }
+#pragma unroll
+    for (int i = 0; i < SL; ++i) {
+      c.meta[i] = meta[i];
+      c.rowsm[i] = row[i];
+    }
   }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");   // these reads come before
-  __builtin_amdgcn_wave_barrier();                          // the next chunk's writes
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 // --------------------------------------------------------------------------
