@@ -92,6 +92,12 @@ int check_weight(const q4nx_weight* w, const char* name) {
 #ifndef Q4NX_SMALL_ROWS
 #define Q4NX_SMALL_ROWS 1024
 #endif
+#ifndef Q4NX_MKS_SHIFT
+#define Q4NX_MKS_SHIFT 2
+#endif
+#ifndef Q4NX_MKS_CPW8
+#define Q4NX_MKS_CPW8 2
+#endif
 #ifndef Q4NX_SMALL_CPW
 #define Q4NX_SMALL_CPW 2
 #endif
@@ -134,9 +140,15 @@ int pick_waves(int kind, int64_t total_tr, int M, int max_tc) {
   return (total_tr >= Q4NX_SMALL_ROWS || M > 2 || max_tc < Q4NX_SMALL_MIN_TC) ? 4 : 16;
 }
 
-int pick_ks(int waves, int64_t total_tr, int TC) {
+int pick_ks(int waves, int64_t total_tr, int TC, bool mfma = false) {
   if (waves == 16) return pow2_at_least((TC + Q4NX_SMALL_CPW - 1) / Q4NX_SMALL_CPW, 16);
-  if (waves == 8) return pow2_at_least((TC + Q4NX_SMALL_CPW - 1) / Q4NX_SMALL_CPW, 8);
+  if (waves == 8) {
+    const int cpw = mfma ? Q4NX_MKS_CPW8 : Q4NX_SMALL_CPW;
+    return pow2_at_least((TC + cpw - 1) / cpw, 8);
+  }
+  // the matrix-core kernel stages M >= 3 rows of records per workgroup, so
+  // it takes fewer, longer workgroups
+  if (mfma) total_tr <<= Q4NX_MKS_SHIFT;
   int ks = total_tr >= 2048 ? 1 : (total_tr >= 1024 ? 2 : 4);
   const int lim = TC >= 4 ? 4 : (TC >= 2 ? 2 : 1);
   return ks < lim ? ks : lim;
@@ -145,6 +157,7 @@ int pick_ks(int waves, int64_t total_tr, int TC) {
 // Launch shape of one kind's jobs (all valid, same M) in one launch.
 struct BatchShape {
   int waves, xl, parts;   // parts: units per tile row
+  bool mfma;              // k_gemv_q4m (q4 kinds, prepared records, M >= kGemvMfmaMinM)
 };
 
 BatchShape batch_shape(int kind, int64_t total_tr, int max_tc, int M) {
@@ -157,6 +170,7 @@ BatchShape batch_shape(int kind, int64_t total_tr, int max_tc, int M) {
   }
   const bool q4 = kind == q4nx::KIND_Q4_1 || kind == q4nx::KIND_Q4_K;
   sh.parts = !(q4 && sh.xl > 0) ? 1 : total_tr <= Q4NX_ROWSPLIT4_TR ? 4 : total_tr <= Q4NX_ROWSPLIT_TR ? 2 : 1;
+  sh.mfma = q4 && sh.xl > 0 && M >= q4nx::kGemvMfmaMinM;
   return sh;
 }
 
@@ -170,7 +184,7 @@ int fill_job(q4nx::GemvJob& g, const q4nx_gemv_job* j, const BatchShape& sh, int
   g.TC = j->w.cols / 256;
   g.ldx = j->w.cols;
   g.ldy = j->w.rows;
-  g.ks = pick_ks(sh.waves, total_tr, g.TC);
+  g.ks = pick_ks(sh.waves, total_tr, g.TC, sh.mfma);
   g.wg_begin = wg_begin;
   const int rpw = sh.waves / g.ks;
   return (g.TR * sh.parts + rpw - 1) / rpw;
@@ -225,7 +239,8 @@ bool topk_shape(const q4nx_weight* w, int M, int k, TopkShape& t) {
   g.TC = TC;
   g.ldx = w->cols;
   g.ldy = w->rows;
-  g.ks = pick_ks(4, TR, TC);
+  // the K split q4nx_gemv takes for this weight and M (so the logits agree bit for bit)
+  g.ks = pick_ks(4, TR, TC, q4 && M >= q4nx::kGemvMfmaMinM);
   g.wg_begin = 0;
   t.b.n_jobs = 1;
   const int rpw = 4 / g.ks;

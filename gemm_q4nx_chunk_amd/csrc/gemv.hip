@@ -231,6 +231,173 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_q4x(const GemvBatch b) {
   }
 }
 
+// k_gemv_q4x for M = 2 .. 8 activation rows with the products on the matrix
+// cores (q4_compute_mfma).  The dot chain's work grows with M (16 dot2 per
+// group and row); here a group's products for four activation rows are 8
+// small MFMAs, so the vector work per chunk stays that of one row: signed code
+// pairs, and per group and row two FMAs.  Each lane reads one record per block
+// of four rows instead of M, which also frees the registers the dot chain held
+// for them.  Records, staging, chunk ring and units are those of k_gemv_q4x;
+// only the lanes' places in a slice differ (the lane holds row
+// (l & 3) + 4 ((l >> 2) & 1) and group l >> 3 instead of row l >> 3 and
+// group l & 7), so its chunk loads are those of k_gemv_q4x's lane
+// 8 row + group, and the 8 lanes of one row (one per group) meet through
+// xor-shuffles over lane bits 3..5.
+template <int KIND, int M, int WAVES, int D, int SL, bool TOPK = false>
+__global__ __launch_bounds__(64 * WAVES) void k_gemv_q4m(const GemvBatch b) {
+  constexpr int NT = 64 * WAVES;
+  constexpr int XRP = 2;
+  constexpr int CB = ChunkBytes<KIND>::value;
+  constexpr int PARTS = 4 / SL;       // units per tile row
+  constexpr int UR = 8 * SL;          // output rows per unit
+  constexpr int NB = (M + 3) / 4;     // blocks of four activation rows
+  extern __shared__ __attribute__((aligned(16))) uint32_t xl[];
+  __shared__ float red[WAVES][UR][M];
+  const GemvJob J = gemv_job(b);
+  const int ks = J.ks, rpw = WAVES / ks;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int slot = wave / ks, part = wave % ks;
+  const int NU = J.TR * PARTS;
+  const int u0 = (blockIdx.x - J.wg_begin) * rpw;
+  const int u = u0 + slot < NU ? u0 + slot : NU - 1;          // spare waves redo the last unit, unstored
+  const int tr = u / PARTS, i0 = (u - tr * PARTS) * SL;
+  const int TC = J.TC;
+  const int c0 = part * TC / ks, c1 = (part + 1) * TC / ks;
+  const int R = M * TC * 8;
+  const int col = lane & 3;                        // the lane's activation row in a block
+  const int lrow = col + 4 * ((lane >> 2) & 1);    // its weight row in a slice
+  const int gg = lane >> 3;                        // its group in a tile column
+  const int lidx = 8 * lrow + gg;                  // k_gemv_q4x's lane for that (row, group)
+
+  // 1.-3. activations staged as records, as in k_gemv_q4x
+  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(J.x, (uint32_t)(((M - 1) * J.ldx + TC * 256) * 2));
+  auto xpart_off = [&](int q) {
+    const int r = q >> 2, m = r / (TC * 8), rem = r - m * TC * 8;
+    return (uint32_t)(m * J.ldx + 32 * rem + 8 * (q & 3)) * 2;   // q >= 4R: m >= M, past the resource
+  };
+  u32x4 xr[XRP];
+#pragma unroll
+  for (int i = 0; i < XRP; ++i)
+    xr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs, xpart_off(tid + NT * i), 0, 0));
+  const __amdgpu_buffer_rsrc_t wrs =
+      make_rsrc(J.w + ((size_t)tr * TC + c0) * CB, (uint32_t)((c1 - c0) * CB));
+  Q4Chunk<KIND, SL> ring[D];
+#pragma unroll
+  for (int j = 0; j < D; ++j) q4_load_rs<KIND>(wrs, j * CB, lidx, ring[j], i0);
+  float* sums = reinterpret_cast<float*>(xl + 16 * R);
+  auto put = [&](int q, const u32x4 v) {
+    uint32_t pr[4];
+    float f, X;
+    x_record_part(v, pr, f, X);
+    const int r = q >> 2;
+    if (r < R) {
+      *reinterpret_cast<u32x4*>(xl + 16 * r + 4 * (q & 3)) = u32x4{pr[0], pr[1], pr[2], pr[3]};
+      if ((q & 3) == 0) {
+        sums[2 * r] = f;
+        sums[2 * r + 1] = X;
+      }
+    }
+  };
+#pragma unroll
+  for (int i = 0; i < XRP; ++i) put(tid + NT * i, xr[i]);
+  constexpr int NS = M >= 3 ? 4 : 1;
+  for (int q0 = tid + NT * XRP; q0 < 4 * R; q0 += NS * NT) {
+    u32x4 v[NS];
+#pragma unroll
+    for (int i = 0; i < NS; ++i)
+      v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs, xpart_off(q0 + NT * i), 0, 0));
+#pragma unroll
+    for (int i = 0; i < NS; ++i) put(q0 + NT * i, v[i]);
+  }
+  __syncthreads();
+
+  const Q4Consts k = q4_consts();
+  float acc[SL][M];
+#pragma unroll
+  for (int i = 0; i < SL; ++i)
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[i][m] = 0.f;
+  auto step = [&](int j, int c) {
+    __builtin_amdgcn_sched_barrier(0);
+    uint32_t pa[NB][16];
+    float fv[NB][4], Xv[NB][4];
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk) {
+      // rows past M repeat row M - 1 (in bounds); their results are dropped
+      const int ma = 4 * blk + col < M ? 4 * blk + col : M - 1;
+      const int ra = (ma * TC + c) * 8 + gg;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(xl + 16 * ra + 4 * d);
+        pa[blk][4 * d] = v.x;
+        pa[blk][4 * d + 1] = v.y;
+        pa[blk][4 * d + 2] = v.z;
+        pa[blk][4 * d + 3] = v.w;
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int mt = 4 * blk + t < M ? 4 * blk + t : M - 1;
+        const int rt = (mt * TC + c) * 8 + gg;
+        const u32x2 fx = *reinterpret_cast<const u32x2*>(sums + 2 * rt);
+        fv[blk][t] = __uint_as_float(fx.x);
+        Xv[blk][t] = __uint_as_float(fx.y);
+      }
+    }
+    q4_compute_mfma<KIND, M, NB, SL>(ring[j], pa, fv, Xv, k, acc);
+    q4_load_rs<KIND>(wrs, (uint32_t)(c + D - c0) * CB, lidx, ring[j], i0);
+  };
+  int base = c0;
+  for (; base + D <= c1; base += D) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) step(j, base + j);
+  }
+#pragma unroll
+  for (int j = 0; j + 1 < D; ++j)
+    if (base + j < c1) step(j, base + j);
+
+  // the 8 groups of a row: lanes lrow + 8 g' for g' = 0..7 (bits 3..5)
+#pragma unroll
+  for (int i = 0; i < SL; ++i)
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      float v = acc[i][m];
+      v += __shfl_xor(v, 8);
+      v += __shfl_xor(v, 16);
+      v += __shfl_xor(v, 32);
+      acc[i][m] = v;
+    }
+  if (gg == 0) {
+#pragma unroll
+    for (int i = 0; i < SL; ++i)
+#pragma unroll
+      for (int m = 0; m < M; ++m) red[wave][8 * i + lrow][m] = acc[i][m];
+  }
+  __syncthreads();
+  __shared__ float tv[TOPK ? M : 1][TOPK ? kTopkRows : 1];
+  for (int idx = tid; idx < rpw * UR * M; idx += NT) {
+    const int s = idx / (UR * M), rem = idx - s * UR * M;
+    const int r = rem / M, m = rem - r * M;
+    const int t = u0 + s;   // unit: tile row t / PARTS, rows UR * (t % PARTS) + r of it
+    if (t < NU) {
+      float v = 0.f;
+      for (int p = 0; p < ks; ++p) v += red[s * ks + p][r][m];
+      if constexpr (TOPK) {
+        tv[m][s * UR + r] = v;
+        if (J.y) J.y[(size_t)m * J.ldy + UR * t + r] = v;
+      } else {
+        __builtin_nontemporal_store(v, &J.y[(size_t)m * J.ldy + UR * t + r]);   // written once
+      }
+    }
+  }
+  if constexpr (TOPK) {   // the same pick as k_gemv_q4x's
+    __shared__ uint32_t s_flag;
+    __syncthreads();
+    const int nr = (NU - u0 < rpw ? NU - u0 : rpw) * UR;
+    topk_epilogue<M, WAVES>(b.tk, tv, nr, (uint32_t)(UR * u0), &s_flag);
+  }
+}
+
 // Q8 with the workgroup's activations staged once in LDS and an unconditional
 // buffer-load chunk ring: the same structure as k_gemv_q4x, so a step waits
 // only for its own chunk.
@@ -543,7 +710,12 @@ static void launch_xl(F* kern, int n_wg, int threads, int xl_bytes, hipStream_t 
 template <int KIND, int M>
 static hipError_t launch_topk(const GemvBatch& b, int n_wg, int xl_bytes, hipStream_t s) {
   constexpr int D = GemvXDepth<M, 4>::value;
-  if constexpr (KIND == KIND_Q4_1 || KIND == KIND_Q4_K) {
+  if constexpr ((KIND == KIND_Q4_1 || KIND == KIND_Q4_K) && M >= kGemvMfmaMinM && M >= 2) {
+    // the products of q4nx_gemv at this M, so the picked values are its logits bit for bit
+    if (b.sl == 2) launch_xl(k_gemv_q4m<KIND, M, 4, D, 2, true>, n_wg, 256, xl_bytes, s, b);
+    else if (b.sl == 1) launch_xl(k_gemv_q4m<KIND, M, 4, D, 1, true>, n_wg, 256, xl_bytes, s, b);
+    else launch_xl(k_gemv_q4m<KIND, M, 4, D, 4, true>, n_wg, 256, xl_bytes, s, b);
+  } else if constexpr (KIND == KIND_Q4_1 || KIND == KIND_Q4_K) {
     if (b.sl == 2) launch_xl(k_gemv_q4x<KIND, M, 4, D, 2, true>, n_wg, 256, xl_bytes, s, b);
     else if (b.sl == 1) launch_xl(k_gemv_q4x<KIND, M, 4, D, 1, true>, n_wg, 256, xl_bytes, s, b);
     else launch_xl(k_gemv_q4x<KIND, M, 4, D, 4, true>, n_wg, 256, xl_bytes, s, b);
@@ -579,6 +751,14 @@ template <int KIND, int M, int WAVES>
 static hipError_t launch_one(const GemvBatch& b, int n_wg, int xl_bytes, hipStream_t s) {
   if constexpr (KIND == KIND_Q4_1 || KIND == KIND_Q4_K) {
     constexpr int D = GemvXDepth<M, WAVES>::value;
+    if constexpr (M >= kGemvMfmaMinM && M >= 2) {   // the matrix-core products
+      if (xl_bytes > 0) {
+        if (b.sl == 2) launch_xl(k_gemv_q4m<KIND, M, WAVES, D, 2>, n_wg, 64 * WAVES, xl_bytes, s, b);
+        else if (b.sl == 1) launch_xl(k_gemv_q4m<KIND, M, WAVES, D, 1>, n_wg, 64 * WAVES, xl_bytes, s, b);
+        else launch_xl(k_gemv_q4m<KIND, M, WAVES, D, 4>, n_wg, 64 * WAVES, xl_bytes, s, b);
+        return hipGetLastError();
+      }
+    }
     if (xl_bytes > 0 && b.sl == 2)
       launch_xl(k_gemv_q4x<KIND, M, WAVES, D, 2>, n_wg, 64 * WAVES, xl_bytes, s, b);
     else if (xl_bytes > 0 && b.sl == 1)

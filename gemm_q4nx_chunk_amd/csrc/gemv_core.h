@@ -530,6 +530,71 @@ __device__ __forceinline__ void q4_compute_b(const Q4Chunk<KIND, SL>& c, const X
   }
 }
 
+// The same products for several activation rows on the matrix cores
+// (v_mfma_f32_4x4x4_16b_f16: 16 independent 4x4 blocks, 4 products deep).
+// The lanes of a wave split a slice as 4-lane blocks: lane l holds the codes
+// of row (l & 3) + 4 ((l >> 2) & 1), group l >> 3, and the record of that
+// group for activation row 4 blk + (l & 3).  Block l / 4 multiplies the
+// records (4 activation rows x 4 columns of the group) by the codes (4 columns
+// x 4 weight rows), and after the group's 8 steps lane l holds, for its own
+// weight row, D[t] = sum over the group of code * record for activation rows
+// 4 blk + t, t = 0..3.  Step st takes chain pairs 2 st and 2 st + 1 of both
+// the record and the codes, so every product pairs the same column.  Products
+// of a code and an fp16 are exact and the sum is kept in fp32, as in the dot
+// chain; a record kept in bf16 (f < 0) takes the bf16 form of the same step
+// (v_mfma_f32_4x4x4_16b_bf16, exact small-integer codes), whose rows for the
+// fp16 records are discarded.  fv, Xv: f and X of the records of activation
+// rows 4 blk + t in the lane's group.
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+template <int KIND, int M, int NB, int SL>
+__device__ __forceinline__ void q4_compute_mfma(const Q4Chunk<KIND, SL>& c, const uint32_t (&pa)[NB][16],
+                                                const float (&fv)[NB][4], const float (&Xv)[NB][4],
+                                                const Q4Consts& k, float (&acc)[SL][M]) {
+  bool slow = false;
+#pragma unroll
+  for (int blk = 0; blk < NB; ++blk)
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      if (4 * blk + t < M) slow |= fv[blk][t] < 0.f;
+  const bool wslow = __builtin_amdgcn_ballot_w64(slow) != 0;   // uniform
+#pragma unroll
+  for (int i = 0; i < SL; ++i) {
+    const Q4Group gp = q4_group<KIND, SL>(c, i);
+    uint32_t cp[16];
+    q4_signed(c.q[i], gp, k, cp);
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk) {
+      f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        const f16x4 a = __builtin_bit_cast(f16x4, u32x2{pa[blk][2 * st], pa[blk][2 * st + 1]});
+        const f16x4 w = __builtin_bit_cast(f16x4, u32x2{cp[2 * st], cp[2 * st + 1]});
+        d = __builtin_amdgcn_mfma_f32_4x4x4f16(a, w, d, 0, 0, 0);
+      }
+      if (wslow) {
+        f32x4 e = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < 8; ++st) {
+          const i16x4 a = __builtin_bit_cast(i16x4, u32x2{pa[blk][2 * st], pa[blk][2 * st + 1]});
+          const i16x4 w = __builtin_bit_cast(
+              i16x4, u32x2{f16pair_to_bf16(cp[2 * st]), f16pair_to_bf16(cp[2 * st + 1])});
+          e = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(a, w, e, 0, 0, 0);
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          if (fv[blk][t] < 0.f) d[t] = e[t];
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int m = 4 * blk + t;
+        if (m < M) acc[i][m] = fmaf(gp.s * fabsf(fv[blk][t]), d[t], fmaf(gp.delta, Xv[blk][t], acc[i][m]));
+      }
+    }
+  }
+}
+
 // ===========================================================================
 // Q8 (both code layouts)
 // ===========================================================================

@@ -150,6 +150,12 @@ __device__ __forceinline__ GemvJob gemv_job(const GemvBatch& b) {
 // Host-side launchers (gemv.hip, gemm.hip, decode.hip, moe.hip).
 // Dynamic LDS bytes of the prepared-activation GEMV for a launch whose jobs
 // have at most max_tc tile columns, or 0 when that kernel does not apply.
+// Activation rows from which q4 launches with prepared records take the
+// matrix-core products (k_gemv_q4m) instead of the dot chain (k_gemv_q4x).
+#ifndef Q4NX_GEMV_MFMA_MIN_M
+#define Q4NX_GEMV_MFMA_MIN_M 3
+#endif
+constexpr int kGemvMfmaMinM = Q4NX_GEMV_MFMA_MIN_M;
 int gemv_xl_bytes(int kind, int M, int waves, int max_tc);
 hipError_t launch_gemv(int kind, int M, int waves, const GemvBatch& b, int n_wg, int xl_bytes,
                        hipStream_t s);

@@ -214,7 +214,7 @@ def _x_extreme(g, M, K):
 
 
 @pytest.mark.parametrize("kind", ["q4_1", "q4_k"])
-@pytest.mark.parametrize("M", [1, 2, 4])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 6, 8])
 def test_gemv_activation_extremes(kind, M):
     N, K = SMALL
     g = synth.rng("gpu-edge", "x-extreme", kind, M)

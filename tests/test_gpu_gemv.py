@@ -219,7 +219,7 @@ def test_mixed_q4k_layer_and_q8_lm_head_full_size(layout):
 
 
 @pytest.mark.parametrize("kind,layout", KINDS)
-@pytest.mark.parametrize("M", [2, 3, 4])
+@pytest.mark.parametrize("M", [2, 3, 4, 5, 8])
 def test_verify_window_slot_invariance(kind, layout, M):
     """A verify window of M tokens (Strata article, section 6.2, batch slots):
     a token's result does not depend on the slot it occupies -- permuting the
@@ -278,10 +278,12 @@ def test_batched_at_the_job_limit(M):
 @pytest.mark.parametrize("M", [1, 2, 4])
 def test_launch_of_several_rounds(kind, M):
     """A launch of more workgroups than the CUs hold at once (the 28672 x 4096
-    gate|up of an 8B layer): sampled tile rows against the oracle, and its
-    first 256 tile rows bit for bit against the same rows as a launch that
-    fits in one round (the same K split and chunk order)."""
-    N, K = 28672, 4096
+    gate|up of an 8B layer; at M >= 3, whose matrix-core launches give each
+    wave a whole K range and so take fewer workgroups, three of them side by
+    side): sampled tile rows against the oracle, and its first 512 tile rows
+    bit for bit against the same rows as a launch that fits in one round (the
+    same K split and chunk order)."""
+    N, K = (28672 if M <= 2 else 86016), 4096
     g = synth.rng("gpu-gemv", "upw", kind)
     ch = synth.gen_q4_1(g, N, K, zero="normal") if kind == "q4_1" else synth.gen_q4_k(g, N, K)
     x = synth.gen_x(synth.rng("gpu-gemv", "upw-x", kind, M), M, K)
@@ -291,8 +293,8 @@ def test_launch_of_several_rounds(kind, M):
     yr, a = oracle.gemv_ref(W, x)
     ysub = np.concatenate([y[:, 32 * t:32 * t + 32] for t in tr], axis=1)
     assert oracle.tol_ratio(ysub, yr, a) <= 1.0
-    part = gemv(dev_u8(np.ascontiguousarray(ch[:256])), 8192, K, kind, x)
-    np.testing.assert_array_equal(part.view(np.uint32), y[:, :8192].view(np.uint32))
+    part = gemv(dev_u8(np.ascontiguousarray(ch[:512])), 16384, K, kind, x)
+    np.testing.assert_array_equal(part.view(np.uint32), y[:, :16384].view(np.uint32))
 
 
 @pytest.mark.parametrize("N,M", [(151936, 1), (151936, 2), (40960, 1), (40960, 3)])
