@@ -238,11 +238,12 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_q4x(const GemvBatch b) {
 // pairs, and per group and row two FMAs.  Each lane reads one record per block
 // of four rows instead of M, which also frees the registers the dot chain held
 // for them.  Records, staging, chunk ring and units are those of k_gemv_q4x;
-// only the lanes' places in a slice differ (the lane holds row
-// (l & 3) + 4 ((l >> 2) & 1) and group l >> 3 instead of row l >> 3 and
-// group l & 7), so its chunk loads are those of k_gemv_q4x's lane
-// 8 row + group, and the 8 lanes of one row (one per group) meet through
-// xor-shuffles over lane bits 3..5.
+// only the lanes' places in a slice differ (lane l holds row
+// (l & 3) + 4 ((l >> 4) & 1) and group ((l >> 2) & 3) + 4 (l >> 5) instead of
+// row l >> 3 and group l & 7), so its chunk loads are those of k_gemv_q4x's
+// lane 8 row + group, and the 8 lanes of one row (one per group) meet through
+// xor-shuffles over lane bits 2, 3 and 5.  At M = 1 the dot chain is faster
+// (decode step 1.08 against 1.045 ms, Q4_K lm_head 4.9 against 5.4 TB/s).
 template <int KIND, int M, int WAVES, int D, int SL, bool TOPK = false>
 __global__ __launch_bounds__(64 * WAVES) void k_gemv_q4m(const GemvBatch b) {
   constexpr int NT = 64 * WAVES;
@@ -265,10 +266,13 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_q4m(const GemvBatch b) {
   const int TC = J.TC;
   const int c0 = part * TC / ks, c1 = (part + 1) * TC / ks;
   const int R = M * TC * 8;
-  const int col = lane & 3;                        // the lane's activation row in a block
-  const int lrow = col + 4 * ((lane >> 2) & 1);    // its weight row in a slice
-  const int gg = lane >> 3;                        // its group in a tile column
-  const int lidx = 8 * lrow + gg;                  // k_gemv_q4x's lane for that (row, group)
+  // A quarter-wave (16 lanes, four blocks) takes rows 4 h .. 4 h + 3 and groups
+  // 4 v .. 4 v + 3 of a slice, h = bit 4 and v = bit 5 of the lane: four
+  // 64-byte runs, one per row, for each 16-byte load instruction.
+  const int col = lane & 3;                             // the lane's activation row in a block
+  const int lrow = col + 4 * ((lane >> 4) & 1);         // its weight row in a slice
+  const int gg = ((lane >> 2) & 3) + 4 * (lane >> 5);   // its group in a tile column
+  const int lidx = 8 * lrow + gg;                       // k_gemv_q4x's lane for that (row, group)
 
   // 1.-3. activations staged as records, as in k_gemv_q4x
   const __amdgpu_buffer_rsrc_t xrs = make_rsrc(J.x, (uint32_t)(((M - 1) * J.ldx + TC * 256) * 2));
@@ -356,14 +360,14 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_q4m(const GemvBatch b) {
   for (int j = 0; j + 1 < D; ++j)
     if (base + j < c1) step(j, base + j);
 
-  // the 8 groups of a row: lanes lrow + 8 g' for g' = 0..7 (bits 3..5)
+  // the 8 groups of a row: the lanes that differ in bits 2, 3 and 5
 #pragma unroll
   for (int i = 0; i < SL; ++i)
 #pragma unroll
     for (int m = 0; m < M; ++m) {
       float v = acc[i][m];
+      v += __shfl_xor(v, 4);
       v += __shfl_xor(v, 8);
-      v += __shfl_xor(v, 16);
       v += __shfl_xor(v, 32);
       acc[i][m] = v;
     }

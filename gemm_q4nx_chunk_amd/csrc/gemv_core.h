@@ -532,9 +532,11 @@ __device__ __forceinline__ void q4_compute_b(const Q4Chunk<KIND, SL>& c, const X
 
 // The same products for several activation rows on the matrix cores
 // (v_mfma_f32_4x4x4_16b_f16: 16 independent 4x4 blocks, 4 products deep).
-// The lanes of a wave split a slice as 4-lane blocks: lane l holds the codes
-// of row (l & 3) + 4 ((l >> 2) & 1), group l >> 3, and the record of that
-// group for activation row 4 blk + (l & 3).  Block l / 4 multiplies the
+// The lanes of a wave split a slice as 4-lane blocks: the 4 lanes of block
+// l / 4 hold the codes of 4 rows of one group (k_gemv_q4m gives the order),
+// and lane l the record of that group for activation row 4 blk + (l & 3)
+// (on gfx950, A row i and B column j of a block come from its lane i and j,
+// and result D[r][j] sits in register r of lane j).  Block l / 4 multiplies the
 // records (4 activation rows x 4 columns of the group) by the codes (4 columns
 // x 4 weight rows), and after the group's 8 steps lane l holds, for its own
 // weight row, D[t] = sum over the group of code * record for activation rows

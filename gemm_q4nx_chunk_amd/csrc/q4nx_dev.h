@@ -153,7 +153,7 @@ __device__ __forceinline__ GemvJob gemv_job(const GemvBatch& b) {
 // Activation rows from which q4 launches with prepared records take the
 // matrix-core products (k_gemv_q4m) instead of the dot chain (k_gemv_q4x).
 #ifndef Q4NX_GEMV_MFMA_MIN_M
-#define Q4NX_GEMV_MFMA_MIN_M 3
+#define Q4NX_GEMV_MFMA_MIN_M 2
 #endif
 constexpr int kGemvMfmaMinM = Q4NX_GEMV_MFMA_MIN_M;
 int gemv_xl_bytes(int kind, int M, int waves, int max_tc);
