@@ -525,6 +525,8 @@ def gemm_leg(steps, warmup, graph):
         msm, _ = time_calls(runm, steps, warmup, graph)
         res[f"M{M}"] = {"ms_per_block": msm, "GB_s": nbytes / (msm * 1e-3) / 1e9,
                         "pct_hbm_peak": 100 * nbytes / (msm * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    # a verify window of M tokens against one token over the same weights
+    res["window_cost_vs_M1"] = {f"M{M}": res[f"M{M}"]["ms_per_block"] / res["M1"]["ms_per_block"] for M in (2, 4)}
     del w
     return res
 

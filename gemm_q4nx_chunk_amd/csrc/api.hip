@@ -95,9 +95,6 @@ int check_weight(const q4nx_weight* w, const char* name) {
 #ifndef Q4NX_MKS_SHIFT
 #define Q4NX_MKS_SHIFT 2
 #endif
-#ifndef Q4NX_MKS_CPW8
-#define Q4NX_MKS_CPW8 2
-#endif
 #ifndef Q4NX_SMALL_CPW
 #define Q4NX_SMALL_CPW 2
 #endif
@@ -142,10 +139,7 @@ int pick_waves(int kind, int64_t total_tr, int M, int max_tc) {
 
 int pick_ks(int waves, int64_t total_tr, int TC, bool mfma = false) {
   if (waves == 16) return pow2_at_least((TC + Q4NX_SMALL_CPW - 1) / Q4NX_SMALL_CPW, 16);
-  if (waves == 8) {
-    const int cpw = mfma ? Q4NX_MKS_CPW8 : Q4NX_SMALL_CPW;
-    return pow2_at_least((TC + cpw - 1) / cpw, 8);
-  }
+  if (waves == 8) return pow2_at_least((TC + Q4NX_SMALL_CPW - 1) / Q4NX_SMALL_CPW, 8);
   // the matrix-core kernel stages M >= 3 rows of records per workgroup, so
   // it takes fewer, longer workgroups
   if (mfma) total_tr <<= Q4NX_MKS_SHIFT;
