@@ -247,7 +247,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_q4x(const GemvBatch b) {
 template <int KIND, int M, int WAVES, int D, int SL, bool TOPK = false>
 __global__ __launch_bounds__(64 * WAVES) void k_gemv_q4m(const GemvBatch b) {
   constexpr int NT = 64 * WAVES;
-  constexpr int XRP = 2;
+  constexpr int XRP = 4;   // staging parts per thread loaded before the first chunks
   constexpr int CB = ChunkBytes<KIND>::value;
   constexpr int PARTS = 4 / SL;       // units per tile row
   constexpr int UR = 8 * SL;          // output rows per unit
@@ -274,7 +274,10 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_q4m(const GemvBatch b) {
   const int gg = ((lane >> 2) & 3) + 4 * (lane >> 5);   // its group in a tile column
   const int lidx = 8 * lrow + gg;                       // k_gemv_q4x's lane for that (row, group)
 
-  // 1.-3. activations staged as records, as in k_gemv_q4x
+  // 1.-3. activations staged as records, as in k_gemv_q4x, with more of the
+  // staging loads in flight (this kernel has the registers): 4 parts per
+  // thread ahead of the chunk loads, then 4 at a time.  8B block against 2
+  // and 1 (at M = 2): M = 2 1.355 -> 1.295 ms, M = 4 1.71 -> 1.60 ms.
   const __amdgpu_buffer_rsrc_t xrs = make_rsrc(J.x, (uint32_t)(((M - 1) * J.ldx + TC * 256) * 2));
   auto xpart_off = [&](int q) {
     const int r = q >> 2, m = r / (TC * 8), rem = r - m * TC * 8;
@@ -305,7 +308,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_q4m(const GemvBatch b) {
   };
 #pragma unroll
   for (int i = 0; i < XRP; ++i) put(tid + NT * i, xr[i]);
-  constexpr int NS = M >= 3 ? 4 : 1;
+  constexpr int NS = 4;
   for (int q0 = tid + NT * XRP; q0 < 4 * R; q0 += NS * NT) {
     u32x4 v[NS];
 #pragma unroll
