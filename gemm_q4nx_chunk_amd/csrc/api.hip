@@ -194,6 +194,28 @@ int run_batch(int kind, const q4nx_gemv_job* const* jobs, int n, int M, hipStrea
     max_tc = std::max(max_tc, jobs[i]->w.cols / 256);
   }
   const BatchShape sh = batch_shape(kind, total_tr, max_tc, M);
+  // q4 kinds at M = 5..8 whose records do not fit in LDS (long K): two passes
+  // of 4 rows through the matrix-core kernel, rows 0..3 and then M-4..M-1,
+  // instead of the kernel that loads activations per chunk.  Each pass reads
+  // the weights once; a row computed by both comes out with the same bits
+  // both times (same kernel, shape and K split), so the second write changes
+  // nothing and a row's bits do not depend on its slot.
+  const bool q4 = kind == q4nx::KIND_Q4_1 || kind == q4nx::KIND_Q4_K;
+  if (q4 && M > 4 && sh.xl <= 0 && q4nx::gemv_xl_bytes(kind, 4, 4, max_tc) > 0) {
+    std::vector<q4nx_gemv_job> part(n);
+    std::vector<const q4nx_gemv_job*> ptr(n);
+    for (int m0 : {0, M - 4}) {
+      for (int i = 0; i < n; ++i) {
+        part[i] = *jobs[i];
+        part[i].x = jobs[i]->x + (size_t)m0 * jobs[i]->w.cols;
+        part[i].y = jobs[i]->y + (size_t)m0 * jobs[i]->w.rows;
+        ptr[i] = &part[i];
+      }
+      const int st = run_batch(kind, ptr.data(), n, 4, s);
+      if (st != Q4NX_OK) return st;
+    }
+    return Q4NX_OK;
+  }
   for (int i0 = 0; i0 < n; i0 += q4nx::kMaxBatch) {
     const int cnt = n - i0 < q4nx::kMaxBatch ? n - i0 : q4nx::kMaxBatch;
     q4nx::GemvBatch b;

@@ -236,13 +236,13 @@ def test_verify_window_slot_invariance(kind, layout, M):
 
 @pytest.mark.parametrize("kind", ["q4_1", "q4_k"])
 @pytest.mark.parametrize("N,K,M", [(64, 14336, 2), (64, 14336, 4), (96, 7424, 3), (32, 40960, 1), (160, 3328, 8),
-                                   (416, 14336, 3), (1056, 4608, 4)])
+                                   (416, 14336, 3), (1056, 4608, 4), (96, 14336, 5), (160, 14336, 8)])
 def test_long_activation_rows(kind, N, K, M):
     """Activation rows too long for one register load per thread (several
     rows, long K, odd tile-column counts; 4-, 8- and 16-wave workgroups, the
-    8-wave ones at M = 3 and 4 over at least 17 tile columns): against the
-    oracle, and a permutation of the rows of x permutes the rows of y bit for
-    bit."""
+    8-wave ones at M = 3 and 4 over at least 17 tile columns; at M = 5 and 8
+    over 56 tile columns, two overlapping 4-row passes): against the oracle,
+    and a permutation of the rows of x permutes the rows of y bit for bit."""
     ch = _gen(kind, None, N, K, "longrows")
     d = dev_u8(ch)
     x = synth.gen_x(synth.rng("gpu-gemv", "longrows", kind, N, K, M), M, K)
