@@ -94,7 +94,9 @@ def _one_hot_check(ch, kind, layout, N, K, cols):
 @pytest.mark.parametrize("kind,layout", KINDS)
 def test_one_hot_activation_gives_the_column(kind, layout):
     """x = e_k returns column k of the decoded weights bit for bit: the signed
-    codes and their center make s (c - c0) + (z + c0 s) one rounding of s c + z."""
+    codes and their center make s (c - c0) + (z + c0 s) one rounding of s c + z.
+    The columns go in calls of up to 4 rows (M = 4 and 3: the matrix-core
+    products; a single row: the dot chain), so the pin holds for both."""
     N, K = 64, 512
     _one_hot_check(_gen(kind, layout, N, K, "onehot"), kind, layout, N, K, [0, 5, 31, 32, 255, 256, 511])
 
